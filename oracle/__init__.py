@@ -1,0 +1,193 @@
+"""Plain fp64 CPU oracle for the pyramid Top-K block selection (ctypes wrapper).
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package. It shares no code
+with the HIP library under ``block_selection_amd/`` and never calls it.
+
+The arithmetic lives in ``pisa_oracle.c`` (fp64, plain loops, OpenMP over
+independent walks); this module only marshals numpy arrays. Each function
+names the passage of the pages it follows in the C source.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pisa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libpisa_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (IEEE double arithmetic, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-Wall", "-Wno-unknown-pragmas", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    i64, i32, dbl, lng = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_long
+    lib.pisa_oracle_num_levels.argtypes = [i64, i32, i32]
+    lib.pisa_oracle_num_levels.restype = i32
+    lib.pisa_oracle_level_sizes.argtypes = [i64, i32, i32, P, i32]
+    lib.pisa_oracle_level_sizes.restype = i32
+    lib.pisa_oracle_build_pyramid.argtypes = [P, i64, i32, i32, i32, i32, P, i32]
+    lib.pisa_oracle_build_pyramid.restype = i32
+    lib.pisa_oracle_walk.argtypes = [P, P, i64, P, P, i64, i32, i32, i32, i32, i32, i32,
+                                     P, P, P, i32]
+    lib.pisa_oracle_walk.restype = i32
+    lib.pisa_oracle_walk_trace.argtypes = [P, i64, i32, P, P, i64, i32, i32, i32, i32, i32, i32,
+                                           P, P, P, P, P, i32]
+    lib.pisa_oracle_walk_trace.restype = i32
+    lib.pisa_oracle_node_score.argtypes = [P, i64, i32, P, P, i64, i32, i32, i32, i32, i32,
+                                           i32, i64]
+    lib.pisa_oracle_node_score.restype = dbl
+    lib.pisa_oracle_validate.argtypes = [P, i64, i32, P, P, i64, i32, i32, i32, i32, i32, i32,
+                                         P, dbl, lng]
+    lib.pisa_oracle_validate.restype = i32
+    _lib = lib
+    return lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def level_sizes(N: int, C: int = 64, g: int = 2) -> list:
+    """[M_1, ..., M_L]: leaf blocks, then ceil-halving up to the single root."""
+    buf = np.zeros(64, np.int64)
+    L = _load().pisa_oracle_level_sizes(N, C, g, _p(buf), 64)
+    if L < 0:
+        raise ValueError("bad geometry")
+    return [int(x) for x in buf[:L]]
+
+
+def level_offsets(N: int, C: int = 64, g: int = 2) -> list:
+    """Row offset of each level (1..L) inside one KV head's pyramid."""
+    out, acc = [], 0
+    for m in level_sizes(N, C, g):
+        out.append(acc)
+        acc += m
+    return out
+
+
+def build_pyramid(k: np.ndarray, C: int = 64, g: int = 2, nthreads: int = 0) -> np.ndarray:
+    """k: float [N, Hkv, d] -> double [Hkv, sum(M_l), d] of raw-key means."""
+    k = _f32(k)
+    N, Hkv, d = k.shape
+    total = sum(level_sizes(N, C, g))
+    pyr = np.zeros((Hkv, total, d), np.float64)
+    rc = _load().pisa_oracle_build_pyramid(_p(k), N, Hkv, d, C, g, _p(pyr), nthreads)
+    if rc != 0:
+        raise RuntimeError(f"oracle build_pyramid failed ({rc})")
+    return pyr
+
+
+def walk(q_rows: np.ndarray, t_rows, k: np.ndarray, pyr: np.ndarray, topk: int,
+         C: int = 64, g: int = 2, nthreads: int = 0):
+    """Walks for the query rows of positions t_rows (one batch element).
+
+    q_rows: float [n, Hq, d]; k: float [N, Hkv, d]; pyr from build_pyramid.
+    Returns (idx int32 [n, Hkv, topk] ascending, -1 padded;
+             min_gap double [n, Hkv] (inf if nothing was scored);
+             gap_level int32 [n, Hkv]).
+    """
+    q_rows, k = _f32(q_rows), _f32(k)
+    t_rows = np.ascontiguousarray(t_rows, dtype=np.int64)
+    n, Hq, d = q_rows.shape
+    N, Hkv, _ = k.shape
+    assert t_rows.shape == (n,)
+    pyr = np.ascontiguousarray(pyr, dtype=np.float64)
+    idx = np.zeros((n, Hkv, topk), np.int32)
+    gap = np.zeros((n, Hkv), np.float64)
+    lvl = np.zeros((n, Hkv), np.int32)
+    rc = _load().pisa_oracle_walk(_p(q_rows), _p(t_rows), n, _p(k), _p(pyr), N, Hq, Hkv, d, C, g,
+                                  topk, _p(idx), _p(gap), _p(lvl), nthreads)
+    if rc != 0:
+        raise RuntimeError(f"oracle walk failed ({rc})")
+    return idx, gap, lvl
+
+
+def walk_trace(q_row: np.ndarray, t: int, j: int, k: np.ndarray, pyr: np.ndarray, topk: int,
+               C: int = 64, g: int = 2):
+    """One walk with every candidate recorded.
+
+    Returns (idx [topk], records) where records is a list of
+    (level, node, score or nan, kept) in the order the walk considered them.
+    """
+    q_row, k = _f32(q_row), _f32(k)
+    Hq, d = q_row.shape
+    N, Hkv, _ = k.shape
+    cap = 4096
+    lv = np.zeros(cap, np.int32)
+    nd = np.zeros(cap, np.int64)
+    sc = np.zeros(cap, np.float64)
+    kp = np.zeros(cap, np.int32)
+    idx = np.zeros(topk, np.int32)
+    pyr = np.ascontiguousarray(pyr, dtype=np.float64)
+    n = _load().pisa_oracle_walk_trace(_p(q_row), t, j, _p(k), _p(pyr), N, Hq, Hkv, d, C, g, topk,
+                                       _p(idx), _p(lv), _p(nd), _p(sc), _p(kp), cap)
+    if n < 0:
+        raise RuntimeError(f"oracle walk_trace failed ({n})")
+    n = min(n, cap)
+    recs = [(int(lv[i]), int(nd[i]), float(sc[i]), bool(kp[i])) for i in range(n)]
+    return idx, recs
+
+
+def node_score(q_row: np.ndarray, t: int, j: int, k: np.ndarray, pyr: np.ndarray, level: int,
+               node: int, C: int = 64, g: int = 2) -> float:
+    """Score of one node (sum over the group's heads of the LSE over its eligible children)."""
+    q_row, k = _f32(q_row), _f32(k)
+    Hq, d = q_row.shape
+    N, Hkv, _ = k.shape
+    pyr = np.ascontiguousarray(pyr, dtype=np.float64)
+    return float(_load().pisa_oracle_node_score(_p(q_row), t, j, _p(k), _p(pyr), N, Hq, Hkv, d,
+                                                C, g, level, node))
+
+
+def validate(q_row: np.ndarray, t: int, j: int, k: np.ndarray, pyr: np.ndarray, topk: int,
+             target, eps: float, budget: int = 200000, C: int = 64, g: int = 2) -> int:
+    """1 if target is reachable by resolving near-ties within eps, 0 if not, -1 if undecided."""
+    q_row, k = _f32(q_row), _f32(k)
+    Hq, d = q_row.shape
+    N, Hkv, _ = k.shape
+    tg = np.ascontiguousarray(target, dtype=np.int32)
+    assert tg.shape == (topk,)
+    pyr = np.ascontiguousarray(pyr, dtype=np.float64)
+    r = _load().pisa_oracle_validate(_p(q_row), t, j, _p(k), _p(pyr), N, Hq, Hkv, d, C, g, topk,
+                                     _p(tg), eps, budget)
+    if r == -2:
+        raise RuntimeError("oracle validate: bad arguments")
+    return int(r)
+
+
+def decode_step(k_all: np.ndarray, n: int, q_new: np.ndarray, topk: int, C: int = 64, g: int = 2,
+                nthreads: int = 0):
+    """Selection after appending key n: rebuild over keys 0..n and walk at t = n.
+
+    k_all: float [>= n+1, Hkv, d]; q_new: float [Hq, d].
+    Returns (pyr, idx [Hkv, topk], min_gap [Hkv]).
+    """
+    k = _f32(k_all[: n + 1])
+    pyr = build_pyramid(k, C, g, nthreads)
+    idx, gap, _ = walk(q_new[None], np.array([n]), k, pyr, topk, C, g, nthreads)
+    return pyr, idx[0], gap[0]
