@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Selection-latency benchmark of the pyramid Top-K block selection on one GPU.
+
+A step is one pass of the whole selection stage over one synthetic batch:
+pisa_build_pyramid (mean pyramid over all keys) followed by
+pisa_select_prefill (the coarse-to-fine walk for every query position and KV
+head). Inputs are seeded N(0,1) bf16 Q/K shaped like the selection-latency
+benchmark of the pages (B=1, Hq=32, Hkv=2, d=64, C=64, g=2, K=8), resident in
+HBM before timing starts; attention over the selected blocks is not part of a
+step. Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long256k]
+                  [--no-cpu-baseline] [--no-extras]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
+HBM_PEAK_GBS = 8000.0
+
+
+def _hash_sources(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "block_selection_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def walk_counts(N: int, topk: int, GQ: int, Hkv: int, C: int = 64):
+    """Algorithmic work of one prefill selection, from the level geometry alone.
+
+    For each position t the number of candidates at level l is the eligible
+    children of min(K, eligible-at-level-above) survivors, capped by the
+    eligible node count; a level is scored only when it has more than K.
+    Each scored upper candidate costs (eligible children) logits per head, each
+    scored leaf its eligible raw keys per head. Returns (logits, lse_terms,
+    fetched_bytes) summed over all walks; the count assumes the causal
+    frontier node survives (exact for full-depth walks).
+    """
+    t = np.arange(N, dtype=np.int64)
+    sizes, span = [], C
+    m = -(-N // C)
+    while True:
+        sizes.append((m, span))
+        if m == 1:
+            break
+        m, span = -(-m // 2), span * 2
+    L = len(sizes)
+    logits = np.zeros(N, np.float64)
+    lse = np.zeros(N, np.float64)
+    surv = np.ones(N, np.int64)
+    for l in range(L, 0, -1):
+        M, sp = sizes[l - 1]
+        elig = np.minimum(M, t // sp + 1)
+        cand = np.ones(N, np.int64) if l == L else np.minimum(2 * surv, elig)
+        scored = cand > topk
+        if l >= 2:
+            # candidates have two children except the frontier one when its right child is ineligible
+            child_elig = np.minimum(sizes[l - 2][0], t // sizes[l - 2][1] + 1)
+            n_children = np.minimum(2 * cand, child_elig)
+            logits += np.where(scored, n_children, 0) * GQ
+        else:
+            keys = np.minimum(cand * C, t + 1)
+            logits += np.where(scored, keys, 0) * GQ
+        lse += np.where(scored, cand, 0) * GQ
+        surv = np.where(scored, topk, cand)
+    return float(logits.sum() * Hkv), float(lse.sum() * Hkv)
+
+
+def roofline_peaks():
+    path = os.path.join(PROFILES, "device_peaks.json")
+    if os.path.exists(path):
+        with open(path) as f:
+            return json.load(f)
+    return None
+
+
+def measured_traffic(kernel_key: str, src_hash: str):
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tab = json.load(f)
+    ent = tab.get(kernel_key)
+    if not ent or ent.get("source_hash") != src_hash:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, topk: int, n_positions: int, seed: int = 1):
+    """The fp64 oracle on the host cores, on a seeded sample of query positions."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    env_t = os.environ.get("OMP_NUM_THREADS")
+    if env_t and env_t.isdigit():
+        threads = min(threads, int(env_t))
+    N = inp.q.shape[1]
+    rng = np.random.default_rng(seed)
+    ts = np.sort(rng.choice(N, size=min(n_positions, N), replace=False)).astype(np.int64)
+    k0 = inp.k[0]
+    q_rows = np.ascontiguousarray(inp.q[0, ts])
+    t0 = time.perf_counter()
+    pyr = oracle.build_pyramid(k0, nthreads=threads)
+    t1 = time.perf_counter()
+    oracle.walk(q_rows, ts, k0, pyr, topk, nthreads=threads)
+    t2 = time.perf_counter()
+    build_s, walk_s = t1 - t0, t2 - t1
+    per_query = walk_s / len(ts) + build_s / N
+    return {"value": 1.0 / per_query, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": (f"full fp64 pyramid build over N={N} keys ({build_s:.2f} s) plus walks for "
+                       f"{len(ts)} seeded random query positions x {inp.k.shape[2]} KV heads "
+                       f"({walk_s:.2f} s); queries/s = 1/(walk_s/positions + build_s/N)")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long256k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--cpu-positions", type=int, default=8192)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the selection shards by KV head or query range with no exchange, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_selection_amd import ops, synth
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.WORKLOADS[args.workload]
+
+    def setup(wl, N=None):
+        t0 = time.perf_counter()
+        inp = synth.make_prefill(wl, N=N)
+        N = inp.q.shape[1]
+        dims = ops.make_dims(wl.B, wl.Hq, wl.Hkv, wl.topk, wl.dtype)
+        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+        def dev_t(x):
+            if wl.dtype == "bf16":
+                return torch.from_numpy(synth.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(x).to(dev)
+        q, k = dev_t(inp.q), dev_t(inp.k)
+        assert q.dtype == tdt
+        pyr = ops.alloc_pyramid(dims, N, dev)
+        out = torch.empty((wl.B, N, wl.Hkv, wl.topk), dtype=torch.int32, device=dev)
+        ws = ops.alloc_workspace(dims, N, False, dev)
+        log(f"inputs {wl.name} N={N} ready in {time.perf_counter() - t0:.1f} s")
+        return inp, N, dims, q, k, pyr, out, ws
+
+    def time_steps(N, dims, q, k, pyr, out, ws, steps, warmup):
+        stream = torch.cuda.current_stream()
+        for _ in range(warmup):
+            ops.build_pyramid(k, N, N, dims, pyr)
+            ops.select_prefill(q, k, pyr, N, N, dims, out, ws)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for i in range(steps):
+            ev[i][0].record(stream)
+            ops.build_pyramid(k, N, N, dims, pyr)
+            ev[i][1].record(stream)
+            ops.select_prefill(q, k, pyr, N, N, dims, out, ws)
+            ev[i][2].record(stream)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        total_ms = t_start.elapsed_time(t_end)
+        build = np.array([e[0].elapsed_time(e[1]) for e in ev])
+        walk = np.array([e[1].elapsed_time(e[2]) for e in ev])
+        return total_ms, build, walk
+
+    inp, N, dims, q, k, pyr, out, ws = setup(wl)
+    total_ms, build_ms, walk_ms = time_steps(N, dims, q, k, pyr, out, ws, args.steps, args.warmup)
+    ms_per_step = total_ms / args.steps
+    value = wl.B * N / (ms_per_step / 1e3)
+    log(f"N={N}: {ms_per_step:.3f} ms/step (build {build_ms.mean():.3f} ms, walk {walk_ms.mean():.3f} ms)")
+
+    GQ = wl.Hq // wl.Hkv
+    logits, lse_terms = walk_counts(N, wl.topk, GQ, wl.Hkv)
+    transc = logits + lse_terms               # one exp per logit, one log per LSE term
+    walk_s = walk_ms.mean() / 1e3
+    peaks = roofline_peaks()
+    src_hash = _hash_sources(["select.hip", "pisa_device.h"])
+    traffic = measured_traffic(f"walk_kernel:{wl.name}", src_hash)
+    exp_peak = peaks["transcendental_per_s"] if peaks else None
+    achieved = transc / walk_s
+    roofline = {
+        "kernel": "walk_kernel (coarse-to-fine walk, all levels)",
+        "bound": "alu",
+        "achieved": achieved / 1e9,
+        "peak": exp_peak / 1e9 if exp_peak else None,
+        "unit": "G transcendental/s (one exp per logit + one log per LSE term)",
+        "frac": (achieved / exp_peak) if exp_peak else None,
+        "traffic": traffic,
+        "algorithmic_transcendentals_per_launch": transc,
+        "algorithmic_logits_per_launch": logits,
+        "launch_ms": walk_ms.mean(),
+    }
+    # the pyramid build is HBM-bound: compulsory bytes = keys read once + every node written once
+    elt = 2 if wl.dtype == "bf16" else 4
+    build_bytes = wl.B * N * wl.Hkv * wl.d * elt + wl.B * wl.Hkv * ops.pyramid_nodes(dims, N) * wl.d * 4
+    # compulsory HBM bytes of the walk: Q read once, K read once, indices written once
+    walk_bytes = wl.B * N * (wl.Hq * wl.d * elt + wl.Hkv * wl.d * elt + wl.Hkv * wl.topk * 4)
+    hbm = {
+        "build_ms": build_ms.mean(),
+        "build_compulsory_GBs": build_bytes / (build_ms.mean() / 1e3) / 1e9,
+        "build_frac_of_8TBs": build_bytes / (build_ms.mean() / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "walk_compulsory_GBs": walk_bytes / walk_s / 1e9,
+        "walk_compulsory_frac_of_8TBs": walk_bytes / walk_s / 1e9 / HBM_PEAK_GBS,
+    }
+    if traffic:
+        hbm["walk_measured_GBs"] = traffic / walk_s / 1e9
+        hbm["walk_measured_frac_of_8TBs"] = traffic / walk_s / 1e9 / HBM_PEAK_GBS
+
+    result = {
+        "metric": "Top-K selection latency (ms) + queries/s at N=64K-256K, Hq=32 Hkv=2 d=64",
+        "value": value,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic: seeded N(0,1) Q/K rounded to bf16 (numpy default_rng(0))",
+        "config": {"workload": f"prefill selection {wl.name}", "B": wl.B, "N": N, "Hq": wl.Hq,
+                   "Hkv": wl.Hkv, "d": wl.d, "C": wl.C, "g": wl.g, "K": wl.topk,
+                   "step": "pisa_build_pyramid + pisa_select_prefill"},
+        "latency_ms": {"mean": ms_per_step, "median_build_plus_walk": float(np.median(build_ms + walk_ms)),
+                       "min_build_plus_walk": float(np.min(build_ms + walk_ms))},
+        "roofline": roofline,
+        "hbm": hbm,
+    }
+    del q, k, pyr, out, ws
+
+    if not args.no_extras:
+        sweep = {}
+        for name in ("long64k", "long128k"):
+            if name == args.workload:
+                continue
+            w2 = synth.WORKLOADS[name]
+            _, N2, d2, q2, k2, p2, o2, ws2 = setup(w2)
+            tot2, b2, wk2 = time_steps(N2, d2, q2, k2, p2, o2, ws2, 10, 3)
+            sweep[name] = {"N": N2, "ms": tot2 / 10, "queries_per_s": N2 / (tot2 / 10 / 1e3),
+                           "build_ms": float(b2.mean()), "walk_ms": float(wk2.mean())}
+            del q2, k2, p2, o2, ws2
+        result["sweep"] = sweep
+        result["decode"] = decode_bench(torch, ops, synth, dev, log)
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(inp, wl.topk, args.cpu_positions)
+    print(json.dumps(result), flush=True)
+
+
+def decode_bench(torch, ops, synth, dev, log):
+    """Decode workload: 131072 prebuilt keys, then 256 sequential refresh+select steps (K=32)."""
+    wl = synth.WORKLOADS["decode128k"]
+    inp = synth.make_decode(wl)
+    N0, steps = wl.N, wl.decode_steps
+    cap = N0 + steps
+    dims = ops.make_dims(1, wl.Hq, wl.Hkv, wl.topk, "bf16")
+
+    def dev_t(x):
+        return torch.from_numpy(synth.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    kc = np.zeros((1, cap, wl.Hkv, wl.d), np.float32)
+    kc[0, :N0] = inp.k_ctx[0]
+    k_cache = dev_t(kc)
+    k_new, q_new = dev_t(inp.k_new), dev_t(inp.q_new)
+    pyr = ops.alloc_pyramid(dims, cap, dev)
+    out = torch.empty((1, wl.Hkv, wl.topk), dtype=torch.int32, device=dev)
+    ws = ops.alloc_workspace(dims, cap, True, dev)
+    kn = [k_new[s].contiguous() for s in range(steps)]
+    qn = [q_new[s].contiguous() for s in range(steps)]
+    stream = torch.cuda.current_stream()
+    times = []
+    for rep in range(3):   # first repetition is warm-up
+        ops.build_pyramid(k_cache, N0, cap, dims, pyr)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for s in range(steps):
+            ops.decode_update_select(qn[s], kn[s], k_cache, pyr, N0 + s, cap, dims, out, ws)
+            ev[s + 1].record(stream)
+        torch.cuda.synchronize()
+        if rep:
+            times.append([ev[s].elapsed_time(ev[s + 1]) * 1e3 for s in range(steps)])
+    per = np.array(times)
+    res = {"context": N0, "steps": steps, "K": wl.topk, "us_per_step_mean": float(per.mean()),
+           "us_per_step_median": float(np.median(per)), "us_per_step_p90": float(np.percentile(per, 90)),
+           "steps_per_s": 1e6 / float(per.mean())}
+    log(f"decode: {res['us_per_step_mean']:.1f} us/step")
+    return res
+
+
+if __name__ == "__main__":
+    main()

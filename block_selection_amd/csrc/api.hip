@@ -1,0 +1,194 @@
+// api.hip -- the C ABI of libpisa.so (declared in include/pisa.h).
+//
+// Host side only: validates arguments, derives the pyramid geometry and
+// enqueues the kernels on the caller's stream. No allocation, no
+// synchronisation, no global state.
+#include <limits.h>
+#include <string.h>
+
+#include "pisa.h"
+#include "pisa_device.h"
+
+namespace pisa {
+
+template <typename KT>
+__global__ void build_subtree_kernel(const KT*, Geom, float*);
+__global__ void build_upper_kernel(Geom, float*);
+template <typename KT>
+__global__ void decode_refresh_kernel(const KT*, KT*, Geom, float*);
+template <typename KT>
+__global__ void walk_kernel(const KT*, const KT*, const float*, Geom, int64_t, int64_t, int32_t*);
+
+// Level sizes for n keys: M[1] = ceil(n/64), M[l+1] = ceil(M[l]/2) until 1. Returns L.
+static int level_sizes(int64_t n, int64_t M[kMaxLevels + 1]) {
+    int64_t m = (n + kC - 1) / kC;
+    int l = 1;
+    for (;;) {
+        M[l] = m;
+        if (m == 1 || l == kMaxLevels) break;
+        m = (m + 1) / 2;
+        ++l;
+    }
+    return l;
+}
+
+static int check_dims(const pisa_dims* d) {
+    if (!d) return PISA_ERR_INVALID_ARG;
+    if (d->B < 1 || d->Hq < 1 || d->Hkv < 1 || d->topk < 1) return PISA_ERR_INVALID_ARG;
+    if (d->Hq % d->Hkv != 0) return PISA_ERR_INVALID_ARG;
+    if (d->dtype != PISA_DTYPE_F32 && d->dtype != PISA_DTYPE_BF16) return PISA_ERR_INVALID_ARG;
+    if (d->d != kD || d->C != kC || d->g != 2) return PISA_ERR_UNSUPPORTED;
+    if (d->Hq / d->Hkv > kMaxGroup || d->topk > kMaxTopK) return PISA_ERR_UNSUPPORTED;
+    return PISA_OK;
+}
+
+// Geometry for n keys inside a layout sized for cap keys.
+static int make_geom(const pisa_dims* d, int64_t n, int64_t cap, Geom* G) {
+    if (n < 1 || cap < 1) return PISA_ERR_INVALID_ARG;
+    if (n > cap) return PISA_ERR_CAPACITY;
+    if (cap > (int64_t)INT_MAX) return PISA_ERR_UNSUPPORTED;
+    memset(G, 0, sizeof(*G));
+    int64_t Mc[kMaxLevels + 1] = {0}, Mn[kMaxLevels + 1] = {0};
+    const int Lc = level_sizes(cap, Mc);
+    const int Ln = level_sizes(n, Mn);
+    int64_t off = 0;
+    for (int l = 1; l <= Lc; ++l) { G->off[l] = off; off += Mc[l]; }
+    G->P = off;
+    for (int l = 1; l <= Ln; ++l) G->M[l] = (int32_t)Mn[l];
+    G->L = Ln;
+    G->N = n;
+    G->cap = cap;
+    G->B = d->B; G->Hq = d->Hq; G->Hkv = d->Hkv; G->GQ = d->Hq / d->Hkv; G->topk = d->topk;
+    return PISA_OK;
+}
+
+static int launch_status() {
+    return (hipGetLastError() == hipSuccess) ? PISA_OK : PISA_ERR_HIP;
+}
+
+template <typename KT>
+static int build_impl(const KT* k, const Geom& G, float* pyr, hipStream_t s) {
+    const int nsub = (G.M[1] + 15) / 16;
+    const int64_t grid = (int64_t)G.B * G.Hkv * nsub;
+    if (grid > INT_MAX) return PISA_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(build_subtree_kernel<KT>, dim3((unsigned)grid), dim3(256), 0, s, k, G, pyr);
+    if (G.L > 5)
+        hipLaunchKernelGGL(build_upper_kernel, dim3((unsigned)(G.B * G.Hkv)), dim3(256), 0, s, G, pyr);
+    return launch_status();
+}
+
+template <typename KT>
+static int walk_impl(const KT* q, const KT* k, const float* pyr, const Geom& G, int64_t t0,
+                     int64_t NT, int32_t* out, hipStream_t s) {
+    const int64_t walks = (int64_t)G.B * NT * G.Hkv;
+    int64_t grid = (walks + 3) / 4;
+    if (grid > (1 << 22)) grid = 1 << 22;
+    hipLaunchKernelGGL(walk_kernel<KT>, dim3((unsigned)grid), dim3(256), 0, s, q, k, pyr, G, t0, NT,
+                       out);
+    return launch_status();
+}
+
+}  // namespace pisa
+
+using namespace pisa;
+
+extern "C" {
+
+int64_t pisa_pyramid_nodes(const pisa_dims* dims, int64_t n_capacity) {
+    if (check_dims(dims) != PISA_OK || n_capacity < 1) return -1;
+    int64_t M[kMaxLevels + 1] = {0};
+    const int L = level_sizes(n_capacity, M);
+    int64_t tot = 0;
+    for (int l = 1; l <= L; ++l) tot += M[l];
+    return tot;
+}
+
+int64_t pisa_level_offset(const pisa_dims* dims, int64_t n_capacity, int32_t level) {
+    if (check_dims(dims) != PISA_OK || n_capacity < 1) return -1;
+    int64_t M[kMaxLevels + 1] = {0};
+    const int L = level_sizes(n_capacity, M);
+    if (level < 1 || level > L) return -1;
+    int64_t off = 0;
+    for (int l = 1; l < level; ++l) off += M[l];
+    return off;
+}
+
+size_t pisa_pyramid_bytes(const pisa_dims* dims, int64_t n_capacity) {
+    const int64_t nodes = pisa_pyramid_nodes(dims, n_capacity);
+    if (nodes < 0) return 0;
+    return (size_t)dims->B * (size_t)dims->Hkv * (size_t)nodes * kD * sizeof(float);
+}
+
+size_t pisa_workspace_bytes(const pisa_dims* dims, int64_t N, int32_t is_decode) {
+    (void)dims; (void)N; (void)is_decode;
+    return 0;
+}
+
+int pisa_build_pyramid(const void* k, int64_t N, int64_t n_capacity, const pisa_dims* dims,
+                       float* pyramid, void* stream) {
+    int rc = check_dims(dims);
+    if (rc != PISA_OK) return rc;
+    if (!k || !pyramid) return PISA_ERR_INVALID_ARG;
+    Geom G;
+    if ((rc = make_geom(dims, N, n_capacity, &G)) != PISA_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    if (dims->dtype == PISA_DTYPE_BF16) return build_impl((const uint16_t*)k, G, pyramid, s);
+    return build_impl((const float*)k, G, pyramid, s);
+}
+
+int pisa_select_prefill(const void* q, const void* k, const float* pyramid, int64_t N,
+                        int64_t n_capacity, const pisa_dims* dims, int32_t* out_idx,
+                        void* workspace, size_t ws_bytes, void* stream) {
+    int rc = check_dims(dims);
+    if (rc != PISA_OK) return rc;
+    if (!q || !k || !pyramid || !out_idx) return PISA_ERR_INVALID_ARG;
+    Geom G;
+    if ((rc = make_geom(dims, N, n_capacity, &G)) != PISA_OK) return rc;
+    if (ws_bytes < pisa_workspace_bytes(dims, N, 0) || (!workspace && pisa_workspace_bytes(dims, N, 0)))
+        return PISA_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    if (dims->dtype == PISA_DTYPE_BF16)
+        return walk_impl((const uint16_t*)q, (const uint16_t*)k, pyramid, G, 0, N, out_idx, s);
+    return walk_impl((const float*)q, (const float*)k, pyramid, G, 0, N, out_idx, s);
+}
+
+int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cache, float* pyramid,
+                              int64_t n_before, int64_t n_capacity, const pisa_dims* dims,
+                              int32_t* out_idx, void* workspace, size_t ws_bytes, void* stream) {
+    int rc = check_dims(dims);
+    if (rc != PISA_OK) return rc;
+    if (!q_new || !k_new || !k_cache || !pyramid || !out_idx) return PISA_ERR_INVALID_ARG;
+    if (n_before < 1) return PISA_ERR_INVALID_ARG;
+    Geom G;
+    if ((rc = make_geom(dims, n_before + 1, n_capacity, &G)) != PISA_OK) return rc;
+    if (ws_bytes < pisa_workspace_bytes(dims, n_capacity, 1) ||
+        (!workspace && pisa_workspace_bytes(dims, n_capacity, 1)))
+        return PISA_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    const unsigned nbh = (unsigned)(dims->B * dims->Hkv);
+    if (dims->dtype == PISA_DTYPE_BF16) {
+        hipLaunchKernelGGL(decode_refresh_kernel<uint16_t>, dim3(nbh), dim3(64), 0, s,
+                           (const uint16_t*)k_new, (uint16_t*)k_cache, G, pyramid);
+        if ((rc = launch_status()) != PISA_OK) return rc;
+        return walk_impl((const uint16_t*)q_new, (const uint16_t*)k_cache, pyramid, G, n_before, 1,
+                         out_idx, s);
+    }
+    hipLaunchKernelGGL(decode_refresh_kernel<float>, dim3(nbh), dim3(64), 0, s,
+                       (const float*)k_new, (float*)k_cache, G, pyramid);
+    if ((rc = launch_status()) != PISA_OK) return rc;
+    return walk_impl((const float*)q_new, (const float*)k_cache, pyramid, G, n_before, 1, out_idx, s);
+}
+
+const char* pisa_status_string(int status) {
+    switch (status) {
+        case PISA_OK: return "ok";
+        case PISA_ERR_INVALID_ARG: return "invalid argument";
+        case PISA_ERR_UNSUPPORTED: return "unsupported dimensions";
+        case PISA_ERR_WORKSPACE: return "workspace too small";
+        case PISA_ERR_CAPACITY: return "length exceeds capacity";
+        case PISA_ERR_HIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// pisa_device.h -- geometry and wavefront helpers shared by the gfx950 kernels.
+//
+// Pyramid geometry (reading note "Block Sparse Attention with Log-Linear
+// Complexity", section 3.1): level 1 holds ceil(N/64) leaf blocks of 64 raw
+// keys and every level above halves the node count (rounding up) until a
+// single root remains. Node i of level l >= 1 covers raw keys
+// [i * 64 * 2^(l-1), min((i+1) * 64 * 2^(l-1), N)).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pisa {
+
+constexpr int kD = 64;          // head dimension
+constexpr int kC = 64;          // raw keys per leaf block
+constexpr int kLog2C = 6;
+constexpr int kMaxLevels = 40;  // levels for up to 2^31 keys plus margin
+constexpr int kMaxTopK = 32;    // 2*topk candidate slots fit one 64-lane wavefront
+constexpr int kMaxGroup = 16;   // query heads per KV head: one 16-column MFMA tile
+
+// Geometry of one call, passed by value to kernels.
+struct Geom {
+    int64_t N;                    // keys present
+    int64_t cap;                  // key capacity (row stride of k per batch element)
+    int64_t P;                    // pyramid rows per (batch, KV head) in the capacity layout
+    int64_t off[kMaxLevels + 1];  // row offset of level l (capacity layout)
+    int32_t M[kMaxLevels + 1];    // nodes at level l for N keys
+    int32_t L;                    // root level for N keys
+    int32_t B, Hq, Hkv, GQ, topk;
+};
+
+// Raw keys covered by a full node of level l (l = 0: one key).
+__host__ __device__ inline int64_t span_of(int l) { return l == 0 ? 1 : (int64_t)kC << (l - 1); }
+
+// First raw key of node i at level l; a node is eligible for query t iff this is <= t.
+__host__ __device__ inline int64_t first_key(int l, int64_t i) { return i * span_of(l); }
+
+// Raw keys actually covered by node i of level l when n keys exist (0 if the node does not exist).
+__host__ __device__ inline int64_t covered(int l, int64_t i, int64_t n) {
+    const int64_t lo = first_key(l, i);
+    if (lo >= n) return 0;
+    const int64_t s = span_of(l);
+    return (n - lo < s) ? (n - lo) : s;
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Eight consecutive elements of a row as floats (bf16 or fp32 storage).
+__device__ inline void load8_f32(const uint16_t* p, float v[8]) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ inline void load8_f32(const float* p, float v[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+}
+
+__device__ inline float shfl_f(float v, int src) { return __shfl(v, src, 64); }
+__device__ inline int shfl_i(int v, int src) { return __shfl(v, src, 64); }
+__device__ inline float xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+__device__ inline float readlane_f(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+__device__ inline int readlane_i(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
+__device__ inline uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// Number of set bits of m below this lane.
+__device__ inline int lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Lane i sends v to lane dst_i (all lanes active; each destination written at most once).
+__device__ inline int push_to_lane(int dst, int v) { return __builtin_amdgcn_ds_permute(dst << 2, v); }
+
+// Count-weighted mean of two children with explicit roundings, so that the
+// full build and the decode refresh produce identical bits.
+__device__ inline float parent_mean(float a, float ca, float b, float cb) {
+    if (cb == 0.0f) return a;
+    return __fdiv_rn(__fmaf_rn(ca, a, __fmul_rn(cb, b)), ca + cb);
+}
+
+}  // namespace pisa

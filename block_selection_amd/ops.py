@@ -1,0 +1,167 @@
+"""Thin ctypes binding over libpisa.so (C ABI in include/pisa.h).
+
+Argument marshalling only: every step of the selection runs in the HIP
+kernels of libpisa.so. Tensors are PyTorch device tensors (ROCm), used for
+their memory and streams; the calls enqueue on the current torch stream
+unless a stream is given. If the library is missing this module raises at
+import time: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpisa.so")
+
+PISA_OK = 0
+PISA_ERR_INVALID_ARG = -1
+PISA_ERR_UNSUPPORTED = -2
+PISA_ERR_WORKSPACE = -3
+PISA_ERR_CAPACITY = -4
+PISA_ERR_HIP = -5
+PISA_DTYPE_F32 = 0
+PISA_DTYPE_BF16 = 1
+
+EXPORTED = ("pisa_pyramid_nodes", "pisa_level_offset", "pisa_pyramid_bytes", "pisa_workspace_bytes",
+            "pisa_build_pyramid", "pisa_select_prefill", "pisa_decode_update_select",
+            "pisa_status_string")
+
+
+class Dims(ctypes.Structure):
+    """Mirror of pisa_dims."""
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("C", ctypes.c_int32), ("g", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == PISA_DTYPE_BF16 else torch.float32
+
+
+class PisaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({status_string(status)})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libpisa.so not built ({LIB_PATH}); run `python -m block_selection_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    D = ctypes.POINTER(Dims)
+    lib.pisa_pyramid_nodes.argtypes = [D, i64]
+    lib.pisa_pyramid_nodes.restype = i64
+    lib.pisa_level_offset.argtypes = [D, i64, i32]
+    lib.pisa_level_offset.restype = i64
+    lib.pisa_pyramid_bytes.argtypes = [D, i64]
+    lib.pisa_pyramid_bytes.restype = sz
+    lib.pisa_workspace_bytes.argtypes = [D, i64, i32]
+    lib.pisa_workspace_bytes.restype = sz
+    lib.pisa_build_pyramid.argtypes = [P, i64, i64, D, P, P]
+    lib.pisa_build_pyramid.restype = ctypes.c_int
+    lib.pisa_select_prefill.argtypes = [P, P, P, i64, i64, D, P, P, sz, P]
+    lib.pisa_select_prefill.restype = ctypes.c_int
+    lib.pisa_decode_update_select.argtypes = [P, P, P, P, i64, i64, D, P, P, sz, P]
+    lib.pisa_decode_update_select.restype = ctypes.c_int
+    lib.pisa_status_string.argtypes = [ctypes.c_int]
+    lib.pisa_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.pisa_status_string(status).decode()
+
+
+def make_dims(B: int, Hq: int, Hkv: int, topk: int, dtype: str = "bf16", d: int = 64, C: int = 64,
+              g: int = 2) -> Dims:
+    dt = {"bf16": PISA_DTYPE_BF16, "f32": PISA_DTYPE_F32}[dtype]
+    return Dims(B, Hq, Hkv, d, C, g, topk, dt)
+
+
+def pyramid_nodes(dims: Dims, n_capacity: int) -> int:
+    return int(lib.pisa_pyramid_nodes(ctypes.byref(dims), n_capacity))
+
+
+def level_offset(dims: Dims, n_capacity: int, level: int) -> int:
+    return int(lib.pisa_level_offset(ctypes.byref(dims), n_capacity, level))
+
+
+def pyramid_bytes(dims: Dims, n_capacity: int) -> int:
+    return int(lib.pisa_pyramid_bytes(ctypes.byref(dims), n_capacity))
+
+
+def workspace_bytes(dims: Dims, N: int, is_decode: bool = False) -> int:
+    return int(lib.pisa_workspace_bytes(ctypes.byref(dims), N, int(bool(is_decode))))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, dtype, numel: int):
+    if not t.is_cuda or not t.is_contiguous() or t.dtype != dtype or t.numel() != numel:
+        raise ValueError(f"{name}: expected a contiguous device tensor of {numel} {dtype}, got "
+                         f"{tuple(t.shape)} {t.dtype} on {t.device}")
+
+
+def alloc_pyramid(dims: Dims, n_capacity: int, device="cuda") -> torch.Tensor:
+    return torch.empty((dims.B, dims.Hkv, pyramid_nodes(dims, n_capacity), dims.d),
+                       dtype=torch.float32, device=device)
+
+
+def alloc_workspace(dims: Dims, N: int, is_decode: bool = False, device="cuda") -> Optional[torch.Tensor]:
+    n = workspace_bytes(dims, N, is_decode)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def build_pyramid(k: torch.Tensor, N: int, n_capacity: int, dims: Dims, pyramid: torch.Tensor,
+                  stream=None) -> None:
+    _check(k, "k", dims.torch_dtype, dims.B * n_capacity * dims.Hkv * dims.d)
+    _check(pyramid, "pyramid", torch.float32, dims.B * dims.Hkv * pyramid_nodes(dims, n_capacity) * dims.d)
+    rc = lib.pisa_build_pyramid(_ptr(k), N, n_capacity, ctypes.byref(dims), _ptr(pyramid), _stream(stream))
+    if rc != PISA_OK:
+        raise PisaError("pisa_build_pyramid", rc)
+
+
+def select_prefill(q: torch.Tensor, k: torch.Tensor, pyramid: torch.Tensor, N: int, n_capacity: int,
+                   dims: Dims, out_idx: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                   stream=None) -> None:
+    _check(q, "q", dims.torch_dtype, dims.B * N * dims.Hq * dims.d)
+    _check(k, "k", dims.torch_dtype, dims.B * n_capacity * dims.Hkv * dims.d)
+    _check(pyramid, "pyramid", torch.float32, dims.B * dims.Hkv * pyramid_nodes(dims, n_capacity) * dims.d)
+    _check(out_idx, "out_idx", torch.int32, dims.B * N * dims.Hkv * dims.topk)
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.pisa_select_prefill(_ptr(q), _ptr(k), _ptr(pyramid), N, n_capacity, ctypes.byref(dims),
+                                 _ptr(out_idx), _ptr(workspace), ws_n, _stream(stream))
+    if rc != PISA_OK:
+        raise PisaError("pisa_select_prefill", rc)
+
+
+def decode_update_select(q_new: torch.Tensor, k_new: torch.Tensor, k_cache: torch.Tensor,
+                         pyramid: torch.Tensor, n_before: int, n_capacity: int, dims: Dims,
+                         out_idx: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                         stream=None) -> None:
+    _check(q_new, "q_new", dims.torch_dtype, dims.B * dims.Hq * dims.d)
+    _check(k_new, "k_new", dims.torch_dtype, dims.B * dims.Hkv * dims.d)
+    _check(k_cache, "k_cache", dims.torch_dtype, dims.B * n_capacity * dims.Hkv * dims.d)
+    _check(pyramid, "pyramid", torch.float32, dims.B * dims.Hkv * pyramid_nodes(dims, n_capacity) * dims.d)
+    _check(out_idx, "out_idx", torch.int32, dims.B * dims.Hkv * dims.topk)
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.pisa_decode_update_select(_ptr(q_new), _ptr(k_new), _ptr(k_cache), _ptr(pyramid), n_before,
+                                       n_capacity, ctypes.byref(dims), _ptr(out_idx), _ptr(workspace),
+                                       ws_n, _stream(stream))
+    if rc != PISA_OK:
+        raise PisaError("pisa_decode_update_select", rc)

@@ -1,0 +1,145 @@
+/*
+ * pisa.h -- C ABI of libpisa.so: pyramid Top-K block selection for
+ * block-sparse attention (the PISA selection stage) on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method (pages: "Block Sparse Attention with Log-Linear Complexity",
+ * qqtang-code reading note, sections 3.1, 3.2, "Scoring: LogSumExp" and 4.1;
+ * and the ai4snews summary "PISA cuts block-sparse attention selection to
+ * O(N log N) with pyramid Top-K", second paragraph):
+ *   - keys are mean-pooled into a pyramid: level 1 holds leaf blocks of C raw
+ *     keys, every level above merges g=2 adjacent nodes, up to one root;
+ *   - each query, per KV head, walks it from the root down: at every level
+ *     only the children of the previous level's survivors are candidates; if
+ *     there are at most K of them they all survive unscored, otherwise each is
+ *     scored by the LogSumExp of the query's logits against its children's
+ *     summaries (raw keys at the leaf level), summed over the query heads of
+ *     the GQA group, and the K best survive; the leaf survivors are the
+ *     selected key blocks;
+ *   - decoding keeps the pyramid and, per new token, refreshes only the new
+ *     token's leaf mean and the ancestors of that leaf before walking.
+ *
+ * Conventions fixed by this library where the pages are silent:
+ *   logit = q.k / sqrt(d); level sizes M_1 = ceil(N/C), M_{l+1} = ceil(M_l/g)
+ *   down to 1; a node that covers fewer raw keys than a full one (right edge)
+ *   summarises the mean of the raw keys it covers; a node is eligible for
+ *   query position t iff its first raw key index is <= t, and only eligible
+ *   children enter a parent's LSE (raw keys > t are masked at the leaves);
+ *   the at-most-K rule counts eligible candidates; query head h belongs to KV
+ *   head h / (Hq/Hkv); equal scores rank the lower node index first; each
+ *   output row lists the selected leaf indices in ascending order, padded
+ *   with -1.
+ *
+ * Supported shapes: d = 64, C = 64, g = 2, 1 <= Hq/Hkv <= 16, 1 <= topk <= 32.
+ * Other values return PISA_ERR_UNSUPPORTED before anything is launched.
+ *
+ * Memory: every pointer argument is DEVICE memory owned by the caller; the
+ * library allocates nothing, keeps no global state and never synchronises
+ * the stream. All work is enqueued asynchronously on `stream` (a hipStream_t;
+ * NULL means the null stream). Arguments are validated on the host before any
+ * launch; a launch failure returns PISA_ERR_HIP. Faults inside kernels
+ * surface at the caller's next synchronisation. Values are not checked
+ * (NaN/Inf inputs give unspecified indices).
+ */
+#ifndef PISA_H_
+#define PISA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PISA_OK = 0,
+    PISA_ERR_INVALID_ARG = -1,  /* null pointer, non-positive size, Hq % Hkv != 0, ... */
+    PISA_ERR_UNSUPPORTED = -2,  /* d, C, g, group size or topk outside the supported set */
+    PISA_ERR_WORKSPACE = -3,    /* workspace smaller than pisa_workspace_bytes() */
+    PISA_ERR_CAPACITY = -4,     /* N (or n_before + 1) exceeds n_capacity */
+    PISA_ERR_HIP = -5           /* a HIP launch reported an error */
+} pisa_status;
+
+typedef enum { PISA_DTYPE_F32 = 0, PISA_DTYPE_BF16 = 1 } pisa_dtype;
+
+/* Problem dimensions. dtype is the element type of q and k (both the same). */
+typedef struct {
+    int32_t B;      /* batch */
+    int32_t Hq;     /* query heads */
+    int32_t Hkv;    /* key heads; Hq % Hkv == 0, group size GQ = Hq / Hkv */
+    int32_t d;      /* head dimension (64) */
+    int32_t C;      /* raw keys per leaf block (64) */
+    int32_t g;      /* children per parent (2) */
+    int32_t topk;   /* K: blocks kept per level and selected per query */
+    int32_t dtype;  /* pisa_dtype of q and k */
+} pisa_dims;
+
+/* Rows (nodes) per (batch, KV head) of a pyramid laid out for n_capacity
+ * keys: sum over levels l >= 1 of M_l(n_capacity). Returns -1 on bad input. */
+int64_t pisa_pyramid_nodes(const pisa_dims* dims, int64_t n_capacity);
+
+/* Row offset of level l (1 = leaf blocks) inside one (batch, KV head) slab of
+ * that layout; -1 if l is outside 1..L(n_capacity). */
+int64_t pisa_level_offset(const pisa_dims* dims, int64_t n_capacity, int32_t level);
+
+/* Bytes of the fp32 pyramid: B * Hkv * pisa_pyramid_nodes() * d * 4. */
+size_t pisa_pyramid_bytes(const pisa_dims* dims, int64_t n_capacity);
+
+/* Device workspace that pisa_select_prefill (is_decode = 0, N = sequence
+ * length) or pisa_decode_update_select (is_decode = 1, N = n_capacity) needs.
+ * May be 0; then a NULL workspace is accepted. */
+size_t pisa_workspace_bytes(const pisa_dims* dims, int64_t N, int32_t is_decode);
+
+/*
+ * Builds the mean pyramid over keys 0..N-1 (reading note, section 3.1).
+ *   k        [B, n_capacity, Hkv, d] of dims->dtype, row-major; rows >= N unused.
+ *   pyramid  fp32 [B, Hkv, pisa_pyramid_nodes(n_capacity), d]; level l occupies
+ *            rows pisa_level_offset(l) .. + M_l(N) - 1 of each (batch, head)
+ *            slab; rows for nodes that do not exist at length N are not written.
+ * Each node holds the fp32 mean of the raw keys it covers (leaf sums in fp32,
+ * parents as count-weighted means of their children).
+ */
+int pisa_build_pyramid(const void* k, int64_t N, int64_t n_capacity, const pisa_dims* dims,
+                       float* pyramid, void* stream);
+
+/*
+ * Prefill selection for every query position t in 0..N-1 (reading note,
+ * sections 3.2, "Scoring: LogSumExp", 4.1).
+ *   q        [B, N, Hq, d] of dims->dtype.
+ *   k        [B, n_capacity, Hkv, d], the keys the pyramid was built from.
+ *   pyramid  as written by pisa_build_pyramid for the same N and n_capacity.
+ *   out_idx  int32 [B, N, Hkv, topk]: ascending leaf indices, -1 padded.
+ *   workspace at least pisa_workspace_bytes(dims, N, 0) bytes of device memory.
+ * Scores use fp32 arithmetic: bf16 (or fp32) q.k products accumulated in fp32,
+ * fp32 summaries, fp32 LogSumExp.
+ */
+int pisa_select_prefill(const void* q, const void* k, const float* pyramid, int64_t N,
+                        int64_t n_capacity, const pisa_dims* dims, int32_t* out_idx,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * One decoding step (ai4snews summary, second paragraph): appends k_new as key
+ * n_before, refreshes the pyramid along the new key's leaf and its ancestors
+ * only (nodes created by the new key included), then selects for the query
+ * q_new at position t = n_before over n_before + 1 keys.
+ *   q_new    [B, Hq, d]; k_new [B, Hkv, d] (dims->dtype).
+ *   k_cache  [B, n_capacity, Hkv, d]; row n_before is written.
+ *   pyramid  the pyramid of keys 0..n_before-1 (n_before >= 1) in the
+ *            n_capacity layout; updated in place to cover n_before + 1 keys.
+ *   out_idx  int32 [B, Hkv, topk]: ascending leaf indices, -1 padded.
+ * The refreshed nodes are bitwise equal to what pisa_build_pyramid writes for
+ * n_before + 1 keys. Steps on one pyramid must be enqueued in order.
+ */
+int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cache,
+                              float* pyramid, int64_t n_before, int64_t n_capacity,
+                              const pisa_dims* dims, int32_t* out_idx, void* workspace,
+                              size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* pisa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PISA_H_ */

@@ -1,0 +1,157 @@
+"""Shared helpers for the GPU parity tests: seeded inputs on the device, the
+HIP path through the C ABI, and the parity rule against the fp64 oracle.
+
+Parity rule (selection): for every (position t, KV head) the GPU's index set
+must equal the oracle's, except when the oracle's walk had a near-tie, i.e.
+its K-th and (K+1)-th scores differed by less than NEAR_TIE at some scored
+level. Such walks are counted; a mismatching one must also be reachable by
+resolving the near-ties within NEAR_TIE (oracle.validate) and must never be
+unreachable. Pyramid rule: per node, ||gpu - ref||_2 <= 1e-5 ||ref||_2 and
+max|gpu - ref| <= 1e-5 max|ref|.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+import oracle
+from block_selection_amd import synth
+
+NEAR_TIE = 1e-3
+PYR_RTOL = 1e-5
+
+
+def to_device(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """float32 array (bf16-exact values for bf16) -> contiguous device tensor."""
+    if dtype == "bf16":
+        bits = synth.bf16_bits(x)
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+
+@dataclasses.dataclass
+class GpuPrefill:
+    pyramid: np.ndarray    # [B, Hkv, P, d] fp32 (capacity layout)
+    idx: np.ndarray        # [B, N, Hkv, K] int32
+    dims: object
+    cap: int
+
+
+def run_prefill(q: np.ndarray, k: np.ndarray, topk: int, dtype: str, cap: int | None = None,
+                device="cuda") -> GpuPrefill:
+    from block_selection_amd import ops
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    cap = N if cap is None else cap
+    dims = ops.make_dims(B, Hq, Hkv, topk, dtype)
+    kk = np.zeros((B, cap, Hkv, d), np.float32)
+    kk[:, :N] = k
+    qt, kt = to_device(q, dtype, device), to_device(kk, dtype, device)
+    pyr = ops.alloc_pyramid(dims, cap, device)
+    pyr.fill_(float("nan"))
+    out = torch.full((B, N, Hkv, topk), -7, dtype=torch.int32, device=device)
+    ws = ops.alloc_workspace(dims, N, False, device)
+    ops.build_pyramid(kt, N, cap, dims, pyr)
+    ops.select_prefill(qt, kt, pyr, N, cap, dims, out, ws)
+    torch.cuda.synchronize()
+    return GpuPrefill(pyr.cpu().numpy(), out.cpu().numpy(), dims, cap)
+
+
+def pyramid_levels(pyr_bh: np.ndarray, N: int, cap: int):
+    """Split one (batch, head) capacity-layout slab into per-level arrays for N keys."""
+    sizes = oracle.level_sizes(N)
+    cap_offs = oracle.level_offsets(cap)
+    return [pyr_bh[cap_offs[l]:cap_offs[l] + m] for l, m in enumerate(sizes)]
+
+
+def check_pyramid(gpu_pyr: np.ndarray, ref_pyr: np.ndarray, N: int, cap: int) -> float:
+    """gpu_pyr [B, Hkv, P, d] vs oracle ref [Hkv, total, d] (B = 1). Returns the worst ratio."""
+    sizes = oracle.level_sizes(N)
+    ref_offs = oracle.level_offsets(N)
+    worst = 0.0
+    for j in range(ref_pyr.shape[0]):
+        got_levels = pyramid_levels(gpu_pyr[0, j], N, cap)
+        for l, m in enumerate(sizes):
+            ref = ref_pyr[j, ref_offs[l]:ref_offs[l] + m]
+            got = got_levels[l].astype(np.float64)
+            assert np.all(np.isfinite(got)), f"non-finite pyramid values at level {l + 1}"
+            diff = got - ref
+            n2 = np.linalg.norm(diff, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+            ninf = np.abs(diff).max(axis=1) / np.maximum(np.abs(ref).max(axis=1), 1e-30)
+            worst = max(worst, float(n2.max()), float(ninf.max()))
+            bad = np.nonzero((n2 > PYR_RTOL) | (ninf > PYR_RTOL))[0]
+            assert bad.size == 0, (f"head {j} level {l + 1}: {bad.size} nodes beyond tolerance, "
+                                   f"worst {max(n2.max(), ninf.max()):.3e} at node {bad[0]}")
+    return worst
+
+
+@dataclasses.dataclass
+class ParityReport:
+    walks: int = 0
+    exact: int = 0
+    near_tie_walks: int = 0
+    mismatch_near_tie: int = 0
+    mismatch_valid: int = 0
+    mismatch_invalid: int = 0
+    mismatch_unverified: int = 0
+    hard_fail: int = 0
+    first_fail: tuple = ()
+
+    def ok(self) -> bool:
+        return self.hard_fail == 0 and self.mismatch_invalid == 0
+
+    def __str__(self):
+        return (f"walks={self.walks} exact={self.exact} near_tie_walks={self.near_tie_walks} "
+                f"mismatch(near-tie)={self.mismatch_near_tie} valid={self.mismatch_valid} "
+                f"invalid={self.mismatch_invalid} unverified={self.mismatch_unverified} "
+                f"hard_fail={self.hard_fail} first_fail={self.first_fail}")
+
+
+def compare_selection(gpu_idx: np.ndarray, ts: np.ndarray, q: np.ndarray, k: np.ndarray,
+                      ref_pyr: np.ndarray, topk: int, validate_budget: int = 200000,
+                      ora=None) -> ParityReport:
+    """gpu_idx [len(ts), Hkv, K] for positions ts (B = 1); q [N, Hq, d]; k [N, Hkv, d]."""
+    if ora is None:
+        ora = oracle.walk(q[ts], ts, k, ref_pyr, topk)
+    o_idx, o_gap, _ = ora
+    rep = ParityReport()
+    Hkv = k.shape[1]
+    for i, t in enumerate(ts):
+        for j in range(Hkv):
+            rep.walks += 1
+            near = o_gap[i, j] < NEAR_TIE
+            rep.near_tie_walks += int(near)
+            if np.array_equal(gpu_idx[i, j], o_idx[i, j]):
+                rep.exact += 1
+                continue
+            if not near:
+                rep.hard_fail += 1
+                if not rep.first_fail:
+                    rep.first_fail = (int(t), j, gpu_idx[i, j].tolist(), o_idx[i, j].tolist(),
+                                      float(o_gap[i, j]))
+                continue
+            rep.mismatch_near_tie += 1
+            v = oracle.validate(q[t], int(t), j, k, ref_pyr, topk, gpu_idx[i, j], NEAR_TIE,
+                                validate_budget)
+            if v == 1:
+                rep.mismatch_valid += 1
+            elif v == 0:
+                rep.mismatch_invalid += 1
+                if not rep.first_fail:
+                    rep.first_fail = (int(t), j, gpu_idx[i, j].tolist(), o_idx[i, j].tolist(),
+                                      float(o_gap[i, j]), "invalid")
+            else:
+                rep.mismatch_unverified += 1
+    return rep
+
+
+def sample_positions(N: int, n: int, topk: int, seed: int = 0) -> np.ndarray:
+    """Edge positions (first, block boundaries, the at-most-K region, last) plus random ones."""
+    rng = np.random.default_rng(seed)
+    edges = {0, 1, 63, 64, 65, topk * 64 - 1, topk * 64, 2 * topk * 64, N // 2 - 1, N // 2,
+             N - 65, N - 64, N - 2, N - 1}
+    edges = {t for t in edges if 0 <= t < N}
+    rest = rng.choice(N, size=min(n, N), replace=False)
+    return np.array(sorted(edges | set(rest.tolist())), dtype=np.int64)

@@ -1,0 +1,217 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Pyramids are compared node by node, selections walk by walk under the rule in
+pisa_testlib (bit-exact index sets; near-ties counted and validated). Small
+workloads are compared at every query position; the long ones at sampled
+positions (block edges, the at-most-K region, the last rows, plus seeded
+random rows), in the same launch configuration the benchmark times.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_selection_amd import synth
+from pisa_testlib import (check_pyramid, compare_selection, pyramid_levels, run_prefill,
+                          sample_positions, to_device)
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _log(name, rep, extra=None):
+    line = {"test": name, **{k: v for k, v in rep.__dict__.items() if k != "first_fail"}}
+    if extra:
+        line.update(extra)
+    print(json.dumps(line), flush=True)
+    path = os.environ.get("PISA_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(line) + "\n")
+
+
+def _prefill_case(wl, n_sample=None, N=None, cap=None):
+    inp = synth.make_prefill(wl, N=N)
+    N = inp.q.shape[1]
+    print(f"[case] {wl.name} N={N} Hq={wl.Hq} Hkv={wl.Hkv} K={wl.topk} dtype={wl.dtype} cap={cap}",
+          flush=True)
+    gpu = run_prefill(inp.q, inp.k, wl.topk, wl.dtype, cap=cap)
+    k0 = inp.k[0]
+    ref_pyr = oracle.build_pyramid(k0)
+    worst = check_pyramid(gpu.pyramid, ref_pyr, N, gpu.cap)
+    ts = np.arange(N) if n_sample is None else sample_positions(N, n_sample, wl.topk)
+    rep = compare_selection(gpu.idx[0, ts], ts, inp.q[0], k0, ref_pyr, wl.topk)
+    _log(f"prefill_{wl.name}_N{N}", rep, {"pyramid_worst_rel": worst, "positions": int(len(ts))})
+    assert rep.ok(), str(rep)
+    return inp, gpu, rep
+
+
+def test_prefill_tiny_all_positions():
+    _prefill_case(synth.WORKLOADS["tiny"])
+
+
+def test_prefill_short_all_positions():
+    _prefill_case(synth.WORKLOADS["short"])
+
+
+def test_prefill_mid_planted_sampled():
+    wl = synth.WORKLOADS["mid_planted"]
+    inp, gpu, rep = _prefill_case(wl, n_sample=3000)
+
+
+@pytest.mark.parametrize("name", ["long64k", "long128k", "long256k"])
+def test_prefill_long_sampled(name):
+    _prefill_case(synth.WORKLOADS[name], n_sample=1200)
+
+
+@pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 1000, 4001])
+def test_prefill_ragged_lengths(N):
+    wl = synth.Workload("ragged", N=N, Hq=32, Hkv=2, topk=8, dtype="bf16", seed=N)
+    _prefill_case(wl)
+
+
+@pytest.mark.parametrize("Hq,Hkv,K,dtype", [(8, 1, 32, "bf16"), (16, 2, 1, "bf16"), (6, 3, 5, "f32"),
+                                             (16, 1, 16, "bf16"), (2, 2, 8, "f32")])
+def test_prefill_shape_variants(Hq, Hkv, K, dtype):
+    wl = synth.Workload("variant", N=8192, Hq=Hq, Hkv=Hkv, topk=K, dtype=dtype, seed=Hq * 100 + K)
+    _prefill_case(wl, n_sample=1500)
+
+
+def test_prefill_capacity_layout():
+    """A pyramid laid out for more keys than present (as decoding uses) selects the same."""
+    wl = synth.Workload("cap", N=5000, Hq=32, Hkv=2, topk=8, dtype="bf16", seed=5)
+    _prefill_case(wl, n_sample=800, cap=9000)
+
+
+def test_closed_form_walk_on_gpu():
+    """Hand-derived selections (tests/golden/closed_form_walk.json), including an exact tie."""
+    with open(os.path.join(GOLDEN, "closed_form_walk.json")) as f:
+        fx = json.load(f)
+    N, C, d = fx["N"], fx["C"], fx["d"]
+    k = np.zeros((1, N, 1, d), np.float32)
+    for b, c in enumerate(fx["leaf_logit"]):
+        k[0, b * C:(b + 1) * C, 0, 0] = c
+    q = np.zeros((1, N, 1, d), np.float32)
+    q[0, :, 0, 0] = fx["q_first_coord"]
+    for dtype in ("f32", "bf16"):
+        gpu = run_prefill(q, k, fx["topk"], dtype)
+        for case in fx["cases"]:
+            assert gpu.idx[0, case["t"], 0].tolist() == case["expect"], (dtype, case["t"])
+
+
+def test_zero_keys_ties_lowest_index():
+    """All logits 0: full blocks tie exactly; the lowest eligible indices must win, bit-exact."""
+    N, K = 8192, 8
+    rng = np.random.default_rng(4)
+    q = synth.bf16_round(rng.standard_normal((1, N, 32, 64), dtype=np.float32))
+    k = np.zeros((1, N, 2, 64), np.float32)
+    gpu = run_prefill(q, k, K, "bf16")
+    n_elig = np.arange(N) // 64 + 1
+    want = np.full((N, K), -1, np.int32)
+    for t in range(N):
+        m = min(K, n_elig[t])
+        want[t, :m] = np.arange(m)
+    for j in range(2):
+        assert np.array_equal(gpu.idx[0, :, j], want)
+
+
+def test_prefill_deterministic():
+    wl = synth.WORKLOADS["short"]
+    inp = synth.make_prefill(wl)
+    a = run_prefill(inp.q, inp.k, wl.topk, wl.dtype)
+    b = run_prefill(inp.q, inp.k, wl.topk, wl.dtype)
+    assert np.array_equal(a.idx, b.idx)
+    assert np.array_equal(a.pyramid.view(np.uint32), b.pyramid.view(np.uint32))
+
+
+def test_planted_recall_matches_oracle():
+    """Planted blocks: the GPU's recall over the sampled positions equals the oracle's."""
+    wl = synth.WORKLOADS["mid_planted"]
+    inp = synth.make_prefill(wl)
+    gpu = run_prefill(inp.q, inp.k, wl.topk, wl.dtype)
+    k0 = inp.k[0]
+    ref_pyr = oracle.build_pyramid(k0)
+    ts = sample_positions(wl.N, 1500, wl.topk, seed=9)
+    ts = ts[ts >= wl.topk * 64]
+    o_idx, _, _ = oracle.walk(inp.q[0, ts], ts, k0, ref_pyr, wl.topk)
+    planted = set(inp.planted.tolist())
+
+    def recall(idx):
+        vals = []
+        for i, t in enumerate(ts):
+            elig = {b for b in planted if b * 64 <= t}
+            if not elig:
+                continue
+            for j in range(2):
+                sel = set(idx[i, j].tolist())
+                vals.append(len(sel & elig) / min(wl.topk, len(elig)))
+        return float(np.mean(vals))
+
+    r_gpu, r_ora = recall(gpu.idx[0, ts]), recall(o_idx)
+    print(json.dumps({"planted_recall_gpu": r_gpu, "planted_recall_oracle": r_ora}), flush=True)
+    assert abs(r_gpu - r_ora) < 0.01
+
+
+# ------------------------------------------------------------------ decode ---
+
+def _decode_run(N0, steps, check_every=1, oracle_every=1):
+    from block_selection_amd import ops
+    wl = synth.Workload("decode", N=N0, Hq=32, Hkv=2, topk=32, dtype="bf16", decode_steps=steps)
+    inp = synth.make_decode(wl)
+    cap = N0 + steps
+    dims = ops.make_dims(1, 32, 2, 32, "bf16")
+    k_all = np.concatenate([inp.k_ctx[0], inp.k_new[:, 0]], axis=0)   # [cap, Hkv, d]
+    kc_host = np.zeros((1, cap, 2, 64), np.float32)
+    kc_host[0, :N0] = inp.k_ctx[0]
+    k_cache = to_device(kc_host, "bf16")
+    pyr = ops.alloc_pyramid(dims, cap)
+    ops.build_pyramid(k_cache, N0, cap, dims, pyr)
+    k_new = to_device(inp.k_new, "bf16")      # [steps, 1, Hkv, d]
+    q_new = to_device(inp.q_new, "bf16")      # [steps, 1, Hq, d]
+    out = torch.full((1, 2, 32), -7, dtype=torch.int32, device="cuda")
+    ws = ops.alloc_workspace(dims, cap, True)
+    ref_k = to_device(np.concatenate([kc_host[0, :N0], inp.k_new[:, 0]], 0)[None], "bf16")
+    pyr_rb = ops.alloc_pyramid(dims, cap)
+    mism = near = 0
+    for s in range(steps):
+        n = N0 + s
+        ops.decode_update_select(q_new[s].contiguous(), k_new[s].contiguous(), k_cache, pyr, n, cap,
+                                 dims, out, ws)
+        torch.cuda.synchronize()
+        gpu_idx = out.cpu().numpy()[0]
+        if s % check_every == 0 or s == steps - 1:
+            # incremental == full rebuild, bitwise, on every node that exists at n + 1 keys
+            ops.build_pyramid(ref_k, n + 1, cap, dims, pyr_rb)
+            a, b = pyr.cpu().numpy(), pyr_rb.cpu().numpy()
+            for j in range(2):
+                for la, lb in zip(pyramid_levels(a[0, j], n + 1, cap), pyramid_levels(b[0, j], n + 1, cap)):
+                    assert np.array_equal(la.view(np.uint32), lb.view(np.uint32)), (s, j)
+        if s % oracle_every == 0 or s == steps - 1:
+            ref_pyr, o_idx, o_gap = oracle.decode_step(k_all, n, inp.q_new[s, 0], 32)
+            if s == 0 or s == steps - 1:
+                check_pyramid(pyr.cpu().numpy(), ref_pyr, n + 1, cap)
+            for j in range(2):
+                if not np.array_equal(gpu_idx[j], o_idx[j]):
+                    mism += 1
+                    assert o_gap[j] < 1e-3, (s, j, gpu_idx[j], o_idx[j], o_gap[j])
+                    v = oracle.validate(inp.q_new[s, 0], n, j, k_all[: n + 1], ref_pyr, 32, gpu_idx[j],
+                                        1e-3)
+                    assert v != 0, (s, j)
+                near += int(o_gap[j] < 1e-3)
+    return mism, near
+
+
+def test_decode_small_context():
+    """Decode from 1000 keys: crosses leaf boundaries and two new pyramid levels."""
+    mism, near = _decode_run(1000, 100)
+    print(json.dumps({"decode_small_mismatch_near_tie": mism, "near_tie_walks": near}), flush=True)
+
+
+def test_decode_128k_256_steps():
+    """The decode workload: 131072 prebuilt keys, 256 steps, K = 32; step 0 adds a root level."""
+    mism, near = _decode_run(131072, 256, check_every=1, oracle_every=1)
+    print(json.dumps({"decode128k_mismatch_near_tie": mism, "near_tie_walks": near}), flush=True)
