@@ -163,7 +163,7 @@ def main():
         assert q.dtype == tdt
         pyr = ops.alloc_pyramid(dims, N, dev)
         out = torch.empty((wl.B, N, wl.Hkv, wl.topk), dtype=torch.int32, device=dev)
-        ws = ops.alloc_workspace(dims, N, False, dev)
+        ws = ops.alloc_workspace(dims, N, N, device=dev)
         log(f"inputs {wl.name} N={N} ready in {time.perf_counter() - t0:.1f} s")
         return inp, N, dims, q, k, pyr, out, ws
 
@@ -202,7 +202,7 @@ def main():
     transc = logits + lse_terms               # one exp per logit, one log per LSE term
     walk_s = walk_ms.mean() / 1e3
     peaks = roofline_peaks()
-    src_hash = _hash_sources(["select.hip", "pisa_device.h"])
+    src_hash = _hash_sources(["upper.hip", "leaf.hip", "pisa_device.h"])
     traffic = measured_traffic(f"walk_kernel:{wl.name}", src_hash)
     exp_peak = peaks["transcendental_per_s"] if peaks else None
     achieved = transc / walk_s
@@ -293,7 +293,7 @@ def decode_bench(torch, ops, synth, dev, log):
     k_new, q_new = dev_t(inp.k_new), dev_t(inp.q_new)
     pyr = ops.alloc_pyramid(dims, cap, dev)
     out = torch.empty((1, wl.Hkv, wl.topk), dtype=torch.int32, device=dev)
-    ws = ops.alloc_workspace(dims, cap, True, dev)
+    ws = ops.alloc_workspace(dims, 1, cap, is_decode=True, device=dev)
     kn = [k_new[s].contiguous() for s in range(steps)]
     qn = [q_new[s].contiguous() for s in range(steps)]
     stream = torch.cuda.current_stream()

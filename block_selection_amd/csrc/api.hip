@@ -16,8 +16,40 @@ __global__ void build_subtree_kernel(const KT*, Geom, float*);
 __global__ void build_upper_kernel(Geom, float*);
 template <typename KT>
 __global__ void decode_refresh_kernel(const KT*, KT*, Geom, float*);
+__global__ void split_planes_kernel(const float*, uint16_t*, int64_t);
+template <typename KT, int SLOTS>
+__global__ void walk_upper_kernel(const KT*, const uint16_t*, const float*, Geom, UpperCfg, int64_t,
+                                  int64_t, int32_t*, int32_t*);
 template <typename KT>
-__global__ void walk_kernel(const KT*, const KT*, const float*, Geom, int64_t, int64_t, int32_t*);
+__global__ void leaf_walk_kernel(const KT*, const KT*, Geom, int64_t, int64_t, const int32_t*,
+                                 const int32_t*, int32_t*);
+
+constexpr int kLdsBudgetNodes = 240;     // 240 * 272 B = 63.75 KiB of staged coarse levels
+constexpr size_t kAlign = 256;
+
+static size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace carve-up for `walks` walks over a pyramid of P rows per (batch, head).
+struct Workspace {
+    uint16_t* planes;    // [2][B*Hkv*P*64] bf16 hi/lo planes (bf16 inputs only)
+    int32_t* cand;       // [walks][2K] leaf candidates
+    int32_t* ncand;      // [walks]
+    size_t bytes;
+};
+
+static Workspace carve(const pisa_dims* d, int64_t P, int64_t walks, char* base) {
+    Workspace w;
+    size_t off = 0;
+    const size_t planes = (d->dtype == PISA_DTYPE_BF16) ? (size_t)2 * d->B * d->Hkv * P * kD * 2 : 0;
+    w.planes = (uint16_t*)(base ? base + off : nullptr);
+    off = align_up(off + planes);
+    w.cand = (int32_t*)(base ? base + off : nullptr);
+    off = align_up(off + (size_t)walks * 2 * d->topk * sizeof(int32_t));
+    w.ncand = (int32_t*)(base ? base + off : nullptr);
+    off = align_up(off + (size_t)walks * sizeof(int32_t));
+    w.bytes = off;
+    return w;
+}
 
 // Level sizes for n keys: M[1] = ceil(n/64), M[l+1] = ceil(M[l]/2) until 1. Returns L.
 static int level_sizes(int64_t n, int64_t M[kMaxLevels + 1]) {
@@ -77,14 +109,72 @@ static int build_impl(const KT* k, const Geom& G, float* pyr, hipStream_t s) {
     return launch_status();
 }
 
+// Coarse levels to stage in LDS: the highest level that is ever read as children
+// (one below the highest level with more than K nodes) and as many levels below it
+// as fit the LDS budget.
+static UpperCfg upper_cfg(const Geom& G) {
+    UpperCfg U;
+    memset(&U, 0, sizeof(U));
+    U.j_lo = 1;
+    U.j_hi = 0;
+    int top = 0;
+    for (int l = G.L; l >= 1; --l) {
+        if (G.M[l] > G.topk) { top = l; break; }
+    }
+    const int j_hi = top - 1;
+    if (j_hi < 1) return U;
+    int nodes = 0, j_lo = j_hi + 1;
+    while (j_lo - 1 >= 1 && nodes + G.M[j_lo - 1] <= kLdsBudgetNodes) {
+        --j_lo;
+        nodes += G.M[j_lo];
+    }
+    if (j_lo > j_hi) return U;
+    U.j_lo = j_lo;
+    U.j_hi = j_hi;
+    int slot = 0;
+    for (int j = j_lo; j <= j_hi; ++j) { U.lds_first[j] = slot; slot += G.M[j]; }
+    U.lds_nodes = slot;
+    return U;
+}
+
+template <typename KT, int SLOTS>
+static void launch_upper(const KT* q, const uint16_t* planes, const float* pyr, const Geom& G,
+                         const UpperCfg& U, int64_t t0, int64_t NT, const Workspace& W, hipStream_t s) {
+    constexpr int WPW = 64 / SLOTS;
+    const int64_t groups = (NT + WPW - 1) / WPW;
+    const int bh = G.B * G.Hkv;
+    int64_t gx = (groups + 7) / 8;
+    const int64_t cap = (4096 + bh - 1) / bh;
+    if (gx > cap) gx = cap;
+    if (gx < 1) gx = 1;
+    const size_t lds = (sizeof(KT) == 2) ? (size_t)U.lds_nodes * kLdsNodeBytes : 0;
+    hipLaunchKernelGGL((walk_upper_kernel<KT, SLOTS>), dim3((unsigned)gx, (unsigned)bh), dim3(512), lds, s,
+                       q, planes, pyr, G, U, t0, NT, W.cand, W.ncand);
+}
+
 template <typename KT>
-static int walk_impl(const KT* q, const KT* k, const float* pyr, const Geom& G, int64_t t0,
-                     int64_t NT, int32_t* out, hipStream_t s) {
+static int select_impl(const KT* q, const KT* k, const float* pyr, const Geom& G, int64_t t0,
+                       int64_t NT, int32_t* out, const Workspace& W, hipStream_t s) {
+    UpperCfg U = upper_cfg(G);
+    if (sizeof(KT) == 2) {
+        const int64_t n = (int64_t)G.B * G.Hkv * G.P * kD;
+        int64_t grid = (n + 255) / 256;
+        if (grid > 8192) grid = 8192;
+        hipLaunchKernelGGL(split_planes_kernel, dim3((unsigned)grid), dim3(256), 0, s, pyr, W.planes, n);
+    } else {
+        U.j_lo = 1;
+        U.j_hi = 0;
+        U.lds_nodes = 0;
+    }
+    const int slots = 2 * G.topk;
+    if (slots <= 16) launch_upper<KT, 16>(q, W.planes, pyr, G, U, t0, NT, W, s);
+    else if (slots <= 32) launch_upper<KT, 32>(q, W.planes, pyr, G, U, t0, NT, W, s);
+    else launch_upper<KT, 64>(q, W.planes, pyr, G, U, t0, NT, W, s);
     const int64_t walks = (int64_t)G.B * NT * G.Hkv;
     int64_t grid = (walks + 3) / 4;
     if (grid > (1 << 22)) grid = 1 << 22;
-    hipLaunchKernelGGL(walk_kernel<KT>, dim3((unsigned)grid), dim3(256), 0, s, q, k, pyr, G, t0, NT,
-                       out);
+    hipLaunchKernelGGL(leaf_walk_kernel<KT>, dim3((unsigned)grid), dim3(256), 0, s, q, k, G, t0, NT,
+                       W.cand, W.ncand, out);
     return launch_status();
 }
 
@@ -119,9 +209,11 @@ size_t pisa_pyramid_bytes(const pisa_dims* dims, int64_t n_capacity) {
     return (size_t)dims->B * (size_t)dims->Hkv * (size_t)nodes * kD * sizeof(float);
 }
 
-size_t pisa_workspace_bytes(const pisa_dims* dims, int64_t N, int32_t is_decode) {
-    (void)dims; (void)N; (void)is_decode;
-    return 0;
+size_t pisa_workspace_bytes(const pisa_dims* dims, int64_t N, int64_t n_capacity, int32_t is_decode) {
+    if (check_dims(dims) != PISA_OK || n_capacity < 1 || (!is_decode && (N < 1 || N > n_capacity))) return 0;
+    const int64_t P = pisa_pyramid_nodes(dims, n_capacity);
+    const int64_t walks = is_decode ? (int64_t)dims->B * dims->Hkv : (int64_t)dims->B * N * dims->Hkv;
+    return carve(dims, P, walks, nullptr).bytes;
 }
 
 int pisa_build_pyramid(const void* k, int64_t N, int64_t n_capacity, const pisa_dims* dims,
@@ -144,12 +236,12 @@ int pisa_select_prefill(const void* q, const void* k, const float* pyramid, int6
     if (!q || !k || !pyramid || !out_idx) return PISA_ERR_INVALID_ARG;
     Geom G;
     if ((rc = make_geom(dims, N, n_capacity, &G)) != PISA_OK) return rc;
-    if (ws_bytes < pisa_workspace_bytes(dims, N, 0) || (!workspace && pisa_workspace_bytes(dims, N, 0)))
-        return PISA_ERR_WORKSPACE;
+    const Workspace W = carve(dims, G.P, (int64_t)dims->B * N * dims->Hkv, (char*)workspace);
+    if (!workspace || ws_bytes < W.bytes) return PISA_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     if (dims->dtype == PISA_DTYPE_BF16)
-        return walk_impl((const uint16_t*)q, (const uint16_t*)k, pyramid, G, 0, N, out_idx, s);
-    return walk_impl((const float*)q, (const float*)k, pyramid, G, 0, N, out_idx, s);
+        return select_impl((const uint16_t*)q, (const uint16_t*)k, pyramid, G, 0, N, out_idx, W, s);
+    return select_impl((const float*)q, (const float*)k, pyramid, G, 0, N, out_idx, W, s);
 }
 
 int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cache, float* pyramid,
@@ -161,22 +253,21 @@ int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cach
     if (n_before < 1) return PISA_ERR_INVALID_ARG;
     Geom G;
     if ((rc = make_geom(dims, n_before + 1, n_capacity, &G)) != PISA_OK) return rc;
-    if (ws_bytes < pisa_workspace_bytes(dims, n_capacity, 1) ||
-        (!workspace && pisa_workspace_bytes(dims, n_capacity, 1)))
-        return PISA_ERR_WORKSPACE;
+    const Workspace W = carve(dims, G.P, (int64_t)dims->B * dims->Hkv, (char*)workspace);
+    if (!workspace || ws_bytes < W.bytes) return PISA_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     const unsigned nbh = (unsigned)(dims->B * dims->Hkv);
     if (dims->dtype == PISA_DTYPE_BF16) {
         hipLaunchKernelGGL(decode_refresh_kernel<uint16_t>, dim3(nbh), dim3(64), 0, s,
                            (const uint16_t*)k_new, (uint16_t*)k_cache, G, pyramid);
         if ((rc = launch_status()) != PISA_OK) return rc;
-        return walk_impl((const uint16_t*)q_new, (const uint16_t*)k_cache, pyramid, G, n_before, 1,
-                         out_idx, s);
+        return select_impl((const uint16_t*)q_new, (const uint16_t*)k_cache, pyramid, G, n_before, 1,
+                           out_idx, W, s);
     }
     hipLaunchKernelGGL(decode_refresh_kernel<float>, dim3(nbh), dim3(64), 0, s,
                        (const float*)k_new, (float*)k_cache, G, pyramid);
     if ((rc = launch_status()) != PISA_OK) return rc;
-    return walk_impl((const float*)q_new, (const float*)k_cache, pyramid, G, n_before, 1, out_idx, s);
+    return select_impl((const float*)q_new, (const float*)k_cache, pyramid, G, n_before, 1, out_idx, W, s);
 }
 
 const char* pisa_status_string(int status) {

@@ -44,6 +44,17 @@ __host__ __device__ inline int64_t covered(int l, int64_t i, int64_t n) {
     return (n - lo < s) ? (n - lo) : s;
 }
 
+// Coarse pyramid levels staged in LDS by the upper-level walk: levels j_lo..j_hi
+// (none if j_lo > j_hi), node i of level j at LDS slot lds_first[j] + i, each slot
+// holding the hi and lo bf16 planes of the node (kLdsNodeBytes, padded against
+// bank conflicts).
+constexpr int kLdsNodeBytes = 272;
+struct UpperCfg {
+    int32_t j_lo, j_hi;
+    int32_t lds_first[kMaxLevels + 1];
+    int32_t lds_nodes;
+};
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -1,0 +1,339 @@
+// upper.hip -- the coarse-to-fine walk above the leaf level (gfx950).
+//
+// Reading note "Block Sparse Attention with Log-Linear Complexity", section
+// 3.2 and "Scoring: LogSumExp": from the root down to level 2, the candidates
+// of a level are the children of the previous survivors; a level with at most
+// K candidates keeps them all, otherwise each candidate scores the LSE of the
+// query's logits against its (at most two) children's summaries, summed over
+// the query heads of the GQA group (section 4.1), and the K best survive. The
+// kernel stops at level 2 and writes, per walk, the children of the level-2
+// survivors: the leaf-block candidates, ascending, -1 padded.
+//
+// Layout and arithmetic:
+//   * The fp32 summaries are pre-multiplied by log2(e)/sqrt(64) and split
+//     into two bf16 planes (hi = rne(x), lo = rne(x - hi); a 17-bit mantissa),
+//     so one bf16 MFMA chain v_mfma_f32_16x16x32_bf16 (hi and lo, two k-steps)
+//     yields base-2 logits directly. fp32 inputs use fp32 summaries on
+//     v_mfma_f32_16x16x4_f32 instead (exact products).
+//   * A wavefront walks 64/SLOTS queries at once, SLOTS = 16, 32 or 64 lanes
+//     per walk (2K <= SLOTS): lane i of a segment holds candidate slot i.
+//     Children rows of a walk fill 16-row MFMA tiles (rows = children, columns
+//     = the group's query heads); a lane holds both children of two
+//     candidates, so the pairwise LSE is in-lane and the group sum is four DPP
+//     adds across the 16 head columns.
+//   * The coarsest levels that can be read as children are staged in LDS
+//     once per workgroup; finer levels are gathered from global memory (L2).
+//   * Top-K: bitonic sort inside each segment by (score desc, node asc).
+#include "pisa_device.h"
+
+namespace pisa {
+
+constexpr float kScale2 = 0.125f * 1.4426950408889634f;   // log2(e) / sqrt(64)
+
+__device__ inline uint32_t rne_bf16_bits(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// planes[0] = rne(x * s), planes[1] = rne(x * s - hi), elementwise over the whole pyramid.
+__global__ __launch_bounds__(256) void split_planes_kernel(const float* __restrict__ pyr,
+                                                           uint16_t* __restrict__ planes,
+                                                           int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const float v = pyr[i] * kScale2;
+        const uint32_t hi = rne_bf16_bits(v);
+        const float r = v - __uint_as_float(hi << 16);
+        planes[i] = (uint16_t)hi;
+        planes[n + i] = (uint16_t)rne_bf16_bits(r);
+    }
+}
+
+// ---------------------------------------------------------------- lane moves --
+
+template <int J>
+__device__ inline int lane_xor(int v) {
+    if constexpr (J == 1) return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+    else if constexpr (J == 2) return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+    else if constexpr (J == 8) return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);
+    else if constexpr (J == 4 || J == 16) return __builtin_amdgcn_ds_swizzle(v, 0x1F | (J << 10));
+    else return __shfl_xor(v, J, 64);
+}
+template <int J>
+__device__ inline float lane_xor_f(float v) { return __int_as_float(lane_xor<J>(__float_as_int(v))); }
+
+// Sum over the 16 lanes of a DPP row (all lanes receive it).
+__device__ inline float row16_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+    return v;
+}
+
+// Does (sa, na) come before (sb, nb)? Higher score first, then lower node index.
+__device__ inline bool precedes(float sa, int na, float sb, int nb) {
+    return sa > sb || (sa == sb && na < nb);
+}
+
+template <int J>
+__device__ inline void bitonic_step(float& s, int& nd, int i, int k) {
+    const float so = lane_xor_f<J>(s);
+    const int no = lane_xor<J>(nd);
+    const bool lower = (i & J) == 0;
+    const bool up = (i & k) == 0;
+    const bool self_first = precedes(s, nd, so, no);
+    const bool keep_self = (lower == up) ? self_first : !self_first;
+    if (!keep_self) { s = so; nd = no; }
+}
+
+// Sort (s, nd) inside each segment of SLOTS lanes so that segment lane 0 comes first.
+template <int SLOTS>
+__device__ inline void segment_sort(float& s, int& nd, int i) {
+#pragma unroll
+    for (int k = 2; k <= SLOTS; k <<= 1) {
+        if (k >= 64) { bitonic_step<32>(s, nd, i, k); }
+        if (k >= 32) { bitonic_step<16>(s, nd, i, k); }
+        if (k >= 16) { bitonic_step<8>(s, nd, i, k); }
+        if (k >= 8) { bitonic_step<4>(s, nd, i, k); }
+        if (k >= 4) { bitonic_step<2>(s, nd, i, k); }
+        bitonic_step<1>(s, nd, i, k);
+    }
+}
+
+// ------------------------------------------------------------ upper scoring --
+
+template <typename KT>
+struct UpperQ;
+
+// bf16 queries: B operand of the bf16 MFMA, dims {8g..8g+7} and {32+8g..32+8g+7}.
+template <>
+struct UpperQ<uint16_t> {
+    bf16x8 k0, k1;
+    __device__ void load(const uint16_t* row, bool valid, int gq) {
+        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+        if (valid) {
+            a = *reinterpret_cast<const u32x4*>(row + 8 * gq);
+            b = *reinterpret_cast<const u32x4*>(row + 32 + 8 * gq);
+        }
+        k0 = __builtin_bit_cast(bf16x8, a);
+        k1 = __builtin_bit_cast(bf16x8, b);
+    }
+};
+
+template <>
+struct UpperQ<float> {
+    float f[16];
+    __device__ void load(const float* row, bool valid, int gq) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) f[i] = 0.f;
+        if (valid) {
+            load8_f32(row + 8 * gq, f);
+            load8_f32(row + 32 + 8 * gq, f + 8);
+        }
+    }
+};
+
+// Base-2 logits of one 16-row tile of children (row = lane % 16) against the query.
+__device__ inline f32x4 child_tile_bf16(const UpperQ<uint16_t>& q, const uint16_t* __restrict__ planes,
+                                        int64_t plane_stride, int64_t row_elem, const char* lds,
+                                        int lds_node, bool valid, int gq) {
+    u32x4 h0 = {0u, 0u, 0u, 0u}, h1 = h0, l0 = h0, l1 = h0;
+    if (valid) {
+        if (lds_node >= 0) {
+            const char* p = lds + (int64_t)lds_node * kLdsNodeBytes;
+            h0 = *reinterpret_cast<const u32x4*>(p + 16 * gq);
+            h1 = *reinterpret_cast<const u32x4*>(p + 64 + 16 * gq);
+            l0 = *reinterpret_cast<const u32x4*>(p + 128 + 16 * gq);
+            l1 = *reinterpret_cast<const u32x4*>(p + 192 + 16 * gq);
+        } else {
+            const uint16_t* p = planes + row_elem;
+            h0 = *reinterpret_cast<const u32x4*>(p + 8 * gq);
+            h1 = *reinterpret_cast<const u32x4*>(p + 32 + 8 * gq);
+            l0 = *reinterpret_cast<const u32x4*>(p + plane_stride + 8 * gq);
+            l1 = *reinterpret_cast<const u32x4*>(p + plane_stride + 32 + 8 * gq);
+        }
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h0), q.k0, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h1), q.k1, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, l0), q.k0, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, l1), q.k1, acc, 0, 0, 0);
+    return acc;
+}
+
+__device__ inline f32x4 child_tile_f32(const UpperQ<float>& q, const float* __restrict__ pyr_row,
+                                       bool valid, int gq) {
+    float a[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a[i] = 0.f;
+    if (valid) {
+        load8_f32(pyr_row + 8 * gq, a);
+        load8_f32(pyr_row + 32 + 8 * gq, a + 8);
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 16; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], q.f[s], acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] *= kScale2;
+    return acc;
+}
+
+// log2(2^a + 2^b)
+__device__ inline float log2_add_exp2(float a, float b) {
+    const float m = fmaxf(a, b), d = fminf(a, b) - m;
+    return m + __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(d));
+}
+
+// Walks for positions t0 + ti, ti in [0, NT), of batch element b and KV head kvh
+// (blockIdx.y = b * Hkv + kvh). Output per walk (index (b*NT + ti)*Hkv + kvh):
+// cand_out[2K] ascending leaf candidates (-1 padded) and ncand_out = their count.
+template <typename KT, int SLOTS>
+__global__ __launch_bounds__(512) void walk_upper_kernel(const KT* __restrict__ q,
+                                                         const uint16_t* __restrict__ planes,
+                                                         const float* __restrict__ pyr, Geom G,
+                                                         UpperCfg U, int64_t t0, int64_t NT,
+                                                         int32_t* __restrict__ cand_out,
+                                                         int32_t* __restrict__ ncand_out) {
+    constexpr int WPW = 64 / SLOTS;
+    extern __shared__ u32x4 lds_u4[];
+    char* lds = reinterpret_cast<char*>(lds_u4);
+    const int bh = blockIdx.y;
+    const int b = bh / G.Hkv, kvh = bh % G.Hkv;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+    const int seg = lane / SLOTS, i = lane % SLOTS, gq = lane >> 4, n = lane & 15;
+    const int K = G.topk;
+    const int64_t plane_stride = (int64_t)G.B * G.Hkv * G.P * kD;
+    const int64_t bh_row0 = (int64_t)bh * G.P;
+
+    // stage the coarse levels: node j-level i -> LDS slot lds_first[j] + i, planes hi|lo
+    if constexpr (sizeof(KT) == 2) {
+        for (int j = U.j_lo; j <= U.j_hi; ++j) {
+            const int m = G.M[j];
+            for (int c = threadIdx.x; c < m * 16; c += blockDim.x) {
+                const int node = c >> 4, part = c & 15;        // part: plane (part>>3), 16-B chunk (part&7)
+                const uint16_t* src = planes + (part >> 3) * plane_stride +
+                                      (bh_row0 + G.off[j] + node) * kD + (part & 7) * 8;
+                *reinterpret_cast<u32x4*>(lds + (int64_t)(U.lds_first[j] + node) * kLdsNodeBytes +
+                                          (part >> 3) * 128 + (part & 7) * 16) =
+                    *reinterpret_cast<const u32x4*>(src);
+            }
+        }
+        __syncthreads();
+    }
+
+    const int64_t ngroups = (NT + WPW - 1) / WPW;
+    for (int64_t grp = (int64_t)blockIdx.x * nwaves + wave; grp < ngroups;
+         grp += (int64_t)gridDim.x * nwaves) {
+        // queries of the WPW walks of this wavefront
+        UpperQ<KT> qf[WPW];
+        int64_t tw[WPW];
+#pragma unroll
+        for (int w = 0; w < WPW; ++w) {
+            const int64_t ti = grp * WPW + w;
+            tw[w] = t0 + ti;
+            const bool ok = ti < NT && n < G.GQ;
+            const KT* qrow = q + (((int64_t)b * NT + (ti < NT ? ti : 0)) * G.Hq + (int64_t)kvh * G.GQ + n) * kD;
+            qf[w].load(qrow, ok, gq);
+        }
+        const int64_t my_ti = grp * WPW + seg;
+        const int64_t my_t = t0 + my_ti;
+        const bool my_ok = my_ti < NT;
+
+        int surv = (i == 0 && my_ok) ? 0 : -1;   // survivors of the level above, segment lanes 0..K-1
+        for (int l = G.L; l >= 2; --l) {
+            int cand;
+            if (l == G.L) {
+                cand = surv;
+            } else {
+                const int par = shfl_i(surv, seg * SLOTS + (i >> 1));
+                const int64_t child = 2 * (int64_t)par + (i & 1);
+                const bool ok = i < 2 * K && par >= 0 && child < G.M[l] && first_key(l, child) <= my_t;
+                cand = ok ? (int)child : -1;
+            }
+            // does any walk of this wavefront have more than K candidates here?
+            const uint64_t vm = ballot(cand >= 0);
+            bool need = false;
+#pragma unroll
+            for (int w = 0; w < WPW; ++w) {
+                const uint64_t segm = (SLOTS == 64) ? ~0ull : (((1ull << SLOTS) - 1) << (w * SLOTS));
+                need |= __popcll(vm & segm) > K;
+            }
+            float my = (cand >= 0) ? 0.0f : -INFINITY;
+            if (need) {
+                const int lc = l - 1;
+                const int64_t Mc = G.M[lc];
+                const bool in_lds = (sizeof(KT) == 2) && lc >= U.j_lo && lc <= U.j_hi;
+#pragma unroll
+                for (int w = 0; w < WPW; ++w) {
+#pragma unroll
+                    for (int tau = 0; tau < SLOTS / 8; ++tau) {
+                        const int cs = 16 * tau + n;                 // child slot of this MFMA row
+                        const int par = shfl_i(cand, w * SLOTS + (cs >> 1));
+                        const int64_t child = 2 * (int64_t)par + (cs & 1);
+                        const bool valid = par >= 0 && child < Mc && first_key(lc, child) <= tw[w];
+                        f32x4 acc;
+                        if constexpr (sizeof(KT) == 2) {
+                            acc = child_tile_bf16(qf[w], planes, plane_stride,
+                                                  (bh_row0 + G.off[lc] + child) * kD, lds,
+                                                  in_lds ? U.lds_first[lc] + (int)child : -1, valid, gq);
+                        } else {
+                            acc = child_tile_f32(qf[w], pyr + (bh_row0 + G.off[lc] + child) * kD, valid, gq);
+                        }
+                        float sc[2];
+#pragma unroll
+                        for (int p = 0; p < 2; ++p) {
+                            const int pp = shfl_i(cand, w * SLOTS + 8 * tau + 2 * gq + p);
+                            const int64_t right = 2 * (int64_t)pp + 1;
+                            const bool has_right = pp >= 0 && right < Mc && first_key(lc, right) <= tw[w];
+                            const float lse2 = has_right ? log2_add_exp2(acc[2 * p], acc[2 * p + 1]) : acc[2 * p];
+                            const float s = row16_sum(n < G.GQ ? lse2 : 0.0f);
+                            sc[p] = (pp >= 0) ? s : -INFINITY;
+                        }
+                        const int src = 16 * ((i & 7) >> 1);
+                        const float v0 = shfl_f(sc[0], src), v1 = shfl_f(sc[1], src);
+                        if (seg == w && (i >> 3) == tau) my = (i & 1) ? v1 : v0;
+                    }
+                }
+                if (cand < 0) my = -INFINITY;
+            }
+            int nd = (cand >= 0) ? cand : INT_MAX;
+            segment_sort<SLOTS>(my, nd, i);
+            surv = (i < K && nd != INT_MAX) ? nd : -1;
+        }
+        // leaf candidates: children of the level-2 survivors (or the root if it is a leaf)
+        int leaf;
+        if (G.L == 1) {
+            leaf = surv;
+        } else {
+            const int par = shfl_i(surv, seg * SLOTS + (i >> 1));
+            const int64_t child = 2 * (int64_t)par + (i & 1);
+            const bool ok = i < 2 * K && par >= 0 && child < G.M[1] && first_key(1, child) <= my_t;
+            leaf = ok ? (int)child : -1;
+        }
+        // ascending order, -1 last (equal scores: lower index first)
+        float zero = 0.0f;
+        int nd = (leaf >= 0) ? leaf : INT_MAX;
+        segment_sort<SLOTS>(zero, nd, i);
+        leaf = (nd != INT_MAX && i < 2 * K) ? nd : -1;
+        const uint64_t lm = ballot(leaf >= 0);
+        const uint64_t segm = (SLOTS == 64) ? ~0ull : (((1ull << SLOTS) - 1) << (seg * SLOTS));
+        if (my_ok && i < 2 * K) {
+            const int64_t wid = ((int64_t)b * NT + my_ti) * G.Hkv + kvh;
+            cand_out[wid * (2 * K) + i] = leaf;
+            if (i == 0) ncand_out[wid] = __popcll(lm & segm);
+        }
+    }
+}
+
+#define PISA_INST_UPPER(KT, S)                                                                   \
+    template __global__ void walk_upper_kernel<KT, S>(const KT*, const uint16_t*, const float*, \
+                                                      Geom, UpperCfg, int64_t, int64_t, int32_t*, \
+                                                      int32_t*);
+PISA_INST_UPPER(uint16_t, 16)
+PISA_INST_UPPER(uint16_t, 32)
+PISA_INST_UPPER(uint16_t, 64)
+PISA_INST_UPPER(float, 16)
+PISA_INST_UPPER(float, 32)
+PISA_INST_UPPER(float, 64)
+
+}  // namespace pisa

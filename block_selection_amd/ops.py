@@ -60,7 +60,7 @@ def _load() -> ctypes.CDLL:
     lib.pisa_level_offset.restype = i64
     lib.pisa_pyramid_bytes.argtypes = [D, i64]
     lib.pisa_pyramid_bytes.restype = sz
-    lib.pisa_workspace_bytes.argtypes = [D, i64, i32]
+    lib.pisa_workspace_bytes.argtypes = [D, i64, i64, i32]
     lib.pisa_workspace_bytes.restype = sz
     lib.pisa_build_pyramid.argtypes = [P, i64, i64, D, P, P]
     lib.pisa_build_pyramid.restype = ctypes.c_int
@@ -98,8 +98,9 @@ def pyramid_bytes(dims: Dims, n_capacity: int) -> int:
     return int(lib.pisa_pyramid_bytes(ctypes.byref(dims), n_capacity))
 
 
-def workspace_bytes(dims: Dims, N: int, is_decode: bool = False) -> int:
-    return int(lib.pisa_workspace_bytes(ctypes.byref(dims), N, int(bool(is_decode))))
+def workspace_bytes(dims: Dims, N: int, n_capacity: Optional[int] = None, is_decode: bool = False) -> int:
+    cap = N if n_capacity is None else n_capacity
+    return int(lib.pisa_workspace_bytes(ctypes.byref(dims), N, cap, int(bool(is_decode))))
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -122,8 +123,9 @@ def alloc_pyramid(dims: Dims, n_capacity: int, device="cuda") -> torch.Tensor:
                        dtype=torch.float32, device=device)
 
 
-def alloc_workspace(dims: Dims, N: int, is_decode: bool = False, device="cuda") -> Optional[torch.Tensor]:
-    n = workspace_bytes(dims, N, is_decode)
+def alloc_workspace(dims: Dims, N: int, n_capacity: Optional[int] = None, is_decode: bool = False,
+                    device="cuda") -> Optional[torch.Tensor]:
+    n = workspace_bytes(dims, N, n_capacity, is_decode)
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 

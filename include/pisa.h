@@ -86,9 +86,11 @@ int64_t pisa_level_offset(const pisa_dims* dims, int64_t n_capacity, int32_t lev
 size_t pisa_pyramid_bytes(const pisa_dims* dims, int64_t n_capacity);
 
 /* Device workspace that pisa_select_prefill (is_decode = 0, N = sequence
- * length) or pisa_decode_update_select (is_decode = 1, N = n_capacity) needs.
- * May be 0; then a NULL workspace is accepted. */
-size_t pisa_workspace_bytes(const pisa_dims* dims, int64_t N, int32_t is_decode);
+ * length) or pisa_decode_update_select (is_decode = 1; N is ignored) needs for
+ * a pyramid laid out for n_capacity keys. Returns 0 on bad input. The
+ * workspace holds scratch data between the kernels of one call; its contents
+ * need not be initialised and are meaningless after the call. */
+size_t pisa_workspace_bytes(const pisa_dims* dims, int64_t N, int64_t n_capacity, int32_t is_decode);
 
 /*
  * Builds the mean pyramid over keys 0..N-1 (reading note, section 3.1).
@@ -109,9 +111,11 @@ int pisa_build_pyramid(const void* k, int64_t N, int64_t n_capacity, const pisa_
  *   k        [B, n_capacity, Hkv, d], the keys the pyramid was built from.
  *   pyramid  as written by pisa_build_pyramid for the same N and n_capacity.
  *   out_idx  int32 [B, N, Hkv, topk]: ascending leaf indices, -1 padded.
- *   workspace at least pisa_workspace_bytes(dims, N, 0) bytes of device memory.
- * Scores use fp32 arithmetic: bf16 (or fp32) q.k products accumulated in fp32,
- * fp32 summaries, fp32 LogSumExp.
+ *   workspace at least pisa_workspace_bytes(dims, N, n_capacity, 0) bytes of device memory.
+ * Arithmetic: leaf scores use the exact bf16 (or fp32) q.k products accumulated
+ * in fp32; upper-level scores multiply bf16 queries by the fp32 summaries held
+ * as a hi + lo pair of bf16 values (relative error <= 2^-17 per element; fp32
+ * inputs use fp32 summaries directly); LogSumExp in fp32.
  */
 int pisa_select_prefill(const void* q, const void* k, const float* pyramid, int64_t N,
                         int64_t n_capacity, const pisa_dims* dims, int32_t* out_idx,

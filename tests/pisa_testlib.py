@@ -52,7 +52,7 @@ def run_prefill(q: np.ndarray, k: np.ndarray, topk: int, dtype: str, cap: int | 
     pyr = ops.alloc_pyramid(dims, cap, device)
     pyr.fill_(float("nan"))
     out = torch.full((B, N, Hkv, topk), -7, dtype=torch.int32, device=device)
-    ws = ops.alloc_workspace(dims, N, False, device)
+    ws = ops.alloc_workspace(dims, N, cap, device=device)
     ops.build_pyramid(kt, N, cap, dims, pyr)
     ops.select_prefill(qt, kt, pyr, N, cap, dims, out, ws)
     torch.cuda.synchronize()

@@ -1,0 +1,69 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/pisa.h declares, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "pisa.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(pisa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    from block_selection_amd import ops
+    names = _declared()
+    assert set(names) == set(ops.EXPORTED)
+    for n in names:
+        assert hasattr(ops.lib, n), n
+
+
+def test_geometry_helpers():
+    from block_selection_amd import ops
+    d = ops.make_dims(1, 32, 2, 8)
+    assert ops.pyramid_nodes(d, 262144) == 8191
+    assert ops.level_offset(d, 262144, 1) == 0
+    assert ops.level_offset(d, 262144, 2) == 4096
+    assert ops.level_offset(d, 262144, 13) == 8190
+    assert ops.level_offset(d, 262144, 14) == -1
+    assert ops.pyramid_bytes(d, 262144) == 2 * 8191 * 64 * 4
+    assert ops.pyramid_nodes(d, 1) == 1
+    assert ops.workspace_bytes(d, 4096) > 0
+    assert ops.workspace_bytes(d, 1, 131328, is_decode=True) > 0
+    assert ops.workspace_bytes(d, 5000, 4000) == 0
+
+
+def _call_select(ops, dims, N=64, cap=64, ws=8, ws_bytes=1 << 30, ptr=8):
+    p = ctypes.c_void_p(ptr)
+    return ops.lib.pisa_select_prefill(p, p, p, N, cap, ctypes.byref(dims), p,
+                                       ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+
+
+def test_argument_errors_return_before_launch():
+    from block_selection_amd import ops
+    good = ops.make_dims(1, 32, 2, 8)
+    assert _call_select(ops, ops.make_dims(1, 32, 2, 8, d=32)) == ops.PISA_ERR_UNSUPPORTED
+    assert _call_select(ops, ops.make_dims(1, 32, 2, 8, C=32)) == ops.PISA_ERR_UNSUPPORTED
+    assert _call_select(ops, ops.make_dims(1, 32, 2, 8, g=4)) == ops.PISA_ERR_UNSUPPORTED
+    assert _call_select(ops, ops.make_dims(1, 34, 1, 8)) == ops.PISA_ERR_UNSUPPORTED   # group of 34
+    assert _call_select(ops, ops.make_dims(1, 32, 2, 33)) == ops.PISA_ERR_UNSUPPORTED
+    assert _call_select(ops, ops.make_dims(1, 31, 2, 8)) == ops.PISA_ERR_INVALID_ARG
+    assert _call_select(ops, ops.make_dims(1, 32, 2, 0)) == ops.PISA_ERR_INVALID_ARG
+    assert _call_select(ops, ops.make_dims(0, 32, 2, 8)) == ops.PISA_ERR_INVALID_ARG
+    assert _call_select(ops, good, N=65, cap=64) == ops.PISA_ERR_CAPACITY
+    assert _call_select(ops, good, N=0) == ops.PISA_ERR_INVALID_ARG
+    assert _call_select(ops, good, ws=0) == ops.PISA_ERR_WORKSPACE
+    assert _call_select(ops, good, ws_bytes=16) == ops.PISA_ERR_WORKSPACE
+    assert _call_select(ops, good, ptr=0) == ops.PISA_ERR_INVALID_ARG
+    p = ctypes.c_void_p(8)
+    assert ops.lib.pisa_build_pyramid(None, 64, 64, ctypes.byref(good), p, None) == ops.PISA_ERR_INVALID_ARG
+    assert ops.lib.pisa_decode_update_select(p, p, p, p, 0, 64, ctypes.byref(good), p, p, 1 << 30,
+                                             None) == ops.PISA_ERR_INVALID_ARG
+    assert ops.lib.pisa_decode_update_select(p, p, p, p, 64, 64, ctypes.byref(good), p, p, 1 << 30,
+                                             None) == ops.PISA_ERR_CAPACITY
+    assert ops.status_string(ops.PISA_ERR_WORKSPACE) == "workspace too small"

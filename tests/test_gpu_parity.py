@@ -173,7 +173,7 @@ def _decode_run(N0, steps, check_every=1, oracle_every=1):
     k_new = to_device(inp.k_new, "bf16")      # [steps, 1, Hkv, d]
     q_new = to_device(inp.q_new, "bf16")      # [steps, 1, Hq, d]
     out = torch.full((1, 2, 32), -7, dtype=torch.int32, device="cuda")
-    ws = ops.alloc_workspace(dims, cap, True)
+    ws = ops.alloc_workspace(dims, 1, cap, is_decode=True)
     ref_k = to_device(np.concatenate([kc_host[0, :N0], inp.k_new[:, 0]], 0)[None], "bf16")
     pyr_rb = ops.alloc_pyramid(dims, cap)
     mism = near = 0
