@@ -24,7 +24,16 @@ template <typename KT>
 __global__ void leaf_walk_kernel(const KT*, const KT*, Geom, int64_t, int64_t, const int32_t*,
                                  const int32_t*, int32_t*);
 
-constexpr int kLdsBudgetNodes = 240;     // 240 * 272 B = 63.75 KiB of staged coarse levels
+__global__ void fill_u32_kernel(uint32_t*, int64_t, uint32_t);
+template <int SL>
+__global__ void bucket_pass_kernel(const int32_t*, const int32_t*, Geom, ClusterGeom, int64_t, uint32_t*,
+                                   const uint32_t*, uint2*, int);
+__global__ void scan_groups_kernel(const uint32_t*, ClusterGeom, uint32_t*, int4*, uint32_t*);
+__global__ void leaf_cluster_kernel(const uint16_t*, const uint16_t*, Geom, ClusterGeom, int64_t,
+                                    const int4*, const uint2*, const uint32_t*, float*);
+template <int SLOTS>
+__global__ void final_topk_kernel(const int32_t*, const int32_t*, const float*, Geom, int64_t, int32_t*);
+
 constexpr size_t kAlign = 256;
 
 static size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -34,19 +43,50 @@ struct Workspace {
     uint16_t* planes;    // [2][B*Hkv*P*64] bf16 hi/lo planes (bf16 inputs only)
     int32_t* cand;       // [walks][2K] leaf candidates
     int32_t* ncand;      // [walks]
+    // clustered leaf scoring (prefill, bf16 inputs)
+    float* score;        // [walks][2K]
+    uint32_t* counts;    // [nb]
+    uint32_t* offsets;   // [nb]
+    uint2* entries;      // [walks * 2K] incidences grouped by bucket
+    int4* items;         // [walks * 2K / kItemMax + ngroups]
+    uint32_t* meta;      // [0] items, [1] entries
+    ClusterGeom CG;
+    bool clustered;
     size_t bytes;
 };
 
-static Workspace carve(const pisa_dims* d, int64_t P, int64_t walks, char* base) {
+// N positions per batch element (1 for a decoding step) over a pyramid of P rows.
+static Workspace carve(const pisa_dims* d, int64_t N, int64_t P, bool decode, char* base) {
     Workspace w;
+    memset(&w, 0, sizeof(w));
+    const int64_t walks = (int64_t)d->B * (decode ? 1 : N) * d->Hkv;
+    const int64_t cs = 2 * (int64_t)d->topk;
     size_t off = 0;
+    auto take = [&](size_t bytes) -> char* {
+        char* p = base ? base + off : nullptr;
+        off = align_up(off + bytes);
+        return p;
+    };
     const size_t planes = (d->dtype == PISA_DTYPE_BF16) ? (size_t)2 * d->B * d->Hkv * P * kD * 2 : 0;
-    w.planes = (uint16_t*)(base ? base + off : nullptr);
-    off = align_up(off + planes);
-    w.cand = (int32_t*)(base ? base + off : nullptr);
-    off = align_up(off + (size_t)walks * 2 * d->topk * sizeof(int32_t));
-    w.ncand = (int32_t*)(base ? base + off : nullptr);
-    off = align_up(off + (size_t)walks * sizeof(int32_t));
+    w.planes = (uint16_t*)take(planes);
+    w.cand = (int32_t*)take((size_t)walks * cs * sizeof(int32_t));
+    w.ncand = (int32_t*)take((size_t)walks * sizeof(int32_t));
+    const int64_t m1 = (N + kC - 1) / kC;
+    const int64_t nsb = (m1 + kSbLeaves - 1) / kSbLeaves;
+    // clustered leaf scoring for bf16 prefill while the per-range LDS histogram fits
+    w.clustered = !decode && d->dtype == PISA_DTYPE_BF16 && d->Hkv * nsb <= 16384;
+    if (w.clustered) {
+        w.CG.NR = (int32_t)((N + kRangeT - 1) / kRangeT);
+        w.CG.NSB = (int32_t)nsb;
+        w.CG.ngroups = (int32_t)(d->B * d->Hkv * nsb);
+        w.CG.nb = w.CG.ngroups * w.CG.NR;
+        w.score = (float*)take((size_t)walks * cs * sizeof(float));
+        w.counts = (uint32_t*)take((size_t)w.CG.nb * 4);
+        w.offsets = (uint32_t*)take((size_t)w.CG.nb * 4);
+        w.entries = (uint2*)take((size_t)walks * cs * sizeof(uint2));
+        w.items = (int4*)take(((size_t)walks * cs / kItemMax + w.CG.ngroups + 1) * sizeof(int4));
+        w.meta = (uint32_t*)take(16);
+    }
     w.bytes = off;
     return w;
 }
@@ -138,23 +178,77 @@ static UpperCfg upper_cfg(const Geom& G) {
 }
 
 template <typename KT, int SLOTS>
-static void launch_upper(const KT* q, const uint16_t* planes, const float* pyr, const Geom& G,
-                         const UpperCfg& U, int64_t t0, int64_t NT, const Workspace& W, hipStream_t s) {
+static int launch_upper(const KT* q, const uint16_t* planes, const float* pyr, const Geom& G,
+                        const UpperCfg& U, int64_t t0, int64_t NT, const Workspace& W, int cus, hipStream_t s) {
     constexpr int WPW = 64 / SLOTS;
+    constexpr int nwaves = kUpperThreads / 64;
     const int64_t groups = (NT + WPW - 1) / WPW;
     const int bh = G.B * G.Hkv;
-    int64_t gx = (groups + 7) / 8;
-    const int64_t cap = (4096 + bh - 1) / bh;
-    if (gx > cap) gx = cap;
-    if (gx < 1) gx = 1;
+    // one workgroup per CU (LDS-bound), a multiple of 8 so that XCDs split evenly
+    int64_t need = (int64_t)bh * ((groups + nwaves - 1) / nwaves);
+    int64_t nwg = need < cus ? need : cus;
+    nwg = (nwg + 7) / 8 * 8;
+    if (nwg < bh) nwg = bh;
     const size_t lds = (sizeof(KT) == 2) ? (size_t)U.lds_nodes * kLdsNodeBytes : 0;
-    hipLaunchKernelGGL((walk_upper_kernel<KT, SLOTS>), dim3((unsigned)gx, (unsigned)bh), dim3(512), lds, s,
+    const void* fn = (const void*)walk_upper_kernel<KT, SLOTS>;
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return PISA_ERR_HIP;
+    hipLaunchKernelGGL((walk_upper_kernel<KT, SLOTS>), dim3((unsigned)nwg), dim3(kUpperThreads), lds, s,
                        q, planes, pyr, G, U, t0, NT, W.cand, W.ncand);
+    return PISA_OK;
+}
+
+static int device_cus(int* cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PISA_ERR_HIP;
+    if (hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return PISA_ERR_HIP;
+    return PISA_OK;
+}
+
+// Leaf stage after the upper walk has recorded its incidences: bucket offsets and
+// work items, entries grouped by bucket, clustered scoring, final top-K per walk.
+static int cluster_leaf_stage(const uint16_t* q, const uint16_t* k, const Geom& G, int64_t NT, int32_t* out,
+                              const Workspace& W, int cus, hipStream_t s) {
+    const int64_t walks = (int64_t)G.B * NT * G.Hkv;
+    const ClusterGeom& CG = W.CG;
+    const int slots = 2 * G.topk;
+    const dim3 bgrid((unsigned)CG.NR, (unsigned)G.B);
+    const size_t bins = (size_t)G.Hkv * CG.NSB * 4;
+    for (int fill = 0; fill < 2; ++fill) {
+        if (fill)
+            hipLaunchKernelGGL(scan_groups_kernel, dim3(1), dim3(1024), 0, s, W.counts, CG, W.offsets, W.items, W.meta);
+        if (slots <= 16)
+            hipLaunchKernelGGL(bucket_pass_kernel<16>, bgrid, dim3(256), bins, s, W.cand, W.ncand, G, CG, NT, W.counts,
+                               W.offsets, W.entries, fill);
+        else if (slots <= 32)
+            hipLaunchKernelGGL(bucket_pass_kernel<32>, bgrid, dim3(256), bins, s, W.cand, W.ncand, G, CG, NT, W.counts,
+                               W.offsets, W.entries, fill);
+        else
+            hipLaunchKernelGGL(bucket_pass_kernel<64>, bgrid, dim3(256), bins, s, W.cand, W.ncand, G, CG, NT, W.counts,
+                               W.offsets, W.entries, fill);
+    }
+    if (hipFuncSetAttribute((const void*)leaf_cluster_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kSbLdsBytes) != hipSuccess)
+        return PISA_ERR_HIP;
+    hipLaunchKernelGGL(leaf_cluster_kernel, dim3((unsigned)cus), dim3(kClusterThreads), kSbLdsBytes, s, q, k, G,
+                       CG, NT, W.items, W.entries, W.meta, W.score);
+    const int wpw = slots <= 16 ? 4 : (slots <= 32 ? 2 : 1);
+    int64_t fgrid = ((walks + wpw - 1) / wpw + 3) / 4;
+    if (fgrid > 65536) fgrid = 65536;
+    if (slots <= 16)
+        hipLaunchKernelGGL(final_topk_kernel<16>, dim3((unsigned)fgrid), dim3(256), 0, s, W.cand, W.ncand, W.score, G, NT, out);
+    else if (slots <= 32)
+        hipLaunchKernelGGL(final_topk_kernel<32>, dim3((unsigned)fgrid), dim3(256), 0, s, W.cand, W.ncand, W.score, G, NT, out);
+    else
+        hipLaunchKernelGGL(final_topk_kernel<64>, dim3((unsigned)fgrid), dim3(256), 0, s, W.cand, W.ncand, W.score, G, NT, out);
+    return launch_status();
 }
 
 template <typename KT>
 static int select_impl(const KT* q, const KT* k, const float* pyr, const Geom& G, int64_t t0,
                        int64_t NT, int32_t* out, const Workspace& W, hipStream_t s) {
+    int rc, cus = 256;
+    if ((rc = device_cus(&cus)) != PISA_OK) return rc;
     UpperCfg U = upper_cfg(G);
     if (sizeof(KT) == 2) {
         const int64_t n = (int64_t)G.B * G.Hkv * G.P * kD;
@@ -167,15 +261,19 @@ static int select_impl(const KT* q, const KT* k, const float* pyr, const Geom& G
         U.lds_nodes = 0;
     }
     const int slots = 2 * G.topk;
-    if (slots <= 16) launch_upper<KT, 16>(q, W.planes, pyr, G, U, t0, NT, W, s);
-    else if (slots <= 32) launch_upper<KT, 32>(q, W.planes, pyr, G, U, t0, NT, W, s);
-    else launch_upper<KT, 64>(q, W.planes, pyr, G, U, t0, NT, W, s);
+    if (slots <= 16) rc = launch_upper<KT, 16>(q, W.planes, pyr, G, U, t0, NT, W, cus, s);
+    else if (slots <= 32) rc = launch_upper<KT, 32>(q, W.planes, pyr, G, U, t0, NT, W, cus, s);
+    else rc = launch_upper<KT, 64>(q, W.planes, pyr, G, U, t0, NT, W, cus, s);
+    if (rc != PISA_OK) return rc;
     const int64_t walks = (int64_t)G.B * NT * G.Hkv;
-    int64_t grid = (walks + 3) / 4;
-    if (grid > (1 << 22)) grid = 1 << 22;
-    hipLaunchKernelGGL(leaf_walk_kernel<KT>, dim3((unsigned)grid), dim3(256), 0, s, q, k, G, t0, NT,
-                       W.cand, W.ncand, out);
-    return launch_status();
+    if (!W.clustered) {
+        int64_t grid = (walks + 3) / 4;
+        if (grid > (1 << 22)) grid = 1 << 22;
+        hipLaunchKernelGGL(leaf_walk_kernel<KT>, dim3((unsigned)grid), dim3(256), 0, s, q, k, G, t0, NT,
+                           W.cand, W.ncand, out);
+        return launch_status();
+    }
+    return cluster_leaf_stage((const uint16_t*)q, (const uint16_t*)k, G, NT, out, W, cus, s);
 }
 
 }  // namespace pisa
@@ -212,8 +310,7 @@ size_t pisa_pyramid_bytes(const pisa_dims* dims, int64_t n_capacity) {
 size_t pisa_workspace_bytes(const pisa_dims* dims, int64_t N, int64_t n_capacity, int32_t is_decode) {
     if (check_dims(dims) != PISA_OK || n_capacity < 1 || (!is_decode && (N < 1 || N > n_capacity))) return 0;
     const int64_t P = pisa_pyramid_nodes(dims, n_capacity);
-    const int64_t walks = is_decode ? (int64_t)dims->B * dims->Hkv : (int64_t)dims->B * N * dims->Hkv;
-    return carve(dims, P, walks, nullptr).bytes;
+    return carve(dims, is_decode ? 1 : N, P, is_decode != 0, nullptr).bytes;
 }
 
 int pisa_build_pyramid(const void* k, int64_t N, int64_t n_capacity, const pisa_dims* dims,
@@ -236,7 +333,7 @@ int pisa_select_prefill(const void* q, const void* k, const float* pyramid, int6
     if (!q || !k || !pyramid || !out_idx) return PISA_ERR_INVALID_ARG;
     Geom G;
     if ((rc = make_geom(dims, N, n_capacity, &G)) != PISA_OK) return rc;
-    const Workspace W = carve(dims, G.P, (int64_t)dims->B * N * dims->Hkv, (char*)workspace);
+    const Workspace W = carve(dims, N, G.P, false, (char*)workspace);
     if (!workspace || ws_bytes < W.bytes) return PISA_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     if (dims->dtype == PISA_DTYPE_BF16)
@@ -253,7 +350,7 @@ int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cach
     if (n_before < 1) return PISA_ERR_INVALID_ARG;
     Geom G;
     if ((rc = make_geom(dims, n_before + 1, n_capacity, &G)) != PISA_OK) return rc;
-    const Workspace W = carve(dims, G.P, (int64_t)dims->B * dims->Hkv, (char*)workspace);
+    const Workspace W = carve(dims, 1, G.P, true, (char*)workspace);
     if (!workspace || ws_bytes < W.bytes) return PISA_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     const unsigned nbh = (unsigned)(dims->B * dims->Hkv);

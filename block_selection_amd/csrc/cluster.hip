@@ -1,0 +1,357 @@
+// cluster.hip -- clustered leaf-level scoring for prefill (gfx950).
+//
+// The leaf level is where the walk spends its work: every candidate leaf needs
+// the exact LSE over its 64 raw keys for each of the group's query heads
+// (reading note "Block Sparse Attention with Log-Linear Complexity", "Scoring:
+// LogSumExp" and section 4.1). The pages' prefill kernel clusters queries that
+// need the same candidate key block so each loaded block is reused (ai4snews
+// summary, second paragraph; reading note section 5.1). Here the cluster is a
+// 16-leaf superblock (1024 keys, 128 KiB of bf16 per KV head, held in LDS) and
+// its group of walks:
+//   1. bucket_pass (count): one incidence per run of a walk's ascending leaf
+//      candidates inside a superblock, counted per bucket (batch, KV head,
+//      superblock, range of query positions) in an LDS histogram;
+//   2. scan_groups: bucket offsets and work items of at most kItemMax entries
+//      of one (batch, KV head, superblock) group;
+//   3. bucket_pass (fill): incidences written as entries at their offsets;
+//   4. leaf_cluster: persistent workgroups take items; a workgroup stages the
+//      superblock's keys in LDS once, then each wavefront takes entries (the
+//      next entry's queries are prefetched while the current one is scored)
+//      and scores every leaf of the entry's mask from LDS;
+//   5. final_topk: per walk, the K best leaf candidates in ascending order.
+// Per incidence the walk's queries (2 KiB) are read once; the keys of a
+// superblock are read from memory once per work item.
+#include "lanes.h"
+
+namespace pisa {
+
+constexpr float kScale2L = 0.125f * 1.4426950408889634f;
+
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
+}
+
+// Counting (fill = 0) or placing (fill = 1) the incidences of one range of kRangeT
+// query positions of batch element blockIdx.y (range blockIdx.x). One incidence per
+// run of a walk's ascending leaf candidates inside a 16-leaf superblock; a walk with
+// at most K candidates has none (its candidates are all kept). The workgroup owns the
+// buckets (b, kvh, sb, r) of its range: an LDS histogram counts them, and in the fill
+// pass the same bins, seeded with the bucket offsets, hand out entry positions.
+// Entry = {walk, leaf mask (bits = leaf offsets in the superblock) | first slot << 16}.
+template <int SL>
+__global__ __launch_bounds__(256) void bucket_pass_kernel(const int32_t* __restrict__ cand,
+                                                          const int32_t* __restrict__ ncand, Geom G,
+                                                          ClusterGeom CG, int64_t NT,
+                                                          uint32_t* __restrict__ counts,
+                                                          const uint32_t* __restrict__ offsets,
+                                                          uint2* __restrict__ entries, int fill) {
+    extern __shared__ uint32_t bins[];
+    constexpr int WPW = 64 / SL;
+    const int r = blockIdx.x, b = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, seg = lane / SL, i = lane % SL;
+    const int K = G.topk, CS = 2 * G.topk;
+    const int nbins = G.Hkv * CG.NSB;
+    for (int x = tid; x < nbins; x += 256) {
+        const int64_t bkt = ((int64_t)b * nbins + x) * CG.NR + r;
+        bins[x] = fill ? offsets[bkt] : 0u;
+    }
+    __syncthreads();
+    const int64_t t_lo = (int64_t)r * kRangeT;
+    const int64_t t_hi = (t_lo + kRangeT < NT) ? t_lo + kRangeT : NT;
+    const int64_t w_lo = ((int64_t)b * NT + t_lo) * G.Hkv, w_hi = ((int64_t)b * NT + t_hi) * G.Hkv;
+    for (int64_t w0 = w_lo + (int64_t)(tid >> 6) * WPW; w0 < w_hi; w0 += 4 * WPW) {
+        const int64_t w = w0 + seg;
+        const bool ok = w < w_hi;
+        const int nc = ok ? ncand[w] : 0;
+        const int leaf = (ok && i < CS && i < nc) ? cand[w * CS + i] : -1;
+        const int kvh = (int)(w % G.Hkv);
+        const int sbv = (leaf >= 0) ? leaf / kSbLeaves : -1;
+        const int prev = shfl_i(sbv, lane > 0 ? lane - 1 : 0);
+        const bool start = nc > K && leaf >= 0 && (i == 0 || prev != sbv);
+        uint32_t m = (leaf >= 0) ? (1u << (leaf % kSbLeaves)) : 0u;
+        if (fill) {
+            // OR of the run's leaf bits into its first lane (candidates ascend, so a run
+            // is a contiguous stretch of lanes with equal superblock)
+#pragma unroll
+            for (int dd = 1; dd < kSbLeaves; dd <<= 1) {
+                const int src = (lane + dd < 64) ? lane + dd : lane;
+                const uint32_t om = (uint32_t)shfl_i((int)m, src);
+                const int osb = shfl_i(sbv, src);
+                if (i + dd < SL && sbv >= 0 && osb == sbv) m |= om;
+            }
+        }
+        if (start) {
+            const uint32_t pos = atomicAdd(&bins[kvh * CG.NSB + sbv], 1u);
+            if (fill) entries[pos] = make_uint2((uint32_t)w, m | ((uint32_t)i << 16));
+        }
+    }
+    __syncthreads();
+    if (!fill) {
+        for (int x = tid; x < nbins; x += 256) counts[((int64_t)b * nbins + x) * CG.NR + r] = bins[x];
+    }
+}
+
+// One workgroup: entry offsets of every bucket (groups (b, kvh, sb) in order, ranges
+// inside a group consecutive) and work items of at most kItemMax entries of one group.
+// meta[0] = number of items, meta[1] = number of entries.
+__global__ __launch_bounds__(1024) void scan_groups_kernel(const uint32_t* __restrict__ counts, ClusterGeom CG,
+                                                           uint32_t* __restrict__ offsets,
+                                                           int4* __restrict__ items,
+                                                           uint32_t* __restrict__ meta) {
+    __shared__ uint32_t s_e[1024], s_i[1024];
+    const int tid = threadIdx.x;
+    const int per = (CG.ngroups + 1023) / 1024;
+    const int lo = tid * per, hi = min(CG.ngroups, lo + per);
+    uint32_t se = 0, si = 0;
+    for (int g = lo; g < hi; ++g) {
+        uint32_t tot = 0;
+        for (int r = 0; r < CG.NR; ++r) tot += counts[(int64_t)g * CG.NR + r];
+        se += tot;
+        si += (tot + kItemMax - 1) / kItemMax;
+    }
+    s_e[tid] = se;
+    s_i[tid] = si;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {       // inclusive Hillis-Steele scan
+        const uint32_t ae = (tid >= d) ? s_e[tid - d] : 0u;
+        const uint32_t ai = (tid >= d) ? s_i[tid - d] : 0u;
+        __syncthreads();
+        s_e[tid] += ae;
+        s_i[tid] += ai;
+        __syncthreads();
+    }
+    uint32_t eoff = s_e[tid] - se, ioff = s_i[tid] - si;
+    for (int g = lo; g < hi; ++g) {
+        const uint32_t g0 = eoff;
+        for (int r = 0; r < CG.NR; ++r) {
+            offsets[(int64_t)g * CG.NR + r] = eoff;
+            eoff += counts[(int64_t)g * CG.NR + r];
+        }
+        const uint32_t tot = eoff - g0;
+        for (uint32_t p = 0; p * kItemMax < tot; ++p)
+            items[ioff++] = make_int4(g, (int)(g0 + p * kItemMax), (int)min((uint32_t)kItemMax, tot - p * kItemMax), 0);
+    }
+    if (tid == 1023) {
+        meta[0] = s_i[1023];
+        meta[1] = s_e[1023];
+    }
+}
+
+template __global__ void bucket_pass_kernel<16>(const int32_t*, const int32_t*, Geom, ClusterGeom, int64_t,
+                                                uint32_t*, const uint32_t*, uint2*, int);
+template __global__ void bucket_pass_kernel<32>(const int32_t*, const int32_t*, Geom, ClusterGeom, int64_t,
+                                                uint32_t*, const uint32_t*, uint2*, int);
+template __global__ void bucket_pass_kernel<64>(const int32_t*, const int32_t*, Geom, ClusterGeom, int64_t,
+                                                uint32_t*, const uint32_t*, uint2*, int);
+
+// LDS image of a superblock: key row r (0..1023) at r*128 bytes, its 16-byte chunk c
+// stored at chunk position c ^ (r & 7) so that the MFMA A-fragment reads of 8
+// consecutive rows hit distinct banks.
+__device__ inline int sb_lds_offset(int r, int chunk) { return r * 128 + ((chunk ^ (r & 7)) << 4); }
+
+// Exact LSE (base 2) over the raw keys <= t of NL leaves (bits = leaf offsets in the
+// superblock) for one walk, summed over the group's heads. The NL leaves are
+// processed side by side so their MFMA and reduction chains overlap.
+template <int NL>
+__device__ inline void score_leaves(const char* lds, int64_t key_base, const int bits[NL], int64_t t,
+                                    const bf16x8 q0, const bf16x8 q1, int n, int gq, int GQ, float out[NL]) {
+    f32x4 acc[NL][4];
+#pragma unroll
+    for (int j = 0; j < NL; ++j)
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau) {
+            const int r = bits[j] * kC + 16 * tau + n;
+            const u32x4 a0 = *reinterpret_cast<const u32x4*>(lds + sb_lds_offset(r, gq));
+            const u32x4 a1 = *reinterpret_cast<const u32x4*>(lds + sb_lds_offset(r, 4 + gq));
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), q0, c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), q1, c, 0, 0, 0);
+            acc[j][tau] = c;
+        }
+    // lane holds keys key0 + 16*tau + 4*gq + r of head n; keys with offset > lim are masked
+    int lim[NL];
+    bool full = true;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        const int64_t l64 = t - (key_base + bits[j] * kC);
+        lim[j] = (l64 >= kC - 1) ? kC - 1 : (int)l64;
+        full = full && (lim[j] == kC - 1);
+    }
+    float mx[NL], s[NL];
+    if (full) {
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) m = fmaxf(m, acc[j][tau][r]);
+            mx[j] = m;
+        }
+#pragma unroll
+        for (int j = 0; j < NL; ++j) mx[j] = cols4_max(mx[j]);
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const float moff = mx[j] * kScale2L;
+            float a = 0.f;
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) a += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[j][tau][r], kScale2L, -moff));
+            s[j] = a;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (16 * tau + 4 * gq + r <= lim[j]) m = fmaxf(m, acc[j][tau][r]);
+            mx[j] = cols4_max(m);
+            const float moff = mx[j] * kScale2L;
+            float a = 0.f;
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[j][tau][r], kScale2L, -moff));
+                    a += (16 * tau + 4 * gq + r <= lim[j]) ? e2 : 0.0f;
+                }
+            s[j] = a;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        const float sj = cols4_sum(s[j]);
+        const float lse2 = mx[j] * kScale2L + __builtin_amdgcn_logf(sj);
+        out[j] = row16_sum((n < GQ) ? lse2 : 0.0f);
+    }
+}
+
+// Scores of every leaf of `mask` for one walk; lane 0 writes them to score_row in
+// mask order (= ascending candidate slots).
+__device__ inline void score_entry(const char* lds, int64_t key_base, uint32_t mask, int64_t t,
+                                   const bf16x8 q0, const bf16x8 q1, int n, int gq, int lane, int GQ,
+                                   float* __restrict__ score_row) {
+    int slot = 0;
+    while (mask) {
+        const int b0 = __builtin_ctz(mask);
+        mask &= mask - 1;
+        if (mask) {
+            const int b1 = __builtin_ctz(mask);
+            mask &= mask - 1;
+            const int bits[2] = {b0, b1};
+            float out[2];
+            score_leaves<2>(lds, key_base, bits, t, q0, q1, n, gq, GQ, out);
+            if (lane == 0) { score_row[slot] = out[0]; score_row[slot + 1] = out[1]; }
+            slot += 2;
+        } else {
+            const int bits[1] = {b0};
+            float out[1];
+            score_leaves<1>(lds, key_base, bits, t, q0, q1, n, gq, GQ, out);
+            if (lane == 0) score_row[slot] = out[0];
+            slot += 1;
+        }
+    }
+}
+
+__device__ inline void load_q(const uint16_t* __restrict__ q, int64_t bt, int Hq, int kvh, int GQ, int n,
+                              int gq, u32x4& qa, u32x4& qb) {
+    qa = {0u, 0u, 0u, 0u};
+    qb = {0u, 0u, 0u, 0u};
+    if (n < GQ) {
+        const uint16_t* qrow = q + (bt * Hq + (int64_t)kvh * GQ + n) * kD;
+        qa = *reinterpret_cast<const u32x4*>(qrow + 8 * gq);
+        qb = *reinterpret_cast<const u32x4*>(qrow + 32 + 8 * gq);
+    }
+}
+
+__global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, Geom G, ClusterGeom CG, int64_t NT,
+    const int4* __restrict__ items, const uint2* __restrict__ entries, const uint32_t* __restrict__ meta,
+    float* __restrict__ score) {
+    extern __shared__ u32x4 lds_u4[];
+    char* lds = reinterpret_cast<char*>(lds_u4);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = kClusterThreads / 64;
+    const int n = lane & 15, gq = lane >> 4;
+    const int CS = 2 * G.topk;
+    const uint32_t n_items = meta[0];
+    const int64_t row_stride = (int64_t)G.Hkv * kD;
+
+    for (uint32_t it = blockIdx.x; it < n_items; it += gridDim.x) {
+        const int4 item = items[it];
+        const int grp = item.x;
+        const int sb = grp % CG.NSB;
+        const int kvh = (grp / CG.NSB) % G.Hkv;
+        const int b = grp / (CG.NSB * G.Hkv);
+        const int64_t key_base = (int64_t)sb * kSbKeys;
+        const uint16_t* kb = k + ((int64_t)b * G.cap * G.Hkv + kvh) * kD;
+        const int e_end = item.y + item.z;
+        // first entry and its queries: issued before the key staging so they overlap it
+        int e = item.y + wave;
+        uint2 ent = (e < e_end) ? entries[e] : make_uint2(0u, 0u);
+        uint2 ent_next = (e + nwaves < e_end) ? entries[e + nwaves] : make_uint2(0u, 0u);
+        u32x4 qa, qb;
+        load_q(q, (int64_t)(ent.x / G.Hkv), G.Hq, kvh, G.GQ, e < e_end ? n : kMaxGroup, gq, qa, qb);
+        __syncthreads();   // the previous item's readers are done with LDS
+        for (int idx = tid; idx < kSbKeys * 8; idx += kClusterThreads) {
+            const int r = idx >> 3, ch = idx & 7;
+            const int64_t key = key_base + r;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (key < G.N) v = *reinterpret_cast<const u32x4*>(kb + key * row_stride + ch * 8);
+            *reinterpret_cast<u32x4*>(lds + sb_lds_offset(r, ch)) = v;
+        }
+        __syncthreads();
+        for (; e < e_end; e += nwaves) {
+            // prefetch: next entry's queries, and the entry after it
+            u32x4 na, nb2;
+            const bool has_next = e + nwaves < e_end;
+            load_q(q, (int64_t)(ent_next.x / G.Hkv), G.Hq, kvh, G.GQ, has_next ? n : kMaxGroup, gq, na, nb2);
+            const uint2 ent_nn = (e + 2 * nwaves < e_end) ? entries[e + 2 * nwaves] : make_uint2(0u, 0u);
+            const int64_t w = ent.x;
+            const int64_t t = (w / G.Hkv) % NT;
+            score_entry(lds, key_base, ent.y & 0xffffu, t, __builtin_bit_cast(bf16x8, qa),
+                        __builtin_bit_cast(bf16x8, qb), n, gq, lane, G.GQ, score + w * CS + (ent.y >> 16));
+            ent = ent_next;
+            ent_next = ent_nn;
+            qa = na;
+            qb = nb2;
+        }
+    }
+}
+
+// Per walk (SLOTS lanes each): at most K candidates are all kept; otherwise the K best
+// by (score desc, index asc). Written in ascending leaf order, -1 padded.
+template <int SLOTS>
+__global__ __launch_bounds__(256) void final_topk_kernel(const int32_t* __restrict__ cand,
+                                                         const int32_t* __restrict__ ncand,
+                                                         const float* __restrict__ score, Geom G,
+                                                         int64_t NT, int32_t* __restrict__ out) {
+    constexpr int WPW = 64 / SLOTS;
+    const int K = G.topk, CS = 2 * G.topk;
+    const int lane = threadIdx.x & 63, seg = lane / SLOTS, i = lane % SLOTS;
+    const int64_t walks = (int64_t)G.B * NT * G.Hkv;
+    const int64_t groups = (walks + WPW - 1) / WPW;
+    for (int64_t grp = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); grp < groups; grp += (int64_t)gridDim.x * 4) {
+        const int64_t w = grp * WPW + seg;
+        const bool ok = w < walks;
+        const int nc = ok ? ncand[w] : 0;
+        const int c = (ok && i < CS) ? cand[w * CS + i] : -1;
+        float s = -INFINITY;
+        if (c >= 0) s = (nc > K) ? score[w * CS + i] : 0.0f;
+        int nd = (c >= 0) ? c : INT_MAX;
+        segment_sort<SLOTS>(s, nd, i);
+        float z = 0.0f;
+        int nd2 = (i < K) ? nd : INT_MAX;
+        segment_sort<SLOTS>(z, nd2, i);
+        if (ok && i < K) out[w * K + i] = (nd2 != INT_MAX) ? nd2 : -1;
+    }
+}
+
+template __global__ void final_topk_kernel<16>(const int32_t*, const int32_t*, const float*, Geom, int64_t, int32_t*);
+template __global__ void final_topk_kernel<32>(const int32_t*, const int32_t*, const float*, Geom, int64_t, int32_t*);
+template __global__ void final_topk_kernel<64>(const int32_t*, const int32_t*, const float*, Geom, int64_t, int32_t*);
+
+}  // namespace pisa

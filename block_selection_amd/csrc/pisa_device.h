@@ -49,12 +49,31 @@ __host__ __device__ inline int64_t covered(int l, int64_t i, int64_t n) {
 // holding the hi and lo bf16 planes of the node (kLdsNodeBytes, padded against
 // bank conflicts).
 constexpr int kLdsNodeBytes = 272;
+constexpr int kUpperThreads = 1024;
+constexpr int kLdsBudgetNodes = 480;     // 480 * 272 B = 127.5 KiB
 struct UpperCfg {
     int32_t j_lo, j_hi;
     int32_t lds_first[kMaxLevels + 1];
     int32_t lds_nodes;
 };
 
+// Clustered leaf scoring (prefill): superblocks of 16 leaves; incidences are
+// bucketed by (batch, KV head, superblock, range of kRangeT query positions), so
+// that each bucket is counted and filled by one workgroup and the entries of one
+// (batch, KV head, superblock) group are contiguous; work items hold at most
+// kItemMax entries of one group.
+constexpr int kSbLeaves = 16;
+constexpr int kSbKeys = kSbLeaves * kC;           // 1024 keys
+constexpr int kRangeT = 2048;                      // query positions per range
+constexpr int kItemMax = 1024;                     // entries per work item
+constexpr int kClusterThreads = 1024;
+constexpr int kSbLdsBytes = kSbKeys * kD * 2;      // 128 KiB of bf16 keys
+struct ClusterGeom {
+    int32_t NR;      // position ranges per batch element
+    int32_t NSB;     // superblocks per KV head
+    int32_t ngroups; // B * Hkv * NSB
+    int32_t nb;      // buckets = ngroups * NR
+};
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

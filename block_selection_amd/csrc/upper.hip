@@ -24,7 +24,7 @@
 //   * The coarsest levels that can be read as children are staged in LDS
 //     once per workgroup; finer levels are gathered from global memory (L2).
 //   * Top-K: bitonic sort inside each segment by (score desc, node asc).
-#include "pisa_device.h"
+#include "lanes.h"
 
 namespace pisa {
 
@@ -45,58 +45,6 @@ __global__ __launch_bounds__(256) void split_planes_kernel(const float* __restri
         const float r = v - __uint_as_float(hi << 16);
         planes[i] = (uint16_t)hi;
         planes[n + i] = (uint16_t)rne_bf16_bits(r);
-    }
-}
-
-// ---------------------------------------------------------------- lane moves --
-
-template <int J>
-__device__ inline int lane_xor(int v) {
-    if constexpr (J == 1) return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
-    else if constexpr (J == 2) return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
-    else if constexpr (J == 8) return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);
-    else if constexpr (J == 4 || J == 16) return __builtin_amdgcn_ds_swizzle(v, 0x1F | (J << 10));
-    else return __shfl_xor(v, J, 64);
-}
-template <int J>
-__device__ inline float lane_xor_f(float v) { return __int_as_float(lane_xor<J>(__float_as_int(v))); }
-
-// Sum over the 16 lanes of a DPP row (all lanes receive it).
-__device__ inline float row16_sum(float v) {
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
-    return v;
-}
-
-// Does (sa, na) come before (sb, nb)? Higher score first, then lower node index.
-__device__ inline bool precedes(float sa, int na, float sb, int nb) {
-    return sa > sb || (sa == sb && na < nb);
-}
-
-template <int J>
-__device__ inline void bitonic_step(float& s, int& nd, int i, int k) {
-    const float so = lane_xor_f<J>(s);
-    const int no = lane_xor<J>(nd);
-    const bool lower = (i & J) == 0;
-    const bool up = (i & k) == 0;
-    const bool self_first = precedes(s, nd, so, no);
-    const bool keep_self = (lower == up) ? self_first : !self_first;
-    if (!keep_self) { s = so; nd = no; }
-}
-
-// Sort (s, nd) inside each segment of SLOTS lanes so that segment lane 0 comes first.
-template <int SLOTS>
-__device__ inline void segment_sort(float& s, int& nd, int i) {
-#pragma unroll
-    for (int k = 2; k <= SLOTS; k <<= 1) {
-        if (k >= 64) { bitonic_step<32>(s, nd, i, k); }
-        if (k >= 32) { bitonic_step<16>(s, nd, i, k); }
-        if (k >= 16) { bitonic_step<8>(s, nd, i, k); }
-        if (k >= 8) { bitonic_step<4>(s, nd, i, k); }
-        if (k >= 4) { bitonic_step<2>(s, nd, i, k); }
-        bitonic_step<1>(s, nd, i, k);
     }
 }
 
@@ -184,11 +132,10 @@ __device__ inline float log2_add_exp2(float a, float b) {
     return m + __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(d));
 }
 
-// Walks for positions t0 + ti, ti in [0, NT), of batch element b and KV head kvh
-// (blockIdx.y = b * Hkv + kvh). Output per walk (index (b*NT + ti)*Hkv + kvh):
+// Walks for positions t0 + ti, ti in [0, NT), of every batch element and KV head. Output per walk (index (b*NT + ti)*Hkv + kvh):
 // cand_out[2K] ascending leaf candidates (-1 padded) and ncand_out = their count.
 template <typename KT, int SLOTS>
-__global__ __launch_bounds__(512) void walk_upper_kernel(const KT* __restrict__ q,
+__global__ __launch_bounds__(kUpperThreads) void walk_upper_kernel(const KT* __restrict__ q,
                                                          const uint16_t* __restrict__ planes,
                                                          const float* __restrict__ pyr, Geom G,
                                                          UpperCfg U, int64_t t0, int64_t NT,
@@ -197,7 +144,20 @@ __global__ __launch_bounds__(512) void walk_upper_kernel(const KT* __restrict__ 
     constexpr int WPW = 64 / SLOTS;
     extern __shared__ u32x4 lds_u4[];
     char* lds = reinterpret_cast<char*>(lds_u4);
-    const int bh = blockIdx.y;
+    // XCD-aware placement: workgroup i runs on XCD i % 8; when B*Hkv divides 8, every
+    // XCD serves a single (batch, KV head), so its L2 holds that head's finer levels only.
+    const int BH = G.B * G.Hkv;
+    const int id = blockIdx.x, nwg = gridDim.x;
+    int bh, peer, npeers;
+    if (BH <= 8 && 8 % BH == 0 && nwg % 8 == 0) {
+        bh = (id % 8) % BH;
+        peer = (id / 8) * (8 / BH) + (id % 8) / BH;
+        npeers = nwg / BH;
+    } else {
+        bh = id % BH;
+        peer = id / BH;
+        npeers = (nwg - bh + BH - 1) / BH;
+    }
     const int b = bh / G.Hkv, kvh = bh % G.Hkv;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
     const int seg = lane / SLOTS, i = lane % SLOTS, gq = lane >> 4, n = lane & 15;
@@ -222,8 +182,7 @@ __global__ __launch_bounds__(512) void walk_upper_kernel(const KT* __restrict__ 
     }
 
     const int64_t ngroups = (NT + WPW - 1) / WPW;
-    for (int64_t grp = (int64_t)blockIdx.x * nwaves + wave; grp < ngroups;
-         grp += (int64_t)gridDim.x * nwaves) {
+    for (int64_t grp = (int64_t)peer * nwaves + wave; grp < ngroups; grp += (int64_t)npeers * nwaves) {
         // queries of the WPW walks of this wavefront
         UpperQ<KT> qf[WPW];
         int64_t tw[WPW];
@@ -317,10 +276,11 @@ __global__ __launch_bounds__(512) void walk_upper_kernel(const KT* __restrict__ 
         leaf = (nd != INT_MAX && i < 2 * K) ? nd : -1;
         const uint64_t lm = ballot(leaf >= 0);
         const uint64_t segm = (SLOTS == 64) ? ~0ull : (((1ull << SLOTS) - 1) << (seg * SLOTS));
+        const int64_t wid = ((int64_t)b * NT + my_ti) * G.Hkv + kvh;
+        const int nc_seg = __popcll(lm & segm);
         if (my_ok && i < 2 * K) {
-            const int64_t wid = ((int64_t)b * NT + my_ti) * G.Hkv + kvh;
             cand_out[wid * (2 * K) + i] = leaf;
-            if (i == 0) ncand_out[wid] = __popcll(lm & segm);
+            if (i == 0) ncand_out[wid] = nc_seg;
         }
     }
 }
