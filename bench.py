@@ -130,7 +130,9 @@ def main():
     ap.add_argument("--workload", default="long256k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--cpu-positions", type=int, default=8192)
+    ap.add_argument("--cpu-positions", type=int, default=65536)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 256 MiB device-to-device copy first (reference kernel for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -191,6 +193,13 @@ def main():
         walk = np.array([e[1].elapsed_time(e[2]) for e in ev])
         return total_ms, build, walk
 
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 268435456 bytes read + 268435456 bytes written")
+        del src, dst
     inp, N, dims, q, k, pyr, out, ws = setup(wl)
     total_ms, build_ms, walk_ms = time_steps(N, dims, q, k, pyr, out, ws, args.steps, args.warmup)
     ms_per_step = total_ms / args.steps

@@ -151,9 +151,11 @@ __device__ inline int sb_lds_offset(int r, int chunk) { return r * 128 + ((chunk
 
 // Exact LSE (base 2) over the raw keys <= t of NL leaves (bits = leaf offsets in the
 // superblock) for one walk, summed over the group's heads. The NL leaves are
-// processed side by side so their MFMA and reduction chains overlap.
+// processed side by side so their MFMA and reduction chains overlap. The sum of
+// 2^x is first taken without a shift; if it overflows or is tiny for any lane the
+// wavefront redoes it shifted by the maximum (the LSE is the same up to rounding).
 template <int NL>
-__device__ inline void score_leaves(const char* lds, int64_t key_base, const int bits[NL], int64_t t,
+__device__ inline void score_leaves(const char* lds, int key_base, const int bits[NL], int t,
                                     const bf16x8 q0, const bf16x8 q1, int n, int gq, int GQ, float out[NL]) {
     f32x4 acc[NL][4];
 #pragma unroll
@@ -173,34 +175,35 @@ __device__ inline void score_leaves(const char* lds, int64_t key_base, const int
     bool full = true;
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-        const int64_t l64 = t - (key_base + bits[j] * kC);
-        lim[j] = (l64 >= kC - 1) ? kC - 1 : (int)l64;
+        lim[j] = min(t - (key_base + bits[j] * kC), kC - 1);
         full = full && (lim[j] == kC - 1);
     }
-    float mx[NL], s[NL];
-    if (full) {
+    float s[NL], shift[NL];
 #pragma unroll
-        for (int j = 0; j < NL; ++j) {
-            float m = -INFINITY;
-#pragma unroll
-            for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) m = fmaxf(m, acc[j][tau][r]);
-            mx[j] = m;
-        }
-#pragma unroll
-        for (int j = 0; j < NL; ++j) mx[j] = cols4_max(mx[j]);
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-            const float moff = mx[j] * kScale2L;
-            float a = 0.f;
+    for (int j = 0; j < NL; ++j) {
+        float a = 0.f;
+        if (full) {
 #pragma unroll
             for (int tau = 0; tau < 4; ++tau)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) a += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[j][tau][r], kScale2L, -moff));
-            s[j] = a;
+                for (int r = 0; r < 4; ++r) a += __builtin_amdgcn_exp2f(acc[j][tau][r] * kScale2L);
+        } else {
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float e2 = __builtin_amdgcn_exp2f(acc[j][tau][r] * kScale2L);
+                    a += (16 * tau + 4 * gq + r <= lim[j]) ? e2 : 0.0f;
+                }
         }
-    } else {
+        s[j] = cols4_sum(a);
+        shift[j] = 0.0f;
+    }
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) bad = bad || !(s[j] < INFINITY && s[j] > 0x1p-100f);
+    if (ballot(bad)) {
+        // rare: shift by the maximum logit of each column
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
             float m = -INFINITY;
@@ -209,8 +212,7 @@ __device__ inline void score_leaves(const char* lds, int64_t key_base, const int
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     if (16 * tau + 4 * gq + r <= lim[j]) m = fmaxf(m, acc[j][tau][r]);
-            mx[j] = cols4_max(m);
-            const float moff = mx[j] * kScale2L;
+            const float moff = cols4_max(m) * kScale2L;
             float a = 0.f;
 #pragma unroll
             for (int tau = 0; tau < 4; ++tau)
@@ -219,20 +221,20 @@ __device__ inline void score_leaves(const char* lds, int64_t key_base, const int
                     const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[j][tau][r], kScale2L, -moff));
                     a += (16 * tau + 4 * gq + r <= lim[j]) ? e2 : 0.0f;
                 }
-            s[j] = a;
+            s[j] = cols4_sum(a);
+            shift[j] = moff;
         }
     }
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-        const float sj = cols4_sum(s[j]);
-        const float lse2 = mx[j] * kScale2L + __builtin_amdgcn_logf(sj);
+        const float lse2 = shift[j] + __builtin_amdgcn_logf(s[j]);
         out[j] = row16_sum((n < GQ) ? lse2 : 0.0f);
     }
 }
 
 // Scores of every leaf of `mask` for one walk; lane 0 writes them to score_row in
 // mask order (= ascending candidate slots).
-__device__ inline void score_entry(const char* lds, int64_t key_base, uint32_t mask, int64_t t,
+__device__ inline void score_entry(const char* lds, int key_base, uint32_t mask, int t,
                                    const bf16x8 q0, const bf16x8 q1, int n, int gq, int lane, int GQ,
                                    float* __restrict__ score_row) {
     int slot = 0;
@@ -272,6 +274,7 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, Geom G, ClusterGeom CG, int64_t NT,
     const int4* __restrict__ items, const uint2* __restrict__ entries, const uint32_t* __restrict__ meta,
     float* __restrict__ score) {
+    static_assert(kItemMax <= 64 * (kClusterThreads / 64), "a wavefront holds its entries in one VGPR pair");
     extern __shared__ u32x4 lds_u4[];
     char* lds = reinterpret_cast<char*>(lds_u4);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = kClusterThreads / 64;
@@ -286,38 +289,48 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
         const int sb = grp % CG.NSB;
         const int kvh = (grp / CG.NSB) % G.Hkv;
         const int b = grp / (CG.NSB * G.Hkv);
-        const int64_t key_base = (int64_t)sb * kSbKeys;
+        const int key_base = sb * kSbKeys;
         const uint16_t* kb = k + ((int64_t)b * G.cap * G.Hkv + kvh) * kD;
-        const int e_end = item.y + item.z;
-        // first entry and its queries: issued before the key staging so they overlap it
-        int e = item.y + wave;
-        uint2 ent = (e < e_end) ? entries[e] : make_uint2(0u, 0u);
-        uint2 ent_next = (e + nwaves < e_end) ? entries[e + nwaves] : make_uint2(0u, 0u);
-        u32x4 qa, qb;
-        load_q(q, (int64_t)(ent.x / G.Hkv), G.Hq, kvh, G.GQ, e < e_end ? n : kMaxGroup, gq, qa, qb);
+        // this wavefront's entries item.y + wave + j*nwaves, j < cnt: lane j holds entry j
+        const int first = item.y + wave;
+        const int cnt = (item.z > wave) ? (item.z - wave + nwaves - 1) / nwaves : 0;
+        const uint2 ev = (lane < cnt) ? entries[first + lane * nwaves] : make_uint2(0u, 0u);
+        // queries of the first three entries, in flight during the key staging
+        u32x4 qa0, qb0, qa1, qb1, qa2, qb2;
+        auto qload = [&](int j, u32x4& qa, u32x4& qb) {
+            const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)ev.x, j);
+            load_q(q, (int64_t)(w / (uint32_t)G.Hkv), G.Hq, kvh, G.GQ, j < cnt ? n : kMaxGroup, gq, qa, qb);
+        };
+        qload(0, qa0, qb0);
+        qload(1, qa1, qb1);
+        qload(2, qa2, qb2);
         __syncthreads();   // the previous item's readers are done with LDS
         for (int idx = tid; idx < kSbKeys * 8; idx += kClusterThreads) {
             const int r = idx >> 3, ch = idx & 7;
-            const int64_t key = key_base + r;
+            const int key = key_base + r;
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (key < G.N) v = *reinterpret_cast<const u32x4*>(kb + key * row_stride + ch * 8);
+            if (key < G.N) v = *reinterpret_cast<const u32x4*>(kb + (int64_t)key * row_stride + ch * 8);
             *reinterpret_cast<u32x4*>(lds + sb_lds_offset(r, ch)) = v;
         }
         __syncthreads();
-        for (; e < e_end; e += nwaves) {
-            // prefetch: next entry's queries, and the entry after it
-            u32x4 na, nb2;
-            const bool has_next = e + nwaves < e_end;
-            load_q(q, (int64_t)(ent_next.x / G.Hkv), G.Hq, kvh, G.GQ, has_next ? n : kMaxGroup, gq, na, nb2);
-            const uint2 ent_nn = (e + 2 * nwaves < e_end) ? entries[e + 2 * nwaves] : make_uint2(0u, 0u);
-            const int64_t w = ent.x;
-            const int64_t t = (w / G.Hkv) % NT;
-            score_entry(lds, key_base, ent.y & 0xffffu, t, __builtin_bit_cast(bf16x8, qa),
-                        __builtin_bit_cast(bf16x8, qb), n, gq, lane, G.GQ, score + w * CS + (ent.y >> 16));
-            ent = ent_next;
-            ent_next = ent_nn;
-            qa = na;
-            qb = nb2;
+        auto process = [&](int j, const u32x4& qa, const u32x4& qb) {
+            const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)ev.x, j);
+            const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)ev.y, j);
+            const int t = (int)((w / (uint32_t)G.Hkv) % (uint32_t)NT);
+            score_entry(lds, key_base, y & 0xffffu, t, __builtin_bit_cast(bf16x8, qa), __builtin_bit_cast(bf16x8, qb),
+                        n, gq, lane, G.GQ, score + (int64_t)w * CS + (y >> 16));
+        };
+        for (int j = 0; j < cnt; j += 3) {
+            process(j, qa0, qb0);
+            qload(j + 3 < 64 ? j + 3 : 63, qa0, qb0);
+            if (j + 1 < cnt) {
+                process(j + 1, qa1, qb1);
+                qload(j + 4 < 64 ? j + 4 : 63, qa1, qb1);
+            }
+            if (j + 2 < cnt) {
+                process(j + 2, qa2, qb2);
+                qload(j + 5 < 64 ? j + 5 : 63, qa2, qb2);
+            }
         }
     }
 }

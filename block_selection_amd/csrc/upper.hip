@@ -85,6 +85,7 @@ struct UpperQ<float> {
 __device__ inline f32x4 child_tile_bf16(const UpperQ<uint16_t>& q, const uint16_t* __restrict__ planes,
                                         int64_t plane_stride, int64_t row_elem, const char* lds,
                                         int lds_node, bool valid, int gq) {
+    // planes: hi plane of this level; the lo plane is plane_stride elements further
     u32x4 h0 = {0u, 0u, 0u, 0u}, h1 = h0, l0 = h0, l1 = h0;
     if (valid) {
         if (lds_node >= 0) {
@@ -205,9 +206,9 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_kernel(const KT* __r
                 cand = surv;
             } else {
                 const int par = shfl_i(surv, seg * SLOTS + (i >> 1));
-                const int64_t child = 2 * (int64_t)par + (i & 1);
-                const bool ok = i < 2 * K && par >= 0 && child < G.M[l] && first_key(l, child) <= my_t;
-                cand = ok ? (int)child : -1;
+                const int child = 2 * par + (i & 1);
+                const bool ok = i < 2 * K && par >= 0 && child < G.M[l] && child <= (int)(my_t >> (kLog2C + l - 1));
+                cand = ok ? child : -1;
             }
             // does any walk of this wavefront have more than K candidates here?
             const uint64_t vm = ballot(cand >= 0);
@@ -220,30 +221,34 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_kernel(const KT* __r
             float my = (cand >= 0) ? 0.0f : -INFINITY;
             if (need) {
                 const int lc = l - 1;
-                const int64_t Mc = G.M[lc];
+                const int Mc = G.M[lc];
+                const int sh = kLog2C + lc - 1;              // first key of node i at level lc: i << sh
                 const bool in_lds = (sizeof(KT) == 2) && lc >= U.j_lo && lc <= U.j_hi;
+                const uint16_t* plane_lvl = planes + (bh_row0 + G.off[lc]) * kD;
+                const float* pyr_lvl = pyr + (bh_row0 + G.off[lc]) * kD;
+                const int lds_lvl = in_lds ? U.lds_first[lc] : 0;
 #pragma unroll
                 for (int w = 0; w < WPW; ++w) {
+                    const int tl = (int)(tw[w] >> sh);         // children <= tl are eligible
 #pragma unroll
                     for (int tau = 0; tau < SLOTS / 8; ++tau) {
                         const int cs = 16 * tau + n;                 // child slot of this MFMA row
                         const int par = shfl_i(cand, w * SLOTS + (cs >> 1));
-                        const int64_t child = 2 * (int64_t)par + (cs & 1);
-                        const bool valid = par >= 0 && child < Mc && first_key(lc, child) <= tw[w];
+                        const int child = 2 * par + (cs & 1);
+                        const bool valid = par >= 0 && child < Mc && child <= tl;
                         f32x4 acc;
                         if constexpr (sizeof(KT) == 2) {
-                            acc = child_tile_bf16(qf[w], planes, plane_stride,
-                                                  (bh_row0 + G.off[lc] + child) * kD, lds,
-                                                  in_lds ? U.lds_first[lc] + (int)child : -1, valid, gq);
+                            acc = child_tile_bf16(qf[w], plane_lvl, plane_stride, (int64_t)child * kD, lds,
+                                                  in_lds ? lds_lvl + child : -1, valid, gq);
                         } else {
-                            acc = child_tile_f32(qf[w], pyr + (bh_row0 + G.off[lc] + child) * kD, valid, gq);
+                            acc = child_tile_f32(qf[w], pyr_lvl + (int64_t)child * kD, valid, gq);
                         }
                         float sc[2];
 #pragma unroll
                         for (int p = 0; p < 2; ++p) {
                             const int pp = shfl_i(cand, w * SLOTS + 8 * tau + 2 * gq + p);
-                            const int64_t right = 2 * (int64_t)pp + 1;
-                            const bool has_right = pp >= 0 && right < Mc && first_key(lc, right) <= tw[w];
+                            const int right = 2 * pp + 1;
+                            const bool has_right = pp >= 0 && right < Mc && right <= tl;
                             const float lse2 = has_right ? log2_add_exp2(acc[2 * p], acc[2 * p + 1]) : acc[2 * p];
                             const float s = row16_sum(n < G.GQ ? lse2 : 0.0f);
                             sc[p] = (pp >= 0) ? s : -INFINITY;
@@ -265,9 +270,9 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_kernel(const KT* __r
             leaf = surv;
         } else {
             const int par = shfl_i(surv, seg * SLOTS + (i >> 1));
-            const int64_t child = 2 * (int64_t)par + (i & 1);
-            const bool ok = i < 2 * K && par >= 0 && child < G.M[1] && first_key(1, child) <= my_t;
-            leaf = ok ? (int)child : -1;
+            const int child = 2 * par + (i & 1);
+            const bool ok = i < 2 * K && par >= 0 && child < G.M[1] && child <= (int)(my_t >> kLog2C);
+            leaf = ok ? child : -1;
         }
         // ascending order, -1 last (equal scores: lower index first)
         float zero = 0.0f;
