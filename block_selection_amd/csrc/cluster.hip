@@ -155,7 +155,7 @@ __device__ inline int sb_lds_offset(int r, int chunk) { return r * 128 + ((chunk
 // 2^x is first taken without a shift; if it overflows or is tiny for any lane the
 // wavefront redoes it shifted by the maximum (the LSE is the same up to rounding).
 template <int NL>
-__device__ inline void score_leaves(const char* lds, int key_base, const int bits[NL], int t,
+__device__ inline void score_leaves(const lds_char_t* lds, int key_base, const int bits[NL], int t,
                                     const bf16x8 q0, const bf16x8 q1, int n, int gq, int GQ, float out[NL]) {
     f32x4 acc[NL][4];
 #pragma unroll
@@ -163,8 +163,8 @@ __device__ inline void score_leaves(const char* lds, int key_base, const int bit
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
             const int r = bits[j] * kC + 16 * tau + n;
-            const u32x4 a0 = *reinterpret_cast<const u32x4*>(lds + sb_lds_offset(r, gq));
-            const u32x4 a1 = *reinterpret_cast<const u32x4*>(lds + sb_lds_offset(r, 4 + gq));
+            const u32x4 a0 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, gq));
+            const u32x4 a1 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, 4 + gq));
             f32x4 c = {0.f, 0.f, 0.f, 0.f};
             c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), q0, c, 0, 0, 0);
             c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), q1, c, 0, 0, 0);
@@ -234,7 +234,7 @@ __device__ inline void score_leaves(const char* lds, int key_base, const int bit
 
 // Scores of every leaf of `mask` for one walk; lane 0 writes them to score_row in
 // mask order (= ascending candidate slots).
-__device__ inline void score_entry(const char* lds, int key_base, uint32_t mask, int t,
+__device__ inline void score_entry(const lds_char_t* lds, int key_base, uint32_t mask, int t,
                                    const bf16x8 q0, const bf16x8 q1, int n, int gq, int lane, int GQ,
                                    float* __restrict__ score_row) {
     int slot = 0;
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
     float* __restrict__ score) {
     static_assert(kItemMax <= 64 * (kClusterThreads / 64), "a wavefront holds its entries in one VGPR pair");
     extern __shared__ u32x4 lds_u4[];
-    char* lds = reinterpret_cast<char*>(lds_u4);
+    lds_char_t* lds = (lds_char_t*)lds_u4;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = kClusterThreads / 64;
     const int n = lane & 15, gq = lane >> 4;
     const int CS = 2 * G.topk;
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
             const int key = key_base + r;
             u32x4 v = {0u, 0u, 0u, 0u};
             if (key < G.N) v = *reinterpret_cast<const u32x4*>(kb + (int64_t)key * row_stride + ch * 8);
-            *reinterpret_cast<u32x4*>(lds + sb_lds_offset(r, ch)) = v;
+            *reinterpret_cast<lds_u32x4_t*>(lds + sb_lds_offset(r, ch)) = v;
         }
         __syncthreads();
         auto process = [&](int j, const u32x4& qa, const u32x4& qb) {

@@ -81,27 +81,9 @@ struct UpperQ<float> {
     }
 };
 
-// Base-2 logits of one 16-row tile of children (row = lane % 16) against the query.
-__device__ inline f32x4 child_tile_bf16(const UpperQ<uint16_t>& q, const uint16_t* __restrict__ planes,
-                                        int64_t plane_stride, int64_t row_elem, const char* lds,
-                                        int lds_node, bool valid, int gq) {
-    // planes: hi plane of this level; the lo plane is plane_stride elements further
-    u32x4 h0 = {0u, 0u, 0u, 0u}, h1 = h0, l0 = h0, l1 = h0;
-    if (valid) {
-        if (lds_node >= 0) {
-            const char* p = lds + (int64_t)lds_node * kLdsNodeBytes;
-            h0 = *reinterpret_cast<const u32x4*>(p + 16 * gq);
-            h1 = *reinterpret_cast<const u32x4*>(p + 64 + 16 * gq);
-            l0 = *reinterpret_cast<const u32x4*>(p + 128 + 16 * gq);
-            l1 = *reinterpret_cast<const u32x4*>(p + 192 + 16 * gq);
-        } else {
-            const uint16_t* p = planes + row_elem;
-            h0 = *reinterpret_cast<const u32x4*>(p + 8 * gq);
-            h1 = *reinterpret_cast<const u32x4*>(p + 32 + 8 * gq);
-            l0 = *reinterpret_cast<const u32x4*>(p + plane_stride + 8 * gq);
-            l1 = *reinterpret_cast<const u32x4*>(p + plane_stride + 32 + 8 * gq);
-        }
-    }
+// Base-2 logits of one 16-row tile of children (row = lane % 16) against the query:
+// hi and lo planes, two k-steps each.
+__device__ inline f32x4 child_tile_mfma(const UpperQ<uint16_t>& q, u32x4 h0, u32x4 h1, u32x4 l0, u32x4 l1) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h0), q.k0, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h1), q.k1, acc, 0, 0, 0);
@@ -110,15 +92,30 @@ __device__ inline f32x4 child_tile_bf16(const UpperQ<uint16_t>& q, const uint16_
     return acc;
 }
 
-__device__ inline f32x4 child_tile_f32(const UpperQ<float>& q, const float* __restrict__ pyr_row,
-                                       bool valid, int gq) {
+// Row from the LDS-staged coarse levels (node slot lds_node).
+__device__ inline f32x4 child_tile_lds(const UpperQ<uint16_t>& q, const lds_char_t* lds, int lds_node, int gq) {
+    const lds_char_t* p = lds + lds_node * kLdsNodeBytes;
+    const u32x4 h0 = *reinterpret_cast<const lds_u32x4_t*>(p + 16 * gq);
+    const u32x4 h1 = *reinterpret_cast<const lds_u32x4_t*>(p + 64 + 16 * gq);
+    const u32x4 l0 = *reinterpret_cast<const lds_u32x4_t*>(p + 128 + 16 * gq);
+    const u32x4 l1 = *reinterpret_cast<const lds_u32x4_t*>(p + 192 + 16 * gq);
+    return child_tile_mfma(q, h0, h1, l0, l1);
+}
+
+// Row from global memory (hi plane at `plane`, lo plane plane_stride elements further).
+__device__ inline f32x4 child_tile_global(const UpperQ<uint16_t>& q, const uint16_t* __restrict__ plane,
+                                          int64_t plane_stride, int gq) {
+    const u32x4 h0 = *reinterpret_cast<const u32x4*>(plane + 8 * gq);
+    const u32x4 h1 = *reinterpret_cast<const u32x4*>(plane + 32 + 8 * gq);
+    const u32x4 l0 = *reinterpret_cast<const u32x4*>(plane + plane_stride + 8 * gq);
+    const u32x4 l1 = *reinterpret_cast<const u32x4*>(plane + plane_stride + 32 + 8 * gq);
+    return child_tile_mfma(q, h0, h1, l0, l1);
+}
+
+__device__ inline f32x4 child_tile_f32(const UpperQ<float>& q, const float* __restrict__ pyr_row, int gq) {
     float a[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) a[i] = 0.f;
-    if (valid) {
-        load8_f32(pyr_row + 8 * gq, a);
-        load8_f32(pyr_row + 32 + 8 * gq, a + 8);
-    }
+    load8_f32(pyr_row + 8 * gq, a);
+    load8_f32(pyr_row + 32 + 8 * gq, a + 8);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 16; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], q.f[s], acc, 0, 0, 0);
@@ -133,8 +130,65 @@ __device__ inline float log2_add_exp2(float a, float b) {
     return m + __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(d));
 }
 
-// Walks for positions t0 + ti, ti in [0, NT), of every batch element and KV head. Output per walk (index (b*NT + ti)*Hkv + kvh):
-// cand_out[2K] ascending leaf candidates (-1 padded) and ncand_out = their count.
+// ------------------------------------------------------------- tile layout --
+// Candidate slot m (0 <= m < SLOTS) of walk w of a wavefront lives in lane
+//   16 * g + (SLOTS/4) * w + 2 * tau + p,   with m = 8 * tau + 2 * g + p.
+// A 16-row MFMA tile tau of walk w holds children 2m, 2m+1 of slots m = 8 tau .. 8 tau + 7
+// in rows 2(m - 8 tau) and 2(m - 8 tau) + 1; the result lane (g, n) holds rows 4g .. 4g+3,
+// i.e. both children of slots 8 tau + 2g and 8 tau + 2g + 1: the slots whose home lanes
+// are in the same 16-lane row g. After the sum over the head columns a candidate's
+// score is present in its home row, so it is taken by a select, without a lane move.
+// Flipping bit J of the slot index moves between lanes lane ^ slot_bit_lane(J).
+template <int SLOTS>
+__device__ constexpr int slot_lane(int w, int m) {
+    return 16 * ((m >> 1) & 3) + (SLOTS / 4) * w + 2 * (m >> 3) + (m & 1);
+}
+constexpr int slot_bit_lane(int J) { return J == 1 ? 1 : J == 2 ? 16 : J == 4 ? 32 : J == 8 ? 2 : J == 16 ? 4 : 8; }
+
+// value of lane (lane ^ X) for the lane offsets used by the tile layout
+template <int X>
+__device__ inline int tile_xor(int v) {
+    if constexpr (X == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+        return (int)(((threadIdx.x >> 4) & 1) ? r[0] : r[1]);
+    } else if constexpr (X == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+        return (int)(((threadIdx.x >> 5) & 1) ? r[0] : r[1]);
+    } else {
+        return lane_xor<X>(v);
+    }
+}
+
+template <int J>
+__device__ inline void tile_bitonic_step(float& s, int& nd, int m, int k) {
+    constexpr int X = slot_bit_lane(J);
+    const float so = __int_as_float(tile_xor<X>(__float_as_int(s)));
+    const int no = tile_xor<X>(nd);
+    const bool lower = (m & J) == 0;
+    const bool up = (m & k) == 0;
+    const bool self_first = precedes(s, nd, so, no);
+    const bool keep_self = (lower == up) ? self_first : !self_first;
+    if (!keep_self) { s = so; nd = no; }
+}
+
+// Bitonic sort of each walk's SLOTS slots in tile layout (m = this lane's slot):
+// afterwards slot 0 holds the element that precedes all others.
+template <int SLOTS>
+__device__ inline void tile_sort(float& s, int& nd, int m) {
+#pragma unroll
+    for (int k = 2; k <= SLOTS; k <<= 1) {
+        if (k >= 64) { tile_bitonic_step<32>(s, nd, m, k); }
+        if (k >= 32) { tile_bitonic_step<16>(s, nd, m, k); }
+        if (k >= 16) { tile_bitonic_step<8>(s, nd, m, k); }
+        if (k >= 8) { tile_bitonic_step<4>(s, nd, m, k); }
+        if (k >= 4) { tile_bitonic_step<2>(s, nd, m, k); }
+        tile_bitonic_step<1>(s, nd, m, k);
+    }
+}
+
+// Walks for positions t0 + ti, ti in [0, NT), of every batch element and KV head.
+// Output per walk (index (b*NT + ti)*Hkv + kvh): cand_out[2K] ascending leaf
+// candidates (-1 padded) and ncand_out = their count.
 template <typename KT, int SLOTS>
 __global__ __launch_bounds__(kUpperThreads) void walk_upper_kernel(const KT* __restrict__ q,
                                                          const uint16_t* __restrict__ planes,
@@ -142,9 +196,9 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_kernel(const KT* __r
                                                          UpperCfg U, int64_t t0, int64_t NT,
                                                          int32_t* __restrict__ cand_out,
                                                          int32_t* __restrict__ ncand_out) {
-    constexpr int WPW = 64 / SLOTS;
+    constexpr int WPW = 64 / SLOTS, QW = SLOTS / 4;
     extern __shared__ u32x4 lds_u4[];
-    char* lds = reinterpret_cast<char*>(lds_u4);
+    lds_char_t* lds = (lds_char_t*)lds_u4;
     // XCD-aware placement: workgroup i runs on XCD i % 8; when B*Hkv divides 8, every
     // XCD serves a single (batch, KV head), so its L2 holds that head's finer levels only.
     const int BH = G.B * G.Hkv;
@@ -161,25 +215,36 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_kernel(const KT* __r
     }
     const int b = bh / G.Hkv, kvh = bh % G.Hkv;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-    const int seg = lane / SLOTS, i = lane % SLOTS, gq = lane >> 4, n = lane & 15;
+    const int gq = lane >> 4, n = lane & 15;
+    const int wl = n / QW, ql = n % QW;                       // this lane's walk and position in its row
+    const int ml = 8 * (ql >> 1) + 2 * gq + (ql & 1);         // this lane's candidate slot
     const int K = G.topk;
     const int64_t plane_stride = (int64_t)G.B * G.Hkv * G.P * kD;
     const int64_t bh_row0 = (int64_t)bh * G.P;
 
-    // stage the coarse levels: node j-level i -> LDS slot lds_first[j] + i, planes hi|lo
+    // stage the coarse levels: node i of level j -> LDS slot lds_first[j] + i, planes hi|lo
     if constexpr (sizeof(KT) == 2) {
         for (int j = U.j_lo; j <= U.j_hi; ++j) {
-            const int m = G.M[j];
-            for (int c = threadIdx.x; c < m * 16; c += blockDim.x) {
+            const int mj = G.M[j];
+            for (int c = threadIdx.x; c < mj * 16; c += blockDim.x) {
                 const int node = c >> 4, part = c & 15;        // part: plane (part>>3), 16-B chunk (part&7)
                 const uint16_t* src = planes + (part >> 3) * plane_stride +
                                       (bh_row0 + G.off[j] + node) * kD + (part & 7) * 8;
-                *reinterpret_cast<u32x4*>(lds + (int64_t)(U.lds_first[j] + node) * kLdsNodeBytes +
-                                          (part >> 3) * 128 + (part & 7) * 16) =
+                *reinterpret_cast<lds_u32x4_t*>(lds + (U.lds_first[j] + node) * kLdsNodeBytes +
+                                                (part >> 3) * 128 + (part & 7) * 16) =
                     *reinterpret_cast<const u32x4*>(src);
             }
         }
         __syncthreads();
+    }
+
+    // lanes of walk w: bits of a wavefront mask
+    uint64_t wmask[WPW];
+#pragma unroll
+    for (int w = 0; w < WPW; ++w) {
+        uint64_t mk = 0;
+        for (int m = 0; m < SLOTS; ++m) mk |= 1ull << slot_lane<SLOTS>(w, m);
+        wmask[w] = mk;
     }
 
     const int64_t ngroups = (NT + WPW - 1) / WPW;
@@ -195,29 +260,26 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_kernel(const KT* __r
             const KT* qrow = q + (((int64_t)b * NT + (ti < NT ? ti : 0)) * G.Hq + (int64_t)kvh * G.GQ + n) * kD;
             qf[w].load(qrow, ok, gq);
         }
-        const int64_t my_ti = grp * WPW + seg;
+        const int64_t my_ti = grp * WPW + wl;
         const int64_t my_t = t0 + my_ti;
         const bool my_ok = my_ti < NT;
 
-        int surv = (i == 0 && my_ok) ? 0 : -1;   // survivors of the level above, segment lanes 0..K-1
+        int surv = (ml == 0 && my_ok) ? 0 : -1;   // survivors of the level above, slots 0..K-1
         for (int l = G.L; l >= 2; --l) {
             int cand;
             if (l == G.L) {
                 cand = surv;
             } else {
-                const int par = shfl_i(surv, seg * SLOTS + (i >> 1));
-                const int child = 2 * par + (i & 1);
-                const bool ok = i < 2 * K && par >= 0 && child < G.M[l] && child <= (int)(my_t >> (kLog2C + l - 1));
+                const int par = shfl_i(surv, slot_lane<SLOTS>(wl, ml >> 1));
+                const int child = 2 * par + (ml & 1);
+                const bool ok = ml < 2 * K && par >= 0 && child < G.M[l] && child <= (int)(my_t >> (kLog2C + l - 1));
                 cand = ok ? child : -1;
             }
             // does any walk of this wavefront have more than K candidates here?
             const uint64_t vm = ballot(cand >= 0);
             bool need = false;
 #pragma unroll
-            for (int w = 0; w < WPW; ++w) {
-                const uint64_t segm = (SLOTS == 64) ? ~0ull : (((1ull << SLOTS) - 1) << (w * SLOTS));
-                need |= __popcll(vm & segm) > K;
-            }
+            for (int w = 0; w < WPW; ++w) need |= __popcll(vm & wmask[w]) > K;
             float my = (cand >= 0) ? 0.0f : -INFINITY;
             if (need) {
                 const int lc = l - 1;
@@ -232,60 +294,60 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_kernel(const KT* __r
                     const int tl = (int)(tw[w] >> sh);         // children <= tl are eligible
 #pragma unroll
                     for (int tau = 0; tau < SLOTS / 8; ++tau) {
-                        const int cs = 16 * tau + n;                 // child slot of this MFMA row
-                        const int par = shfl_i(cand, w * SLOTS + (cs >> 1));
-                        const int child = 2 * par + (cs & 1);
+                        // MFMA row n: child (n & 1) of slot 8 tau + n/2
+                        const int par = shfl_i(cand, slot_lane<SLOTS>(w, 8 * tau + (n >> 1)));
+                        const int child = 2 * par + (n & 1);
                         const bool valid = par >= 0 && child < Mc && child <= tl;
+                        const int row = valid ? child : 0;      // invalid rows read row 0; their results are unused
+                        const uint32_t rows_ok = (uint32_t)ballot(valid);   // bit r: row r valid
                         f32x4 acc;
                         if constexpr (sizeof(KT) == 2) {
-                            acc = child_tile_bf16(qf[w], plane_lvl, plane_stride, (int64_t)child * kD, lds,
-                                                  in_lds ? lds_lvl + child : -1, valid, gq);
+                            if (in_lds) acc = child_tile_lds(qf[w], lds, lds_lvl + row, gq);
+                            else acc = child_tile_global(qf[w], plane_lvl + (int64_t)row * kD, plane_stride, gq);
                         } else {
-                            acc = child_tile_f32(qf[w], pyr_lvl + (int64_t)child * kD, valid, gq);
+                            acc = child_tile_f32(qf[w], pyr_lvl + (int64_t)row * kD, gq);
                         }
                         float sc[2];
 #pragma unroll
                         for (int p = 0; p < 2; ++p) {
-                            const int pp = shfl_i(cand, w * SLOTS + 8 * tau + 2 * gq + p);
-                            const int right = 2 * pp + 1;
-                            const bool has_right = pp >= 0 && right < Mc && right <= tl;
-                            const float lse2 = has_right ? log2_add_exp2(acc[2 * p], acc[2 * p + 1]) : acc[2 * p];
-                            const float s = row16_sum(n < G.GQ ? lse2 : 0.0f);
-                            sc[p] = (pp >= 0) ? s : -INFINITY;
+                            const bool lv = (rows_ok >> (4 * gq + 2 * p)) & 1u;       // candidate exists
+                            const bool rv = (rows_ok >> (4 * gq + 2 * p + 1)) & 1u;   // its right child counts
+                            const float lse2 = rv ? log2_add_exp2(acc[2 * p], acc[2 * p + 1]) : acc[2 * p];
+                            const float sm = row16_sum(n < G.GQ ? lse2 : 0.0f);
+                            sc[p] = lv ? sm : -INFINITY;
                         }
-                        const int src = 16 * ((i & 7) >> 1);
-                        const float v0 = shfl_f(sc[0], src), v1 = shfl_f(sc[1], src);
-                        if (seg == w && (i >> 3) == tau) my = (i & 1) ? v1 : v0;
+                        if (wl == w && (ql >> 1) == tau) my = (ql & 1) ? sc[1] : sc[0];
                     }
                 }
                 if (cand < 0) my = -INFINITY;
             }
             int nd = (cand >= 0) ? cand : INT_MAX;
-            segment_sort<SLOTS>(my, nd, i);
-            surv = (i < K && nd != INT_MAX) ? nd : -1;
+            tile_sort<SLOTS>(my, nd, ml);
+            surv = (ml < K && nd != INT_MAX) ? nd : -1;
         }
         // leaf candidates: children of the level-2 survivors (or the root if it is a leaf)
         int leaf;
         if (G.L == 1) {
             leaf = surv;
         } else {
-            const int par = shfl_i(surv, seg * SLOTS + (i >> 1));
-            const int child = 2 * par + (i & 1);
-            const bool ok = i < 2 * K && par >= 0 && child < G.M[1] && child <= (int)(my_t >> kLog2C);
+            const int par = shfl_i(surv, slot_lane<SLOTS>(wl, ml >> 1));
+            const int child = 2 * par + (ml & 1);
+            const bool ok = ml < 2 * K && par >= 0 && child < G.M[1] && child <= (int)(my_t >> kLog2C);
             leaf = ok ? child : -1;
         }
         // ascending order, -1 last (equal scores: lower index first)
         float zero = 0.0f;
         int nd = (leaf >= 0) ? leaf : INT_MAX;
-        segment_sort<SLOTS>(zero, nd, i);
-        leaf = (nd != INT_MAX && i < 2 * K) ? nd : -1;
+        tile_sort<SLOTS>(zero, nd, ml);
+        leaf = (nd != INT_MAX && ml < 2 * K) ? nd : -1;
         const uint64_t lm = ballot(leaf >= 0);
-        const uint64_t segm = (SLOTS == 64) ? ~0ull : (((1ull << SLOTS) - 1) << (seg * SLOTS));
-        const int64_t wid = ((int64_t)b * NT + my_ti) * G.Hkv + kvh;
-        const int nc_seg = __popcll(lm & segm);
-        if (my_ok && i < 2 * K) {
-            cand_out[wid * (2 * K) + i] = leaf;
-            if (i == 0) ncand_out[wid] = nc_seg;
+        uint64_t mine = 0;
+#pragma unroll
+        for (int w = 0; w < WPW; ++w) mine = (wl == w) ? wmask[w] : mine;
+        if (my_ok && ml < 2 * K) {
+            const int64_t wid = ((int64_t)b * NT + my_ti) * G.Hkv + kvh;
+            cand_out[wid * (2 * K) + ml] = leaf;
+            if (ml == 0) ncand_out[wid] = __popcll(lm & mine);
         }
     }
 }
