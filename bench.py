@@ -15,6 +15,7 @@ step. Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -42,10 +43,11 @@ def walk_counts(N: int, topk: int, GQ: int, Hkv: int, C: int = 64):
     For each position t the number of candidates at level l is the eligible
     children of min(K, eligible-at-level-above) survivors, capped by the
     eligible node count; a level is scored only when it has more than K.
-    Each scored upper candidate costs (eligible children) logits per head, each
-    scored leaf its eligible raw keys per head. Returns (logits, lse_terms,
-    fetched_bytes) summed over all walks; the count assumes the causal
-    frontier node survives (exact for full-depth walks).
+    A scored upper candidate costs (eligible children) logits per head, a scored
+    leaf its eligible raw keys per head; every scored candidate costs one LSE
+    (one log) per head. The count assumes the causal frontier node survives
+    (exact for full-depth walks). Returns a dict of totals over all walks:
+    leaf_logits, leaf_lse, upper_logits, upper_lse, leaf_pairs.
     """
     t = np.arange(N, dtype=np.int64)
     sizes, span = [], C
@@ -56,8 +58,7 @@ def walk_counts(N: int, topk: int, GQ: int, Hkv: int, C: int = 64):
             break
         m, span = -(-m // 2), span * 2
     L = len(sizes)
-    logits = np.zeros(N, np.float64)
-    lse = np.zeros(N, np.float64)
+    out = dict(leaf_logits=0.0, leaf_lse=0.0, upper_logits=0.0, upper_lse=0.0, leaf_pairs=0.0)
     surv = np.ones(N, np.int64)
     for l in range(L, 0, -1):
         M, sp = sizes[l - 1]
@@ -65,28 +66,28 @@ def walk_counts(N: int, topk: int, GQ: int, Hkv: int, C: int = 64):
         cand = np.ones(N, np.int64) if l == L else np.minimum(2 * surv, elig)
         scored = cand > topk
         if l >= 2:
-            # candidates have two children except the frontier one when its right child is ineligible
             child_elig = np.minimum(sizes[l - 2][0], t // sizes[l - 2][1] + 1)
             n_children = np.minimum(2 * cand, child_elig)
-            logits += np.where(scored, n_children, 0) * GQ
+            out["upper_logits"] += float(np.where(scored, n_children, 0).sum()) * GQ * Hkv
+            out["upper_lse"] += float(np.where(scored, cand, 0).sum()) * GQ * Hkv
         else:
             keys = np.minimum(cand * C, t + 1)
-            logits += np.where(scored, keys, 0) * GQ
-        lse += np.where(scored, cand, 0) * GQ
+            out["leaf_logits"] += float(np.where(scored, keys, 0).sum()) * GQ * Hkv
+            out["leaf_lse"] += float(np.where(scored, cand, 0).sum()) * GQ * Hkv
+            out["leaf_pairs"] += float(np.where(scored, cand, 0).sum()) * Hkv
         surv = np.where(scored, topk, cand)
-    return float(logits.sum() * Hkv), float(lse.sum() * Hkv)
+    return out
 
 
-def roofline_peaks():
-    path = os.path.join(PROFILES, "device_peaks.json")
-    if os.path.exists(path):
-        with open(path) as f:
-            return json.load(f)
-    return None
+# MI355X transcendental peak: 256 CUs x 32 lanes/clock (v_exp_f32 / v_log_f32 issue at half the
+# 64-lane VALU rate) x 2.4 GHz
+TRANSCENDENTAL_PEAK = 256 * 32 * 2.4e9
 
 
 def measured_traffic(kernel_key: str, src_hash: str):
-    path = os.path.join(PROFILES, "traffic.json")
+    """HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters (already scaled by
+    the copy-kernel calibration), or None when the kernel sources changed since."""
+    path = os.path.join(PROFILES, "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -169,13 +170,37 @@ def main():
         log(f"inputs {wl.name} N={N} ready in {time.perf_counter() - t0:.1f} s")
         return inp, N, dims, q, k, pyr, out, ws
 
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def hip_events(n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            evs.append(e.value)
+        return evs
+
+    def hip_ms(e0, e1):
+        f = ctypes.c_float()
+        if hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(e0), ctypes.c_void_p(e1)) != 0:
+            return float("nan")
+        return f.value
+
     def time_steps(N, dims, q, k, pyr, out, ws, steps, warmup):
+        """K timed steps bracketed by synchronisations; HIP events on the library's stream
+        mark every step (build, then select) and, inside select, the upper-walk and
+        leaf-scoring stages."""
         stream = torch.cuda.current_stream()
         for _ in range(warmup):
             ops.build_pyramid(k, N, N, dims, pyr)
             ops.select_prefill(q, k, pyr, N, N, dims, out, ws)
         torch.cuda.synchronize()
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        stage = [hip_events(4) for _ in range(steps)]
         t_start = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -184,14 +209,19 @@ def main():
             ev[i][0].record(stream)
             ops.build_pyramid(k, N, N, dims, pyr)
             ev[i][1].record(stream)
-            ops.select_prefill(q, k, pyr, N, N, dims, out, ws)
+            ops.select_prefill_profiled(q, k, pyr, N, N, dims, out, ws, stage[i])
             ev[i][2].record(stream)
         t_end.record(stream)
         torch.cuda.synchronize()
         total_ms = t_start.elapsed_time(t_end)
         build = np.array([e[0].elapsed_time(e[1]) for e in ev])
         walk = np.array([e[1].elapsed_time(e[2]) for e in ev])
-        return total_ms, build, walk
+        upper = np.array([hip_ms(sg[0], sg[1]) for sg in stage])
+        leaf = np.array([hip_ms(sg[2], sg[3]) for sg in stage])
+        for sg in stage:
+            for e in sg:
+                hip.hipEventDestroy(ctypes.c_void_p(e))
+        return total_ms, build, walk, upper, leaf
 
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
@@ -201,47 +231,61 @@ def main():
         log("copy calibration: 268435456 bytes read + 268435456 bytes written")
         del src, dst
     inp, N, dims, q, k, pyr, out, ws = setup(wl)
-    total_ms, build_ms, walk_ms = time_steps(N, dims, q, k, pyr, out, ws, args.steps, args.warmup)
+    total_ms, build_ms, walk_ms, upper_ms, leaf_ms_steps = time_steps(N, dims, q, k, pyr, out, ws, args.steps,
+                                                                      args.warmup)
     ms_per_step = total_ms / args.steps
     value = wl.B * N / (ms_per_step / 1e3)
-    log(f"N={N}: {ms_per_step:.3f} ms/step (build {build_ms.mean():.3f} ms, walk {walk_ms.mean():.3f} ms)")
+    log(f"N={N}: {ms_per_step:.3f} ms/step (build {build_ms.mean():.3f} ms, select {walk_ms.mean():.3f} ms: "
+        f"upper walk {np.mean(upper_ms):.3f} ms, leaf scoring {np.mean(leaf_ms_steps):.3f} ms)")
 
     GQ = wl.Hq // wl.Hkv
-    logits, lse_terms = walk_counts(N, wl.topk, GQ, wl.Hkv)
-    transc = logits + lse_terms               # one exp per logit, one log per LSE term
-    walk_s = walk_ms.mean() / 1e3
-    peaks = roofline_peaks()
-    src_hash = _hash_sources(["upper.hip", "leaf.hip", "pisa_device.h"])
-    traffic = measured_traffic(f"walk_kernel:{wl.name}", src_hash)
-    exp_peak = peaks["transcendental_per_s"] if peaks else None
-    achieved = transc / walk_s
+    wc = walk_counts(N, wl.topk, GQ, wl.Hkv)
+    clustered = wl.dtype == "bf16"
+    kname = "leaf_cluster_kernel" if clustered else "leaf_walk_kernel"
+    src_hash = _hash_sources(["cluster.hip", "lanes.h", "pisa_device.h"])
+    traffic = measured_traffic(f"{kname}:{wl.name}", src_hash)
+    # dominant kernel: the clustered leaf scoring; its duration is measured with HIP events
+    # on the stream the library launches on, around a separate timed pass of the same call
+    leaf_ms = float(np.mean(leaf_ms_steps))
+    transc = wc["leaf_logits"] + wc["leaf_lse"]
+    achieved = transc / (leaf_ms / 1e3)
     roofline = {
-        "kernel": "walk_kernel (coarse-to-fine walk, all levels)",
+        "kernel": f"{kname} (exact raw-key LSE of every scored (walk, leaf) pair)",
         "bound": "alu",
         "achieved": achieved / 1e9,
-        "peak": exp_peak / 1e9 if exp_peak else None,
-        "unit": "G transcendental/s (one exp per logit + one log per LSE term)",
-        "frac": (achieved / exp_peak) if exp_peak else None,
+        "peak": TRANSCENDENTAL_PEAK / 1e9,
+        "unit": "G transcendental/s (one exp per leaf logit + one log per leaf LSE)",
+        "frac": achieved / TRANSCENDENTAL_PEAK,
         "traffic": traffic,
-        "algorithmic_transcendentals_per_launch": transc,
-        "algorithmic_logits_per_launch": logits,
-        "launch_ms": walk_ms.mean(),
+        "algorithmic_per_launch": transc,
+        "leaf_pairs_per_launch": wc["leaf_pairs"],
+        "launch_ms": leaf_ms,
     }
-    # the pyramid build is HBM-bound: compulsory bytes = keys read once + every node written once
+    walk_s = walk_ms.mean() / 1e3
+    upper_transc = wc["upper_logits"] + wc["upper_lse"]
     elt = 2 if wl.dtype == "bf16" else 4
+    # the pyramid build is HBM-bound: compulsory bytes = keys read once + every node written once
     build_bytes = wl.B * N * wl.Hkv * wl.d * elt + wl.B * wl.Hkv * ops.pyramid_nodes(dims, N) * wl.d * 4
-    # compulsory HBM bytes of the walk: Q read once, K read once, indices written once
+    # compulsory HBM bytes of the selection: Q read once, K read once, indices written once
     walk_bytes = wl.B * N * (wl.Hq * wl.d * elt + wl.Hkv * wl.d * elt + wl.Hkv * wl.topk * 4)
     hbm = {
         "build_ms": build_ms.mean(),
         "build_compulsory_GBs": build_bytes / (build_ms.mean() / 1e3) / 1e9,
         "build_frac_of_8TBs": build_bytes / (build_ms.mean() / 1e3) / 1e9 / HBM_PEAK_GBS,
-        "walk_compulsory_GBs": walk_bytes / walk_s / 1e9,
-        "walk_compulsory_frac_of_8TBs": walk_bytes / walk_s / 1e9 / HBM_PEAK_GBS,
+        "select_compulsory_GBs": walk_bytes / walk_s / 1e9,
+        "select_compulsory_frac_of_8TBs": walk_bytes / walk_s / 1e9 / HBM_PEAK_GBS,
     }
     if traffic:
-        hbm["walk_measured_GBs"] = traffic / walk_s / 1e9
-        hbm["walk_measured_frac_of_8TBs"] = traffic / walk_s / 1e9 / HBM_PEAK_GBS
+        hbm["leaf_kernel_measured_GBs"] = traffic / (leaf_ms / 1e3) / 1e9
+        hbm["leaf_kernel_measured_frac_of_8TBs"] = traffic / (leaf_ms / 1e3) / 1e9 / HBM_PEAK_GBS
+    work = {
+        "select_ms": walk_ms.mean(),
+        "upper_walk_ms": float(np.mean(upper_ms)),
+        "leaf_scoring_ms": leaf_ms,
+        "all_transcendentals_per_step": transc + upper_transc,
+        "select_transcendental_frac": (transc + upper_transc) / walk_s / TRANSCENDENTAL_PEAK,
+        "upper_logits": wc["upper_logits"], "leaf_logits": wc["leaf_logits"],
+    }
 
     result = {
         "metric": "Top-K selection latency (ms) + queries/s at N=64K-256K, Hq=32 Hkv=2 d=64",
@@ -263,6 +307,7 @@ def main():
                        "min_build_plus_walk": float(np.min(build_ms + walk_ms))},
         "roofline": roofline,
         "hbm": hbm,
+        "work": work,
     }
     del q, k, pyr, out, ws
 
@@ -273,7 +318,7 @@ def main():
                 continue
             w2 = synth.WORKLOADS[name]
             _, N2, d2, q2, k2, p2, o2, ws2 = setup(w2)
-            tot2, b2, wk2 = time_steps(N2, d2, q2, k2, p2, o2, ws2, 10, 3)
+            tot2, b2, wk2, _, _ = time_steps(N2, d2, q2, k2, p2, o2, ws2, 10, 3)
             sweep[name] = {"N": N2, "ms": tot2 / 10, "queries_per_s": N2 / (tot2 / 10 / 1e3),
                            "build_ms": float(b2.mean()), "walk_ms": float(wk2.mean())}
             del q2, k2, p2, o2, ws2

@@ -207,8 +207,12 @@ static int device_cus(int* cus) {
 
 // Leaf stage after the upper walk has recorded its incidences: bucket offsets and
 // work items, entries grouped by bucket, clustered scoring, final top-K per walk.
+static void mark(void* const* ev, int i, hipStream_t s) {
+    if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], s);
+}
+
 static int cluster_leaf_stage(const uint16_t* q, const uint16_t* k, const Geom& G, int64_t NT, int32_t* out,
-                              const Workspace& W, int cus, hipStream_t s) {
+                              const Workspace& W, int cus, hipStream_t s, void* const* ev) {
     const int64_t walks = (int64_t)G.B * NT * G.Hkv;
     const ClusterGeom& CG = W.CG;
     const int slots = 2 * G.topk;
@@ -218,20 +222,22 @@ static int cluster_leaf_stage(const uint16_t* q, const uint16_t* k, const Geom& 
         if (fill)
             hipLaunchKernelGGL(scan_groups_kernel, dim3(1), dim3(1024), 0, s, W.counts, CG, W.offsets, W.items, W.meta);
         if (slots <= 16)
-            hipLaunchKernelGGL(bucket_pass_kernel<16>, bgrid, dim3(256), bins, s, W.cand, W.ncand, G, CG, NT, W.counts,
+            hipLaunchKernelGGL(bucket_pass_kernel<16>, bgrid, dim3(1024), bins, s, W.cand, W.ncand, G, CG, NT, W.counts,
                                W.offsets, W.entries, fill);
         else if (slots <= 32)
-            hipLaunchKernelGGL(bucket_pass_kernel<32>, bgrid, dim3(256), bins, s, W.cand, W.ncand, G, CG, NT, W.counts,
+            hipLaunchKernelGGL(bucket_pass_kernel<32>, bgrid, dim3(1024), bins, s, W.cand, W.ncand, G, CG, NT, W.counts,
                                W.offsets, W.entries, fill);
         else
-            hipLaunchKernelGGL(bucket_pass_kernel<64>, bgrid, dim3(256), bins, s, W.cand, W.ncand, G, CG, NT, W.counts,
+            hipLaunchKernelGGL(bucket_pass_kernel<64>, bgrid, dim3(1024), bins, s, W.cand, W.ncand, G, CG, NT, W.counts,
                                W.offsets, W.entries, fill);
     }
     if (hipFuncSetAttribute((const void*)leaf_cluster_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                             kSbLdsBytes) != hipSuccess)
         return PISA_ERR_HIP;
+    mark(ev, 2, s);
     hipLaunchKernelGGL(leaf_cluster_kernel, dim3((unsigned)cus), dim3(kClusterThreads), kSbLdsBytes, s, q, k, G,
                        CG, NT, W.items, W.entries, W.meta, W.score);
+    mark(ev, 3, s);
     const int wpw = slots <= 16 ? 4 : (slots <= 32 ? 2 : 1);
     int64_t fgrid = ((walks + wpw - 1) / wpw + 3) / 4;
     if (fgrid > 65536) fgrid = 65536;
@@ -246,7 +252,7 @@ static int cluster_leaf_stage(const uint16_t* q, const uint16_t* k, const Geom& 
 
 template <typename KT>
 static int select_impl(const KT* q, const KT* k, const float* pyr, const Geom& G, int64_t t0,
-                       int64_t NT, int32_t* out, const Workspace& W, hipStream_t s) {
+                       int64_t NT, int32_t* out, const Workspace& W, hipStream_t s, void* const* ev) {
     int rc, cus = 256;
     if ((rc = device_cus(&cus)) != PISA_OK) return rc;
     UpperCfg U = upper_cfg(G);
@@ -261,19 +267,23 @@ static int select_impl(const KT* q, const KT* k, const float* pyr, const Geom& G
         U.lds_nodes = 0;
     }
     const int slots = 2 * G.topk;
+    mark(ev, 0, s);
     if (slots <= 16) rc = launch_upper<KT, 16>(q, W.planes, pyr, G, U, t0, NT, W, cus, s);
     else if (slots <= 32) rc = launch_upper<KT, 32>(q, W.planes, pyr, G, U, t0, NT, W, cus, s);
     else rc = launch_upper<KT, 64>(q, W.planes, pyr, G, U, t0, NT, W, cus, s);
     if (rc != PISA_OK) return rc;
+    mark(ev, 1, s);
     const int64_t walks = (int64_t)G.B * NT * G.Hkv;
     if (!W.clustered) {
         int64_t grid = (walks + 3) / 4;
         if (grid > (1 << 22)) grid = 1 << 22;
+        mark(ev, 2, s);
         hipLaunchKernelGGL(leaf_walk_kernel<KT>, dim3((unsigned)grid), dim3(256), 0, s, q, k, G, t0, NT,
                            W.cand, W.ncand, out);
+        mark(ev, 3, s);
         return launch_status();
     }
-    return cluster_leaf_stage((const uint16_t*)q, (const uint16_t*)k, G, NT, out, W, cus, s);
+    return cluster_leaf_stage((const uint16_t*)q, (const uint16_t*)k, G, NT, out, W, cus, s, ev);
 }
 
 }  // namespace pisa
@@ -325,9 +335,10 @@ int pisa_build_pyramid(const void* k, int64_t N, int64_t n_capacity, const pisa_
     return build_impl((const float*)k, G, pyramid, s);
 }
 
-int pisa_select_prefill(const void* q, const void* k, const float* pyramid, int64_t N,
-                        int64_t n_capacity, const pisa_dims* dims, int32_t* out_idx,
-                        void* workspace, size_t ws_bytes, void* stream) {
+int pisa_select_prefill_profiled(const void* q, const void* k, const float* pyramid, int64_t N,
+                                 int64_t n_capacity, const pisa_dims* dims, int32_t* out_idx,
+                                 void* workspace, size_t ws_bytes, void* stream,
+                                 void* const* stage_events) {
     int rc = check_dims(dims);
     if (rc != PISA_OK) return rc;
     if (!q || !k || !pyramid || !out_idx) return PISA_ERR_INVALID_ARG;
@@ -337,8 +348,15 @@ int pisa_select_prefill(const void* q, const void* k, const float* pyramid, int6
     if (!workspace || ws_bytes < W.bytes) return PISA_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     if (dims->dtype == PISA_DTYPE_BF16)
-        return select_impl((const uint16_t*)q, (const uint16_t*)k, pyramid, G, 0, N, out_idx, W, s);
-    return select_impl((const float*)q, (const float*)k, pyramid, G, 0, N, out_idx, W, s);
+        return select_impl((const uint16_t*)q, (const uint16_t*)k, pyramid, G, 0, N, out_idx, W, s, stage_events);
+    return select_impl((const float*)q, (const float*)k, pyramid, G, 0, N, out_idx, W, s, stage_events);
+}
+
+int pisa_select_prefill(const void* q, const void* k, const float* pyramid, int64_t N,
+                        int64_t n_capacity, const pisa_dims* dims, int32_t* out_idx,
+                        void* workspace, size_t ws_bytes, void* stream) {
+    return pisa_select_prefill_profiled(q, k, pyramid, N, n_capacity, dims, out_idx, workspace, ws_bytes,
+                                        stream, nullptr);
 }
 
 int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cache, float* pyramid,
@@ -359,12 +377,13 @@ int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cach
                            (const uint16_t*)k_new, (uint16_t*)k_cache, G, pyramid);
         if ((rc = launch_status()) != PISA_OK) return rc;
         return select_impl((const uint16_t*)q_new, (const uint16_t*)k_cache, pyramid, G, n_before, 1,
-                           out_idx, W, s);
+                           out_idx, W, s, nullptr);
     }
     hipLaunchKernelGGL(decode_refresh_kernel<float>, dim3(nbh), dim3(64), 0, s,
                        (const float*)k_new, (float*)k_cache, G, pyramid);
     if ((rc = launch_status()) != PISA_OK) return rc;
-    return select_impl((const float*)q_new, (const float*)k_cache, pyramid, G, n_before, 1, out_idx, W, s);
+    return select_impl((const float*)q_new, (const float*)k_cache, pyramid, G, n_before, 1, out_idx, W, s,
+                       nullptr);
 }
 
 const char* pisa_status_string(int status) {

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p,
 // pass the same bins, seeded with the bucket offsets, hand out entry positions.
 // Entry = {walk, leaf mask (bits = leaf offsets in the superblock) | first slot << 16}.
 template <int SL>
-__global__ __launch_bounds__(256) void bucket_pass_kernel(const int32_t* __restrict__ cand,
+__global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __restrict__ cand,
                                                           const int32_t* __restrict__ ncand, Geom G,
                                                           ClusterGeom CG, int64_t NT,
                                                           uint32_t* __restrict__ counts,
@@ -51,15 +51,17 @@ __global__ __launch_bounds__(256) void bucket_pass_kernel(const int32_t* __restr
     const int tid = threadIdx.x, lane = tid & 63, seg = lane / SL, i = lane % SL;
     const int K = G.topk, CS = 2 * G.topk;
     const int nbins = G.Hkv * CG.NSB;
-    for (int x = tid; x < nbins; x += 256) {
-        const int64_t bkt = ((int64_t)b * nbins + x) * CG.NR + r;
+    const int nthr = blockDim.x, nw = nthr >> 6;
+    // bucket (range r, group g = (b, kvh, sb)) lives at r * ngroups + g
+    for (int x = tid; x < nbins; x += nthr) {
+        const int64_t bkt = (int64_t)r * CG.ngroups + (int64_t)b * nbins + x;
         bins[x] = fill ? offsets[bkt] : 0u;
     }
     __syncthreads();
     const int64_t t_lo = (int64_t)r * kRangeT;
     const int64_t t_hi = (t_lo + kRangeT < NT) ? t_lo + kRangeT : NT;
     const int64_t w_lo = ((int64_t)b * NT + t_lo) * G.Hkv, w_hi = ((int64_t)b * NT + t_hi) * G.Hkv;
-    for (int64_t w0 = w_lo + (int64_t)(tid >> 6) * WPW; w0 < w_hi; w0 += 4 * WPW) {
+    for (int64_t w0 = w_lo + (int64_t)(tid >> 6) * WPW; w0 < w_hi; w0 += (int64_t)nw * WPW) {
         const int64_t w = w0 + seg;
         const bool ok = w < w_hi;
         const int nc = ok ? ncand[w] : 0;
@@ -87,12 +89,14 @@ __global__ __launch_bounds__(256) void bucket_pass_kernel(const int32_t* __restr
     }
     __syncthreads();
     if (!fill) {
-        for (int x = tid; x < nbins; x += 256) counts[((int64_t)b * nbins + x) * CG.NR + r] = bins[x];
+        for (int x = tid; x < nbins; x += nthr) counts[(int64_t)r * CG.ngroups + (int64_t)b * nbins + x] = bins[x];
     }
 }
 
 // One workgroup: entry offsets of every bucket (groups (b, kvh, sb) in order, ranges
 // inside a group consecutive) and work items of at most kItemMax entries of one group.
+// Buckets are stored range-major (r * ngroups + g), so that the threads, one group each,
+// read consecutive words.
 // meta[0] = number of items, meta[1] = number of entries.
 __global__ __launch_bounds__(1024) void scan_groups_kernel(const uint32_t* __restrict__ counts, ClusterGeom CG,
                                                            uint32_t* __restrict__ offsets,
@@ -105,7 +109,7 @@ __global__ __launch_bounds__(1024) void scan_groups_kernel(const uint32_t* __res
     uint32_t se = 0, si = 0;
     for (int g = lo; g < hi; ++g) {
         uint32_t tot = 0;
-        for (int r = 0; r < CG.NR; ++r) tot += counts[(int64_t)g * CG.NR + r];
+        for (int r = 0; r < CG.NR; ++r) tot += counts[(int64_t)r * CG.ngroups + g];
         se += tot;
         si += (tot + kItemMax - 1) / kItemMax;
     }
@@ -124,8 +128,8 @@ __global__ __launch_bounds__(1024) void scan_groups_kernel(const uint32_t* __res
     for (int g = lo; g < hi; ++g) {
         const uint32_t g0 = eoff;
         for (int r = 0; r < CG.NR; ++r) {
-            offsets[(int64_t)g * CG.NR + r] = eoff;
-            eoff += counts[(int64_t)g * CG.NR + r];
+            offsets[(int64_t)r * CG.ngroups + g] = eoff;
+            eoff += counts[(int64_t)r * CG.ngroups + g];
         }
         const uint32_t tot = eoff - g0;
         for (uint32_t p = 0; p * kItemMax < tot; ++p)

@@ -27,8 +27,8 @@ PISA_DTYPE_F32 = 0
 PISA_DTYPE_BF16 = 1
 
 EXPORTED = ("pisa_pyramid_nodes", "pisa_level_offset", "pisa_pyramid_bytes", "pisa_workspace_bytes",
-            "pisa_build_pyramid", "pisa_select_prefill", "pisa_decode_update_select",
-            "pisa_status_string")
+            "pisa_build_pyramid", "pisa_select_prefill", "pisa_select_prefill_profiled",
+            "pisa_decode_update_select", "pisa_status_string")
 
 
 class Dims(ctypes.Structure):
@@ -66,6 +66,8 @@ def _load() -> ctypes.CDLL:
     lib.pisa_build_pyramid.restype = ctypes.c_int
     lib.pisa_select_prefill.argtypes = [P, P, P, i64, i64, D, P, P, sz, P]
     lib.pisa_select_prefill.restype = ctypes.c_int
+    lib.pisa_select_prefill_profiled.argtypes = [P, P, P, i64, i64, D, P, P, sz, P, P]
+    lib.pisa_select_prefill_profiled.restype = ctypes.c_int
     lib.pisa_decode_update_select.argtypes = [P, P, P, P, i64, i64, D, P, P, sz, P]
     lib.pisa_decode_update_select.restype = ctypes.c_int
     lib.pisa_status_string.argtypes = [ctypes.c_int]
@@ -150,6 +152,23 @@ def select_prefill(q: torch.Tensor, k: torch.Tensor, pyramid: torch.Tensor, N: i
                                  _ptr(out_idx), _ptr(workspace), ws_n, _stream(stream))
     if rc != PISA_OK:
         raise PisaError("pisa_select_prefill", rc)
+
+
+def select_prefill_profiled(q: torch.Tensor, k: torch.Tensor, pyramid: torch.Tensor, N: int, n_capacity: int,
+                            dims: Dims, out_idx: torch.Tensor, workspace: Optional[torch.Tensor],
+                            stage_events, stream=None) -> None:
+    """pisa_select_prefill recording 4 caller-created hipEvent_t handles (ints or None) at stage
+    boundaries: before/after the upper-level walk, before/after the leaf-scoring kernel."""
+    _check(q, "q", dims.torch_dtype, dims.B * N * dims.Hq * dims.d)
+    _check(k, "k", dims.torch_dtype, dims.B * n_capacity * dims.Hkv * dims.d)
+    _check(pyramid, "pyramid", torch.float32, dims.B * dims.Hkv * pyramid_nodes(dims, n_capacity) * dims.d)
+    _check(out_idx, "out_idx", torch.int32, dims.B * N * dims.Hkv * dims.topk)
+    ev = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e) if e else None for e in stage_events])
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.pisa_select_prefill_profiled(_ptr(q), _ptr(k), _ptr(pyramid), N, n_capacity, ctypes.byref(dims),
+                                          _ptr(out_idx), _ptr(workspace), ws_n, _stream(stream), ev)
+    if rc != PISA_OK:
+        raise PisaError("pisa_select_prefill_profiled", rc)
 
 
 def decode_update_select(q_new: torch.Tensor, k_new: torch.Tensor, k_cache: torch.Tensor,

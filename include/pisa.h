@@ -122,6 +122,21 @@ int pisa_select_prefill(const void* q, const void* k, const float* pyramid, int6
                         void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Profiling variant of pisa_select_prefill: the same work, plus hipEventRecord
+ * of caller-created hipEvent_t handles on `stream` at stage boundaries, so that
+ * each stage's duration can be measured on the stream it runs on:
+ *   stage_events[0]  before the upper-level walk (levels L .. 2),
+ *   stage_events[1]  after it,
+ *   stage_events[2]  before the leaf-level scoring kernel,
+ *   stage_events[3]  after it.
+ * stage_events may be NULL, and so may any entry (that event is skipped).
+ */
+int pisa_select_prefill_profiled(const void* q, const void* k, const float* pyramid, int64_t N,
+                                 int64_t n_capacity, const pisa_dims* dims, int32_t* out_idx,
+                                 void* workspace, size_t ws_bytes, void* stream,
+                                 void* const* stage_events);
+
+/*
  * One decoding step (ai4snews summary, second paragraph): appends k_new as key
  * n_before, refreshes the pyramid along the new key's leaf and its ancestors
  * only (nodes created by the new key included), then selects for the query
