@@ -30,7 +30,7 @@ __global__ void bucket_pass_kernel(const int32_t*, const int32_t*, Geom, Cluster
                                    const uint32_t*, uint2*, int);
 __global__ void scan_groups_kernel(const uint32_t*, ClusterGeom, uint32_t*, int4*, uint32_t*);
 __global__ void leaf_cluster_kernel(const uint16_t*, const uint16_t*, Geom, ClusterGeom, int64_t,
-                                    const int4*, const uint2*, const uint32_t*, float*);
+                                    const int4*, const uint2*, const uint32_t*, float*, float*);
 template <int SLOTS>
 __global__ void final_topk_kernel(const int32_t*, const int32_t*, const float*, Geom, int64_t, int32_t*);
 
@@ -45,6 +45,7 @@ struct Workspace {
     int32_t* ncand;      // [walks]
     // clustered leaf scoring (prefill, bf16 inputs)
     float* score;        // [walks][2K]
+    float* sink;         // [kClusterThreads] stores of lanes without a score
     uint32_t* counts;    // [nb]
     uint32_t* offsets;   // [nb]
     uint2* entries;      // [walks * 2K] incidences grouped by bucket
@@ -81,6 +82,7 @@ static Workspace carve(const pisa_dims* d, int64_t N, int64_t P, bool decode, ch
         w.CG.ngroups = (int32_t)(d->B * d->Hkv * nsb);
         w.CG.nb = w.CG.ngroups * w.CG.NR;
         w.score = (float*)take((size_t)walks * cs * sizeof(float));
+        w.sink = (float*)take((size_t)kClusterThreads * sizeof(float));
         w.counts = (uint32_t*)take((size_t)w.CG.nb * 4);
         w.offsets = (uint32_t*)take((size_t)w.CG.nb * 4);
         w.entries = (uint2*)take((size_t)walks * cs * sizeof(uint2));
@@ -236,7 +238,7 @@ static int cluster_leaf_stage(const uint16_t* q, const uint16_t* k, const Geom& 
         return PISA_ERR_HIP;
     mark(ev, 2, s);
     hipLaunchKernelGGL(leaf_cluster_kernel, dim3((unsigned)cus), dim3(kClusterThreads), kSbLdsBytes, s, q, k, G,
-                       CG, NT, W.items, W.entries, W.meta, W.score);
+                       CG, NT, W.items, W.entries, W.meta, W.score, W.sink);
     mark(ev, 3, s);
     const int wpw = slots <= 16 ? 4 : (slots <= 32 ? 2 : 1);
     int64_t fgrid = ((walks + wpw - 1) / wpw + 3) / 4;

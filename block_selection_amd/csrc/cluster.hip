@@ -236,11 +236,15 @@ __device__ inline void score_leaves(const lds_char_t* lds, int key_base, const i
     }
 }
 
-// Scores of every leaf of `mask` for one walk; lane 0 writes them to score_row in
-// mask order (= ascending candidate slots).
+// Scores of every leaf of `mask` for one walk. The i-th leaf's score (mask order =
+// ascending candidate slots) ends up in lane i and is written with one store per
+// entry, so the loop over leaves issues no memory operation (that keeps the wait
+// counters exact and the next entries' query prefetches in flight).
 __device__ inline void score_entry(const lds_char_t* lds, int key_base, uint32_t mask, int t,
                                    const bf16x8 q0, const bf16x8 q1, int n, int gq, int lane, int GQ,
-                                   float* __restrict__ score_row) {
+                                   float* __restrict__ score_row, float* __restrict__ sink) {
+    const int nslots = __popc(mask);
+    float mine = 0.0f;
     int slot = 0;
     while (mask) {
         const int b0 = __builtin_ctz(mask);
@@ -251,33 +255,36 @@ __device__ inline void score_entry(const lds_char_t* lds, int key_base, uint32_t
             const int bits[2] = {b0, b1};
             float out[2];
             score_leaves<2>(lds, key_base, bits, t, q0, q1, n, gq, GQ, out);
-            if (lane == 0) { score_row[slot] = out[0]; score_row[slot + 1] = out[1]; }
+            mine = (lane == slot) ? out[0] : mine;
+            mine = (lane == slot + 1) ? out[1] : mine;
             slot += 2;
         } else {
             const int bits[1] = {b0};
             float out[1];
             score_leaves<1>(lds, key_base, bits, t, q0, q1, n, gq, GQ, out);
-            if (lane == 0) score_row[slot] = out[0];
+            mine = (lane == slot) ? out[0] : mine;
             slot += 1;
         }
     }
+    // every lane stores (lanes without a score into the sink) so the store count is fixed
+    float* dst = (lane < nslots) ? score_row + lane : sink + lane;
+    *dst = mine;
 }
 
+// B fragments of one walk's queries: head n of the group, dims {8gq..8gq+7} and
+// {32+8gq..32+8gq+7}. Always loads (columns n >= GQ read head 0; their results are
+// excluded from the group sum), so the number of loads per entry is fixed.
 __device__ inline void load_q(const uint16_t* __restrict__ q, int64_t bt, int Hq, int kvh, int GQ, int n,
                               int gq, u32x4& qa, u32x4& qb) {
-    qa = {0u, 0u, 0u, 0u};
-    qb = {0u, 0u, 0u, 0u};
-    if (n < GQ) {
-        const uint16_t* qrow = q + (bt * Hq + (int64_t)kvh * GQ + n) * kD;
-        qa = *reinterpret_cast<const u32x4*>(qrow + 8 * gq);
-        qb = *reinterpret_cast<const u32x4*>(qrow + 32 + 8 * gq);
-    }
+    const uint16_t* qrow = q + (bt * Hq + (int64_t)kvh * GQ + (n < GQ ? n : 0)) * kD;
+    qa = *reinterpret_cast<const u32x4*>(qrow + 8 * gq);
+    qb = *reinterpret_cast<const u32x4*>(qrow + 32 + 8 * gq);
 }
 
 __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, Geom G, ClusterGeom CG, int64_t NT,
     const int4* __restrict__ items, const uint2* __restrict__ entries, const uint32_t* __restrict__ meta,
-    float* __restrict__ score) {
+    float* __restrict__ score, float* __restrict__ sink) {
     static_assert(kItemMax <= 64 * (kClusterThreads / 64), "a wavefront holds its entries in one VGPR pair");
     extern __shared__ u32x4 lds_u4[];
     lds_char_t* lds = (lds_char_t*)lds_u4;
@@ -301,9 +308,10 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
         const uint2 ev = (lane < cnt) ? entries[first + lane * nwaves] : make_uint2(0u, 0u);
         // queries of the first three entries, in flight during the key staging
         u32x4 qa0, qb0, qa1, qb1, qa2, qb2;
+        // lanes j >= cnt of ev hold walk 0: prefetches past the end load a valid query row
         auto qload = [&](int j, u32x4& qa, u32x4& qb) {
             const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)ev.x, j);
-            load_q(q, (int64_t)(w / (uint32_t)G.Hkv), G.Hq, kvh, G.GQ, j < cnt ? n : kMaxGroup, gq, qa, qb);
+            load_q(q, (int64_t)(w / (uint32_t)G.Hkv), G.Hq, kvh, G.GQ, n, gq, qa, qb);
         };
         qload(0, qa0, qb0);
         qload(1, qa1, qb1);
@@ -317,24 +325,25 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
             *reinterpret_cast<lds_u32x4_t*>(lds + sb_lds_offset(r, ch)) = v;
         }
         __syncthreads();
+        // j runs past cnt (up to cnt + 1 <= 65) in the last iteration: such entries get an
+        // empty mask, so they score nothing and only store to the sink
         auto process = [&](int j, const u32x4& qa, const u32x4& qb) {
-            const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)ev.x, j);
-            const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)ev.y, j);
+            const int jl = min(j, 63);
+            const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)ev.x, jl);
+            const uint32_t y = (j < cnt) ? (uint32_t)__builtin_amdgcn_readlane((int)ev.y, jl) : 0u;
             const int t = (int)((w / (uint32_t)G.Hkv) % (uint32_t)NT);
             score_entry(lds, key_base, y & 0xffffu, t, __builtin_bit_cast(bf16x8, qa), __builtin_bit_cast(bf16x8, qb),
-                        n, gq, lane, G.GQ, score + (int64_t)w * CS + (y >> 16));
+                        n, gq, lane, G.GQ, score + (int64_t)w * CS + (y >> 16), sink + wave * 64);
         };
+        // steady state: a fixed sequence of memory operations per iteration (one store per
+        // entry, two loads per prefetch), so wait counts stay exact across iterations
         for (int j = 0; j < cnt; j += 3) {
             process(j, qa0, qb0);
-            qload(j + 3 < 64 ? j + 3 : 63, qa0, qb0);
-            if (j + 1 < cnt) {
-                process(j + 1, qa1, qb1);
-                qload(j + 4 < 64 ? j + 4 : 63, qa1, qb1);
-            }
-            if (j + 2 < cnt) {
-                process(j + 2, qa2, qb2);
-                qload(j + 5 < 64 ? j + 5 : 63, qa2, qb2);
-            }
+            qload(min(j + 3, 63), qa0, qb0);
+            process(j + 1, qa1, qb1);
+            qload(min(j + 4, 63), qa1, qb1);
+            process(j + 2, qa2, qb2);
+            qload(min(j + 5, 63), qa2, qb2);
         }
     }
 }
