@@ -242,7 +242,7 @@ def main():
     wc = walk_counts(N, wl.topk, GQ, wl.Hkv)
     clustered = wl.dtype == "bf16"
     kname = "leaf_cluster_kernel" if clustered else "leaf_walk_kernel"
-    src_hash = _hash_sources(["cluster.hip", "lanes.h", "pisa_device.h"])
+    src_hash = _hash_sources(["cluster.hip", "walk_math.h", "lanes.h", "pisa_device.h"])
     traffic = measured_traffic(f"{kname}:{wl.name}", src_hash)
     # dominant kernel: the clustered leaf scoring; its duration is measured with HIP events
     # on the stream the library launches on, around a separate timed pass of the same call

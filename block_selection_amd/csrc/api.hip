@@ -16,6 +16,8 @@ __global__ void build_subtree_kernel(const KT*, Geom, float*);
 __global__ void build_upper_kernel(Geom, float*);
 template <typename KT>
 __global__ void decode_refresh_kernel(const KT*, KT*, Geom, float*);
+__global__ void decode_step_kernel(const uint16_t*, const uint16_t*, uint16_t*, float*, Geom, uint32_t*, float*,
+                                   int32_t*);
 __global__ void split_planes_kernel(const float*, uint16_t*, int64_t);
 template <typename KT, int SLOTS>
 __global__ void walk_upper_kernel(const KT*, const uint16_t*, const float*, Geom, UpperCfg, int64_t,
@@ -51,6 +53,9 @@ struct Workspace {
     uint2* entries;      // [walks * 2K] incidences grouped by bucket
     int4* items;         // [walks * 2K / kItemMax + ngroups]
     uint32_t* meta;      // [0] items, [1] entries
+    // fused bf16 decoding step
+    uint32_t* done;      // [B*Hkv] completion counters (zero between steps)
+    float* leaf_score;   // [B*Hkv][64] leaf scores of one step
     ClusterGeom CG;
     bool clustered;
     size_t bytes;
@@ -68,6 +73,13 @@ static Workspace carve(const pisa_dims* d, int64_t N, int64_t P, bool decode, ch
         off = align_up(off + bytes);
         return p;
     };
+    if (decode && d->dtype == PISA_DTYPE_BF16) {
+        // the counters come first so that the zero-once contract covers a fixed prefix
+        w.done = (uint32_t*)take((size_t)d->B * d->Hkv * sizeof(uint32_t));
+        w.leaf_score = (float*)take((size_t)d->B * d->Hkv * 64 * sizeof(float));
+        w.bytes = off;
+        return w;
+    }
     const size_t planes = (d->dtype == PISA_DTYPE_BF16) ? (size_t)2 * d->B * d->Hkv * P * kD * 2 : 0;
     w.planes = (uint16_t*)take(planes);
     w.cand = (int32_t*)take((size_t)walks * cs * sizeof(int32_t));
@@ -375,11 +387,13 @@ int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cach
     hipStream_t s = (hipStream_t)stream;
     const unsigned nbh = (unsigned)(dims->B * dims->Hkv);
     if (dims->dtype == PISA_DTYPE_BF16) {
-        hipLaunchKernelGGL(decode_refresh_kernel<uint16_t>, dim3(nbh), dim3(64), 0, s,
-                           (const uint16_t*)k_new, (uint16_t*)k_cache, G, pyramid);
-        if ((rc = launch_status()) != PISA_OK) return rc;
-        return select_impl((const uint16_t*)q_new, (const uint16_t*)k_cache, pyramid, G, n_before, 1,
-                           out_idx, W, s, nullptr);
+        // append, refresh, walk and leaf top-K in one launch: ceil(2K/8) workgroups per
+        // (batch, KV head), the last one to finish writes the selection
+        const unsigned parts = (unsigned)((2 * dims->topk + 7) / 8);
+        hipLaunchKernelGGL(decode_step_kernel, dim3(parts, nbh), dim3(kDecodeThreads), 0, s,
+                           (const uint16_t*)q_new, (const uint16_t*)k_new, (uint16_t*)k_cache, pyramid, G, W.done,
+                           W.leaf_score, out_idx);
+        return launch_status();
     }
     hipLaunchKernelGGL(decode_refresh_kernel<float>, dim3(nbh), dim3(64), 0, s,
                        (const float*)k_new, (float*)k_cache, G, pyramid);

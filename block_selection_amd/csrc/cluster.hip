@@ -21,11 +21,9 @@
 //   5. final_topk: per walk, the K best leaf candidates in ascending order.
 // Per incidence the walk's queries (2 KiB) are read once; the keys of a
 // superblock are read from memory once per work item.
-#include "lanes.h"
+#include "walk_math.h"
 
 namespace pisa {
-
-constexpr float kScale2L = 0.125f * 1.4426950408889634f;
 
 __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
@@ -155,9 +153,7 @@ __device__ inline int sb_lds_offset(int r, int chunk) { return r * 128 + ((chunk
 
 // Exact LSE (base 2) over the raw keys <= t of NL leaves (bits = leaf offsets in the
 // superblock) for one walk, summed over the group's heads. The NL leaves are
-// processed side by side so their MFMA and reduction chains overlap. The sum of
-// 2^x is first taken without a shift; if it overflows or is tiny for any lane the
-// wavefront redoes it shifted by the maximum (the LSE is the same up to rounding).
+// processed side by side so their MFMA and reduction chains overlap.
 template <int NL>
 __device__ inline void score_leaves(const lds_char_t* lds, int key_base, const int bits[NL], int t,
                                     const bf16x8 q0, const bf16x8 q1, int n, int gq, int GQ, float out[NL]) {
@@ -176,64 +172,9 @@ __device__ inline void score_leaves(const lds_char_t* lds, int key_base, const i
         }
     // lane holds keys key0 + 16*tau + 4*gq + r of head n; keys with offset > lim are masked
     int lim[NL];
-    bool full = true;
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
-        lim[j] = min(t - (key_base + bits[j] * kC), kC - 1);
-        full = full && (lim[j] == kC - 1);
-    }
-    float s[NL], shift[NL];
-#pragma unroll
-    for (int j = 0; j < NL; ++j) {
-        float a = 0.f;
-        if (full) {
-#pragma unroll
-            for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) a += __builtin_amdgcn_exp2f(acc[j][tau][r] * kScale2L);
-        } else {
-#pragma unroll
-            for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float e2 = __builtin_amdgcn_exp2f(acc[j][tau][r] * kScale2L);
-                    a += (16 * tau + 4 * gq + r <= lim[j]) ? e2 : 0.0f;
-                }
-        }
-        s[j] = cols4_sum(a);
-        shift[j] = 0.0f;
-    }
-    bool bad = false;
-#pragma unroll
-    for (int j = 0; j < NL; ++j) bad = bad || !(s[j] < INFINITY && s[j] > 0x1p-100f);
-    if (ballot(bad)) {
-        // rare: shift by the maximum logit of each column
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-            float m = -INFINITY;
-#pragma unroll
-            for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (16 * tau + 4 * gq + r <= lim[j]) m = fmaxf(m, acc[j][tau][r]);
-            const float moff = cols4_max(m) * kScale2L;
-            float a = 0.f;
-#pragma unroll
-            for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[j][tau][r], kScale2L, -moff));
-                    a += (16 * tau + 4 * gq + r <= lim[j]) ? e2 : 0.0f;
-                }
-            s[j] = cols4_sum(a);
-            shift[j] = moff;
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < NL; ++j) {
-        const float lse2 = shift[j] + __builtin_amdgcn_logf(s[j]);
-        out[j] = row16_sum((n < GQ) ? lse2 : 0.0f);
-    }
+    for (int j = 0; j < NL; ++j) lim[j] = min(t - (key_base + bits[j] * kC), kC - 1);
+    leaf_lse_from_acc<NL>(acc, lim, n, gq, GQ, out);
 }
 
 // Scores of every leaf of `mask` for one walk. The i-th leaf's score (mask order =

@@ -1,0 +1,191 @@
+// decode.hip -- one decoding step (append, refresh, walk, leaf top-K) in one launch (gfx950).
+//
+// ai4snews summary, second paragraph: a decoding step refreshes only the new
+// token's leaf and its ancestors, then selects. Reading note "Block Sparse
+// Attention with Log-Linear Complexity", section 3.2 (the walk from the root,
+// keeping all candidates of a level that has at most K of them), "Scoring:
+// LogSumExp" and section 4.1 (per-head LSE summed over the GQA group).
+//
+// ceil(2K / 8) workgroups of 8 wavefronts per (batch, KV head); the query position
+// is t = N - 1, the appended key. Every workgroup
+//   1. appends the key and refreshes its leaf and ancestor path (wavefront 0; the
+//      copies in the other workgroups write identical bits);
+//   2. walks from the root down to level 2: the candidates of a level sit in the
+//      2K <= 64 lanes of every wavefront; when there are more than K of them, their
+//      children fill up to eight 16-row tiles, one per wavefront (summaries read from
+//      the fp32 pyramid and split into hi/lo bf16 planes in registers), the candidate
+//      scores go through LDS (double-buffered, so one barrier per level), and every
+//      wavefront sorts the 64 slots itself;
+//   3. scores the candidate leaves of its 8 slots, one per wavefront, from the raw keys
+//      in global memory, into a per-(batch, KV head) row of the workspace.
+// The last workgroup to finish (a completion counter that it resets) takes the K best
+// leaves and writes them ascending, -1 padded. Spreading the leaf stage over several
+// CUs matters: its random 8 KiB key blocks are fetched far faster by several CUs than
+// one CU's outstanding-request capacity allows.
+// The arithmetic is that of the prefill kernels (walk_math.h), so the step selects
+// exactly what prefill selects at the same query position.
+#include "pyramid_math.h"
+#include "walk_math.h"
+
+namespace pisa {
+
+// Leaf scores of NL leaves from raw bf16 keys in global memory (keys > t masked).
+template <int NL>
+__device__ inline void score_leaves_global(const uint16_t* __restrict__ kbase, int64_t row_stride,
+                                           const int (&leaf)[NL], int64_t t, const bf16x8 q0, const bf16x8 q1,
+                                           int n, int gq, int GQ, float out[NL]) {
+    f32x4 acc[NL][4];
+#pragma unroll
+    for (int j = 0; j < NL; ++j)
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau) {
+            // rows past t read row t (their logits are masked), so every load is unconditional
+            // and all 8 * NL of them are in flight together
+            const int64_t key = (int64_t)leaf[j] * kC + 16 * tau + n;
+            const uint16_t* row = kbase + ((key <= t) ? key : t) * row_stride;
+            const u32x4 a0 = *reinterpret_cast<const u32x4*>(row + 8 * gq);
+            const u32x4 a1 = *reinterpret_cast<const u32x4*>(row + 32 + 8 * gq);
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), q0, c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), q1, c, 0, 0, 0);
+            acc[j][tau] = c;
+        }
+    int lim[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        const int64_t l64 = t - (int64_t)leaf[j] * kC;
+        lim[j] = (l64 < kC - 1) ? (int)l64 : kC - 1;
+    }
+    leaf_lse_from_acc<NL>(acc, lim, n, gq, GQ, out);
+}
+
+__global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint16_t* __restrict__ q_new,
+                                                                     const uint16_t* __restrict__ k_new,
+                                                                     uint16_t* __restrict__ k_cache,
+                                                                     float* __restrict__ pyr, Geom G,
+                                                                     uint32_t* __restrict__ done,
+                                                                     float* __restrict__ leaf_score,
+                                                                     int32_t* __restrict__ out) {
+    __shared__ float s_score[2][64];
+    __shared__ int s_last;
+    const int part = blockIdx.x, nparts = gridDim.x;   // leaf slots 8*part .. 8*part+7
+    const int bh = blockIdx.y, b = bh / G.Hkv, kvh = bh % G.Hkv;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, gq = lane >> 4;
+    const int K = G.topk;
+    const int64_t t = G.N - 1;
+    const int64_t row_stride = (int64_t)G.Hkv * kD;
+    uint16_t* kbase = k_cache + ((int64_t)b * G.cap * G.Hkv + kvh) * kD;
+    float* pyr_bh = pyr + (int64_t)bh * G.P * kD;
+
+    // MFMA B fragments of query head n of the group (zero columns beyond the group)
+    u32x4 qa = {0u, 0u, 0u, 0u}, qb = {0u, 0u, 0u, 0u};
+    if (n < G.GQ) {
+        const uint16_t* qrow = q_new + ((int64_t)b * G.Hq + (int64_t)kvh * G.GQ + n) * kD;
+        qa = *reinterpret_cast<const u32x4*>(qrow + 8 * gq);
+        qb = *reinterpret_cast<const u32x4*>(qrow + 32 + 8 * gq);
+    }
+    const bf16x8 q0 = __builtin_bit_cast(bf16x8, qa), q1 = __builtin_bit_cast(bf16x8, qb);
+
+    // Every workgroup of this (batch, KV head) refreshes the path: the copies compute and
+    // store identical bits and read only nodes and keys this step does not change.
+    if (wave == 0) refresh_wave<uint16_t>(k_new + (int64_t)bh * kD, kbase, row_stride, G, pyr_bh, lane);
+    __syncthreads();   // the refreshed path is visible to every wavefront of the workgroup
+
+    // candidate slot = lane; slot 2i + c holds child c of survivor i (survivors in lanes 0..K-1)
+    int surv = -1, buf = 0;
+    for (int l = G.L; l >= 2; --l) {
+        int cand;
+        if (l == G.L) {
+            cand = (lane == 0) ? 0 : -1;
+        } else {
+            const int par = shfl_i(surv, lane >> 1);
+            const int child = 2 * par + (lane & 1);
+            const bool ok = lane < 2 * K && par >= 0 && child < G.M[l] && child <= (int)(t >> (kLog2C + l - 1));
+            cand = ok ? child : -1;
+        }
+        const uint64_t vm = ballot(cand >= 0);
+        const int nc = __popcll(vm);
+        if (nc <= K) {
+            // every candidate survives: compact them into lanes 0 .. nc-1
+            const int dst = (cand >= 0) ? lanes_below(vm) : nc + lanes_below(~vm);
+            const int got = push_to_lane(dst, cand);
+            surv = (lane < nc) ? got : -1;
+            continue;
+        }
+        const int lc = l - 1;
+        {
+            // tile `wave`: row n = child (n & 1) of slot 8 * wave + n / 2
+            const int par = shfl_i(cand, 8 * wave + (n >> 1));
+            const int child = 2 * par + (n & 1);
+            const bool valid = par >= 0 && child < G.M[lc] && child <= (int)(t >> (kLog2C + lc - 1));
+            const uint32_t rows_ok = (uint32_t)ballot(valid);   // bit r: row r is an eligible child
+            if (rows_ok) {
+                const float* row = pyr_bh + (G.off[lc] + (valid ? child : 0)) * kD;
+                float v0[8], v1[8];
+                load8_f32(row + 8 * gq, v0);
+                load8_f32(row + 32 + 8 * gq, v1);
+                u32x4 h0, l0, h1, l1;
+                split8(v0, h0, l0);
+                split8(v1, h1, l1);
+                const f32x4 acc = child_tile_mfma(q0, q1, h0, h1, l0, l1);
+                float sc[2];
+                pair_scores(acc, rows_ok, gq, n, G.GQ, sc);
+                if (n == 0) {
+                    s_score[buf][8 * wave + 2 * gq] = sc[0];
+                    s_score[buf][8 * wave + 2 * gq + 1] = sc[1];
+                }
+            }
+        }
+        __syncthreads();
+        float my = (cand >= 0) ? s_score[buf][lane] : -INFINITY;
+        buf ^= 1;
+        int nd = (cand >= 0) ? cand : INT_MAX;
+        segment_sort<64>(my, nd, lane);
+        surv = (lane < K && nd != INT_MAX) ? nd : -1;
+    }
+
+    // leaf candidates: children of the level-2 survivors (the root itself if it is a leaf)
+    int leaf;
+    if (G.L == 1) {
+        leaf = (lane == 0) ? 0 : -1;
+    } else {
+        const int par = shfl_i(surv, lane >> 1);
+        const int child = 2 * par + (lane & 1);
+        const bool ok = lane < 2 * K && par >= 0 && child < G.M[1] && child <= (int)(t >> kLog2C);
+        leaf = ok ? child : -1;
+    }
+    const bool scored = __popcll(ballot(leaf >= 0)) > K;
+    if (scored) {
+        // this wavefront's leaf slot; the score goes to the per-(batch, KV head) row in
+        // the workspace, and the last workgroup to finish reads the whole row
+        const int slot = 8 * part + wave;
+        const int f = readlane_i(leaf, slot);
+        if (f >= 0) {
+            const int fl[1] = {f};
+            float o[1];
+            score_leaves_global<1>(kbase, row_stride, fl, t, q0, q1, n, gq, G.GQ, o);
+            if (lane == 0) leaf_score[(int64_t)bh * 64 + slot] = o[0];
+        }
+        __threadfence();   // scores visible device-wide before this workgroup counts itself done
+        __syncthreads();
+        if (threadIdx.x == 0) s_last = (atomicAdd(&done[bh], 1u) == (uint32_t)(nparts - 1));
+        __syncthreads();
+        if (!s_last) return;
+        __threadfence();   // acquire: the other workgroups' scores
+    } else if (part != 0) {
+        return;            // at most K candidates: all kept, workgroup 0 writes them
+    }
+    if (wave == 0) {
+        float my = (leaf >= 0) ? (scored ? leaf_score[(int64_t)bh * 64 + lane] : 0.0f) : -INFINITY;
+        int nd = (leaf >= 0) ? leaf : INT_MAX;
+        segment_sort<64>(my, nd, lane);
+        int keep = (lane < K && nd != INT_MAX) ? nd : INT_MAX;
+        float zero = 0.0f;
+        segment_sort<64>(zero, keep, lane);   // ascending, INT_MAX last
+        if (lane < K) out[(int64_t)bh * K + lane] = (keep != INT_MAX) ? keep : -1;
+        if (scored && lane == 0) done[bh] = 0u;   // ready for the next step
+    }
+}
+
+}  // namespace pisa

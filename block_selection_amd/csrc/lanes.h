@@ -2,21 +2,37 @@
 //
 // DPP row operations move data inside 16-lane rows without the LDS crossbar;
 // v_permlane16_swap / v_permlane32_swap (gfx950) exchange rows and wavefront
-// halves; ds_swizzle and ds_bpermute are used only where no VALU form exists.
+// halves. Every xor distance of a 64-lane bitonic network is a VALU move.
 #pragma once
 
 #include "pisa_device.h"
 
 namespace pisa {
 
-// value of lane (lane ^ J)
+// value of lane (lane ^ J), by VALU moves only (no LDS crossbar round trip)
 template <int J>
 __device__ inline int lane_xor(int v) {
-    if constexpr (J == 1) return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
-    else if constexpr (J == 2) return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
-    else if constexpr (J == 8) return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false); // row_ror 8
-    else if constexpr (J == 4 || J == 16) return __builtin_amdgcn_ds_swizzle(v, 0x1F | (J << 10));
-    else return __shfl_xor(v, J, 64);
+    if constexpr (J == 1) {
+        return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);    // quad_perm 1,0,3,2
+    } else if constexpr (J == 2) {
+        return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);    // quad_perm 2,3,0,1
+    } else if constexpr (J == 4) {
+        // row_half_mirror takes lane ^ 7 inside each 8-lane half row, quad_perm 3,2,1,0 then
+        // lane ^ 3: together lane ^ 4
+        const int m = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+        return __builtin_amdgcn_update_dpp(0, m, 0x1B, 0xF, 0xF, false);
+    } else if constexpr (J == 8) {
+        return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);   // row_ror 8
+    } else if constexpr (J == 16) {
+        // v_permlane16_swap exchanges odd rows of its first operand with even rows of the
+        // second; with both = v, result[0] holds row r ^ 1 on odd rows, result[1] on even rows
+        const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+        return (int)(((threadIdx.x >> 4) & 1) ? r[0] : r[1]);
+    } else {
+        static_assert(J == 32, "lane_xor: J must be 1, 2, 4, 8, 16 or 32");
+        const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+        return (int)(((threadIdx.x >> 5) & 1) ? r[0] : r[1]);
+    }
 }
 template <int J>
 __device__ inline float lane_xor_f(float v) { return __int_as_float(lane_xor<J>(__float_as_int(v))); }

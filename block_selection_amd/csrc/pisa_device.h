@@ -74,6 +74,9 @@ struct ClusterGeom {
     int32_t ngroups; // B * Hkv * NSB
     int32_t nb;      // buckets = ngroups * NR
 };
+// Fused decode step: workgroups of 8 wavefronts, ceil(2K / 8) per (batch, KV head).
+constexpr int kDecodeThreads = 512;
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -12,52 +12,9 @@
 // formula (parent_mean), so a refreshed pyramid is bitwise equal to a rebuild.
 // HBM traffic of the build: one read of the keys (N*Hkv*64 elements) plus one
 // fp32 write of every node (about 2*N/64*Hkv*64*4 bytes).
-#include "pisa_device.h"
+#include "pyramid_math.h"
 
 namespace pisa {
-
-// Mean of leaf `leaf` over keys [64*leaf, n) for one (batch, KV head), computed by one
-// wavefront. Lane = 8*r + c: lane c of each row group owns dims 8c..8c+7; row group r
-// sums keys r, r+8, ..., then the 8 row groups are combined by a xor butterfly (all
-// lanes end with identical sums). Row `alt_key`, if in range, is read from `alt_row`.
-template <typename KT>
-__device__ inline void leaf_mean_wave(const KT* kbase, int64_t row_stride, int64_t leaf,
-                                      int64_t n, const KT* alt_row, int64_t alt_key,
-                                      int lane, float mean[8]) {
-    const int r = lane >> 3, c = lane & 7;
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-    const int64_t k0 = leaf * kC;
-#pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-        const int64_t key = k0 + rr * 8 + r;
-        if (key < n) {
-            const KT* row = (key == alt_key) ? alt_row : kbase + key * row_stride;
-            float v[8];
-            load8_f32(row + 8 * c, v);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += v[e];
-        }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        acc[e] += xor_f(acc[e], 8);
-        acc[e] += xor_f(acc[e], 16);
-        acc[e] += xor_f(acc[e], 32);
-    }
-    const int64_t cnt64 = (n - k0 < kC) ? (n - k0) : kC;
-    const float cnt = (float)cnt64;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) mean[e] = __fdiv_rn(acc[e], cnt);
-}
-
-__device__ inline float* pyr_row(float* pyr, const Geom& G, int bh, int l, int64_t i) {
-    return pyr + ((int64_t)bh * G.P + G.off[l] + i) * kD;
-}
-__device__ inline const float* pyr_row(const float* pyr, const Geom& G, int bh, int l, int64_t i) {
-    return pyr + ((int64_t)bh * G.P + G.off[l] + i) * kD;
-}
 
 constexpr int kSubLeaves = 16;   // leaves per workgroup subtree (levels 1..5)
 constexpr int kSubLevels = 5;
@@ -135,52 +92,17 @@ __global__ __launch_bounds__(256) void build_upper_kernel(Geom G, float* __restr
 
 // Decode refresh for one (batch, KV head): writes k_new as key n (= G.N - 1), recomputes
 // the mean of leaf n/64 and then every ancestor of that leaf up to the root of G.
+// Decode refresh alone, one wavefront per (batch, KV head): key row N-1 appended,
+// its leaf and every ancestor recomputed.
 template <typename KT>
 __global__ __launch_bounds__(64) void decode_refresh_kernel(const KT* __restrict__ k_new,
                                                             KT* __restrict__ k_cache, Geom G,
                                                             float* __restrict__ pyr) {
     const int bh = blockIdx.x;
     const int b = bh / G.Hkv, kvh = bh % G.Hkv;
-    const int lane = threadIdx.x;
-    const int64_t n = G.N - 1;
-    const int64_t row_stride = (int64_t)G.Hkv * kD;
-    const KT* krow_new = k_new + (int64_t)bh * kD;
     KT* kbase = k_cache + ((int64_t)b * G.cap * G.Hkv + kvh) * kD;
-    if (lane < kD) kbase[n * row_stride + lane] = krow_new[lane];
-
-    const int64_t leaf = n >> kLog2C;
-    float mean[8];
-    leaf_mean_wave<KT>(kbase, row_stride, leaf, G.N, krow_new, n, lane, mean);
-    if (lane < 8) {
-        float* dst = pyr_row(pyr, G, bh, 1, leaf) + 8 * lane;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dst[e] = mean[e];
-    }
-    // lane e takes dim e of the leaf mean (held by lanes with c = e/8)
-    float own = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float v = shfl_f(mean[e], lane >> 3);
-        if ((lane & 7) == e) own = v;
-    }
-    int64_t node = leaf;
-    for (int l = 2; l <= G.L; ++l) {
-        const int64_t child = node;
-        node >>= 1;
-        const int64_t left = 2 * node, right = left + 1;
-        const float ca = (float)covered(l - 1, left, G.N);
-        const float cb = (float)covered(l - 1, right, G.N);
-        float a, bv;
-        if (child == left) {
-            a = own;
-            bv = (cb > 0.0f) ? pyr_row(pyr, G, bh, l - 1, right)[lane] : 0.0f;
-        } else {
-            a = pyr_row(pyr, G, bh, l - 1, left)[lane];
-            bv = own;
-        }
-        own = parent_mean(a, ca, bv, cb);
-        pyr_row(pyr, G, bh, l, node)[lane] = own;
-    }
+    refresh_wave<KT>(k_new + (int64_t)bh * kD, kbase, (int64_t)G.Hkv * kD, G, pyr + (int64_t)bh * G.P * kD,
+                     threadIdx.x);
 }
 
 template __global__ void build_subtree_kernel<uint16_t>(const uint16_t*, Geom, float*);

@@ -24,27 +24,19 @@
 //   * The coarsest levels that can be read as children are staged in LDS
 //     once per workgroup; finer levels are gathered from global memory (L2).
 //   * Top-K: bitonic sort inside each segment by (score desc, node asc).
-#include "lanes.h"
+#include "walk_math.h"
 
 namespace pisa {
-
-constexpr float kScale2 = 0.125f * 1.4426950408889634f;   // log2(e) / sqrt(64)
-
-__device__ inline uint32_t rne_bf16_bits(float x) {
-    const uint32_t u = __float_as_uint(x);
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
 
 // planes[0] = rne(x * s), planes[1] = rne(x * s - hi), elementwise over the whole pyramid.
 __global__ __launch_bounds__(256) void split_planes_kernel(const float* __restrict__ pyr,
                                                            uint16_t* __restrict__ planes,
                                                            int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-        const float v = pyr[i] * kScale2;
-        const uint32_t hi = rne_bf16_bits(v);
-        const float r = v - __uint_as_float(hi << 16);
+        uint32_t hi, lo;
+        split_scaled(pyr[i], hi, lo);
         planes[i] = (uint16_t)hi;
-        planes[n + i] = (uint16_t)rne_bf16_bits(r);
+        planes[n + i] = (uint16_t)lo;
     }
 }
 
@@ -81,17 +73,6 @@ struct UpperQ<float> {
     }
 };
 
-// Base-2 logits of one 16-row tile of children (row = lane % 16) against the query:
-// hi and lo planes, two k-steps each.
-__device__ inline f32x4 child_tile_mfma(const UpperQ<uint16_t>& q, u32x4 h0, u32x4 h1, u32x4 l0, u32x4 l1) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h0), q.k0, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h1), q.k1, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, l0), q.k0, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, l1), q.k1, acc, 0, 0, 0);
-    return acc;
-}
-
 // Row from the LDS-staged coarse levels (node slot lds_node).
 __device__ inline f32x4 child_tile_lds(const UpperQ<uint16_t>& q, const lds_char_t* lds, int lds_node, int gq) {
     const lds_char_t* p = lds + lds_node * kLdsNodeBytes;
@@ -99,7 +80,7 @@ __device__ inline f32x4 child_tile_lds(const UpperQ<uint16_t>& q, const lds_char
     const u32x4 h1 = *reinterpret_cast<const lds_u32x4_t*>(p + 64 + 16 * gq);
     const u32x4 l0 = *reinterpret_cast<const lds_u32x4_t*>(p + 128 + 16 * gq);
     const u32x4 l1 = *reinterpret_cast<const lds_u32x4_t*>(p + 192 + 16 * gq);
-    return child_tile_mfma(q, h0, h1, l0, l1);
+    return child_tile_mfma(q.k0, q.k1, h0, h1, l0, l1);
 }
 
 // Row from global memory (hi plane at `plane`, lo plane plane_stride elements further).
@@ -109,7 +90,7 @@ __device__ inline f32x4 child_tile_global(const UpperQ<uint16_t>& q, const uint1
     const u32x4 h1 = *reinterpret_cast<const u32x4*>(plane + 32 + 8 * gq);
     const u32x4 l0 = *reinterpret_cast<const u32x4*>(plane + plane_stride + 8 * gq);
     const u32x4 l1 = *reinterpret_cast<const u32x4*>(plane + plane_stride + 32 + 8 * gq);
-    return child_tile_mfma(q, h0, h1, l0, l1);
+    return child_tile_mfma(q.k0, q.k1, h0, h1, l0, l1);
 }
 
 __device__ inline f32x4 child_tile_f32(const UpperQ<float>& q, const float* __restrict__ pyr_row, int gq) {
@@ -122,12 +103,6 @@ __device__ inline f32x4 child_tile_f32(const UpperQ<float>& q, const float* __re
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] *= kScale2;
     return acc;
-}
-
-// log2(2^a + 2^b)
-__device__ inline float log2_add_exp2(float a, float b) {
-    const float m = fmaxf(a, b), d = fminf(a, b) - m;
-    return m + __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(d));
 }
 
 // ------------------------------------------------------------- tile layout --
@@ -145,25 +120,11 @@ __device__ constexpr int slot_lane(int w, int m) {
 }
 constexpr int slot_bit_lane(int J) { return J == 1 ? 1 : J == 2 ? 16 : J == 4 ? 32 : J == 8 ? 2 : J == 16 ? 4 : 8; }
 
-// value of lane (lane ^ X) for the lane offsets used by the tile layout
-template <int X>
-__device__ inline int tile_xor(int v) {
-    if constexpr (X == 16) {
-        const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
-        return (int)(((threadIdx.x >> 4) & 1) ? r[0] : r[1]);
-    } else if constexpr (X == 32) {
-        const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
-        return (int)(((threadIdx.x >> 5) & 1) ? r[0] : r[1]);
-    } else {
-        return lane_xor<X>(v);
-    }
-}
-
 template <int J>
 __device__ inline void tile_bitonic_step(float& s, int& nd, int m, int k) {
     constexpr int X = slot_bit_lane(J);
-    const float so = __int_as_float(tile_xor<X>(__float_as_int(s)));
-    const int no = tile_xor<X>(nd);
+    const float so = __int_as_float(lane_xor<X>(__float_as_int(s)));
+    const int no = lane_xor<X>(nd);
     const bool lower = (m & J) == 0;
     const bool up = (m & k) == 0;
     const bool self_first = precedes(s, nd, so, no);
@@ -308,14 +269,7 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_kernel(const KT* __r
                             acc = child_tile_f32(qf[w], pyr_lvl + (int64_t)row * kD, gq);
                         }
                         float sc[2];
-#pragma unroll
-                        for (int p = 0; p < 2; ++p) {
-                            const bool lv = (rows_ok >> (4 * gq + 2 * p)) & 1u;       // candidate exists
-                            const bool rv = (rows_ok >> (4 * gq + 2 * p + 1)) & 1u;   // its right child counts
-                            const float lse2 = rv ? log2_add_exp2(acc[2 * p], acc[2 * p + 1]) : acc[2 * p];
-                            const float sm = row16_sum(n < G.GQ ? lse2 : 0.0f);
-                            sc[p] = lv ? sm : -INFINITY;
-                        }
+                        pair_scores(acc, rows_ok, gq, n, G.GQ, sc);
                         if (wl == w && (ql >> 1) == tau) my = (ql & 1) ? sc[1] : sc[0];
                     }
                 }

@@ -128,7 +128,8 @@ def alloc_pyramid(dims: Dims, n_capacity: int, device="cuda") -> torch.Tensor:
 def alloc_workspace(dims: Dims, N: int, n_capacity: Optional[int] = None, is_decode: bool = False,
                     device="cuda") -> Optional[torch.Tensor]:
     n = workspace_bytes(dims, N, n_capacity, is_decode)
-    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+    # zero-filled: a decode workspace starts with completion counters that must be zero
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
 
 
 def build_pyramid(k: torch.Tensor, N: int, n_capacity: int, dims: Dims, pyramid: torch.Tensor,

@@ -87,9 +87,14 @@ size_t pisa_pyramid_bytes(const pisa_dims* dims, int64_t n_capacity);
 
 /* Device workspace that pisa_select_prefill (is_decode = 0, N = sequence
  * length) or pisa_decode_update_select (is_decode = 1; N is ignored) needs for
- * a pyramid laid out for n_capacity keys. Returns 0 on bad input. The
- * workspace holds scratch data between the kernels of one call; its contents
- * need not be initialised and are meaningless after the call. */
+ * a pyramid laid out for n_capacity keys. Returns 0 on bad input.
+ * Prefill: scratch between the kernels of one call; its contents need not be
+ * initialised and are meaningless after the call.
+ * Decode with bf16 inputs: the workspace starts with one completion counter
+ * per (batch, KV head) (4 * B * Hkv bytes) that must be zero before the first
+ * step (e.g. allocate it zero-filled); every step leaves the counters at zero
+ * again. Do not share a decode workspace with prefill calls, or zero it again
+ * before the next step. */
 size_t pisa_workspace_bytes(const pisa_dims* dims, int64_t N, int64_t n_capacity, int32_t is_decode);
 
 /*

@@ -215,3 +215,40 @@ def test_decode_128k_256_steps():
     """The decode workload: 131072 prebuilt keys, 256 steps, K = 32; step 0 adds a root level."""
     mism, near = _decode_run(131072, 256, check_every=1, oracle_every=1)
     print(json.dumps({"decode128k_mismatch_near_tie": mism, "near_tie_walks": near}), flush=True)
+
+
+@pytest.mark.parametrize("topk", [32, 8])
+def test_decode_equals_prefill_at_same_position(topk):
+    """A decode step selects, bit for bit, what prefill selects for position n over n + 1 keys
+    (both paths share the scoring arithmetic); 5000 context keys, 24 steps."""
+    from block_selection_amd import ops
+    N0, steps = 5000, 24
+    wl = synth.Workload("decode", N=N0, Hq=32, Hkv=2, topk=topk, dtype="bf16", decode_steps=steps)
+    inp = synth.make_decode(wl)
+    cap = N0 + steps
+    dims = ops.make_dims(1, 32, 2, topk, "bf16")
+    kc_host = np.zeros((1, cap, 2, 64), np.float32)
+    kc_host[0, :N0] = inp.k_ctx[0]
+    k_cache = to_device(kc_host, "bf16")
+    pyr = ops.alloc_pyramid(dims, cap)
+    ops.build_pyramid(k_cache, N0, cap, dims, pyr)
+    k_new = to_device(inp.k_new, "bf16")
+    q_new = to_device(inp.q_new, "bf16")
+    out = torch.full((1, 2, topk), -7, dtype=torch.int32, device="cuda")
+    ws = ops.alloc_workspace(dims, 1, cap, is_decode=True)
+    k_all = np.concatenate([inp.k_ctx[0], inp.k_new[:, 0]], axis=0)
+    checked = 0
+    for s in range(steps):
+        n = N0 + s
+        print(f"[case] decode-vs-prefill K={topk} step={s} n={n}", flush=True)
+        ops.decode_update_select(q_new[s].contiguous(), k_new[s].contiguous(), k_cache, pyr, n, cap,
+                                 dims, out, ws)
+        if s % 6 == 0 or s == steps - 1:
+            torch.cuda.synchronize()
+            dec = out.cpu().numpy()[0]
+            q = np.zeros((1, n + 1, 32, 64), np.float32)
+            q[0, n] = inp.q_new[s, 0]
+            ref = run_prefill(q, k_all[None, : n + 1], topk, "bf16")
+            assert np.array_equal(dec, ref.idx[0, n]), (s, dec, ref.idx[0, n])
+            checked += 1
+    assert checked == 5
