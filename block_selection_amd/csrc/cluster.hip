@@ -308,11 +308,8 @@ __global__ __launch_bounds__(256) void final_topk_kernel(const int32_t* __restri
         const int c = (ok && i < CS) ? cand[w * CS + i] : -1;
         float s = -INFINITY;
         if (c >= 0) s = (nc > K) ? score[w * CS + i] : 0.0f;
-        int nd = (c >= 0) ? c : INT_MAX;
-        segment_sort<SLOTS>(s, nd, i);
-        float z = 0.0f;
-        int nd2 = (i < K) ? nd : INT_MAX;
-        segment_sort<SLOTS>(z, nd2, i);
+        const int nd = select_sort<SLOTS>(s, (c >= 0) ? c : INT_MAX, i);
+        const int nd2 = index_sort<SLOTS>((i < K) ? nd : INT_MAX, i);
         if (ok && i < K) out[w * K + i] = (nd2 != INT_MAX) ? nd2 : -1;
     }
 }

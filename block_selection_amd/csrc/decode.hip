@@ -138,10 +138,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
             }
         }
         __syncthreads();
-        float my = (cand >= 0) ? s_score[buf][lane] : -INFINITY;
+        const float my = (cand >= 0) ? s_score[buf][lane] : -INFINITY;
         buf ^= 1;
-        int nd = (cand >= 0) ? cand : INT_MAX;
-        segment_sort<64>(my, nd, lane);
+        const int nd = select_sort<64>(my, (cand >= 0) ? cand : INT_MAX, lane);
         surv = (lane < K && nd != INT_MAX) ? nd : -1;
     }
 
@@ -177,12 +176,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
         return;            // at most K candidates: all kept, workgroup 0 writes them
     }
     if (wave == 0) {
-        float my = (leaf >= 0) ? (scored ? leaf_score[(int64_t)bh * 64 + lane] : 0.0f) : -INFINITY;
-        int nd = (leaf >= 0) ? leaf : INT_MAX;
-        segment_sort<64>(my, nd, lane);
-        int keep = (lane < K && nd != INT_MAX) ? nd : INT_MAX;
-        float zero = 0.0f;
-        segment_sort<64>(zero, keep, lane);   // ascending, INT_MAX last
+        const float my = (leaf >= 0) ? (scored ? leaf_score[(int64_t)bh * 64 + lane] : 0.0f) : -INFINITY;
+        const int nd = select_sort<64>(my, (leaf >= 0) ? leaf : INT_MAX, lane);
+        const int keep = index_sort<64>((lane < K) ? nd : INT_MAX, lane);   // ascending, INT_MAX last
         if (lane < K) out[(int64_t)bh * K + lane] = (keep != INT_MAX) ? keep : -1;
         if (scored && lane == 0) done[bh] = 0u;   // ready for the next step
     }

@@ -12,17 +12,18 @@ namespace pisa {
 // value of lane (lane ^ J), by VALU moves only (no LDS crossbar round trip)
 template <int J>
 __device__ inline int lane_xor(int v) {
+    // every source lane of these patterns exists, so no "old" value is needed
     if constexpr (J == 1) {
-        return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);    // quad_perm 1,0,3,2
+        return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);    // quad_perm 1,0,3,2
     } else if constexpr (J == 2) {
-        return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);    // quad_perm 2,3,0,1
+        return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);    // quad_perm 2,3,0,1
     } else if constexpr (J == 4) {
         // row_half_mirror takes lane ^ 7 inside each 8-lane half row, quad_perm 3,2,1,0 then
         // lane ^ 3: together lane ^ 4
-        const int m = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
-        return __builtin_amdgcn_update_dpp(0, m, 0x1B, 0xF, 0xF, false);
+        const int m = __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true);
+        return __builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, true);
     } else if constexpr (J == 8) {
-        return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);   // row_ror 8
+        return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true);   // row_ror 8
     } else if constexpr (J == 16) {
         // v_permlane16_swap exchanges odd rows of its first operand with even rows of the
         // second; with both = v, result[0] holds row r ^ 1 on odd rows, result[1] on even rows
@@ -60,35 +61,70 @@ __device__ inline float cols4_sum(float v) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Does (sa, na) come before (sb, nb)? Higher score first, then lower index.
-__device__ inline bool precedes(float sa, int na, float sb, int nb) {
-    return sa > sb || (sa == sb && na < nb);
+// ---------------------------------------------------------------- sorting --
+// Selection order: higher score first, equal scores lower index first. A (score,
+// index) pair is packed into one 64-bit key whose descending unsigned order is the
+// selection order: the score's bits mapped to an order-preserving unsigned integer
+// (-0 folded into +0 so the two tie), then the complemented index. A bitonic step
+// is then two lane moves, one 64-bit compare and two selects.
+__device__ inline uint64_t select_key(float s, int nd) {
+    const uint32_t u = __float_as_uint(s + 0.0f);
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)o << 32) | (uint64_t)(~(uint32_t)nd);
+}
+__device__ inline int key_index(uint64_t key) { return (int)~(uint32_t)key; }
+
+template <int X>
+__device__ inline uint32_t lane_xor_u32(uint32_t v) { return (uint32_t)lane_xor<X>((int)v); }
+template <int X>
+__device__ inline uint64_t lane_xor_u64(uint64_t v) {
+    const uint64_t lo = lane_xor_u32<X>((uint32_t)v), hi = lane_xor_u32<X>((uint32_t)(v >> 32));
+    return (hi << 32) | lo;
 }
 
-template <int J>
-__device__ inline void bitonic_step(float& s, int& nd, int i, int k) {
-    const float so = lane_xor_f<J>(s);
-    const int no = lane_xor<J>(nd);
-    const bool lower = (i & J) == 0;
-    const bool up = (i & k) == 0;
-    const bool self_first = precedes(s, nd, so, no);
-    const bool keep_self = (lower == up) ? self_first : !self_first;
-    if (!keep_self) { s = so; nd = no; }
+// Compare-exchange of a descending bitonic network: this lane holds slot m, its
+// partner slot m ^ J sits X lanes away; k is the size of the sequences being merged.
+template <int J, int X, typename T>
+__device__ inline void key_step(T& key, int m, int k) {
+    T o;
+    if constexpr (sizeof(T) == 8) o = lane_xor_u64<X>(key);
+    else o = lane_xor_u32<X>(key);
+    const bool flip = ((m & J) == 0) != ((m & k) == 0);
+    key = ((key > o) != flip) ? key : o;
 }
 
-// Bitonic sort of (s, nd) inside each segment of SLOTS lanes (i = lane % SLOTS):
-// afterwards segment lane 0 holds the element that precedes all others.
-template <int SLOTS>
-__device__ inline void segment_sort(float& s, int& nd, int i) {
+// Plain lane layout: slot i of a segment is lane offset i.
+struct SegmentLanes {
+    static constexpr int of(int J) { return J; }
+};
+
+// Descending sort of the keys of each segment of SLOTS slots (slot m of this lane).
+template <int SLOTS, typename Lanes, typename T>
+__device__ inline T bitonic_desc(T key, int m) {
 #pragma unroll
     for (int k = 2; k <= SLOTS; k <<= 1) {
-        if (k >= 64) { bitonic_step<32>(s, nd, i, k); }
-        if (k >= 32) { bitonic_step<16>(s, nd, i, k); }
-        if (k >= 16) { bitonic_step<8>(s, nd, i, k); }
-        if (k >= 8) { bitonic_step<4>(s, nd, i, k); }
-        if (k >= 4) { bitonic_step<2>(s, nd, i, k); }
-        bitonic_step<1>(s, nd, i, k);
+        if (k >= 64) key_step<32, Lanes::of(32)>(key, m, k);
+        if (k >= 32) key_step<16, Lanes::of(16)>(key, m, k);
+        if (k >= 16) key_step<8, Lanes::of(8)>(key, m, k);
+        if (k >= 8) key_step<4, Lanes::of(4)>(key, m, k);
+        if (k >= 4) key_step<2, Lanes::of(2)>(key, m, k);
+        key_step<1, Lanes::of(1)>(key, m, k);
     }
+    return key;
+}
+
+// The index at slot m after ordering each segment's (score, index) pairs by selection
+// order (slot 0 = the pair that precedes all others).
+template <int SLOTS, typename Lanes = SegmentLanes>
+__device__ inline int select_sort(float s, int nd, int m) {
+    return key_index(bitonic_desc<SLOTS, Lanes>(select_key(s, nd), m));
+}
+
+// The index at slot m after sorting each segment's indices ascending (nonnegative
+// indices; INT_MAX sorts last).
+template <int SLOTS, typename Lanes = SegmentLanes>
+__device__ inline int index_sort(int nd, int m) {
+    return (int)~bitonic_desc<SLOTS, Lanes>(~(uint32_t)nd, m);
 }
 
 }  // namespace pisa

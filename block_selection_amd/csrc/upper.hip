@@ -23,7 +23,7 @@
 //     adds across the 16 head columns.
 //   * The coarsest levels that can be read as children are staged in LDS
 //     once per workgroup; finer levels are gathered from global memory (L2).
-//   * Top-K: bitonic sort inside each segment by (score desc, node asc).
+//   * Top-K: bitonic sort of each walk's slots on 64-bit (score, node) keys.
 #include "walk_math.h"
 
 namespace pisa {
@@ -120,32 +120,10 @@ __device__ constexpr int slot_lane(int w, int m) {
 }
 constexpr int slot_bit_lane(int J) { return J == 1 ? 1 : J == 2 ? 16 : J == 4 ? 32 : J == 8 ? 2 : J == 16 ? 4 : 8; }
 
-template <int J>
-__device__ inline void tile_bitonic_step(float& s, int& nd, int m, int k) {
-    constexpr int X = slot_bit_lane(J);
-    const float so = __int_as_float(lane_xor<X>(__float_as_int(s)));
-    const int no = lane_xor<X>(nd);
-    const bool lower = (m & J) == 0;
-    const bool up = (m & k) == 0;
-    const bool self_first = precedes(s, nd, so, no);
-    const bool keep_self = (lower == up) ? self_first : !self_first;
-    if (!keep_self) { s = so; nd = no; }
-}
-
-// Bitonic sort of each walk's SLOTS slots in tile layout (m = this lane's slot):
-// afterwards slot 0 holds the element that precedes all others.
-template <int SLOTS>
-__device__ inline void tile_sort(float& s, int& nd, int m) {
-#pragma unroll
-    for (int k = 2; k <= SLOTS; k <<= 1) {
-        if (k >= 64) { tile_bitonic_step<32>(s, nd, m, k); }
-        if (k >= 32) { tile_bitonic_step<16>(s, nd, m, k); }
-        if (k >= 16) { tile_bitonic_step<8>(s, nd, m, k); }
-        if (k >= 8) { tile_bitonic_step<4>(s, nd, m, k); }
-        if (k >= 4) { tile_bitonic_step<2>(s, nd, m, k); }
-        tile_bitonic_step<1>(s, nd, m, k);
-    }
-}
+// Slot bit J of the tile layout is lane bit slot_bit_lane(J).
+struct TileLanes {
+    static constexpr int of(int J) { return slot_bit_lane(J); }
+};
 
 // Walks for positions t0 + ti, ti in [0, NT), of every batch element and KV head.
 // Output per walk (index (b*NT + ti)*Hkv + kvh): cand_out[2K] ascending leaf
@@ -275,8 +253,7 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_kernel(const KT* __r
                 }
                 if (cand < 0) my = -INFINITY;
             }
-            int nd = (cand >= 0) ? cand : INT_MAX;
-            tile_sort<SLOTS>(my, nd, ml);
+            const int nd = select_sort<SLOTS, TileLanes>(my, (cand >= 0) ? cand : INT_MAX, ml);
             surv = (ml < K && nd != INT_MAX) ? nd : -1;
         }
         // leaf candidates: children of the level-2 survivors (or the root if it is a leaf)
@@ -289,10 +266,8 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_kernel(const KT* __r
             const bool ok = ml < 2 * K && par >= 0 && child < G.M[1] && child <= (int)(my_t >> kLog2C);
             leaf = ok ? child : -1;
         }
-        // ascending order, -1 last (equal scores: lower index first)
-        float zero = 0.0f;
-        int nd = (leaf >= 0) ? leaf : INT_MAX;
-        tile_sort<SLOTS>(zero, nd, ml);
+        // ascending order, -1 last
+        const int nd = index_sort<SLOTS, TileLanes>((leaf >= 0) ? leaf : INT_MAX, ml);
         leaf = (nd != INT_MAX && ml < 2 * K) ? nd : -1;
         const uint64_t lm = ballot(leaf >= 0);
         uint64_t mine = 0;
