@@ -73,26 +73,6 @@ struct UpperQ<float> {
     }
 };
 
-// Row from the LDS-staged coarse levels (node slot lds_node).
-__device__ inline f32x4 child_tile_lds(const UpperQ<uint16_t>& q, const lds_char_t* lds, int lds_node, int gq) {
-    const lds_char_t* p = lds + lds_node * kLdsNodeBytes;
-    const u32x4 h0 = *reinterpret_cast<const lds_u32x4_t*>(p + 16 * gq);
-    const u32x4 h1 = *reinterpret_cast<const lds_u32x4_t*>(p + 64 + 16 * gq);
-    const u32x4 l0 = *reinterpret_cast<const lds_u32x4_t*>(p + 128 + 16 * gq);
-    const u32x4 l1 = *reinterpret_cast<const lds_u32x4_t*>(p + 192 + 16 * gq);
-    return child_tile_mfma(q.k0, q.k1, h0, h1, l0, l1);
-}
-
-// Row from global memory (hi plane at `plane`, lo plane plane_stride elements further).
-__device__ inline f32x4 child_tile_global(const UpperQ<uint16_t>& q, const uint16_t* __restrict__ plane,
-                                          int64_t plane_stride, int gq) {
-    const u32x4 h0 = *reinterpret_cast<const u32x4*>(plane + 8 * gq);
-    const u32x4 h1 = *reinterpret_cast<const u32x4*>(plane + 32 + 8 * gq);
-    const u32x4 l0 = *reinterpret_cast<const u32x4*>(plane + plane_stride + 8 * gq);
-    const u32x4 l1 = *reinterpret_cast<const u32x4*>(plane + plane_stride + 32 + 8 * gq);
-    return child_tile_mfma(q.k0, q.k1, h0, h1, l0, l1);
-}
-
 __device__ inline f32x4 child_tile_f32(const UpperQ<float>& q, const float* __restrict__ pyr_row, int gq) {
     float a[16];
     load8_f32(pyr_row + 8 * gq, a);
@@ -120,10 +100,82 @@ __device__ constexpr int slot_lane(int w, int m) {
 }
 constexpr int slot_bit_lane(int J) { return J == 1 ? 1 : J == 2 ? 16 : J == 4 ? 32 : J == 8 ? 2 : J == 16 ? 4 : 8; }
 
+// Children rows of one bf16 tile: hi and lo planes, two k-steps each.
+struct TileRows {
+    u32x4 h0, h1, l0, l1;
+};
+
+__device__ inline TileRows rows_lds(const lds_char_t* lds, int lds_node, int gq) {
+    const lds_char_t* p = lds + lds_node * kLdsNodeBytes;
+    TileRows r;
+    r.h0 = *reinterpret_cast<const lds_u32x4_t*>(p + 16 * gq);
+    r.h1 = *reinterpret_cast<const lds_u32x4_t*>(p + 64 + 16 * gq);
+    r.l0 = *reinterpret_cast<const lds_u32x4_t*>(p + 128 + 16 * gq);
+    r.l1 = *reinterpret_cast<const lds_u32x4_t*>(p + 192 + 16 * gq);
+    return r;
+}
+
+__device__ inline TileRows rows_global(const uint16_t* __restrict__ plane, int64_t plane_stride, int gq) {
+    TileRows r;
+    r.h0 = *reinterpret_cast<const u32x4*>(plane + 8 * gq);
+    r.h1 = *reinterpret_cast<const u32x4*>(plane + 32 + 8 * gq);
+    r.l0 = *reinterpret_cast<const u32x4*>(plane + plane_stride + 8 * gq);
+    r.l1 = *reinterpret_cast<const u32x4*>(plane + plane_stride + 32 + 8 * gq);
+    return r;
+}
+
 // Slot bit J of the tile layout is lane bit slot_bit_lane(J).
 struct TileLanes {
     static constexpr int of(int J) { return slot_bit_lane(J); }
 };
+
+// One scored level of the bf16 walk for the wavefront's 64/SLOTS walks: the tiles are
+// scored in order with the next tile's children rows already loading (from LDS or from global memory, fixed per level), so a
+// tile's load latency hides behind the previous tile's MFMA and LSE work. Returns the
+// score of this lane's candidate slot.
+template <int SLOTS, bool FROM_LDS>
+__device__ inline float score_level_bf16(const UpperQ<uint16_t> (&qf)[64 / SLOTS], const int64_t (&tw)[64 / SLOTS],
+                                         int cand, int sh, int Mc, const lds_char_t* lds, int lds_lvl,
+                                         const uint16_t* __restrict__ plane_lvl, int64_t plane_stride, int n,
+                                         int gq, int wl, int ql, int GQ) {
+    constexpr int TPW = SLOTS / 8, NT = (64 / SLOTS) * TPW;
+    // children row of tile i (w, tau) for this lane: MFMA row n = child (n & 1) of slot
+    // 8 tau + n/2; invalid rows read row 0 and their results are unused
+    auto pick = [&](int i, int& row) -> uint32_t {
+        const int w = i / TPW, tau = i % TPW;
+        const int par = shfl_i(cand, slot_lane<SLOTS>(w, 8 * tau + (n >> 1)));
+        const int child = 2 * par + (n & 1);
+        const bool valid = par >= 0 && child < Mc && child <= (int)(tw[w] >> sh);
+        row = valid ? child : 0;
+        return (uint32_t)ballot(valid);
+    };
+    auto fetch = [&](int row) -> TileRows {
+        if constexpr (FROM_LDS) return rows_lds(lds, lds_lvl + row, gq);
+        else return rows_global(plane_lvl + (int64_t)row * kD, plane_stride, gq);
+    };
+    float my = 0.0f;
+    int row0;
+    uint32_t rok = pick(0, row0);
+    TileRows cur = fetch(row0);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        TileRows nxt = cur;
+        uint32_t rok_next = 0;
+        if (i + 1 < NT) {
+            int rown;
+            rok_next = pick(i + 1, rown);
+            nxt = fetch(rown);
+        }
+        const int w = i / TPW, tau = i % TPW;
+        const f32x4 acc = child_tile_mfma(qf[w].k0, qf[w].k1, cur.h0, cur.h1, cur.l0, cur.l1);
+        float sc[2];
+        pair_scores(acc, rok, gq, n, GQ, sc);
+        if (wl == w && (ql >> 1) == tau) my = (ql & 1) ? sc[1] : sc[0];
+        cur = nxt;
+        rok = rok_next;
+    }
+    return my;
+}
 
 // Walks for positions t0 + ti, ti in [0, NT), of every batch element and KV head.
 // Output per walk (index (b*NT + ti)*Hkv + kvh): cand_out[2K] ascending leaf
@@ -228,6 +280,14 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_kernel(const KT* __r
                 const uint16_t* plane_lvl = planes + (bh_row0 + G.off[lc]) * kD;
                 const float* pyr_lvl = pyr + (bh_row0 + G.off[lc]) * kD;
                 const int lds_lvl = in_lds ? U.lds_first[lc] : 0;
+                if constexpr (sizeof(KT) == 2) {
+                    if (in_lds)
+                        my = score_level_bf16<SLOTS, true>(qf, tw, cand, sh, Mc, lds, lds_lvl, plane_lvl, plane_stride,
+                                                           n, gq, wl, ql, G.GQ);
+                    else
+                        my = score_level_bf16<SLOTS, false>(qf, tw, cand, sh, Mc, lds, lds_lvl, plane_lvl,
+                                                            plane_stride, n, gq, wl, ql, G.GQ);
+                } else {
 #pragma unroll
                 for (int w = 0; w < WPW; ++w) {
                     const int tl = (int)(tw[w] >> sh);         // children <= tl are eligible
@@ -239,17 +299,12 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_kernel(const KT* __r
                         const bool valid = par >= 0 && child < Mc && child <= tl;
                         const int row = valid ? child : 0;      // invalid rows read row 0; their results are unused
                         const uint32_t rows_ok = (uint32_t)ballot(valid);   // bit r: row r valid
-                        f32x4 acc;
-                        if constexpr (sizeof(KT) == 2) {
-                            if (in_lds) acc = child_tile_lds(qf[w], lds, lds_lvl + row, gq);
-                            else acc = child_tile_global(qf[w], plane_lvl + (int64_t)row * kD, plane_stride, gq);
-                        } else {
-                            acc = child_tile_f32(qf[w], pyr_lvl + (int64_t)row * kD, gq);
-                        }
+                        const f32x4 acc = child_tile_f32(qf[w], pyr_lvl + (int64_t)row * kD, gq);
                         float sc[2];
                         pair_scores(acc, rows_ok, gq, n, G.GQ, sc);
                         if (wl == w && (ql >> 1) == tau) my = (ql & 1) ? sc[1] : sc[0];
                     }
+                }
                 }
                 if (cand < 0) my = -INFINITY;
             }
