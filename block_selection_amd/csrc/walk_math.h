@@ -69,6 +69,12 @@ __device__ inline float log2_add_exp2(float a, float b) {
 // one without an eligible right child takes its left child's logit alone. Every lane of
 // row group gq receives both sums over the group's heads (columns n < GQ).
 __device__ inline void pair_scores(const f32x4& acc, uint32_t rows_ok, int gq, int n, int GQ, float sc[2]) {
+    if ((rows_ok & 0xffffu) == 0xffffu && GQ == kMaxGroup) {
+        // every child eligible and every column a head of the group: no masks (same result)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) sc[p] = row16_sum(log2_add_exp2(acc[2 * p], acc[2 * p + 1]));
+        return;
+    }
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const bool lv = (rows_ok >> (4 * gq + 2 * p)) & 1u;
