@@ -8,7 +8,7 @@
 // summary, second paragraph; reading note section 5.1). Here the cluster is a
 // 16-leaf superblock (1024 keys, 128 KiB of bf16 per KV head, held in LDS) and
 // its group of walks:
-//   1. bucket_pass (count): one incidence per run of a walk's ascending leaf
+//   1. bucket_pass (count): one incidence per sibling pair of a walk's leaf
 //      candidates inside a superblock, counted per bucket (batch, KV head,
 //      superblock, range of query positions) in an LDS histogram;
 //   2. scan_groups: bucket offsets and work items of at most kItemMax entries
@@ -31,11 +31,12 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p,
 
 // Counting (fill = 0) or placing (fill = 1) the incidences of one range of kRangeT
 // query positions of batch element blockIdx.y (range blockIdx.x). One incidence per
-// run of a walk's ascending leaf candidates inside a 16-leaf superblock; a walk with
-// at most K candidates has none (its candidates are all kept). The workgroup owns the
+// sibling pair of a walk's leaf candidates (the children of one level-2 survivor); a
+// walk with at most K candidates has none (its candidates are all kept). The workgroup owns the
 // buckets (b, kvh, sb, r) of its range: an LDS histogram counts them, and in the fill
 // pass the same bins, seeded with the bucket offsets, hand out entry positions.
-// Entry = {walk, leaf mask (bits = leaf offsets in the superblock) | first slot << 16}.
+// Entry = {walk, leaf mask | first slot << 16}: the mask holds the superblock offsets of
+// one leaf or of a sibling pair.
 template <int SL>
 __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __restrict__ cand,
                                                           const int32_t* __restrict__ ncand, Geom G,
@@ -66,20 +67,14 @@ __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __rest
         const int leaf = (ok && i < CS && i < nc) ? cand[w * CS + i] : -1;
         const int kvh = (int)(w % G.Hkv);
         const int sbv = (leaf >= 0) ? leaf / kSbLeaves : -1;
-        const int prev = shfl_i(sbv, lane > 0 ? lane - 1 : 0);
-        const bool start = nc > K && leaf >= 0 && (i == 0 || prev != sbv);
-        uint32_t m = (leaf >= 0) ? (1u << (leaf % kSbLeaves)) : 0u;
-        if (fill) {
-            // OR of the run's leaf bits into its first lane (candidates ascend, so a run
-            // is a contiguous stretch of lanes with equal superblock)
-#pragma unroll
-            for (int dd = 1; dd < kSbLeaves; dd <<= 1) {
-                const int src = (lane + dd < 64) ? lane + dd : lane;
-                const uint32_t om = (uint32_t)shfl_i((int)m, src);
-                const int osb = shfl_i(sbv, src);
-                if (i + dd < SL && sbv >= 0 && osb == sbv) m |= om;
-            }
-        }
+        // candidates ascend and come as sibling pairs (2c, then 2c+1 if eligible): an entry
+        // starts at an even leaf, or at an odd one whose sibling is not a candidate
+        const int prv = shfl_i(leaf, lane > 0 ? lane - 1 : 0);
+        const int nxt = shfl_i(leaf, lane < 63 ? lane + 1 : lane);
+        const bool even = (leaf & 1) == 0;
+        const bool start = nc > K && leaf >= 0 && (even || i == 0 || prv != leaf - 1);
+        const bool pair = even && i + 1 < SL && nxt == leaf + 1;
+        const uint32_t m = (leaf >= 0) ? ((pair ? 3u : 1u) << (leaf % kSbLeaves)) : 0u;
         if (start) {
             const uint32_t pos = atomicAdd(&bins[kvh * CG.NSB + sbv], 1u);
             if (fill) entries[pos] = make_uint2((uint32_t)w, m | ((uint32_t)i << 16));
@@ -151,65 +146,38 @@ template __global__ void bucket_pass_kernel<64>(const int32_t*, const int32_t*, 
 // consecutive rows hit distinct banks.
 __device__ inline int sb_lds_offset(int r, int chunk) { return r * 128 + ((chunk ^ (r & 7)) << 4); }
 
-// Exact LSE (base 2) over the raw keys <= t of NL leaves (bits = leaf offsets in the
-// superblock) for one walk, summed over the group's heads. The NL leaves are
-// processed side by side so their MFMA and reduction chains overlap.
-template <int NL>
-__device__ inline void score_leaves(const lds_char_t* lds, int key_base, const int bits[NL], int t,
-                                    const bf16x8 q0, const bf16x8 q1, int n, int gq, int GQ, float out[NL]) {
-    f32x4 acc[NL][4];
-#pragma unroll
-    for (int j = 0; j < NL; ++j)
-#pragma unroll
-        for (int tau = 0; tau < 4; ++tau) {
-            const int r = bits[j] * kC + 16 * tau + n;
-            const u32x4 a0 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, gq));
-            const u32x4 a1 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, 4 + gq));
-            f32x4 c = {0.f, 0.f, 0.f, 0.f};
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), q0, c, 0, 0, 0);
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), q1, c, 0, 0, 0);
-            acc[j][tau] = c;
-        }
-    // lane holds keys key0 + 16*tau + 4*gq + r of head n; keys with offset > lim are masked
-    int lim[NL];
-#pragma unroll
-    for (int j = 0; j < NL; ++j) lim[j] = min(t - (key_base + bits[j] * kC), kC - 1);
-    leaf_lse_from_acc<NL>(acc, lim, n, gq, GQ, out);
-}
-
-// Scores of every leaf of `mask` for one walk. The i-th leaf's score (mask order =
-// ascending candidate slots) ends up in lane i and is written with one store per
-// entry, so the loop over leaves issues no memory operation (that keeps the wait
-// counters exact and the next entries' query prefetches in flight).
+// Scores of the leaves of one entry (mask: one leaf, or a sibling pair at bits b, b+1)
+// for one walk: lane 0 writes the first leaf's score, lane 16 the second's, every other
+// lane stores into the sink, so each entry issues exactly one store instruction (that
+// keeps the wait counters exact and the next entries' query prefetches in flight).
+// An empty mask (padding entry) scores nothing.
 __device__ inline void score_entry(const lds_char_t* lds, int key_base, uint32_t mask, int t,
                                    const bf16x8 q0, const bf16x8 q1, int n, int gq, int lane, int GQ,
                                    float* __restrict__ score_row, float* __restrict__ sink) {
-    const int nslots = __popc(mask);
-    float mine = 0.0f;
-    int slot = 0;
-    while (mask) {
+    float v = 0.0f;
+    bool two = false;
+    if (mask) {
         const int b0 = __builtin_ctz(mask);
-        mask &= mask - 1;
-        if (mask) {
-            const int b1 = __builtin_ctz(mask);
-            mask &= mask - 1;
-            const int bits[2] = {b0, b1};
-            float out[2];
-            score_leaves<2>(lds, key_base, bits, t, q0, q1, n, gq, GQ, out);
-            mine = (lane == slot) ? out[0] : mine;
-            mine = (lane == slot + 1) ? out[1] : mine;
-            slot += 2;
-        } else {
-            const int bits[1] = {b0};
-            float out[1];
-            score_leaves<1>(lds, key_base, bits, t, q0, q1, n, gq, GQ, out);
-            mine = (lane == slot) ? out[0] : mine;
-            slot += 1;
-        }
+        two = (mask >> (b0 + 1)) & 1u;
+        const int bits[2] = {b0, two ? b0 + 1 : b0};
+        f32x4 acc[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau) {
+                const int r = bits[j] * kC + 16 * tau + n;
+                const u32x4 a0 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, gq));
+                const u32x4 a1 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, 4 + gq));
+                f32x4 c = {0.f, 0.f, 0.f, 0.f};
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), q0, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), q1, c, 0, 0, 0);
+                acc[j][tau] = c;
+            }
+        const int lim[2] = {min(t - (key_base + bits[0] * kC), kC - 1), min(t - (key_base + bits[1] * kC), kC - 1)};
+        v = leaf_lse_pair(acc, lim, n, gq, GQ);
     }
-    // every lane stores (lanes without a score into the sink) so the store count is fixed
-    float* dst = (lane < nslots) ? score_row + lane : sink + lane;
-    *dst = mine;
+    float* dst = (mask && lane == 0) ? score_row : ((two && lane == 16) ? score_row + 1 : sink + lane);
+    *dst = v;
 }
 
 // B fragments of one walk's queries: head n of the group, dims {8gq..8gq+7} and
