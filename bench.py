@@ -84,6 +84,58 @@ def walk_counts(N: int, topk: int, GQ: int, Hkv: int, C: int = 64):
 TRANSCENDENTAL_PEAK = 256 * 32 * 2.4e9
 
 
+# sources of the two walk kernels (a traffic figure is only valid for the code it was taken on)
+LEAF_SOURCES = ["cluster.hip", "walk_math.h", "lanes.h", "pisa_device.h"]
+UPPER_SOURCES = ["upper.hip", "walk_math.h", "lanes.h", "pisa_device.h"]
+COPY_BYTES = 256 << 20          # the calibration copy: 256 MiB read + 256 MiB written
+
+
+def write_traffic(fetch_dir: str, write_dir: str, workload: str = "long256k") -> None:
+    """Summarise two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of
+    `bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-extras --copy-calibration` into
+    profiles/hbm_traffic.json: HBM bytes per launch of the two walk kernels, each counter
+    scaled by what it reads for the calibration copy of known size."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not path:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        vals = {}
+        with open(path[0]) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+
+    def find(tab, key):
+        hits = [v for k, v in tab.items() if key in k]
+        if not hits:
+            raise SystemExit(f"kernel {key} not in the counter runs")
+        return float(np.mean(hits[0]))
+
+    copy_f, copy_w = find(fetch, "copyBuffer"), find(write, "copyBuffer")
+    fs, wsc = COPY_BYTES / (copy_f * 1024), COPY_BYTES / (copy_w * 1024)
+    out = {"_calibration": {
+        "copy_bytes_each_way": COPY_BYTES, "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
+        "fetch_scale": fs, "write_scale": wsc,
+        "command": ("rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> -o run -- "
+                    "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-extras --copy-calibration; "
+                    "python3 bench.py --write-traffic <fetch dir> <write dir>")}}
+    for key, srcs in (("leaf_cluster_kernel", LEAF_SOURCES), ("walk_upper_kernel<unsigned short, 16>", UPPER_SOURCES)):
+        f_kib, w_kib = find(fetch, key), find(write, key)
+        out[f"{key.split('<')[0]}:{workload}"] = {
+            "fetch_kib": f_kib, "write_kib": w_kib,
+            "bytes_per_launch": f_kib * 1024 * fs + w_kib * 1024 * wsc,
+            "source_hash": _hash_sources(srcs)}
+    with open(os.path.join(PROFILES, "hbm_traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def measured_traffic(kernel_key: str, src_hash: str):
     """HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters (already scaled by
     the copy-kernel calibration), or None when the kernel sources changed since."""
@@ -134,7 +186,13 @@ def main():
     ap.add_argument("--cpu-positions", type=int, default=65536)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device-to-device copy first (reference kernel for HBM counters)")
+    ap.add_argument("--decode-only", action="store_true", help="time only the decode workload")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs into profiles/hbm_traffic.json (no GPU)")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the selection shards by KV head or query range with no exchange, see the design notes)",
@@ -223,6 +281,10 @@ def main():
                 hip.hipEventDestroy(ctypes.c_void_p(e))
         return total_ms, build, walk, upper, leaf
 
+    if args.decode_only:
+        print(json.dumps({"decode": decode_bench(torch, ops, synth, dev, log)}), flush=True)
+        return
+
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -242,8 +304,8 @@ def main():
     wc = walk_counts(N, wl.topk, GQ, wl.Hkv)
     clustered = wl.dtype == "bf16"
     kname = "leaf_cluster_kernel" if clustered else "leaf_walk_kernel"
-    src_hash = _hash_sources(["cluster.hip", "walk_math.h", "lanes.h", "pisa_device.h"])
-    traffic = measured_traffic(f"{kname}:{wl.name}", src_hash)
+    traffic = measured_traffic(f"{kname}:{wl.name}", _hash_sources(LEAF_SOURCES))
+    upper_traffic = measured_traffic(f"walk_upper_kernel:{wl.name}", _hash_sources(UPPER_SOURCES))
     # dominant kernel: the clustered leaf scoring; its duration is measured with HIP events
     # on the stream the library launches on, around a separate timed pass of the same call
     leaf_ms = float(np.mean(leaf_ms_steps))
@@ -263,6 +325,20 @@ def main():
     }
     walk_s = walk_ms.mean() / 1e3
     upper_transc = wc["upper_logits"] + wc["upper_lse"]
+    upper_ms = float(np.mean(upper_ms))
+    # the second kernel: the coarse-to-fine walk above the leaves (one exp per child logit and
+    # one log per candidate LSE, the pairwise form log2(1 + 2^d) of two children)
+    roofline_upper = {
+        "kernel": "walk_upper_kernel (scored levels above the leaves)",
+        "bound": "alu",
+        "achieved": upper_transc / (upper_ms / 1e3) / 1e9,
+        "peak": TRANSCENDENTAL_PEAK / 1e9,
+        "unit": "G transcendental/s",
+        "frac": upper_transc / (upper_ms / 1e3) / TRANSCENDENTAL_PEAK,
+        "traffic": upper_traffic,
+        "algorithmic_per_launch": upper_transc,
+        "launch_ms": upper_ms,
+    }
     elt = 2 if wl.dtype == "bf16" else 4
     # the pyramid build is HBM-bound: compulsory bytes = keys read once + every node written once
     build_bytes = wl.B * N * wl.Hkv * wl.d * elt + wl.B * wl.Hkv * ops.pyramid_nodes(dims, N) * wl.d * 4
@@ -280,7 +356,7 @@ def main():
         hbm["leaf_kernel_measured_frac_of_8TBs"] = traffic / (leaf_ms / 1e3) / 1e9 / HBM_PEAK_GBS
     work = {
         "select_ms": walk_ms.mean(),
-        "upper_walk_ms": float(np.mean(upper_ms)),
+        "upper_walk_ms": upper_ms,
         "leaf_scoring_ms": leaf_ms,
         "all_transcendentals_per_step": transc + upper_transc,
         "select_transcendental_frac": (transc + upper_transc) / walk_s / TRANSCENDENTAL_PEAK,
@@ -306,6 +382,7 @@ def main():
         "latency_ms": {"mean": ms_per_step, "median_build_plus_walk": float(np.median(build_ms + walk_ms)),
                        "min_build_plus_walk": float(np.min(build_ms + walk_ms))},
         "roofline": roofline,
+        "roofline_upper": roofline_upper,
         "hbm": hbm,
         "work": work,
     }
@@ -363,8 +440,21 @@ def decode_bench(torch, ops, synth, dev, log):
         torch.cuda.synchronize()
         if rep:
             times.append([ev[s].elapsed_time(ev[s + 1]) * 1e3 for s in range(steps)])
+    # launch floor: an empty kernel (torch's zero-cycle sleep) enqueued and timed the same way
+    fl = []
+    for rep in range(2):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for s in range(steps):
+            torch.cuda._sleep(0)
+            ev[s + 1].record(stream)
+        torch.cuda.synchronize()
+        if rep:
+            fl = [ev[s].elapsed_time(ev[s + 1]) * 1e3 for s in range(steps)]
     per = np.array(times)
     res = {"context": N0, "steps": steps, "K": wl.topk, "us_per_step_mean": float(per.mean()),
+           "empty_kernel_launch_us": float(np.mean(fl)),
            "us_per_step_median": float(np.median(per)), "us_per_step_p90": float(np.percentile(per, 90)),
            "steps_per_s": 1e6 / float(per.mean())}
     log(f"decode: {res['us_per_step_mean']:.1f} us/step")

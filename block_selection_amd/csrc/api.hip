@@ -32,7 +32,7 @@ __global__ void bucket_pass_kernel(const int32_t*, const int32_t*, Geom, Cluster
                                    const uint32_t*, uint2*, int);
 __global__ void scan_groups_kernel(const uint32_t*, ClusterGeom, uint32_t*, int4*, uint32_t*);
 __global__ void leaf_cluster_kernel(const uint16_t*, const uint16_t*, Geom, ClusterGeom, int64_t,
-                                    const int4*, const uint2*, const uint32_t*, float*, float*);
+                                    const int4*, const uint2*, uint32_t*, float*, float*);
 template <int SLOTS>
 __global__ void final_topk_kernel(const int32_t*, const int32_t*, const float*, Geom, int64_t, int32_t*);
 

@@ -14,7 +14,7 @@
 //   2. scan_groups: bucket offsets and work items of at most kItemMax entries
 //      of one (batch, KV head, superblock) group;
 //   3. bucket_pass (fill): incidences written as entries at their offsets;
-//   4. leaf_cluster: persistent workgroups take items; a workgroup stages the
+//   4. leaf_cluster: persistent workgroups take items from a counter; a workgroup stages the
 //      superblock's keys in LDS once, then each wavefront takes entries (the
 //      next entry's queries are prefetched while the current one is scored)
 //      and scores every leaf of the entry's mask from LDS;
@@ -88,36 +88,42 @@ __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __rest
 
 // One workgroup: entry offsets of every bucket (groups (b, kvh, sb) in order, ranges
 // inside a group consecutive) and work items of at most kItemMax entries of one group.
-// Buckets are stored range-major (r * ngroups + g), so that the threads, one group each,
-// read consecutive words.
-// meta[0] = number of items, meta[1] = number of entries.
+// Items holding kItemMax entries come first, the smaller remainders after them, so
+// that the workgroups taking items in order finish together.
+// meta[0] = number of items, meta[1] = number of entries, meta[2] = 0 (the counter the
+// scoring workgroups take items from).
 __global__ __launch_bounds__(1024) void scan_groups_kernel(const uint32_t* __restrict__ counts, ClusterGeom CG,
                                                            uint32_t* __restrict__ offsets,
                                                            int4* __restrict__ items,
                                                            uint32_t* __restrict__ meta) {
-    __shared__ uint32_t s_e[1024], s_i[1024];
+    __shared__ uint32_t s_e[1024], s_f[1024], s_p[1024];
     const int tid = threadIdx.x;
     const int per = (CG.ngroups + 1023) / 1024;
     const int lo = tid * per, hi = min(CG.ngroups, lo + per);
-    uint32_t se = 0, si = 0;
+    uint32_t se = 0, sf = 0, sp = 0;
     for (int g = lo; g < hi; ++g) {
         uint32_t tot = 0;
         for (int r = 0; r < CG.NR; ++r) tot += counts[(int64_t)r * CG.ngroups + g];
         se += tot;
-        si += (tot + kItemMax - 1) / kItemMax;
+        sf += tot / kItemMax;              // full items
+        sp += (tot % kItemMax) ? 1u : 0u;  // remainder item
     }
     s_e[tid] = se;
-    s_i[tid] = si;
+    s_f[tid] = sf;
+    s_p[tid] = sp;
     __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {       // inclusive Hillis-Steele scan
+    for (int d = 1; d < 1024; d <<= 1) {       // inclusive Hillis-Steele scans
         const uint32_t ae = (tid >= d) ? s_e[tid - d] : 0u;
-        const uint32_t ai = (tid >= d) ? s_i[tid - d] : 0u;
+        const uint32_t af = (tid >= d) ? s_f[tid - d] : 0u;
+        const uint32_t ap = (tid >= d) ? s_p[tid - d] : 0u;
         __syncthreads();
         s_e[tid] += ae;
-        s_i[tid] += ai;
+        s_f[tid] += af;
+        s_p[tid] += ap;
         __syncthreads();
     }
-    uint32_t eoff = s_e[tid] - se, ioff = s_i[tid] - si;
+    const uint32_t nfull = s_f[1023];
+    uint32_t eoff = s_e[tid] - se, foff = s_f[tid] - sf, poff = nfull + s_p[tid] - sp;
     for (int g = lo; g < hi; ++g) {
         const uint32_t g0 = eoff;
         for (int r = 0; r < CG.NR; ++r) {
@@ -125,12 +131,15 @@ __global__ __launch_bounds__(1024) void scan_groups_kernel(const uint32_t* __res
             eoff += counts[(int64_t)r * CG.ngroups + g];
         }
         const uint32_t tot = eoff - g0;
-        for (uint32_t p = 0; p * kItemMax < tot; ++p)
-            items[ioff++] = make_int4(g, (int)(g0 + p * kItemMax), (int)min((uint32_t)kItemMax, tot - p * kItemMax), 0);
+        for (uint32_t p = 0; p * kItemMax < tot; ++p) {
+            const uint32_t len = min((uint32_t)kItemMax, tot - p * kItemMax);
+            items[(len == kItemMax) ? foff++ : poff++] = make_int4(g, (int)(g0 + p * kItemMax), (int)len, 0);
+        }
     }
     if (tid == 1023) {
-        meta[0] = s_i[1023];
+        meta[0] = nfull + s_p[1023];
         meta[1] = s_e[1023];
+        meta[2] = 0u;
     }
 }
 
@@ -192,7 +201,7 @@ __device__ inline void load_q(const uint16_t* __restrict__ q, int64_t bt, int Hq
 
 __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, Geom G, ClusterGeom CG, int64_t NT,
-    const int4* __restrict__ items, const uint2* __restrict__ entries, const uint32_t* __restrict__ meta,
+    const int4* __restrict__ items, const uint2* __restrict__ entries, uint32_t* __restrict__ meta,
     float* __restrict__ score, float* __restrict__ sink) {
     static_assert(kItemMax <= 64 * (kClusterThreads / 64), "a wavefront holds its entries in one VGPR pair");
     extern __shared__ u32x4 lds_u4[];
@@ -200,10 +209,17 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = kClusterThreads / 64;
     const int n = lane & 15, gq = lane >> 4;
     const int CS = 2 * G.topk;
+    __shared__ uint32_t s_item;
     const uint32_t n_items = meta[0];
     const int64_t row_stride = (int64_t)G.Hkv * kD;
 
-    for (uint32_t it = blockIdx.x; it < n_items; it += gridDim.x) {
+    // items are taken from a counter, so a workgroup that finishes early takes the next one
+    for (;;) {
+        __syncthreads();   // the previous item's readers are done with LDS and s_item
+        if (threadIdx.x == 0) s_item = atomicAdd(&meta[2], 1u);
+        __syncthreads();
+        const uint32_t it = s_item;
+        if (it >= n_items) break;
         const int4 item = items[it];
         const int grp = item.x;
         const int sb = grp % CG.NSB;
@@ -225,7 +241,6 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
         qload(0, qa0, qb0);
         qload(1, qa1, qb1);
         qload(2, qa2, qb2);
-        __syncthreads();   // the previous item's readers are done with LDS
         for (int idx = tid; idx < kSbKeys * 8; idx += kClusterThreads) {
             const int r = idx >> 3, ch = idx & 7;
             const int key = key_base + r;
