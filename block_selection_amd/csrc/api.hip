@@ -22,6 +22,10 @@ __global__ void split_planes_kernel(const float*, uint16_t*, int64_t);
 template <typename KT, int SLOTS>
 __global__ void walk_upper_kernel(const KT*, const uint16_t*, const float*, Geom, UpperCfg, int64_t,
                                   int64_t, int32_t*, int32_t*);
+template <int SLOTS>
+__global__ void walk_upper_delta_kernel(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg, int64_t,
+                                        int64_t, int32_t*, int32_t*);
+__global__ void delta_planes_kernel(const float*, uint16_t*, Geom);
 template <typename KT>
 __global__ void leaf_walk_kernel(const KT*, const KT*, Geom, int64_t, int64_t, const int32_t*,
                                  const int32_t*, int32_t*);
@@ -42,7 +46,8 @@ static size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace carve-up for `walks` walks over a pyramid of P rows per (batch, head).
 struct Workspace {
-    uint16_t* planes;    // [2][B*Hkv*P*64] bf16 hi/lo planes (bf16 inputs only)
+    uint16_t* planes;    // [2][B*Hkv*P*64] bf16 hi/lo planes of the summaries (bf16 inputs only)
+    uint16_t* dplanes;   // [2][B*Hkv*P*64] bf16 hi/lo planes of delta(c) = s(2c) - s(c), levels >= 2
     int32_t* cand;       // [walks][2K] leaf candidates
     int32_t* ncand;      // [walks]
     // clustered leaf scoring (prefill, bf16 inputs)
@@ -82,6 +87,7 @@ static Workspace carve(const pisa_dims* d, int64_t N, int64_t P, bool decode, ch
     }
     const size_t planes = (d->dtype == PISA_DTYPE_BF16) ? (size_t)2 * d->B * d->Hkv * P * kD * 2 : 0;
     w.planes = (uint16_t*)take(planes);
+    w.dplanes = (uint16_t*)take(planes);
     w.cand = (int32_t*)take((size_t)walks * cs * sizeof(int32_t));
     w.ncand = (int32_t*)take((size_t)walks * sizeof(int32_t));
     const int64_t m1 = (N + kC - 1) / kC;
@@ -191,6 +197,54 @@ static UpperCfg upper_cfg(const Geom& G) {
     return U;
 }
 
+// LDS staging for the delta-form walk: the delta rows of the candidate levels from the
+// first level that can be scored (the highest with more than K nodes) downward, while
+// they fit.
+static UpperCfg upper_cfg_delta(const Geom& G) {
+    UpperCfg U;
+    memset(&U, 0, sizeof(U));
+    U.j_lo = 1;
+    U.j_hi = 0;
+    int top = 0;
+    for (int l = G.L; l >= 2; --l) {
+        if (G.M[l] > G.topk) { top = l; break; }
+    }
+    if (top < 2) return U;
+    int nodes = 0, j_lo = top + 1;
+    while (j_lo - 1 >= 2 && nodes + G.M[j_lo - 1] <= kLdsDeltaBudgetNodes) {
+        --j_lo;
+        nodes += G.M[j_lo];
+    }
+    if (j_lo > top) return U;
+    U.j_lo = j_lo;
+    U.j_hi = top;
+    int slot = 0;
+    for (int j = j_lo; j <= top; ++j) { U.lds_first[j] = slot; slot += G.M[j]; }
+    U.lds_nodes = slot;
+    return U;
+}
+
+template <int SLOTS>
+static int launch_upper_delta(const uint16_t* q, const Geom& G, const UpperCfg& U, int64_t t0, int64_t NT,
+                              const Workspace& W, int cus, hipStream_t s) {
+    constexpr int WPW = 64 / SLOTS;
+    constexpr int nwaves = kUpperThreads / 64;
+    const int64_t groups = (NT + WPW - 1) / WPW;
+    const int bh = G.B * G.Hkv;
+    // one workgroup per CU (LDS-bound), a multiple of 8 so that XCDs split evenly
+    int64_t need = (int64_t)bh * ((groups + nwaves - 1) / nwaves);
+    int64_t nwg = need < cus ? need : cus;
+    nwg = (nwg + 7) / 8 * 8;
+    if (nwg < bh) nwg = bh;
+    const size_t lds = (size_t)U.lds_nodes * kLdsNodeBytes;
+    const void* fn = (const void*)walk_upper_delta_kernel<SLOTS>;
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return PISA_ERR_HIP;
+    hipLaunchKernelGGL((walk_upper_delta_kernel<SLOTS>), dim3((unsigned)nwg), dim3(kUpperThreads), lds, s, q,
+                       W.planes, W.dplanes, G, U, t0, NT, W.cand, W.ncand);
+    return PISA_OK;
+}
+
 template <typename KT, int SLOTS>
 static int launch_upper(const KT* q, const uint16_t* planes, const float* pyr, const Geom& G,
                         const UpperCfg& U, int64_t t0, int64_t NT, const Workspace& W, int cus, hipStream_t s) {
@@ -269,22 +323,35 @@ static int select_impl(const KT* q, const KT* k, const float* pyr, const Geom& G
                        int64_t NT, int32_t* out, const Workspace& W, hipStream_t s, void* const* ev) {
     int rc, cus = 256;
     if ((rc = device_cus(&cus)) != PISA_OK) return rc;
-    UpperCfg U = upper_cfg(G);
-    if (sizeof(KT) == 2) {
+    const int slots = 2 * G.topk;
+    if constexpr (sizeof(KT) == 2) {
+        // summary planes (the candidates' own rows, ragged children) and delta planes
         const int64_t n = (int64_t)G.B * G.Hkv * G.P * kD;
         int64_t grid = (n + 255) / 256;
         if (grid > 8192) grid = 8192;
         hipLaunchKernelGGL(split_planes_kernel, dim3((unsigned)grid), dim3(256), 0, s, pyr, W.planes, n);
+        int64_t drows = 0;
+        for (int l = 2; l <= G.L; ++l) drows += G.M[l];
+        int64_t dgrid = (drows * kD + 255) / 256;
+        if (dgrid > 4096) dgrid = 4096;
+        if (dgrid > 0)
+            hipLaunchKernelGGL(delta_planes_kernel, dim3((unsigned)dgrid, (unsigned)(G.B * G.Hkv)), dim3(256), 0, s,
+                               pyr, W.dplanes, G);
+        const UpperCfg U = upper_cfg_delta(G);
+        mark(ev, 0, s);
+        if (slots <= 16) rc = launch_upper_delta<16>(q, G, U, t0, NT, W, cus, s);
+        else if (slots <= 32) rc = launch_upper_delta<32>(q, G, U, t0, NT, W, cus, s);
+        else rc = launch_upper_delta<64>(q, G, U, t0, NT, W, cus, s);
     } else {
+        UpperCfg U = upper_cfg(G);
         U.j_lo = 1;
         U.j_hi = 0;
         U.lds_nodes = 0;
+        mark(ev, 0, s);
+        if (slots <= 16) rc = launch_upper<KT, 16>(q, W.planes, pyr, G, U, t0, NT, W, cus, s);
+        else if (slots <= 32) rc = launch_upper<KT, 32>(q, W.planes, pyr, G, U, t0, NT, W, cus, s);
+        else rc = launch_upper<KT, 64>(q, W.planes, pyr, G, U, t0, NT, W, cus, s);
     }
-    const int slots = 2 * G.topk;
-    mark(ev, 0, s);
-    if (slots <= 16) rc = launch_upper<KT, 16>(q, W.planes, pyr, G, U, t0, NT, W, cus, s);
-    else if (slots <= 32) rc = launch_upper<KT, 32>(q, W.planes, pyr, G, U, t0, NT, W, cus, s);
-    else rc = launch_upper<KT, 64>(q, W.planes, pyr, G, U, t0, NT, W, cus, s);
     if (rc != PISA_OK) return rc;
     mark(ev, 1, s);
     const int64_t walks = (int64_t)G.B * NT * G.Hkv;

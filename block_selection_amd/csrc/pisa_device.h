@@ -51,6 +51,7 @@ __host__ __device__ inline int64_t covered(int l, int64_t i, int64_t n) {
 constexpr int kLdsNodeBytes = 272;
 constexpr int kUpperThreads = 1024;
 constexpr int kLdsBudgetNodes = 480;     // 480 * 272 B = 127.5 KiB
+constexpr int kLdsDeltaBudgetNodes = 504; // 504 * 272 B = 133.9 KiB (delta-form walk)
 struct UpperCfg {
     int32_t j_lo, j_hi;
     int32_t lds_first[kMaxLevels + 1];

@@ -336,6 +336,311 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_kernel(const KT* __r
     }
 }
 
+// ------------------------------------------------------ delta-form bf16 walk --
+// The bf16 walk scores a candidate from ONE summary row, delta(c) = s(2c) - s(c), and a
+// carried head-summed logit P(c) (walk_math.h, "delta form"): half the rows, MFMAs and
+// gather traffic of scoring from both children. The candidate's own summary is read
+// only at the first scored level of a walk (to start P), and the children of the one
+// ragged node of a level (a partial right child) are read directly.
+
+// delta planes: row c of level l >= 2 holds hi/lo bf16 planes of
+// (s_{l-1}(2c) - s_l(c)) * log2(e)/8, rounded like the summary planes. Grid: (chunks, B*Hkv).
+__global__ __launch_bounds__(256) void delta_planes_kernel(const float* __restrict__ pyr,
+                                                           uint16_t* __restrict__ dplanes, Geom G) {
+    const int bh = blockIdx.y;
+    int64_t total = 0;
+    for (int l = 2; l <= G.L; ++l) total += (int64_t)G.M[l] * kD;
+    const int64_t plane_stride = (int64_t)G.B * G.Hkv * G.P * kD;
+    const float* base = pyr + (int64_t)bh * G.P * kD;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        const int e = (int)(i & (kD - 1));
+        int64_t r = i >> 6;
+        int l = 2;
+        while (r >= G.M[l]) { r -= G.M[l]; ++l; }
+        const int64_t prow = G.off[l] + r, crow = G.off[l - 1] + 2 * r;
+        uint32_t hi, lo;
+        split_scaled(base[crow * kD + e] - base[prow * kD + e], hi, lo);
+        const int64_t o = ((int64_t)bh * G.P + prow) * kD + e;
+        dplanes[o] = (uint16_t)hi;
+        dplanes[plane_stride + o] = (uint16_t)lo;
+    }
+}
+
+// Slot layout: slot m of walk w (SLOTS = 16 * TPW slots per walk) lives in lane
+//   16 * ((m >> 2) & 3) + 4 * (w * TPW + (m >> 4)) + (m & 3),
+// so tile u = w * TPW + (m >> 4) holds slots 16 (m >> 4) .. + 15 of walk w in MFMA rows
+// 0..15, and after head_sum4 the sum of row 4g + i sits in lane (g, n) for n & 3 = i:
+// in place for the lanes with (n >> 2) == u. Slot bits 0..5 map to lane bits 0, 1, 4, 5,
+// 2, 3: every bitonic partner is a DPP or permlane move away.
+template <int SLOTS>
+__device__ constexpr int dslot_lane(int w, int m) {
+    return 16 * ((m >> 2) & 3) + 4 * (w * (SLOTS / 16) + (m >> 4)) + (m & 3);
+}
+constexpr int dslot_bit_lane(int J) { return J == 1 ? 1 : J == 2 ? 2 : J == 4 ? 16 : J == 8 ? 32 : J == 16 ? 4 : 8; }
+struct DeltaLanes {
+    static constexpr int of(int J) { return dslot_bit_lane(J); }
+};
+
+// Selection key that also records the slot a candidate came from: selection order
+// (score desc, node asc); low word (2^26 - 1 - node) << 6 | slot, 0 for an empty slot.
+// Nodes of levels >= 2 are below 2^24.
+__device__ inline uint64_t slot_key(float s, int node, int slot) {
+    const uint32_t u = __float_as_uint(s + 0.0f);
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t low = (node >= 0) ? (((uint32_t)((1 << 26) - 1 - node) << 6) | (uint32_t)slot) : 0u;
+    return ((uint64_t)o << 32) | low;
+}
+__device__ inline int key_node(uint32_t low) { return (low >> 6) ? (1 << 26) - 1 - (int)(low >> 6) : -1; }
+__device__ inline int key_slot(uint32_t low) { return (int)(low & 63u); }
+
+template <int SLOTS>
+__global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const uint16_t* __restrict__ q,
+                                                                         const uint16_t* __restrict__ splanes,
+                                                                         const uint16_t* __restrict__ dplanes,
+                                                                         Geom G, UpperCfg U, int64_t t0, int64_t NT,
+                                                                         int32_t* __restrict__ cand_out,
+                                                                         int32_t* __restrict__ ncand_out) {
+    constexpr int WPW = 64 / SLOTS, TPW = SLOTS / 16, NTILE = WPW * TPW;
+    static_assert(NTILE == 4, "four 16-row tiles per wavefront");
+    extern __shared__ u32x4 lds_u4[];
+    lds_char_t* lds = (lds_char_t*)lds_u4;
+    // XCD-aware placement: workgroup i runs on XCD i % 8; when B*Hkv divides 8, every
+    // XCD serves a single (batch, KV head), so its L2 holds that head's finer levels only.
+    const int BH = G.B * G.Hkv;
+    const int id = blockIdx.x, nwg = gridDim.x;
+    int bh, peer, npeers;
+    if (BH <= 8 && 8 % BH == 0 && nwg % 8 == 0) {
+        bh = (id % 8) % BH;
+        peer = (id / 8) * (8 / BH) + (id % 8) / BH;
+        npeers = nwg / BH;
+    } else {
+        bh = id % BH;
+        peer = id / BH;
+        npeers = (nwg - bh + BH - 1) / BH;
+    }
+    const int b = bh / G.Hkv, kvh = bh % G.Hkv;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+    const int gq = lane >> 4, n = lane & 15;
+    const int u = (lane >> 2) & 3;                           // tile whose results land in this lane
+    const int wl = u / TPW;                                  // this lane's walk
+    const int ml = 16 * (u % TPW) + 4 * gq + (lane & 3);     // this lane's slot
+    const int K = G.topk;
+    const int64_t plane_stride = (int64_t)G.B * G.Hkv * G.P * kD;
+    const int64_t bh_row0 = (int64_t)bh * G.P;
+
+    // stage the delta rows of the coarse candidate levels: node i of level j -> LDS slot
+    // lds_first[j] + i, planes hi|lo
+    for (int j = U.j_lo; j <= U.j_hi; ++j) {
+        const int mj = G.M[j];
+        for (int c = threadIdx.x; c < mj * 16; c += blockDim.x) {
+            const int node = c >> 4, part = c & 15;
+            const uint16_t* src = dplanes + (part >> 3) * plane_stride + (bh_row0 + G.off[j] + node) * kD +
+                                  (part & 7) * 8;
+            *reinterpret_cast<lds_u32x4_t*>(lds + (U.lds_first[j] + node) * kLdsNodeBytes + (part >> 3) * 128 +
+                                            (part & 7) * 16) = *reinterpret_cast<const u32x4*>(src);
+        }
+    }
+    __syncthreads();
+
+    uint64_t wmask[WPW];
+#pragma unroll
+    for (int w = 0; w < WPW; ++w) {
+        uint64_t mk = 0;
+        for (int m = 0; m < SLOTS; ++m) mk |= 1ull << dslot_lane<SLOTS>(w, m);
+        wmask[w] = mk;
+    }
+    const bool full_group = G.GQ == kMaxGroup;
+
+    const int64_t ngroups = (NT + WPW - 1) / WPW;
+    for (int64_t grp = (int64_t)peer * nwaves + wave; grp < ngroups; grp += (int64_t)npeers * nwaves) {
+        UpperQ<uint16_t> qf[WPW];
+        int64_t tw[WPW];
+#pragma unroll
+        for (int w = 0; w < WPW; ++w) {
+            const int64_t ti = grp * WPW + w;
+            tw[w] = t0 + ti;
+            const bool ok = ti < NT && n < G.GQ;
+            const uint16_t* qrow = q + (((int64_t)b * NT + (ti < NT ? ti : 0)) * G.Hq + (int64_t)kvh * G.GQ + n) * kD;
+            qf[w].load(qrow, ok, gq);
+        }
+        const int64_t my_ti = grp * WPW + wl;
+        const int64_t my_t = t0 + my_ti;
+        const bool my_ok = my_ti < NT;
+
+        uint32_t surv_low = 0;     // sorted key low word in slots < K: the survivors
+        float Pa = 0.0f, Pb = 0.0f;  // head-summed logits of this slot's candidate's children
+        uint32_t pk = 0;           // walks whose candidates' P is known (scored at the level above)
+        for (int l = G.L; l >= 2; --l) {
+            int cand;
+            float P = 0.0f;
+            if (l == G.L) {
+                cand = (ml == 0 && my_ok) ? 0 : -1;
+            } else {
+                const uint32_t lowk = (uint32_t)shfl_i((int)surv_low, dslot_lane<SLOTS>(wl, ml >> 1));
+                const int pnode = key_node(lowk);
+                const int child = 2 * pnode + (ml & 1);
+                const bool ok = ml < 2 * K && pnode >= 0 && child < G.M[l] &&
+                                child <= (int)(my_t >> (kLog2C + l - 1));
+                cand = ok ? child : -1;
+                const int src = dslot_lane<SLOTS>(wl, key_slot(lowk));
+                const float pa = shfl_f(Pa, src), pb = shfl_f(Pb, src);
+                P = (ml & 1) ? pb : pa;
+            }
+            const uint64_t vm = ballot(cand >= 0);
+            uint32_t scored = 0;
+#pragma unroll
+            for (int w = 0; w < WPW; ++w) scored |= (__popcll(vm & wmask[w]) > K) ? (1u << w) : 0u;
+            float score = 0.0f;
+            Pa = 0.0f;
+            Pb = 0.0f;
+            if (scored) {
+                const int lc = l - 1;
+                const int shc = kLog2C + lc - 1;            // first key of a level-lc node i: i << shc
+                const int Mc = G.M[lc];
+                // candidate of MFMA row n of tile i (walk i / TPW, slots 16 (i % TPW) + n)
+                auto row_cand = [&](int i) -> int {
+                    return shfl_i(cand, dslot_lane<SLOTS>(i / TPW, 16 * (i % TPW) + n));
+                };
+                // (1) P of the candidates of walks that were not scored at the level above:
+                // head sums of the logits of the candidates' own summaries
+                const uint32_t need_p = scored & ~pk;
+                if (need_p) {
+#pragma unroll
+                    for (int i = 0; i < NTILE; ++i) {
+                        const int c = row_cand(i);
+                        const TileRows r = rows_global(splanes + (bh_row0 + G.off[l] + (c >= 0 ? c : 0)) * kD,
+                                                       plane_stride, gq);
+                        const f32x4 acc = child_tile_mfma(qf[i / TPW].k0, qf[i / TPW].k1, r.h0, r.h1, r.l0, r.l1);
+                        float v[4];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) v[k] = (n < G.GQ) ? acc[k] : 0.0f;
+                        const float ps = head_sum4(v, n);
+                        if (u == i && ((need_p >> wl) & 1)) P = ps;
+                    }
+                }
+                // (2) the delta tiles, the next tile's row in flight
+                const bool in_lds = l >= U.j_lo && l <= U.j_hi;
+                const int lds_lvl = in_lds ? U.lds_first[l] : 0;
+                const uint16_t* dplane_lvl = dplanes + (bh_row0 + G.off[l]) * kD;
+                auto pick = [&](int i, int& row) -> uint32_t {
+                    const int c = row_cand(i);
+                    const int rc = 2 * c + 1;                 // right child
+                    const bool rv = c >= 0 && rc < Mc && rc <= (int)(tw[i / TPW] >> shc);
+                    row = (c >= 0) ? c : 0;
+                    return (uint32_t)ballot(rv);              // bit r: row r has an eligible right child
+                };
+                auto fetch = [&](int row) -> TileRows {
+                    if (in_lds) return rows_lds(lds, lds_lvl + row, gq);
+                    return rows_global(dplane_lvl + (int64_t)row * kD, plane_stride, gq);
+                };
+                float F = 0.0f, D = 0.0f;
+                int row0;
+                uint32_t rvm = pick(0, row0);
+                TileRows cur = fetch(row0);
+#pragma unroll
+                for (int i = 0; i < NTILE; ++i) {
+                    TileRows nxt = cur;
+                    uint32_t rvm_next = 0;
+                    if (i + 1 < NTILE) {
+                        int rown;
+                        rvm_next = pick(i + 1, rown);
+                        nxt = fetch(rown);
+                    }
+                    const f32x4 acc = child_tile_mfma(qf[i / TPW].k0, qf[i / TPW].k1, cur.h0, cur.h1, cur.l0, cur.l1);
+                    float tv[4], dv[4];
+                    if ((rvm & 0xffffu) == 0xffffu && full_group) {
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            dv[k] = acc[k];
+                            tv[k] = pair_lse_term(acc[k]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const bool rv = (rvm >> (4 * gq + k)) & 1u;
+                            dv[k] = (n < G.GQ) ? acc[k] : 0.0f;
+                            tv[k] = (n < G.GQ) ? (rv ? pair_lse_term(acc[k]) : acc[k]) : 0.0f;
+                        }
+                    }
+                    const float Ft = head_sum4(tv, n), Dt = head_sum4(dv, n);
+                    if (u == i) {
+                        F = Ft;
+                        D = Dt;
+                    }
+                    cur = nxt;
+                    rvm = rvm_next;
+                }
+                score = P + F;
+                Pa = P + D;
+                Pb = P - D;
+                // (3) the ragged node of level l (a partial right child): its two children are
+                // read directly when a walk has it as a candidate with an eligible right child
+                const int crag = G.M[l] - 1, brag = 2 * crag + 1;
+                if (brag < Mc && covered(lc, brag, G.N) < span_of(lc)) {
+                    const bool is_rag = cand == crag && brag <= (int)(my_t >> shc);
+                    const uint64_t rm = ballot(is_rag);
+#pragma unroll
+                    for (int w = 0; w < WPW; ++w) {
+                        if (rm & wmask[w]) {
+                            const int crow = (n == 1) ? brag : brag - 1;
+                            const TileRows r = rows_global(splanes + (bh_row0 + G.off[lc] + crow) * kD, plane_stride, gq);
+                            const f32x4 acc = child_tile_mfma(qf[w].k0, qf[w].k1, r.h0, r.h1, r.l0, r.l1);
+                            // lane (0, n): acc[0] = left child's logit, acc[1] = right child's
+                            float v[4];
+                            v[0] = (n < G.GQ) ? log2_add_exp2(acc[0], acc[1]) : 0.0f;
+                            v[1] = (n < G.GQ) ? acc[0] : 0.0f;
+                            v[2] = (n < G.GQ) ? acc[1] : 0.0f;
+                            v[3] = 0.0f;
+                            const float x = head_sum4(v, n);
+                            const float f_fix = readlane_f(x, 0), pa_fix = readlane_f(x, 1), pb_fix = readlane_f(x, 2);
+                            if (is_rag && wl == w) {
+                                score = f_fix;
+                                Pa = pa_fix;
+                                Pb = pb_fix;
+                            }
+                        }
+                    }
+                }
+            }
+            pk = scored;
+            // walks with at most K candidates keep them all whatever their scores
+            const uint64_t key = slot_key((cand >= 0) ? score : -INFINITY, cand, ml);
+            const uint64_t sorted = bitonic_desc<SLOTS, DeltaLanes>(key, ml);
+            surv_low = (ml < K) ? (uint32_t)sorted : 0u;
+        }
+        // leaf candidates: children of the level-2 survivors (or the root if it is a leaf)
+        int leaf;
+        if (G.L == 1) {
+            leaf = (ml == 0 && my_ok) ? 0 : -1;
+        } else {
+            const uint32_t lowk = (uint32_t)shfl_i((int)surv_low, dslot_lane<SLOTS>(wl, ml >> 1));
+            const int pnode = key_node(lowk);
+            const int child = 2 * pnode + (ml & 1);
+            const bool ok = ml < 2 * K && pnode >= 0 && child < G.M[1] && child <= (int)(my_t >> kLog2C);
+            leaf = ok ? child : -1;
+        }
+        // ascending order, -1 last
+        const int nd = index_sort<SLOTS, DeltaLanes>((leaf >= 0) ? leaf : INT_MAX, ml);
+        leaf = (nd != INT_MAX && ml < 2 * K) ? nd : -1;
+        const uint64_t lm = ballot(leaf >= 0);
+        uint64_t mine = 0;
+#pragma unroll
+        for (int w = 0; w < WPW; ++w) mine = (wl == w) ? wmask[w] : mine;
+        if (my_ok && ml < 2 * K) {
+            const int64_t wid = ((int64_t)b * NT + my_ti) * G.Hkv + kvh;
+            cand_out[wid * (2 * K) + ml] = leaf;
+            if (ml == 0) ncand_out[wid] = __popcll(lm & mine);
+        }
+    }
+}
+
+template __global__ void walk_upper_delta_kernel<16>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg,
+                                                     int64_t, int64_t, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_kernel<32>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg,
+                                                     int64_t, int64_t, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_kernel<64>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg,
+                                                     int64_t, int64_t, int32_t*, int32_t*);
+
 #define PISA_INST_UPPER(KT, S)                                                                   \
     template __global__ void walk_upper_kernel<KT, S>(const KT*, const uint16_t*, const float*, \
                                                       Geom, UpperCfg, int64_t, int64_t, int32_t*, \

@@ -85,6 +85,43 @@ __device__ inline void pair_scores(const f32x4& acc, uint32_t rows_ok, int gq, i
     }
 }
 
+// ---------------------------------------------------------------- delta form --
+// For a candidate c with children a = 2c and b = 2c+1 and a query head, write the
+// base-2 logits as L_a = p + d and L_b = p - d, with p the logit of c's own summary and
+// d the logit of delta(c) = s(a) - s(c). L_a = p + d holds for every node; L_b = p - d
+// holds when c is the plain mean of two children (every node except the one ragged
+// node at the right edge of a level). Then LSE(L_a, L_b) = p + g(d) with
+// g(d) = log2(2^d + 2^-d), and the group-summed score is P(c) + sum_h g(d_h), where
+// P(c) = sum_h p_h is carried down the walk: P(a) = P + D, P(b) = P - D, D = sum_h d_h.
+// One summary row (delta) per candidate replaces the two children rows.
+
+// log2(2^d + 2^-d) = |d| + log2(1 + 2^(-2|d|))
+__device__ inline float pair_lse_term(float d) {
+    const float a = fabsf(d);
+    return a + __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(-2.0f * a));
+}
+
+// Sums over the 16 head columns of four values per lane: v[i] in lane (g, n) belongs to
+// tile row 4g + i and head column n. Afterwards every lane (g, n) holds the sum of row
+// 4g + (n & 3); the four lanes of a row group that hold the same row get bitwise equal
+// sums (a reduce-scatter over lane ^ 2 and lane ^ 1, then a symmetric butterfly over
+// lane ^ 8 and lane ^ 4), so the result does not depend on which of them is read.
+__device__ inline float head_sum4(const float v[4], int n) {
+    const bool b1 = (n >> 1) & 1, b0 = n & 1;
+    // lane ^ 2: lanes with b1 = 0 keep rows 0, 1 and hand over rows 2, 3 (and vice versa)
+    const float k0 = b1 ? v[2] : v[0], k1 = b1 ? v[3] : v[1];
+    const float s0 = b1 ? v[0] : v[2], s1 = b1 ? v[1] : v[3];
+    const float r0 = k0 + lane_xor_f<2>(s0);
+    const float r1 = k1 + lane_xor_f<2>(s1);
+    // lane ^ 1: keep row 2 b1 + b0
+    const float k = b0 ? r1 : r0, sd = b0 ? r0 : r1;
+    float x = k + lane_xor_f<1>(sd);
+    // the four quads of the row group
+    x = x + lane_xor_f<8>(x);
+    x = x + lane_xor_f<4>(x);
+    return x;
+}
+
 // Leaf scores from the MFMA results of NL leaves: acc[j][tau] holds, in lane (gq, n),
 // the natural-scale logits of keys 16*tau + 4*gq + r (r = 0..3) of leaf j for head n.
 // Keys with offset > lim[j] are masked. Per head the base-2 LSE is taken without a max
