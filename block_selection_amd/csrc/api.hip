@@ -19,9 +19,8 @@ __global__ void decode_refresh_kernel(const KT*, KT*, Geom, float*);
 __global__ void decode_step_kernel(const uint16_t*, const uint16_t*, uint16_t*, float*, Geom, uint32_t*, float*,
                                    int32_t*);
 __global__ void split_planes_kernel(const float*, uint16_t*, int64_t);
-template <typename KT, int SLOTS>
-__global__ void walk_upper_kernel(const KT*, const uint16_t*, const float*, Geom, UpperCfg, int64_t,
-                                  int64_t, int32_t*, int32_t*);
+template <int SLOTS>
+__global__ void walk_upper_f32_kernel(const float*, const float*, Geom, int64_t, int64_t, int32_t*, int32_t*);
 template <int SLOTS>
 __global__ void walk_upper_delta_kernel(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg, int64_t,
                                         int64_t, int32_t*, int32_t*);
@@ -172,31 +171,6 @@ static int build_impl(const KT* k, const Geom& G, float* pyr, hipStream_t s) {
 // Coarse levels to stage in LDS: the highest level that is ever read as children
 // (one below the highest level with more than K nodes) and as many levels below it
 // as fit the LDS budget.
-static UpperCfg upper_cfg(const Geom& G) {
-    UpperCfg U;
-    memset(&U, 0, sizeof(U));
-    U.j_lo = 1;
-    U.j_hi = 0;
-    int top = 0;
-    for (int l = G.L; l >= 1; --l) {
-        if (G.M[l] > G.topk) { top = l; break; }
-    }
-    const int j_hi = top - 1;
-    if (j_hi < 1) return U;
-    int nodes = 0, j_lo = j_hi + 1;
-    while (j_lo - 1 >= 1 && nodes + G.M[j_lo - 1] <= kLdsBudgetNodes) {
-        --j_lo;
-        nodes += G.M[j_lo];
-    }
-    if (j_lo > j_hi) return U;
-    U.j_lo = j_lo;
-    U.j_hi = j_hi;
-    int slot = 0;
-    for (int j = j_lo; j <= j_hi; ++j) { U.lds_first[j] = slot; slot += G.M[j]; }
-    U.lds_nodes = slot;
-    return U;
-}
-
 // LDS staging for the delta-form walk: the delta rows of the candidate levels from the
 // first level that can be scored (the highest with more than K nodes) downward, while
 // they fit.
@@ -245,24 +219,19 @@ static int launch_upper_delta(const uint16_t* q, const Geom& G, const UpperCfg& 
     return PISA_OK;
 }
 
-template <typename KT, int SLOTS>
-static int launch_upper(const KT* q, const uint16_t* planes, const float* pyr, const Geom& G,
-                        const UpperCfg& U, int64_t t0, int64_t NT, const Workspace& W, int cus, hipStream_t s) {
+template <int SLOTS>
+static int launch_upper_f32(const float* q, const float* pyr, const Geom& G, int64_t t0, int64_t NT,
+                            const Workspace& W, int cus, hipStream_t s) {
     constexpr int WPW = 64 / SLOTS;
     constexpr int nwaves = kUpperThreads / 64;
     const int64_t groups = (NT + WPW - 1) / WPW;
     const int bh = G.B * G.Hkv;
-    // one workgroup per CU (LDS-bound), a multiple of 8 so that XCDs split evenly
     int64_t need = (int64_t)bh * ((groups + nwaves - 1) / nwaves);
     int64_t nwg = need < cus ? need : cus;
     nwg = (nwg + 7) / 8 * 8;
     if (nwg < bh) nwg = bh;
-    const size_t lds = (sizeof(KT) == 2) ? (size_t)U.lds_nodes * kLdsNodeBytes : 0;
-    const void* fn = (const void*)walk_upper_kernel<KT, SLOTS>;
-    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-        return PISA_ERR_HIP;
-    hipLaunchKernelGGL((walk_upper_kernel<KT, SLOTS>), dim3((unsigned)nwg), dim3(kUpperThreads), lds, s,
-                       q, planes, pyr, G, U, t0, NT, W.cand, W.ncand);
+    hipLaunchKernelGGL((walk_upper_f32_kernel<SLOTS>), dim3((unsigned)nwg), dim3(kUpperThreads), 0, s, q, pyr, G, t0,
+                       NT, W.cand, W.ncand);
     return PISA_OK;
 }
 
@@ -343,14 +312,10 @@ static int select_impl(const KT* q, const KT* k, const float* pyr, const Geom& G
         else if (slots <= 32) rc = launch_upper_delta<32>(q, G, U, t0, NT, W, cus, s);
         else rc = launch_upper_delta<64>(q, G, U, t0, NT, W, cus, s);
     } else {
-        UpperCfg U = upper_cfg(G);
-        U.j_lo = 1;
-        U.j_hi = 0;
-        U.lds_nodes = 0;
         mark(ev, 0, s);
-        if (slots <= 16) rc = launch_upper<KT, 16>(q, W.planes, pyr, G, U, t0, NT, W, cus, s);
-        else if (slots <= 32) rc = launch_upper<KT, 32>(q, W.planes, pyr, G, U, t0, NT, W, cus, s);
-        else rc = launch_upper<KT, 64>(q, W.planes, pyr, G, U, t0, NT, W, cus, s);
+        if (slots <= 16) rc = launch_upper_f32<16>(q, pyr, G, t0, NT, W, cus, s);
+        else if (slots <= 32) rc = launch_upper_f32<32>(q, pyr, G, t0, NT, W, cus, s);
+        else rc = launch_upper_f32<64>(q, pyr, G, t0, NT, W, cus, s);
     }
     if (rc != PISA_OK) return rc;
     mark(ev, 1, s);

@@ -66,7 +66,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
                                                                      uint32_t* __restrict__ done,
                                                                      float* __restrict__ leaf_score,
                                                                      int32_t* __restrict__ out) {
-    __shared__ float s_score[2][64];
+    __shared__ float s_F[2][64], s_D[2][64], s_P[2][64], s_fix[2][4];
+    __shared__ int s_fixslot[2];
     __shared__ int s_last;
     const int part = blockIdx.x, nparts = gridDim.x;   // leaf slots 8*part .. 8*part+7
     const int bh = blockIdx.y, b = bh / G.Hkv, kvh = bh % G.Hkv;
@@ -92,56 +93,143 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
     if (wave == 0) refresh_wave<uint16_t>(k_new + (int64_t)bh * kD, kbase, row_stride, G, pyr_bh, lane);
     __syncthreads();   // the refreshed path is visible to every wavefront of the workgroup
 
-    // candidate slot = lane; slot 2i + c holds child c of survivor i (survivors in lanes 0..K-1)
-    int surv = -1, buf = 0;
+    // candidate slot = lane; slot 2i + c holds child c of survivor i. A survivor is kept as
+    // the low word of its selection key (node and the slot it came from); Pa / Pb hold, in
+    // the slot a candidate was scored in, the head-summed logits of its two children.
+    uint32_t surv_low = 0;
+    float Pa = 0.0f, Pb = 0.0f;
+    bool pk = false;                 // P of this level's candidates known (scored level above)
+    int buf = 0;
     for (int l = G.L; l >= 2; --l) {
         int cand;
+        float P = 0.0f;
         if (l == G.L) {
             cand = (lane == 0) ? 0 : -1;
         } else {
-            const int par = shfl_i(surv, lane >> 1);
-            const int child = 2 * par + (lane & 1);
-            const bool ok = lane < 2 * K && par >= 0 && child < G.M[l] && child <= (int)(t >> (kLog2C + l - 1));
+            const uint32_t lowk = (uint32_t)shfl_i((int)surv_low, lane >> 1);
+            const int pnode = key_node(lowk);
+            const int child = 2 * pnode + (lane & 1);
+            const bool ok = lane < 2 * K && pnode >= 0 && child < G.M[l] && child <= (int)(t >> (kLog2C + l - 1));
             cand = ok ? child : -1;
+            const int src = key_slot(lowk);
+            const float pa = shfl_f(Pa, src), pb = shfl_f(Pb, src);
+            P = (lane & 1) ? pb : pa;
         }
         const uint64_t vm = ballot(cand >= 0);
         const int nc = __popcll(vm);
         if (nc <= K) {
             // every candidate survives: compact them into lanes 0 .. nc-1
+            const uint32_t low = (cand >= 0) ? (((uint32_t)((1 << 26) - 1 - cand) << 6) | (uint32_t)lane) : 0u;
             const int dst = (cand >= 0) ? lanes_below(vm) : nc + lanes_below(~vm);
-            const int got = push_to_lane(dst, cand);
-            surv = (lane < nc) ? got : -1;
+            const uint32_t got = (uint32_t)push_to_lane(dst, (int)low);
+            surv_low = (lane < nc) ? got : 0u;
+            Pa = Pb = 0.0f;
+            pk = false;
             continue;
         }
         const int lc = l - 1;
-        {
-            // tile `wave`: row n = child (n & 1) of slot 8 * wave + n / 2
-            const int par = shfl_i(cand, 8 * wave + (n >> 1));
-            const int child = 2 * par + (n & 1);
-            const bool valid = par >= 0 && child < G.M[lc] && child <= (int)(t >> (kLog2C + lc - 1));
-            const uint32_t rows_ok = (uint32_t)ballot(valid);   // bit r: row r is an eligible child
-            if (rows_ok) {
-                const float* row = pyr_bh + (G.off[lc] + (valid ? child : 0)) * kD;
-                float v0[8], v1[8];
-                load8_f32(row + 8 * gq, v0);
-                load8_f32(row + 32 + 8 * gq, v1);
+        const int shc = kLog2C + lc - 1;            // first key of a level-lc node i: i << shc
+        const int Mc = G.M[lc];
+        if (wave < 4) {
+            // tile `wave`: MFMA row n = candidate of slot 16 * wave + n
+            const int c = shfl_i(cand, 16 * wave + n);
+            const int rc = 2 * c + 1;
+            const bool rv = c >= 0 && rc < Mc && rc <= (int)(t >> shc);
+            const uint32_t rvm = (uint32_t)ballot(rv);
+            const int cc = (c >= 0) ? c : 0;
+            const float* prow = pyr_bh + (G.off[l] + cc) * kD;
+            const float* crow = pyr_bh + (G.off[lc] + 2 * cc) * kD;
+            float vc0[8], vc1[8], vp0[8], vp1[8];
+            load8_f32(crow + 8 * gq, vc0);
+            load8_f32(crow + 32 + 8 * gq, vc1);
+            load8_f32(prow + 8 * gq, vp0);
+            load8_f32(prow + 32 + 8 * gq, vp1);
+            {
+                float d0[8], d1[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    d0[e] = vc0[e] - vp0[e];
+                    d1[e] = vc1[e] - vp1[e];
+                }
                 u32x4 h0, l0, h1, l1;
-                split8(v0, h0, l0);
-                split8(v1, h1, l1);
+                split8(d0, h0, l0);
+                split8(d1, h1, l1);
                 const f32x4 acc = child_tile_mfma(q0, q1, h0, h1, l0, l1);
-                float sc[2];
-                pair_scores(acc, rows_ok, gq, n, G.GQ, sc);
-                if (n == 0) {
-                    s_score[buf][8 * wave + 2 * gq] = sc[0];
-                    s_score[buf][8 * wave + 2 * gq + 1] = sc[1];
+                float tv[4], dv[4];
+                if ((rvm & 0xffffu) == 0xffffu && G.GQ == kMaxGroup) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        dv[k] = acc[k];
+                        tv[k] = pair_lse_term(acc[k]);
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const bool rk = (rvm >> (4 * gq + k)) & 1u;
+                        dv[k] = (n < G.GQ) ? acc[k] : 0.0f;
+                        tv[k] = (n < G.GQ) ? (rk ? pair_lse_term(acc[k]) : acc[k]) : 0.0f;
+                    }
+                }
+                const float F = head_sum4(tv, n), D = head_sum4(dv, n);
+                if (n < 4) {
+                    s_F[buf][16 * wave + 4 * gq + n] = F;
+                    s_D[buf][16 * wave + 4 * gq + n] = D;
                 }
             }
+            if (!pk) {
+                // P of the candidates: head sums of the logits of their own summaries
+                u32x4 h0, l0, h1, l1;
+                split8(vp0, h0, l0);
+                split8(vp1, h1, l1);
+                const f32x4 acc = child_tile_mfma(q0, q1, h0, h1, l0, l1);
+                float v[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v[k] = (n < G.GQ) ? acc[k] : 0.0f;
+                const float ps = head_sum4(v, n);
+                if (n < 4) s_P[buf][16 * wave + 4 * gq + n] = ps;
+            }
+        } else if (wave == 4) {
+            // the ragged node of level l (a partial right child), read directly when it is a
+            // candidate with an eligible right child
+            int fix_slot = -1;
+            const int crag = G.M[l] - 1, brag = 2 * crag + 1;
+            if (brag < Mc && covered(lc, brag, G.N) < span_of(lc)) {
+                const uint64_t rm = ballot(cand == crag && brag <= (int)(t >> shc));
+                if (rm) {
+                    fix_slot = __builtin_ctzll(rm);
+                    const float* row = pyr_bh + (G.off[lc] + ((n == 1) ? brag : brag - 1)) * kD;
+                    float v0[8], v1[8];
+                    load8_f32(row + 8 * gq, v0);
+                    load8_f32(row + 32 + 8 * gq, v1);
+                    u32x4 h0, l0, h1, l1;
+                    split8(v0, h0, l0);
+                    split8(v1, h1, l1);
+                    const f32x4 acc = child_tile_mfma(q0, q1, h0, h1, l0, l1);
+                    float v[4];
+                    v[0] = (n < G.GQ) ? log2_add_exp2(acc[0], acc[1]) : 0.0f;
+                    v[1] = (n < G.GQ) ? acc[0] : 0.0f;
+                    v[2] = (n < G.GQ) ? acc[1] : 0.0f;
+                    v[3] = 0.0f;
+                    const float x = head_sum4(v, n);
+                    if (lane < 3) s_fix[buf][lane] = x;
+                }
+            }
+            if (lane == 0) s_fixslot[buf] = fix_slot;
         }
         __syncthreads();
-        const float my = (cand >= 0) ? s_score[buf][lane] : -INFINITY;
+        if (!pk) P = s_P[buf][lane];
+        float score = P + s_F[buf][lane];
+        Pa = P + s_D[buf][lane];
+        Pb = P - s_D[buf][lane];
+        if (lane == s_fixslot[buf]) {
+            score = s_fix[buf][0];
+            Pa = s_fix[buf][1];
+            Pb = s_fix[buf][2];
+        }
         buf ^= 1;
-        const int nd = select_sort<64>(my, (cand >= 0) ? cand : INT_MAX, lane);
-        surv = (lane < K && nd != INT_MAX) ? nd : -1;
+        pk = true;
+        const uint64_t sorted = bitonic_desc<64, SegmentLanes>(slot_key((cand >= 0) ? score : -INFINITY, cand, lane), lane);
+        surv_low = (lane < K) ? (uint32_t)sorted : 0u;
     }
 
     // leaf candidates: children of the level-2 survivors (the root itself if it is a leaf)
@@ -149,7 +237,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
     if (G.L == 1) {
         leaf = (lane == 0) ? 0 : -1;
     } else {
-        const int par = shfl_i(surv, lane >> 1);
+        const int par = key_node((uint32_t)shfl_i((int)surv_low, lane >> 1));
         const int child = 2 * par + (lane & 1);
         const bool ok = lane < 2 * K && par >= 0 && child < G.M[1] && child <= (int)(t >> kLog2C);
         leaf = ok ? child : -1;

@@ -44,14 +44,13 @@ __host__ __device__ inline int64_t covered(int l, int64_t i, int64_t n) {
     return (n - lo < s) ? (n - lo) : s;
 }
 
-// Coarse pyramid levels staged in LDS by the upper-level walk: levels j_lo..j_hi
-// (none if j_lo > j_hi), node i of level j at LDS slot lds_first[j] + i, each slot
-// holding the hi and lo bf16 planes of the node (kLdsNodeBytes, padded against
-// bank conflicts).
+// Coarse candidate levels staged in LDS by the bf16 upper-level walk: levels
+// j_lo..j_hi (none if j_lo > j_hi), node i of level j at LDS slot lds_first[j] + i, each
+// slot holding the hi and lo bf16 planes of the node's delta row (kLdsNodeBytes, padded
+// against bank conflicts).
 constexpr int kLdsNodeBytes = 272;
 constexpr int kUpperThreads = 1024;
-constexpr int kLdsBudgetNodes = 480;     // 480 * 272 B = 127.5 KiB
-constexpr int kLdsDeltaBudgetNodes = 504; // 504 * 272 B = 133.9 KiB (delta-form walk)
+constexpr int kLdsDeltaBudgetNodes = 504; // 504 * 272 B = 133.9 KiB
 struct UpperCfg {
     int32_t j_lo, j_hi;
     int32_t lds_first[kMaxLevels + 1];

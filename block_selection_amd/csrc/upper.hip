@@ -129,67 +129,17 @@ struct TileLanes {
     static constexpr int of(int J) { return slot_bit_lane(J); }
 };
 
-// One scored level of the bf16 walk for the wavefront's 64/SLOTS walks: the tiles are
-// scored in order with the next tile's children rows already loading (from LDS or from global memory, fixed per level), so a
-// tile's load latency hides behind the previous tile's MFMA and LSE work. Returns the
-// score of this lane's candidate slot.
-template <int SLOTS, bool FROM_LDS>
-__device__ inline float score_level_bf16(const UpperQ<uint16_t> (&qf)[64 / SLOTS], const int64_t (&tw)[64 / SLOTS],
-                                         int cand, int sh, int Mc, const lds_char_t* lds, int lds_lvl,
-                                         const uint16_t* __restrict__ plane_lvl, int64_t plane_stride, int n,
-                                         int gq, int wl, int ql, int GQ) {
-    constexpr int TPW = SLOTS / 8, NT = (64 / SLOTS) * TPW;
-    // children row of tile i (w, tau) for this lane: MFMA row n = child (n & 1) of slot
-    // 8 tau + n/2; invalid rows read row 0 and their results are unused
-    auto pick = [&](int i, int& row) -> uint32_t {
-        const int w = i / TPW, tau = i % TPW;
-        const int par = shfl_i(cand, slot_lane<SLOTS>(w, 8 * tau + (n >> 1)));
-        const int child = 2 * par + (n & 1);
-        const bool valid = par >= 0 && child < Mc && child <= (int)(tw[w] >> sh);
-        row = valid ? child : 0;
-        return (uint32_t)ballot(valid);
-    };
-    auto fetch = [&](int row) -> TileRows {
-        if constexpr (FROM_LDS) return rows_lds(lds, lds_lvl + row, gq);
-        else return rows_global(plane_lvl + (int64_t)row * kD, plane_stride, gq);
-    };
-    float my = 0.0f;
-    int row0;
-    uint32_t rok = pick(0, row0);
-    TileRows cur = fetch(row0);
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-        TileRows nxt = cur;
-        uint32_t rok_next = 0;
-        if (i + 1 < NT) {
-            int rown;
-            rok_next = pick(i + 1, rown);
-            nxt = fetch(rown);
-        }
-        const int w = i / TPW, tau = i % TPW;
-        const f32x4 acc = child_tile_mfma(qf[w].k0, qf[w].k1, cur.h0, cur.h1, cur.l0, cur.l1);
-        float sc[2];
-        pair_scores(acc, rok, gq, n, GQ, sc);
-        if (wl == w && (ql >> 1) == tau) my = (ql & 1) ? sc[1] : sc[0];
-        cur = nxt;
-        rok = rok_next;
-    }
-    return my;
-}
-
-// Walks for positions t0 + ti, ti in [0, NT), of every batch element and KV head.
-// Output per walk (index (b*NT + ti)*Hkv + kvh): cand_out[2K] ascending leaf
-// candidates (-1 padded) and ncand_out = their count.
-template <typename KT, int SLOTS>
-__global__ __launch_bounds__(kUpperThreads) void walk_upper_kernel(const KT* __restrict__ q,
-                                                         const uint16_t* __restrict__ planes,
-                                                         const float* __restrict__ pyr, Geom G,
-                                                         UpperCfg U, int64_t t0, int64_t NT,
-                                                         int32_t* __restrict__ cand_out,
-                                                         int32_t* __restrict__ ncand_out) {
+// fp32 inputs: walks for positions t0 + ti, ti in [0, NT), of every batch element and KV
+// head, scoring each candidate from its two children rows of the fp32 pyramid on
+// v_mfma_f32_16x16x4_f32. Output per walk (index (b*NT + ti)*Hkv + kvh): cand_out[2K]
+// ascending leaf candidates (-1 padded) and ncand_out = their count.
+template <int SLOTS>
+__global__ __launch_bounds__(kUpperThreads) void walk_upper_f32_kernel(const float* __restrict__ q,
+                                                             const float* __restrict__ pyr, Geom G, int64_t t0,
+                                                             int64_t NT, int32_t* __restrict__ cand_out,
+                                                             int32_t* __restrict__ ncand_out) {
+    using KT = float;
     constexpr int WPW = 64 / SLOTS, QW = SLOTS / 4;
-    extern __shared__ u32x4 lds_u4[];
-    lds_char_t* lds = (lds_char_t*)lds_u4;
     // XCD-aware placement: workgroup i runs on XCD i % 8; when B*Hkv divides 8, every
     // XCD serves a single (batch, KV head), so its L2 holds that head's finer levels only.
     const int BH = G.B * G.Hkv;
@@ -210,24 +160,7 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_kernel(const KT* __r
     const int wl = n / QW, ql = n % QW;                       // this lane's walk and position in its row
     const int ml = 8 * (ql >> 1) + 2 * gq + (ql & 1);         // this lane's candidate slot
     const int K = G.topk;
-    const int64_t plane_stride = (int64_t)G.B * G.Hkv * G.P * kD;
     const int64_t bh_row0 = (int64_t)bh * G.P;
-
-    // stage the coarse levels: node i of level j -> LDS slot lds_first[j] + i, planes hi|lo
-    if constexpr (sizeof(KT) == 2) {
-        for (int j = U.j_lo; j <= U.j_hi; ++j) {
-            const int mj = G.M[j];
-            for (int c = threadIdx.x; c < mj * 16; c += blockDim.x) {
-                const int node = c >> 4, part = c & 15;        // part: plane (part>>3), 16-B chunk (part&7)
-                const uint16_t* src = planes + (part >> 3) * plane_stride +
-                                      (bh_row0 + G.off[j] + node) * kD + (part & 7) * 8;
-                *reinterpret_cast<lds_u32x4_t*>(lds + (U.lds_first[j] + node) * kLdsNodeBytes +
-                                                (part >> 3) * 128 + (part & 7) * 16) =
-                    *reinterpret_cast<const u32x4*>(src);
-            }
-        }
-        __syncthreads();
-    }
 
     // lanes of walk w: bits of a wavefront mask
     uint64_t wmask[WPW];
@@ -276,18 +209,7 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_kernel(const KT* __r
                 const int lc = l - 1;
                 const int Mc = G.M[lc];
                 const int sh = kLog2C + lc - 1;              // first key of node i at level lc: i << sh
-                const bool in_lds = (sizeof(KT) == 2) && lc >= U.j_lo && lc <= U.j_hi;
-                const uint16_t* plane_lvl = planes + (bh_row0 + G.off[lc]) * kD;
                 const float* pyr_lvl = pyr + (bh_row0 + G.off[lc]) * kD;
-                const int lds_lvl = in_lds ? U.lds_first[lc] : 0;
-                if constexpr (sizeof(KT) == 2) {
-                    if (in_lds)
-                        my = score_level_bf16<SLOTS, true>(qf, tw, cand, sh, Mc, lds, lds_lvl, plane_lvl, plane_stride,
-                                                           n, gq, wl, ql, G.GQ);
-                    else
-                        my = score_level_bf16<SLOTS, false>(qf, tw, cand, sh, Mc, lds, lds_lvl, plane_lvl,
-                                                            plane_stride, n, gq, wl, ql, G.GQ);
-                } else {
 #pragma unroll
                 for (int w = 0; w < WPW; ++w) {
                     const int tl = (int)(tw[w] >> sh);         // children <= tl are eligible
@@ -304,7 +226,6 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_kernel(const KT* __r
                         pair_scores(acc, rows_ok, gq, n, G.GQ, sc);
                         if (wl == w && (ql >> 1) == tau) my = (ql & 1) ? sc[1] : sc[0];
                     }
-                }
                 }
                 if (cand < 0) my = -INFINITY;
             }
@@ -380,18 +301,6 @@ constexpr int dslot_bit_lane(int J) { return J == 1 ? 1 : J == 2 ? 2 : J == 4 ? 
 struct DeltaLanes {
     static constexpr int of(int J) { return dslot_bit_lane(J); }
 };
-
-// Selection key that also records the slot a candidate came from: selection order
-// (score desc, node asc); low word (2^26 - 1 - node) << 6 | slot, 0 for an empty slot.
-// Nodes of levels >= 2 are below 2^24.
-__device__ inline uint64_t slot_key(float s, int node, int slot) {
-    const uint32_t u = __float_as_uint(s + 0.0f);
-    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    const uint32_t low = (node >= 0) ? (((uint32_t)((1 << 26) - 1 - node) << 6) | (uint32_t)slot) : 0u;
-    return ((uint64_t)o << 32) | low;
-}
-__device__ inline int key_node(uint32_t low) { return (low >> 6) ? (1 << 26) - 1 - (int)(low >> 6) : -1; }
-__device__ inline int key_slot(uint32_t low) { return (int)(low & 63u); }
 
 template <int SLOTS>
 __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const uint16_t* __restrict__ q,
@@ -641,15 +550,11 @@ template __global__ void walk_upper_delta_kernel<32>(const uint16_t*, const uint
 template __global__ void walk_upper_delta_kernel<64>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg,
                                                      int64_t, int64_t, int32_t*, int32_t*);
 
-#define PISA_INST_UPPER(KT, S)                                                                   \
-    template __global__ void walk_upper_kernel<KT, S>(const KT*, const uint16_t*, const float*, \
-                                                      Geom, UpperCfg, int64_t, int64_t, int32_t*, \
-                                                      int32_t*);
-PISA_INST_UPPER(uint16_t, 16)
-PISA_INST_UPPER(uint16_t, 32)
-PISA_INST_UPPER(uint16_t, 64)
-PISA_INST_UPPER(float, 16)
-PISA_INST_UPPER(float, 32)
-PISA_INST_UPPER(float, 64)
+template __global__ void walk_upper_f32_kernel<16>(const float*, const float*, Geom, int64_t, int64_t, int32_t*,
+                                                   int32_t*);
+template __global__ void walk_upper_f32_kernel<32>(const float*, const float*, Geom, int64_t, int64_t, int32_t*,
+                                                   int32_t*);
+template __global__ void walk_upper_f32_kernel<64>(const float*, const float*, Geom, int64_t, int64_t, int32_t*,
+                                                   int32_t*);
 
 }  // namespace pisa

@@ -122,6 +122,18 @@ __device__ inline float head_sum4(const float v[4], int n) {
     return x;
 }
 
+// Selection key that also records the slot a candidate came from: selection order
+// (score desc, node asc); low word (2^26 - 1 - node) << 6 | slot, 0 for an empty slot.
+// Nodes of levels >= 2 are below 2^24.
+__device__ inline uint64_t slot_key(float s, int node, int slot) {
+    const uint32_t u = __float_as_uint(s + 0.0f);
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t low = (node >= 0) ? (((uint32_t)((1 << 26) - 1 - node) << 6) | (uint32_t)slot) : 0u;
+    return ((uint64_t)o << 32) | low;
+}
+__device__ inline int key_node(uint32_t low) { return (low >> 6) ? (1 << 26) - 1 - (int)(low >> 6) : -1; }
+__device__ inline int key_slot(uint32_t low) { return (int)(low & 63u); }
+
 // Leaf scores from the MFMA results of NL leaves: acc[j][tau] holds, in lane (gq, n),
 // the natural-scale logits of keys 16*tau + 4*gq + r (r = 0..3) of leaf j for head n.
 // Keys with offset > lim[j] are masked. Per head the base-2 LSE is taken without a max
