@@ -125,7 +125,7 @@ def write_traffic(fetch_dir: str, write_dir: str, workload: str = "long256k") ->
         "command": ("rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> -o run -- "
                     "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-extras --copy-calibration; "
                     "python3 bench.py --write-traffic <fetch dir> <write dir>")}}
-    for key, srcs in (("leaf_cluster_kernel", LEAF_SOURCES), ("walk_upper_kernel<unsigned short, 16>", UPPER_SOURCES)):
+    for key, srcs in (("leaf_cluster_kernel", LEAF_SOURCES), ("walk_upper_delta_kernel<16>", UPPER_SOURCES)):
         f_kib, w_kib = find(fetch, key), find(write, key)
         out[f"{key.split('<')[0]}:{workload}"] = {
             "fetch_kib": f_kib, "write_kib": w_kib,
@@ -305,7 +305,7 @@ def main():
     clustered = wl.dtype == "bf16"
     kname = "leaf_cluster_kernel" if clustered else "leaf_walk_kernel"
     traffic = measured_traffic(f"{kname}:{wl.name}", _hash_sources(LEAF_SOURCES))
-    upper_traffic = measured_traffic(f"walk_upper_kernel:{wl.name}", _hash_sources(UPPER_SOURCES))
+    upper_traffic = measured_traffic(f"walk_upper_delta_kernel:{wl.name}", _hash_sources(UPPER_SOURCES))
     # dominant kernel: the clustered leaf scoring; its duration is measured with HIP events
     # on the stream the library launches on, around a separate timed pass of the same call
     leaf_ms = float(np.mean(leaf_ms_steps))
@@ -329,7 +329,7 @@ def main():
     # the second kernel: the coarse-to-fine walk above the leaves (one exp per child logit and
     # one log per candidate LSE, the pairwise form log2(1 + 2^d) of two children)
     roofline_upper = {
-        "kernel": "walk_upper_kernel (scored levels above the leaves)",
+        "kernel": "walk_upper_delta_kernel (scored levels above the leaves)",
         "bound": "alu",
         "achieved": upper_transc / (upper_ms / 1e3) / 1e9,
         "peak": TRANSCENDENTAL_PEAK / 1e9,
