@@ -155,38 +155,122 @@ template __global__ void bucket_pass_kernel<64>(const int32_t*, const int32_t*, 
 // consecutive rows hit distinct banks.
 __device__ inline int sb_lds_offset(int r, int chunk) { return r * 128 + ((chunk ^ (r & 7)) << 4); }
 
-// Scores of the leaves of one entry (mask: one leaf, or a sibling pair at bits b, b+1)
-// for one walk: lane 0 writes the first leaf's score, lane 16 the second's, every other
-// lane stores into the sink, so each entry issues exactly one store instruction (that
-// keeps the wait counters exact and the next entries' query prefetches in flight).
-// An empty mask (padding entry) scores nothing.
-__device__ inline void score_entry(const lds_char_t* lds, int key_base, uint32_t mask, int t,
-                                   const bf16x8 q0, const bf16x8 q1, int n, int gq, int lane, int GQ,
-                                   float* __restrict__ score_row, float* __restrict__ sink) {
-    float v = 0.0f;
-    bool two = false;
-    if (mask) {
-        const int b0 = __builtin_ctz(mask);
-        two = (mask >> (b0 + 1)) & 1u;
-        const int bits[2] = {b0, two ? b0 + 1 : b0};
-        f32x4 acc[2][4];
+// MFMA logits of one leaf (superblock offset `bit`) for one walk's query fragments:
+// acc[tau] in lane (gq, n) holds keys 16 tau + 4 gq + r of head n.
+__device__ inline void leaf_logits(const lds_char_t* lds, int bit, const bf16x8 q0, const bf16x8 q1, int n, int gq,
+                                   f32x4 acc[4]) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int tau = 0; tau < 4; ++tau) {
-                const int r = bits[j] * kC + 16 * tau + n;
-                const u32x4 a0 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, gq));
-                const u32x4 a1 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, 4 + gq));
-                f32x4 c = {0.f, 0.f, 0.f, 0.f};
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), q0, c, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), q1, c, 0, 0, 0);
-                acc[j][tau] = c;
-            }
-        const int lim[2] = {min(t - (key_base + bits[0] * kC), kC - 1), min(t - (key_base + bits[1] * kC), kC - 1)};
-        v = leaf_lse_pair(acc, lim, n, gq, GQ);
+    for (int tau = 0; tau < 4; ++tau) {
+        const int r = bit * kC + 16 * tau + n;
+        const u32x4 a0 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, gq));
+        const u32x4 a1 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, 4 + gq));
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), q0, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), q1, c, 0, 0, 0);
+        acc[tau] = c;
     }
-    float* dst = (mask && lane == 0) ? score_row : ((two && lane == 16) ? score_row + 1 : sink + lane);
-    *dst = v;
+}
+
+// This lane's sum of 2^(logit) over its 16 keys of a leaf, keys past lim masked (the
+// order of leaf_lse_from_acc).
+__device__ inline float lane_exp_sum(const f32x4 (&acc)[4], int lim, bool full, int gq) {
+    float v = 0.f;
+    if (full) {
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v += __builtin_amdgcn_exp2f(acc[tau][r] * kScale2);
+    } else {
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float e2 = __builtin_amdgcn_exp2f(acc[tau][r] * kScale2);
+                v += (16 * tau + 4 * gq + r <= lim) ? e2 : 0.0f;
+            }
+    }
+    return v;
+}
+
+// Scores of a unit: two walks a and b (b may repeat a) against the two leaves of one
+// sibling pair (superblock offsets bits[0], bits[1]; the second may repeat the first).
+// Each key fragment is read from LDS once and used for both walks. The four
+// (walk, leaf) sums are reduced in one vector; returns, in lanes of row group r,
+// the score of (walk r >> 1, leaf r & 1), bitwise what leaf_lse_from_acc gives for the
+// leaf alone. lim[] are per (walk, leaf) in that row order; an ineligible leaf (lim < 0)
+// is computed with one key and its score discarded by the caller.
+__device__ inline float score_unit(const lds_char_t* lds, const int (&bits)[2], const int (&lim_in)[4],
+                                   const bf16x8 qa0, const bf16x8 qa1, const bf16x8 qb0, const bf16x8 qb1, int n,
+                                   int gq, int GQ) {
+    int lim[4];
+    bool full = true;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        lim[r] = max(lim_in[r], 0);
+        full = full && lim[r] == kC - 1;
+    }
+    float sum[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        f32x4 acca[4], accb[4];
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau) {
+            const int r = bits[j] * kC + 16 * tau + n;
+            const u32x4 a0 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, gq));
+            const u32x4 a1 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, 4 + gq));
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), qa0, c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), qa1, c, 0, 0, 0);
+            acca[tau] = c;
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), qb0, d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), qb1, d, 0, 0, 0);
+            accb[tau] = d;
+        }
+        sum[j] = lane_exp_sum(acca, lim[j], full, gq);
+        sum[2 + j] = lane_exp_sum(accb, lim[2 + j], full, gq);
+    }
+    // column totals of the four sums in one vector: row r = (walk r >> 1, leaf r & 1)
+    const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(sum[0]), __float_as_uint(sum[1]), false, false);
+    const float Sa = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(sum[2]), __float_as_uint(sum[3]), false, false);
+    const float Sb = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+    const auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(Sa), __float_as_uint(Sb), false, false);
+    float T = __uint_as_float(z[0]) + __uint_as_float(z[1]);
+    float shift = 0.0f;
+    const uint64_t bad = ballot(!(T < INFINITY && T > 0x1p-100f));
+    if (bad) {
+#pragma unroll 1
+        for (int r = 0; r < 4; ++r) {
+            if (bad & (0xffffull << (16 * r))) {
+                // rare: this (walk, leaf) again, shifted by each column's maximum logit
+                f32x4 acc[4];
+                leaf_logits(lds, bits[r & 1], (r >> 1) ? qb0 : qa0, (r >> 1) ? qb1 : qa1, n, gq, acc);
+                float m = -INFINITY;
+#pragma unroll
+                for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        if (16 * tau + 4 * gq + k <= lim[r]) m = fmaxf(m, acc[tau][k]);
+                const float moff = cols4_max(m) * kScale2;
+                float v = 0.f;
+#pragma unroll
+                for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[tau][k], kScale2, -moff));
+                        v += (16 * tau + 4 * gq + k <= lim[r]) ? e2 : 0.0f;
+                    }
+                const float sr = cols4_sum(v);
+                if (gq == r) {
+                    T = sr;
+                    shift = moff;
+                }
+            }
+        }
+    }
+    const float lse2 = shift + __builtin_amdgcn_logf(T);
+    return row16_sum((n < GQ) ? lse2 : 0.0f);
 }
 
 // B fragments of one walk's queries: head n of the group, dims {8gq..8gq+7} and
@@ -230,17 +314,46 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
         // this wavefront's entries item.y + wave + j*nwaves, j < cnt: lane j holds entry j
         const int first = item.y + wave;
         const int cnt = (item.z > wave) ? (item.z - wave + nwaves - 1) / nwaves : 0;
-        const uint2 ev = (lane < cnt) ? entries[first + lane * nwaves] : make_uint2(0u, 0u);
-        // queries of the first three entries, in flight during the key staging
-        u32x4 qa0, qb0, qa1, qb1, qa2, qb2;
-        // lanes j >= cnt of ev hold walk 0: prefetches past the end load a valid query row
-        auto qload = [&](int j, u32x4& qa, u32x4& qb) {
-            const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)ev.x, j);
-            load_q(q, (int64_t)(w / (uint32_t)G.Hkv), G.Hq, kvh, G.GQ, n, gq, qa, qb);
+        const uint2 ev0 = (lane < cnt) ? entries[first + lane * nwaves] : make_uint2(0u, 0u);
+        // Units: the wavefront's entries are ordered by sibling pair (a 64-lane sort), and
+        // two entries of the same pair form a unit whose key fragments are read once.
+        // Lane u < nunits ends up holding unit u: entries (ua, ub); ub.y = 0 if alone.
+        const uint32_t m0 = ev0.y & 0xffffu;
+        const int pr0 = (lane < cnt && m0) ? (__builtin_ctz(m0) >> 1) : 15;
+        const uint32_t skey = index_sort<64>(((uint32_t)pr0 << 6) | (uint32_t)lane, lane);   // ascending
+        const int pj = (int)(skey >> 6), sl = (int)(skey & 63u);
+        const uint2 ev = make_uint2((uint32_t)shfl_i((int)ev0.x, sl), (uint32_t)shfl_i((int)ev0.y, sl));
+        int rk = 0;
+#pragma unroll
+        for (int v = 0; v < kSbLeaves / 2; ++v) {
+            const uint64_t mv = ballot(pj == v);
+            if (pj == v) rk = lanes_below(mv);
+        }
+        const int pj_next = shfl_i(pj, lane < 63 ? lane + 1 : lane);
+        const bool leader = pj < kSbLeaves / 2 && (rk & 1) == 0;
+        const bool has_b = leader && lane < 63 && pj_next == pj;
+        const uint64_t lm = ballot(leader);
+        const int nunits = __popcll(lm);
+        const int lead = push_to_lane(leader ? lanes_below(lm) : nunits + lanes_below(~lm), lane);
+        const int hb = push_to_lane(leader ? lanes_below(lm) : nunits + lanes_below(~lm), has_b ? 1 : 0);
+        // (cross-lane reads with every lane active: a lane outside a branch supplies nothing)
+        const bool uok = lane < nunits;
+        const uint32_t sax = (uint32_t)shfl_i((int)ev.x, lead), say = (uint32_t)shfl_i((int)ev.y, lead);
+        const uint32_t sbx = (uint32_t)shfl_i((int)ev.x, min(lead + 1, 63));
+        const uint32_t sby = (uint32_t)shfl_i((int)ev.y, min(lead + 1, 63));
+        const uint32_t uax = uok ? sax : 0u, uay = uok ? say : 0u;
+        const uint32_t ubx = uok ? sbx : 0u, uby = (uok && hb) ? sby : 0u;
+        // queries of the first two units, in flight during the key staging; units past
+        // nunits read walk 0 (a valid row) and score nothing
+        u32x4 qa0, qa1, qb0, qb1, ra0, ra1, rb0, rb1;
+        auto qload = [&](int u, u32x4& a0, u32x4& a1, u32x4& b0, u32x4& b1) {
+            const uint32_t wa = (uint32_t)__builtin_amdgcn_readlane((int)uax, u);
+            const uint32_t wb = (uint32_t)__builtin_amdgcn_readlane((int)(uby ? ubx : uax), u);
+            load_q(q, (int64_t)(wa / (uint32_t)G.Hkv), G.Hq, kvh, G.GQ, n, gq, a0, a1);
+            load_q(q, (int64_t)(wb / (uint32_t)G.Hkv), G.Hq, kvh, G.GQ, n, gq, b0, b1);
         };
-        qload(0, qa0, qb0);
-        qload(1, qa1, qb1);
-        qload(2, qa2, qb2);
+        qload(0, qa0, qa1, qb0, qb1);
+        qload(1, ra0, ra1, rb0, rb1);
         for (int idx = tid; idx < kSbKeys * 8; idx += kClusterThreads) {
             const int r = idx >> 3, ch = idx & 7;
             const int key = key_base + r;
@@ -249,25 +362,45 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
             *reinterpret_cast<lds_u32x4_t*>(lds + sb_lds_offset(r, ch)) = v;
         }
         __syncthreads();
-        // j runs past cnt (up to cnt + 1 <= 65) in the last iteration: such entries get an
-        // empty mask, so they score nothing and only store to the sink
-        auto process = [&](int j, const u32x4& qa, const u32x4& qb) {
-            const int jl = min(j, 63);
-            const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)ev.x, jl);
-            const uint32_t y = (j < cnt) ? (uint32_t)__builtin_amdgcn_readlane((int)ev.y, jl) : 0u;
-            const int t = (int)((w / (uint32_t)G.Hkv) % (uint32_t)NT);
-            score_entry(lds, key_base, y & 0xffffu, t, __builtin_bit_cast(bf16x8, qa), __builtin_bit_cast(bf16x8, qb),
-                        n, gq, lane, G.GQ, score + (int64_t)w * CS + (y >> 16), sink + wave * 64);
+        // one store instruction per unit: lanes 0 / 16 write walk a's two leaves, lanes 32 / 48
+        // walk b's, every other lane (and every lane of an empty unit) writes the sink
+        auto process = [&](int u, const u32x4& a0, const u32x4& a1, const u32x4& b0, const u32x4& b1) {
+            const int ul = min(u, 63);
+            const uint32_t wa = (uint32_t)__builtin_amdgcn_readlane((int)uax, ul);
+            const uint32_t ya = (u < nunits) ? (uint32_t)__builtin_amdgcn_readlane((int)uay, ul) : 0u;
+            const uint32_t wbr = (uint32_t)__builtin_amdgcn_readlane((int)ubx, ul);
+            const uint32_t yb = (u < nunits) ? (uint32_t)__builtin_amdgcn_readlane((int)uby, ul) : 0u;
+            const uint32_t ma = ya & 0xffffu, mb = yb & 0xffffu;
+            const uint32_t wb = mb ? wbr : wa;
+            float v = 0.0f;
+            bool two_a = false, two_b = false;
+            if (ma) {
+                const int b0i = __builtin_ctz(ma);
+                two_a = (ma >> (b0i + 1)) & 1u;
+                two_b = (mb >> (b0i + 1)) & 1u;
+                const int bits[2] = {b0i, b0i + 1 < kSbLeaves ? b0i + 1 : b0i};
+                const int ta = (int)((wa / (uint32_t)G.Hkv) % (uint32_t)NT);
+                const int tb = (int)((wb / (uint32_t)G.Hkv) % (uint32_t)NT);
+                const int k0 = key_base + b0i * kC;
+                const int lim[4] = {min(ta - k0, kC - 1), min(ta - k0 - kC, kC - 1), min(tb - k0, kC - 1),
+                                    min(tb - k0 - kC, kC - 1)};
+                v = score_unit(lds, bits, lim, __builtin_bit_cast(bf16x8, a0), __builtin_bit_cast(bf16x8, a1),
+                               __builtin_bit_cast(bf16x8, b0), __builtin_bit_cast(bf16x8, b1), n, gq, G.GQ);
+            }
+            float* dst = sink + wave * 64 + lane;
+            if (lane == 0 && ma) dst = score + (int64_t)wa * CS + (ya >> 16);
+            if (lane == 16 && two_a) dst = score + (int64_t)wa * CS + (ya >> 16) + 1;
+            if (lane == 32 && mb) dst = score + (int64_t)wb * CS + (yb >> 16);
+            if (lane == 48 && two_b) dst = score + (int64_t)wb * CS + (yb >> 16) + 1;
+            *dst = v;
         };
         // steady state: a fixed sequence of memory operations per iteration (one store per
-        // entry, two loads per prefetch), so wait counts stay exact across iterations
-        for (int j = 0; j < cnt; j += 3) {
-            process(j, qa0, qb0);
-            qload(min(j + 3, 63), qa0, qb0);
-            process(j + 1, qa1, qb1);
-            qload(min(j + 4, 63), qa1, qb1);
-            process(j + 2, qa2, qb2);
-            qload(min(j + 5, 63), qa2, qb2);
+        // unit, four loads per prefetch), so wait counts stay exact across iterations
+        for (int u = 0; u < nunits; u += 2) {
+            process(u, qa0, qa1, qb0, qb1);
+            qload(min(u + 2, 63), qa0, qa1, qb0, qb1);
+            process(u + 1, ra0, ra1, rb0, rb1);
+            qload(min(u + 3, 63), ra0, ra1, rb0, rb1);
         }
     }
 }
