@@ -194,6 +194,10 @@ static UpperCfg upper_cfg_delta(const Geom& G) {
     U.j_hi = top;
     int slot = 0;
     for (int j = j_lo; j <= top; ++j) { U.lds_first[j] = slot; slot += G.M[j]; }
+    // the summary rows of the top scored level follow (at most 2K nodes)
+    U.s_level = top;
+    U.s_first = slot;
+    slot += G.M[top];
     U.lds_nodes = slot;
     return U;
 }

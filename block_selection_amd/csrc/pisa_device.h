@@ -55,6 +55,9 @@ struct UpperCfg {
     int32_t j_lo, j_hi;
     int32_t lds_first[kMaxLevels + 1];
     int32_t lds_nodes;
+    // summary (not delta) rows of level s_level at LDS slots s_first + i: the candidates of
+    // the level where most walks start scoring (0: none staged)
+    int32_t s_level, s_first;
 };
 
 // Clustered leaf scoring (prefill): superblocks of 16 leaves; incidences are

@@ -349,6 +349,16 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const u
                                             (part & 7) * 16) = *reinterpret_cast<const u32x4*>(src);
         }
     }
+    if (U.s_level >= 2) {
+        const int ms = G.M[U.s_level];
+        for (int c = threadIdx.x; c < ms * 16; c += blockDim.x) {
+            const int node = c >> 4, part = c & 15;
+            const uint16_t* src = splanes + (part >> 3) * plane_stride + (bh_row0 + G.off[U.s_level] + node) * kD +
+                                  (part & 7) * 8;
+            *reinterpret_cast<lds_u32x4_t*>(lds + (U.s_first + node) * kLdsNodeBytes + (part >> 3) * 128 +
+                                            (part & 7) * 16) = *reinterpret_cast<const u32x4*>(src);
+        }
+    }
     __syncthreads();
 
     uint64_t wmask[WPW];
@@ -414,11 +424,13 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const u
                 // head sums of the logits of the candidates' own summaries
                 const uint32_t need_p = scored & ~pk;
                 if (need_p) {
+                    const bool s_lds = l == U.s_level;
 #pragma unroll
                     for (int i = 0; i < NTILE; ++i) {
                         const int c = row_cand(i);
-                        const TileRows r = rows_global(splanes + (bh_row0 + G.off[l] + (c >= 0 ? c : 0)) * kD,
-                                                       plane_stride, gq);
+                        const int cc = (c >= 0) ? c : 0;
+                        const TileRows r = s_lds ? rows_lds(lds, U.s_first + cc, gq)
+                                                 : rows_global(splanes + (bh_row0 + G.off[l] + cc) * kD, plane_stride, gq);
                         const f32x4 acc = child_tile_mfma(qf[i / TPW].k0, qf[i / TPW].k1, r.h0, r.h1, r.l0, r.l1);
                         float v[4];
 #pragma unroll
