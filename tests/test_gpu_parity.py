@@ -252,3 +252,61 @@ def test_decode_equals_prefill_at_same_position(topk):
             assert np.array_equal(dec, ref.idx[0, n]), (s, dec, ref.idx[0, n])
             checked += 1
     assert checked == 5
+
+
+@pytest.mark.parametrize("B,dtype", [(3, "bf16"), (4, "bf16"), (3, "f32")])
+def test_prefill_batched(B, dtype):
+    """Several batch elements with their own keys and queries (B*Hkv = 6 or 8 walks per
+    position): each element matches the oracle run on it alone."""
+    wl = synth.Workload("batched", N=3001, Hq=8, Hkv=2, topk=8, dtype=dtype, B=B, seed=11)
+    inp = synth.make_prefill(wl)
+    N = wl.N
+    print(f"[case] batched B={B} N={N} dtype={dtype}", flush=True)
+    gpu = run_prefill(inp.q, inp.k, wl.topk, dtype)
+    for b in range(B):
+        ref_pyr = oracle.build_pyramid(inp.k[b])
+        check_pyramid(gpu.pyramid[b:b + 1], ref_pyr, N, gpu.cap)
+        ts = sample_positions(N, 500, wl.topk)
+        rep = compare_selection(gpu.idx[b, ts], ts, inp.q[b], inp.k[b], ref_pyr, wl.topk)
+        _log(f"prefill_batched_B{B}_{dtype}_b{b}", rep)
+        assert rep.ok(), (b, str(rep))
+
+
+def test_decode_batched():
+    """Decode with B=2: per batch element, the refreshed pyramid equals a rebuild bitwise and
+    the selection matches the oracle (near-ties validated)."""
+    from block_selection_amd import ops
+    B, N0, steps, K = 2, 2000, 12, 16
+    wl = synth.Workload("decode_b2", N=N0, Hq=16, Hkv=2, topk=K, dtype="bf16", B=B, decode_steps=steps, seed=5)
+    inp = synth.make_decode(wl)
+    cap = N0 + steps
+    dims = ops.make_dims(B, 16, 2, K, "bf16")
+    kc_host = np.zeros((B, cap, 2, 64), np.float32)
+    kc_host[:, :N0] = inp.k_ctx
+    k_cache = to_device(kc_host, "bf16")
+    pyr = ops.alloc_pyramid(dims, cap)
+    ops.build_pyramid(k_cache, N0, cap, dims, pyr)
+    k_new, q_new = to_device(inp.k_new, "bf16"), to_device(inp.q_new, "bf16")
+    out = torch.full((B, 2, K), -7, dtype=torch.int32, device="cuda")
+    ws = ops.alloc_workspace(dims, 1, cap, is_decode=True)
+    pyr_rb = ops.alloc_pyramid(dims, cap)
+    k_all = np.concatenate([inp.k_ctx, np.transpose(inp.k_new, (1, 0, 2, 3))], axis=1)   # [B, cap, Hkv, d]
+    ref_k = to_device(k_all, "bf16")
+    for s in range(steps):
+        n = N0 + s
+        print(f"[case] decode B=2 step={s}", flush=True)
+        ops.decode_update_select(q_new[s].contiguous(), k_new[s].contiguous(), k_cache, pyr, n, cap, dims, out, ws)
+        torch.cuda.synchronize()
+        ops.build_pyramid(ref_k, n + 1, cap, dims, pyr_rb)
+        a, r = pyr.cpu().numpy(), pyr_rb.cpu().numpy()
+        got = out.cpu().numpy()
+        for b in range(B):
+            for j in range(2):
+                for la, lb in zip(pyramid_levels(a[b, j], n + 1, cap), pyramid_levels(r[b, j], n + 1, cap)):
+                    assert np.array_equal(la.view(np.uint32), lb.view(np.uint32)), (s, b, j)
+            ref_pyr, o_idx, o_gap = oracle.decode_step(k_all[b], n, inp.q_new[s, b], K)
+            for j in range(2):
+                if not np.array_equal(got[b, j], o_idx[j]):
+                    assert o_gap[j] < 1e-3, (s, b, j, got[b, j], o_idx[j], o_gap[j])
+                    v = oracle.validate(inp.q_new[s, b], n, j, k_all[b, : n + 1], ref_pyr, K, got[b, j], 1e-3)
+                    assert v != 0, (s, b, j)
