@@ -35,8 +35,8 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p,
 // walk with at most K candidates has none (its candidates are all kept). The workgroup owns the
 // buckets (b, kvh, sb, r) of its range: an LDS histogram counts them, and in the fill
 // pass the same bins, seeded with the bucket offsets, hand out entry positions.
-// Entry = {walk, leaf mask | first slot << 16}: the mask holds the superblock offsets of
-// one leaf or of a sibling pair.
+// Entry = {query position t, leaf mask | first slot << 16}: the mask holds the superblock
+// offsets of one leaf or of a sibling pair (batch element and KV head are the bucket's).
 template <int SL>
 __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __restrict__ cand,
                                                           const int32_t* __restrict__ ncand, Geom G,
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __rest
         const uint32_t m = (leaf >= 0) ? ((pair ? 3u : 1u) << (leaf % kSbLeaves)) : 0u;
         if (start) {
             const uint32_t pos = atomicAdd(&bins[kvh * CG.NSB + sbv], 1u);
-            if (fill) entries[pos] = make_uint2((uint32_t)w, m | ((uint32_t)i << 16));
+            if (fill) entries[pos] = make_uint2((uint32_t)(w / G.Hkv - (int64_t)b * NT), m | ((uint32_t)i << 16));
         }
     }
     __syncthreads();
@@ -171,25 +171,32 @@ __device__ inline void leaf_logits(const lds_char_t* lds, int bit, const bf16x8 
     }
 }
 
-// This lane's sum of 2^(logit) over its 16 keys of a leaf, keys past lim masked (the
-// order of leaf_lse_from_acc).
-__device__ inline float lane_exp_sum(const f32x4 (&acc)[4], int lim, bool full, int gq) {
-    float v = 0.f;
-    if (full) {
+// This lane's exp sums of the four (walk, leaf) combinations of a unit (see score_unit),
+// in row order r = (walk r >> 1, leaf r & 1).
+template <bool kFull>
+__device__ inline void unit_exp_sums(const lds_char_t* lds, const int (&bits)[2], const int (&lim)[4],
+                                     const bf16x8 qa0, const bf16x8 qa1, const bf16x8 qb0, const bf16x8 qb1,
+                                     int n, int gq, float (&sum)[4]) {
 #pragma unroll
-        for (int tau = 0; tau < 4; ++tau)
+    for (int j = 0; j < 2; ++j) {
+        f32x4 acca[4], accb[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v += __builtin_amdgcn_exp2f(acc[tau][r] * kScale2);
-    } else {
-#pragma unroll
-        for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float e2 = __builtin_amdgcn_exp2f(acc[tau][r] * kScale2);
-                v += (16 * tau + 4 * gq + r <= lim) ? e2 : 0.0f;
-            }
+        for (int tau = 0; tau < 4; ++tau) {
+            const int r = bits[j] * kC + 16 * tau + n;
+            const u32x4 a0 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, gq));
+            const u32x4 a1 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, 4 + gq));
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), qa0, c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), qa1, c, 0, 0, 0);
+            acca[tau] = c;
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), qb0, d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), qb1, d, 0, 0, 0);
+            accb[tau] = d;
+        }
+        sum[j] = leaf_exp_sum<kFull>(acca, lim[j], gq);
+        sum[2 + j] = leaf_exp_sum<kFull>(accb, lim[2 + j], gq);
     }
-    return v;
 }
 
 // Scores of a unit: two walks a and b (b may repeat a) against the two leaves of one
@@ -209,27 +216,12 @@ __device__ inline float score_unit(const lds_char_t* lds, const int (&bits)[2], 
         lim[r] = max(lim_in[r], 0);
         full = full && lim[r] == kC - 1;
     }
+    // one branch per unit: a unit with no masked key (the common case) runs straight-line code
     float sum[4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        f32x4 acca[4], accb[4];
-#pragma unroll
-        for (int tau = 0; tau < 4; ++tau) {
-            const int r = bits[j] * kC + 16 * tau + n;
-            const u32x4 a0 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, gq));
-            const u32x4 a1 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, 4 + gq));
-            f32x4 c = {0.f, 0.f, 0.f, 0.f};
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), qa0, c, 0, 0, 0);
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), qa1, c, 0, 0, 0);
-            acca[tau] = c;
-            f32x4 d = {0.f, 0.f, 0.f, 0.f};
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), qb0, d, 0, 0, 0);
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), qb1, d, 0, 0, 0);
-            accb[tau] = d;
-        }
-        sum[j] = lane_exp_sum(acca, lim[j], full, gq);
-        sum[2 + j] = lane_exp_sum(accb, lim[2 + j], full, gq);
-    }
+    if (full)
+        unit_exp_sums<true>(lds, bits, lim, qa0, qa1, qb0, qb1, n, gq, sum);
+    else
+        unit_exp_sums<false>(lds, bits, lim, qa0, qa1, qb0, qb1, n, gq, sum);
     // column totals of the four sums in one vector: row r = (walk r >> 1, leaf r & 1)
     const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(sum[0]), __float_as_uint(sum[1]), false, false);
     const float Sa = __uint_as_float(x[0]) + __uint_as_float(x[1]);
@@ -246,21 +238,8 @@ __device__ inline float score_unit(const lds_char_t* lds, const int (&bits)[2], 
                 // rare: this (walk, leaf) again, shifted by each column's maximum logit
                 f32x4 acc[4];
                 leaf_logits(lds, bits[r & 1], (r >> 1) ? qb0 : qa0, (r >> 1) ? qb1 : qa1, n, gq, acc);
-                float m = -INFINITY;
-#pragma unroll
-                for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        if (16 * tau + 4 * gq + k <= lim[r]) m = fmaxf(m, acc[tau][k]);
-                const float moff = cols4_max(m) * kScale2;
-                float v = 0.f;
-#pragma unroll
-                for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[tau][k], kScale2, -moff));
-                        v += (16 * tau + 4 * gq + k <= lim[r]) ? e2 : 0.0f;
-                    }
+                const float moff = cols4_max(leaf_lane_max(acc, lim[r], gq)) * kScale2;
+                const float v = leaf_exp_sum<false>(acc, lim[r], gq, moff);
                 const float sr = cols4_sum(v);
                 if (gq == r) {
                     T = sr;
@@ -346,11 +325,12 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
         // queries of the first two units, in flight during the key staging; units past
         // nunits read walk 0 (a valid row) and score nothing
         u32x4 qa0, qa1, qb0, qb1, ra0, ra1, rb0, rb1;
+        const int64_t bt0 = (int64_t)b * NT;   // entries hold positions t of batch element b
         auto qload = [&](int u, u32x4& a0, u32x4& a1, u32x4& b0, u32x4& b1) {
-            const uint32_t wa = (uint32_t)__builtin_amdgcn_readlane((int)uax, u);
-            const uint32_t wb = (uint32_t)__builtin_amdgcn_readlane((int)(uby ? ubx : uax), u);
-            load_q(q, (int64_t)(wa / (uint32_t)G.Hkv), G.Hq, kvh, G.GQ, n, gq, a0, a1);
-            load_q(q, (int64_t)(wb / (uint32_t)G.Hkv), G.Hq, kvh, G.GQ, n, gq, b0, b1);
+            const uint32_t ta = (uint32_t)__builtin_amdgcn_readlane((int)uax, u);
+            const uint32_t tb = (uint32_t)__builtin_amdgcn_readlane((int)(uby ? ubx : uax), u);
+            load_q(q, bt0 + ta, G.Hq, kvh, G.GQ, n, gq, a0, a1);
+            load_q(q, bt0 + tb, G.Hq, kvh, G.GQ, n, gq, b0, b1);
         };
         qload(0, qa0, qa1, qb0, qb1);
         qload(1, ra0, ra1, rb0, rb1);
@@ -366,12 +346,14 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
         // walk b's, every other lane (and every lane of an empty unit) writes the sink
         auto process = [&](int u, const u32x4& a0, const u32x4& a1, const u32x4& b0, const u32x4& b1) {
             const int ul = min(u, 63);
-            const uint32_t wa = (uint32_t)__builtin_amdgcn_readlane((int)uax, ul);
+            const uint32_t tua = (uint32_t)__builtin_amdgcn_readlane((int)uax, ul);
             const uint32_t ya = (u < nunits) ? (uint32_t)__builtin_amdgcn_readlane((int)uay, ul) : 0u;
-            const uint32_t wbr = (uint32_t)__builtin_amdgcn_readlane((int)ubx, ul);
+            const uint32_t tbr = (uint32_t)__builtin_amdgcn_readlane((int)ubx, ul);
             const uint32_t yb = (u < nunits) ? (uint32_t)__builtin_amdgcn_readlane((int)uby, ul) : 0u;
             const uint32_t ma = ya & 0xffffu, mb = yb & 0xffffu;
-            const uint32_t wb = mb ? wbr : wa;
+            const uint32_t tub = mb ? tbr : tua;
+            // walk index (b, t, kvh)
+            const int64_t wa = (bt0 + tua) * G.Hkv + kvh, wb = (bt0 + tub) * G.Hkv + kvh;
             float v = 0.0f;
             bool two_a = false, two_b = false;
             if (ma) {
@@ -379,8 +361,7 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
                 two_a = (ma >> (b0i + 1)) & 1u;
                 two_b = (mb >> (b0i + 1)) & 1u;
                 const int bits[2] = {b0i, b0i + 1 < kSbLeaves ? b0i + 1 : b0i};
-                const int ta = (int)((wa / (uint32_t)G.Hkv) % (uint32_t)NT);
-                const int tb = (int)((wb / (uint32_t)G.Hkv) % (uint32_t)NT);
+                const int ta = (int)tua, tb = (int)tub;
                 const int k0 = key_base + b0i * kC;
                 const int lim[4] = {min(ta - k0, kC - 1), min(ta - k0 - kC, kC - 1), min(tb - k0, kC - 1),
                                     min(tb - k0 - kC, kC - 1)};
@@ -388,10 +369,10 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
                                __builtin_bit_cast(bf16x8, b0), __builtin_bit_cast(bf16x8, b1), n, gq, G.GQ);
             }
             float* dst = sink + wave * 64 + lane;
-            if (lane == 0 && ma) dst = score + (int64_t)wa * CS + (ya >> 16);
-            if (lane == 16 && two_a) dst = score + (int64_t)wa * CS + (ya >> 16) + 1;
-            if (lane == 32 && mb) dst = score + (int64_t)wb * CS + (yb >> 16);
-            if (lane == 48 && two_b) dst = score + (int64_t)wb * CS + (yb >> 16) + 1;
+            if (lane == 0 && ma) dst = score + wa * CS + (ya >> 16);
+            if (lane == 16 && two_a) dst = score + wa * CS + (ya >> 16) + 1;
+            if (lane == 32 && mb) dst = score + wb * CS + (yb >> 16);
+            if (lane == 48 && two_b) dst = score + wb * CS + (yb >> 16) + 1;
             *dst = v;
         };
         // steady state: a fixed sequence of memory operations per iteration (one store per

@@ -134,6 +134,38 @@ __device__ inline uint64_t slot_key(float s, int node, int slot) {
 __device__ inline int key_node(uint32_t low) { return (low >> 6) ? (1 << 26) - 1 - (int)(low >> 6) : -1; }
 __device__ inline int key_slot(uint32_t low) { return (int)(low & 63u); }
 
+// This lane's sum over its 16 keys of one leaf (acc[tau][r]: key 16 tau + 4 gq + r) of
+// 2^(logit * kScale2 - shift), keys past lim masked (kFull: none are). The 16 terms are
+// added as a balanced tree in one fixed order, so every leaf scorer that uses this gets
+// the same bits for the same logits.
+template <bool kFull>
+__device__ inline float leaf_exp_sum(const f32x4 (&acc)[4], int lim, int gq, float shift = 0.0f) {
+    float e[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int tau = i >> 2, r = i & 3;
+        const float x = (shift == 0.0f) ? acc[tau][r] * kScale2 : __builtin_fmaf(acc[tau][r], kScale2, -shift);
+        const float e2 = __builtin_amdgcn_exp2f(x);
+        e[i] = (kFull || 16 * tau + 4 * gq + r <= lim) ? e2 : 0.0f;
+    }
+#pragma unroll
+    for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2 * w) e[i] = e[i] + e[i + w];
+    return e[0];
+}
+
+// Largest unmasked logit (natural scale) of this lane's 16 keys of one leaf.
+__device__ inline float leaf_lane_max(const f32x4 (&acc)[4], int lim, int gq) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (16 * tau + 4 * gq + r <= lim) m = fmaxf(m, acc[tau][r]);
+    return m;
+}
+
 // Leaf scores from the MFMA results of NL leaves: acc[j][tau] holds, in lane (gq, n),
 // the natural-scale logits of keys 16*tau + 4*gq + r (r = 0..3) of leaf j for head n.
 // Keys with offset > lim[j] are masked. Per head the base-2 LSE is taken without a max
@@ -149,44 +181,15 @@ __device__ inline void leaf_lse_from_acc(const f32x4 (&acc)[NL][4], const int (&
     float s[NL], shift[NL];
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-        float a = 0.f;
-        if (full) {
-#pragma unroll
-            for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) a += __builtin_amdgcn_exp2f(acc[j][tau][r] * kScale2);
-        } else {
-#pragma unroll
-            for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float e2 = __builtin_amdgcn_exp2f(acc[j][tau][r] * kScale2);
-                    a += (16 * tau + 4 * gq + r <= lim[j]) ? e2 : 0.0f;
-                }
-        }
-        s[j] = cols4_sum(a);
+        s[j] = cols4_sum(full ? leaf_exp_sum<true>(acc[j], lim[j], gq) : leaf_exp_sum<false>(acc[j], lim[j], gq));
         shift[j] = 0.0f;
     }
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
         if (ballot(!(s[j] < INFINITY && s[j] > 0x1p-100f))) {
             // rare: shift by the maximum logit of each column
-            float m = -INFINITY;
-#pragma unroll
-            for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (16 * tau + 4 * gq + r <= lim[j]) m = fmaxf(m, acc[j][tau][r]);
-            const float moff = cols4_max(m) * kScale2;
-            float a = 0.f;
-#pragma unroll
-            for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[j][tau][r], kScale2, -moff));
-                    a += (16 * tau + 4 * gq + r <= lim[j]) ? e2 : 0.0f;
-                }
-            s[j] = cols4_sum(a);
+            const float moff = cols4_max(leaf_lane_max(acc[j], lim[j], gq)) * kScale2;
+            s[j] = cols4_sum(leaf_exp_sum<false>(acc[j], lim[j], gq, moff));
             shift[j] = moff;
         }
     }
@@ -195,74 +198,6 @@ __device__ inline void leaf_lse_from_acc(const f32x4 (&acc)[NL][4], const int (&
         const float lse2 = shift[j] + __builtin_amdgcn_logf(s[j]);
         out[j] = row16_sum((n < GQ) ? lse2 : 0.0f);
     }
-}
-
-// Scores of two leaves (a sibling pair) from their MFMA results, reduced together: the
-// two leaves' per-lane sums share one permlane16 and one permlane32 exchange, one log
-// and one 16-lane row sum. Lanes of rows 0 and 2 (gq even) receive leaf 0's score,
-// rows 1 and 3 leaf 1's. The additions happen in the same order as in
-// leaf_lse_from_acc, so each score is bitwise what that function gives for the leaf
-// alone (including the shifted fallback, decided per leaf).
-__device__ inline float leaf_lse_pair(const f32x4 (&acc)[2][4], const int (&lim)[2], int n, int gq, int GQ) {
-    const bool full = lim[0] == kC - 1 && lim[1] == kC - 1;
-    float a[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        float v = 0.f;
-        if (full) {
-#pragma unroll
-            for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) v += __builtin_amdgcn_exp2f(acc[j][tau][r] * kScale2);
-        } else {
-#pragma unroll
-            for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float e2 = __builtin_amdgcn_exp2f(acc[j][tau][r] * kScale2);
-                    v += (16 * tau + 4 * gq + r <= lim[j]) ? e2 : 0.0f;
-                }
-        }
-        a[j] = v;
-    }
-    // rows (r0, r1, r2, r3) of x[0] + x[1]: leaf 0 rows 0+1, leaf 1 rows 0+1, leaf 0 rows
-    // 2+3, leaf 1 rows 2+3; then the two halves are added
-    const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[0]), __float_as_uint(a[1]), false, false);
-    const float S = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-    const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(S), __float_as_uint(S), false, false);
-    float T = __uint_as_float(y[0]) + __uint_as_float(y[1]);
-    float shift = 0.0f;
-    const uint64_t bad = ballot(!(T < INFINITY && T > 0x1p-100f));
-    if (bad) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            if (bad & (0xffffull << (16 * j))) {
-                // rare: shift leaf j by the maximum logit of each column
-                float m = -INFINITY;
-#pragma unroll
-                for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (16 * tau + 4 * gq + r <= lim[j]) m = fmaxf(m, acc[j][tau][r]);
-                const float moff = cols4_max(m) * kScale2;
-                float v = 0.f;
-#pragma unroll
-                for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[j][tau][r], kScale2, -moff));
-                        v += (16 * tau + 4 * gq + r <= lim[j]) ? e2 : 0.0f;
-                    }
-                const float sj = cols4_sum(v);
-                if ((gq & 1) == j) {
-                    T = sj;
-                    shift = moff;
-                }
-            }
-        }
-    }
-    const float lse2 = shift + __builtin_amdgcn_logf(T);
-    return row16_sum((n < GQ) ? lse2 : 0.0f);
 }
 
 }  // namespace pisa
