@@ -405,7 +405,8 @@ __global__ __launch_bounds__(256) void final_topk_kernel(const int32_t* __restri
         const int c = (ok && i < CS) ? cand[w * CS + i] : -1;
         float s = -INFINITY;
         if (c >= 0) s = (nc > K) ? score[w * CS + i] : 0.0f;
-        const int nd = select_sort<SLOTS>(s, (c >= 0) ? c : INT_MAX, i);
+        const int cidx = (c >= 0) ? c : INT_MAX;
+        const int nd = (2 * K == SLOTS) ? select_top_half<SLOTS>(s, cidx, i) : select_sort<SLOTS>(s, cidx, i);
         const int nd2 = index_sort<SLOTS>((i < K) ? nd : INT_MAX, i);
         if (ok && i < K) out[w * K + i] = (nd2 != INT_MAX) ? nd2 : -1;
     }

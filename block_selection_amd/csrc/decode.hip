@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
         const int shc = kLog2C + lc - 1;            // first key of a level-lc node i: i << shc
         const int Mc = G.M[lc];
         if (wave < 4) {
-            // tile `wave`: MFMA row n = candidate of slot 16 * wave + n
+            // tile `wave`: MFMA column n = candidate of slot 16 * wave + n
             const int c = shfl_i(cand, 16 * wave + n);
             const int rc = 2 * c + 1;
             const bool rv = c >= 0 && rc < Mc && rc <= (int)(t >> shc);
@@ -154,26 +154,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
                 u32x4 h0, l0, h1, l1;
                 split8(d0, h0, l0);
                 split8(d1, h1, l1);
-                const f32x4 acc = child_tile_mfma(q0, q1, h0, h1, l0, l1);
-                float tv[4], dv[4];
-                if ((rvm & 0xffffu) == 0xffffu && G.GQ == kMaxGroup) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        dv[k] = acc[k];
-                        tv[k] = pair_lse_term(acc[k]);
-                    }
-                } else {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const bool rk = (rvm >> (4 * gq + k)) & 1u;
-                        dv[k] = (n < G.GQ) ? acc[k] : 0.0f;
-                        tv[k] = (n < G.GQ) ? (rk ? pair_lse_term(acc[k]) : acc[k]) : 0.0f;
-                    }
-                }
-                const float F = head_sum4(tv, n), D = head_sum4(dv, n);
-                if (n < 4) {
-                    s_F[buf][16 * wave + 4 * gq + n] = F;
-                    s_D[buf][16 * wave + 4 * gq + n] = D;
+                const f32x4 acc = summary_tile_mfma(q0, q1, h0, h1, l0, l1);
+                float F, D;
+                delta_tile_sums(acc, rvm, n, gq, G.GQ, F, D);
+                if (gq == 0) {
+                    s_F[buf][16 * wave + n] = F;
+                    s_D[buf][16 * wave + n] = D;
                 }
             }
             if (!pk) {
@@ -181,12 +167,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
                 u32x4 h0, l0, h1, l1;
                 split8(vp0, h0, l0);
                 split8(vp1, h1, l1);
-                const f32x4 acc = child_tile_mfma(q0, q1, h0, h1, l0, l1);
-                float v[4];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) v[k] = (n < G.GQ) ? acc[k] : 0.0f;
-                const float ps = head_sum4(v, n);
-                if (n < 4) s_P[buf][16 * wave + 4 * gq + n] = ps;
+                const f32x4 acc = summary_tile_mfma(q0, q1, h0, h1, l0, l1);
+                const float ps = tile_head_sums(acc, gq, G.GQ);
+                if (gq == 0) s_P[buf][16 * wave + n] = ps;
             }
         } else if (wave == 4) {
             // the ragged node of level l (a partial right child), read directly when it is a
@@ -204,14 +187,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
                     u32x4 h0, l0, h1, l1;
                     split8(v0, h0, l0);
                     split8(v1, h1, l1);
-                    const f32x4 acc = child_tile_mfma(q0, q1, h0, h1, l0, l1);
-                    float v[4];
-                    v[0] = (n < G.GQ) ? log2_add_exp2(acc[0], acc[1]) : 0.0f;
-                    v[1] = (n < G.GQ) ? acc[0] : 0.0f;
-                    v[2] = (n < G.GQ) ? acc[1] : 0.0f;
-                    v[3] = 0.0f;
-                    const float x = head_sum4(v, n);
-                    if (lane < 3) s_fix[buf][lane] = x;
+                    const f32x4 acc = summary_tile_mfma(q0, q1, h0, h1, l0, l1);   // column 0: left, 1: right
+                    float xf, xp;
+                    ragged_sums(acc, gq, G.GQ, xf, xp);
+                    if (lane == 0) {
+                        s_fix[buf][0] = xf;
+                        s_fix[buf][1] = xp;
+                    }
+                    if (lane == 1) s_fix[buf][2] = xp;
                 }
             }
             if (lane == 0) s_fixslot[buf] = fix_slot;
@@ -228,7 +211,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
         }
         buf ^= 1;
         pk = true;
-        const uint64_t sorted = bitonic_desc<64, SegmentLanes>(slot_key((cand >= 0) ? score : -INFINITY, cand, lane), lane);
+        const uint64_t key = slot_key((cand >= 0) ? score : -INFINITY, cand, lane);
+        // the survivors are the K best as a set; with 2K = 64 a partial network finds them
+        const uint64_t sorted = (2 * K == 64) ? bitonic_top_half<64, SegmentLanes>(key, lane)
+                                              : bitonic_desc<64, SegmentLanes>(key, lane);
         surv_low = (lane < K) ? (uint32_t)sorted : 0u;
     }
 
@@ -265,7 +251,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
     }
     if (wave == 0) {
         const float my = (leaf >= 0) ? (scored ? leaf_score[(int64_t)bh * 64 + lane] : 0.0f) : -INFINITY;
-        const int nd = select_sort<64>(my, (leaf >= 0) ? leaf : INT_MAX, lane);
+        const int lidx = (leaf >= 0) ? leaf : INT_MAX;
+        const int nd = (2 * K == 64) ? select_top_half<64>(my, lidx, lane) : select_sort<64>(my, lidx, lane);
         const int keep = index_sort<64>((lane < K) ? nd : INT_MAX, lane);   // ascending, INT_MAX last
         if (lane < K) out[(int64_t)bh * K + lane] = (keep != INT_MAX) ? keep : -1;
         if (scored && lane == 0) done[bh] = 0u;   // ready for the next step

@@ -113,11 +113,38 @@ __device__ inline T bitonic_desc(T key, int m) {
     return key;
 }
 
+// The SLOTS/2 largest keys of each segment, in slots 0 .. SLOTS/2 - 1 in no particular
+// order: the halves are sorted in opposite directions (the network above up to sequences
+// of SLOTS/2), then one compare-exchange of slot m with m + SLOTS/2 splits the bitonic
+// whole into its larger and smaller halves. log2(SLOTS) - 1 fewer steps than the sort.
+template <int SLOTS, typename Lanes, typename T>
+__device__ inline T bitonic_top_half(T key, int m) {
+    static_assert(SLOTS >= 2, "a segment holds at least two slots");
+#pragma unroll
+    for (int k = 2; k < SLOTS; k <<= 1) {
+        if (k >= 64) key_step<32, Lanes::of(32)>(key, m, k);
+        if (k >= 32) key_step<16, Lanes::of(16)>(key, m, k);
+        if (k >= 16) key_step<8, Lanes::of(8)>(key, m, k);
+        if (k >= 8) key_step<4, Lanes::of(4)>(key, m, k);
+        if (k >= 4) key_step<2, Lanes::of(2)>(key, m, k);
+        key_step<1, Lanes::of(1)>(key, m, k);
+    }
+    key_step<SLOTS / 2, Lanes::of(SLOTS / 2)>(key, m, SLOTS);
+    return key;
+}
+
 // The index at slot m after ordering each segment's (score, index) pairs by selection
 // order (slot 0 = the pair that precedes all others).
 template <int SLOTS, typename Lanes = SegmentLanes>
 __device__ inline int select_sort(float s, int nd, int m) {
     return key_index(bitonic_desc<SLOTS, Lanes>(select_key(s, nd), m));
+}
+
+// The index at slot m < SLOTS/2 after keeping each segment's SLOTS/2 (score, index) pairs
+// that come first in selection order (unordered among themselves).
+template <int SLOTS, typename Lanes = SegmentLanes>
+__device__ inline int select_top_half(float s, int nd, int m) {
+    return key_index(bitonic_top_half<SLOTS, Lanes>(select_key(s, nd), m));
 }
 
 // The index at slot m after sorting each segment's indices ascending (nonnegative

@@ -229,7 +229,10 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_f32_kernel(const flo
                 }
                 if (cand < 0) my = -INFINITY;
             }
-            const int nd = select_sort<SLOTS, TileLanes>(my, (cand >= 0) ? cand : INT_MAX, ml);
+            // the survivors are the K best as a set; with 2K = SLOTS a partial network finds them
+            const int cidx = (cand >= 0) ? cand : INT_MAX;
+            const int nd = (2 * K == SLOTS) ? select_top_half<SLOTS, TileLanes>(my, cidx, ml)
+                                            : select_sort<SLOTS, TileLanes>(my, cidx, ml);
             surv = (ml < K && nd != INT_MAX) ? nd : -1;
         }
         // leaf candidates: children of the level-2 survivors (or the root if it is a leaf)
@@ -288,19 +291,11 @@ __global__ __launch_bounds__(256) void delta_planes_kernel(const float* __restri
 }
 
 // Slot layout: slot m of walk w (SLOTS = 16 * TPW slots per walk) lives in lane
-//   16 * ((m >> 2) & 3) + 4 * (w * TPW + (m >> 4)) + (m & 3),
-// so tile u = w * TPW + (m >> 4) holds slots 16 (m >> 4) .. + 15 of walk w in MFMA rows
-// 0..15, and after head_sum4 the sum of row 4g + i sits in lane (g, n) for n & 3 = i:
-// in place for the lanes with (n >> 2) == u. Slot bits 0..5 map to lane bits 0, 1, 4, 5,
-// 2, 3: every bitonic partner is a DPP or permlane move away.
+// w * SLOTS + m. Tile i (lanes 16i .. 16i+15) puts the candidates of its 16 slots in its
+// MFMA columns, and the head sums of column n reach every lane of that column, so lane
+// 16i + n takes tile i's sums of column n.
 template <int SLOTS>
-__device__ constexpr int dslot_lane(int w, int m) {
-    return 16 * ((m >> 2) & 3) + 4 * (w * (SLOTS / 16) + (m >> 4)) + (m & 3);
-}
-constexpr int dslot_bit_lane(int J) { return J == 1 ? 1 : J == 2 ? 2 : J == 4 ? 16 : J == 8 ? 32 : J == 16 ? 4 : 8; }
-struct DeltaLanes {
-    static constexpr int of(int J) { return dslot_bit_lane(J); }
-};
+__device__ constexpr int dslot_lane(int w, int m) { return w * SLOTS + m; }
 
 template <int SLOTS>
 __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const uint16_t* __restrict__ q,
@@ -330,9 +325,9 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const u
     const int b = bh / G.Hkv, kvh = bh % G.Hkv;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
     const int gq = lane >> 4, n = lane & 15;
-    const int u = (lane >> 2) & 3;                           // tile whose results land in this lane
-    const int wl = u / TPW;                                  // this lane's walk
-    const int ml = 16 * (u % TPW) + 4 * gq + (lane & 3);     // this lane's slot
+    const int u = gq;                                        // tile whose results land in this lane
+    const int wl = lane / SLOTS;                             // this lane's walk
+    const int ml = lane % SLOTS;                             // this lane's slot
     const int K = G.topk;
     const int64_t plane_stride = (int64_t)G.B * G.Hkv * G.P * kD;
     const int64_t bh_row0 = (int64_t)bh * G.P;
@@ -368,7 +363,6 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const u
         for (int m = 0; m < SLOTS; ++m) mk |= 1ull << dslot_lane<SLOTS>(w, m);
         wmask[w] = mk;
     }
-    const bool full_group = G.GQ == kMaxGroup;
 
     const int64_t ngroups = (NT + WPW - 1) / WPW;
     for (int64_t grp = (int64_t)peer * nwaves + wave; grp < ngroups; grp += (int64_t)npeers * nwaves) {
@@ -416,10 +410,8 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const u
                 const int lc = l - 1;
                 const int shc = kLog2C + lc - 1;            // first key of a level-lc node i: i << shc
                 const int Mc = G.M[lc];
-                // candidate of MFMA row n of tile i (walk i / TPW, slots 16 (i % TPW) + n)
-                auto row_cand = [&](int i) -> int {
-                    return shfl_i(cand, dslot_lane<SLOTS>(i / TPW, 16 * (i % TPW) + n));
-                };
+                // candidate of MFMA column n of tile i (lane 16i + n)
+                auto row_cand = [&](int i) -> int { return shfl_i(cand, 16 * i + n); };
                 // (1) P of the candidates of walks that were not scored at the level above:
                 // head sums of the logits of the candidates' own summaries
                 const uint32_t need_p = scored & ~pk;
@@ -431,11 +423,8 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const u
                         const int cc = (c >= 0) ? c : 0;
                         const TileRows r = s_lds ? rows_lds(lds, U.s_first + cc, gq)
                                                  : rows_global(splanes + (bh_row0 + G.off[l] + cc) * kD, plane_stride, gq);
-                        const f32x4 acc = child_tile_mfma(qf[i / TPW].k0, qf[i / TPW].k1, r.h0, r.h1, r.l0, r.l1);
-                        float v[4];
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) v[k] = (n < G.GQ) ? acc[k] : 0.0f;
-                        const float ps = head_sum4(v, n);
+                        const f32x4 acc = summary_tile_mfma(qf[i / TPW].k0, qf[i / TPW].k1, r.h0, r.h1, r.l0, r.l1);
+                        const float ps = tile_head_sums(acc, gq, G.GQ);
                         if (u == i && ((need_p >> wl) & 1)) P = ps;
                     }
                 }
@@ -448,7 +437,7 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const u
                     const int rc = 2 * c + 1;                 // right child
                     const bool rv = c >= 0 && rc < Mc && rc <= (int)(tw[i / TPW] >> shc);
                     row = (c >= 0) ? c : 0;
-                    return (uint32_t)ballot(rv);              // bit r: row r has an eligible right child
+                    return (uint32_t)ballot(rv);              // bit n: column n has an eligible right child
                 };
                 auto fetch = [&](int row) -> TileRows {
                     if (in_lds) return rows_lds(lds, lds_lvl + row, gq);
@@ -467,23 +456,9 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const u
                         rvm_next = pick(i + 1, rown);
                         nxt = fetch(rown);
                     }
-                    const f32x4 acc = child_tile_mfma(qf[i / TPW].k0, qf[i / TPW].k1, cur.h0, cur.h1, cur.l0, cur.l1);
-                    float tv[4], dv[4];
-                    if ((rvm & 0xffffu) == 0xffffu && full_group) {
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) {
-                            dv[k] = acc[k];
-                            tv[k] = pair_lse_term(acc[k]);
-                        }
-                    } else {
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) {
-                            const bool rv = (rvm >> (4 * gq + k)) & 1u;
-                            dv[k] = (n < G.GQ) ? acc[k] : 0.0f;
-                            tv[k] = (n < G.GQ) ? (rv ? pair_lse_term(acc[k]) : acc[k]) : 0.0f;
-                        }
-                    }
-                    const float Ft = head_sum4(tv, n), Dt = head_sum4(dv, n);
+                    const f32x4 acc = summary_tile_mfma(qf[i / TPW].k0, qf[i / TPW].k1, cur.h0, cur.h1, cur.l0, cur.l1);
+                    float Ft, Dt;
+                    delta_tile_sums(acc, rvm, n, gq, G.GQ, Ft, Dt);
                     if (u == i) {
                         F = Ft;
                         D = Dt;
@@ -503,17 +478,12 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const u
 #pragma unroll
                     for (int w = 0; w < WPW; ++w) {
                         if (rm & wmask[w]) {
-                            const int crow = (n == 1) ? brag : brag - 1;
+                            const int crow = (n == 1) ? brag : brag - 1;   // column 0: left child, 1: right
                             const TileRows r = rows_global(splanes + (bh_row0 + G.off[lc] + crow) * kD, plane_stride, gq);
-                            const f32x4 acc = child_tile_mfma(qf[w].k0, qf[w].k1, r.h0, r.h1, r.l0, r.l1);
-                            // lane (0, n): acc[0] = left child's logit, acc[1] = right child's
-                            float v[4];
-                            v[0] = (n < G.GQ) ? log2_add_exp2(acc[0], acc[1]) : 0.0f;
-                            v[1] = (n < G.GQ) ? acc[0] : 0.0f;
-                            v[2] = (n < G.GQ) ? acc[1] : 0.0f;
-                            v[3] = 0.0f;
-                            const float x = head_sum4(v, n);
-                            const float f_fix = readlane_f(x, 0), pa_fix = readlane_f(x, 1), pb_fix = readlane_f(x, 2);
+                            const f32x4 acc = summary_tile_mfma(qf[w].k0, qf[w].k1, r.h0, r.h1, r.l0, r.l1);
+                            float xf, xp;
+                            ragged_sums(acc, gq, G.GQ, xf, xp);
+                            const float f_fix = readlane_f(xf, 0), pa_fix = readlane_f(xp, 0), pb_fix = readlane_f(xp, 1);
                             if (is_rag && wl == w) {
                                 score = f_fix;
                                 Pa = pa_fix;
@@ -526,7 +496,9 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const u
             pk = scored;
             // walks with at most K candidates keep them all whatever their scores
             const uint64_t key = slot_key((cand >= 0) ? score : -INFINITY, cand, ml);
-            const uint64_t sorted = bitonic_desc<SLOTS, DeltaLanes>(key, ml);
+            // the survivors are the K best as a set; with 2K = SLOTS a partial network finds them
+            const uint64_t sorted = (2 * K == SLOTS) ? bitonic_top_half<SLOTS, SegmentLanes>(key, ml)
+                                                     : bitonic_desc<SLOTS, SegmentLanes>(key, ml);
             surv_low = (ml < K) ? (uint32_t)sorted : 0u;
         }
         // leaf candidates: children of the level-2 survivors (or the root if it is a leaf)
@@ -541,7 +513,7 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const u
             leaf = ok ? child : -1;
         }
         // ascending order, -1 last
-        const int nd = index_sort<SLOTS, DeltaLanes>((leaf >= 0) ? leaf : INT_MAX, ml);
+        const int nd = index_sort<SLOTS, SegmentLanes>((leaf >= 0) ? leaf : INT_MAX, ml);
         leaf = (nd != INT_MAX && ml < 2 * K) ? nd : -1;
         const uint64_t lm = ballot(leaf >= 0);
         uint64_t mine = 0;

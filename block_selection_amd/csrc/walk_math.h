@@ -44,17 +44,49 @@ __device__ inline void split8(const float v[8], u32x4& h, u32x4& l) {
     }
 }
 
-// Base-2 logits of a 16-row tile of summaries (row = lane % 16) against the query
-// fragments q0 (dims 8gq..8gq+7) and q1 (dims 32+8gq..32+8gq+7): hi plane then lo
-// plane, two k-steps each, one accumulation chain.
-__device__ inline f32x4 child_tile_mfma(const bf16x8 q0, const bf16x8 q1, u32x4 h0, u32x4 h1, u32x4 l0,
-                                        u32x4 l1) {
+// Base-2 logits of 16 summary rows against the group's query heads, one MFMA tile: the
+// queries are the A operand (tile row m = head m) and the rows the B operand (tile column
+// n = the row that lane n % 16 supplies). Fragments: q0 / q1 hold dims 8gq..8gq+7 /
+// 32+8gq..32+8gq+7 of head n, h* / l* the same dims of row n's hi / lo planes. Hi plane
+// then lo plane, two k-steps each, one accumulation chain. Lane (gq, n) receives the logits
+// of heads 4gq..4gq+3 against row n.
+__device__ inline f32x4 summary_tile_mfma(const bf16x8 q0, const bf16x8 q1, u32x4 h0, u32x4 h1, u32x4 l0,
+                                          u32x4 l1) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h0), q0, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, h1), q1, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, l0), q0, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, l1), q1, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q0, __builtin_bit_cast(bf16x8, h0), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q1, __builtin_bit_cast(bf16x8, h1), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q0, __builtin_bit_cast(bf16x8, l0), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q1, __builtin_bit_cast(bf16x8, l1), acc, 0, 0, 0);
     return acc;
+}
+
+// Sum over the heads of a summary tile: lane (gq, n) adds its four heads as
+// (v0 + v1) + (v2 + v3), then the four row groups are added pairwise (lane ^ 16, then
+// lane ^ 32). Every lane of column n receives the same bits.
+__device__ inline float heads_total(const float v[4]) { return cols4_sum((v[0] + v[1]) + (v[2] + v[3])); }
+
+// Two head sums at once, in the order of heads_total: one permlane16 exchange packs the
+// two quantities into alternate row groups, one permlane32 exchange completes both, and a
+// last permlane16 exchange hands each lane both totals of its column.
+__device__ inline void heads_total2(const float f[4], const float d[4], float& F, float& D) {
+    const float sf = (f[0] + f[1]) + (f[2] + f[3]), sd = (d[0] + d[1]) + (d[2] + d[3]);
+    // row groups 0..3 of the sum: f 0+1, d 0+1, f 2+3, d 2+3
+    const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(sf), __float_as_uint(sd), false, false);
+    const float S = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    // row groups: F, D, F, D
+    const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(S), __float_as_uint(S), false, false);
+    const float T = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+    const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(T), __float_as_uint(T), false, false);
+    F = __uint_as_float(z[0]);
+    D = __uint_as_float(z[1]);
+}
+
+// Head sum of the logits of each column of a summary tile (heads past the group masked).
+__device__ inline float tile_head_sums(const f32x4& acc, int gq, int GQ) {
+    float v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = (4 * gq + k < GQ) ? acc[k] : 0.0f;
+    return heads_total(v);
 }
 
 // log2(2^a + 2^b)
@@ -101,25 +133,44 @@ __device__ inline float pair_lse_term(float d) {
     return a + __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(-2.0f * a));
 }
 
-// Sums over the 16 head columns of four values per lane: v[i] in lane (g, n) belongs to
-// tile row 4g + i and head column n. Afterwards every lane (g, n) holds the sum of row
-// 4g + (n & 3); the four lanes of a row group that hold the same row get bitwise equal
-// sums (a reduce-scatter over lane ^ 2 and lane ^ 1, then a symmetric butterfly over
-// lane ^ 8 and lane ^ 4), so the result does not depend on which of them is read.
-__device__ inline float head_sum4(const float v[4], int n) {
-    const bool b1 = (n >> 1) & 1, b0 = n & 1;
-    // lane ^ 2: lanes with b1 = 0 keep rows 0, 1 and hand over rows 2, 3 (and vice versa)
-    const float k0 = b1 ? v[2] : v[0], k1 = b1 ? v[3] : v[1];
-    const float s0 = b1 ? v[0] : v[2], s1 = b1 ? v[1] : v[3];
-    const float r0 = k0 + lane_xor_f<2>(s0);
-    const float r1 = k1 + lane_xor_f<2>(s1);
-    // lane ^ 1: keep row 2 b1 + b0
-    const float k = b0 ? r1 : r0, sd = b0 ? r0 : r1;
-    float x = k + lane_xor_f<1>(sd);
-    // the four quads of the row group
-    x = x + lane_xor_f<8>(x);
-    x = x + lane_xor_f<4>(x);
-    return x;
+// Pair sums of a delta tile (column n = candidate n, its delta row): F = sum over the
+// group's heads of g(d), or of d alone when the candidate has no eligible right child
+// (bit n of rvm clear), and D = sum of d. Every lane of column n receives both.
+__device__ inline void delta_tile_sums(const f32x4& acc, uint32_t rvm, int n, int gq, int GQ, float& F, float& D) {
+    float tv[4], dv[4];
+    if ((rvm & 0xffffu) == 0xffffu && GQ == kMaxGroup) {
+        // every right child eligible and every row a head of the group (same result)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            dv[k] = acc[k];
+            tv[k] = pair_lse_term(acc[k]);
+        }
+    } else {
+        const bool rv = (rvm >> n) & 1u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const bool h = 4 * gq + k < GQ;
+            dv[k] = h ? acc[k] : 0.0f;
+            tv[k] = h ? (rv ? pair_lse_term(acc[k]) : acc[k]) : 0.0f;
+        }
+    }
+    heads_total2(tv, dv, F, D);
+}
+
+// The ragged node's children read directly: column 0 of the tile holds the left child's
+// logits, column 1 the right child's. F (read in column 0) = sum over the group's heads
+// of log2(2^L + 2^R); Pc (column c) = the head sum of child c's logits. Call with every
+// lane active (a lane exchange).
+__device__ inline void ragged_sums(const f32x4& acc, int gq, int GQ, float& F, float& Pc) {
+    float fv[4], pv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float r = lane_xor_f<1>(acc[k]);   // column 1 into column 0
+        const bool h = 4 * gq + k < GQ;
+        fv[k] = h ? log2_add_exp2(acc[k], r) : 0.0f;
+        pv[k] = h ? acc[k] : 0.0f;
+    }
+    heads_total2(fv, pv, F, Pc);
 }
 
 // Selection key that also records the slot a candidate came from: selection order
