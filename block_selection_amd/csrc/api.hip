@@ -32,7 +32,8 @@ __global__ void leaf_walk_kernel(const KT*, const KT*, Geom, int64_t, int64_t, c
 __global__ void fill_u32_kernel(uint32_t*, int64_t, uint32_t);
 template <int SL>
 __global__ void bucket_pass_kernel(const int32_t*, const int32_t*, Geom, ClusterGeom, int64_t, uint32_t*,
-                                   const uint32_t*, uint2*, int);
+                                   const uint32_t*, const uint32_t*, uint2*, int);
+__global__ void group_offsets_kernel(const uint32_t*, ClusterGeom, uint32_t*, uint32_t*);
 __global__ void scan_groups_kernel(const uint32_t*, ClusterGeom, uint32_t*, int4*, uint32_t*);
 __global__ void leaf_cluster_kernel(const uint16_t*, const uint16_t*, Geom, ClusterGeom, int64_t,
                                     const int4*, const uint2*, uint32_t*, float*, float*);
@@ -52,8 +53,10 @@ struct Workspace {
     // clustered leaf scoring (prefill, bf16 inputs)
     float* score;        // [walks][2K]
     float* sink;         // [kClusterThreads] stores of lanes without a score
-    uint32_t* counts;    // [nb]
-    uint32_t* offsets;   // [nb]
+    uint32_t* counts;    // [nb] group-major: bucket (range r, group g) at g * NR + r
+    uint32_t* offsets;   // [nb] offset of each bucket inside its group
+    uint32_t* gtot;      // [ngroups] entries per group
+    uint32_t* gbase;     // [ngroups] first entry of each group
     uint2* entries;      // [walks * 2K] incidences grouped by bucket
     int4* items;         // [walks * 2K / kItemMax + ngroups]
     uint32_t* meta;      // [0] items, [1] entries
@@ -102,6 +105,8 @@ static Workspace carve(const pisa_dims* d, int64_t N, int64_t P, bool decode, ch
         w.sink = (float*)take((size_t)kClusterThreads * sizeof(float));
         w.counts = (uint32_t*)take((size_t)w.CG.nb * 4);
         w.offsets = (uint32_t*)take((size_t)w.CG.nb * 4);
+        w.gtot = (uint32_t*)take((size_t)w.CG.ngroups * 4);
+        w.gbase = (uint32_t*)take((size_t)w.CG.ngroups * 4);
         w.entries = (uint2*)take((size_t)walks * cs * sizeof(uint2));
         w.items = (int4*)take(((size_t)walks * cs / kItemMax + w.CG.ngroups + 1) * sizeof(int4));
         w.meta = (uint32_t*)take(16);
@@ -260,17 +265,20 @@ static int cluster_leaf_stage(const uint16_t* q, const uint16_t* k, const Geom& 
     const dim3 bgrid((unsigned)CG.NR, (unsigned)G.B);
     const size_t bins = (size_t)G.Hkv * CG.NSB * 4;
     for (int fill = 0; fill < 2; ++fill) {
-        if (fill)
-            hipLaunchKernelGGL(scan_groups_kernel, dim3(1), dim3(1024), 0, s, W.counts, CG, W.offsets, W.items, W.meta);
+        if (fill) {
+            hipLaunchKernelGGL(group_offsets_kernel, dim3((unsigned)((CG.ngroups + 3) / 4)), dim3(256), 0, s, W.counts,
+                               CG, W.offsets, W.gtot);
+            hipLaunchKernelGGL(scan_groups_kernel, dim3(1), dim3(1024), 0, s, W.gtot, CG, W.gbase, W.items, W.meta);
+        }
         if (slots <= 16)
             hipLaunchKernelGGL(bucket_pass_kernel<16>, bgrid, dim3(1024), bins, s, W.cand, W.ncand, G, CG, NT, W.counts,
-                               W.offsets, W.entries, fill);
+                               W.offsets, W.gbase, W.entries, fill);
         else if (slots <= 32)
             hipLaunchKernelGGL(bucket_pass_kernel<32>, bgrid, dim3(1024), bins, s, W.cand, W.ncand, G, CG, NT, W.counts,
-                               W.offsets, W.entries, fill);
+                               W.offsets, W.gbase, W.entries, fill);
         else
             hipLaunchKernelGGL(bucket_pass_kernel<64>, bgrid, dim3(1024), bins, s, W.cand, W.ncand, G, CG, NT, W.counts,
-                               W.offsets, W.entries, fill);
+                               W.offsets, W.gbase, W.entries, fill);
     }
     if (hipFuncSetAttribute((const void*)leaf_cluster_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                             kSbLdsBytes) != hipSuccess)

@@ -11,8 +11,10 @@
 //   1. bucket_pass (count): one incidence per sibling pair of a walk's leaf
 //      candidates inside a superblock, counted per bucket (batch, KV head,
 //      superblock, range of query positions) in an LDS histogram;
-//   2. scan_groups: bucket offsets and work items of at most kItemMax entries
-//      of one (batch, KV head, superblock) group;
+//   2. group_offsets: per (batch, KV head, superblock) group, one wavefront scans
+//      its ranges' counts (bucket offsets inside the group, group total);
+//      scan_groups: group offsets and work items of at most kItemMax entries of
+//      one group;
 //   3. bucket_pass (fill): incidences written as entries at their offsets;
 //   4. leaf_cluster: persistent workgroups take items from a counter; a workgroup stages the
 //      superblock's keys in LDS once, then each wavefront takes entries (the
@@ -37,12 +39,15 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p,
 // pass the same bins, seeded with the bucket offsets, hand out entry positions.
 // Entry = {query position t, leaf mask | first slot << 16}: the mask holds the superblock
 // offsets of one leaf or of a sibling pair (batch element and KV head are the bucket's).
+// Counts and offsets are group-major: bucket (range r, group g) at g * NR + r; the fill
+// pass starts bucket (r, g) at gbase[g] + offsets[g * NR + r].
 template <int SL>
 __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __restrict__ cand,
                                                           const int32_t* __restrict__ ncand, Geom G,
                                                           ClusterGeom CG, int64_t NT,
                                                           uint32_t* __restrict__ counts,
                                                           const uint32_t* __restrict__ offsets,
+                                                          const uint32_t* __restrict__ gbase,
                                                           uint2* __restrict__ entries, int fill) {
     extern __shared__ uint32_t bins[];
     constexpr int WPW = 64 / SL;
@@ -51,10 +56,10 @@ __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __rest
     const int K = G.topk, CS = 2 * G.topk;
     const int nbins = G.Hkv * CG.NSB;
     const int nthr = blockDim.x, nw = nthr >> 6;
-    // bucket (range r, group g = (b, kvh, sb)) lives at r * ngroups + g
+    // bin x = kvh * NSB + sb is group g = b * nbins + x
     for (int x = tid; x < nbins; x += nthr) {
-        const int64_t bkt = (int64_t)r * CG.ngroups + (int64_t)b * nbins + x;
-        bins[x] = fill ? offsets[bkt] : 0u;
+        const int64_t g = (int64_t)b * nbins + x;
+        bins[x] = fill ? gbase[g] + offsets[g * CG.NR + r] : 0u;
     }
     __syncthreads();
     const int64_t t_lo = (int64_t)r * kRangeT;
@@ -82,18 +87,44 @@ __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __rest
     }
     __syncthreads();
     if (!fill) {
-        for (int x = tid; x < nbins; x += nthr) counts[(int64_t)r * CG.ngroups + (int64_t)b * nbins + x] = bins[x];
+        for (int x = tid; x < nbins; x += nthr) counts[((int64_t)b * nbins + x) * CG.NR + r] = bins[x];
     }
 }
 
-// One workgroup: entry offsets of every bucket (groups (b, kvh, sb) in order, ranges
-// inside a group consecutive) and work items of at most kItemMax entries of one group.
-// Items holding kItemMax entries come first, the smaller remainders after them, so
-// that the workgroups taking items in order finish together.
-// meta[0] = number of items, meta[1] = number of entries, meta[2] = 0 (the counter the
-// scoring workgroups take items from).
-__global__ __launch_bounds__(1024) void scan_groups_kernel(const uint32_t* __restrict__ counts, ClusterGeom CG,
-                                                           uint32_t* __restrict__ offsets,
+// One wavefront per group g: the exclusive scan of its ranges' counts (the offset of
+// each bucket inside the group) and the group's total. Grid: ceil(ngroups / 4)
+// workgroups of 4 wavefronts.
+__global__ __launch_bounds__(256) void group_offsets_kernel(const uint32_t* __restrict__ counts, ClusterGeom CG,
+                                                            uint32_t* __restrict__ offsets,
+                                                            uint32_t* __restrict__ gtot) {
+    const int lane = threadIdx.x & 63;
+    const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (g >= CG.ngroups) return;   // whole wavefronts leave together
+    const uint32_t* c = counts + g * CG.NR;
+    uint32_t* o = offsets + g * CG.NR;
+    uint32_t run = 0;
+    for (int r0 = 0; r0 < CG.NR; r0 += 64) {
+        const int r = r0 + lane;
+        const uint32_t v = (r < CG.NR) ? c[r] : 0u;
+        uint32_t x = v;   // inclusive scan over the wavefront
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t y = (uint32_t)shfl_i((int)x, lane >= d ? lane - d : lane);
+            x += (lane >= d) ? y : 0u;
+        }
+        if (r < CG.NR) o[r] = run + x - v;
+        run += (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+    }
+    if (lane == 0) gtot[g] = run;
+}
+
+// One workgroup: the entry offset of every group (groups in order) and work items of at
+// most kItemMax entries of one group. Items holding kItemMax entries come first, the
+// smaller remainders after them, so that the workgroups taking items in order finish
+// together. meta[0] = number of items, meta[1] = number of entries, meta[2] = 0 (the
+// counter the scoring workgroups take items from).
+__global__ __launch_bounds__(1024) void scan_groups_kernel(const uint32_t* __restrict__ gtot, ClusterGeom CG,
+                                                           uint32_t* __restrict__ gbase,
                                                            int4* __restrict__ items,
                                                            uint32_t* __restrict__ meta) {
     __shared__ uint32_t s_e[1024], s_f[1024], s_p[1024];
@@ -102,8 +133,7 @@ __global__ __launch_bounds__(1024) void scan_groups_kernel(const uint32_t* __res
     const int lo = tid * per, hi = min(CG.ngroups, lo + per);
     uint32_t se = 0, sf = 0, sp = 0;
     for (int g = lo; g < hi; ++g) {
-        uint32_t tot = 0;
-        for (int r = 0; r < CG.NR; ++r) tot += counts[(int64_t)r * CG.ngroups + g];
+        const uint32_t tot = gtot[g];
         se += tot;
         sf += tot / kItemMax;              // full items
         sp += (tot % kItemMax) ? 1u : 0u;  // remainder item
@@ -125,12 +155,9 @@ __global__ __launch_bounds__(1024) void scan_groups_kernel(const uint32_t* __res
     const uint32_t nfull = s_f[1023];
     uint32_t eoff = s_e[tid] - se, foff = s_f[tid] - sf, poff = nfull + s_p[tid] - sp;
     for (int g = lo; g < hi; ++g) {
-        const uint32_t g0 = eoff;
-        for (int r = 0; r < CG.NR; ++r) {
-            offsets[(int64_t)r * CG.ngroups + g] = eoff;
-            eoff += counts[(int64_t)r * CG.ngroups + g];
-        }
-        const uint32_t tot = eoff - g0;
+        const uint32_t g0 = eoff, tot = gtot[g];
+        gbase[g] = g0;
+        eoff += tot;
         for (uint32_t p = 0; p * kItemMax < tot; ++p) {
             const uint32_t len = min((uint32_t)kItemMax, tot - p * kItemMax);
             items[(len == kItemMax) ? foff++ : poff++] = make_int4(g, (int)(g0 + p * kItemMax), (int)len, 0);
@@ -144,11 +171,11 @@ __global__ __launch_bounds__(1024) void scan_groups_kernel(const uint32_t* __res
 }
 
 template __global__ void bucket_pass_kernel<16>(const int32_t*, const int32_t*, Geom, ClusterGeom, int64_t,
-                                                uint32_t*, const uint32_t*, uint2*, int);
+                                                uint32_t*, const uint32_t*, const uint32_t*, uint2*, int);
 template __global__ void bucket_pass_kernel<32>(const int32_t*, const int32_t*, Geom, ClusterGeom, int64_t,
-                                                uint32_t*, const uint32_t*, uint2*, int);
+                                                uint32_t*, const uint32_t*, const uint32_t*, uint2*, int);
 template __global__ void bucket_pass_kernel<64>(const int32_t*, const int32_t*, Geom, ClusterGeom, int64_t,
-                                                uint32_t*, const uint32_t*, uint2*, int);
+                                                uint32_t*, const uint32_t*, const uint32_t*, uint2*, int);
 
 // LDS image of a superblock: key row r (0..1023) at r*128 bytes, its 16-byte chunk c
 // stored at chunk position c ^ (r & 7) so that the MFMA A-fragment reads of 8

@@ -67,7 +67,7 @@ struct UpperCfg {
 // kItemMax entries of one group.
 constexpr int kSbLeaves = 16;
 constexpr int kSbKeys = kSbLeaves * kC;           // 1024 keys
-constexpr int kRangeT = 2048;                      // query positions per range
+constexpr int kRangeT = 512;                       // query positions per range
 constexpr int kItemMax = 1024;                     // entries per work item
 constexpr int kClusterThreads = 1024;
 constexpr int kSbLdsBytes = kSbKeys * kD * 2;      // 128 KiB of bf16 keys
