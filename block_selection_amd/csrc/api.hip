@@ -169,7 +169,7 @@ static int build_impl(const KT* k, const Geom& G, float* pyr, hipStream_t s) {
     if (grid > INT_MAX) return PISA_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(build_subtree_kernel<KT>, dim3((unsigned)grid), dim3(256), 0, s, k, G, pyr);
     if (G.L > 5)
-        hipLaunchKernelGGL(build_upper_kernel, dim3((unsigned)(G.B * G.Hkv)), dim3(256), 0, s, G, pyr);
+        hipLaunchKernelGGL(build_upper_kernel, dim3((unsigned)(G.B * G.Hkv)), dim3(1024), 0, s, G, pyr);
     return launch_status();
 }
 

@@ -72,21 +72,41 @@ __global__ __launch_bounds__(256) void build_subtree_kernel(const KT* __restrict
     }
 }
 
-// Levels 6..L for one (batch, KV head): one workgroup, level by level through global memory.
-__global__ __launch_bounds__(256) void build_upper_kernel(Geom G, float* __restrict__ pyr) {
+// Levels 6..L for one (batch, KV head): one workgroup, level by level. A level of at
+// most kUpperLdsNodes nodes is also kept in LDS (two buffers, alternating), so the
+// dependent chain of small levels near the root reads its children from LDS instead of
+// memory. Same parent formula and operands either way.
+constexpr int kUpperLdsNodes = 128;   // 32 KiB of fp32 rows per buffer
+__global__ __launch_bounds__(1024) void build_upper_kernel(Geom G, float* __restrict__ pyr) {
+    __shared__ float s_lv[2][kUpperLdsNodes * kD];
     const int bh = blockIdx.x;
+    bool in_lds = false;   // level l - 1 is in s_lv[cur]
+    int cur = 0;
     for (int l = kSubLevels + 1; l <= G.L; ++l) {
         const int64_t n = G.M[l];
-        for (int64_t idx = threadIdx.x; idx < n * kD; idx += 256) {
+        const bool keep = n <= kUpperLdsNodes;   // then every level above fits as well
+        for (int64_t idx = threadIdx.x; idx < n * kD; idx += 1024) {
             const int64_t node = idx / kD;
             const int e = (int)(idx % kD);
             const float ca = (float)covered(l - 1, 2 * node, G.N);
             const float cb = (float)covered(l - 1, 2 * node + 1, G.N);
-            const float a = pyr_row(pyr, G, bh, l - 1, 2 * node)[e];
-            const float bv = (cb > 0.0f) ? pyr_row(pyr, G, bh, l - 1, 2 * node + 1)[e] : 0.0f;
-            pyr_row(pyr, G, bh, l, node)[e] = parent_mean(a, ca, bv, cb);
+            float a, bv;
+            if (in_lds) {
+                a = s_lv[cur][(2 * node) * kD + e];
+                bv = (cb > 0.0f) ? s_lv[cur][(2 * node + 1) * kD + e] : 0.0f;
+            } else {
+                a = pyr_row(pyr, G, bh, l - 1, 2 * node)[e];
+                bv = (cb > 0.0f) ? pyr_row(pyr, G, bh, l - 1, 2 * node + 1)[e] : 0.0f;
+            }
+            const float v = parent_mean(a, ca, bv, cb);
+            pyr_row(pyr, G, bh, l, node)[e] = v;
+            if (keep) s_lv[cur ^ 1][idx] = v;
         }
-        __syncthreads();
+        __syncthreads();   // level l complete (global and LDS) before level l + 1 reads it
+        if (keep) {
+            in_lds = true;
+            cur ^= 1;
+        }
     }
 }
 
