@@ -199,30 +199,49 @@ __device__ inline void leaf_logits(const lds_char_t* lds, int bit, const bf16x8 
 }
 
 // This lane's exp sums of the four (walk, leaf) combinations of a unit (see score_unit),
-// in row order r = (walk r >> 1, leaf r & 1).
+// in row order r = (walk r >> 1, leaf r & 1). The eight 16-key tiles (leaf j, tile tau)
+// run as a pipeline: the key fragments of the next tile are read from LDS while the
+// current one is multiplied and exponentiated (two fragment buffers, half the registers
+// of reading a whole leaf ahead). Per tile each walk's four terms are added as
+// (e0 + e1) + (e2 + e3), and the four tiles of a leaf as (t0 + t1) + (t2 + t3): the
+// balanced-tree order of leaf_exp_sum.
 template <bool kFull>
 __device__ inline void unit_exp_sums(const lds_char_t* lds, const int (&bits)[2], const int (&lim)[4],
                                      const bf16x8 qa0, const bf16x8 qa1, const bf16x8 qb0, const bf16x8 qb1,
                                      int n, int gq, float (&sum)[4]) {
+    u32x4 fa[2], fb[2];
+    auto read = [&](int st) {
+        const int r = bits[st >> 2] * kC + 16 * (st & 3) + n;
+        fa[st & 1] = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, gq));
+        fb[st & 1] = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, 4 + gq));
+    };
+    auto tile_sum = [&](const f32x4& c, int tau, int lm) -> float {
+        float e[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        f32x4 acca[4], accb[4];
-#pragma unroll
-        for (int tau = 0; tau < 4; ++tau) {
-            const int r = bits[j] * kC + 16 * tau + n;
-            const u32x4 a0 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, gq));
-            const u32x4 a1 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, 4 + gq));
-            f32x4 c = {0.f, 0.f, 0.f, 0.f};
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), qa0, c, 0, 0, 0);
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), qa1, c, 0, 0, 0);
-            acca[tau] = c;
-            f32x4 d = {0.f, 0.f, 0.f, 0.f};
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), qb0, d, 0, 0, 0);
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), qb1, d, 0, 0, 0);
-            accb[tau] = d;
+        for (int k = 0; k < 4; ++k) {
+            const float e2 = __builtin_amdgcn_exp2f(c[k] * kScale2);
+            e[k] = (kFull || 16 * tau + 4 * gq + k <= lm) ? e2 : 0.0f;
         }
-        sum[j] = leaf_exp_sum<kFull>(acca, lim[j], gq);
-        sum[2 + j] = leaf_exp_sum<kFull>(accb, lim[2 + j], gq);
+        return (e[0] + e[1]) + (e[2] + e[3]);
+    };
+    float ta[4], tb[4];
+    read(0);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+        const int j = st >> 2, tau = st & 3, b = st & 1;
+        if (st + 1 < 8) read(st + 1);
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[b]), qa0, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[b]), qa1, c, 0, 0, 0);
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[b]), qb0, d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[b]), qb1, d, 0, 0, 0);
+        ta[tau] = tile_sum(c, tau, lim[j]);
+        tb[tau] = tile_sum(d, tau, lim[2 + j]);
+        if (tau == 3) {
+            sum[j] = (ta[0] + ta[1]) + (ta[2] + ta[3]);
+            sum[2 + j] = (tb[0] + tb[1]) + (tb[2] + tb[3]);
+        }
     }
 }
 
