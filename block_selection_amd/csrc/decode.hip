@@ -148,8 +148,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
                 float d0[8], d1[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    d0[e] = vc0[e] - vp0[e];
-                    d1[e] = vc1[e] - vp1[e];
+                    d0[e] = 2.0f * (vc0[e] - vp0[e]);   // doubled delta, as in the prefill planes
+                    d1[e] = 2.0f * (vc1[e] - vp1[e]);
                 }
                 u32x4 h0, l0, h1, l1;
                 split8(d0, h0, l0);

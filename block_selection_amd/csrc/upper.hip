@@ -268,7 +268,8 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_f32_kernel(const flo
 // ragged node of a level (a partial right child) are read directly.
 
 // delta planes: row c of level l >= 2 holds hi/lo bf16 planes of
-// (s_{l-1}(2c) - s_l(c)) * log2(e)/8, rounded like the summary planes. Grid: (chunks, B*Hkv).
+// 2 (s_{l-1}(2c) - s_l(c)) * log2(e)/8 (the doubled delta), rounded like the summary
+// planes. Grid: (chunks, B*Hkv).
 __global__ __launch_bounds__(256) void delta_planes_kernel(const float* __restrict__ pyr,
                                                            uint16_t* __restrict__ dplanes, Geom G) {
     const int bh = blockIdx.y;
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(256) void delta_planes_kernel(const float* __restri
         while (r >= G.M[l]) { r -= G.M[l]; ++l; }
         const int64_t prow = G.off[l] + r, crow = G.off[l - 1] + 2 * r;
         uint32_t hi, lo;
-        split_scaled(base[crow * kD + e] - base[prow * kD + e], hi, lo);
+        split_scaled(2.0f * (base[crow * kD + e] - base[prow * kD + e]), hi, lo);
         const int64_t o = ((int64_t)bh * G.P + prow) * kD + e;
         dplanes[o] = (uint16_t)hi;
         dplanes[plane_stride + o] = (uint16_t)lo;

@@ -125,17 +125,19 @@ __device__ inline void pair_scores(const f32x4& acc, uint32_t rows_ok, int gq, i
 // node at the right edge of a level). Then LSE(L_a, L_b) = p + g(d) with
 // g(d) = log2(2^d + 2^-d), and the group-summed score is P(c) + sum_h g(d_h), where
 // P(c) = sum_h p_h is carried down the walk: P(a) = P + D, P(b) = P - D, D = sum_h d_h.
-// One summary row (delta) per candidate replaces the two children rows.
+// One summary row (delta) per candidate replaces the two children rows. The delta rows
+// are stored doubled (2 delta: exact, as is every step below), so a tile yields x = 2d.
 
-// log2(2^d + 2^-d) = |d| + log2(1 + 2^(-2|d|))
-__device__ inline float pair_lse_term(float d) {
-    const float a = fabsf(d);
-    return a + __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(-2.0f * a));
+// g(d) = log2(2^d + 2^-d) = |d| + log2(1 + 2^(-2|d|)), from x = 2d: the exponent -|x|
+// needs no multiply, and |d| = |x| / 2 folds into one fma.
+__device__ inline float pair_lse_term2(float x) {
+    return __builtin_fmaf(fabsf(x), 0.5f, __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(-fabsf(x))));
 }
 
-// Pair sums of a delta tile (column n = candidate n, its delta row): F = sum over the
-// group's heads of g(d), or of d alone when the candidate has no eligible right child
-// (bit n of rvm clear), and D = sum of d. Every lane of column n receives both.
+// Pair sums of a delta tile (column n = candidate n, its doubled delta row: acc = 2d):
+// F = sum over the group's heads of g(d), or of d alone when the candidate has no
+// eligible right child (bit n of rvm clear), and D = sum of d. Every lane of column n
+// receives both. Halving is exact, so D = (sum of 2d) / 2 has the bits of the sum of d.
 __device__ inline void delta_tile_sums(const f32x4& acc, uint32_t rvm, int n, int gq, int GQ, float& F, float& D) {
     float tv[4], dv[4];
     if ((rvm & 0xffffu) == 0xffffu && GQ == kMaxGroup) {
@@ -143,7 +145,7 @@ __device__ inline void delta_tile_sums(const f32x4& acc, uint32_t rvm, int n, in
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             dv[k] = acc[k];
-            tv[k] = pair_lse_term(acc[k]);
+            tv[k] = pair_lse_term2(acc[k]);
         }
     } else {
         const bool rv = (rvm >> n) & 1u;
@@ -151,10 +153,12 @@ __device__ inline void delta_tile_sums(const f32x4& acc, uint32_t rvm, int n, in
         for (int k = 0; k < 4; ++k) {
             const bool h = 4 * gq + k < GQ;
             dv[k] = h ? acc[k] : 0.0f;
-            tv[k] = h ? (rv ? pair_lse_term(acc[k]) : acc[k]) : 0.0f;
+            tv[k] = h ? (rv ? pair_lse_term2(acc[k]) : 0.5f * acc[k]) : 0.0f;
         }
     }
-    heads_total2(tv, dv, F, D);
+    float D2;
+    heads_total2(tv, dv, F, D2);
+    D = 0.5f * D2;
 }
 
 // The ragged node's children read directly: column 0 of the tile holds the left child's
