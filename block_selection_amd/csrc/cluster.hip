@@ -204,8 +204,9 @@ __device__ inline void leaf_logits(const lds_char_t* lds, int bit, const bf16x8 
 // current one is multiplied and exponentiated (two fragment buffers, half the registers
 // of reading a whole leaf ahead). Per tile each walk's four terms are added as
 // (e0 + e1) + (e2 + e3), and the four tiles of a leaf as (t0 + t1) + (t2 + t3): the
-// balanced-tree order of leaf_exp_sum.
-template <bool kFull>
+// balanced-tree order of leaf_exp_sum. Without a second walk (kTwo false) walk b's rows
+// repeat walk a's sums.
+template <bool kFull, bool kTwo>
 __device__ inline void unit_exp_sums(const lds_char_t* lds, const int (&bits)[2], const int (&lim)[4],
                                      const bf16x8 qa0, const bf16x8 qa1, const bf16x8 qb0, const bf16x8 qb1,
                                      int n, int gq, float (&sum)[4]) {
@@ -233,14 +234,16 @@ __device__ inline void unit_exp_sums(const lds_char_t* lds, const int (&bits)[2]
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
         c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[b]), qa0, c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[b]), qa1, c, 0, 0, 0);
-        f32x4 d = {0.f, 0.f, 0.f, 0.f};
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[b]), qb0, d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[b]), qb1, d, 0, 0, 0);
         ta[tau] = tile_sum(c, tau, lim[j]);
-        tb[tau] = tile_sum(d, tau, lim[2 + j]);
+        if (kTwo) {
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[b]), qb0, d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[b]), qb1, d, 0, 0, 0);
+            tb[tau] = tile_sum(d, tau, lim[2 + j]);
+        }
         if (tau == 3) {
             sum[j] = (ta[0] + ta[1]) + (ta[2] + ta[3]);
-            sum[2 + j] = (tb[0] + tb[1]) + (tb[2] + tb[3]);
+            sum[2 + j] = kTwo ? (tb[0] + tb[1]) + (tb[2] + tb[3]) : sum[j];
         }
     }
 }
@@ -251,10 +254,11 @@ __device__ inline void unit_exp_sums(const lds_char_t* lds, const int (&bits)[2]
 // (walk, leaf) sums are reduced in one vector; returns, in lanes of row group r,
 // the score of (walk r >> 1, leaf r & 1), bitwise what leaf_lse_from_acc gives for the
 // leaf alone. lim[] are per (walk, leaf) in that row order; an ineligible leaf (lim < 0)
-// is computed with one key and its score discarded by the caller.
+// is computed with one key and its score discarded by the caller. two = false: the unit has
+// walk a only (b repeats a), whose second copy is not computed.
 __device__ inline float score_unit(const lds_char_t* lds, const int (&bits)[2], const int (&lim_in)[4],
                                    const bf16x8 qa0, const bf16x8 qa1, const bf16x8 qb0, const bf16x8 qb1, int n,
-                                   int gq, int GQ) {
+                                   int gq, int GQ, bool two) {
     int lim[4];
     bool full = true;
 #pragma unroll
@@ -264,10 +268,14 @@ __device__ inline float score_unit(const lds_char_t* lds, const int (&bits)[2], 
     }
     // one branch per unit: a unit with no masked key (the common case) runs straight-line code
     float sum[4];
-    if (full)
-        unit_exp_sums<true>(lds, bits, lim, qa0, qa1, qb0, qb1, n, gq, sum);
+    if (full && two)
+        unit_exp_sums<true, true>(lds, bits, lim, qa0, qa1, qb0, qb1, n, gq, sum);
+    else if (full)
+        unit_exp_sums<true, false>(lds, bits, lim, qa0, qa1, qb0, qb1, n, gq, sum);
+    else if (two)
+        unit_exp_sums<false, true>(lds, bits, lim, qa0, qa1, qb0, qb1, n, gq, sum);
     else
-        unit_exp_sums<false>(lds, bits, lim, qa0, qa1, qb0, qb1, n, gq, sum);
+        unit_exp_sums<false, false>(lds, bits, lim, qa0, qa1, qb0, qb1, n, gq, sum);
     // column totals of the four sums in one vector: row r = (walk r >> 1, leaf r & 1)
     const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(sum[0]), __float_as_uint(sum[1]), false, false);
     const float Sa = __uint_as_float(x[0]) + __uint_as_float(x[1]);
@@ -412,7 +420,8 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
                 const int lim[4] = {min(ta - k0, kC - 1), min(ta - k0 - kC, kC - 1), min(tb - k0, kC - 1),
                                     min(tb - k0 - kC, kC - 1)};
                 v = score_unit(lds, bits, lim, __builtin_bit_cast(bf16x8, a0), __builtin_bit_cast(bf16x8, a1),
-                               __builtin_bit_cast(bf16x8, b0), __builtin_bit_cast(bf16x8, b1), n, gq, G.GQ);
+                               __builtin_bit_cast(bf16x8, b0), __builtin_bit_cast(bf16x8, b1), n, gq, G.GQ,
+                               mb != 0u);
             }
             float* dst = sink + wave * 64 + lane;
             if (lane == 0 && ma) dst = score + wa * CS + (ya >> 16);

@@ -75,7 +75,8 @@ def test_prefill_ragged_lengths(N):
 
 
 @pytest.mark.parametrize("Hq,Hkv,K,dtype", [(8, 1, 32, "bf16"), (16, 2, 1, "bf16"), (6, 3, 5, "f32"),
-                                             (16, 1, 16, "bf16"), (2, 2, 8, "f32")])
+                                             (16, 1, 16, "bf16"), (2, 2, 8, "f32"), (12, 3, 5, "bf16"),
+                                             (32, 2, 12, "bf16")])
 def test_prefill_shape_variants(Hq, Hkv, K, dtype):
     wl = synth.Workload("variant", N=8192, Hq=Hq, Hkv=Hkv, topk=K, dtype=dtype, seed=Hq * 100 + K)
     _prefill_case(wl, n_sample=1500)
