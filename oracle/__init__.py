@@ -48,20 +48,32 @@ def _load():
     lib.pisa_oracle_level_sizes.restype = i32
     lib.pisa_oracle_build_pyramid.argtypes = [P, i64, i32, i32, i32, i32, P, i32]
     lib.pisa_oracle_build_pyramid.restype = i32
-    lib.pisa_oracle_walk.argtypes = [P, P, i64, P, P, i64, i32, i32, i32, i32, i32, i32,
+    lib.pisa_oracle_walk.argtypes = [P, P, i64, P, P, i64, i32, i32, i32, i32, i32, i32, i32,
                                      P, P, P, i32]
     lib.pisa_oracle_walk.restype = i32
-    lib.pisa_oracle_walk_trace.argtypes = [P, i64, i32, P, P, i64, i32, i32, i32, i32, i32, i32,
+    lib.pisa_oracle_walk_trace.argtypes = [P, i64, i32, P, P, i64, i32, i32, i32, i32, i32, i32, i32,
                                            P, P, P, P, P, i32]
     lib.pisa_oracle_walk_trace.restype = i32
     lib.pisa_oracle_node_score.argtypes = [P, i64, i32, P, P, i64, i32, i32, i32, i32, i32,
-                                           i32, i64]
+                                           i32, i64, i32]
     lib.pisa_oracle_node_score.restype = dbl
-    lib.pisa_oracle_validate.argtypes = [P, i64, i32, P, P, i64, i32, i32, i32, i32, i32, i32,
+    lib.pisa_oracle_validate.argtypes = [P, i64, i32, P, P, i64, i32, i32, i32, i32, i32, i32, i32,
                                          P, dbl, lng]
     lib.pisa_oracle_validate.restype = i32
     _lib = lib
     return lib
+
+
+# Candidate scores (per head, over the eligible children's logits; summed over the group):
+# "lse" the LogSumExp, "mean" their mean, "mean_half_var" their mean plus half their
+# (population) variance -- the first- and second-order truncations of the LSE expansion.
+SCORES = {"lse": 0, "mean": 1, "mean_half_var": 2}
+
+
+def _score(score: str) -> int:
+    if score not in SCORES:
+        raise ValueError(f"score must be one of {sorted(SCORES)}")
+    return SCORES[score]
 
 
 def _p(a: np.ndarray):
@@ -103,7 +115,7 @@ def build_pyramid(k: np.ndarray, C: int = 64, g: int = 2, nthreads: int = 0) -> 
 
 
 def walk(q_rows: np.ndarray, t_rows, k: np.ndarray, pyr: np.ndarray, topk: int,
-         C: int = 64, g: int = 2, nthreads: int = 0):
+         C: int = 64, g: int = 2, nthreads: int = 0, score: str = "lse"):
     """Walks for the query rows of positions t_rows (one batch element).
 
     q_rows: float [n, Hq, d]; k: float [N, Hkv, d]; pyr from build_pyramid.
@@ -121,14 +133,14 @@ def walk(q_rows: np.ndarray, t_rows, k: np.ndarray, pyr: np.ndarray, topk: int,
     gap = np.zeros((n, Hkv), np.float64)
     lvl = np.zeros((n, Hkv), np.int32)
     rc = _load().pisa_oracle_walk(_p(q_rows), _p(t_rows), n, _p(k), _p(pyr), N, Hq, Hkv, d, C, g,
-                                  topk, _p(idx), _p(gap), _p(lvl), nthreads)
+                                  topk, _score(score), _p(idx), _p(gap), _p(lvl), nthreads)
     if rc != 0:
         raise RuntimeError(f"oracle walk failed ({rc})")
     return idx, gap, lvl
 
 
 def walk_trace(q_row: np.ndarray, t: int, j: int, k: np.ndarray, pyr: np.ndarray, topk: int,
-               C: int = 64, g: int = 2):
+               C: int = 64, g: int = 2, score: str = "lse"):
     """One walk with every candidate recorded.
 
     Returns (idx [topk], records) where records is a list of
@@ -145,7 +157,7 @@ def walk_trace(q_row: np.ndarray, t: int, j: int, k: np.ndarray, pyr: np.ndarray
     idx = np.zeros(topk, np.int32)
     pyr = np.ascontiguousarray(pyr, dtype=np.float64)
     n = _load().pisa_oracle_walk_trace(_p(q_row), t, j, _p(k), _p(pyr), N, Hq, Hkv, d, C, g, topk,
-                                       _p(idx), _p(lv), _p(nd), _p(sc), _p(kp), cap)
+                                       _score(score), _p(idx), _p(lv), _p(nd), _p(sc), _p(kp), cap)
     if n < 0:
         raise RuntimeError(f"oracle walk_trace failed ({n})")
     n = min(n, cap)
@@ -154,18 +166,19 @@ def walk_trace(q_row: np.ndarray, t: int, j: int, k: np.ndarray, pyr: np.ndarray
 
 
 def node_score(q_row: np.ndarray, t: int, j: int, k: np.ndarray, pyr: np.ndarray, level: int,
-               node: int, C: int = 64, g: int = 2) -> float:
-    """Score of one node (sum over the group's heads of the LSE over its eligible children)."""
+               node: int, C: int = 64, g: int = 2, score: str = "lse") -> float:
+    """Score of one node (sum over the group's heads of the score over its eligible children)."""
     q_row, k = _f32(q_row), _f32(k)
     Hq, d = q_row.shape
     N, Hkv, _ = k.shape
     pyr = np.ascontiguousarray(pyr, dtype=np.float64)
     return float(_load().pisa_oracle_node_score(_p(q_row), t, j, _p(k), _p(pyr), N, Hq, Hkv, d,
-                                                C, g, level, node))
+                                                C, g, level, node, _score(score)))
 
 
 def validate(q_row: np.ndarray, t: int, j: int, k: np.ndarray, pyr: np.ndarray, topk: int,
-             target, eps: float, budget: int = 200000, C: int = 64, g: int = 2) -> int:
+             target, eps: float, budget: int = 200000, C: int = 64, g: int = 2,
+             score: str = "lse") -> int:
     """1 if target is reachable by resolving near-ties within eps, 0 if not, -1 if undecided."""
     q_row, k = _f32(q_row), _f32(k)
     Hq, d = q_row.shape
@@ -174,14 +187,14 @@ def validate(q_row: np.ndarray, t: int, j: int, k: np.ndarray, pyr: np.ndarray, 
     assert tg.shape == (topk,)
     pyr = np.ascontiguousarray(pyr, dtype=np.float64)
     r = _load().pisa_oracle_validate(_p(q_row), t, j, _p(k), _p(pyr), N, Hq, Hkv, d, C, g, topk,
-                                     _p(tg), eps, budget)
+                                     _score(score), _p(tg), eps, budget)
     if r == -2:
         raise RuntimeError("oracle validate: bad arguments")
     return int(r)
 
 
 def decode_step(k_all: np.ndarray, n: int, q_new: np.ndarray, topk: int, C: int = 64, g: int = 2,
-                nthreads: int = 0):
+                nthreads: int = 0, score: str = "lse"):
     """Selection after appending key n: rebuild over keys 0..n and walk at t = n.
 
     k_all: float [>= n+1, Hkv, d]; q_new: float [Hq, d].
@@ -189,5 +202,5 @@ def decode_step(k_all: np.ndarray, n: int, q_new: np.ndarray, topk: int, C: int 
     """
     k = _f32(k_all[: n + 1])
     pyr = build_pyramid(k, C, g, nthreads)
-    idx, gap, _ = walk(q_new[None], np.array([n]), k, pyr, topk, C, g, nthreads)
+    idx, gap, _ = walk(q_new[None], np.array([n]), k, pyr, topk, C, g, nthreads, score)
     return pyr, idx[0], gap[0]

@@ -20,6 +20,11 @@
  *     the leaf level, which makes the leaf score the exact raw-key LSE).
  *   - same note, section 4.1: the query heads of one GQA group add their
  *     LSE scores into one block score and share the selection.
+ *   - same note, "Scoring: LogSumExp" (the Taylor expansion that follows
+ *     it): dropping log m from the expansion of the LSE of m logits around
+ *     their mean and truncating it gives the two ablation scores, the mean
+ *     of the logits (first order, "PISA-1") and the mean plus half their
+ *     variance (second order, "PISA-2"). The walk takes any of the three.
  *
  * Readings taken where the pages are silent (each listed in the design notes):
  *   logit = q.k / sqrt(d); level sizes M_{l+1} = ceil(M_l / g) up to one node;
@@ -28,7 +33,9 @@
  *   eligible children enter a parent's LSE (at the leaf level: raw keys > t are
  *   masked); the "at most K" rule counts eligible candidates; GQA head h maps
  *   to KV head h / (Hq/Hkv); ties rank the lower node index first; the output
- *   is the leaf set in ascending order, padded with -1.
+ *   is the leaf set in ascending order, padded with -1; the variance of the
+ *   second-order score is the population variance (1/m) of the m eligible
+ *   children's logits, the one the expansion produces.
  *
  * Arithmetic: every sum, dot product, exp and log is in double precision. The
  * inputs are float arrays holding exactly the values the GPU sees (bf16 values
@@ -45,9 +52,13 @@
 #define ORACLE_MAX_LEVELS 64
 #define ORACLE_MAX_TOPK 256
 
+/* candidate scores per head over the eligible children's logits z_1..z_m */
+enum { SCORE_LSE = 0, SCORE_MEAN = 1, SCORE_MEAN_HALF_VAR = 2 };
+
 typedef struct {
     int64_t N;      /* number of keys */
     int Hq, Hkv, d, C, g, topk;
+    int score;      /* SCORE_* */
     int L;          /* number of levels above the raw keys */
     int64_t M[ORACLE_MAX_LEVELS + 1];     /* M[l] nodes at level l (1..L) */
     int64_t span[ORACLE_MAX_LEVELS + 1];  /* raw keys covered by a full node at level l */
@@ -155,7 +166,8 @@ static void node_vec(const geom_t* G, const float* k, const double* pyr, int j, 
  * Score of candidate `node` at level l >= 1 for query row q (all Hq heads) at
  * position t, KV head j: the sum over the group's heads of the LogSumExp of
  * the scaled dot products with the node's eligible children (reading note,
- * "Scoring: LogSumExp" and section 4.1).
+ * "Scoring: LogSumExp" and section 4.1), or of their mean, or of their mean
+ * plus half their variance (the truncated expansions that follow it).
  */
 static double node_score(const geom_t* G, const float* q, const float* k, const double* pyr,
                          int64_t t, int j, int l, int64_t node, double* scratch) {
@@ -179,12 +191,22 @@ static double node_score(const geom_t* G, const float* q, const float* k, const 
             for (int e = 0; e < d; e++) dot += (double)qh[e] * v[e];
             z[nz++] = dot * inv_sqrt_d;
         }
-        /* log(sum exp(z)), evaluated around the maximum for range safety */
-        double m = -INFINITY;
-        for (int c = 0; c < nz; c++) if (z[c] > m) m = z[c];
-        double s = 0.0;
-        for (int c = 0; c < nz; c++) s += exp(z[c] - m);
-        S += m + log(s);
+        if (G->score == SCORE_LSE) {
+            /* log(sum exp(z)), evaluated around the maximum for range safety */
+            double m = -INFINITY;
+            for (int c = 0; c < nz; c++) if (z[c] > m) m = z[c];
+            double s = 0.0;
+            for (int c = 0; c < nz; c++) s += exp(z[c] - m);
+            S += m + log(s);
+        } else {
+            double mean = 0.0;
+            for (int c = 0; c < nz; c++) mean += z[c];
+            mean /= nz;
+            double var = 0.0;
+            for (int c = 0; c < nz; c++) var += (z[c] - mean) * (z[c] - mean);
+            var /= nz;
+            S += (G->score == SCORE_MEAN) ? mean : mean + 0.5 * var;
+        }
     }
     return S;
 }
@@ -285,11 +307,13 @@ static void walk_one(const geom_t* G, const float* q, const float* k, const doub
  */
 int pisa_oracle_walk(const float* q_rows, const int64_t* t_rows, int64_t n_rows,
                      const float* k, const double* pyr, int64_t N, int Hq, int Hkv, int d,
-                     int C, int g, int topk, int32_t* out_idx, double* min_gap,
+                     int C, int g, int topk, int score, int32_t* out_idx, double* min_gap,
                      int32_t* gap_level, int nthreads) {
     geom_t G;
     if (topk < 1 || topk > ORACLE_MAX_TOPK) return -1;
     if (make_geom(&G, N, Hq, Hkv, d, C, g, topk) != 0) return -1;
+    if (score < SCORE_LSE || score > SCORE_MEAN_HALF_VAR) return -1;
+    G.score = score;
     for (int64_t i = 0; i < n_rows; i++) if (t_rows[i] < 0 || t_rows[i] >= N) return -2;
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -314,12 +338,14 @@ int pisa_oracle_walk(const float* q_rows, const int64_t* t_rows, int64_t n_rows,
  * Returns the number of entries (may exceed cap; then only cap are written).
  */
 int pisa_oracle_walk_trace(const float* q_row, int64_t t, int j, const float* k, const double* pyr,
-                           int64_t N, int Hq, int Hkv, int d, int C, int g, int topk,
+                           int64_t N, int Hq, int Hkv, int d, int C, int g, int topk, int score_mode,
                            int32_t* out_idx, int32_t* lvl, int64_t* node, double* score,
                            int32_t* kept, int cap) {
     geom_t G;
     if (topk < 1 || topk > ORACLE_MAX_TOPK) return -1;
     if (make_geom(&G, N, Hq, Hkv, d, C, g, topk) != 0) return -1;
+    if (score_mode < SCORE_LSE || score_mode > SCORE_MEAN_HALF_VAR) return -1;
+    G.score = score_mode;
     if (t < 0 || t >= N || j < 0 || j >= Hkv) return -2;
     trace_t tr = {0, cap, lvl, node, score, kept};
     walk_one(&G, q_row, k, pyr, t, j, out_idx, NULL, NULL, &tr);
@@ -329,9 +355,11 @@ int pisa_oracle_walk_trace(const float* q_row, int64_t t, int j, const float* k,
 /* Exposes one node score (for the brute-force pins). */
 double pisa_oracle_node_score(const float* q_row, int64_t t, int j, const float* k,
                               const double* pyr, int64_t N, int Hq, int Hkv, int d, int C,
-                              int g, int l, int64_t node) {
+                              int g, int l, int64_t node, int score) {
     geom_t G;
     if (make_geom(&G, N, Hq, Hkv, d, C, g, 1) != 0) return NAN;
+    if (score < SCORE_LSE || score > SCORE_MEAN_HALF_VAR) return NAN;
+    G.score = score;
     if (l < 1 || l > G.L || node < 0 || node >= G.M[l]) return NAN;
     if (first_key(&G, l, node) > t) return NAN;
     double* scratch = (double*)malloc(sizeof(double) * (G.C + G.g + G.d + 8));
@@ -445,11 +473,13 @@ static int vwalk(vctx_t* V, int l, const int64_t* surv, int nsurv) {
  * ran out first.
  */
 int pisa_oracle_validate(const float* q_row, int64_t t, int j, const float* k, const double* pyr,
-                         int64_t N, int Hq, int Hkv, int d, int C, int g, int topk,
+                         int64_t N, int Hq, int Hkv, int d, int C, int g, int topk, int score,
                          const int32_t* target, double eps, long budget) {
     geom_t G;
     if (topk < 1 || topk > ORACLE_MAX_TOPK) return -2;
     if (make_geom(&G, N, Hq, Hkv, d, C, g, topk) != 0) return -2;
+    if (score < SCORE_LSE || score > SCORE_MEAN_HALF_VAR) return -2;
+    G.score = score;
     if (t < 0 || t >= N || j < 0 || j >= Hkv) return -2;
     int64_t tg[ORACLE_MAX_TOPK];
     int nt = 0;
