@@ -386,6 +386,17 @@ def main():
         "hbm": hbm,
         "work": work,
     }
+    if not args.no_extras:
+        # the pages' two ablation scores on the same workload and launch configuration
+        variants = {}
+        for sc in ("mean", "mean_half_var"):
+            dims_s = ops.make_dims(wl.B, wl.Hq, wl.Hkv, wl.topk, wl.dtype, score=sc)
+            tot_s, b_s, wk_s, up_s, lf_s = time_steps(N, dims_s, q, k, pyr, out, ws, 10, 3)
+            variants[sc] = {"ms_per_step": tot_s / 10, "queries_per_s": wl.B * N / (tot_s / 10 / 1e3),
+                            "upper_walk_ms": float(up_s.mean()), "leaf_scoring_ms": float(lf_s.mean())}
+            log(f"score {sc}: {tot_s / 10:.3f} ms/step (upper walk {up_s.mean():.3f} ms, "
+                f"leaf scoring {lf_s.mean():.3f} ms)")
+        result["score_variants"] = variants
     del q, k, pyr, out, ws
 
     if not args.no_extras:

@@ -16,12 +16,13 @@ __global__ void build_subtree_kernel(const KT*, Geom, float*);
 __global__ void build_upper_kernel(Geom, float*);
 template <typename KT>
 __global__ void decode_refresh_kernel(const KT*, KT*, Geom, float*);
+template <int S>
 __global__ void decode_step_kernel(const uint16_t*, const uint16_t*, uint16_t*, float*, Geom, uint32_t*, float*,
                                    int32_t*);
 __global__ void split_planes_kernel(const float*, uint16_t*, int64_t);
-template <int SLOTS>
+template <int SLOTS, int S>
 __global__ void walk_upper_f32_kernel(const float*, const float*, Geom, int64_t, int64_t, int32_t*, int32_t*);
-template <int SLOTS>
+template <int SLOTS, int S>
 __global__ void walk_upper_delta_kernel(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg, int64_t,
                                         int64_t, int32_t*, int32_t*);
 __global__ void delta_planes_kernel(const float*, uint16_t*, Geom);
@@ -35,8 +36,34 @@ __global__ void bucket_pass_kernel(const int32_t*, const int32_t*, Geom, Cluster
                                    const uint32_t*, const uint32_t*, uint2*, int);
 __global__ void group_offsets_kernel(const uint32_t*, ClusterGeom, uint32_t*, uint32_t*);
 __global__ void scan_groups_kernel(const uint32_t*, ClusterGeom, uint32_t*, int4*, uint32_t*);
+template <int S>
 __global__ void leaf_cluster_kernel(const uint16_t*, const uint16_t*, Geom, ClusterGeom, int64_t,
                                     const int4*, const uint2*, uint32_t*, float*, float*);
+
+// The kernels that score candidates are built once per candidate score (pisa_score);
+// these pick the build for G.score.
+template <int SLOTS>
+static const void* upper_delta_fn(int score) {
+    if (score == kScoreMean) return (const void*)walk_upper_delta_kernel<SLOTS, kScoreMean>;
+    if (score == kScoreMeanHalfVar) return (const void*)walk_upper_delta_kernel<SLOTS, kScoreMeanHalfVar>;
+    return (const void*)walk_upper_delta_kernel<SLOTS, kScoreLse>;
+}
+template <int SLOTS>
+static const void* upper_f32_fn(int score) {
+    if (score == kScoreMean) return (const void*)walk_upper_f32_kernel<SLOTS, kScoreMean>;
+    if (score == kScoreMeanHalfVar) return (const void*)walk_upper_f32_kernel<SLOTS, kScoreMeanHalfVar>;
+    return (const void*)walk_upper_f32_kernel<SLOTS, kScoreLse>;
+}
+static const void* leaf_cluster_fn(int score) {
+    if (score == kScoreMean) return (const void*)leaf_cluster_kernel<kScoreMean>;
+    if (score == kScoreMeanHalfVar) return (const void*)leaf_cluster_kernel<kScoreMeanHalfVar>;
+    return (const void*)leaf_cluster_kernel<kScoreLse>;
+}
+static const void* decode_step_fn(int score) {
+    if (score == kScoreMean) return (const void*)decode_step_kernel<kScoreMean>;
+    if (score == kScoreMeanHalfVar) return (const void*)decode_step_kernel<kScoreMeanHalfVar>;
+    return (const void*)decode_step_kernel<kScoreLse>;
+}
 template <int SLOTS>
 __global__ void final_topk_kernel(const int32_t*, const int32_t*, const float*, Geom, int64_t, int32_t*);
 
@@ -133,6 +160,7 @@ static int check_dims(const pisa_dims* d) {
     if (d->B < 1 || d->Hq < 1 || d->Hkv < 1 || d->topk < 1) return PISA_ERR_INVALID_ARG;
     if (d->Hq % d->Hkv != 0) return PISA_ERR_INVALID_ARG;
     if (d->dtype != PISA_DTYPE_F32 && d->dtype != PISA_DTYPE_BF16) return PISA_ERR_INVALID_ARG;
+    if (d->score < PISA_SCORE_LSE || d->score > PISA_SCORE_MEAN_HALF_VAR) return PISA_ERR_INVALID_ARG;
     if (d->d != kD || d->C != kC || d->g != 2) return PISA_ERR_UNSUPPORTED;
     if (d->Hq / d->Hkv > kMaxGroup || d->topk > kMaxTopK) return PISA_ERR_UNSUPPORTED;
     return PISA_OK;
@@ -155,6 +183,7 @@ static int make_geom(const pisa_dims* d, int64_t n, int64_t cap, Geom* G) {
     G->N = n;
     G->cap = cap;
     G->B = d->B; G->Hq = d->Hq; G->Hkv = d->Hkv; G->GQ = d->Hq / d->Hkv; G->topk = d->topk;
+    G->score = d->score;
     return PISA_OK;
 }
 
@@ -220,11 +249,15 @@ static int launch_upper_delta(const uint16_t* q, const Geom& G, const UpperCfg& 
     nwg = (nwg + 7) / 8 * 8;
     if (nwg < bh) nwg = bh;
     const size_t lds = (size_t)U.lds_nodes * kLdsNodeBytes;
-    const void* fn = (const void*)walk_upper_delta_kernel<SLOTS>;
+    const void* fn = upper_delta_fn<SLOTS>(G.score);
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return PISA_ERR_HIP;
-    hipLaunchKernelGGL((walk_upper_delta_kernel<SLOTS>), dim3((unsigned)nwg), dim3(kUpperThreads), lds, s, q,
-                       W.planes, W.dplanes, G, U, t0, NT, W.cand, W.ncand);
+    const uint16_t* planes = W.planes;
+    const uint16_t* dplanes = W.dplanes;
+    void* args[] = {(void*)&q, (void*)&planes, (void*)&dplanes, (void*)&G, (void*)&U, (void*)&t0, (void*)&NT,
+                    (void*)&W.cand, (void*)&W.ncand};
+    if (hipLaunchKernel(fn, dim3((unsigned)nwg), dim3(kUpperThreads), args, lds, s) != hipSuccess)
+        return PISA_ERR_HIP;
     return PISA_OK;
 }
 
@@ -239,8 +272,10 @@ static int launch_upper_f32(const float* q, const float* pyr, const Geom& G, int
     int64_t nwg = need < cus ? need : cus;
     nwg = (nwg + 7) / 8 * 8;
     if (nwg < bh) nwg = bh;
-    hipLaunchKernelGGL((walk_upper_f32_kernel<SLOTS>), dim3((unsigned)nwg), dim3(kUpperThreads), 0, s, q, pyr, G, t0,
-                       NT, W.cand, W.ncand);
+    void* args[] = {(void*)&q, (void*)&pyr, (void*)&G, (void*)&t0, (void*)&NT, (void*)&W.cand, (void*)&W.ncand};
+    if (hipLaunchKernel(upper_f32_fn<SLOTS>(G.score), dim3((unsigned)nwg), dim3(kUpperThreads), args, 0, s) !=
+        hipSuccess)
+        return PISA_ERR_HIP;
     return PISA_OK;
 }
 
@@ -280,12 +315,18 @@ static int cluster_leaf_stage(const uint16_t* q, const uint16_t* k, const Geom& 
             hipLaunchKernelGGL(bucket_pass_kernel<64>, bgrid, dim3(1024), bins, s, W.cand, W.ncand, G, CG, NT, W.counts,
                                W.offsets, W.gbase, W.entries, fill);
     }
-    if (hipFuncSetAttribute((const void*)leaf_cluster_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            kSbLdsBytes) != hipSuccess)
+    const void* leaf_fn = leaf_cluster_fn(G.score);
+    if (hipFuncSetAttribute(leaf_fn, hipFuncAttributeMaxDynamicSharedMemorySize, kSbLdsBytes) != hipSuccess)
         return PISA_ERR_HIP;
     mark(ev, 2, s);
-    hipLaunchKernelGGL(leaf_cluster_kernel, dim3((unsigned)cus), dim3(kClusterThreads), kSbLdsBytes, s, q, k, G,
-                       CG, NT, W.items, W.entries, W.meta, W.score, W.sink);
+    {
+        const int4* items = W.items;
+        const uint2* entries = W.entries;
+        void* args[] = {(void*)&q, (void*)&k, (void*)&G, (void*)&CG, (void*)&NT, (void*)&items, (void*)&entries,
+                        (void*)&W.meta, (void*)&W.score, (void*)&W.sink};
+        if (hipLaunchKernel(leaf_fn, dim3((unsigned)cus), dim3(kClusterThreads), args, kSbLdsBytes, s) != hipSuccess)
+            return PISA_ERR_HIP;
+    }
     mark(ev, 3, s);
     const int wpw = slots <= 16 ? 4 : (slots <= 32 ? 2 : 1);
     int64_t fgrid = ((walks + wpw - 1) / wpw + 3) / 4;
@@ -434,9 +475,14 @@ int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cach
         // append, refresh, walk and leaf top-K in one launch: ceil(2K/8) workgroups per
         // (batch, KV head), the last one to finish writes the selection
         const unsigned parts = (unsigned)((2 * dims->topk + 7) / 8);
-        hipLaunchKernelGGL(decode_step_kernel, dim3(parts, nbh), dim3(kDecodeThreads), 0, s,
-                           (const uint16_t*)q_new, (const uint16_t*)k_new, (uint16_t*)k_cache, pyramid, G, W.done,
-                           W.leaf_score, out_idx);
+        const uint16_t* qn = (const uint16_t*)q_new;
+        const uint16_t* kn = (const uint16_t*)k_new;
+        uint16_t* kc = (uint16_t*)k_cache;
+        void* args[] = {(void*)&qn, (void*)&kn, (void*)&kc, (void*)&pyramid, (void*)&G, (void*)&W.done,
+                        (void*)&W.leaf_score, (void*)&out_idx};
+        if (hipLaunchKernel(decode_step_fn(G.score), dim3(parts, nbh), dim3(kDecodeThreads), args, 0, s) !=
+            hipSuccess)
+            return PISA_ERR_HIP;
         return launch_status();
     }
     hipLaunchKernelGGL(decode_refresh_kernel<float>, dim3(nbh), dim3(64), 0, s,

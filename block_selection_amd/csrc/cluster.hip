@@ -306,6 +306,63 @@ __device__ inline float score_unit(const lds_char_t* lds, const int (&bits)[2], 
     return row16_sum((n < GQ) ? lse2 : 0.0f);
 }
 
+// Truncated scores of a unit (the layout and result convention of score_unit): the
+// moments of the four (walk, leaf) combinations, each key fragment read once for both
+// walks (walk b skipped when two is false), reduced over the row groups in one packed
+// exchange per moment (the order of cols4_sum), then mean (+ var/2) per head and the
+// group sum: the bits leaf_trunc_from_acc gives for each leaf alone.
+template <int S>
+__device__ inline float score_unit_trunc(const lds_char_t* lds, const int (&bits)[2], const int (&lim_in)[4],
+                                         const bf16x8 qa0, const bf16x8 qa1, const bf16x8 qb0, const bf16x8 qb1,
+                                         int n, int gq, int GQ, bool two) {
+    int lim[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lim[r] = max(lim_in[r], 0);
+    float s1[4], s2[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        f32x4 acca[4], accb[4];
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau) {
+            const int r = bits[j] * kC + 16 * tau + n;
+            const u32x4 a0 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, gq));
+            const u32x4 a1 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, 4 + gq));
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), qa0, c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), qa1, c, 0, 0, 0);
+            acca[tau] = c;
+            if (two) {
+                f32x4 d = {0.f, 0.f, 0.f, 0.f};
+                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), qb0, d, 0, 0, 0);
+                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), qb1, d, 0, 0, 0);
+                accb[tau] = d;
+            }
+        }
+        if (lim[j] == kC - 1) leaf_moments<true>(acca, lim[j], gq, s1[j], s2[j]);
+        else leaf_moments<false>(acca, lim[j], gq, s1[j], s2[j]);
+        if (two) {
+            if (lim[2 + j] == kC - 1) leaf_moments<true>(accb, lim[2 + j], gq, s1[2 + j], s2[2 + j]);
+            else leaf_moments<false>(accb, lim[2 + j], gq, s1[2 + j], s2[2 + j]);
+        } else {
+            s1[2 + j] = s1[j];
+            s2[2 + j] = s2[j];
+        }
+    }
+    // column totals of the four combinations: row group r = (walk r >> 1, leaf r & 1)
+    auto pack = [](const float (&v)[4]) -> float {
+        const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[0]), __float_as_uint(v[1]), false, false);
+        const float a = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+        const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[2]), __float_as_uint(v[3]), false, false);
+        const float b = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+        const auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        return __uint_as_float(z[0]) + __uint_as_float(z[1]);
+    };
+    const float T1 = pack(s1), T2 = pack(s2);
+    const int my_lim = (gq == 0) ? lim[0] : (gq == 1) ? lim[1] : (gq == 2) ? lim[2] : lim[3];
+    const float v = trunc_score2<S>(T1, T2, my_lim + 1);
+    return row16_sum((n < GQ) ? v : 0.0f);
+}
+
 // B fragments of one walk's queries: head n of the group, dims {8gq..8gq+7} and
 // {32+8gq..32+8gq+7}. Always loads (columns n >= GQ read head 0; their results are
 // excluded from the group sum), so the number of loads per entry is fixed.
@@ -316,6 +373,7 @@ __device__ inline void load_q(const uint16_t* __restrict__ q, int64_t bt, int Hq
     qb = *reinterpret_cast<const u32x4*>(qrow + 32 + 8 * gq);
 }
 
+template <int S>
 __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, Geom G, ClusterGeom CG, int64_t NT,
     const int4* __restrict__ items, const uint2* __restrict__ entries, uint32_t* __restrict__ meta,
@@ -419,9 +477,12 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
                 const int k0 = key_base + b0i * kC;
                 const int lim[4] = {min(ta - k0, kC - 1), min(ta - k0 - kC, kC - 1), min(tb - k0, kC - 1),
                                     min(tb - k0 - kC, kC - 1)};
-                v = score_unit(lds, bits, lim, __builtin_bit_cast(bf16x8, a0), __builtin_bit_cast(bf16x8, a1),
-                               __builtin_bit_cast(bf16x8, b0), __builtin_bit_cast(bf16x8, b1), n, gq, G.GQ,
-                               mb != 0u);
+                const bf16x8 fa0 = __builtin_bit_cast(bf16x8, a0), fa1 = __builtin_bit_cast(bf16x8, a1);
+                const bf16x8 fb0 = __builtin_bit_cast(bf16x8, b0), fb1 = __builtin_bit_cast(bf16x8, b1);
+                if constexpr (S == kScoreLse)
+                    v = score_unit(lds, bits, lim, fa0, fa1, fb0, fb1, n, gq, G.GQ, mb != 0u);
+                else
+                    v = score_unit_trunc<S>(lds, bits, lim, fa0, fa1, fb0, fb1, n, gq, G.GQ, mb != 0u);
             }
             float* dst = sink + wave * 64 + lane;
             if (lane == 0 && ma) dst = score + wa * CS + (ya >> 16);
@@ -440,6 +501,14 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
         }
     }
 }
+
+#define PISA_LEAF_CLUSTER_INST(S)                                                                         \
+    template __global__ void leaf_cluster_kernel<S>(const uint16_t*, const uint16_t*, Geom, ClusterGeom, int64_t, \
+                                                    const int4*, const uint2*, uint32_t*, float*, float*);
+PISA_LEAF_CLUSTER_INST(kScoreLse)
+PISA_LEAF_CLUSTER_INST(kScoreMean)
+PISA_LEAF_CLUSTER_INST(kScoreMeanHalfVar)
+#undef PISA_LEAF_CLUSTER_INST
 
 // Per walk (SLOTS lanes each): at most K candidates are all kept; otherwise the K best
 // by (score desc, index asc). Written in ascending leaf order, -1 padded.

@@ -30,7 +30,7 @@
 namespace pisa {
 
 // Leaf scores of NL leaves from raw bf16 keys in global memory (keys > t masked).
-template <int NL>
+template <int NL, int S>
 __device__ inline void score_leaves_global(const uint16_t* __restrict__ kbase, int64_t row_stride,
                                            const int (&leaf)[NL], int64_t t, const bf16x8 q0, const bf16x8 q1,
                                            int n, int gq, int GQ, float out[NL]) {
@@ -56,9 +56,10 @@ __device__ inline void score_leaves_global(const uint16_t* __restrict__ kbase, i
         const int64_t l64 = t - (int64_t)leaf[j] * kC;
         lim[j] = (l64 < kC - 1) ? (int)l64 : kC - 1;
     }
-    leaf_lse_from_acc<NL>(acc, lim, n, gq, GQ, out);
+    leaf_scores_from_acc<NL, S>(acc, lim, n, gq, GQ, out);
 }
 
+template <int S>
 __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint16_t* __restrict__ q_new,
                                                                      const uint16_t* __restrict__ k_new,
                                                                      uint16_t* __restrict__ k_cache,
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
                 split8(d1, h1, l1);
                 const f32x4 acc = summary_tile_mfma(q0, q1, h0, h1, l0, l1);
                 float F, D;
-                delta_tile_sums(acc, rvm, n, gq, G.GQ, F, D);
+                delta_tile_sums<S>(acc, rvm, n, gq, G.GQ, F, D);
                 if (gq == 0) {
                     s_F[buf][16 * wave + n] = F;
                     s_D[buf][16 * wave + n] = D;
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
                     split8(v1, h1, l1);
                     const f32x4 acc = summary_tile_mfma(q0, q1, h0, h1, l0, l1);   // column 0: left, 1: right
                     float xf, xp;
-                    ragged_sums(acc, gq, G.GQ, xf, xp);
+                    ragged_sums<S>(acc, gq, G.GQ, xf, xp);
                     if (lane == 0) {
                         s_fix[buf][0] = xf;
                         s_fix[buf][1] = xp;
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
         if (f >= 0) {
             const int fl[1] = {f};
             float o[1];
-            score_leaves_global<1>(kbase, row_stride, fl, t, q0, q1, n, gq, G.GQ, o);
+            score_leaves_global<1, S>(kbase, row_stride, fl, t, q0, q1, n, gq, G.GQ, o);
             if (lane == 0) leaf_score[(int64_t)bh * 64 + slot] = o[0];
         }
         __threadfence();   // scores visible device-wide before this workgroup counts itself done
@@ -258,5 +259,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
         if (scored && lane == 0) done[bh] = 0u;   // ready for the next step
     }
 }
+
+#define PISA_DECODE_INST(S)                                                                              \
+    template __global__ void decode_step_kernel<S>(const uint16_t*, const uint16_t*, uint16_t*, float*, Geom, \
+                                                   uint32_t*, float*, int32_t*);
+PISA_DECODE_INST(kScoreLse)
+PISA_DECODE_INST(kScoreMean)
+PISA_DECODE_INST(kScoreMeanHalfVar)
+#undef PISA_DECODE_INST
 
 }  // namespace pisa

@@ -129,6 +129,30 @@ __device__ inline float score_leaf(const KT* kbase, int64_t row_stride, const Ge
     }
     // lane holds keys key0 + 16*tau + 4*gq + r for head n
     const float c2 = 0.125f * kLog2e;
+    if (G.score != kScoreLse) {
+        // truncated scores: moments of the base-2 logits of the keys <= t, then mean
+        // (+ var/2), in natural units like the LSE below
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t key = key0 + 16 * tau + 4 * gq + r;
+                const float v = (key <= t) ? acc[tau][r] * c2 : 0.0f;
+                s1 += v;
+                s2 += v * v;
+            }
+        s1 += xor_f(s1, 16);
+        s1 += xor_f(s1, 32);
+        s2 += xor_f(s2, 16);
+        s2 += xor_f(s2, 32);
+        const int64_t m64 = t - key0 + 1;
+        const float m = (float)((m64 < kC) ? m64 : kC);
+        const float mean = s1 / m;
+        const float var = s2 / m - mean * mean;
+        const float sc = (G.score == kScoreMean) ? mean : mean + 0.5f * kLn2 * var;
+        return group_sum(sc * kLn2, n, G.GQ);
+    }
     float z[16];
     float mx = -INFINITY;
 #pragma unroll

@@ -28,7 +28,9 @@ struct Geom {
     int32_t M[kMaxLevels + 1];    // nodes at level l for N keys
     int32_t L;                    // root level for N keys
     int32_t B, Hq, Hkv, GQ, topk;
+    int32_t score;                // candidate score: kScoreLse, kScoreMean or kScoreMeanHalfVar
 };
+constexpr int kScoreLse = 0, kScoreMean = 1, kScoreMeanHalfVar = 2;   // the values of pisa_score
 
 // Raw keys covered by a full node of level l (l = 0: one key).
 __host__ __device__ inline int64_t span_of(int l) { return l == 0 ? 1 : (int64_t)kC << (l - 1); }

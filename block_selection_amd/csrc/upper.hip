@@ -133,7 +133,7 @@ struct TileLanes {
 // head, scoring each candidate from its two children rows of the fp32 pyramid on
 // v_mfma_f32_16x16x4_f32. Output per walk (index (b*NT + ti)*Hkv + kvh): cand_out[2K]
 // ascending leaf candidates (-1 padded) and ncand_out = their count.
-template <int SLOTS>
+template <int SLOTS, int S>
 __global__ __launch_bounds__(kUpperThreads) void walk_upper_f32_kernel(const float* __restrict__ q,
                                                              const float* __restrict__ pyr, Geom G, int64_t t0,
                                                              int64_t NT, int32_t* __restrict__ cand_out,
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_f32_kernel(const flo
                         const uint32_t rows_ok = (uint32_t)ballot(valid);   // bit r: row r valid
                         const f32x4 acc = child_tile_f32(qf[w], pyr_lvl + (int64_t)row * kD, gq);
                         float sc[2];
-                        pair_scores(acc, rows_ok, gq, n, G.GQ, sc);
+                        pair_scores<S>(acc, rows_ok, gq, n, G.GQ, sc);
                         if (wl == w && (ql >> 1) == tau) my = (ql & 1) ? sc[1] : sc[0];
                     }
                 }
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(256) void delta_planes_kernel(const float* __restri
 template <int SLOTS>
 __device__ constexpr int dslot_lane(int w, int m) { return w * SLOTS + m; }
 
-template <int SLOTS>
+template <int SLOTS, int S>
 __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const uint16_t* __restrict__ q,
                                                                          const uint16_t* __restrict__ splanes,
                                                                          const uint16_t* __restrict__ dplanes,
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const u
                     }
                     const f32x4 acc = summary_tile_mfma(qf[i / TPW].k0, qf[i / TPW].k1, cur.h0, cur.h1, cur.l0, cur.l1);
                     float Ft, Dt;
-                    delta_tile_sums(acc, rvm, n, gq, G.GQ, Ft, Dt);
+                    delta_tile_sums<S>(acc, rvm, n, gq, G.GQ, Ft, Dt);
                     if (u == i) {
                         F = Ft;
                         D = Dt;
@@ -483,7 +483,7 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const u
                             const TileRows r = rows_global(splanes + (bh_row0 + G.off[lc] + crow) * kD, plane_stride, gq);
                             const f32x4 acc = summary_tile_mfma(qf[w].k0, qf[w].k1, r.h0, r.h1, r.l0, r.l1);
                             float xf, xp;
-                            ragged_sums(acc, gq, G.GQ, xf, xp);
+                            ragged_sums<S>(acc, gq, G.GQ, xf, xp);
                             const float f_fix = readlane_f(xf, 0), pa_fix = readlane_f(xp, 0), pb_fix = readlane_f(xp, 1);
                             if (is_rag && wl == w) {
                                 score = f_fix;
@@ -528,18 +528,23 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const u
     }
 }
 
-template __global__ void walk_upper_delta_kernel<16>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg,
-                                                     int64_t, int64_t, int32_t*, int32_t*);
-template __global__ void walk_upper_delta_kernel<32>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg,
-                                                     int64_t, int64_t, int32_t*, int32_t*);
-template __global__ void walk_upper_delta_kernel<64>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg,
-                                                     int64_t, int64_t, int32_t*, int32_t*);
-
-template __global__ void walk_upper_f32_kernel<16>(const float*, const float*, Geom, int64_t, int64_t, int32_t*,
-                                                   int32_t*);
-template __global__ void walk_upper_f32_kernel<32>(const float*, const float*, Geom, int64_t, int64_t, int32_t*,
-                                                   int32_t*);
-template __global__ void walk_upper_f32_kernel<64>(const float*, const float*, Geom, int64_t, int64_t, int32_t*,
-                                                   int32_t*);
+template __global__ void walk_upper_delta_kernel<16, kScoreLse>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg, int64_t, int64_t, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_kernel<16, kScoreMean>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg, int64_t, int64_t, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_kernel<16, kScoreMeanHalfVar>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg, int64_t, int64_t, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_kernel<32, kScoreLse>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg, int64_t, int64_t, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_kernel<32, kScoreMean>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg, int64_t, int64_t, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_kernel<32, kScoreMeanHalfVar>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg, int64_t, int64_t, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_kernel<64, kScoreLse>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg, int64_t, int64_t, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_kernel<64, kScoreMean>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg, int64_t, int64_t, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_kernel<64, kScoreMeanHalfVar>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg, int64_t, int64_t, int32_t*, int32_t*);
+template __global__ void walk_upper_f32_kernel<16, kScoreLse>(const float*, const float*, Geom, int64_t, int64_t, int32_t*, int32_t*);
+template __global__ void walk_upper_f32_kernel<16, kScoreMean>(const float*, const float*, Geom, int64_t, int64_t, int32_t*, int32_t*);
+template __global__ void walk_upper_f32_kernel<16, kScoreMeanHalfVar>(const float*, const float*, Geom, int64_t, int64_t, int32_t*, int32_t*);
+template __global__ void walk_upper_f32_kernel<32, kScoreLse>(const float*, const float*, Geom, int64_t, int64_t, int32_t*, int32_t*);
+template __global__ void walk_upper_f32_kernel<32, kScoreMean>(const float*, const float*, Geom, int64_t, int64_t, int32_t*, int32_t*);
+template __global__ void walk_upper_f32_kernel<32, kScoreMeanHalfVar>(const float*, const float*, Geom, int64_t, int64_t, int32_t*, int32_t*);
+template __global__ void walk_upper_f32_kernel<64, kScoreLse>(const float*, const float*, Geom, int64_t, int64_t, int32_t*, int32_t*);
+template __global__ void walk_upper_f32_kernel<64, kScoreMean>(const float*, const float*, Geom, int64_t, int64_t, int32_t*, int32_t*);
+template __global__ void walk_upper_f32_kernel<64, kScoreMeanHalfVar>(const float*, const float*, Geom, int64_t, int64_t, int32_t*, int32_t*);
 
 }  // namespace pisa

@@ -18,6 +18,12 @@ namespace pisa {
 
 constexpr float kScale2 = 0.125f * 1.4426950408889634f;   // log2(e) / sqrt(64)
 
+// Truncated scores (the pages' ablations of the LSE): per head, mean(z) or
+// mean(z) + var(z)/2 over the candidate's m eligible child logits z (population
+// variance). Scores are kept in base-2 units x = z log2(e), i.e. log2(e) times the
+// natural score (the order is the same): mean(x) + var(x) ln(2) / 2.
+constexpr float kHalfVar2 = 0.5f * 0.6931471805599453f;    // ln(2) / 2
+
 __device__ inline uint32_t rne_bf16_bits(float x) {
     const uint32_t u = __float_as_uint(x);
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
@@ -95,23 +101,36 @@ __device__ inline float log2_add_exp2(float a, float b) {
     return m + __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(d));
 }
 
+// Base-2 score of one head over two child logits a and b: LSE, mean, or mean plus half
+// the variance. The score S (kScore*) is a compile-time parameter throughout, so each
+// kernel is built once per score and the LSE kernels carry no code of the others.
+template <int S>
+__device__ inline float combine2(float a, float b) {
+    if constexpr (S == kScoreLse) return log2_add_exp2(a, b);
+    const float mean = 0.5f * (a + b);
+    if constexpr (S == kScoreMean) return mean;
+    const float h = 0.5f * (a - b);                    // var of two values = ((a - b) / 2)^2
+    return __builtin_fmaf(h * h, kHalfVar2, mean);
+}
+
 // Scores of the two candidates whose children fill rows 4gq..4gq+3 of a child tile
 // (candidate p: left child row 4gq+2p, right child row 4gq+2p+1). rows_ok bit r says
 // row r is an eligible child; a candidate without an eligible left child scores -inf,
 // one without an eligible right child takes its left child's logit alone. Every lane of
 // row group gq receives both sums over the group's heads (columns n < GQ).
+template <int S>
 __device__ inline void pair_scores(const f32x4& acc, uint32_t rows_ok, int gq, int n, int GQ, float sc[2]) {
     if ((rows_ok & 0xffffu) == 0xffffu && GQ == kMaxGroup) {
         // every child eligible and every column a head of the group: no masks (same result)
 #pragma unroll
-        for (int p = 0; p < 2; ++p) sc[p] = row16_sum(log2_add_exp2(acc[2 * p], acc[2 * p + 1]));
+        for (int p = 0; p < 2; ++p) sc[p] = row16_sum(combine2<S>(acc[2 * p], acc[2 * p + 1]));
         return;
     }
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
         const bool lv = (rows_ok >> (4 * gq + 2 * p)) & 1u;
         const bool rv = (rows_ok >> (4 * gq + 2 * p + 1)) & 1u;
-        const float lse2 = rv ? log2_add_exp2(acc[2 * p], acc[2 * p + 1]) : acc[2 * p];
+        const float lse2 = rv ? combine2<S>(acc[2 * p], acc[2 * p + 1]) : acc[2 * p];
         const float sm = row16_sum(n < GQ ? lse2 : 0.0f);
         sc[p] = lv ? sm : -INFINITY;
     }
@@ -133,11 +152,21 @@ __device__ inline void pair_scores(const f32x4& acc, uint32_t rows_ok, int gq, i
 __device__ inline float pair_lse_term2(float x) {
     return __builtin_fmaf(fabsf(x), 0.5f, __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(-fabsf(x))));
 }
+// The same pair term for each score, from x = 2d: the children's logits p +- d have mean
+// p (the term is 0: the score is the carried P) and variance d^2 = x^2 / 4.
+template <int S>
+__device__ inline float pair_term2(float x) {
+    if constexpr (S == kScoreLse) return pair_lse_term2(x);
+    if constexpr (S == kScoreMean) return 0.0f;
+    return (x * x) * (0.25f * kHalfVar2);
+}
 
 // Pair sums of a delta tile (column n = candidate n, its doubled delta row: acc = 2d):
-// F = sum over the group's heads of g(d), or of d alone when the candidate has no
-// eligible right child (bit n of rvm clear), and D = sum of d. Every lane of column n
-// receives both. Halving is exact, so D = (sum of 2d) / 2 has the bits of the sum of d.
+// F = sum over the group's heads of the pair term (g(d) for the LSE), or of d alone when
+// the candidate has no eligible right child (bit n of rvm clear: one child, whose logit
+// is p + d for every score), and D = sum of d. Every lane of column n receives both.
+// Halving is exact, so D = (sum of 2d) / 2 has the bits of the sum of d.
+template <int S>
 __device__ inline void delta_tile_sums(const f32x4& acc, uint32_t rvm, int n, int gq, int GQ, float& F, float& D) {
     float tv[4], dv[4];
     if ((rvm & 0xffffu) == 0xffffu && GQ == kMaxGroup) {
@@ -145,7 +174,7 @@ __device__ inline void delta_tile_sums(const f32x4& acc, uint32_t rvm, int n, in
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             dv[k] = acc[k];
-            tv[k] = pair_lse_term2(acc[k]);
+            tv[k] = pair_term2<S>(acc[k]);
         }
     } else {
         const bool rv = (rvm >> n) & 1u;
@@ -153,7 +182,7 @@ __device__ inline void delta_tile_sums(const f32x4& acc, uint32_t rvm, int n, in
         for (int k = 0; k < 4; ++k) {
             const bool h = 4 * gq + k < GQ;
             dv[k] = h ? acc[k] : 0.0f;
-            tv[k] = h ? (rv ? pair_lse_term2(acc[k]) : 0.5f * acc[k]) : 0.0f;
+            tv[k] = h ? (rv ? pair_term2<S>(acc[k]) : 0.5f * acc[k]) : 0.0f;
         }
     }
     float D2;
@@ -163,15 +192,16 @@ __device__ inline void delta_tile_sums(const f32x4& acc, uint32_t rvm, int n, in
 
 // The ragged node's children read directly: column 0 of the tile holds the left child's
 // logits, column 1 the right child's. F (read in column 0) = sum over the group's heads
-// of log2(2^L + 2^R); Pc (column c) = the head sum of child c's logits. Call with every
-// lane active (a lane exchange).
+// of the score of the two (log2(2^L + 2^R) for the LSE); Pc (column c) = the head sum of
+// child c's logits. Call with every lane active (a lane exchange).
+template <int S>
 __device__ inline void ragged_sums(const f32x4& acc, int gq, int GQ, float& F, float& Pc) {
     float fv[4], pv[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const float r = lane_xor_f<1>(acc[k]);   // column 1 into column 0
         const bool h = 4 * gq + k < GQ;
-        fv[k] = h ? log2_add_exp2(acc[k], r) : 0.0f;
+        fv[k] = h ? combine2<S>(acc[k], r) : 0.0f;
         pv[k] = h ? acc[k] : 0.0f;
     }
     heads_total2(fv, pv, F, Pc);
@@ -221,6 +251,41 @@ __device__ inline float leaf_lane_max(const f32x4 (&acc)[4], int lim, int gq) {
     return m;
 }
 
+// This lane's first and second moments over its 16 keys of one leaf: s1 = sum of x,
+// s2 = sum of x^2 for the base-2 logits x = logit * kScale2 of the keys up to lim
+// (kFull: all), in the balanced-tree order of leaf_exp_sum.
+template <bool kFull>
+__device__ inline void leaf_moments(const f32x4 (&acc)[4], int lim, int gq, float& s1, float& s2) {
+#pragma clang fp contract(off)   // the same roundings wherever this is inlined
+    float a[16], b[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int tau = i >> 2, r = i & 3;
+        const float x = acc[tau][r] * kScale2;
+        const bool in = kFull || 16 * tau + 4 * gq + r <= lim;
+        a[i] = in ? x : 0.0f;
+        b[i] = in ? x * x : 0.0f;
+    }
+#pragma unroll
+    for (int w = 1; w < 16; w <<= 1)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2 * w) {
+            a[i] = a[i] + a[i + w];
+            b[i] = b[i] + b[i + w];
+        }
+    s1 = a[0];
+    s2 = b[0];
+}
+
+// Truncated score of one head over m keys from the moment totals (base-2 units).
+template <int S>
+__device__ inline float trunc_score2(float S1, float S2, int m) {
+    const float inv = 1.0f / (float)m;
+    const float mean = S1 * inv;
+    if constexpr (S == kScoreMean) return mean;
+    return __builtin_fmaf(__builtin_fmaf(S2, inv, -mean * mean), kHalfVar2, mean);
+}
+
 // Leaf scores from the MFMA results of NL leaves: acc[j][tau] holds, in lane (gq, n),
 // the natural-scale logits of keys 16*tau + 4*gq + r (r = 0..3) of leaf j for head n.
 // Keys with offset > lim[j] are masked. Per head the base-2 LSE is taken without a max
@@ -253,6 +318,30 @@ __device__ inline void leaf_lse_from_acc(const f32x4 (&acc)[NL][4], const int (&
         const float lse2 = shift[j] + __builtin_amdgcn_logf(s[j]);
         out[j] = row16_sum((n < GQ) ? lse2 : 0.0f);
     }
+}
+
+// The truncated scores of NL leaves from the same MFMA results (keys up to lim[j]):
+// per head the moment totals over the leaf's lim[j] + 1 keys, then mean (+ var/2),
+// summed over the group's heads.
+template <int NL, int S>
+__device__ inline void leaf_trunc_from_acc(const f32x4 (&acc)[NL][4], const int (&lim)[NL], int n, int gq, int GQ,
+                                           float out[NL]) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        float s1, s2;
+        if (lim[j] == kC - 1) leaf_moments<true>(acc[j], lim[j], gq, s1, s2);
+        else leaf_moments<false>(acc[j], lim[j], gq, s1, s2);
+        const float v = trunc_score2<S>(cols4_sum(s1), cols4_sum(s2), lim[j] + 1);
+        out[j] = row16_sum((n < GQ) ? v : 0.0f);
+    }
+}
+
+// Leaf scores for any score: the LSE or a truncation.
+template <int NL, int S>
+__device__ inline void leaf_scores_from_acc(const f32x4 (&acc)[NL][4], const int (&lim)[NL], int n, int gq,
+                                            int GQ, float out[NL]) {
+    if constexpr (S == kScoreLse) leaf_lse_from_acc<NL>(acc, lim, n, gq, GQ, out);
+    else leaf_trunc_from_acc<NL, S>(acc, lim, n, gq, GQ, out);
 }
 
 }  // namespace pisa

@@ -35,7 +35,7 @@ class Dims(ctypes.Structure):
     """Mirror of pisa_dims."""
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("C", ctypes.c_int32), ("g", ctypes.c_int32),
-                ("topk", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("topk", ctypes.c_int32), ("dtype", ctypes.c_int32), ("score", ctypes.c_int32)]
 
     @property
     def torch_dtype(self):
@@ -82,10 +82,14 @@ def status_string(status: int) -> str:
     return lib.pisa_status_string(status).decode()
 
 
+# candidate scores (pisa_score): the LogSumExp of the method and its two truncations
+SCORES = {"lse": 0, "mean": 1, "mean_half_var": 2}
+
+
 def make_dims(B: int, Hq: int, Hkv: int, topk: int, dtype: str = "bf16", d: int = 64, C: int = 64,
-              g: int = 2) -> Dims:
+              g: int = 2, score: str = "lse") -> Dims:
     dt = {"bf16": PISA_DTYPE_BF16, "f32": PISA_DTYPE_F32}[dtype]
-    return Dims(B, Hq, Hkv, d, C, g, topk, dt)
+    return Dims(B, Hq, Hkv, d, C, g, topk, dt, SCORES[score])
 
 
 def pyramid_nodes(dims: Dims, n_capacity: int) -> int:

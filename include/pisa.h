@@ -62,6 +62,19 @@ typedef enum {
 
 typedef enum { PISA_DTYPE_F32 = 0, PISA_DTYPE_BF16 = 1 } pisa_dtype;
 
+/* Candidate score, per query head over the candidate's eligible children's
+ * logits z_1..z_m (child summaries; raw keys at the leaf level), summed over
+ * the GQA group. Reading note "Block Sparse Attention with Log-Linear
+ * Complexity", "Scoring: LogSumExp": the method's score is the LogSumExp;
+ * dropping log m from its expansion around the mean of the z and truncating
+ * gives the pages' two ablation scores, the mean (first order) and the mean
+ * plus half the population variance (second order). */
+typedef enum {
+    PISA_SCORE_LSE = 0,            /* log sum exp(z) (the method) */
+    PISA_SCORE_MEAN = 1,           /* mean(z) */
+    PISA_SCORE_MEAN_HALF_VAR = 2   /* mean(z) + var(z) / 2, var over the m logits (1/m) */
+} pisa_score;
+
 /* Problem dimensions. dtype is the element type of q and k (both the same). */
 typedef struct {
     int32_t B;      /* batch */
@@ -72,6 +85,7 @@ typedef struct {
     int32_t g;      /* children per parent (2) */
     int32_t topk;   /* K: blocks kept per level and selected per query */
     int32_t dtype;  /* pisa_dtype of q and k */
+    int32_t score;  /* pisa_score; other values return PISA_ERR_INVALID_ARG */
 } pisa_dims;
 
 /* Rows (nodes) per (batch, KV head) of a pyramid laid out for n_capacity

@@ -40,12 +40,12 @@ class GpuPrefill:
 
 
 def run_prefill(q: np.ndarray, k: np.ndarray, topk: int, dtype: str, cap: int | None = None,
-                device="cuda") -> GpuPrefill:
+                device="cuda", score: str = "lse") -> GpuPrefill:
     from block_selection_amd import ops
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     cap = N if cap is None else cap
-    dims = ops.make_dims(B, Hq, Hkv, topk, dtype)
+    dims = ops.make_dims(B, Hq, Hkv, topk, dtype, score=score)
     kk = np.zeros((B, cap, Hkv, d), np.float32)
     kk[:, :N] = k
     qt, kt = to_device(q, dtype, device), to_device(kk, dtype, device)
@@ -111,10 +111,10 @@ class ParityReport:
 
 def compare_selection(gpu_idx: np.ndarray, ts: np.ndarray, q: np.ndarray, k: np.ndarray,
                       ref_pyr: np.ndarray, topk: int, validate_budget: int = 200000,
-                      ora=None) -> ParityReport:
+                      ora=None, score: str = "lse") -> ParityReport:
     """gpu_idx [len(ts), Hkv, K] for positions ts (B = 1); q [N, Hq, d]; k [N, Hkv, d]."""
     if ora is None:
-        ora = oracle.walk(q[ts], ts, k, ref_pyr, topk)
+        ora = oracle.walk(q[ts], ts, k, ref_pyr, topk, score=score)
     o_idx, o_gap, _ = ora
     rep = ParityReport()
     Hkv = k.shape[1]
@@ -134,7 +134,7 @@ def compare_selection(gpu_idx: np.ndarray, ts: np.ndarray, q: np.ndarray, k: np.
                 continue
             rep.mismatch_near_tie += 1
             v = oracle.validate(q[t], int(t), j, k, ref_pyr, topk, gpu_idx[i, j], NEAR_TIE,
-                                validate_budget)
+                                validate_budget, score=score)
             if v == 1:
                 rep.mismatch_valid += 1
             elif v == 0:

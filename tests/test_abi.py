@@ -55,6 +55,11 @@ def test_argument_errors_return_before_launch():
     assert _call_select(ops, ops.make_dims(1, 31, 2, 8)) == ops.PISA_ERR_INVALID_ARG
     assert _call_select(ops, ops.make_dims(1, 32, 2, 0)) == ops.PISA_ERR_INVALID_ARG
     assert _call_select(ops, ops.make_dims(0, 32, 2, 8)) == ops.PISA_ERR_INVALID_ARG
+    bad_score = ops.make_dims(1, 32, 2, 8)
+    bad_score.score = 3                                   # not a pisa_score
+    assert _call_select(ops, bad_score) == ops.PISA_ERR_INVALID_ARG
+    for sc in ("lse", "mean", "mean_half_var"):           # every score passes the dims checks
+        assert _call_select(ops, ops.make_dims(1, 32, 2, 8, score=sc), ws_bytes=16) == ops.PISA_ERR_WORKSPACE
     assert _call_select(ops, good, N=65, cap=64) == ops.PISA_ERR_CAPACITY
     assert _call_select(ops, good, N=0) == ops.PISA_ERR_INVALID_ARG
     assert _call_select(ops, good, ws=0) == ops.PISA_ERR_WORKSPACE

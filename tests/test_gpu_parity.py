@@ -34,18 +34,19 @@ def _log(name, rep, extra=None):
             f.write(json.dumps(line) + "\n")
 
 
-def _prefill_case(wl, n_sample=None, N=None, cap=None):
+def _prefill_case(wl, n_sample=None, N=None, cap=None, score="lse"):
     inp = synth.make_prefill(wl, N=N)
     N = inp.q.shape[1]
-    print(f"[case] {wl.name} N={N} Hq={wl.Hq} Hkv={wl.Hkv} K={wl.topk} dtype={wl.dtype} cap={cap}",
-          flush=True)
-    gpu = run_prefill(inp.q, inp.k, wl.topk, wl.dtype, cap=cap)
+    print(f"[case] {wl.name} N={N} Hq={wl.Hq} Hkv={wl.Hkv} K={wl.topk} dtype={wl.dtype} cap={cap} "
+          f"score={score}", flush=True)
+    gpu = run_prefill(inp.q, inp.k, wl.topk, wl.dtype, cap=cap, score=score)
     k0 = inp.k[0]
     ref_pyr = oracle.build_pyramid(k0)
     worst = check_pyramid(gpu.pyramid, ref_pyr, N, gpu.cap)
     ts = np.arange(N) if n_sample is None else sample_positions(N, n_sample, wl.topk)
-    rep = compare_selection(gpu.idx[0, ts], ts, inp.q[0], k0, ref_pyr, wl.topk)
-    _log(f"prefill_{wl.name}_N{N}", rep, {"pyramid_worst_rel": worst, "positions": int(len(ts))})
+    rep = compare_selection(gpu.idx[0, ts], ts, inp.q[0], k0, ref_pyr, wl.topk, score=score)
+    tag = "" if score == "lse" else f"_{score}"
+    _log(f"prefill_{wl.name}_N{N}{tag}", rep, {"pyramid_worst_rel": worst, "positions": int(len(ts))})
     assert rep.ok(), str(rep)
     return inp, gpu, rep
 
@@ -80,6 +81,27 @@ def test_prefill_ragged_lengths(N):
 def test_prefill_shape_variants(Hq, Hkv, K, dtype):
     wl = synth.Workload("variant", N=8192, Hq=Hq, Hkv=Hkv, topk=K, dtype=dtype, seed=Hq * 100 + K)
     _prefill_case(wl, n_sample=1500)
+
+
+# The pages' two ablation scores (first- and second-order truncations of the LSE):
+# the same walk, each scored against the oracle with the same score.
+@pytest.mark.parametrize("score", ["mean", "mean_half_var"])
+@pytest.mark.parametrize("name", ["tiny", "short"])
+def test_prefill_truncated_scores(name, score):
+    _prefill_case(synth.WORKLOADS[name], score=score)
+
+
+@pytest.mark.parametrize("score", ["mean", "mean_half_var"])
+@pytest.mark.parametrize("N,Hq,Hkv,K,dtype", [(4001, 32, 2, 8, "bf16"), (8192, 12, 3, 5, "bf16"),
+                                               (8192, 16, 1, 16, "bf16"), (3000, 6, 3, 5, "f32")])
+def test_prefill_truncated_scores_shapes(N, Hq, Hkv, K, dtype, score):
+    wl = synth.Workload("trunc", N=N, Hq=Hq, Hkv=Hkv, topk=K, dtype=dtype, seed=N + K)
+    _prefill_case(wl, n_sample=1200, score=score)
+
+
+@pytest.mark.parametrize("score", ["mean", "mean_half_var"])
+def test_prefill_truncated_scores_long64k(score):
+    _prefill_case(synth.WORKLOADS["long64k"], n_sample=600, score=score)
 
 
 def test_prefill_capacity_layout():
@@ -159,12 +181,12 @@ def test_planted_recall_matches_oracle():
 
 # ------------------------------------------------------------------ decode ---
 
-def _decode_run(N0, steps, check_every=1, oracle_every=1):
+def _decode_run(N0, steps, check_every=1, oracle_every=1, score="lse"):
     from block_selection_amd import ops
     wl = synth.Workload("decode", N=N0, Hq=32, Hkv=2, topk=32, dtype="bf16", decode_steps=steps)
     inp = synth.make_decode(wl)
     cap = N0 + steps
-    dims = ops.make_dims(1, 32, 2, 32, "bf16")
+    dims = ops.make_dims(1, 32, 2, 32, "bf16", score=score)
     k_all = np.concatenate([inp.k_ctx[0], inp.k_new[:, 0]], axis=0)   # [cap, Hkv, d]
     kc_host = np.zeros((1, cap, 2, 64), np.float32)
     kc_host[0, :N0] = inp.k_ctx[0]
@@ -192,7 +214,7 @@ def _decode_run(N0, steps, check_every=1, oracle_every=1):
                 for la, lb in zip(pyramid_levels(a[0, j], n + 1, cap), pyramid_levels(b[0, j], n + 1, cap)):
                     assert np.array_equal(la.view(np.uint32), lb.view(np.uint32)), (s, j)
         if s % oracle_every == 0 or s == steps - 1:
-            ref_pyr, o_idx, o_gap = oracle.decode_step(k_all, n, inp.q_new[s, 0], 32)
+            ref_pyr, o_idx, o_gap = oracle.decode_step(k_all, n, inp.q_new[s, 0], 32, score=score)
             if s == 0 or s == steps - 1:
                 check_pyramid(pyr.cpu().numpy(), ref_pyr, n + 1, cap)
             for j in range(2):
@@ -200,7 +222,7 @@ def _decode_run(N0, steps, check_every=1, oracle_every=1):
                     mism += 1
                     assert o_gap[j] < 1e-3, (s, j, gpu_idx[j], o_idx[j], o_gap[j])
                     v = oracle.validate(inp.q_new[s, 0], n, j, k_all[: n + 1], ref_pyr, 32, gpu_idx[j],
-                                        1e-3)
+                                        1e-3, score=score)
                     assert v != 0, (s, j)
                 near += int(o_gap[j] < 1e-3)
     return mism, near
@@ -212,14 +234,21 @@ def test_decode_small_context():
     print(json.dumps({"decode_small_mismatch_near_tie": mism, "near_tie_walks": near}), flush=True)
 
 
+@pytest.mark.parametrize("score", ["mean", "mean_half_var"])
+def test_decode_truncated_scores(score):
+    """Decode from 1000 keys with the truncated scores: rebuild-equal pyramid, oracle parity."""
+    mism, near = _decode_run(1000, 60, score=score)
+    print(json.dumps({f"decode_{score}_mismatch_near_tie": mism, "near_tie_walks": near}), flush=True)
+
+
 def test_decode_128k_256_steps():
     """The decode workload: 131072 prebuilt keys, 256 steps, K = 32; step 0 adds a root level."""
     mism, near = _decode_run(131072, 256, check_every=1, oracle_every=1)
     print(json.dumps({"decode128k_mismatch_near_tie": mism, "near_tie_walks": near}), flush=True)
 
 
-@pytest.mark.parametrize("topk", [32, 8])
-def test_decode_equals_prefill_at_same_position(topk):
+@pytest.mark.parametrize("topk,score", [(32, "lse"), (8, "lse"), (32, "mean"), (8, "mean_half_var")])
+def test_decode_equals_prefill_at_same_position(topk, score):
     """A decode step selects, bit for bit, what prefill selects for position n over n + 1 keys
     (both paths share the scoring arithmetic); 5000 context keys, 24 steps."""
     from block_selection_amd import ops
@@ -227,7 +256,7 @@ def test_decode_equals_prefill_at_same_position(topk):
     wl = synth.Workload("decode", N=N0, Hq=32, Hkv=2, topk=topk, dtype="bf16", decode_steps=steps)
     inp = synth.make_decode(wl)
     cap = N0 + steps
-    dims = ops.make_dims(1, 32, 2, topk, "bf16")
+    dims = ops.make_dims(1, 32, 2, topk, "bf16", score=score)
     kc_host = np.zeros((1, cap, 2, 64), np.float32)
     kc_host[0, :N0] = inp.k_ctx[0]
     k_cache = to_device(kc_host, "bf16")
@@ -249,7 +278,7 @@ def test_decode_equals_prefill_at_same_position(topk):
             dec = out.cpu().numpy()[0]
             q = np.zeros((1, n + 1, 32, 64), np.float32)
             q[0, n] = inp.q_new[s, 0]
-            ref = run_prefill(q, k_all[None, : n + 1], topk, "bf16")
+            ref = run_prefill(q, k_all[None, : n + 1], topk, "bf16", score=score)
             assert np.array_equal(dec, ref.idx[0, n]), (s, dec, ref.idx[0, n])
             checked += 1
     assert checked == 5
