@@ -125,7 +125,8 @@ def write_traffic(fetch_dir: str, write_dir: str, workload: str = "long256k") ->
         "command": ("rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> -o run -- "
                     "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-extras --copy-calibration; "
                     "python3 bench.py --write-traffic <fetch dir> <write dir>")}}
-    for key, srcs in (("leaf_cluster_kernel", LEAF_SOURCES), ("walk_upper_delta_kernel<16>", UPPER_SOURCES)):
+    # the LSE builds (score template argument 0) that the headline step runs
+    for key, srcs in (("leaf_cluster_kernel<0>", LEAF_SOURCES), ("walk_upper_delta_kernel<16, 0>", UPPER_SOURCES)):
         f_kib, w_kib = find(fetch, key), find(write, key)
         out[f"{key.split('<')[0]}:{workload}"] = {
             "fetch_kib": f_kib, "write_kib": w_kib,
