@@ -146,3 +146,46 @@ def make_decode(wl: Workload, steps: Optional[int] = None, N0: Optional[int] = N
     if wl.dtype == "bf16":
         k_ctx, k_new, q_new = bf16_round(k_ctx), bf16_round(k_new), bf16_round(q_new)
     return DecodeInputs(wl, k_ctx, k_new, q_new)
+
+
+@dataclasses.dataclass
+class VarlenInputs:
+    """A pack of documents laid end to end: T tokens, document i at rows cu[i] .. cu[i+1]-1."""
+    q: np.ndarray          # float32 [T, Hq, d]
+    k: np.ndarray          # float32 [T, Hkv, d]
+    cu: np.ndarray         # int32 [D + 1], cu[0] = 0, nondecreasing, cu[D] = T
+
+    def q_bits(self) -> np.ndarray:
+        return bf16_bits(self.q)
+
+    def k_bits(self) -> np.ndarray:
+        return bf16_bits(self.k)
+
+
+def doc_lengths(rng: np.random.Generator, T: int, mean_len: float) -> np.ndarray:
+    """Document lengths filling T tokens: exponential draws of the given mean, rounded up
+    to at least one token, the last one cut to fit."""
+    out, tot = [], 0
+    while tot < T:
+        n = max(1, int(np.ceil(rng.exponential(mean_len))))
+        n = min(n, T - tot)
+        out.append(n)
+        tot += n
+    return np.asarray(out, np.int64)
+
+
+def make_varlen(T: int, Hq: int, Hkv: int, dtype: str = "bf16", mean_len: float = 2048.0,
+                lengths=None, seed: int = 0, d: int = 64) -> VarlenInputs:
+    """Draw Q [T, Hq, d], then K [T, Hkv, d], then (unless given) the document lengths."""
+    rng = np.random.default_rng(seed)
+    q = _normal(rng, (T, Hq, d))
+    k = _normal(rng, (T, Hkv, d))
+    if lengths is None:
+        lengths = doc_lengths(rng, T, mean_len)
+    lengths = np.asarray(lengths, np.int64)
+    if lengths.min(initial=0) < 0 or int(lengths.sum()) != T:
+        raise ValueError("document lengths must be >= 0 and sum to T")
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    if dtype == "bf16":
+        q, k = bf16_round(q), bf16_round(k)
+    return VarlenInputs(q, k, cu)

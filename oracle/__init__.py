@@ -204,3 +204,52 @@ def decode_step(k_all: np.ndarray, n: int, q_new: np.ndarray, topk: int, C: int 
     pyr = build_pyramid(k, C, g, nthreads)
     idx, gap, _ = walk(q_new[None], np.array([n]), k, pyr, topk, C, g, nthreads, score)
     return pyr, idx[0], gap[0]
+
+
+# ------------------------------------------------------------------ packed documents --
+# Packed inputs keep document boundaries and allow no attention across documents (the
+# reading note's language-modelling experiments, continued-pretraining settings). Reading:
+# every document is selected exactly as if it were a sequence of its own -- its own pyramid
+# over its own keys, its queries at positions counted from the document's first token, its
+# leaf indices counted from the document's first leaf. Nothing of one document (keys,
+# summaries, blocks straddling a boundary) reaches another's selection.
+
+def doc_of(cu: np.ndarray, rows) -> np.ndarray:
+    """Document of each packed row: the last i with cu[i] <= row (empty documents skipped)."""
+    cu = np.asarray(cu, np.int64)
+    return np.searchsorted(cu, np.asarray(rows, np.int64), side="right") - 1
+
+
+def varlen_pyramids(k: np.ndarray, cu: np.ndarray, C: int = 64, g: int = 2, nthreads: int = 0) -> list:
+    """One pyramid per document (None for an empty one): k float [T, Hkv, d], cu int [D+1]."""
+    cu = np.asarray(cu, np.int64)
+    out = []
+    for i in range(len(cu) - 1):
+        lo, hi = int(cu[i]), int(cu[i + 1])
+        out.append(build_pyramid(k[lo:hi], C, g, nthreads) if hi > lo else None)
+    return out
+
+
+def varlen_walk(q: np.ndarray, k: np.ndarray, cu: np.ndarray, topk: int, rows=None, pyrs=None,
+                C: int = 64, g: int = 2, nthreads: int = 0, score: str = "lse"):
+    """Walks of the packed rows `rows` (default: all), each inside its own document.
+
+    q float [T, Hq, d], k float [T, Hkv, d]. Returns (idx int32 [n, Hkv, topk] of
+    document-local leaf indices, ascending, -1 padded; min_gap [n, Hkv]; gap_level [n, Hkv]).
+    """
+    cu = np.asarray(cu, np.int64)
+    T = int(cu[-1])
+    rows = np.arange(T, dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
+    if pyrs is None:
+        pyrs = varlen_pyramids(k, cu, C, g, nthreads)
+    docs = doc_of(cu, rows)
+    n, Hkv = len(rows), k.shape[1]
+    idx = np.zeros((n, Hkv, topk), np.int32)
+    gap = np.zeros((n, Hkv), np.float64)
+    lvl = np.zeros((n, Hkv), np.int32)
+    for dd in np.unique(docs):
+        sel = np.nonzero(docs == dd)[0]
+        lo, hi = int(cu[dd]), int(cu[dd + 1])
+        i_, g_, l_ = walk(q[rows[sel]], rows[sel] - lo, k[lo:hi], pyrs[dd], topk, C, g, nthreads, score)
+        idx[sel], gap[sel], lvl[sel] = i_, g_, l_
+    return idx, gap, lvl
