@@ -413,6 +413,7 @@ def main():
             del q2, k2, p2, o2, ws2
         result["sweep"] = sweep
         result["decode"] = decode_bench(torch, ops, synth, dev, log)
+        result["packed"] = packed_bench(torch, ops, synth, dev, log)
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
@@ -470,6 +471,64 @@ def decode_bench(torch, ops, synth, dev, log):
            "us_per_step_median": float(np.median(per)), "us_per_step_p90": float(np.percentile(per, 90)),
            "steps_per_s": 1e6 / float(per.mean())}
     log(f"decode: {res['us_per_step_mean']:.1f} us/step")
+    return res
+
+
+def packed_bench(torch, ops, synth, dev, log):
+    """Packed documents (varlen): one pisa_build_pyramid_packed + pisa_select_prefill_packed per
+    step over a pack of random-length documents, next to the same documents selected one call
+    per document through the single-sequence entry points."""
+    res = {}
+    for name, T, mean_len, K in (("packed256k_mean8k", 262144, 8192.0, 8), ("packed16k_k32", 16384, 2048.0, 32)):
+        v = synth.make_varlen(T, 32, 2, "bf16", mean_len=mean_len, seed=1)
+        D = len(v.cu) - 1
+        dims = ops.make_dims(1, 32, 2, K, "bf16")
+
+        def dev_t(x):
+            return torch.from_numpy(synth.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        q, k = dev_t(v.q), dev_t(v.k)
+        cu = torch.from_numpy(v.cu.astype(np.int32)).to(dev)
+        pyr = ops.alloc_pack_pyramid(dims, T, D, dev)
+        out = torch.empty((T, 2, K), dtype=torch.int32, device=dev)
+        ws = ops.alloc_pack_workspace(dims, T, D, dev)
+
+        def packed_step():
+            ops.build_pyramid_packed(k, cu, dims, pyr)
+            ops.select_prefill_packed(q, k, pyr, cu, dims, out, ws)
+        # the same documents, one build + select per document
+        lens = np.diff(v.cu).astype(np.int64)
+        nmax = int(lens.max())
+        pyr1 = ops.alloc_pyramid(dims, nmax, dev)
+        ws1 = ops.alloc_workspace(dims, nmax, nmax, device=dev)
+        out1 = torch.empty((T, 2, K), dtype=torch.int32, device=dev)
+        docs = [(int(v.cu[j]), int(v.cu[j + 1])) for j in range(D) if v.cu[j + 1] > v.cu[j]]
+
+        def per_doc_step():
+            for lo, hi in docs:
+                n = hi - lo
+                p1 = pyr1.view(-1)[: 2 * ops.pyramid_nodes(dims, n) * 64].view(1, 2, -1, 64)
+                ops.build_pyramid(k[lo:hi], n, n, dims, p1)
+                ops.select_prefill(q[lo:hi], k[lo:hi], p1, n, n, dims, out1[lo:hi], ws1)
+        row = {"T": T, "documents": D, "mean_len": mean_len, "K": K}
+        for label, fn in (("packed", packed_step), ("per_document_calls", per_doc_step)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            steps = 10
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            row[label + "_ms"] = ms
+            row[label + "_queries_per_s"] = T / (ms / 1e3)
+        row["same_selection"] = bool(torch.equal(out, out1))
+        log(f"{name}: D={D} packed {row['packed_ms']:.3f} ms, per-document calls "
+            f"{row['per_document_calls_ms']:.3f} ms, identical={row['same_selection']}")
+        res[name] = row
+        del q, k, cu, pyr, out, ws, pyr1, ws1, out1
     return res
 
 

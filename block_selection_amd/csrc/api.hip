@@ -12,8 +12,8 @@
 namespace pisa {
 
 template <typename KT>
-__global__ void build_subtree_kernel(const KT*, Geom, float*);
-__global__ void build_upper_kernel(Geom, float*);
+__global__ void build_subtree_kernel(const KT*, Geom, Pack, float*);
+__global__ void build_upper_kernel(Geom, Pack, float*);
 template <typename KT>
 __global__ void decode_refresh_kernel(const KT*, KT*, Geom, float*);
 template <int S>
@@ -25,19 +25,23 @@ __global__ void walk_upper_f32_kernel(const float*, const float*, Geom, int64_t,
 template <int SLOTS, int S>
 __global__ void walk_upper_delta_kernel(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg, int64_t,
                                         int64_t, int32_t*, int32_t*);
-__global__ void delta_planes_kernel(const float*, uint16_t*, Geom);
+template <int SLOTS, int S>
+__global__ void walk_upper_delta_pack_kernel(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int32_t*,
+                                             int32_t*);
+__global__ void delta_planes_kernel(const float*, uint16_t*, Geom, Pack);
 template <typename KT>
 __global__ void leaf_walk_kernel(const KT*, const KT*, Geom, int64_t, int64_t, const int32_t*,
                                  const int32_t*, int32_t*);
 
 __global__ void fill_u32_kernel(uint32_t*, int64_t, uint32_t);
 template <int SL>
-__global__ void bucket_pass_kernel(const int32_t*, const int32_t*, Geom, ClusterGeom, int64_t, uint32_t*,
-                                   const uint32_t*, const uint32_t*, uint2*, int);
-__global__ void group_offsets_kernel(const uint32_t*, ClusterGeom, uint32_t*, uint32_t*);
+__global__ void bucket_pass_kernel(const int32_t*, const int32_t*, Geom, ClusterGeom, Pack, const int64_t*, int64_t,
+                                   uint32_t*, const uint32_t*, const uint32_t*, uint2*, int);
+__global__ void pack_plan_kernel(Pack, int, int64_t*);
+__global__ void group_offsets_kernel(const uint32_t*, ClusterGeom, Pack, const int64_t*, uint32_t*, uint32_t*);
 __global__ void scan_groups_kernel(const uint32_t*, ClusterGeom, uint32_t*, int4*, uint32_t*);
 template <int S>
-__global__ void leaf_cluster_kernel(const uint16_t*, const uint16_t*, Geom, ClusterGeom, int64_t,
+__global__ void leaf_cluster_kernel(const uint16_t*, const uint16_t*, Geom, ClusterGeom, Pack, int64_t,
                                     const int4*, const uint2*, uint32_t*, float*, float*);
 
 // The kernels that score candidates are built once per candidate score (pisa_score);
@@ -47,6 +51,12 @@ static const void* upper_delta_fn(int score) {
     if (score == kScoreMean) return (const void*)walk_upper_delta_kernel<SLOTS, kScoreMean>;
     if (score == kScoreMeanHalfVar) return (const void*)walk_upper_delta_kernel<SLOTS, kScoreMeanHalfVar>;
     return (const void*)walk_upper_delta_kernel<SLOTS, kScoreLse>;
+}
+template <int SLOTS>
+static const void* upper_pack_fn(int score) {
+    if (score == kScoreMean) return (const void*)walk_upper_delta_pack_kernel<SLOTS, kScoreMean>;
+    if (score == kScoreMeanHalfVar) return (const void*)walk_upper_delta_pack_kernel<SLOTS, kScoreMeanHalfVar>;
+    return (const void*)walk_upper_delta_pack_kernel<SLOTS, kScoreLse>;
 }
 template <int SLOTS>
 static const void* upper_f32_fn(int score) {
@@ -87,6 +97,7 @@ struct Workspace {
     uint2* entries;      // [walks * 2K] incidences grouped by bucket
     int4* items;         // [walks * 2K / kItemMax + ngroups]
     uint32_t* meta;      // [0] items, [1] entries
+    int64_t* cbase;      // [D + 1] first count of each document's block (packs only)
     // fused bf16 decoding step
     uint32_t* done;      // [B*Hkv] completion counters (zero between steps)
     float* leaf_score;   // [B*Hkv][64] leaf scores of one step
@@ -142,6 +153,50 @@ static Workspace carve(const pisa_dims* d, int64_t N, int64_t P, bool decode, ch
     return w;
 }
 
+// Packs of D documents over T tokens (bf16, clustered leaf scoring) on the packed layout
+// of P rows per KV head.
+static int64_t pack_count_bound(int Hkv, int64_t T, int64_t D) {
+    // sum over documents of ceil(n/1024) * ceil(n/512) <= sum (n/1024 + 1)(n/512 + 1)
+    // <= T^2 / 2^19 + 3T/1024 + D
+    return (int64_t)Hkv * (((T + 1023) / 1024) * ((T + 511) / 512) + 3 * T / 1024 + D + 4);
+}
+
+static Workspace carve_pack(const pisa_dims* d, int64_t T, int64_t D, int64_t P, char* base) {
+    Workspace w;
+    memset(&w, 0, sizeof(w));
+    const int64_t walks = T * d->Hkv;
+    const int64_t cs = 2 * (int64_t)d->topk;
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> char* {
+        char* p = base ? base + off : nullptr;
+        off = align_up(off + bytes);
+        return p;
+    };
+    const size_t planes = (size_t)2 * d->Hkv * P * kD * 2;
+    w.planes = (uint16_t*)take(planes);
+    w.dplanes = (uint16_t*)take(planes);
+    w.cand = (int32_t*)take((size_t)walks * cs * sizeof(int32_t));
+    w.ncand = (int32_t*)take((size_t)walks * sizeof(int32_t));
+    w.clustered = true;
+    w.CG.NSB = (int32_t)((T >> (kLog2C + 4)) + D + 1);   // superblock slots per KV head
+    w.CG.NR = (int32_t)((T >> kLog2RangeT) + D + 1);     // range slots
+    w.CG.ngroups = (int32_t)(d->Hkv * (int64_t)w.CG.NSB);
+    const int64_t ncount = pack_count_bound(d->Hkv, T, D);
+    w.CG.nb = 0;
+    w.score = (float*)take((size_t)walks * cs * sizeof(float));
+    w.sink = (float*)take((size_t)kClusterThreads * sizeof(float));
+    w.counts = (uint32_t*)take((size_t)ncount * 4);
+    w.offsets = (uint32_t*)take((size_t)ncount * 4);
+    w.gtot = (uint32_t*)take((size_t)w.CG.ngroups * 4);
+    w.gbase = (uint32_t*)take((size_t)w.CG.ngroups * 4);
+    w.entries = (uint2*)take((size_t)walks * cs * sizeof(uint2));
+    w.items = (int4*)take(((size_t)walks * cs / kItemMax + w.CG.ngroups + 1) * sizeof(int4));
+    w.meta = (uint32_t*)take(16);
+    w.cbase = (int64_t*)take((size_t)(D + 1) * sizeof(int64_t));
+    w.bytes = off;
+    return w;
+}
+
 // Level sizes for n keys: M[1] = ceil(n/64), M[l+1] = ceil(M[l]/2) until 1. Returns L.
 static int level_sizes(int64_t n, int64_t M[kMaxLevels + 1]) {
     int64_t m = (n + kC - 1) / kC;
@@ -187,52 +242,57 @@ static int make_geom(const pisa_dims* d, int64_t n, int64_t cap, Geom* G) {
     return PISA_OK;
 }
 
+// Packed layout for D documents over T tokens: level l (1 .. root_level(T)) has a region of
+// (T >> (5 + l)) + D + 1 rows per KV head; G.M[l] holds the region sizes, G.P their total.
+static int make_pack_geom(const pisa_dims* d, int64_t T, int64_t D, Geom* G) {
+    if (T < 1 || D < 1) return PISA_ERR_INVALID_ARG;
+    if (d->B != 1) return PISA_ERR_INVALID_ARG;
+    if (T > (int64_t)INT_MAX / 2 || D > (int64_t)INT_MAX / 4) return PISA_ERR_UNSUPPORTED;
+    if ((int64_t)d->Hkv * ((T >> (kLog2C + 4)) + D + 1) > (int64_t)INT_MAX) return PISA_ERR_UNSUPPORTED;
+    memset(G, 0, sizeof(*G));
+    const int L = root_level(T);
+    int64_t off = 0;
+    for (int l = 1; l <= L; ++l) {
+        const int64_t R = (T >> (kLog2C + l - 1)) + D + 1;
+        G->off[l] = off;
+        G->M[l] = (int32_t)R;
+        off += R;
+    }
+    G->P = off;
+    G->L = L;
+    G->N = T;
+    G->cap = T;
+    G->B = 1; G->Hq = d->Hq; G->Hkv = d->Hkv; G->GQ = d->Hq / d->Hkv; G->topk = d->topk;
+    G->score = d->score;
+    return PISA_OK;
+}
+
 static int launch_status() {
     return (hipGetLastError() == hipSuccess) ? PISA_OK : PISA_ERR_HIP;
 }
 
 template <typename KT>
-static int build_impl(const KT* k, const Geom& G, float* pyr, hipStream_t s) {
-    const int nsub = (G.M[1] + 15) / 16;
-    const int64_t grid = (int64_t)G.B * G.Hkv * nsub;
-    if (grid > INT_MAX) return PISA_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(build_subtree_kernel<KT>, dim3((unsigned)grid), dim3(256), 0, s, k, G, pyr);
-    if (G.L > 5)
-        hipLaunchKernelGGL(build_upper_kernel, dim3((unsigned)(G.B * G.Hkv)), dim3(1024), 0, s, G, pyr);
+static int build_impl(const KT* k, const Geom& G, const Pack& pk, float* pyr, hipStream_t s) {
+    int64_t grid, ugrid;
+    if (pk.cu) {
+        grid = (int64_t)G.Hkv * ((pk.T >> 10) + pk.D + 1);   // (KV head, subtree slot)
+        ugrid = (int64_t)pk.D * G.Hkv;
+    } else {
+        grid = (int64_t)G.B * G.Hkv * ((G.M[1] + 15) / 16);
+        ugrid = (int64_t)G.B * G.Hkv;
+    }
+    if (grid > INT_MAX || ugrid > INT_MAX) return PISA_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(build_subtree_kernel<KT>, dim3((unsigned)grid), dim3(256), 0, s, k, G, pk, pyr);
+    if (G.L > 5) hipLaunchKernelGGL(build_upper_kernel, dim3((unsigned)ugrid), dim3(1024), 0, s, G, pk, pyr);
     return launch_status();
 }
 
-// Coarse levels to stage in LDS: the highest level that is ever read as children
-// (one below the highest level with more than K nodes) and as many levels below it
-// as fit the LDS budget.
-// LDS staging for the delta-form walk: the delta rows of the candidate levels from the
-// first level that can be scored (the highest with more than K nodes) downward, while
-// they fit.
+// LDS staging of the delta-form walk of one batch element (the same plan the packed walk
+// makes per document on the device).
 static UpperCfg upper_cfg_delta(const Geom& G) {
     UpperCfg U;
     memset(&U, 0, sizeof(U));
-    U.j_lo = 1;
-    U.j_hi = 0;
-    int top = 0;
-    for (int l = G.L; l >= 2; --l) {
-        if (G.M[l] > G.topk) { top = l; break; }
-    }
-    if (top < 2) return U;
-    int nodes = 0, j_lo = top + 1;
-    while (j_lo - 1 >= 2 && nodes + G.M[j_lo - 1] <= kLdsDeltaBudgetNodes) {
-        --j_lo;
-        nodes += G.M[j_lo];
-    }
-    if (j_lo > top) return U;
-    U.j_lo = j_lo;
-    U.j_hi = top;
-    int slot = 0;
-    for (int j = j_lo; j <= top; ++j) { U.lds_first[j] = slot; slot += G.M[j]; }
-    // the summary rows of the top scored level follow (at most 2K nodes)
-    U.s_level = top;
-    U.s_first = slot;
-    slot += G.M[top];
-    U.lds_nodes = slot;
+    upper_cfg_for(batch_seg(G.N, 0), G.topk, U);
     return U;
 }
 
@@ -256,6 +316,30 @@ static int launch_upper_delta(const uint16_t* q, const Geom& G, const UpperCfg& 
     const uint16_t* dplanes = W.dplanes;
     void* args[] = {(void*)&q, (void*)&planes, (void*)&dplanes, (void*)&G, (void*)&U, (void*)&t0, (void*)&NT,
                     (void*)&W.cand, (void*)&W.ncand};
+    if (hipLaunchKernel(fn, dim3((unsigned)nwg), dim3(kUpperThreads), args, lds, s) != hipSuccess)
+        return PISA_ERR_HIP;
+    return PISA_OK;
+}
+
+template <int SLOTS>
+static int launch_upper_pack(const uint16_t* q, const Geom& G, const Pack& pk, const Workspace& W, int cus,
+                             hipStream_t s) {
+    constexpr int WPW = 64 / SLOTS;
+    constexpr int nwaves = kUpperThreads / 64;
+    const int64_t pieces = (pk.T + kRangeT - 1) / kRangeT;
+    const int64_t groups = pieces * ((kRangeT + WPW - 1) / WPW);
+    int64_t need = (int64_t)G.Hkv * ((groups + nwaves - 1) / nwaves);
+    int64_t nwg = need < cus ? need : cus;
+    nwg = (nwg + 7) / 8 * 8;
+    if (nwg < G.Hkv) nwg = G.Hkv;
+    const size_t lds = (size_t)(kLdsDeltaBudgetNodes + 2 * G.topk) * kLdsNodeBytes;
+    const void* fn = upper_pack_fn<SLOTS>(G.score);
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return PISA_ERR_HIP;
+    const uint16_t* planes = W.planes;
+    const uint16_t* dplanes = W.dplanes;
+    void* args[] = {(void*)&q, (void*)&planes, (void*)&dplanes, (void*)&G, (void*)&pk, (void*)&W.cand,
+                    (void*)&W.ncand};
     if (hipLaunchKernel(fn, dim3((unsigned)nwg), dim3(kUpperThreads), args, lds, s) != hipSuccess)
         return PISA_ERR_HIP;
     return PISA_OK;
@@ -292,28 +376,37 @@ static void mark(void* const* ev, int i, hipStream_t s) {
     if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], s);
 }
 
-static int cluster_leaf_stage(const uint16_t* q, const uint16_t* k, const Geom& G, int64_t NT, int32_t* out,
-                              const Workspace& W, int cus, hipStream_t s, void* const* ev) {
+static int cluster_leaf_stage(const uint16_t* q, const uint16_t* k, const Geom& G, const Pack& pk, int64_t NT,
+                              int32_t* out, const Workspace& W, int cus, hipStream_t s, void* const* ev) {
     const int64_t walks = (int64_t)G.B * NT * G.Hkv;
     const ClusterGeom& CG = W.CG;
     const int slots = 2 * G.topk;
-    const dim3 bgrid((unsigned)CG.NR, (unsigned)G.B);
-    const size_t bins = (size_t)G.Hkv * CG.NSB * 4;
+    dim3 bgrid;
+    size_t bins;
+    if (pk.cu) {
+        hipLaunchKernelGGL(pack_plan_kernel, dim3(1), dim3(1024), 0, s, pk, G.Hkv, W.cbase);
+        bgrid = dim3((unsigned)CG.NR, 1u);
+        bins = (size_t)G.Hkv * ((pk.T + kSbKeys - 1) / kSbKeys) * 4;   // the longest document's groups
+    } else {
+        bgrid = dim3((unsigned)CG.NR, (unsigned)G.B);
+        bins = (size_t)G.Hkv * CG.NSB * 4;
+    }
+    const int64_t* cbase = W.cbase;
     for (int fill = 0; fill < 2; ++fill) {
         if (fill) {
             hipLaunchKernelGGL(group_offsets_kernel, dim3((unsigned)((CG.ngroups + 3) / 4)), dim3(256), 0, s, W.counts,
-                               CG, W.offsets, W.gtot);
+                               CG, pk, cbase, W.offsets, W.gtot);
             hipLaunchKernelGGL(scan_groups_kernel, dim3(1), dim3(1024), 0, s, W.gtot, CG, W.gbase, W.items, W.meta);
         }
         if (slots <= 16)
-            hipLaunchKernelGGL(bucket_pass_kernel<16>, bgrid, dim3(1024), bins, s, W.cand, W.ncand, G, CG, NT, W.counts,
-                               W.offsets, W.gbase, W.entries, fill);
+            hipLaunchKernelGGL(bucket_pass_kernel<16>, bgrid, dim3(1024), bins, s, W.cand, W.ncand, G, CG, pk, cbase,
+                               NT, W.counts, W.offsets, W.gbase, W.entries, fill);
         else if (slots <= 32)
-            hipLaunchKernelGGL(bucket_pass_kernel<32>, bgrid, dim3(1024), bins, s, W.cand, W.ncand, G, CG, NT, W.counts,
-                               W.offsets, W.gbase, W.entries, fill);
+            hipLaunchKernelGGL(bucket_pass_kernel<32>, bgrid, dim3(1024), bins, s, W.cand, W.ncand, G, CG, pk, cbase,
+                               NT, W.counts, W.offsets, W.gbase, W.entries, fill);
         else
-            hipLaunchKernelGGL(bucket_pass_kernel<64>, bgrid, dim3(1024), bins, s, W.cand, W.ncand, G, CG, NT, W.counts,
-                               W.offsets, W.gbase, W.entries, fill);
+            hipLaunchKernelGGL(bucket_pass_kernel<64>, bgrid, dim3(1024), bins, s, W.cand, W.ncand, G, CG, pk, cbase,
+                               NT, W.counts, W.offsets, W.gbase, W.entries, fill);
     }
     const void* leaf_fn = leaf_cluster_fn(G.score);
     if (hipFuncSetAttribute(leaf_fn, hipFuncAttributeMaxDynamicSharedMemorySize, kSbLdsBytes) != hipSuccess)
@@ -322,8 +415,8 @@ static int cluster_leaf_stage(const uint16_t* q, const uint16_t* k, const Geom& 
     {
         const int4* items = W.items;
         const uint2* entries = W.entries;
-        void* args[] = {(void*)&q, (void*)&k, (void*)&G, (void*)&CG, (void*)&NT, (void*)&items, (void*)&entries,
-                        (void*)&W.meta, (void*)&W.score, (void*)&W.sink};
+        void* args[] = {(void*)&q, (void*)&k, (void*)&G, (void*)&CG, (void*)&pk, (void*)&NT, (void*)&items,
+                        (void*)&entries, (void*)&W.meta, (void*)&W.score, (void*)&W.sink};
         if (hipLaunchKernel(leaf_fn, dim3((unsigned)cus), dim3(kClusterThreads), args, kSbLdsBytes, s) != hipSuccess)
             return PISA_ERR_HIP;
     }
@@ -340,6 +433,31 @@ static int cluster_leaf_stage(const uint16_t* q, const uint16_t* k, const Geom& 
     return launch_status();
 }
 
+// Summary planes (the candidates' own rows, ragged children) and delta planes of a bf16
+// walk over the pyramid of G (sequences: the batch elements, or the documents of pk).
+static void plane_kernels(const float* pyr, const Geom& G, const Pack& pk, const Workspace& W, hipStream_t s) {
+    const int64_t n = (int64_t)G.B * G.Hkv * G.P * kD;
+    int64_t grid = (n + 255) / 256;
+    if (grid > 8192) grid = 8192;
+    hipLaunchKernelGGL(split_planes_kernel, dim3((unsigned)grid), dim3(256), 0, s, pyr, W.planes, n);
+    if (pk.cu) {
+        // documents average T/D tokens: about T/D * 64 / 64 delta elements per workgroup row
+        int64_t dgrid = (pk.T / pk.D + 255) / 256;
+        if (dgrid < 1) dgrid = 1;
+        if (dgrid > 256) dgrid = 256;
+        hipLaunchKernelGGL(delta_planes_kernel, dim3((unsigned)(pk.D * G.Hkv), (unsigned)dgrid), dim3(256), 0, s,
+                           pyr, W.dplanes, G, pk);
+        return;
+    }
+    int64_t drows = 0;
+    for (int l = 2; l <= G.L; ++l) drows += G.M[l];
+    int64_t dgrid = (drows * kD + 255) / 256;
+    if (dgrid > 4096) dgrid = 4096;
+    if (dgrid > 0)
+        hipLaunchKernelGGL(delta_planes_kernel, dim3((unsigned)dgrid, (unsigned)(G.B * G.Hkv)), dim3(256), 0, s,
+                           pyr, W.dplanes, G, pk);
+}
+
 template <typename KT>
 static int select_impl(const KT* q, const KT* k, const float* pyr, const Geom& G, int64_t t0,
                        int64_t NT, int32_t* out, const Workspace& W, hipStream_t s, void* const* ev) {
@@ -347,18 +465,7 @@ static int select_impl(const KT* q, const KT* k, const float* pyr, const Geom& G
     if ((rc = device_cus(&cus)) != PISA_OK) return rc;
     const int slots = 2 * G.topk;
     if constexpr (sizeof(KT) == 2) {
-        // summary planes (the candidates' own rows, ragged children) and delta planes
-        const int64_t n = (int64_t)G.B * G.Hkv * G.P * kD;
-        int64_t grid = (n + 255) / 256;
-        if (grid > 8192) grid = 8192;
-        hipLaunchKernelGGL(split_planes_kernel, dim3((unsigned)grid), dim3(256), 0, s, pyr, W.planes, n);
-        int64_t drows = 0;
-        for (int l = 2; l <= G.L; ++l) drows += G.M[l];
-        int64_t dgrid = (drows * kD + 255) / 256;
-        if (dgrid > 4096) dgrid = 4096;
-        if (dgrid > 0)
-            hipLaunchKernelGGL(delta_planes_kernel, dim3((unsigned)dgrid, (unsigned)(G.B * G.Hkv)), dim3(256), 0, s,
-                               pyr, W.dplanes, G);
+        plane_kernels(pyr, G, Pack{nullptr, 0, 0}, W, s);
         const UpperCfg U = upper_cfg_delta(G);
         mark(ev, 0, s);
         if (slots <= 16) rc = launch_upper_delta<16>(q, G, U, t0, NT, W, cus, s);
@@ -382,7 +489,23 @@ static int select_impl(const KT* q, const KT* k, const float* pyr, const Geom& G
         mark(ev, 3, s);
         return launch_status();
     }
-    return cluster_leaf_stage((const uint16_t*)q, (const uint16_t*)k, G, NT, out, W, cus, s, ev);
+    return cluster_leaf_stage((const uint16_t*)q, (const uint16_t*)k, G, Pack{nullptr, 0, 0}, NT, out, W, cus, s, ev);
+}
+
+// Packed documents, bf16: planes, the packed walk, clustered leaf scoring, final top-K.
+static int select_pack_impl(const uint16_t* q, const uint16_t* k, const float* pyr, const Geom& G, const Pack& pk,
+                            int32_t* out, const Workspace& W, hipStream_t s, void* const* ev) {
+    int rc, cus = 256;
+    if ((rc = device_cus(&cus)) != PISA_OK) return rc;
+    const int slots = 2 * G.topk;
+    plane_kernels(pyr, G, pk, W, s);
+    mark(ev, 0, s);
+    if (slots <= 16) rc = launch_upper_pack<16>(q, G, pk, W, cus, s);
+    else if (slots <= 32) rc = launch_upper_pack<32>(q, G, pk, W, cus, s);
+    else rc = launch_upper_pack<64>(q, G, pk, W, cus, s);
+    if (rc != PISA_OK) return rc;
+    mark(ev, 1, s);
+    return cluster_leaf_stage(q, k, G, pk, pk.T, out, W, cus, s, ev);
 }
 
 }  // namespace pisa
@@ -430,8 +553,9 @@ int pisa_build_pyramid(const void* k, int64_t N, int64_t n_capacity, const pisa_
     Geom G;
     if ((rc = make_geom(dims, N, n_capacity, &G)) != PISA_OK) return rc;
     hipStream_t s = (hipStream_t)stream;
-    if (dims->dtype == PISA_DTYPE_BF16) return build_impl((const uint16_t*)k, G, pyramid, s);
-    return build_impl((const float*)k, G, pyramid, s);
+    const Pack none{nullptr, 0, 0};
+    if (dims->dtype == PISA_DTYPE_BF16) return build_impl((const uint16_t*)k, G, none, pyramid, s);
+    return build_impl((const float*)k, G, none, pyramid, s);
 }
 
 int pisa_select_prefill_profiled(const void* q, const void* k, const float* pyramid, int64_t N,
@@ -490,6 +614,67 @@ int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cach
     if ((rc = launch_status()) != PISA_OK) return rc;
     return select_impl((const float*)q_new, (const float*)k_cache, pyramid, G, n_before, 1, out_idx, W, s,
                        nullptr);
+}
+
+// ------------------------------------------------------------------ packed documents --
+
+static int check_pack(const pisa_dims* dims, int64_t T, int64_t D, Geom* G) {
+    int rc = check_dims(dims);
+    if (rc != PISA_OK) return rc;
+    return make_pack_geom(dims, T, D, G);
+}
+
+int64_t pisa_pack_pyramid_rows(const pisa_dims* dims, int64_t T, int64_t D) {
+    Geom G;
+    if (check_pack(dims, T, D, &G) != PISA_OK) return -1;
+    return G.P;
+}
+
+int64_t pisa_pack_level_offset(const pisa_dims* dims, int64_t T, int64_t D, int32_t level) {
+    Geom G;
+    if (check_pack(dims, T, D, &G) != PISA_OK || level < 1 || level > G.L) return -1;
+    return G.off[level];
+}
+
+size_t pisa_pack_pyramid_bytes(const pisa_dims* dims, int64_t T, int64_t D) {
+    Geom G;
+    if (check_pack(dims, T, D, &G) != PISA_OK) return 0;
+    return (size_t)dims->Hkv * (size_t)G.P * kD * sizeof(float);
+}
+
+size_t pisa_pack_workspace_bytes(const pisa_dims* dims, int64_t T, int64_t D) {
+    Geom G;
+    if (check_pack(dims, T, D, &G) != PISA_OK) return 0;
+    return carve_pack(dims, T, D, G.P, nullptr).bytes;
+}
+
+int pisa_build_pyramid_packed(const void* k, const int32_t* cu_seqlens, int64_t D, int64_t T,
+                              const pisa_dims* dims, float* pyramid, void* stream) {
+    Geom G;
+    int rc = check_pack(dims, T, D, &G);
+    if (rc != PISA_OK) return rc;
+    if (!k || !cu_seqlens || !pyramid) return PISA_ERR_INVALID_ARG;
+    const Pack pk{cu_seqlens, (int32_t)D, T};
+    hipStream_t s = (hipStream_t)stream;
+    if (dims->dtype == PISA_DTYPE_BF16) return build_impl((const uint16_t*)k, G, pk, pyramid, s);
+    return build_impl((const float*)k, G, pk, pyramid, s);
+}
+
+int pisa_select_prefill_packed(const void* q, const void* k, const float* pyramid, const int32_t* cu_seqlens,
+                               int64_t D, int64_t T, const pisa_dims* dims, int32_t* out_idx,
+                               void* workspace, size_t ws_bytes, void* stream) {
+    Geom G;
+    int rc = check_pack(dims, T, D, &G);
+    if (rc != PISA_OK) return rc;
+    if (!q || !k || !pyramid || !cu_seqlens || !out_idx) return PISA_ERR_INVALID_ARG;
+    if (dims->dtype != PISA_DTYPE_BF16) return PISA_ERR_UNSUPPORTED;
+    // the bucket pass holds one document's (KV head, superblock) bins in LDS
+    if ((int64_t)dims->Hkv * ((T + kSbKeys - 1) / kSbKeys) > 16384) return PISA_ERR_UNSUPPORTED;
+    const Workspace W = carve_pack(dims, T, D, G.P, (char*)workspace);
+    if (!workspace || ws_bytes < W.bytes) return PISA_ERR_WORKSPACE;
+    const Pack pk{cu_seqlens, (int32_t)D, T};
+    return select_pack_impl((const uint16_t*)q, (const uint16_t*)k, pyramid, G, pk, out_idx, W,
+                            (hipStream_t)stream, nullptr);
 }
 
 const char* pisa_status_string(int status) {

@@ -41,30 +41,59 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p,
 // offsets of one leaf or of a sibling pair (batch element and KV head are the bucket's).
 // Counts and offsets are group-major: bucket (range r, group g) at g * NR + r; the fill
 // pass starts bucket (r, g) at gbase[g] + offsets[g * NR + r].
+// With a pack (pk.cu non-null) blockIdx.x is a range slot of the packed layout: range j of
+// one document d (or nothing), positions t count from the document's start, and the
+// workgroup's bins are the document's own groups, x = kvh * nsb_d + s (superblock s of the
+// document is superblock slot (cu[d] >> 10) + d + s, group kvh * CG.NSB + that slot). Its
+// counts sit in the document's block at cbase[d] + x * nr_d + j (nr_d ranges).
 template <int SL>
 __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __restrict__ cand,
                                                           const int32_t* __restrict__ ncand, Geom G,
-                                                          ClusterGeom CG, int64_t NT,
-                                                          uint32_t* __restrict__ counts,
+                                                          ClusterGeom CG, Pack pk, const int64_t* __restrict__ cbase,
+                                                          int64_t NT, uint32_t* __restrict__ counts,
                                                           const uint32_t* __restrict__ offsets,
                                                           const uint32_t* __restrict__ gbase,
                                                           uint2* __restrict__ entries, int fill) {
     extern __shared__ uint32_t bins[];
     constexpr int WPW = 64 / SL;
-    const int r = blockIdx.x, b = blockIdx.y;
+    static_assert(kRangeT == (1 << kLog2RangeT), "range slots use the range size's log2");
+    const int r = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, seg = lane / SL, i = lane % SL;
     const int K = G.topk, CS = 2 * G.topk;
-    const int nbins = G.Hkv * CG.NSB;
     const int nthr = blockDim.x, nw = nthr >> 6;
-    // bin x = kvh * NSB + sb is group g = b * nbins + x
+    int64_t bt0, t_lo, t_hi;   // first query row of the sequence, positions [t_lo, t_hi)
+    int nsb;                   // superblocks per KV head in the bins: x = kvh * nsb + s
+    int64_t g_sb0, c0, c_str;  // bin x -> group (x / nsb) * CG.NSB + g_sb0 + x % nsb; count c0 + x * c_str
+    if (pk.cu) {
+        const int d = pack_find_slot(pk, kLog2RangeT, r);
+        const Seg sg = pack_seg(pk, d);
+        const int64_t j = r - ((sg.lsh >> kLog2RangeT) + d);
+        const int64_t nr = (sg.N + kRangeT - 1) / kRangeT;
+        if (sg.N == 0 || j < 0 || j >= nr) return;   // no positions, no buckets
+        bt0 = sg.lsh;
+        t_lo = j * kRangeT;
+        t_hi = (t_lo + kRangeT < sg.N) ? t_lo + kRangeT : sg.N;
+        nsb = (int)((sg.N + kSbKeys - 1) / kSbKeys);
+        g_sb0 = (sg.lsh >> (kLog2C + 4)) + d;
+        c0 = cbase[d] + j;
+        c_str = nr;
+    } else {
+        const int b = blockIdx.y;
+        bt0 = (int64_t)b * NT;
+        t_lo = (int64_t)r * kRangeT;
+        t_hi = (t_lo + kRangeT < NT) ? t_lo + kRangeT : NT;
+        nsb = CG.NSB;
+        g_sb0 = (int64_t)b * G.Hkv * CG.NSB;
+        c0 = g_sb0 * CG.NR + r;
+        c_str = CG.NR;
+    }
+    const int nbins = G.Hkv * nsb;
     for (int x = tid; x < nbins; x += nthr) {
-        const int64_t g = (int64_t)b * nbins + x;
-        bins[x] = fill ? gbase[g] + offsets[g * CG.NR + r] : 0u;
+        const int64_t g = (int64_t)(x / nsb) * CG.NSB + g_sb0 + x % nsb;
+        bins[x] = fill ? gbase[g] + offsets[c0 + x * c_str] : 0u;
     }
     __syncthreads();
-    const int64_t t_lo = (int64_t)r * kRangeT;
-    const int64_t t_hi = (t_lo + kRangeT < NT) ? t_lo + kRangeT : NT;
-    const int64_t w_lo = ((int64_t)b * NT + t_lo) * G.Hkv, w_hi = ((int64_t)b * NT + t_hi) * G.Hkv;
+    const int64_t w_lo = (bt0 + t_lo) * G.Hkv, w_hi = (bt0 + t_hi) * G.Hkv;
     for (int64_t w0 = w_lo + (int64_t)(tid >> 6) * WPW; w0 < w_hi; w0 += (int64_t)nw * WPW) {
         const int64_t w = w0 + seg;
         const bool ok = w < w_hi;
@@ -81,38 +110,85 @@ __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __rest
         const bool pair = even && i + 1 < SL && nxt == leaf + 1;
         const uint32_t m = (leaf >= 0) ? ((pair ? 3u : 1u) << (leaf % kSbLeaves)) : 0u;
         if (start) {
-            const uint32_t pos = atomicAdd(&bins[kvh * CG.NSB + sbv], 1u);
-            if (fill) entries[pos] = make_uint2((uint32_t)(w / G.Hkv - (int64_t)b * NT), m | ((uint32_t)i << 16));
+            const uint32_t pos = atomicAdd(&bins[kvh * nsb + sbv], 1u);
+            if (fill) entries[pos] = make_uint2((uint32_t)(w / G.Hkv - bt0), m | ((uint32_t)i << 16));
         }
     }
     __syncthreads();
     if (!fill) {
-        for (int x = tid; x < nbins; x += nthr) counts[((int64_t)b * nbins + x) * CG.NR + r] = bins[x];
+        for (int x = tid; x < nbins; x += nthr) counts[c0 + x * c_str] = bins[x];
     }
+}
+
+// Pack plan (one workgroup): cbase[d] = first count of document d's block (KV heads x its
+// superblocks x its ranges), an exclusive scan over the documents; cbase[D] = the total.
+__global__ __launch_bounds__(1024) void pack_plan_kernel(Pack pk, int Hkv, int64_t* __restrict__ cbase) {
+    __shared__ int64_t s_sum[1024];
+    const int tid = threadIdx.x;
+    const int per = (pk.D + 1023) / 1024;
+    const int lo = tid * per, hi = min(pk.D, lo + per);
+    auto size_of = [&](int d) -> int64_t {
+        const Seg sg = pack_seg(pk, d);
+        return (int64_t)Hkv * ((sg.N + kSbKeys - 1) / kSbKeys) * ((sg.N + kRangeT - 1) / kRangeT);
+    };
+    int64_t acc = 0;
+    for (int d = lo; d < hi; ++d) acc += size_of(d);
+    s_sum[tid] = acc;
+    __syncthreads();
+    for (int st = 1; st < 1024; st <<= 1) {   // inclusive Hillis-Steele scan
+        const int64_t add = (tid >= st) ? s_sum[tid - st] : 0;
+        __syncthreads();
+        s_sum[tid] += add;
+        __syncthreads();
+    }
+    int64_t run = s_sum[tid] - acc;
+    for (int d = lo; d < hi; ++d) {
+        cbase[d] = run;
+        run += size_of(d);
+    }
+    if (tid == 1023) cbase[pk.D] = s_sum[1023];
 }
 
 // One wavefront per group g: the exclusive scan of its ranges' counts (the offset of
 // each bucket inside the group) and the group's total. Grid: ceil(ngroups / 4)
-// workgroups of 4 wavefronts.
+// workgroups of 4 wavefronts. With a pack, group g = kvh * CG.NSB + superblock slot; a
+// slot that names no superblock of a document has total 0.
 __global__ __launch_bounds__(256) void group_offsets_kernel(const uint32_t* __restrict__ counts, ClusterGeom CG,
+                                                            Pack pk, const int64_t* __restrict__ cbase,
                                                             uint32_t* __restrict__ offsets,
                                                             uint32_t* __restrict__ gtot) {
     const int lane = threadIdx.x & 63;
     const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (g >= CG.ngroups) return;   // whole wavefronts leave together
-    const uint32_t* c = counts + g * CG.NR;
-    uint32_t* o = offsets + g * CG.NR;
+    int64_t c0 = g * CG.NR;
+    int nr = CG.NR;
+    if (pk.cu) {
+        const int kvh = (int)(g / CG.NSB);
+        const int64_t slot = g % CG.NSB;
+        const int d = pack_find_slot(pk, kLog2C + 4, slot);
+        const Seg sg = pack_seg(pk, d);
+        const int64_t s = slot - ((sg.lsh >> (kLog2C + 4)) + d);
+        const int64_t nsb = (sg.N + kSbKeys - 1) / kSbKeys;
+        if (sg.N == 0 || s < 0 || s >= nsb) {
+            if (lane == 0) gtot[g] = 0u;
+            return;
+        }
+        nr = (int)((sg.N + kRangeT - 1) / kRangeT);
+        c0 = cbase[d] + (kvh * nsb + s) * nr;
+    }
+    const uint32_t* c = counts + c0;
+    uint32_t* o = offsets + c0;
     uint32_t run = 0;
-    for (int r0 = 0; r0 < CG.NR; r0 += 64) {
+    for (int r0 = 0; r0 < nr; r0 += 64) {
         const int r = r0 + lane;
-        const uint32_t v = (r < CG.NR) ? c[r] : 0u;
+        const uint32_t v = (r < nr) ? c[r] : 0u;
         uint32_t x = v;   // inclusive scan over the wavefront
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
             const uint32_t y = (uint32_t)shfl_i((int)x, lane >= d ? lane - d : lane);
             x += (lane >= d) ? y : 0u;
         }
-        if (r < CG.NR) o[r] = run + x - v;
+        if (r < nr) o[r] = run + x - v;
         run += (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
     }
     if (lane == 0) gtot[g] = run;
@@ -170,11 +246,11 @@ __global__ __launch_bounds__(1024) void scan_groups_kernel(const uint32_t* __res
     }
 }
 
-template __global__ void bucket_pass_kernel<16>(const int32_t*, const int32_t*, Geom, ClusterGeom, int64_t,
+template __global__ void bucket_pass_kernel<16>(const int32_t*, const int32_t*, Geom, ClusterGeom, Pack, const int64_t*, int64_t,
                                                 uint32_t*, const uint32_t*, const uint32_t*, uint2*, int);
-template __global__ void bucket_pass_kernel<32>(const int32_t*, const int32_t*, Geom, ClusterGeom, int64_t,
+template __global__ void bucket_pass_kernel<32>(const int32_t*, const int32_t*, Geom, ClusterGeom, Pack, const int64_t*, int64_t,
                                                 uint32_t*, const uint32_t*, const uint32_t*, uint2*, int);
-template __global__ void bucket_pass_kernel<64>(const int32_t*, const int32_t*, Geom, ClusterGeom, int64_t,
+template __global__ void bucket_pass_kernel<64>(const int32_t*, const int32_t*, Geom, ClusterGeom, Pack, const int64_t*, int64_t,
                                                 uint32_t*, const uint32_t*, const uint32_t*, uint2*, int);
 
 // LDS image of a superblock: key row r (0..1023) at r*128 bytes, its 16-byte chunk c
@@ -375,7 +451,7 @@ __device__ inline void load_q(const uint16_t* __restrict__ q, int64_t bt, int Hq
 
 template <int S>
 __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, Geom G, ClusterGeom CG, int64_t NT,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, Geom G, ClusterGeom CG, Pack pk, int64_t NT,
     const int4* __restrict__ items, const uint2* __restrict__ entries, uint32_t* __restrict__ meta,
     float* __restrict__ score, float* __restrict__ sink) {
     static_assert(kItemMax <= 64 * (kClusterThreads / 64), "a wavefront holds its entries in one VGPR pair");
@@ -397,11 +473,27 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
         if (it >= n_items) break;
         const int4 item = items[it];
         const int grp = item.x;
-        const int sb = grp % CG.NSB;
+        const int sbs = grp % CG.NSB;
         const int kvh = (grp / CG.NSB) % G.Hkv;
-        const int b = grp / (CG.NSB * G.Hkv);
+        // the group's sequence: its first query row, first key row and key count
+        int64_t bt0, tk0, nkeys;
+        int sb;
+        if (pk.cu) {
+            const int d = pack_find_slot(pk, kLog2C + 4, sbs);
+            const Seg sg = pack_seg(pk, d);
+            sb = sbs - (int)((sg.lsh >> (kLog2C + 4)) + d);
+            bt0 = sg.lsh;
+            tk0 = sg.tk0;
+            nkeys = sg.N;
+        } else {
+            const int b = grp / (CG.NSB * G.Hkv);
+            sb = sbs;
+            bt0 = (int64_t)b * NT;
+            tk0 = (int64_t)b * G.cap;
+            nkeys = G.N;
+        }
         const int key_base = sb * kSbKeys;
-        const uint16_t* kb = k + ((int64_t)b * G.cap * G.Hkv + kvh) * kD;
+        const uint16_t* kb = k + (tk0 * G.Hkv + kvh) * kD;
         // this wavefront's entries item.y + wave + j*nwaves, j < cnt: lane j holds entry j
         const int first = item.y + wave;
         const int cnt = (item.z > wave) ? (item.z - wave + nwaves - 1) / nwaves : 0;
@@ -437,7 +529,6 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
         // queries of the first two units, in flight during the key staging; units past
         // nunits read walk 0 (a valid row) and score nothing
         u32x4 qa0, qa1, qb0, qb1, ra0, ra1, rb0, rb1;
-        const int64_t bt0 = (int64_t)b * NT;   // entries hold positions t of batch element b
         auto qload = [&](int u, u32x4& a0, u32x4& a1, u32x4& b0, u32x4& b1) {
             const uint32_t ta = (uint32_t)__builtin_amdgcn_readlane((int)uax, u);
             const uint32_t tb = (uint32_t)__builtin_amdgcn_readlane((int)(uby ? ubx : uax), u);
@@ -450,7 +541,7 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
             const int r = idx >> 3, ch = idx & 7;
             const int key = key_base + r;
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (key < G.N) v = *reinterpret_cast<const u32x4*>(kb + (int64_t)key * row_stride + ch * 8);
+            if (key < nkeys) v = *reinterpret_cast<const u32x4*>(kb + (int64_t)key * row_stride + ch * 8);
             *reinterpret_cast<lds_u32x4_t*>(lds + sb_lds_offset(r, ch)) = v;
         }
         __syncthreads();
@@ -503,7 +594,7 @@ __global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
 }
 
 #define PISA_LEAF_CLUSTER_INST(S)                                                                         \
-    template __global__ void leaf_cluster_kernel<S>(const uint16_t*, const uint16_t*, Geom, ClusterGeom, int64_t, \
+    template __global__ void leaf_cluster_kernel<S>(const uint16_t*, const uint16_t*, Geom, ClusterGeom, Pack, int64_t, \
                                                     const int4*, const uint2*, uint32_t*, float*, float*);
 PISA_LEAF_CLUSTER_INST(kScoreLse)
 PISA_LEAF_CLUSTER_INST(kScoreMean)

@@ -46,6 +46,95 @@ __host__ __device__ inline int64_t covered(int l, int64_t i, int64_t n) {
     return (n - lo < s) ? (n - lo) : s;
 }
 
+// Root level of a sequence of n >= 1 keys: ceil(n/64) leaves, halved (rounding up) to 1.
+__host__ __device__ inline int32_t root_level(int64_t n) {
+    int64_t m = (n + kC - 1) / kC;
+    int32_t l = 1;
+    while (m > 1) {
+        m = (m + 1) >> 1;
+        ++l;
+    }
+    return l;
+}
+
+// One independent sequence of a call: a batch element, or one document of a pack.
+// Level l of the sequence has M(l) = ceil(N / (64 * 2^(l-1))) nodes; node i sits at row
+// off[l] + shift(l) + i of its KV head's pyramid region. A batch element has shift 0;
+// document d of a pack, first token a, has shift (a >> (5 + l)) + d (the packed layout).
+struct Seg {
+    int64_t N;     // keys (and query positions) of the sequence; 0 for an empty document
+    int64_t tk0;   // row of its key 0 in the key array (per batch element or pack)
+    int64_t lsh;   // packed layout: first token of the document; 0 for a batch element
+    int32_t ld;    // packed layout: index of the document; 0 for a batch element
+    int32_t L;     // root level
+    __host__ __device__ int32_t M(int l) const { return (int32_t)(((N - 1) >> (kLog2C + l - 1)) + 1); }
+    __host__ __device__ int64_t shift(int l) const { return (lsh >> (kLog2C + l - 1)) + ld; }
+};
+
+__host__ __device__ inline Seg batch_seg(int64_t N, int64_t tk0) {
+    Seg s;
+    s.N = N;
+    s.tk0 = tk0;
+    s.lsh = 0;
+    s.ld = 0;
+    s.L = root_level(N);
+    return s;
+}
+
+// Packed documents: D documents, document d at token rows [cu[d], cu[d+1]) of T. cu is
+// read clamped into [0, T], so any array keeps every access inside the buffers sized for
+// T and D (a cu that is not nondecreasing from 0 to T gives unspecified selections).
+//
+// Packed layout: per KV head, level l (1 <= l <= root_level(T)) has a region of
+// R_l = (T >> (5 + l)) + D + 1 rows; document d's level-l nodes start at its row
+// (cu[d] >> (5 + l)) + d. These starts increase with d by at least the node count, so the
+// documents never overlap, and they are found from cu alone. The same "slot" rule at other
+// granularities (2^s tokens: slot of (d, j) = (cu[d] >> s) + d + j) numbers per-document
+// work units (16-leaf subtrees, superblocks, position ranges) in one flat space.
+struct Pack {
+    const int32_t* cu;
+    int32_t D;
+    int64_t T;
+};
+
+__device__ inline int64_t pack_cu(const Pack& p, int i) {
+    const int64_t v = p.cu[i];
+    return v < 0 ? 0 : (v > p.T ? p.T : v);
+}
+
+// Slots of granularity 2^s: the last document d with (cu[d] >> s) + d <= x.
+__device__ inline int pack_find_slot(const Pack& p, int s, int64_t x) {
+    int lo = 0, hi = p.D - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((pack_cu(p, mid) >> s) + mid <= x) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// The document holding token row x (the last d with cu[d] <= x).
+__device__ inline int pack_find_token(const Pack& p, int64_t x) {
+    int lo = 0, hi = p.D - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pack_cu(p, mid) <= x) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+__device__ inline Seg pack_seg(const Pack& p, int d) {
+    const int64_t a = pack_cu(p, d), b = pack_cu(p, d + 1);
+    Seg s;
+    s.N = b > a ? b - a : 0;
+    s.tk0 = a;
+    s.lsh = a;
+    s.ld = d;
+    s.L = root_level(s.N > 0 ? s.N : 1);
+    return s;
+}
+
 // Coarse candidate levels staged in LDS by the bf16 upper-level walk: levels
 // j_lo..j_hi (none if j_lo > j_hi), node i of level j at LDS slot lds_first[j] + i, each
 // slot holding the hi and lo bf16 planes of the node's delta row (kLdsNodeBytes, padded
@@ -62,6 +151,43 @@ struct UpperCfg {
     int32_t s_level, s_first;
 };
 
+// LDS staging of one sequence's walk: the delta rows of the candidate levels from the first
+// level that can be scored (the highest with more than K nodes) downward while they fit
+// kLdsDeltaBudgetNodes, then that level's summary rows (at most 2K). lds_nodes is at most
+// kLdsDeltaBudgetNodes + 2K.
+__host__ __device__ inline void upper_cfg_for(const Seg& sg, int topk, UpperCfg& U) {
+    U.j_lo = 1;
+    U.j_hi = 0;
+    U.lds_nodes = 0;
+    U.s_level = 0;
+    U.s_first = 0;
+    int top = 0;
+    for (int l = sg.L; l >= 2; --l) {
+        if (sg.M(l) > topk) {
+            top = l;
+            break;
+        }
+    }
+    if (top < 2) return;
+    int nodes = 0, j_lo = top + 1;
+    while (j_lo - 1 >= 2 && nodes + sg.M(j_lo - 1) <= kLdsDeltaBudgetNodes) {
+        --j_lo;
+        nodes += sg.M(j_lo);
+    }
+    if (j_lo > top) return;
+    U.j_lo = j_lo;
+    U.j_hi = top;
+    int slot = 0;
+    for (int j = j_lo; j <= top; ++j) {
+        U.lds_first[j] = slot;
+        slot += sg.M(j);
+    }
+    U.s_level = top;
+    U.s_first = slot;
+    slot += sg.M(top);
+    U.lds_nodes = slot;
+}
+
 // Clustered leaf scoring (prefill): superblocks of 16 leaves; incidences are
 // bucketed by (batch, KV head, superblock, range of kRangeT query positions), so
 // that each bucket is counted and filled by one workgroup and the entries of one
@@ -70,6 +196,7 @@ struct UpperCfg {
 constexpr int kSbLeaves = 16;
 constexpr int kSbKeys = kSbLeaves * kC;           // 1024 keys
 constexpr int kRangeT = 512;                       // query positions per range
+constexpr int kLog2RangeT = 9;
 constexpr int kItemMax = 1024;                     // entries per work item
 constexpr int kClusterThreads = 1024;
 constexpr int kSbLdsBytes = kSbKeys * kD * 2;      // 128 KiB of bf16 keys

@@ -269,23 +269,39 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_f32_kernel(const flo
 
 // delta planes: row c of level l >= 2 holds hi/lo bf16 planes of
 // 2 (s_{l-1}(2c) - s_l(c)) * log2(e)/8 (the doubled delta), rounded like the summary
-// planes. Grid: (chunks, B*Hkv).
+// planes. Grid: (chunks, B * Hkv); with a pack (pk.cu non-null), (D * Hkv, chunks), one
+// row of workgroups per (document, KV head).
 __global__ __launch_bounds__(256) void delta_planes_kernel(const float* __restrict__ pyr,
-                                                           uint16_t* __restrict__ dplanes, Geom G) {
-    const int bh = blockIdx.y;
+                                                           uint16_t* __restrict__ dplanes, Geom G, Pack pk) {
+    int64_t row0;
+    Seg sg;
+    int chunk, nchunks;
+    if (pk.cu) {
+        const int d = blockIdx.x / G.Hkv;
+        sg = pack_seg(pk, d);
+        row0 = (int64_t)(blockIdx.x % G.Hkv) * G.P;
+        chunk = blockIdx.y;
+        nchunks = gridDim.y;
+        if (sg.N == 0) return;
+    } else {
+        sg = batch_seg(G.N, 0);
+        row0 = (int64_t)blockIdx.y * G.P;
+        chunk = blockIdx.x;
+        nchunks = gridDim.x;
+    }
     int64_t total = 0;
-    for (int l = 2; l <= G.L; ++l) total += (int64_t)G.M[l] * kD;
+    for (int l = 2; l <= sg.L; ++l) total += (int64_t)sg.M(l) * kD;
     const int64_t plane_stride = (int64_t)G.B * G.Hkv * G.P * kD;
-    const float* base = pyr + (int64_t)bh * G.P * kD;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const float* base = pyr + row0 * kD;
+    for (int64_t i = (int64_t)chunk * 256 + threadIdx.x; i < total; i += (int64_t)nchunks * 256) {
         const int e = (int)(i & (kD - 1));
         int64_t r = i >> 6;
         int l = 2;
-        while (r >= G.M[l]) { r -= G.M[l]; ++l; }
-        const int64_t prow = G.off[l] + r, crow = G.off[l - 1] + 2 * r;
+        while (r >= sg.M(l)) { r -= sg.M(l); ++l; }
+        const int64_t prow = G.off[l] + sg.shift(l) + r, crow = G.off[l - 1] + sg.shift(l - 1) + 2 * r;
         uint32_t hi, lo;
         split_scaled(2.0f * (base[crow * kD + e] - base[prow * kD + e]), hi, lo);
-        const int64_t o = ((int64_t)bh * G.P + prow) * kD + e;
+        const int64_t o = (row0 + prow) * kD + e;
         dplanes[o] = (uint16_t)hi;
         dplanes[plane_stride + o] = (uint16_t)lo;
     }
@@ -298,22 +314,11 @@ __global__ __launch_bounds__(256) void delta_planes_kernel(const float* __restri
 template <int SLOTS>
 __device__ constexpr int dslot_lane(int w, int m) { return w * SLOTS + m; }
 
-template <int SLOTS, int S>
-__global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const uint16_t* __restrict__ q,
-                                                                         const uint16_t* __restrict__ splanes,
-                                                                         const uint16_t* __restrict__ dplanes,
-                                                                         Geom G, UpperCfg U, int64_t t0, int64_t NT,
-                                                                         int32_t* __restrict__ cand_out,
-                                                                         int32_t* __restrict__ ncand_out) {
-    constexpr int WPW = 64 / SLOTS, TPW = SLOTS / 16, NTILE = WPW * TPW;
-    static_assert(NTILE == 4, "four 16-row tiles per wavefront");
-    extern __shared__ u32x4 lds_u4[];
-    lds_char_t* lds = (lds_char_t*)lds_u4;
-    // XCD-aware placement: workgroup i runs on XCD i % 8; when B*Hkv divides 8, every
-    // XCD serves a single (batch, KV head), so its L2 holds that head's finer levels only.
-    const int BH = G.B * G.Hkv;
+// XCD-aware placement of the walk workgroups: workgroup i runs on XCD i % 8; when B*Hkv
+// divides 8, every XCD serves a single (batch, KV head), so its L2 holds that head's finer
+// levels only.
+__device__ inline void upper_placement(int BH, int& bh, int& peer, int& npeers) {
     const int id = blockIdx.x, nwg = gridDim.x;
-    int bh, peer, npeers;
     if (BH <= 8 && 8 % BH == 0 && nwg % 8 == 0) {
         bh = (id % 8) % BH;
         peer = (id / 8) * (8 / BH) + (id % 8) / BH;
@@ -323,40 +328,52 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const u
         peer = id / BH;
         npeers = (nwg - bh + BH - 1) / BH;
     }
-    const int b = bh / G.Hkv, kvh = bh % G.Hkv;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-    const int gq = lane >> 4, n = lane & 15;
-    const int u = gq;                                        // tile whose results land in this lane
-    const int wl = lane / SLOTS;                             // this lane's walk
-    const int ml = lane % SLOTS;                             // this lane's slot
-    const int K = G.topk;
-    const int64_t plane_stride = (int64_t)G.B * G.Hkv * G.P * kD;
-    const int64_t bh_row0 = (int64_t)bh * G.P;
+}
 
-    // stage the delta rows of the coarse candidate levels: node i of level j -> LDS slot
-    // lds_first[j] + i, planes hi|lo
+// Stage one sequence's rows (U) in LDS, node i of level j -> LDS slot lds_first[j] + i,
+// planes hi|lo; the caller synchronises.
+__device__ inline void stage_upper_lds(lds_char_t* lds, const uint16_t* __restrict__ splanes,
+                                       const uint16_t* __restrict__ dplanes, const Geom& G, const UpperCfg& U,
+                                       const Seg& sg, int64_t bh_row0, int64_t plane_stride) {
     for (int j = U.j_lo; j <= U.j_hi; ++j) {
-        const int mj = G.M[j];
+        const int mj = sg.M(j);
+        const int64_t r0 = bh_row0 + G.off[j] + sg.shift(j);
         for (int c = threadIdx.x; c < mj * 16; c += blockDim.x) {
             const int node = c >> 4, part = c & 15;
-            const uint16_t* src = dplanes + (part >> 3) * plane_stride + (bh_row0 + G.off[j] + node) * kD +
-                                  (part & 7) * 8;
+            const uint16_t* src = dplanes + (part >> 3) * plane_stride + (r0 + node) * kD + (part & 7) * 8;
             *reinterpret_cast<lds_u32x4_t*>(lds + (U.lds_first[j] + node) * kLdsNodeBytes + (part >> 3) * 128 +
                                             (part & 7) * 16) = *reinterpret_cast<const u32x4*>(src);
         }
     }
     if (U.s_level >= 2) {
-        const int ms = G.M[U.s_level];
+        const int ms = sg.M(U.s_level);
+        const int64_t r0 = bh_row0 + G.off[U.s_level] + sg.shift(U.s_level);
         for (int c = threadIdx.x; c < ms * 16; c += blockDim.x) {
             const int node = c >> 4, part = c & 15;
-            const uint16_t* src = splanes + (part >> 3) * plane_stride + (bh_row0 + G.off[U.s_level] + node) * kD +
-                                  (part & 7) * 8;
+            const uint16_t* src = splanes + (part >> 3) * plane_stride + (r0 + node) * kD + (part & 7) * 8;
             *reinterpret_cast<lds_u32x4_t*>(lds + (U.s_first + node) * kLdsNodeBytes + (part >> 3) * 128 +
                                             (part & 7) * 16) = *reinterpret_cast<const u32x4*>(src);
         }
     }
-    __syncthreads();
+}
 
+// The walks of one wavefront: positions t0 + grp * WPW + w (w < WPW, grp * WPW + w < NT) of
+// sequence sg, whose queries (and walk records) are rows qrow0 + grp * WPW + w.
+template <int SLOTS, int S>
+__device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const uint16_t* __restrict__ splanes,
+                                         const uint16_t* __restrict__ dplanes, const Geom& G, const UpperCfg& U,
+                                         const Seg& sg, const lds_char_t* lds, int64_t bh_row0,
+                                         int64_t plane_stride, int kvh, int64_t qrow0, int64_t t0, int64_t NT,
+                                         int64_t grp, int32_t* __restrict__ cand_out,
+                                         int32_t* __restrict__ ncand_out) {
+    constexpr int WPW = 64 / SLOTS, TPW = SLOTS / 16, NTILE = WPW * TPW;
+    static_assert(NTILE == 4, "four 16-row tiles per wavefront");
+    const int lane = threadIdx.x & 63;
+    const int gq = lane >> 4, n = lane & 15;
+    const int u = gq;                                        // tile whose results land in this lane
+    const int wl = lane / SLOTS;                             // this lane's walk
+    const int ml = lane % SLOTS;                             // this lane's slot
+    const int K = G.topk;
     uint64_t wmask[WPW];
 #pragma unroll
     for (int w = 0; w < WPW; ++w) {
@@ -365,165 +382,234 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const u
         wmask[w] = mk;
     }
 
-    const int64_t ngroups = (NT + WPW - 1) / WPW;
-    for (int64_t grp = (int64_t)peer * nwaves + wave; grp < ngroups; grp += (int64_t)npeers * nwaves) {
-        UpperQ<uint16_t> qf[WPW];
-        int64_t tw[WPW];
+    UpperQ<uint16_t> qf[WPW];
+    int64_t tw[WPW];
 #pragma unroll
-        for (int w = 0; w < WPW; ++w) {
-            const int64_t ti = grp * WPW + w;
-            tw[w] = t0 + ti;
-            const bool ok = ti < NT && n < G.GQ;
-            const uint16_t* qrow = q + (((int64_t)b * NT + (ti < NT ? ti : 0)) * G.Hq + (int64_t)kvh * G.GQ + n) * kD;
-            qf[w].load(qrow, ok, gq);
-        }
-        const int64_t my_ti = grp * WPW + wl;
-        const int64_t my_t = t0 + my_ti;
-        const bool my_ok = my_ti < NT;
+    for (int w = 0; w < WPW; ++w) {
+        const int64_t ti = grp * WPW + w;
+        tw[w] = t0 + ti;
+        const bool ok = ti < NT && n < G.GQ;
+        const uint16_t* qrow = q + ((qrow0 + (ti < NT ? ti : 0)) * G.Hq + (int64_t)kvh * G.GQ + n) * kD;
+        qf[w].load(qrow, ok, gq);
+    }
+    const int64_t my_ti = grp * WPW + wl;
+    const int64_t my_t = t0 + my_ti;
+    const bool my_ok = my_ti < NT;
 
-        uint32_t surv_low = 0;     // sorted key low word in slots < K: the survivors
-        float Pa = 0.0f, Pb = 0.0f;  // head-summed logits of this slot's candidate's children
-        uint32_t pk = 0;           // walks whose candidates' P is known (scored at the level above)
-        for (int l = G.L; l >= 2; --l) {
-            int cand;
-            float P = 0.0f;
-            if (l == G.L) {
-                cand = (ml == 0 && my_ok) ? 0 : -1;
-            } else {
-                const uint32_t lowk = (uint32_t)shfl_i((int)surv_low, dslot_lane<SLOTS>(wl, ml >> 1));
-                const int pnode = key_node(lowk);
-                const int child = 2 * pnode + (ml & 1);
-                const bool ok = ml < 2 * K && pnode >= 0 && child < G.M[l] &&
-                                child <= (int)(my_t >> (kLog2C + l - 1));
-                cand = ok ? child : -1;
-                const int src = dslot_lane<SLOTS>(wl, key_slot(lowk));
-                const float pa = shfl_f(Pa, src), pb = shfl_f(Pb, src);
-                P = (ml & 1) ? pb : pa;
-            }
-            const uint64_t vm = ballot(cand >= 0);
-            uint32_t scored = 0;
-#pragma unroll
-            for (int w = 0; w < WPW; ++w) scored |= (__popcll(vm & wmask[w]) > K) ? (1u << w) : 0u;
-            float score = 0.0f;
-            Pa = 0.0f;
-            Pb = 0.0f;
-            if (scored) {
-                const int lc = l - 1;
-                const int shc = kLog2C + lc - 1;            // first key of a level-lc node i: i << shc
-                const int Mc = G.M[lc];
-                // candidate of MFMA column n of tile i (lane 16i + n)
-                auto row_cand = [&](int i) -> int { return shfl_i(cand, 16 * i + n); };
-                // (1) P of the candidates of walks that were not scored at the level above:
-                // head sums of the logits of the candidates' own summaries
-                const uint32_t need_p = scored & ~pk;
-                if (need_p) {
-                    const bool s_lds = l == U.s_level;
-#pragma unroll
-                    for (int i = 0; i < NTILE; ++i) {
-                        const int c = row_cand(i);
-                        const int cc = (c >= 0) ? c : 0;
-                        const TileRows r = s_lds ? rows_lds(lds, U.s_first + cc, gq)
-                                                 : rows_global(splanes + (bh_row0 + G.off[l] + cc) * kD, plane_stride, gq);
-                        const f32x4 acc = summary_tile_mfma(qf[i / TPW].k0, qf[i / TPW].k1, r.h0, r.h1, r.l0, r.l1);
-                        const float ps = tile_head_sums(acc, gq, G.GQ);
-                        if (u == i && ((need_p >> wl) & 1)) P = ps;
-                    }
-                }
-                // (2) the delta tiles, the next tile's row in flight
-                const bool in_lds = l >= U.j_lo && l <= U.j_hi;
-                const int lds_lvl = in_lds ? U.lds_first[l] : 0;
-                const uint16_t* dplane_lvl = dplanes + (bh_row0 + G.off[l]) * kD;
-                auto pick = [&](int i, int& row) -> uint32_t {
-                    const int c = row_cand(i);
-                    const int rc = 2 * c + 1;                 // right child
-                    const bool rv = c >= 0 && rc < Mc && rc <= (int)(tw[i / TPW] >> shc);
-                    row = (c >= 0) ? c : 0;
-                    return (uint32_t)ballot(rv);              // bit n: column n has an eligible right child
-                };
-                auto fetch = [&](int row) -> TileRows {
-                    if (in_lds) return rows_lds(lds, lds_lvl + row, gq);
-                    return rows_global(dplane_lvl + (int64_t)row * kD, plane_stride, gq);
-                };
-                float F = 0.0f, D = 0.0f;
-                int row0;
-                uint32_t rvm = pick(0, row0);
-                TileRows cur = fetch(row0);
-#pragma unroll
-                for (int i = 0; i < NTILE; ++i) {
-                    TileRows nxt = cur;
-                    uint32_t rvm_next = 0;
-                    if (i + 1 < NTILE) {
-                        int rown;
-                        rvm_next = pick(i + 1, rown);
-                        nxt = fetch(rown);
-                    }
-                    const f32x4 acc = summary_tile_mfma(qf[i / TPW].k0, qf[i / TPW].k1, cur.h0, cur.h1, cur.l0, cur.l1);
-                    float Ft, Dt;
-                    delta_tile_sums<S>(acc, rvm, n, gq, G.GQ, Ft, Dt);
-                    if (u == i) {
-                        F = Ft;
-                        D = Dt;
-                    }
-                    cur = nxt;
-                    rvm = rvm_next;
-                }
-                score = P + F;
-                Pa = P + D;
-                Pb = P - D;
-                // (3) the ragged node of level l (a partial right child): its two children are
-                // read directly when a walk has it as a candidate with an eligible right child
-                const int crag = G.M[l] - 1, brag = 2 * crag + 1;
-                if (brag < Mc && covered(lc, brag, G.N) < span_of(lc)) {
-                    const bool is_rag = cand == crag && brag <= (int)(my_t >> shc);
-                    const uint64_t rm = ballot(is_rag);
-#pragma unroll
-                    for (int w = 0; w < WPW; ++w) {
-                        if (rm & wmask[w]) {
-                            const int crow = (n == 1) ? brag : brag - 1;   // column 0: left child, 1: right
-                            const TileRows r = rows_global(splanes + (bh_row0 + G.off[lc] + crow) * kD, plane_stride, gq);
-                            const f32x4 acc = summary_tile_mfma(qf[w].k0, qf[w].k1, r.h0, r.h1, r.l0, r.l1);
-                            float xf, xp;
-                            ragged_sums<S>(acc, gq, G.GQ, xf, xp);
-                            const float f_fix = readlane_f(xf, 0), pa_fix = readlane_f(xp, 0), pb_fix = readlane_f(xp, 1);
-                            if (is_rag && wl == w) {
-                                score = f_fix;
-                                Pa = pa_fix;
-                                Pb = pb_fix;
-                            }
-                        }
-                    }
-                }
-            }
-            pk = scored;
-            // walks with at most K candidates keep them all whatever their scores
-            const uint64_t key = slot_key((cand >= 0) ? score : -INFINITY, cand, ml);
-            // the survivors are the K best as a set; with 2K = SLOTS a partial network finds them
-            const uint64_t sorted = (2 * K == SLOTS) ? bitonic_top_half<SLOTS, SegmentLanes>(key, ml)
-                                                     : bitonic_desc<SLOTS, SegmentLanes>(key, ml);
-            surv_low = (ml < K) ? (uint32_t)sorted : 0u;
-        }
-        // leaf candidates: children of the level-2 survivors (or the root if it is a leaf)
-        int leaf;
-        if (G.L == 1) {
-            leaf = (ml == 0 && my_ok) ? 0 : -1;
+    uint32_t surv_low = 0;     // sorted key low word in slots < K: the survivors
+    float Pa = 0.0f, Pb = 0.0f;  // head-summed logits of this slot's candidate's children
+    uint32_t pk = 0;           // walks whose candidates' P is known (scored at the level above)
+    for (int l = sg.L; l >= 2; --l) {
+        int cand;
+        float P = 0.0f;
+        if (l == sg.L) {
+            cand = (ml == 0 && my_ok) ? 0 : -1;
         } else {
             const uint32_t lowk = (uint32_t)shfl_i((int)surv_low, dslot_lane<SLOTS>(wl, ml >> 1));
             const int pnode = key_node(lowk);
             const int child = 2 * pnode + (ml & 1);
-            const bool ok = ml < 2 * K && pnode >= 0 && child < G.M[1] && child <= (int)(my_t >> kLog2C);
-            leaf = ok ? child : -1;
+            const bool ok = ml < 2 * K && pnode >= 0 && child < sg.M(l) &&
+                            child <= (int)(my_t >> (kLog2C + l - 1));
+            cand = ok ? child : -1;
+            const int src = dslot_lane<SLOTS>(wl, key_slot(lowk));
+            const float pa = shfl_f(Pa, src), pb = shfl_f(Pb, src);
+            P = (ml & 1) ? pb : pa;
         }
-        // ascending order, -1 last
-        const int nd = index_sort<SLOTS, SegmentLanes>((leaf >= 0) ? leaf : INT_MAX, ml);
-        leaf = (nd != INT_MAX && ml < 2 * K) ? nd : -1;
-        const uint64_t lm = ballot(leaf >= 0);
-        uint64_t mine = 0;
+        const uint64_t vm = ballot(cand >= 0);
+        uint32_t scored = 0;
 #pragma unroll
-        for (int w = 0; w < WPW; ++w) mine = (wl == w) ? wmask[w] : mine;
-        if (my_ok && ml < 2 * K) {
-            const int64_t wid = ((int64_t)b * NT + my_ti) * G.Hkv + kvh;
-            cand_out[wid * (2 * K) + ml] = leaf;
-            if (ml == 0) ncand_out[wid] = __popcll(lm & mine);
+        for (int w = 0; w < WPW; ++w) scored |= (__popcll(vm & wmask[w]) > K) ? (1u << w) : 0u;
+        float score = 0.0f;
+        Pa = 0.0f;
+        Pb = 0.0f;
+        if (scored) {
+            const int lc = l - 1;
+            const int shc = kLog2C + lc - 1;            // first key of a level-lc node i: i << shc
+            const int Mc = sg.M(lc);
+            const int64_t row_l = bh_row0 + G.off[l] + sg.shift(l);
+            const int64_t row_lc = bh_row0 + G.off[lc] + sg.shift(lc);
+            // candidate of MFMA column n of tile i (lane 16i + n)
+            auto row_cand = [&](int i) -> int { return shfl_i(cand, 16 * i + n); };
+            // (1) P of the candidates of walks that were not scored at the level above:
+            // head sums of the logits of the candidates' own summaries
+            const uint32_t need_p = scored & ~pk;
+            if (need_p) {
+                const bool s_lds = l == U.s_level;
+#pragma unroll
+                for (int i = 0; i < NTILE; ++i) {
+                    const int c = row_cand(i);
+                    const int cc = (c >= 0) ? c : 0;
+                    const TileRows r = s_lds ? rows_lds(lds, U.s_first + cc, gq)
+                                             : rows_global(splanes + (row_l + cc) * kD, plane_stride, gq);
+                    const f32x4 acc = summary_tile_mfma(qf[i / TPW].k0, qf[i / TPW].k1, r.h0, r.h1, r.l0, r.l1);
+                    const float ps = tile_head_sums(acc, gq, G.GQ);
+                    if (u == i && ((need_p >> wl) & 1)) P = ps;
+                }
+            }
+            // (2) the delta tiles, the next tile's row in flight
+            const bool in_lds = l >= U.j_lo && l <= U.j_hi;
+            const int lds_lvl = in_lds ? U.lds_first[l] : 0;
+            const uint16_t* dplane_lvl = dplanes + row_l * kD;
+            auto pick = [&](int i, int& row) -> uint32_t {
+                const int c = row_cand(i);
+                const int rc = 2 * c + 1;                 // right child
+                const bool rv = c >= 0 && rc < Mc && rc <= (int)(tw[i / TPW] >> shc);
+                row = (c >= 0) ? c : 0;
+                return (uint32_t)ballot(rv);              // bit n: column n has an eligible right child
+            };
+            auto fetch = [&](int row) -> TileRows {
+                if (in_lds) return rows_lds(lds, lds_lvl + row, gq);
+                return rows_global(dplane_lvl + (int64_t)row * kD, plane_stride, gq);
+            };
+            float F = 0.0f, D = 0.0f;
+            int row0;
+            uint32_t rvm = pick(0, row0);
+            TileRows cur = fetch(row0);
+#pragma unroll
+            for (int i = 0; i < NTILE; ++i) {
+                TileRows nxt = cur;
+                uint32_t rvm_next = 0;
+                if (i + 1 < NTILE) {
+                    int rown;
+                    rvm_next = pick(i + 1, rown);
+                    nxt = fetch(rown);
+                }
+                const f32x4 acc = summary_tile_mfma(qf[i / TPW].k0, qf[i / TPW].k1, cur.h0, cur.h1, cur.l0, cur.l1);
+                float Ft, Dt;
+                delta_tile_sums<S>(acc, rvm, n, gq, G.GQ, Ft, Dt);
+                if (u == i) {
+                    F = Ft;
+                    D = Dt;
+                }
+                cur = nxt;
+                rvm = rvm_next;
+            }
+            score = P + F;
+            Pa = P + D;
+            Pb = P - D;
+            // (3) the ragged node of level l (a partial right child): its two children are
+            // read directly when a walk has it as a candidate with an eligible right child
+            const int crag = sg.M(l) - 1, brag = 2 * crag + 1;
+            if (brag < Mc && covered(lc, brag, sg.N) < span_of(lc)) {
+                const bool is_rag = cand == crag && brag <= (int)(my_t >> shc);
+                const uint64_t rm = ballot(is_rag);
+#pragma unroll
+                for (int w = 0; w < WPW; ++w) {
+                    if (rm & wmask[w]) {
+                        const int crow = (n == 1) ? brag : brag - 1;   // column 0: left child, 1: right
+                        const TileRows r = rows_global(splanes + (row_lc + crow) * kD, plane_stride, gq);
+                        const f32x4 acc = summary_tile_mfma(qf[w].k0, qf[w].k1, r.h0, r.h1, r.l0, r.l1);
+                        float xf, xp;
+                        ragged_sums<S>(acc, gq, G.GQ, xf, xp);
+                        const float f_fix = readlane_f(xf, 0), pa_fix = readlane_f(xp, 0), pb_fix = readlane_f(xp, 1);
+                        if (is_rag && wl == w) {
+                            score = f_fix;
+                            Pa = pa_fix;
+                            Pb = pb_fix;
+                        }
+                    }
+                }
+            }
+        }
+        pk = scored;
+        // walks with at most K candidates keep them all whatever their scores
+        const uint64_t key = slot_key((cand >= 0) ? score : -INFINITY, cand, ml);
+        // the survivors are the K best as a set; with 2K = SLOTS a partial network finds them
+        const uint64_t sorted = (2 * K == SLOTS) ? bitonic_top_half<SLOTS, SegmentLanes>(key, ml)
+                                                 : bitonic_desc<SLOTS, SegmentLanes>(key, ml);
+        surv_low = (ml < K) ? (uint32_t)sorted : 0u;
+    }
+    // leaf candidates: children of the level-2 survivors (or the root if it is a leaf)
+    int leaf;
+    if (sg.L == 1) {
+        leaf = (ml == 0 && my_ok) ? 0 : -1;
+    } else {
+        const uint32_t lowk = (uint32_t)shfl_i((int)surv_low, dslot_lane<SLOTS>(wl, ml >> 1));
+        const int pnode = key_node(lowk);
+        const int child = 2 * pnode + (ml & 1);
+        const bool ok = ml < 2 * K && pnode >= 0 && child < sg.M(1) && child <= (int)(my_t >> kLog2C);
+        leaf = ok ? child : -1;
+    }
+    // ascending order, -1 last
+    const int nd = index_sort<SLOTS, SegmentLanes>((leaf >= 0) ? leaf : INT_MAX, ml);
+    leaf = (nd != INT_MAX && ml < 2 * K) ? nd : -1;
+    const uint64_t lm = ballot(leaf >= 0);
+    uint64_t mine = 0;
+#pragma unroll
+    for (int w = 0; w < WPW; ++w) mine = (wl == w) ? wmask[w] : mine;
+    if (my_ok && ml < 2 * K) {
+        const int64_t wid = (qrow0 + my_ti) * G.Hkv + kvh;
+        cand_out[wid * (2 * K) + ml] = leaf;
+        if (ml == 0) ncand_out[wid] = __popcll(lm & mine);
+    }
+}
+
+// bf16 walks of every batch element: positions t0 + ti, ti in [0, NT), query rows b*NT + ti.
+template <int SLOTS, int S>
+__global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const uint16_t* __restrict__ q,
+                                                                         const uint16_t* __restrict__ splanes,
+                                                                         const uint16_t* __restrict__ dplanes,
+                                                                         Geom G, UpperCfg U, int64_t t0, int64_t NT,
+                                                                         int32_t* __restrict__ cand_out,
+                                                                         int32_t* __restrict__ ncand_out) {
+    constexpr int WPW = 64 / SLOTS;
+    extern __shared__ u32x4 lds_u4[];
+    lds_char_t* lds = (lds_char_t*)lds_u4;
+    int bh, peer, npeers;
+    upper_placement(G.B * G.Hkv, bh, peer, npeers);
+    const int b = bh / G.Hkv, kvh = bh % G.Hkv;
+    const int wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+    const int64_t plane_stride = (int64_t)G.B * G.Hkv * G.P * kD;
+    const int64_t bh_row0 = (int64_t)bh * G.P;
+    const Seg sg = batch_seg(G.N, 0);
+    stage_upper_lds(lds, splanes, dplanes, G, U, sg, bh_row0, plane_stride);
+    __syncthreads();
+    const int64_t ngroups = (NT + WPW - 1) / WPW;
+    for (int64_t grp = (int64_t)peer * nwaves + wave; grp < ngroups; grp += (int64_t)npeers * nwaves)
+        upper_delta_group<SLOTS, S>(q, splanes, dplanes, G, U, sg, lds, bh_row0, plane_stride, kvh, (int64_t)b * NT,
+                                    t0, NT, grp, cand_out, ncand_out);
+}
+
+// bf16 walks of a pack of documents (G: the packed layout, B = 1, N = T). The tokens are
+// cut into pieces of kRangeT; the workgroups of a KV head take every npeers-th piece (so
+// each holds early and late positions of long documents alike), and walk the document
+// parts of a piece with that document's rows staged in LDS (restaged only when the
+// document changes).
+template <int SLOTS, int S>
+__global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_pack_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ splanes, const uint16_t* __restrict__ dplanes,
+    Geom G, Pack pk, int32_t* __restrict__ cand_out, int32_t* __restrict__ ncand_out) {
+    constexpr int WPW = 64 / SLOTS;
+    extern __shared__ u32x4 lds_u4[];
+    lds_char_t* lds = (lds_char_t*)lds_u4;
+    __shared__ UpperCfg s_U;
+    int kvh, peer, npeers;
+    upper_placement(G.Hkv, kvh, peer, npeers);
+    const int wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+    const int64_t plane_stride = (int64_t)G.Hkv * G.P * kD;
+    const int64_t bh_row0 = (int64_t)kvh * G.P;
+    const int64_t npieces = (pk.T + kRangeT - 1) / kRangeT;
+    int staged = -1;
+    for (int64_t p = peer; p < npieces; p += npeers) {
+        const int64_t a = p * kRangeT, e = (a + kRangeT < pk.T) ? a + kRangeT : pk.T;
+        for (int d = pack_find_token(pk, a); d < pk.D; ++d) {
+            const Seg sg = pack_seg(pk, d);
+            const int64_t da = sg.lsh, db = da + sg.N;
+            if (da >= e) break;
+            if (sg.N == 0 || db <= a) continue;
+            if (d != staged) {
+                __syncthreads();   // every wavefront is done with the previous document's rows
+                if (threadIdx.x == 0) upper_cfg_for(sg, G.topk, s_U);
+                __syncthreads();
+                stage_upper_lds(lds, splanes, dplanes, G, s_U, sg, bh_row0, plane_stride);
+                __syncthreads();
+                staged = d;
+            }
+            const int64_t lo = (a > da ? a : da) - da, hi = (e < db ? e : db) - da;
+            const int64_t NT = hi - lo, ngroups = (NT + WPW - 1) / WPW;
+            for (int64_t grp = wave; grp < ngroups; grp += nwaves)
+                upper_delta_group<SLOTS, S>(q, splanes, dplanes, G, s_U, sg, lds, bh_row0, plane_stride, kvh,
+                                            da + lo, lo, NT, grp, cand_out, ncand_out);
         }
     }
 }
@@ -537,6 +623,15 @@ template __global__ void walk_upper_delta_kernel<32, kScoreMeanHalfVar>(const ui
 template __global__ void walk_upper_delta_kernel<64, kScoreLse>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg, int64_t, int64_t, int32_t*, int32_t*);
 template __global__ void walk_upper_delta_kernel<64, kScoreMean>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg, int64_t, int64_t, int32_t*, int32_t*);
 template __global__ void walk_upper_delta_kernel<64, kScoreMeanHalfVar>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg, int64_t, int64_t, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_pack_kernel<16, kScoreLse>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_pack_kernel<16, kScoreMean>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_pack_kernel<16, kScoreMeanHalfVar>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_pack_kernel<32, kScoreLse>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_pack_kernel<32, kScoreMean>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_pack_kernel<32, kScoreMeanHalfVar>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_pack_kernel<64, kScoreLse>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_pack_kernel<64, kScoreMean>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_pack_kernel<64, kScoreMeanHalfVar>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int32_t*, int32_t*);
 template __global__ void walk_upper_f32_kernel<16, kScoreLse>(const float*, const float*, Geom, int64_t, int64_t, int32_t*, int32_t*);
 template __global__ void walk_upper_f32_kernel<16, kScoreMean>(const float*, const float*, Geom, int64_t, int64_t, int32_t*, int32_t*);
 template __global__ void walk_upper_f32_kernel<16, kScoreMeanHalfVar>(const float*, const float*, Geom, int64_t, int64_t, int32_t*, int32_t*);

@@ -28,7 +28,9 @@ PISA_DTYPE_BF16 = 1
 
 EXPORTED = ("pisa_pyramid_nodes", "pisa_level_offset", "pisa_pyramid_bytes", "pisa_workspace_bytes",
             "pisa_build_pyramid", "pisa_select_prefill", "pisa_select_prefill_profiled",
-            "pisa_decode_update_select", "pisa_status_string")
+            "pisa_decode_update_select", "pisa_status_string", "pisa_pack_pyramid_rows",
+            "pisa_pack_level_offset", "pisa_pack_pyramid_bytes", "pisa_pack_workspace_bytes",
+            "pisa_build_pyramid_packed", "pisa_select_prefill_packed")
 
 
 class Dims(ctypes.Structure):
@@ -70,6 +72,18 @@ def _load() -> ctypes.CDLL:
     lib.pisa_select_prefill_profiled.restype = ctypes.c_int
     lib.pisa_decode_update_select.argtypes = [P, P, P, P, i64, i64, D, P, P, sz, P]
     lib.pisa_decode_update_select.restype = ctypes.c_int
+    lib.pisa_pack_pyramid_rows.argtypes = [D, i64, i64]
+    lib.pisa_pack_pyramid_rows.restype = i64
+    lib.pisa_pack_level_offset.argtypes = [D, i64, i64, i32]
+    lib.pisa_pack_level_offset.restype = i64
+    lib.pisa_pack_pyramid_bytes.argtypes = [D, i64, i64]
+    lib.pisa_pack_pyramid_bytes.restype = sz
+    lib.pisa_pack_workspace_bytes.argtypes = [D, i64, i64]
+    lib.pisa_pack_workspace_bytes.restype = sz
+    lib.pisa_build_pyramid_packed.argtypes = [P, P, i64, i64, D, P, P]
+    lib.pisa_build_pyramid_packed.restype = ctypes.c_int
+    lib.pisa_select_prefill_packed.argtypes = [P, P, P, P, i64, i64, D, P, P, sz, P]
+    lib.pisa_select_prefill_packed.restype = ctypes.c_int
     lib.pisa_status_string.argtypes = [ctypes.c_int]
     lib.pisa_status_string.restype = ctypes.c_char_p
     return lib
@@ -191,3 +205,58 @@ def decode_update_select(q_new: torch.Tensor, k_new: torch.Tensor, k_cache: torc
                                        ws_n, _stream(stream))
     if rc != PISA_OK:
         raise PisaError("pisa_decode_update_select", rc)
+
+
+# ------------------------------------------------------------------ packed documents --
+# D documents laid end to end in T token rows; cu_seqlens (int32 device tensor [D + 1])
+# holds their first rows and T. Each document is selected as a sequence of its own
+# (positions and leaf indices counted from its start). dims.B must be 1.
+
+def pack_pyramid_rows(dims: Dims, T: int, D: int) -> int:
+    return int(lib.pisa_pack_pyramid_rows(ctypes.byref(dims), T, D))
+
+
+def pack_level_offset(dims: Dims, T: int, D: int, level: int) -> int:
+    return int(lib.pisa_pack_level_offset(ctypes.byref(dims), T, D, level))
+
+
+def pack_workspace_bytes(dims: Dims, T: int, D: int) -> int:
+    return int(lib.pisa_pack_workspace_bytes(ctypes.byref(dims), T, D))
+
+
+def alloc_pack_pyramid(dims: Dims, T: int, D: int, device="cuda") -> torch.Tensor:
+    return torch.empty((dims.Hkv, pack_pyramid_rows(dims, T, D), dims.d), dtype=torch.float32, device=device)
+
+
+def alloc_pack_workspace(dims: Dims, T: int, D: int, device="cuda") -> Optional[torch.Tensor]:
+    n = pack_workspace_bytes(dims, T, D)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def build_pyramid_packed(k: torch.Tensor, cu_seqlens: torch.Tensor, dims: Dims, pyramid: torch.Tensor,
+                         stream=None) -> None:
+    D, T = cu_seqlens.numel() - 1, k.shape[0]
+    _check(k, "k", dims.torch_dtype, T * dims.Hkv * dims.d)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, D + 1)
+    _check(pyramid, "pyramid", torch.float32, dims.Hkv * pack_pyramid_rows(dims, T, D) * dims.d)
+    rc = lib.pisa_build_pyramid_packed(_ptr(k), _ptr(cu_seqlens), D, T, ctypes.byref(dims), _ptr(pyramid),
+                                       _stream(stream))
+    if rc != PISA_OK:
+        raise PisaError("pisa_build_pyramid_packed", rc)
+
+
+def select_prefill_packed(q: torch.Tensor, k: torch.Tensor, pyramid: torch.Tensor, cu_seqlens: torch.Tensor,
+                          dims: Dims, out_idx: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                          stream=None) -> None:
+    D, T = cu_seqlens.numel() - 1, q.shape[0]
+    _check(q, "q", dims.torch_dtype, T * dims.Hq * dims.d)
+    _check(k, "k", dims.torch_dtype, T * dims.Hkv * dims.d)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, D + 1)
+    _check(pyramid, "pyramid", torch.float32, dims.Hkv * pack_pyramid_rows(dims, T, D) * dims.d)
+    _check(out_idx, "out_idx", torch.int32, T * dims.Hkv * dims.topk)
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.pisa_select_prefill_packed(_ptr(q), _ptr(k), _ptr(pyramid), _ptr(cu_seqlens), D, T,
+                                        ctypes.byref(dims), _ptr(out_idx), _ptr(workspace), ws_n,
+                                        _stream(stream))
+    if rc != PISA_OK:
+        raise PisaError("pisa_select_prefill_packed", rc)

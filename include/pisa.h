@@ -173,6 +173,60 @@ int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cach
                               const pisa_dims* dims, int32_t* out_idx, void* workspace,
                               size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------ packed documents
+ *
+ * Packed inputs (reading note "Block Sparse Attention with Log-Linear
+ * Complexity", "Experiments: language modelling and downstream", the
+ * continued-pretraining settings: packed inputs keep the document boundaries
+ * and no document attends into another). D documents lie
+ * end to end in T token rows; cu_seqlens is a DEVICE int32 array [D + 1]:
+ * document i holds rows cu_seqlens[i] .. cu_seqlens[i+1] - 1, cu_seqlens[0] = 0,
+ * cu_seqlens[D] = T, nondecreasing (empty documents allowed). Each document is
+ * selected as a sequence of its own: its own pyramid over its own keys, query
+ * positions and leaf indices counted from the document's first row. dims->B
+ * must be 1 (INVALID_ARG otherwise). cu_seqlens values are read clamped into
+ * [0, T]: an array that breaks the rules above gives unspecified selections,
+ * but every access stays inside the buffers sized for T and D.
+ *
+ * Packed pyramid layout: fp32 [Hkv, pisa_pack_pyramid_rows(T, D), d]. Level l
+ * (1 <= l <= L(T), L(T) the root level of T keys) is a region of
+ * (T >> (5 + l)) + D + 1 rows starting at pisa_pack_level_offset(T, D, l); in
+ * it, node i of document j's level l is row (cu_seqlens[j] >> (5 + l)) + j + i.
+ * Rows no document owns are never written or read.
+ */
+
+/* Rows per KV head of the packed layout for T tokens in D documents (-1 on bad input). */
+int64_t pisa_pack_pyramid_rows(const pisa_dims* dims, int64_t T, int64_t D);
+/* First row of level `level`'s region (-1 on bad input or a level above L(T)). */
+int64_t pisa_pack_level_offset(const pisa_dims* dims, int64_t T, int64_t D, int32_t level);
+/* Bytes of the packed pyramid (0 on bad input). */
+size_t pisa_pack_pyramid_bytes(const pisa_dims* dims, int64_t T, int64_t D);
+/* Device workspace of pisa_select_prefill_packed (0 on bad input). */
+size_t pisa_pack_workspace_bytes(const pisa_dims* dims, int64_t T, int64_t D);
+
+/*
+ * Builds every document's mean pyramid (section 3.1, per document) into the
+ * packed layout. k: [T, Hkv, d] of dims->dtype (bf16 or fp32). Every node is
+ * bitwise what pisa_build_pyramid writes for that document alone.
+ */
+int pisa_build_pyramid_packed(const void* k, const int32_t* cu_seqlens, int64_t D, int64_t T,
+                              const pisa_dims* dims, float* pyramid, void* stream);
+
+/*
+ * Prefill selection for every row of a pack (bf16 only; fp32 returns
+ * PISA_ERR_UNSUPPORTED, as does T with Hkv * ceil(T / 1024) > 16384).
+ *   q        [T, Hq, d] bf16; k [T, Hkv, d] bf16, the keys the pyramid was built from.
+ *   pyramid  as written by pisa_build_pyramid_packed for the same cu_seqlens.
+ *   out_idx  int32 [T, Hkv, topk]: per row, its document's leaf indices,
+ *            ascending, -1 padded (exactly what pisa_select_prefill gives for
+ *            the document alone at B = 1).
+ *   workspace at least pisa_pack_workspace_bytes(dims, T, D) bytes.
+ */
+int pisa_select_prefill_packed(const void* q, const void* k, const float* pyramid,
+                               const int32_t* cu_seqlens, int64_t D, int64_t T,
+                               const pisa_dims* dims, int32_t* out_idx, void* workspace,
+                               size_t ws_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* pisa_status_string(int status);
 

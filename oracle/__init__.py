@@ -207,8 +207,9 @@ def decode_step(k_all: np.ndarray, n: int, q_new: np.ndarray, topk: int, C: int 
 
 
 # ------------------------------------------------------------------ packed documents --
-# Packed inputs keep document boundaries and allow no attention across documents (the
-# reading note's language-modelling experiments, continued-pretraining settings). Reading:
+# Packed inputs keep document boundaries and allow no attention across documents (reading
+# note "Block Sparse Attention with Log-Linear Complexity", "Experiments: language
+# modelling and downstream", the continued-pretraining settings). Reading:
 # every document is selected exactly as if it were a sequence of its own -- its own pyramid
 # over its own keys, its queries at positions counted from the document's first token, its
 # leaf indices counted from the document's first leaf. Nothing of one document (keys,

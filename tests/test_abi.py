@@ -72,3 +72,45 @@ def test_argument_errors_return_before_launch():
     assert ops.lib.pisa_decode_update_select(p, p, p, p, 64, 64, ctypes.byref(good), p, p, 1 << 30,
                                              None) == ops.PISA_ERR_CAPACITY
     assert ops.status_string(ops.PISA_ERR_WORKSPACE) == "workspace too small"
+
+
+def test_pack_geometry_helpers():
+    """Packed layout: level l has (T >> (5 + l)) + D + 1 rows per KV head, levels 1 .. L(T)."""
+    from block_selection_amd import ops
+    d = ops.make_dims(1, 32, 2, 8)
+    for T, D in [(262144, 1), (262144, 64), (16384, 7), (1, 1), (100, 5)]:
+        L = 1
+        m = -(-T // 64)
+        while m > 1:
+            m, L = -(-m // 2), L + 1
+        off = 0
+        for l in range(1, L + 1):
+            assert ops.pack_level_offset(d, T, D, l) == off
+            off += (T >> (5 + l)) + D + 1
+        assert ops.pack_level_offset(d, T, D, L + 1) == -1
+        assert ops.pack_pyramid_rows(d, T, D) == off
+        assert ops.lib.pisa_pack_pyramid_bytes(ctypes.byref(d), T, D) == 2 * off * 64 * 4
+        assert ops.pack_workspace_bytes(d, T, D) > 0
+    assert ops.pack_pyramid_rows(d, 0, 1) == -1
+    assert ops.pack_pyramid_rows(d, 64, 0) == -1
+    assert ops.pack_pyramid_rows(ops.make_dims(2, 32, 2, 8), 64, 1) == -1   # packs have B = 1
+
+
+def test_pack_argument_errors_return_before_launch():
+    from block_selection_amd import ops
+    p = ctypes.c_void_p(8)
+    good = ops.make_dims(1, 32, 2, 8)
+
+    def sel(dims, cu=p, D=3, T=4096, ws_bytes=1 << 34):
+        return ops.lib.pisa_select_prefill_packed(p, p, p, cu, D, T, ctypes.byref(dims), p, p, ws_bytes, None)
+
+    assert sel(good, cu=None) == ops.PISA_ERR_INVALID_ARG
+    assert sel(good, D=0) == ops.PISA_ERR_INVALID_ARG
+    assert sel(good, T=0) == ops.PISA_ERR_INVALID_ARG
+    assert sel(ops.make_dims(2, 32, 2, 8)) == ops.PISA_ERR_INVALID_ARG
+    assert sel(ops.make_dims(1, 32, 2, 8, dtype="f32")) == ops.PISA_ERR_UNSUPPORTED
+    assert sel(ops.make_dims(1, 32, 2, 8, d=32)) == ops.PISA_ERR_UNSUPPORTED
+    assert sel(good, T=1 << 24) == ops.PISA_ERR_UNSUPPORTED   # one document's bins exceed LDS
+    assert sel(good, ws_bytes=16) == ops.PISA_ERR_WORKSPACE
+    assert ops.lib.pisa_build_pyramid_packed(p, None, 3, 4096, ctypes.byref(good), p, None) == ops.PISA_ERR_INVALID_ARG
+    assert ops.lib.pisa_build_pyramid_packed(None, p, 3, 4096, ctypes.byref(good), p, None) == ops.PISA_ERR_INVALID_ARG
