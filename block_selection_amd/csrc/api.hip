@@ -26,8 +26,8 @@ template <int SLOTS, int S>
 __global__ void walk_upper_delta_kernel(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg, int64_t,
                                         int64_t, int32_t*, int32_t*);
 template <int SLOTS, int S>
-__global__ void walk_upper_delta_pack_kernel(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int32_t*,
-                                             int32_t*);
+__global__ void walk_upper_delta_pack_kernel(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int,
+                                             int32_t*, int32_t*);
 __global__ void delta_planes_kernel(const float*, uint16_t*, Geom, Pack);
 template <typename KT>
 __global__ void leaf_walk_kernel(const KT*, const KT*, Geom, int64_t, int64_t, const int32_t*,
@@ -37,7 +37,7 @@ __global__ void fill_u32_kernel(uint32_t*, int64_t, uint32_t);
 template <int SL>
 __global__ void bucket_pass_kernel(const int32_t*, const int32_t*, Geom, ClusterGeom, Pack, const int64_t*, int64_t,
                                    uint32_t*, const uint32_t*, const uint32_t*, uint2*, int);
-__global__ void pack_plan_kernel(Pack, int, int64_t*);
+__global__ void pack_plan_kernel(Pack, int, int, int64_t*);
 __global__ void group_offsets_kernel(const uint32_t*, ClusterGeom, Pack, const int64_t*, uint32_t*, uint32_t*);
 __global__ void scan_groups_kernel(const uint32_t*, ClusterGeom, uint32_t*, int4*, uint32_t*);
 template <int S>
@@ -80,6 +80,15 @@ __global__ void final_topk_kernel(const int32_t*, const int32_t*, const float*, 
 constexpr size_t kAlign = 256;
 
 static size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Positions per bucket range (log2): 512, halved down to 64 while the call has fewer ranges
+// than kRangeWorkgroups (one bucket-pass workgroup per CU of an MI355X).
+constexpr int64_t kRangeWorkgroups = 256;
+static int range_log2(int64_t positions) {
+    int rl = kLog2RangeMax;
+    while (rl > kLog2RangeMin && ((positions + ((int64_t)1 << rl) - 1) >> rl) < kRangeWorkgroups) --rl;
+    return rl;
+}
 
 // Workspace carve-up for `walks` walks over a pyramid of P rows per (batch, head).
 struct Workspace {
@@ -135,7 +144,8 @@ static Workspace carve(const pisa_dims* d, int64_t N, int64_t P, bool decode, ch
     // clustered leaf scoring for bf16 prefill while the per-range LDS histogram fits
     w.clustered = !decode && d->dtype == PISA_DTYPE_BF16 && d->Hkv * nsb <= 16384;
     if (w.clustered) {
-        w.CG.NR = (int32_t)((N + kRangeT - 1) / kRangeT);
+        w.CG.RL = range_log2((int64_t)d->B * N);
+        w.CG.NR = (int32_t)((N + ((int64_t)1 << w.CG.RL) - 1) >> w.CG.RL);
         w.CG.NSB = (int32_t)nsb;
         w.CG.ngroups = (int32_t)(d->B * d->Hkv * nsb);
         w.CG.nb = w.CG.ngroups * w.CG.NR;
@@ -155,10 +165,11 @@ static Workspace carve(const pisa_dims* d, int64_t N, int64_t P, bool decode, ch
 
 // Packs of D documents over T tokens (bf16, clustered leaf scoring) on the packed layout
 // of P rows per KV head.
-static int64_t pack_count_bound(int Hkv, int64_t T, int64_t D) {
-    // sum over documents of ceil(n/1024) * ceil(n/512) <= sum (n/1024 + 1)(n/512 + 1)
-    // <= T^2 / 2^19 + 3T/1024 + D
-    return (int64_t)Hkv * (((T + 1023) / 1024) * ((T + 511) / 512) + 3 * T / 1024 + D + 4);
+static int64_t pack_count_bound(int Hkv, int64_t T, int64_t D, int rl) {
+    // sum over documents of ceil(n/1024) * ceil(n/R) <= sum (n/1024 + 1)(n/R + 1)
+    // <= T^2 / (1024 R) + T/1024 + T/R + D
+    const int64_t R = (int64_t)1 << rl;
+    return (int64_t)Hkv * (((T + 1023) / 1024) * ((T + R - 1) / R) + T / 1024 + T / R + D + 4);
 }
 
 static Workspace carve_pack(const pisa_dims* d, int64_t T, int64_t D, int64_t P, char* base) {
@@ -179,9 +190,10 @@ static Workspace carve_pack(const pisa_dims* d, int64_t T, int64_t D, int64_t P,
     w.ncand = (int32_t*)take((size_t)walks * sizeof(int32_t));
     w.clustered = true;
     w.CG.NSB = (int32_t)((T >> (kLog2C + 4)) + D + 1);   // superblock slots per KV head
-    w.CG.NR = (int32_t)((T >> kLog2RangeT) + D + 1);     // range slots
+    w.CG.RL = range_log2(T);
+    w.CG.NR = (int32_t)((T >> w.CG.RL) + D + 1);        // range slots
     w.CG.ngroups = (int32_t)(d->Hkv * (int64_t)w.CG.NSB);
-    const int64_t ncount = pack_count_bound(d->Hkv, T, D);
+    const int64_t ncount = pack_count_bound(d->Hkv, T, D, w.CG.RL);
     w.CG.nb = 0;
     w.score = (float*)take((size_t)walks * cs * sizeof(float));
     w.sink = (float*)take((size_t)kClusterThreads * sizeof(float));
@@ -326,20 +338,23 @@ static int launch_upper_pack(const uint16_t* q, const Geom& G, const Pack& pk, c
                              hipStream_t s) {
     constexpr int WPW = 64 / SLOTS;
     constexpr int nwaves = kUpperThreads / 64;
-    const int64_t pieces = (pk.T + kRangeT - 1) / kRangeT;
-    const int64_t groups = pieces * ((kRangeT + WPW - 1) / WPW);
+    const int64_t groups = (pk.T + WPW - 1) / WPW + pk.D;
     int64_t need = (int64_t)G.Hkv * ((groups + nwaves - 1) / nwaves);
     int64_t nwg = need < cus ? need : cus;
     nwg = (nwg + 7) / 8 * 8;
     if (nwg < G.Hkv) nwg = G.Hkv;
+    // pieces of 512 tokens, fewer (down to 64) until every workgroup of a KV head has two
+    const int64_t npeers = nwg / G.Hkv;
+    int plog2 = 9;
+    while (plog2 > 6 && ((pk.T + ((int64_t)1 << plog2) - 1) >> plog2) < 2 * npeers) --plog2;
     const size_t lds = (size_t)(kLdsDeltaBudgetNodes + 2 * G.topk) * kLdsNodeBytes;
     const void* fn = upper_pack_fn<SLOTS>(G.score);
     if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return PISA_ERR_HIP;
     const uint16_t* planes = W.planes;
     const uint16_t* dplanes = W.dplanes;
-    void* args[] = {(void*)&q, (void*)&planes, (void*)&dplanes, (void*)&G, (void*)&pk, (void*)&W.cand,
-                    (void*)&W.ncand};
+    void* args[] = {(void*)&q, (void*)&planes, (void*)&dplanes, (void*)&G, (void*)&pk, (void*)&plog2,
+                    (void*)&W.cand, (void*)&W.ncand};
     if (hipLaunchKernel(fn, dim3((unsigned)nwg), dim3(kUpperThreads), args, lds, s) != hipSuccess)
         return PISA_ERR_HIP;
     return PISA_OK;
@@ -384,7 +399,7 @@ static int cluster_leaf_stage(const uint16_t* q, const uint16_t* k, const Geom& 
     dim3 bgrid;
     size_t bins;
     if (pk.cu) {
-        hipLaunchKernelGGL(pack_plan_kernel, dim3(1), dim3(1024), 0, s, pk, G.Hkv, W.cbase);
+        hipLaunchKernelGGL(pack_plan_kernel, dim3(1), dim3(1024), 0, s, pk, G.Hkv, (int)CG.RL, W.cbase);
         bgrid = dim3((unsigned)CG.NR, 1u);
         bins = (size_t)G.Hkv * ((pk.T + kSbKeys - 1) / kSbKeys) * 4;   // the longest document's groups
     } else {

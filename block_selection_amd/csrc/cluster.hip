@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p,
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
 }
 
-// Counting (fill = 0) or placing (fill = 1) the incidences of one range of kRangeT
+// Counting (fill = 0) or placing (fill = 1) the incidences of one range of 2^RL
 // query positions of batch element blockIdx.y (range blockIdx.x). One incidence per
 // sibling pair of a walk's leaf candidates (the children of one level-2 survivor); a
 // walk with at most K candidates has none (its candidates are all kept). The workgroup owns the
@@ -56,7 +56,6 @@ __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __rest
                                                           uint2* __restrict__ entries, int fill) {
     extern __shared__ uint32_t bins[];
     constexpr int WPW = 64 / SL;
-    static_assert(kRangeT == (1 << kLog2RangeT), "range slots use the range size's log2");
     const int r = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, seg = lane / SL, i = lane % SL;
     const int K = G.topk, CS = 2 * G.topk;
@@ -65,14 +64,14 @@ __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __rest
     int nsb;                   // superblocks per KV head in the bins: x = kvh * nsb + s
     int64_t g_sb0, c0, c_str;  // bin x -> group (x / nsb) * CG.NSB + g_sb0 + x % nsb; count c0 + x * c_str
     if (pk.cu) {
-        const int d = pack_find_slot(pk, kLog2RangeT, r);
+        const int d = pack_find_slot(pk, CG.RL, r);
         const Seg sg = pack_seg(pk, d);
-        const int64_t j = r - ((sg.lsh >> kLog2RangeT) + d);
-        const int64_t nr = (sg.N + kRangeT - 1) / kRangeT;
+        const int64_t j = r - ((sg.lsh >> CG.RL) + d);
+        const int64_t nr = sg.N ? ((sg.N - 1) >> CG.RL) + 1 : 0;
         if (sg.N == 0 || j < 0 || j >= nr) return;   // no positions, no buckets
         bt0 = sg.lsh;
-        t_lo = j * kRangeT;
-        t_hi = (t_lo + kRangeT < sg.N) ? t_lo + kRangeT : sg.N;
+        t_lo = j << CG.RL;
+        t_hi = (t_lo + (1 << CG.RL) < sg.N) ? t_lo + (1 << CG.RL) : sg.N;
         nsb = (int)((sg.N + kSbKeys - 1) / kSbKeys);
         g_sb0 = (sg.lsh >> (kLog2C + 4)) + d;
         c0 = cbase[d] + j;
@@ -80,8 +79,8 @@ __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __rest
     } else {
         const int b = blockIdx.y;
         bt0 = (int64_t)b * NT;
-        t_lo = (int64_t)r * kRangeT;
-        t_hi = (t_lo + kRangeT < NT) ? t_lo + kRangeT : NT;
+        t_lo = (int64_t)r << CG.RL;
+        t_hi = (t_lo + (1 << CG.RL) < NT) ? t_lo + (1 << CG.RL) : NT;
         nsb = CG.NSB;
         g_sb0 = (int64_t)b * G.Hkv * CG.NSB;
         c0 = g_sb0 * CG.NR + r;
@@ -122,14 +121,14 @@ __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __rest
 
 // Pack plan (one workgroup): cbase[d] = first count of document d's block (KV heads x its
 // superblocks x its ranges), an exclusive scan over the documents; cbase[D] = the total.
-__global__ __launch_bounds__(1024) void pack_plan_kernel(Pack pk, int Hkv, int64_t* __restrict__ cbase) {
+__global__ __launch_bounds__(1024) void pack_plan_kernel(Pack pk, int Hkv, int RL, int64_t* __restrict__ cbase) {
     __shared__ int64_t s_sum[1024];
     const int tid = threadIdx.x;
     const int per = (pk.D + 1023) / 1024;
     const int lo = tid * per, hi = min(pk.D, lo + per);
     auto size_of = [&](int d) -> int64_t {
         const Seg sg = pack_seg(pk, d);
-        return (int64_t)Hkv * ((sg.N + kSbKeys - 1) / kSbKeys) * ((sg.N + kRangeT - 1) / kRangeT);
+        return sg.N ? (int64_t)Hkv * ((sg.N + kSbKeys - 1) / kSbKeys) * (((sg.N - 1) >> RL) + 1) : 0;
     };
     int64_t acc = 0;
     for (int d = lo; d < hi; ++d) acc += size_of(d);
@@ -173,7 +172,7 @@ __global__ __launch_bounds__(256) void group_offsets_kernel(const uint32_t* __re
             if (lane == 0) gtot[g] = 0u;
             return;
         }
-        nr = (int)((sg.N + kRangeT - 1) / kRangeT);
+        nr = (int)(((sg.N - 1) >> CG.RL) + 1);
         c0 = cbase[d] + (kvh * nsb + s) * nr;
     }
     const uint32_t* c = counts + c0;

@@ -189,22 +189,23 @@ __host__ __device__ inline void upper_cfg_for(const Seg& sg, int topk, UpperCfg&
 }
 
 // Clustered leaf scoring (prefill): superblocks of 16 leaves; incidences are
-// bucketed by (batch, KV head, superblock, range of kRangeT query positions), so
+// bucketed by (batch, KV head, superblock, range of 2^RL query positions), so
 // that each bucket is counted and filled by one workgroup and the entries of one
 // (batch, KV head, superblock) group are contiguous; work items hold at most
-// kItemMax entries of one group.
+// kItemMax entries of one group. Ranges hold 512 positions, or fewer (down to 64)
+// when a call has too few ranges to give every CU a workgroup.
 constexpr int kSbLeaves = 16;
 constexpr int kSbKeys = kSbLeaves * kC;           // 1024 keys
-constexpr int kRangeT = 512;                       // query positions per range
-constexpr int kLog2RangeT = 9;
+constexpr int kLog2RangeMax = 9, kLog2RangeMin = 6;
 constexpr int kItemMax = 1024;                     // entries per work item
 constexpr int kClusterThreads = 1024;
 constexpr int kSbLdsBytes = kSbKeys * kD * 2;      // 128 KiB of bf16 keys
 struct ClusterGeom {
-    int32_t NR;      // position ranges per batch element
-    int32_t NSB;     // superblocks per KV head
+    int32_t NR;      // position ranges per batch element (range slots of a pack)
+    int32_t NSB;     // superblocks per KV head (superblock slots of a pack)
     int32_t ngroups; // B * Hkv * NSB
     int32_t nb;      // buckets = ngroups * NR
+    int32_t RL;      // log2 of the positions per range
 };
 // Fused decode step: workgroups of 8 wavefronts, ceil(2K / 8) per (batch, KV head).
 constexpr int kDecodeThreads = 512;

@@ -571,14 +571,14 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_kernel(const u
 }
 
 // bf16 walks of a pack of documents (G: the packed layout, B = 1, N = T). The tokens are
-// cut into pieces of kRangeT; the workgroups of a KV head take every npeers-th piece (so
+// cut into pieces of 2^plog2 (512, or fewer for small packs); the workgroups of a KV head take every npeers-th piece (so
 // each holds early and late positions of long documents alike), and walk the document
 // parts of a piece with that document's rows staged in LDS (restaged only when the
 // document changes).
 template <int SLOTS, int S>
 __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_pack_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ splanes, const uint16_t* __restrict__ dplanes,
-    Geom G, Pack pk, int32_t* __restrict__ cand_out, int32_t* __restrict__ ncand_out) {
+    Geom G, Pack pk, int plog2, int32_t* __restrict__ cand_out, int32_t* __restrict__ ncand_out) {
     constexpr int WPW = 64 / SLOTS;
     extern __shared__ u32x4 lds_u4[];
     lds_char_t* lds = (lds_char_t*)lds_u4;
@@ -588,10 +588,11 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_delta_pack_kernel(
     const int wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
     const int64_t plane_stride = (int64_t)G.Hkv * G.P * kD;
     const int64_t bh_row0 = (int64_t)kvh * G.P;
-    const int64_t npieces = (pk.T + kRangeT - 1) / kRangeT;
+    const int64_t piece = (int64_t)1 << plog2;
+    const int64_t npieces = (pk.T + piece - 1) >> plog2;
     int staged = -1;
     for (int64_t p = peer; p < npieces; p += npeers) {
-        const int64_t a = p * kRangeT, e = (a + kRangeT < pk.T) ? a + kRangeT : pk.T;
+        const int64_t a = p << plog2, e = (a + piece < pk.T) ? a + piece : pk.T;
         for (int d = pack_find_token(pk, a); d < pk.D; ++d) {
             const Seg sg = pack_seg(pk, d);
             const int64_t da = sg.lsh, db = da + sg.N;
@@ -623,15 +624,15 @@ template __global__ void walk_upper_delta_kernel<32, kScoreMeanHalfVar>(const ui
 template __global__ void walk_upper_delta_kernel<64, kScoreLse>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg, int64_t, int64_t, int32_t*, int32_t*);
 template __global__ void walk_upper_delta_kernel<64, kScoreMean>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg, int64_t, int64_t, int32_t*, int32_t*);
 template __global__ void walk_upper_delta_kernel<64, kScoreMeanHalfVar>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, UpperCfg, int64_t, int64_t, int32_t*, int32_t*);
-template __global__ void walk_upper_delta_pack_kernel<16, kScoreLse>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int32_t*, int32_t*);
-template __global__ void walk_upper_delta_pack_kernel<16, kScoreMean>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int32_t*, int32_t*);
-template __global__ void walk_upper_delta_pack_kernel<16, kScoreMeanHalfVar>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int32_t*, int32_t*);
-template __global__ void walk_upper_delta_pack_kernel<32, kScoreLse>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int32_t*, int32_t*);
-template __global__ void walk_upper_delta_pack_kernel<32, kScoreMean>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int32_t*, int32_t*);
-template __global__ void walk_upper_delta_pack_kernel<32, kScoreMeanHalfVar>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int32_t*, int32_t*);
-template __global__ void walk_upper_delta_pack_kernel<64, kScoreLse>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int32_t*, int32_t*);
-template __global__ void walk_upper_delta_pack_kernel<64, kScoreMean>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int32_t*, int32_t*);
-template __global__ void walk_upper_delta_pack_kernel<64, kScoreMeanHalfVar>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_pack_kernel<16, kScoreLse>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_pack_kernel<16, kScoreMean>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_pack_kernel<16, kScoreMeanHalfVar>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_pack_kernel<32, kScoreLse>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_pack_kernel<32, kScoreMean>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_pack_kernel<32, kScoreMeanHalfVar>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_pack_kernel<64, kScoreLse>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_pack_kernel<64, kScoreMean>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int, int32_t*, int32_t*);
+template __global__ void walk_upper_delta_pack_kernel<64, kScoreMeanHalfVar>(const uint16_t*, const uint16_t*, const uint16_t*, Geom, Pack, int, int32_t*, int32_t*);
 template __global__ void walk_upper_f32_kernel<16, kScoreLse>(const float*, const float*, Geom, int64_t, int64_t, int32_t*, int32_t*);
 template __global__ void walk_upper_f32_kernel<16, kScoreMean>(const float*, const float*, Geom, int64_t, int64_t, int32_t*, int32_t*);
 template __global__ void walk_upper_f32_kernel<16, kScoreMeanHalfVar>(const float*, const float*, Geom, int64_t, int64_t, int32_t*, int32_t*);
