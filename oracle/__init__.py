@@ -60,6 +60,8 @@ def _load():
     lib.pisa_oracle_validate.argtypes = [P, i64, i32, P, P, i64, i32, i32, i32, i32, i32, i32, i32,
                                          P, dbl, lng]
     lib.pisa_oracle_validate.restype = i32
+    lib.pisa_oracle_attention.argtypes = [P, P, i64, P, P, P, i64, i32, i32, i32, i32, i32, P, i32]
+    lib.pisa_oracle_attention.restype = i32
     _lib = lib
     return lib
 
@@ -204,6 +206,25 @@ def decode_step(k_all: np.ndarray, n: int, q_new: np.ndarray, topk: int, C: int 
     pyr = build_pyramid(k, C, g, nthreads)
     idx, gap, _ = walk(q_new[None], np.array([n]), k, pyr, topk, C, g, nthreads, score)
     return pyr, idx[0], gap[0]
+
+
+def attention(q_rows: np.ndarray, t_rows, k: np.ndarray, v: np.ndarray, idx: np.ndarray,
+              C: int = 64, nthreads: int = 0) -> np.ndarray:
+    """Stage two: per query row and head, softmax attention over the keys <= t of the
+    blocks its KV head selected (idx [n, Hkv, K], -1 entries ignored). Returns double
+    [n, Hq, d]."""
+    q_rows, k, v = _f32(q_rows), _f32(k), _f32(v)
+    t_rows = np.ascontiguousarray(t_rows, dtype=np.int64)
+    n, Hq, d = q_rows.shape
+    N, Hkv, _ = k.shape
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    assert idx.shape[:2] == (n, Hkv) and v.shape == k.shape and t_rows.shape == (n,)
+    out = np.zeros((n, Hq, d), np.float64)
+    rc = _load().pisa_oracle_attention(_p(q_rows), _p(t_rows), n, _p(k), _p(v), _p(idx), N, Hq, Hkv, d,
+                                       C, idx.shape[2], _p(out), nthreads)
+    if rc != 0:
+        raise RuntimeError(f"oracle attention failed ({rc})")
+    return out
 
 
 # ------------------------------------------------------------------ packed documents --

@@ -25,6 +25,9 @@
  *     their mean and truncating it gives the two ablation scores, the mean
  *     of the logits (first order, "PISA-1") and the mean plus half their
  *     variance (second order, "PISA-2"). The walk takes any of the three.
+ *   - same note, the two-stage formulation it opens with: stage two attends
+ *     over the original keys and values inside the selected blocks; the
+ *     attention function below is that softmax attention, causally masked.
  *
  * Readings taken where the pages are silent (each listed in the design notes):
  *   logit = q.k / sqrt(d); level sizes M_{l+1} = ceil(M_l / g) up to one node;
@@ -493,4 +496,70 @@ int pisa_oracle_validate(const float* q_row, int64_t t, int j, const float* k, c
     const int r = vwalk(&V, G.L, NULL, 0);
     free(V.scratch);
     return r;
+}
+
+/*
+ * Stage two: attention over the selected blocks ("Block Sparse Attention with
+ * Log-Linear Complexity", the two-stage formulation at the top of the note:
+ * stage two attends over the original keys and values inside the selected
+ * blocks). For query row i at position t and query head h (KV head j = h / GQ),
+ * the keys are those of the blocks idx[i][j][0..topk-1] (entries < 0 ignored;
+ * block b holds keys b*C .. min((b+1)*C, N) - 1) that are <= t (causal); the
+ * output is the softmax of q.k / sqrt(d) over those keys applied to their value
+ * rows. A row whose key set is empty gets zeros.
+ *   q_rows [n_rows][Hq][d], k and v [N][Hkv][d], idx [n_rows][Hkv][topk],
+ *   out [n_rows][Hq][d] (double).
+ */
+int pisa_oracle_attention(const float* q_rows, const int64_t* t_rows, int64_t n_rows, const float* k,
+                          const float* v, const int32_t* idx, int64_t N, int Hq, int Hkv, int d, int C,
+                          int topk, double* out, int nthreads) {
+    if (n_rows < 0 || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || d < 1 || C < 1 || topk < 1) return -1;
+    const int GQ = Hq / Hkv;
+    const double scale = 1.0 / sqrt((double)d);
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 4) reduction(| : bad)
+    for (int64_t i = 0; i < n_rows; i++) {
+        const int64_t t = t_rows[i];
+        if (t < 0 || t >= N) { bad = 1; continue; }
+        double* z = (double*)malloc(sizeof(double) * (size_t)topk * (size_t)C);
+        int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)topk * (size_t)C);
+        for (int h = 0; h < Hq; h++) {
+            const int j = h / GQ;
+            const float* q = q_rows + (i * Hq + h) * (int64_t)d;
+            /* the key set: every key <= t of every selected block */
+            int64_t nk = 0;
+            for (int s = 0; s < topk; s++) {
+                const int64_t b = idx[(i * Hkv + j) * (int64_t)topk + s];
+                if (b < 0) continue;
+                for (int64_t r = b * C; r < (b + 1) * C && r < N && r <= t; r++) key[nk++] = r;
+            }
+            double* o = out + (i * Hq + h) * (int64_t)d;
+            for (int e = 0; e < d; e++) o[e] = 0.0;
+            if (nk == 0) continue;
+            double zmax = -INFINITY;
+            for (int64_t a = 0; a < nk; a++) {
+                const float* kr = k + (key[a] * Hkv + j) * (int64_t)d;
+                double dot = 0.0;
+                for (int e = 0; e < d; e++) dot += (double)q[e] * (double)kr[e];
+                z[a] = dot * scale;
+                if (z[a] > zmax) zmax = z[a];
+            }
+            double den = 0.0;
+            for (int64_t a = 0; a < nk; a++) {
+                z[a] = exp(z[a] - zmax);
+                den += z[a];
+            }
+            for (int64_t a = 0; a < nk; a++) {
+                const float* vr = v + (key[a] * Hkv + j) * (int64_t)d;
+                const double w = z[a] / den;
+                for (int e = 0; e < d; e++) o[e] += w * (double)vr[e];
+            }
+        }
+        free(z);
+        free(key);
+    }
+    return bad ? -1 : 0;
 }
