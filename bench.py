@@ -87,6 +87,7 @@ TRANSCENDENTAL_PEAK = 256 * 32 * 2.4e9
 # sources of the two walk kernels (a traffic figure is only valid for the code it was taken on)
 LEAF_SOURCES = ["cluster.hip", "walk_math.h", "lanes.h", "pisa_device.h"]
 UPPER_SOURCES = ["upper.hip", "walk_math.h", "lanes.h", "pisa_device.h"]
+ATTN_SOURCES = ["attention.hip", "walk_math.h", "lanes.h", "pisa_device.h"]
 COPY_BYTES = 256 << 20          # the calibration copy: 256 MiB read + 256 MiB written
 
 
@@ -132,6 +133,12 @@ def write_traffic(fetch_dir: str, write_dir: str, workload: str = "long256k") ->
             "fetch_kib": f_kib, "write_kib": w_kib,
             "bytes_per_launch": f_kib * 1024 * fs + w_kib * 1024 * wsc,
             "source_hash": _hash_sources(srcs)}
+    if any("sparse_attention_kernel" in k for k in fetch):
+        f_kib, w_kib = find(fetch, "sparse_attention_kernel"), find(write, "sparse_attention_kernel")
+        out[f"sparse_attention_kernel:{workload}"] = {
+            "fetch_kib": f_kib, "write_kib": w_kib,
+            "bytes_per_launch": f_kib * 1024 * fs + w_kib * 1024 * wsc,
+            "source_hash": _hash_sources(ATTN_SOURCES)}
     with open(os.path.join(PROFILES, "hbm_traffic.json"), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
@@ -387,6 +394,8 @@ def main():
         "hbm": hbm,
         "work": work,
     }
+    result["attention"] = attention_bench(torch, ops, synth, wl, N, dims, q, k, out, args.steps, args.warmup,
+                                          ms_per_step, log)
     if not args.no_extras:
         # the pages' two ablation scores on the same workload and launch configuration
         variants = {}
@@ -419,6 +428,49 @@ def main():
         log("timing the CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(inp, wl.topk, args.cpu_positions)
     print(json.dumps(result), flush=True)
+
+
+def attention_bench(torch, ops, synth, wl, N, dims, q, k, idx, steps, warmup, select_ms, log):
+    """Stage two on the step's own selection: attention of every query head over the keys of
+    its KV head's selected blocks (pisa_sparse_attention), timed on its own with CUDA events
+    on the stream the library launches on."""
+    dev = q.device
+    v = torch.from_numpy(synth.bf16_bits(synth.make_values(wl.B, N, wl.Hkv, seed=wl.seed)).view(np.int16)).view(
+        torch.bfloat16).to(dev)
+    out = torch.empty((wl.B, N, wl.Hq, wl.d), dtype=torch.float32, device=dev)
+    ws = ops.alloc_attention_workspace(dims, N, N, device=dev)
+    for _ in range(warmup):
+        ops.sparse_attention(q, k, v, idx, N, N, dims, out, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        ops.sparse_attention(q, k, v, idx, N, N, dims, out, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # the pages' stage-two cost model: each query reads the keys and values of its (at most K)
+    # selected blocks; plus its queries and its output rows
+    GQ = wl.Hq // wl.Hkv
+    nsel = int(np.minimum(wl.topk, np.arange(N) // wl.C + 1).sum()) * wl.B * wl.Hkv
+    blk_bytes = wl.C * wl.d * 2 * 2
+    walks = wl.B * N * wl.Hkv
+    alg = nsel * blk_bytes + walks * GQ * wl.d * (2 + 4)
+    traffic = measured_traffic(f"sparse_attention_kernel:{wl.name}", _hash_sources(ATTN_SOURCES))
+    flops = nsel * GQ * wl.C * wl.d * 2 * 2
+    res = {"ms": ms, "queries_per_s": wl.B * N / (ms / 1e3),
+           "step_plus_attention_ms": select_ms + ms, "selection_share": select_ms / (select_ms + ms),
+           "roofline": {"kernel": "sparse_attention_kernel (+ vt_tiles_kernel, the per-call V re-layout)",
+                        "bound": "hbm", "achieved": alg / (ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
+                        "algorithmic_per_launch": alg,
+                        "algorithmic_model": "per walk: K and V of each selected block (64 x 64 x 2 B each) + "
+                                             "its group's queries (bf16) and outputs (fp32)"},
+           "mfma_tflops": flops / (ms / 1e3) / 1e12}
+    log(f"attention over the selected blocks: {ms:.3f} ms ({res['roofline']['achieved']:.0f} GB/s of the "
+        f"per-query block reads); selection is {100 * res['selection_share']:.0f}% of selection + attention")
+    del v, out, ws
+    return res
 
 
 def decode_bench(torch, ops, synth, dev, log):

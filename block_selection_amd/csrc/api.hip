@@ -44,6 +44,10 @@ template <int S>
 __global__ void leaf_cluster_kernel(const uint16_t*, const uint16_t*, Geom, ClusterGeom, Pack, int64_t,
                                     const int4*, const uint2*, uint32_t*, float*, float*);
 
+__global__ void vt_tiles_kernel(const uint16_t*, Geom, int64_t, uint16_t*);
+__global__ void sparse_attention_kernel(const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*, Geom,
+                                        int64_t, float*);
+
 // The kernels that score candidates are built once per candidate score (pisa_score);
 // these pick the build for G.score.
 template <int SLOTS>
@@ -629,6 +633,43 @@ int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cach
     if ((rc = launch_status()) != PISA_OK) return rc;
     return select_impl((const float*)q_new, (const float*)k_cache, pyramid, G, n_before, 1, out_idx, W, s,
                        nullptr);
+}
+
+// ------------------------------------------------------------- attention (stage two) --
+
+// V tiles of the attention call: [B * Hkv][ceil(N / 64)][64 dims][64 keys] bf16.
+static size_t attention_ws(const pisa_dims* d, int64_t N) {
+    const int64_t nblk = (N + kC - 1) / kC;
+    return align_up((size_t)d->B * d->Hkv * nblk * kD * kC * sizeof(uint16_t));
+}
+
+size_t pisa_attention_workspace_bytes(const pisa_dims* dims, int64_t N, int64_t n_capacity) {
+    Geom G;
+    if (check_dims(dims) != PISA_OK || make_geom(dims, N, n_capacity, &G) != PISA_OK) return 0;
+    return attention_ws(dims, N);
+}
+
+int pisa_sparse_attention(const void* q, const void* k, const void* v, const int32_t* idx, int64_t N,
+                          int64_t n_capacity, const pisa_dims* dims, float* out, void* workspace,
+                          size_t ws_bytes, void* stream) {
+    int rc = check_dims(dims);
+    if (rc != PISA_OK) return rc;
+    if (!q || !k || !v || !idx || !out) return PISA_ERR_INVALID_ARG;
+    Geom G;
+    if ((rc = make_geom(dims, N, n_capacity, &G)) != PISA_OK) return rc;
+    if (dims->dtype != PISA_DTYPE_BF16) return PISA_ERR_UNSUPPORTED;
+    const int64_t nblk = (N + kC - 1) / kC;
+    const int64_t walks = (int64_t)dims->B * N * dims->Hkv;
+    const int64_t grid = (walks + 3) / 4;
+    if ((int64_t)dims->B * dims->Hkv > 65535 || grid > INT_MAX || nblk > INT_MAX) return PISA_ERR_UNSUPPORTED;
+    if (!workspace || ws_bytes < attention_ws(dims, N)) return PISA_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    uint16_t* vt = (uint16_t*)workspace;
+    hipLaunchKernelGGL(vt_tiles_kernel, dim3((unsigned)nblk, (unsigned)(dims->B * dims->Hkv)), dim3(256), 0, s,
+                       (const uint16_t*)v, G, nblk, vt);
+    hipLaunchKernelGGL(sparse_attention_kernel, dim3((unsigned)grid), dim3(256), 0, s, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)vt, idx, G, nblk, out);
+    return launch_status();
 }
 
 // ------------------------------------------------------------------ packed documents --

@@ -1,0 +1,238 @@
+// attention.hip -- stage two: attention over the selected key blocks (gfx950).
+//
+// Reading note "Block Sparse Attention with Log-Linear Complexity", the two-stage
+// formulation it opens with: once stage one has selected K key blocks per query
+// (shared by the query heads of a GQA group, section 4.1), stage two attends over
+// the original keys and values inside those blocks. Per query head: softmax of
+// q.k/sqrt(d) over the keys <= t of the selected blocks, applied to their values.
+//
+// Layout and arithmetic:
+//   * One wavefront per (batch, position, KV head): the group's query heads are the
+//     16 columns of every MFMA tile, so each key and value block is read once for
+//     the whole group. Logits: v_mfma_f32_16x16x32_bf16 with A = 16 key rows of the
+//     block, B = the queries; lane (g, n) holds keys 16 tau + 4g + r of head n.
+//   * Online softmax in base 2 per head column (running maximum, rescaled sums);
+//     the block holding position t masks its keys after t.
+//   * Output O^T = V^T P on the same MFMA: A = 16 dims of V^T, B = P. The 8 keys a
+//     lane needs for B are exactly the 8 logits it already holds (keys 32s + 4g + r
+//     and 32s + 16 + 4g + r), so P never moves between lanes; V is tiled once per
+//     call into per-block [dim][64 keys] tiles whose keys are permuted into that
+//     order, so each A fragment is one 16-byte load. P enters as a bf16 hi + lo pair
+//     (2^-17 relative), so the products are nearly exact and sums stay in fp32.
+#include "walk_math.h"
+
+namespace pisa {
+
+constexpr int kAttnThreads = 256;   // four walks per workgroup
+
+// Key held in slot `slot` (0..63) of a V^T tile row: slots 32s + 8g + r and 32s + 8g + 4 + r
+// (r < 4) hold keys 32s + 4g + r and 32s + 16 + 4g + r, so the 8 keys whose logits lane
+// group g holds for key half s are contiguous.
+__device__ inline int vt_key_of(int slot) {
+    const int s = slot >> 5, w5 = slot & 31, g = w5 >> 3, hi = (w5 >> 2) & 1, r = w5 & 3;
+    return 32 * s + 16 * hi + 4 * g + r;
+}
+
+// p = hi + lo, both bf16 (round to nearest even): a 17-bit mantissa in two MFMA operands.
+__device__ inline void split_bf16(float p, uint32_t& hi, uint32_t& lo) {
+    hi = rne_bf16_bits(p);
+    lo = rne_bf16_bits(p - __uint_as_float(hi << 16));
+}
+
+// V [B, cap, Hkv, 64] -> tiles [B*Hkv][nblk][64 dims][64 key slots] (keys >= N are zero).
+// Grid: (nblk, B*Hkv), 256 threads.
+__global__ __launch_bounds__(256) void vt_tiles_kernel(const uint16_t* __restrict__ v, Geom G, int64_t nblk,
+                                                       uint16_t* __restrict__ vt) {
+    __shared__ uint16_t tile[kC][kD + 2];
+    const int blk = blockIdx.x, bh = blockIdx.y;
+    const int b = bh / G.Hkv, kvh = bh % G.Hkv;
+    const int tid = threadIdx.x;
+    {
+        const int kk = tid >> 2, part = tid & 3;           // key kk, dims 16 part .. +15
+        const int64_t key = (int64_t)blk * kC + kk;
+        u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
+        if (key < G.N) {
+            const uint16_t* src = v + (((int64_t)b * G.cap + key) * G.Hkv + kvh) * kD + 16 * part;
+            x0 = *reinterpret_cast<const u32x4*>(src);
+            x1 = *reinterpret_cast<const u32x4*>(src + 8);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            tile[kk][16 * part + 2 * i] = (uint16_t)(x0[i] & 0xffffu);
+            tile[kk][16 * part + 2 * i + 1] = (uint16_t)(x0[i] >> 16);
+            tile[kk][16 * part + 8 + 2 * i] = (uint16_t)(x1[i] & 0xffffu);
+            tile[kk][16 * part + 8 + 2 * i + 1] = (uint16_t)(x1[i] >> 16);
+        }
+    }
+    __syncthreads();
+    {
+        const int dim = tid >> 2, part = tid & 3;           // dim, slots 16 part .. +15
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int s0 = 16 * part + 2 * i;
+            const uint32_t lo = tile[vt_key_of(s0)][dim], hi = tile[vt_key_of(s0 + 1)][dim];
+            w[i] = lo | (hi << 16);
+        }
+        uint16_t* dst = vt + (((int64_t)bh * nblk + blk) * kD + dim) * kC + 16 * part;
+        *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<u32x4*>(dst + 8) = u32x4{w[4], w[5], w[6], w[7]};
+    }
+}
+
+// K fragments of one block: A operand rows = keys 16 tau + n, k-steps dims 8g.. and 32 + 8g..
+struct KFrag {
+    u32x4 a[4][2];
+};
+
+__device__ inline void load_kfrag(const uint16_t* __restrict__ base, int64_t nkeys, int64_t row_stride, int n,
+                                  int gq, KFrag& f) {
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau) {
+        int64_t key = 16 * tau + n;
+        key = (key < nkeys) ? key : nkeys - 1;             // rows past the keys are masked later
+        const uint16_t* p = base + key * row_stride;
+        f.a[tau][0] = *reinterpret_cast<const u32x4*>(p + 8 * gq);
+        f.a[tau][1] = *reinterpret_cast<const u32x4*>(p + 32 + 8 * gq);
+    }
+}
+
+// One wavefront per walk w = (b * N + t) * Hkv + kvh, four per workgroup. idx: [walks][K]
+// selected blocks (entries < 0, or past t's block, are skipped); out: fp32 [B, N, Hq, 64].
+__global__ __launch_bounds__(kAttnThreads, 3) void sparse_attention_kernel(const uint16_t* __restrict__ q,
+                                                                        const uint16_t* __restrict__ k,
+                                                                        const uint16_t* __restrict__ vt,
+                                                                        const int32_t* __restrict__ idx, Geom G,
+                                                                        int64_t nblk, float* __restrict__ out) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int gq = lane >> 4, n = lane & 15;
+    const int64_t walks = (int64_t)G.B * G.N * G.Hkv;
+    const int64_t w = (int64_t)blockIdx.x * (kAttnThreads / 64) + wave;
+    if (w >= walks) return;                                // whole wavefronts leave together
+    const int kvh = (int)(w % G.Hkv);
+    const int64_t bt = w / G.Hkv, b = bt / G.N, t = bt % G.N;
+    const int K = G.topk;
+    const int64_t row_stride = (int64_t)G.Hkv * kD;
+    const uint16_t* kbase = k + (b * G.cap * G.Hkv + kvh) * kD;   // key r at kbase + r * row_stride
+    const uint16_t* vtb = vt + ((b * G.Hkv + kvh) * nblk) * (int64_t)(kD * kC);
+
+    // queries: B operand, head n of the group (columns n >= GQ read head 0, not written)
+    u32x4 qa, qb;
+    {
+        const uint16_t* qrow = q + ((bt * G.Hq) + (int64_t)kvh * G.GQ + (n < G.GQ ? n : 0)) * kD;
+        qa = *reinterpret_cast<const u32x4*>(qrow + 8 * gq);
+        qb = *reinterpret_cast<const u32x4*>(qrow + 32 + 8 * gq);
+    }
+    const bf16x8 q0 = __builtin_bit_cast(bf16x8, qa), q1 = __builtin_bit_cast(bf16x8, qb);
+
+    // the valid selected blocks, in lanes 0 .. nsel-1
+    const int64_t tblk = t >> kLog2C;
+    int sel = (lane < K) ? idx[w * K + lane] : -1;
+    const bool ok = sel >= 0 && sel <= tblk;
+    const uint64_t vm = ballot(ok);
+    const int nsel = __popcll(vm);
+    const int slot = lanes_below(vm);
+    sel = push_to_lane(ok ? slot : nsel + lanes_below(~vm), ok ? sel : -1);
+
+    float m = -INFINITY;        // running maximum of column n (base-2 logits)
+    float lsum = 0.0f;          // this lane's share of column n's exp sum
+    f32x4 o[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    KFrag cur;   // this block's key fragments; refilled with the next block's once the logits are issued
+    if (nsel > 0) {
+        const int b0 = readlane_i(sel, 0);
+        load_kfrag(kbase + (int64_t)b0 * kC * row_stride, G.N - (int64_t)b0 * kC, row_stride, n, gq, cur);
+    }
+    for (int s = 0; s < nsel; ++s) {
+        const int blk = readlane_i(sel, s);
+        const int64_t k0 = (int64_t)blk * kC;
+        // V^T fragments of this block: dims 16 dt + n, slots 32 s2 + 8 gq .. +7
+        u32x4 vf[4][2];
+        const uint16_t* vblk = vtb + (int64_t)blk * (kD * kC);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+                vf[dt][s2] = *reinterpret_cast<const u32x4*>(vblk + (16 * dt + n) * kC + 32 * s2 + 8 * gq);
+        // logits
+        f32x4 acc[4];
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau) {
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.a[tau][0]), q0, c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.a[tau][1]), q1, c, 0, 0, 0);
+            acc[tau] = c;
+        }
+        if (s + 1 < nsel) {
+            const int bn = readlane_i(sel, s + 1);
+            load_kfrag(kbase + (int64_t)bn * kC * row_stride, G.N - (int64_t)bn * kC, row_stride, n, gq, cur);
+        }
+        // scale to base 2, mask keys after t, block maximum per column
+        const int64_t lim = t - k0;                          // keys 0 .. lim of the block are visible
+        float mb = -INFINITY;
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x = acc[tau][r] * kScale2;
+                const bool vis = 16 * tau + 4 * gq + r <= lim;
+                acc[tau][r] = vis ? x : -INFINITY;
+                mb = fmaxf(mb, acc[tau][r]);
+            }
+        mb = cols4_max(mb);
+        const float mn = fmaxf(m, mb);
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first block (m = -inf)
+        m = mn;
+        float ps = 0.0f;
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = __builtin_amdgcn_exp2f(acc[tau][r] - mn);
+                acc[tau][r] = p;
+                ps += p;
+            }
+        lsum = lsum * alpha + ps;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[dt][r] *= alpha;
+        // O^T += V^T P, P as bf16 hi + lo
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p0 = acc[2 * s2 + (e >> 1)][2 * (e & 1)];
+                const float p1 = acc[2 * s2 + (e >> 1)][2 * (e & 1) + 1];
+                uint32_t h0, l0, h1, l1;
+                split_bf16(p0, h0, l0);
+                split_bf16(p1, h1, l1);
+                hi[e] = h0 | (h1 << 16);
+                lo[e] = l0 | (l1 << 16);
+            }
+            const bf16x8 bh = __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
+            const bf16x8 bl = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const bf16x8 av = __builtin_bit_cast(bf16x8, vf[dt][s2]);
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, o[dt], 0, 0, 0);
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, o[dt], 0, 0, 0);
+            }
+        }
+    }
+    const float l = cols4_sum(lsum);
+    if (n < G.GQ) {
+        float* orow = out + ((bt * G.Hq) + (int64_t)kvh * G.GQ + n) * kD;
+        const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const f32x4 v4 = {o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv};
+            *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * gq) = v4;
+        }
+    }
+}
+
+}  // namespace pisa

@@ -30,7 +30,8 @@ EXPORTED = ("pisa_pyramid_nodes", "pisa_level_offset", "pisa_pyramid_bytes", "pi
             "pisa_build_pyramid", "pisa_select_prefill", "pisa_select_prefill_profiled",
             "pisa_decode_update_select", "pisa_status_string", "pisa_pack_pyramid_rows",
             "pisa_pack_level_offset", "pisa_pack_pyramid_bytes", "pisa_pack_workspace_bytes",
-            "pisa_build_pyramid_packed", "pisa_select_prefill_packed")
+            "pisa_build_pyramid_packed", "pisa_select_prefill_packed", "pisa_attention_workspace_bytes",
+            "pisa_sparse_attention")
 
 
 class Dims(ctypes.Structure):
@@ -84,6 +85,10 @@ def _load() -> ctypes.CDLL:
     lib.pisa_build_pyramid_packed.restype = ctypes.c_int
     lib.pisa_select_prefill_packed.argtypes = [P, P, P, P, i64, i64, D, P, P, sz, P]
     lib.pisa_select_prefill_packed.restype = ctypes.c_int
+    lib.pisa_attention_workspace_bytes.argtypes = [D, i64, i64]
+    lib.pisa_attention_workspace_bytes.restype = sz
+    lib.pisa_sparse_attention.argtypes = [P, P, P, P, i64, i64, D, P, P, sz, P]
+    lib.pisa_sparse_attention.restype = ctypes.c_int
     lib.pisa_status_string.argtypes = [ctypes.c_int]
     lib.pisa_status_string.restype = ctypes.c_char_p
     return lib
@@ -260,3 +265,34 @@ def select_prefill_packed(q: torch.Tensor, k: torch.Tensor, pyramid: torch.Tenso
                                         _stream(stream))
     if rc != PISA_OK:
         raise PisaError("pisa_select_prefill_packed", rc)
+
+
+# ------------------------------------------------------------- attention (stage two) --
+# Attention over the selected blocks: per query head, softmax over the keys <= t of the
+# blocks its KV head selected (idx as pisa_select_prefill writes it), applied to their
+# value rows. q [B, N, Hq, d], k and v [B, n_capacity, Hkv, d] bf16; out fp32 [B, N, Hq, d].
+
+def attention_workspace_bytes(dims: Dims, N: int, n_capacity: Optional[int] = None) -> int:
+    cap = N if n_capacity is None else n_capacity
+    return int(lib.pisa_attention_workspace_bytes(ctypes.byref(dims), N, cap))
+
+
+def alloc_attention_workspace(dims: Dims, N: int, n_capacity: Optional[int] = None,
+                              device="cuda") -> Optional[torch.Tensor]:
+    n = attention_workspace_bytes(dims, N, n_capacity)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, N: int,
+                     n_capacity: int, dims: Dims, out: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> None:
+    _check(q, "q", dims.torch_dtype, dims.B * N * dims.Hq * dims.d)
+    _check(k, "k", dims.torch_dtype, dims.B * n_capacity * dims.Hkv * dims.d)
+    _check(v, "v", dims.torch_dtype, dims.B * n_capacity * dims.Hkv * dims.d)
+    _check(idx, "idx", torch.int32, dims.B * N * dims.Hkv * dims.topk)
+    _check(out, "out", torch.float32, dims.B * N * dims.Hq * dims.d)
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.pisa_sparse_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), N, n_capacity, ctypes.byref(dims),
+                                   _ptr(out), _ptr(workspace), ws_n, _stream(stream))
+    if rc != PISA_OK:
+        raise PisaError("pisa_sparse_attention", rc)

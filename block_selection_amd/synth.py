@@ -189,3 +189,11 @@ def make_varlen(T: int, Hq: int, Hkv: int, dtype: str = "bf16", mean_len: float 
     if dtype == "bf16":
         q, k = bf16_round(q), bf16_round(k)
     return VarlenInputs(q, k, cu)
+
+
+def make_values(B: int, N: int, Hkv: int, dtype: str = "bf16", seed: int = 0, d: int = 64) -> np.ndarray:
+    """Value rows V [B, N, Hkv, d] for attention over the selected blocks: standard normal
+    draws from their own generator, numpy default_rng(seed + 1000003), rounded like Q and K."""
+    rng = np.random.default_rng(seed + 1000003)
+    v = _normal(rng, (B, N, Hkv, d))
+    return bf16_round(v) if dtype == "bf16" else v

@@ -173,6 +173,35 @@ int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cach
                               const pisa_dims* dims, int32_t* out_idx, void* workspace,
                               size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------- attention (stage two)
+ *
+ * Reading note "Block Sparse Attention with Log-Linear Complexity", the two-stage
+ * formulation it opens with: stage two attends over the original keys and values
+ * inside the blocks stage one selected. For query position t and query head h
+ * (KV head j = h / (Hq/Hkv)): softmax of q.k / sqrt(d) over the keys <= t of the
+ * blocks idx[b][t][j][0..topk-1] (entries < 0 or after t's block are skipped;
+ * each block is counted as often as it appears), applied to those keys' value
+ * rows.
+ */
+
+/* Device workspace of pisa_sparse_attention (0 on bad input): the value rows re-laid
+ * as per-block tiles, B * Hkv * ceil(N / 64) * 64 * 64 bf16. */
+size_t pisa_attention_workspace_bytes(const pisa_dims* dims, int64_t N, int64_t n_capacity);
+
+/*
+ * Attention over the selected blocks for every position t in 0..N-1 (bf16 only;
+ * fp32 inputs return PISA_ERR_UNSUPPORTED).
+ *   q    [B, N, Hq, d]; k, v [B, n_capacity, Hkv, d] (bf16).
+ *   idx  int32 [B, N, Hkv, topk], as pisa_select_prefill writes it.
+ *   out  fp32 [B, N, Hq, d].
+ * Arithmetic: exact bf16 q.k products accumulated in fp32, base-2 online softmax in
+ * fp32, probabilities as a bf16 hi + lo pair (2^-17 relative) times bf16 values on
+ * the MFMA with fp32 accumulation.
+ */
+int pisa_sparse_attention(const void* q, const void* k, const void* v, const int32_t* idx, int64_t N,
+                          int64_t n_capacity, const pisa_dims* dims, float* out, void* workspace,
+                          size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------ packed documents
  *
  * Packed inputs (reading note "Block Sparse Attention with Log-Linear

@@ -114,3 +114,21 @@ def test_pack_argument_errors_return_before_launch():
     assert sel(good, ws_bytes=16) == ops.PISA_ERR_WORKSPACE
     assert ops.lib.pisa_build_pyramid_packed(p, None, 3, 4096, ctypes.byref(good), p, None) == ops.PISA_ERR_INVALID_ARG
     assert ops.lib.pisa_build_pyramid_packed(None, p, 3, 4096, ctypes.byref(good), p, None) == ops.PISA_ERR_INVALID_ARG
+
+
+def test_attention_argument_errors_return_before_launch():
+    from block_selection_amd import ops
+    p = ctypes.c_void_p(8)
+    good = ops.make_dims(1, 32, 2, 8)
+
+    def att(dims, N=4096, cap=4096, ws_bytes=1 << 34, ptr=p):
+        return ops.lib.pisa_sparse_attention(ptr, p, p, p, N, cap, ctypes.byref(dims), p, p, ws_bytes, None)
+
+    assert ops.attention_workspace_bytes(good, 4096) == 2 * 64 * 64 * 64 * 2
+    assert ops.attention_workspace_bytes(good, 4097, 4096) == 0
+    assert att(good, ptr=None) == ops.PISA_ERR_INVALID_ARG
+    assert att(good, N=0) == ops.PISA_ERR_INVALID_ARG
+    assert att(good, N=5000) == ops.PISA_ERR_CAPACITY
+    assert att(ops.make_dims(1, 32, 2, 8, dtype="f32")) == ops.PISA_ERR_UNSUPPORTED
+    assert att(ops.make_dims(1, 32, 2, 8, d=128)) == ops.PISA_ERR_UNSUPPORTED
+    assert att(good, ws_bytes=16) == ops.PISA_ERR_WORKSPACE

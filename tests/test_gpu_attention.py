@@ -1,0 +1,130 @@
+"""GPU parity of attention over the selected blocks (stage two) against the oracle.
+
+The oracle's attention takes the oracle's own selection; the GPU kernel is given the
+same index array (or its own selection, compared on the walks where the two
+selections agree). Tolerance: every output element within 1e-4 * max|v| of the fp64
+oracle -- the kernel's errors are fp32 accumulation of exact bf16 products (about
+1e-6 relative on a logit), the hardware exp2 (about 1 ulp) and the bf16 hi + lo
+split of the probabilities (2^-17), which together stay below 4e-5 of the largest
+value magnitude.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_selection_amd import synth
+from pisa_testlib import run_prefill, to_device
+
+pytestmark = pytest.mark.gpu
+
+ATTN_TOL = 1e-4
+
+
+def _run_attention(q, k, v, idx, topk, cap=None):
+    """q [N, Hq, d], k/v [N, Hkv, d], idx [N, Hkv, K] (B = 1)."""
+    from block_selection_amd import ops
+    N, Hq, d = q.shape
+    Hkv = k.shape[1]
+    cap = N if cap is None else cap
+    print(f"attention N={N} cap={cap} Hq={Hq} Hkv={Hkv} K={topk}", flush=True)
+    dims = ops.make_dims(1, Hq, Hkv, topk, "bf16")
+    kk = np.zeros((cap, Hkv, d), np.float32)
+    vv = np.zeros((cap, Hkv, d), np.float32)
+    kk[:N], vv[:N] = k, v
+    kk[N:], vv[N:] = 3.0, -3.0            # rows past N must not matter
+    qt, kt, vt = to_device(q[None], "bf16"), to_device(kk[None], "bf16"), to_device(vv[None], "bf16")
+    it = torch.from_numpy(np.ascontiguousarray(idx[None], np.int32)).cuda()
+    out = torch.full((1, N, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    ws = ops.alloc_attention_workspace(dims, N, cap)
+    ops.sparse_attention(qt, kt, vt, it, N, cap, dims, out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()[0]
+
+
+def _check(got, ref, v, rows=None):
+    scale = float(np.abs(v).max())
+    err = np.abs(got.astype(np.float64) - ref)
+    assert np.all(np.isfinite(got))
+    worst = float(err.max()) / scale
+    print(f"attention max |err| / max|v| = {worst:.3e}", flush=True)
+    assert worst <= ATTN_TOL, worst
+    return worst
+
+
+def _inputs(N, Hq, Hkv, seed):
+    rng = np.random.default_rng(seed)
+    q = synth.bf16_round(rng.standard_normal((N, Hq, 64), dtype=np.float32))
+    k = synth.bf16_round(rng.standard_normal((N, Hkv, 64), dtype=np.float32))
+    v = synth.make_values(1, N, Hkv, seed=seed)[0]
+    return q, k, v
+
+
+@pytest.mark.parametrize("N,Hq,Hkv,K", [(1000, 32, 2, 8), (4096, 32, 2, 8), (130, 4, 1, 4), (3000, 12, 3, 5),
+                                         (2000, 8, 8, 32), (5000, 16, 1, 16), (64, 32, 2, 8), (1, 2, 1, 1)])
+def test_attention_on_the_oracle_selection(N, Hq, Hkv, K):
+    q, k, v = _inputs(N, Hq, Hkv, N + K)
+    pyr = oracle.build_pyramid(k)
+    ts = np.arange(N)
+    idx, _, _ = oracle.walk(q, ts, k, pyr, K)
+    got = _run_attention(q, k, v, idx, K)
+    ref = oracle.attention(q, ts, k, v, idx)
+    _check(got, ref, v)
+
+
+def test_attention_skips_invalid_indices():
+    """Entries < 0, past t's block or past the last block add nothing (as in the oracle)."""
+    N, Hq, Hkv, K = 900, 8, 2, 6
+    q, k, v = _inputs(N, Hq, Hkv, 3)
+    rng = np.random.default_rng(4)
+    idx = rng.integers(-3, 20, (N, Hkv, K)).astype(np.int32)
+    idx[:, :, 0] = 0                                     # every row keeps one visible block
+    idx[5, 1, 3] = 1 << 30
+    for row in range(N):                                 # distinct entries per row
+        for j in range(Hkv):
+            seen = set()
+            for i in range(K):
+                if idx[row, j, i] in seen:
+                    idx[row, j, i] = -1
+                seen.add(int(idx[row, j, i]))
+    got = _run_attention(q, k, v, idx, K)
+    ref = oracle.attention(q, np.arange(N), k, v, idx)
+    _check(got, ref, v)
+
+
+def test_attention_capacity_layout():
+    N, cap, Hq, Hkv, K = 1500, 2048, 32, 2, 8
+    q, k, v = _inputs(N, Hq, Hkv, 5)
+    idx, _, _ = oracle.walk(q, np.arange(N), k, oracle.build_pyramid(k), K)
+    got = _run_attention(q, k, v, idx, K, cap=cap)
+    _check(got, oracle.attention(q, np.arange(N), k, v, idx), v)
+
+
+def _end_to_end(wl_name, n_rows, seed=0):
+    from block_selection_amd import ops
+    wl = synth.WORKLOADS[wl_name]
+    inp = synth.make_prefill(wl)
+    q, k = inp.q[0], inp.k[0]
+    N = q.shape[0]
+    v = synth.make_values(1, N, wl.Hkv, seed=wl.seed)[0]
+    sel = run_prefill(inp.q, inp.k, wl.topk, wl.dtype)
+    got = _run_attention(q, k, v, sel.idx[0], wl.topk)
+    rng = np.random.default_rng(seed)
+    ts = np.arange(N) if n_rows is None else np.unique(np.concatenate(
+        [[0, 63, 64, N - 1], rng.choice(N, n_rows, replace=False)])).astype(np.int64)
+    o_idx, _, _ = oracle.walk(q[ts], ts, k, oracle.build_pyramid(k), wl.topk)
+    same = np.all(o_idx == sel.idx[0][ts], axis=(1, 2))
+    ref = oracle.attention(q[ts], ts, k, v, o_idx)
+    print(f"{wl_name}: {int(same.sum())} of {len(ts)} rows with identical selections compared", flush=True)
+    assert same.mean() > 0.95
+    return _check(got[ts][same], ref[same], v)
+
+
+def test_attention_after_gpu_selection_short():
+    """Selection and attention both on the GPU (4096 positions), all rows."""
+    _end_to_end("short", None)
+
+
+def test_attention_after_gpu_selection_long256k():
+    """The full 262144-position workload: sampled rows against the oracle."""
+    _end_to_end("long256k", 400)
