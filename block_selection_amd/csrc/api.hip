@@ -44,9 +44,9 @@ template <int S>
 __global__ void leaf_cluster_kernel(const uint16_t*, const uint16_t*, Geom, ClusterGeom, Pack, int64_t,
                                     const int4*, const uint2*, uint32_t*, float*, float*);
 
-__global__ void vt_tiles_kernel(const uint16_t*, Geom, int64_t, uint16_t*);
+__global__ void vt_tiles_kernel(const uint16_t*, Geom, Pack, int64_t, uint16_t*);
 __global__ void sparse_attention_kernel(const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*, Geom,
-                                        int64_t, float*);
+                                        Pack, int64_t, float*);
 
 // The kernels that score candidates are built once per candidate score (pisa_score);
 // these pick the build for G.score.
@@ -643,6 +643,18 @@ static size_t attention_ws(const pisa_dims* d, int64_t N) {
     return align_up((size_t)d->B * d->Hkv * nblk * kD * kC * sizeof(uint16_t));
 }
 
+// V re-layout, then one wavefront per (position, KV head). nblk: tiles per (batch, KV head),
+// or packed tile slots per KV head.
+static int attention_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx, const Geom& G,
+                          const Pack& pk, int64_t nblk, float* out, uint16_t* vt, hipStream_t s) {
+    const int64_t walks = (int64_t)G.B * G.N * G.Hkv;
+    hipLaunchKernelGGL(vt_tiles_kernel, dim3((unsigned)nblk, (unsigned)(G.B * G.Hkv)), dim3(256), 0, s, v, G, pk,
+                       nblk, vt);
+    hipLaunchKernelGGL(sparse_attention_kernel, dim3((unsigned)((walks + 3) / 4)), dim3(256), 0, s, q, k,
+                       (const uint16_t*)vt, idx, G, pk, nblk, out);
+    return launch_status();
+}
+
 size_t pisa_attention_workspace_bytes(const pisa_dims* dims, int64_t N, int64_t n_capacity) {
     Geom G;
     if (check_dims(dims) != PISA_OK || make_geom(dims, N, n_capacity, &G) != PISA_OK) return 0;
@@ -663,13 +675,8 @@ int pisa_sparse_attention(const void* q, const void* k, const void* v, const int
     const int64_t grid = (walks + 3) / 4;
     if ((int64_t)dims->B * dims->Hkv > 65535 || grid > INT_MAX || nblk > INT_MAX) return PISA_ERR_UNSUPPORTED;
     if (!workspace || ws_bytes < attention_ws(dims, N)) return PISA_ERR_WORKSPACE;
-    hipStream_t s = (hipStream_t)stream;
-    uint16_t* vt = (uint16_t*)workspace;
-    hipLaunchKernelGGL(vt_tiles_kernel, dim3((unsigned)nblk, (unsigned)(dims->B * dims->Hkv)), dim3(256), 0, s,
-                       (const uint16_t*)v, G, nblk, vt);
-    hipLaunchKernelGGL(sparse_attention_kernel, dim3((unsigned)grid), dim3(256), 0, s, (const uint16_t*)q,
-                       (const uint16_t*)k, (const uint16_t*)vt, idx, G, nblk, out);
-    return launch_status();
+    return attention_impl((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, G, Pack{nullptr, 0, 0},
+                          nblk, out, (uint16_t*)workspace, (hipStream_t)stream);
 }
 
 // ------------------------------------------------------------------ packed documents --
@@ -731,6 +738,31 @@ int pisa_select_prefill_packed(const void* q, const void* k, const float* pyrami
     const Pack pk{cu_seqlens, (int32_t)D, T};
     return select_pack_impl((const uint16_t*)q, (const uint16_t*)k, pyramid, G, pk, out_idx, W,
                             (hipStream_t)stream, nullptr);
+}
+
+// Packs: V tiles in the packed slots, (T >> 6) + D + 1 per KV head.
+static int64_t pack_tile_slots(int64_t T, int64_t D) { return (T >> kLog2C) + D + 1; }
+
+size_t pisa_pack_attention_workspace_bytes(const pisa_dims* dims, int64_t T, int64_t D) {
+    Geom G;
+    if (check_pack(dims, T, D, &G) != PISA_OK) return 0;
+    return align_up((size_t)dims->Hkv * pack_tile_slots(T, D) * kD * kC * sizeof(uint16_t));
+}
+
+int pisa_sparse_attention_packed(const void* q, const void* k, const void* v, const int32_t* idx,
+                                 const int32_t* cu_seqlens, int64_t D, int64_t T, const pisa_dims* dims,
+                                 float* out, void* workspace, size_t ws_bytes, void* stream) {
+    Geom G;
+    int rc = check_pack(dims, T, D, &G);
+    if (rc != PISA_OK) return rc;
+    if (!q || !k || !v || !idx || !cu_seqlens || !out) return PISA_ERR_INVALID_ARG;
+    if (dims->dtype != PISA_DTYPE_BF16) return PISA_ERR_UNSUPPORTED;
+    const int64_t nslots = pack_tile_slots(T, D);
+    if ((T * dims->Hkv + 3) / 4 > INT_MAX || nslots > INT_MAX || dims->Hkv > 65535) return PISA_ERR_UNSUPPORTED;
+    if (!workspace || ws_bytes < pisa_pack_attention_workspace_bytes(dims, T, D)) return PISA_ERR_WORKSPACE;
+    const Pack pk{cu_seqlens, (int32_t)D, T};
+    return attention_impl((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, G, pk, nslots, out,
+                          (uint16_t*)workspace, (hipStream_t)stream);
 }
 
 const char* pisa_status_string(int status) {

@@ -40,19 +40,31 @@ __device__ inline void split_bf16(float p, uint32_t& hi, uint32_t& lo) {
 }
 
 // V [B, cap, Hkv, 64] -> tiles [B*Hkv][nblk][64 dims][64 key slots] (keys >= N are zero).
-// Grid: (nblk, B*Hkv), 256 threads.
-__global__ __launch_bounds__(256) void vt_tiles_kernel(const uint16_t* __restrict__ v, Geom G, int64_t nblk,
-                                                       uint16_t* __restrict__ vt) {
+// Grid: (nblk, B*Hkv), 256 threads. With a pack (pk.cu non-null, B = 1): tile slots of the
+// packed layout, block j of document d at slot (cu[d] >> 6) + d + j (nblk slots per KV
+// head); a slot that names no block is left unwritten.
+__global__ __launch_bounds__(256) void vt_tiles_kernel(const uint16_t* __restrict__ v, Geom G, Pack pk,
+                                                       int64_t nblk, uint16_t* __restrict__ vt) {
     __shared__ uint16_t tile[kC][kD + 2];
     const int blk = blockIdx.x, bh = blockIdx.y;
     const int b = bh / G.Hkv, kvh = bh % G.Hkv;
     const int tid = threadIdx.x;
+    int64_t row0 = (int64_t)b * G.cap, nkeys = G.N, key0 = (int64_t)blk * kC;   // rows of this tile's sequence
+    if (pk.cu) {
+        const int d = pack_find_slot(pk, kLog2C, blk);
+        const Seg sg = pack_seg(pk, d);
+        const int64_t j = blk - ((sg.lsh >> kLog2C) + d);
+        if (sg.N == 0 || j < 0 || j * kC >= sg.N) return;
+        row0 = sg.tk0;
+        nkeys = sg.N;
+        key0 = j * kC;
+    }
     {
         const int kk = tid >> 2, part = tid & 3;           // key kk, dims 16 part .. +15
-        const int64_t key = (int64_t)blk * kC + kk;
+        const int64_t key = key0 + kk;
         u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
-        if (key < G.N) {
-            const uint16_t* src = v + (((int64_t)b * G.cap + key) * G.Hkv + kvh) * kD + 16 * part;
+        if (key < nkeys) {
+            const uint16_t* src = v + ((row0 + key) * G.Hkv + kvh) * kD + 16 * part;
             x0 = *reinterpret_cast<const u32x4*>(src);
             x1 = *reinterpret_cast<const u32x4*>(src + 8);
         }
@@ -80,6 +92,12 @@ __global__ __launch_bounds__(256) void vt_tiles_kernel(const uint16_t* __restric
     }
 }
 
+__device__ inline int64_t uniform_i64(int64_t x) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // K fragments of one block: A operand rows = keys 16 tau + n, k-steps dims 8g.. and 32 + 8g..
 struct KFrag {
     u32x4 a[4][2];
@@ -99,22 +117,40 @@ __device__ inline void load_kfrag(const uint16_t* __restrict__ base, int64_t nke
 
 // One wavefront per walk w = (b * N + t) * Hkv + kvh, four per workgroup. idx: [walks][K]
 // selected blocks (entries < 0, or past t's block, are skipped); out: fp32 [B, N, Hq, 64].
+// With a pack (pk.cu non-null, B = 1, N = T): row t lies in document d, its position and
+// block indices count from cu[d], and its keys, values and tiles are the document's.
 __global__ __launch_bounds__(kAttnThreads, 3) void sparse_attention_kernel(const uint16_t* __restrict__ q,
                                                                         const uint16_t* __restrict__ k,
                                                                         const uint16_t* __restrict__ vt,
                                                                         const int32_t* __restrict__ idx, Geom G,
-                                                                        int64_t nblk, float* __restrict__ out) {
+                                                                        Pack pk, int64_t nblk,
+                                                                        float* __restrict__ out) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int gq = lane >> 4, n = lane & 15;
     const int64_t walks = (int64_t)G.B * G.N * G.Hkv;
     const int64_t w = (int64_t)blockIdx.x * (kAttnThreads / 64) + wave;
     if (w >= walks) return;                                // whole wavefronts leave together
     const int kvh = (int)(w % G.Hkv);
-    const int64_t bt = w / G.Hkv, b = bt / G.N, t = bt % G.N;
+    const int64_t bt = w / G.Hkv;
+    int64_t b = bt / G.N, t = bt % G.N;                    // sequence and position
+    int64_t krow0 = b * G.cap, nkeys = G.N, tile0 = b * G.Hkv * nblk + kvh * nblk;
+    if (pk.cu) {
+        const int d = pack_find_token(pk, bt);
+        const Seg sg = pack_seg(pk, d);
+        t = bt - sg.lsh;
+        krow0 = sg.tk0;
+        nkeys = sg.N;
+        tile0 = kvh * nblk + (sg.lsh >> kLog2C) + d;
+    }
+    // wavefront-uniform: keep them in scalar registers
+    t = uniform_i64(t);
+    krow0 = uniform_i64(krow0);
+    nkeys = uniform_i64(nkeys);
+    tile0 = uniform_i64(tile0);
     const int K = G.topk;
     const int64_t row_stride = (int64_t)G.Hkv * kD;
-    const uint16_t* kbase = k + (b * G.cap * G.Hkv + kvh) * kD;   // key r at kbase + r * row_stride
-    const uint16_t* vtb = vt + ((b * G.Hkv + kvh) * nblk) * (int64_t)(kD * kC);
+    const uint16_t* kbase = k + (krow0 * G.Hkv + kvh) * kD;   // key r at kbase + r * row_stride
+    const uint16_t* vtb = vt + tile0 * (int64_t)(kD * kC);
 
     // queries: B operand, head n of the group (columns n >= GQ read head 0, not written)
     u32x4 qa, qb;
@@ -143,7 +179,7 @@ __global__ __launch_bounds__(kAttnThreads, 3) void sparse_attention_kernel(const
     KFrag cur;   // this block's key fragments; refilled with the next block's once the logits are issued
     if (nsel > 0) {
         const int b0 = readlane_i(sel, 0);
-        load_kfrag(kbase + (int64_t)b0 * kC * row_stride, G.N - (int64_t)b0 * kC, row_stride, n, gq, cur);
+        load_kfrag(kbase + (int64_t)b0 * kC * row_stride, nkeys - (int64_t)b0 * kC, row_stride, n, gq, cur);
     }
     for (int s = 0; s < nsel; ++s) {
         const int blk = readlane_i(sel, s);
@@ -167,7 +203,7 @@ __global__ __launch_bounds__(kAttnThreads, 3) void sparse_attention_kernel(const
         }
         if (s + 1 < nsel) {
             const int bn = readlane_i(sel, s + 1);
-            load_kfrag(kbase + (int64_t)bn * kC * row_stride, G.N - (int64_t)bn * kC, row_stride, n, gq, cur);
+            load_kfrag(kbase + (int64_t)bn * kC * row_stride, nkeys - (int64_t)bn * kC, row_stride, n, gq, cur);
         }
         // scale to base 2, mask keys after t, block maximum per column
         const int64_t lim = t - k0;                          // keys 0 .. lim of the block are visible

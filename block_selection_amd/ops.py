@@ -31,7 +31,7 @@ EXPORTED = ("pisa_pyramid_nodes", "pisa_level_offset", "pisa_pyramid_bytes", "pi
             "pisa_decode_update_select", "pisa_status_string", "pisa_pack_pyramid_rows",
             "pisa_pack_level_offset", "pisa_pack_pyramid_bytes", "pisa_pack_workspace_bytes",
             "pisa_build_pyramid_packed", "pisa_select_prefill_packed", "pisa_attention_workspace_bytes",
-            "pisa_sparse_attention")
+            "pisa_sparse_attention", "pisa_pack_attention_workspace_bytes", "pisa_sparse_attention_packed")
 
 
 class Dims(ctypes.Structure):
@@ -89,6 +89,10 @@ def _load() -> ctypes.CDLL:
     lib.pisa_attention_workspace_bytes.restype = sz
     lib.pisa_sparse_attention.argtypes = [P, P, P, P, i64, i64, D, P, P, sz, P]
     lib.pisa_sparse_attention.restype = ctypes.c_int
+    lib.pisa_pack_attention_workspace_bytes.argtypes = [D, i64, i64]
+    lib.pisa_pack_attention_workspace_bytes.restype = sz
+    lib.pisa_sparse_attention_packed.argtypes = [P, P, P, P, P, i64, i64, D, P, P, sz, P]
+    lib.pisa_sparse_attention_packed.restype = ctypes.c_int
     lib.pisa_status_string.argtypes = [ctypes.c_int]
     lib.pisa_status_string.restype = ctypes.c_char_p
     return lib
@@ -296,3 +300,31 @@ def sparse_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: tor
                                    _ptr(out), _ptr(workspace), ws_n, _stream(stream))
     if rc != PISA_OK:
         raise PisaError("pisa_sparse_attention", rc)
+
+
+def pack_attention_workspace_bytes(dims: Dims, T: int, D: int) -> int:
+    return int(lib.pisa_pack_attention_workspace_bytes(ctypes.byref(dims), T, D))
+
+
+def alloc_pack_attention_workspace(dims: Dims, T: int, D: int, device="cuda") -> Optional[torch.Tensor]:
+    n = pack_attention_workspace_bytes(dims, T, D)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def sparse_attention_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                            cu_seqlens: torch.Tensor, dims: Dims, out: torch.Tensor,
+                            workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Attention over the selected blocks of a pack: idx [T, Hkv, K] of document-local blocks (as
+    select_prefill_packed writes them); each row attends inside its own document only."""
+    D, T = cu_seqlens.numel() - 1, q.shape[0]
+    _check(q, "q", dims.torch_dtype, T * dims.Hq * dims.d)
+    _check(k, "k", dims.torch_dtype, T * dims.Hkv * dims.d)
+    _check(v, "v", dims.torch_dtype, T * dims.Hkv * dims.d)
+    _check(idx, "idx", torch.int32, T * dims.Hkv * dims.topk)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, D + 1)
+    _check(out, "out", torch.float32, T * dims.Hq * dims.d)
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.pisa_sparse_attention_packed(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(cu_seqlens), D, T,
+                                          ctypes.byref(dims), _ptr(out), _ptr(workspace), ws_n, _stream(stream))
+    if rc != PISA_OK:
+        raise PisaError("pisa_sparse_attention_packed", rc)

@@ -256,6 +256,21 @@ int pisa_select_prefill_packed(const void* q, const void* k, const float* pyrami
                                const pisa_dims* dims, int32_t* out_idx, void* workspace,
                                size_t ws_bytes, void* stream);
 
+/* Device workspace of pisa_sparse_attention_packed (0 on bad input): the value rows as
+ * per-block tiles in packed slots, Hkv * ((T >> 6) + D + 1) * 64 * 64 bf16. */
+size_t pisa_pack_attention_workspace_bytes(const pisa_dims* dims, int64_t T, int64_t D);
+
+/*
+ * Attention over the selected blocks for every row of a pack (bf16 only): each row
+ * attends over the keys <= its position of its own document's selected blocks, as
+ * pisa_sparse_attention does for that document alone.
+ *   q [T, Hq, d]; k, v [T, Hkv, d]; idx int32 [T, Hkv, topk] of document-local blocks
+ *   (as pisa_select_prefill_packed writes them); out fp32 [T, Hq, d].
+ */
+int pisa_sparse_attention_packed(const void* q, const void* k, const void* v, const int32_t* idx,
+                                 const int32_t* cu_seqlens, int64_t D, int64_t T, const pisa_dims* dims,
+                                 float* out, void* workspace, size_t ws_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* pisa_status_string(int status);
 

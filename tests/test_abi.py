@@ -132,3 +132,19 @@ def test_attention_argument_errors_return_before_launch():
     assert att(ops.make_dims(1, 32, 2, 8, dtype="f32")) == ops.PISA_ERR_UNSUPPORTED
     assert att(ops.make_dims(1, 32, 2, 8, d=128)) == ops.PISA_ERR_UNSUPPORTED
     assert att(good, ws_bytes=16) == ops.PISA_ERR_WORKSPACE
+
+
+def test_packed_attention_argument_errors_return_before_launch():
+    from block_selection_amd import ops
+    p = ctypes.c_void_p(8)
+    good = ops.make_dims(1, 32, 2, 8)
+
+    def att(dims, cu=p, D=3, T=4096, ws_bytes=1 << 34):
+        return ops.lib.pisa_sparse_attention_packed(p, p, p, p, cu, D, T, ctypes.byref(dims), p, p, ws_bytes, None)
+
+    assert ops.pack_attention_workspace_bytes(good, 4096, 3) == 2 * ((4096 >> 6) + 4) * 64 * 64 * 2
+    assert att(good, cu=None) == ops.PISA_ERR_INVALID_ARG
+    assert att(good, D=0) == ops.PISA_ERR_INVALID_ARG
+    assert att(ops.make_dims(2, 32, 2, 8)) == ops.PISA_ERR_INVALID_ARG
+    assert att(ops.make_dims(1, 32, 2, 8, dtype="f32")) == ops.PISA_ERR_UNSUPPORTED
+    assert att(good, ws_bytes=16) == ops.PISA_ERR_WORKSPACE

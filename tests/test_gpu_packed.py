@@ -149,3 +149,79 @@ def test_packed_long_pack_sampled():
     tl = np.arange(T) - v.cu[docs]
     assert idx.min() >= -1
     assert np.all(idx.max(axis=2) <= (tl // 64)[:, None])
+
+
+def _run_packed_attention(v: synth.VarlenInputs, vals: np.ndarray, idx: np.ndarray, topk: int):
+    from block_selection_amd import ops
+    T, Hq, _ = v.q.shape
+    Hkv = v.k.shape[1]
+    D = len(v.cu) - 1
+    print(f"packed attention T={T} D={D} Hq={Hq} Hkv={Hkv} K={topk}", flush=True)
+    dims = ops.make_dims(1, Hq, Hkv, topk, "bf16")
+    cu = torch.from_numpy(np.ascontiguousarray(v.cu, np.int32)).cuda()
+    out = torch.full((T, Hq, 64), float("nan"), dtype=torch.float32, device="cuda")
+    it = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).cuda()
+    ops.sparse_attention_packed(to_device(v.q, "bf16"), to_device(v.k, "bf16"), to_device(vals, "bf16"), it, cu, dims,
+                                out, ops.alloc_pack_attention_workspace(dims, T, D))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("K", [8, 32])
+def test_packed_attention(K):
+    """Attention of every row over its own document's selected blocks: the oracle per document
+    (on the oracle's selection), and bitwise the single-sequence attention of each document."""
+    from block_selection_amd import ops
+    v = synth.make_varlen(sum(EDGE_LENGTHS), 32, 2, "bf16", lengths=EDGE_LENGTHS, seed=40 + K)
+    vals = synth.make_values(1, int(v.cu[-1]), 2, seed=K)[0]
+    o_idx, _, _ = oracle.varlen_walk(v.q, v.k, v.cu, K)
+    got = _run_packed_attention(v, vals, o_idx, K)
+    assert np.all(np.isfinite(got))
+    scale = float(np.abs(vals).max())
+    worst = 0.0
+    for j in range(len(EDGE_LENGTHS)):
+        lo, hi = int(v.cu[j]), int(v.cu[j + 1])
+        if hi == lo:
+            continue
+        n = hi - lo
+        ref = oracle.attention(v.q[lo:hi], np.arange(n), v.k[lo:hi], vals[lo:hi], o_idx[lo:hi])
+        worst = max(worst, float(np.abs(got[lo:hi] - ref).max()) / scale)
+        # the same document alone through pisa_sparse_attention
+        dims = ops.make_dims(1, 32, 2, K, "bf16")
+        alone = torch.empty((1, n, 32, 64), dtype=torch.float32, device="cuda")
+        ops.sparse_attention(to_device(v.q[None, lo:hi], "bf16"), to_device(v.k[None, lo:hi], "bf16"),
+                             to_device(vals[None, lo:hi], "bf16"),
+                             torch.from_numpy(np.ascontiguousarray(o_idx[None, lo:hi])).cuda(), n, n, dims, alone,
+                             ops.alloc_attention_workspace(dims, n))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(got[lo:hi], alone.cpu().numpy()[0])
+    print(f"packed attention max |err| / max|v| = {worst:.3e}", flush=True)
+    assert worst <= 1e-4
+
+
+def test_packed_selection_then_attention_long():
+    """A 65536-token pack: GPU selection, then GPU attention on it, sampled rows of every
+    document against the oracle's selection and attention."""
+    from block_selection_amd import ops
+    v = synth.make_varlen(65536, 32, 2, "bf16", mean_len=4096.0, seed=9)
+    vals = synth.make_values(1, 65536, 2, seed=9)[0]
+    dims, pyr, idx = _run_packed(v, 8)
+    got = _run_packed_attention(v, vals, idx, 8)
+    rng = np.random.default_rng(2)
+    scale = float(np.abs(vals).max())
+    compared = 0
+    for j in range(len(v.cu) - 1):
+        lo, hi = int(v.cu[j]), int(v.cu[j + 1])
+        if hi == lo:
+            continue
+        n = hi - lo
+        ts = np.unique(np.concatenate([[0, n - 1], rng.choice(n, min(n, 16), replace=False)])).astype(np.int64)
+        kd = v.k[lo:hi]
+        o_idx, _, _ = oracle.walk(v.q[lo:hi][ts], ts, kd, oracle.build_pyramid(kd), 8)
+        same = np.all(o_idx == idx[lo + ts], axis=(1, 2))
+        ref = oracle.attention(v.q[lo:hi][ts], ts, kd, vals[lo:hi], o_idx)
+        err = np.abs(got[lo + ts][same] - ref[same]).max() / scale if same.any() else 0.0
+        assert err <= 1e-4, (j, err)
+        compared += int(same.sum())
+    print(f"packed selection + attention: {compared} rows compared", flush=True)
+    assert compared > 200
