@@ -517,12 +517,33 @@ def decode_bench(torch, ops, synth, dev, log):
         torch.cuda.synchronize()
         if rep:
             fl = [ev[s].elapsed_time(ev[s + 1]) * 1e3 for s in range(steps)]
+    # the same steps, each followed by attention over its selection (pisa_decode_attention,
+    # which also appends the step's value row)
+    vals = synth.make_values(1, cap, wl.Hkv, seed=wl.seed)
+    v_cache = dev_t(vals)
+    vn = [v_cache[0, N0 + s].unsqueeze(0).contiguous() for s in range(steps)]
+    att = torch.empty((1, wl.Hq, wl.d), dtype=torch.float32, device=dev)
+    att_times = []
+    for rep in range(2):
+        ops.build_pyramid(k_cache, N0, cap, dims, pyr)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for s in range(steps):
+            ops.decode_update_select(qn[s], kn[s], k_cache, pyr, N0 + s, cap, dims, out, ws)
+            ops.decode_attention(qn[s], vn[s], k_cache, v_cache, out, N0 + s, cap, dims, att)
+            ev[s + 1].record(stream)
+        torch.cuda.synchronize()
+        if rep:
+            att_times = [ev[s].elapsed_time(ev[s + 1]) * 1e3 for s in range(steps)]
     per = np.array(times)
     res = {"context": N0, "steps": steps, "K": wl.topk, "us_per_step_mean": float(per.mean()),
+           "us_per_step_with_attention": float(np.mean(att_times)),
            "empty_kernel_launch_us": float(np.mean(fl)),
            "us_per_step_median": float(np.median(per)), "us_per_step_p90": float(np.percentile(per, 90)),
            "steps_per_s": 1e6 / float(per.mean())}
-    log(f"decode: {res['us_per_step_mean']:.1f} us/step")
+    log(f"decode: {res['us_per_step_mean']:.1f} us/step, {res['us_per_step_with_attention']:.1f} us/step with "
+        f"attention over the selected blocks")
     return res
 
 

@@ -47,6 +47,8 @@ __global__ void leaf_cluster_kernel(const uint16_t*, const uint16_t*, Geom, Clus
 __global__ void vt_tiles_kernel(const uint16_t*, Geom, Pack, int64_t, uint16_t*);
 __global__ void sparse_attention_kernel(const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*, Geom,
                                         Pack, int64_t, float*);
+__global__ void decode_attention_kernel(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, const int32_t*,
+                                        Geom, int64_t, float*);
 
 // The kernels that score candidates are built once per candidate score (pisa_score);
 // these pick the build for G.score.
@@ -738,6 +740,22 @@ int pisa_select_prefill_packed(const void* q, const void* k, const float* pyrami
     const Pack pk{cu_seqlens, (int32_t)D, T};
     return select_pack_impl((const uint16_t*)q, (const uint16_t*)k, pyramid, G, pk, out_idx, W,
                             (hipStream_t)stream, nullptr);
+}
+
+int pisa_decode_attention(const void* q_new, const void* v_new, const void* k_cache, void* v_cache,
+                          const int32_t* idx, int64_t t, int64_t n_capacity, const pisa_dims* dims, float* out,
+                          void* stream) {
+    int rc = check_dims(dims);
+    if (rc != PISA_OK) return rc;
+    if (!q_new || !k_cache || !v_cache || !idx || !out) return PISA_ERR_INVALID_ARG;
+    if (t < 0) return PISA_ERR_INVALID_ARG;
+    Geom G;
+    if ((rc = make_geom(dims, t + 1, n_capacity, &G)) != PISA_OK) return rc;
+    if (dims->dtype != PISA_DTYPE_BF16) return PISA_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(decode_attention_kernel, dim3((unsigned)(dims->B * dims->Hkv)), dim3(1024), 0, (hipStream_t)stream,
+                       (const uint16_t*)q_new, (const uint16_t*)v_new, (const uint16_t*)k_cache, (uint16_t*)v_cache,
+                       idx, G, t, out);
+    return launch_status();
 }
 
 // Packs: V tiles in the packed slots, (T >> 6) + D + 1 per KV head.

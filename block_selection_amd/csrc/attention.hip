@@ -272,3 +272,185 @@ __global__ __launch_bounds__(kAttnThreads, 3) void sparse_attention_kernel(const
 }
 
 }  // namespace pisa
+
+namespace pisa {
+
+// ------------------------------------------------------------------ decoding step --
+// Attention of one decoding query per (batch, KV head) over its selected blocks: one
+// workgroup of kDecAttnWaves wavefronts; wavefront i takes selected blocks i, i + 16, ...
+// with the same tiles and online softmax as the prefill kernel, the value block staged
+// in its own LDS tile in the permuted [dim][key] order, and the sixteen partial results
+// (running maximum, exp sum, unnormalised output per head) are merged in LDS (the
+// output partials reuse the tile memory).
+constexpr int kDecAttnWaves = 16;
+
+// v_new (may be null): the new token's value row per (batch, KV head), written to row t of v
+// before anything reads it.
+__global__ __launch_bounds__(64 * kDecAttnWaves) void decode_attention_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ v_new, const uint16_t* __restrict__ k,
+    uint16_t* __restrict__ v, const int32_t* __restrict__ idx, Geom G, int64_t t, float* __restrict__ out) {
+    __shared__ uint16_t s_vt[kDecAttnWaves][kD * kC];       // 8 KiB per wavefront
+    __shared__ float s_m[kDecAttnWaves][kMaxGroup], s_l[kDecAttnWaves][kMaxGroup];
+    static_assert(sizeof(float) * kDecAttnWaves * kMaxGroup * kD <= sizeof(uint16_t) * kDecAttnWaves * kD * kC,
+                  "the output partials fit the tile memory");
+    float (*s_o)[kMaxGroup][kD] = reinterpret_cast<float (*)[kMaxGroup][kD]>(&s_vt[0][0]);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int gq = lane >> 4, n = lane & 15;
+    const int bh = blockIdx.x, b = bh / G.Hkv, kvh = bh % G.Hkv;
+    const int K = G.topk;
+    const int64_t row_stride = (int64_t)G.Hkv * kD;
+    const uint16_t* kbase = k + ((int64_t)b * G.cap * G.Hkv + kvh) * kD;
+    const uint16_t* vbase = v + ((int64_t)b * G.cap * G.Hkv + kvh) * kD;
+    if (v_new) {
+        if (threadIdx.x < kD) v[(((int64_t)b * G.cap + t) * G.Hkv + kvh) * kD + threadIdx.x] = v_new[(int64_t)bh * kD + threadIdx.x];
+        __syncthreads();   // the row is read below by this workgroup only
+    }
+    u32x4 qa, qb;
+    {
+        const uint16_t* qrow = q + ((int64_t)b * G.Hq + (int64_t)kvh * G.GQ + (n < G.GQ ? n : 0)) * kD;
+        qa = *reinterpret_cast<const u32x4*>(qrow + 8 * gq);
+        qb = *reinterpret_cast<const u32x4*>(qrow + 32 + 8 * gq);
+    }
+    const bf16x8 q0 = __builtin_bit_cast(bf16x8, qa), q1 = __builtin_bit_cast(bf16x8, qb);
+    const int64_t tblk = t >> kLog2C;
+    int sel = (lane < K) ? idx[(int64_t)bh * K + lane] : -1;
+    const bool ok = sel >= 0 && sel <= tblk;
+    const uint64_t vm = ballot(ok);
+    const int nsel = __popcll(vm);
+    sel = push_to_lane(ok ? lanes_below(vm) : nsel + lanes_below(~vm), ok ? sel : -1);
+
+    float m = -INFINITY, lsum = 0.0f;
+    f32x4 o[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint16_t* tile = s_vt[wave];
+    for (int s = wave; s < nsel; s += kDecAttnWaves) {
+        const int blk = readlane_i(sel, s);
+        const int64_t k0 = (int64_t)blk * kC;
+        const int64_t nkeys = G.N - k0;
+        // value rows of the block -> this wavefront's LDS tile, [dim][slot of key]; all eight
+        // loads in flight together (rows past the keys read the last key and store zeros)
+        u32x4 vx[8];
+        const int part = lane & 7;                                  // dims 8 part .. +7
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int kk = 8 * i + (lane >> 3);
+            const int64_t kr = (kk < nkeys) ? kk : nkeys - 1;
+            vx[i] = *reinterpret_cast<const u32x4*>(vbase + (k0 + kr) * row_stride + 8 * part);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int kk = 8 * i + (lane >> 3);
+            const bool in = kk < nkeys;
+            const int slot = 32 * (kk >> 5) + 8 * ((kk >> 2) & 3) + 4 * ((kk >> 4) & 1) + (kk & 3);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t x = in ? vx[i][e] : 0u;
+                tile[(8 * part + 2 * e) * kC + slot] = (uint16_t)(x & 0xffffu);
+                tile[(8 * part + 2 * e + 1) * kC + slot] = (uint16_t)(x >> 16);
+            }
+        }
+        KFrag kf;
+        load_kfrag(kbase + k0 * row_stride, nkeys, row_stride, n, gq, kf);
+        f32x4 acc[4];
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau) {
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf.a[tau][0]), q0, c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf.a[tau][1]), q1, c, 0, 0, 0);
+            acc[tau] = c;
+        }
+        const int64_t lim = t - k0;
+        float mb = -INFINITY;
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x = acc[tau][r] * kScale2;
+                acc[tau][r] = (16 * tau + 4 * gq + r <= lim) ? x : -INFINITY;
+                mb = fmaxf(mb, acc[tau][r]);
+            }
+        mb = cols4_max(mb);
+        const float mn = fmaxf(m, mb);
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        m = mn;
+        float ps = 0.0f;
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = __builtin_amdgcn_exp2f(acc[tau][r] - mn);
+                acc[tau][r] = p;
+                ps += p;
+            }
+        lsum = lsum * alpha + ps;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[dt][r] *= alpha;
+        // the tile writes above come from this wavefront only: order them before its reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t h0, l0, h1, l1;
+                split_bf16(acc[2 * s2 + (e >> 1)][2 * (e & 1)], h0, l0);
+                split_bf16(acc[2 * s2 + (e >> 1)][2 * (e & 1) + 1], h1, l1);
+                hi[e] = h0 | (h1 << 16);
+                lo[e] = l0 | (l1 << 16);
+            }
+            const bf16x8 bhi = __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
+            const bf16x8 blo = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const u32x4 a = *reinterpret_cast<const lds_u32x4_t*>(
+                    (const lds_char_t*)tile + 2 * ((16 * dt + n) * kC + 32 * s2 + 8 * gq));
+                const bf16x8 av = __builtin_bit_cast(bf16x8, a);
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bhi, o[dt], 0, 0, 0);
+                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, blo, o[dt], 0, 0, 0);
+            }
+        }
+        // the next block's tile writes must not overtake these reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    // partials of this wavefront: column n = head n (the tiles are dead once every wavefront
+    // is past its last block)
+    const float l = cols4_sum(lsum);
+    __syncthreads();
+    if (gq == 0) {
+        s_m[wave][n] = m;
+        s_l[wave][n] = l;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s_o[wave][n][16 * dt + 4 * gq + r] = o[dt][r];
+    __syncthreads();
+    // merge: thread (head h, dims 2e, 2e+1)
+    for (int x = threadIdx.x; x < G.GQ * (kD / 2); x += 64 * kDecAttnWaves) {
+        const int h = x / (kD / 2), e = 2 * (x % (kD / 2));
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kDecAttnWaves; ++w) M = fmaxf(M, s_m[w][h]);
+        float den = 0.0f, n0 = 0.0f, n1 = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kDecAttnWaves; ++w) {
+            const float sc = (s_m[w][h] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s_m[w][h] - M);
+            den += sc * s_l[w][h];
+            n0 += sc * s_o[w][h][e];
+            n1 += sc * s_o[w][h][e + 1];
+        }
+        const float inv = (den > 0.0f) ? 1.0f / den : 0.0f;
+        float* orow = out + ((int64_t)b * G.Hq + (int64_t)kvh * G.GQ + h) * kD + e;
+        orow[0] = n0 * inv;
+        orow[1] = n1 * inv;
+    }
+}
+
+}  // namespace pisa

@@ -31,7 +31,8 @@ EXPORTED = ("pisa_pyramid_nodes", "pisa_level_offset", "pisa_pyramid_bytes", "pi
             "pisa_decode_update_select", "pisa_status_string", "pisa_pack_pyramid_rows",
             "pisa_pack_level_offset", "pisa_pack_pyramid_bytes", "pisa_pack_workspace_bytes",
             "pisa_build_pyramid_packed", "pisa_select_prefill_packed", "pisa_attention_workspace_bytes",
-            "pisa_sparse_attention", "pisa_pack_attention_workspace_bytes", "pisa_sparse_attention_packed")
+            "pisa_sparse_attention", "pisa_pack_attention_workspace_bytes", "pisa_sparse_attention_packed",
+            "pisa_decode_attention")
 
 
 class Dims(ctypes.Structure):
@@ -93,6 +94,8 @@ def _load() -> ctypes.CDLL:
     lib.pisa_pack_attention_workspace_bytes.restype = sz
     lib.pisa_sparse_attention_packed.argtypes = [P, P, P, P, P, i64, i64, D, P, P, sz, P]
     lib.pisa_sparse_attention_packed.restype = ctypes.c_int
+    lib.pisa_decode_attention.argtypes = [P, P, P, P, P, i64, i64, D, P, P]
+    lib.pisa_decode_attention.restype = ctypes.c_int
     lib.pisa_status_string.argtypes = [ctypes.c_int]
     lib.pisa_status_string.restype = ctypes.c_char_p
     return lib
@@ -328,3 +331,21 @@ def sparse_attention_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, i
                                           ctypes.byref(dims), _ptr(out), _ptr(workspace), ws_n, _stream(stream))
     if rc != PISA_OK:
         raise PisaError("pisa_sparse_attention_packed", rc)
+
+
+def decode_attention(q_new: torch.Tensor, v_new: Optional[torch.Tensor], k_cache: torch.Tensor,
+                     v_cache: torch.Tensor, idx: torch.Tensor, t: int, n_capacity: int, dims: Dims,
+                     out: torch.Tensor, stream=None) -> None:
+    """Attention of the decoding query at position t over its selected blocks (idx as
+    decode_update_select writes it); v_new, if given, is written to row t of v_cache first."""
+    _check(q_new, "q_new", dims.torch_dtype, dims.B * dims.Hq * dims.d)
+    if v_new is not None:
+        _check(v_new, "v_new", dims.torch_dtype, dims.B * dims.Hkv * dims.d)
+    _check(k_cache, "k_cache", dims.torch_dtype, dims.B * n_capacity * dims.Hkv * dims.d)
+    _check(v_cache, "v_cache", dims.torch_dtype, dims.B * n_capacity * dims.Hkv * dims.d)
+    _check(idx, "idx", torch.int32, dims.B * dims.Hkv * dims.topk)
+    _check(out, "out", torch.float32, dims.B * dims.Hq * dims.d)
+    rc = lib.pisa_decode_attention(_ptr(q_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(idx), t, n_capacity,
+                                   ctypes.byref(dims), _ptr(out), _stream(stream))
+    if rc != PISA_OK:
+        raise PisaError("pisa_decode_attention", rc)

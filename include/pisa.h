@@ -256,6 +256,20 @@ int pisa_select_prefill_packed(const void* q, const void* k, const float* pyrami
                                const pisa_dims* dims, int32_t* out_idx, void* workspace,
                                size_t ws_bytes, void* stream);
 
+/*
+ * Attention of one decoding step (bf16 only), after pisa_decode_update_select has
+ * selected the blocks for the query at position t = n_before:
+ *   q_new   [B, Hq, d]; v_new [B, Hkv, d] or NULL: the new token's value row, written
+ *           to row t of v_cache first (pisa_decode_update_select writes only the key);
+ *   k_cache, v_cache [B, n_capacity, Hkv, d], rows 0..t valid;
+ *   idx     int32 [B, Hkv, topk] as pisa_decode_update_select writes it;
+ *   out     fp32 [B, Hq, d].
+ * One workgroup per (batch, KV head); no workspace.
+ */
+int pisa_decode_attention(const void* q_new, const void* v_new, const void* k_cache, void* v_cache,
+                          const int32_t* idx, int64_t t, int64_t n_capacity, const pisa_dims* dims, float* out,
+                          void* stream);
+
 /* Device workspace of pisa_sparse_attention_packed (0 on bad input): the value rows as
  * per-block tiles in packed slots, Hkv * ((T >> 6) + D + 1) * 64 * 64 bf16. */
 size_t pisa_pack_attention_workspace_bytes(const pisa_dims* dims, int64_t T, int64_t D);

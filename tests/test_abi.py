@@ -148,3 +148,17 @@ def test_packed_attention_argument_errors_return_before_launch():
     assert att(ops.make_dims(2, 32, 2, 8)) == ops.PISA_ERR_INVALID_ARG
     assert att(ops.make_dims(1, 32, 2, 8, dtype="f32")) == ops.PISA_ERR_UNSUPPORTED
     assert att(good, ws_bytes=16) == ops.PISA_ERR_WORKSPACE
+
+
+def test_decode_attention_argument_errors_return_before_launch():
+    from block_selection_amd import ops
+    p = ctypes.c_void_p(8)
+    good = ops.make_dims(1, 32, 2, 32)
+
+    def att(dims, t=100, cap=4096, ptr=p):
+        return ops.lib.pisa_decode_attention(ptr, None, p, p, p, t, cap, ctypes.byref(dims), p, None)
+
+    assert att(good, ptr=None) == ops.PISA_ERR_INVALID_ARG
+    assert att(good, t=-1) == ops.PISA_ERR_INVALID_ARG
+    assert att(good, t=4096) == ops.PISA_ERR_CAPACITY
+    assert att(ops.make_dims(1, 32, 2, 32, dtype="f32")) == ops.PISA_ERR_UNSUPPORTED

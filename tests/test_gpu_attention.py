@@ -128,3 +128,63 @@ def test_attention_after_gpu_selection_short():
 def test_attention_after_gpu_selection_long256k():
     """The full 262144-position workload: sampled rows against the oracle."""
     _end_to_end("long256k", 400)
+
+
+def test_decode_attention_on_the_oracle_selection():
+    """One decoding query per (batch, KV head): positions across block boundaries, K = 32,
+    the value row of the new token appended by the call."""
+    from block_selection_amd import ops
+    N, Hq, Hkv, K = 6000, 32, 2, 32
+    q, k, v = _inputs(N, Hq, Hkv, 21)
+    cap = N + 64
+    dims = ops.make_dims(1, Hq, Hkv, K, "bf16")
+    for t in (0, 63, 64, 2047, 4000, N - 1):
+        pyr = oracle.build_pyramid(k[:t + 1])
+        idx, _, _ = oracle.walk(q[t:t + 1], np.array([t]), k[:t + 1], pyr, K)
+        kk = np.zeros((1, cap, Hkv, 64), np.float32)
+        vv = np.zeros((1, cap, Hkv, 64), np.float32)
+        kk[0, :t + 1], vv[0, :t] = k[:t + 1], v[:t]
+        vv[0, t + 1:] = 7.0                               # rows after t must not matter
+        kt, vt = to_device(kk, "bf16"), to_device(vv, "bf16")
+        out = torch.full((1, Hq, 64), float("nan"), dtype=torch.float32, device="cuda")
+        print(f"decode attention t={t}", flush=True)
+        ops.decode_attention(to_device(q[t][None], "bf16"), to_device(v[t][None], "bf16"), kt, vt,
+                             torch.from_numpy(idx[0][None].copy()).cuda(), t, cap, dims, out)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(vt.float().cpu().numpy()[0, t], v[t])   # the appended row
+        ref = oracle.attention(q[t:t + 1], np.array([t]), k[:t + 1], v[:t + 1], idx)
+        _check(out.cpu().numpy(), ref, v)
+
+
+def test_decode_steps_select_then_attend():
+    """24 decoding steps over a 20000-key context: pisa_decode_update_select, then
+    pisa_decode_attention on its selection, against the oracle's selection and attention."""
+    from block_selection_amd import ops
+    N0, steps, Hq, Hkv, K = 20000, 24, 32, 2, 32
+    q, k, v = _inputs(N0 + steps, Hq, Hkv, 22)
+    cap = N0 + steps
+    dims = ops.make_dims(1, Hq, Hkv, K, "bf16")
+    kk = np.zeros((1, cap, Hkv, 64), np.float32)
+    vv = np.zeros((1, cap, Hkv, 64), np.float32)
+    kk[0, :N0], vv[0, :N0] = k[:N0], v[:N0]
+    kc, vc = to_device(kk, "bf16"), to_device(vv, "bf16")
+    pyr = ops.alloc_pyramid(dims, cap)
+    ops.build_pyramid(kc, N0, cap, dims, pyr)
+    ws = ops.alloc_workspace(dims, 1, cap, is_decode=True)
+    sel = torch.empty((1, Hkv, K), dtype=torch.int32, device="cuda")
+    out = torch.empty((1, Hq, 64), dtype=torch.float32, device="cuda")
+    compared = 0
+    for s in range(steps):
+        t = N0 + s
+        qn, kn, vn = to_device(q[t][None], "bf16"), to_device(k[t][None], "bf16"), to_device(v[t][None], "bf16")
+        ops.decode_update_select(qn, kn, kc, pyr, t, cap, dims, sel, ws)
+        ops.decode_attention(qn, vn, kc, vc, sel, t, cap, dims, out)
+        torch.cuda.synchronize()
+        o_idx, _, _ = oracle.walk(q[t:t + 1], np.array([t]), k[:t + 1], oracle.build_pyramid(k[:t + 1]), K)
+        if not np.array_equal(o_idx[0], sel.cpu().numpy()[0]):
+            continue
+        ref = oracle.attention(q[t:t + 1], np.array([t]), k[:t + 1], v[:t + 1], o_idx)
+        _check(out.cpu().numpy(), ref, v)
+        compared += 1
+    print(f"decode select + attend: {compared} of {steps} steps compared", flush=True)
+    assert compared >= steps - 2
