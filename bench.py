@@ -158,6 +158,35 @@ def measured_traffic(kernel_key: str, src_hash: str):
     return ent.get("bytes_per_launch")
 
 
+def copy_bandwidth(torch, dev, nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """Device-to-device copy rate (GB/s, bytes read + written) of a 1 GiB buffer: the
+    achievable HBM bandwidth the measured kernel traffic is compared with."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2 * nbytes / (ms / 1e3) / 1e9
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, topk: int, n_positions: int, seed: int = 1):
     """The fp64 oracle on the host cores, on a seeded sample of query positions."""
     import oracle
@@ -177,7 +206,7 @@ def cpu_baseline(inp, topk: int, n_positions: int, seed: int = 1):
     t2 = time.perf_counter()
     build_s, walk_s = t1 - t0, t2 - t1
     per_query = walk_s / len(ts) + build_s / N
-    return {"value": 1.0 / per_query, "unit": "queries/s", "cores": threads, "kind": "oracle",
+    return {"value": 1.0 / per_query, "unit": "queries/s", "cores": threads, "kind": "oracle", "cpu": _cpu_model(),
             "sample": (f"full fp64 pyramid build over N={N} keys ({build_s:.2f} s) plus walks for "
                        f"{len(ts)} seeded random query positions x {inp.k.shape[2]} KV heads "
                        f"({walk_s:.2f} s); queries/s = 1/(walk_s/positions + build_s/N)")}
@@ -359,9 +388,21 @@ def main():
         "select_compulsory_GBs": walk_bytes / walk_s / 1e9,
         "select_compulsory_frac_of_8TBs": walk_bytes / walk_s / 1e9 / HBM_PEAK_GBS,
     }
+    # the pages' IO ledger (reading note section 5.1: per walk, gK candidate blocks whose queries
+    # (GQ heads) and keys (C rows, shared by a tile of Qtile = 4 queries) cross HBM, 2-byte elements)
+    ledger = wl.B * N * wl.Hkv * wl.g * wl.topk * wl.d * (GQ + wl.C / 4) * 2
+    hbm["ledger_bytes"] = ledger
+    hbm["ledger_GBs"] = ledger / (ms_per_step / 1e3) / 1e9
+    hbm["ledger_frac_of_8TBs"] = hbm["ledger_GBs"] / HBM_PEAK_GBS
+    copy_gbs = copy_bandwidth(torch, q.device)
+    hbm["device_copy_GBs"] = copy_gbs
     if traffic:
         hbm["leaf_kernel_measured_GBs"] = traffic / (leaf_ms / 1e3) / 1e9
         hbm["leaf_kernel_measured_frac_of_8TBs"] = traffic / (leaf_ms / 1e3) / 1e9 / HBM_PEAK_GBS
+        hbm["leaf_kernel_measured_frac_of_copy"] = traffic / (leaf_ms / 1e3) / 1e9 / copy_gbs
+    if upper_traffic:
+        hbm["upper_kernel_measured_GBs"] = upper_traffic / (upper_ms / 1e3) / 1e9
+        hbm["upper_kernel_measured_frac_of_copy"] = upper_traffic / (upper_ms / 1e3) / 1e9 / copy_gbs
     work = {
         "select_ms": walk_ms.mean(),
         "upper_walk_ms": upper_ms,
@@ -387,6 +428,7 @@ def main():
         "config": {"workload": f"prefill selection {wl.name}", "B": wl.B, "N": N, "Hq": wl.Hq,
                    "Hkv": wl.Hkv, "d": wl.d, "C": wl.C, "g": wl.g, "K": wl.topk,
                    "step": "pisa_build_pyramid + pisa_select_prefill"},
+        "walks_per_s": wl.B * N * wl.Hkv / (ms_per_step / 1e3),
         "latency_ms": {"mean": ms_per_step, "median_build_plus_walk": float(np.median(build_ms + walk_ms)),
                        "min_build_plus_walk": float(np.min(build_ms + walk_ms))},
         "roofline": roofline,
