@@ -188,3 +188,45 @@ def test_decode_steps_select_then_attend():
         compared += 1
     print(f"decode select + attend: {compared} of {steps} steps compared", flush=True)
     assert compared >= steps - 2
+
+
+def test_attention_batched():
+    """B = 3 batch elements in one call, each against the oracle on its own selection."""
+    from block_selection_amd import ops
+    B, N, Hq, Hkv, K = 3, 1500, 16, 2, 8
+    rng = np.random.default_rng(31)
+    q = synth.bf16_round(rng.standard_normal((B, N, Hq, 64), dtype=np.float32))
+    k = synth.bf16_round(rng.standard_normal((B, N, Hkv, 64), dtype=np.float32))
+    v = synth.make_values(B, N, Hkv, seed=31)
+    idx = np.stack([oracle.walk(q[b], np.arange(N), k[b], oracle.build_pyramid(k[b]), K)[0] for b in range(B)])
+    dims = ops.make_dims(B, Hq, Hkv, K, "bf16")
+    print(f"attention batched B={B} N={N}", flush=True)
+    out = torch.full((B, N, Hq, 64), float("nan"), dtype=torch.float32, device="cuda")
+    ops.sparse_attention(to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16"),
+                         torch.from_numpy(np.ascontiguousarray(idx)).cuda(), N, N, dims, out,
+                         ops.alloc_attention_workspace(dims, N))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(B):
+        _check(got[b], oracle.attention(q[b], np.arange(N), k[b], v[b], idx[b]), v)
+
+
+def test_decode_attention_batched():
+    from block_selection_amd import ops
+    B, N, Hq, Hkv, K = 2, 3000, 32, 2, 32
+    rng = np.random.default_rng(32)
+    q = synth.bf16_round(rng.standard_normal((B, Hq, 64), dtype=np.float32))
+    k = synth.bf16_round(rng.standard_normal((B, N, Hkv, 64), dtype=np.float32))
+    v = synth.make_values(B, N, Hkv, seed=32)
+    t = N - 1
+    idx = np.stack([oracle.walk(q[b][None], np.array([t]), k[b], oracle.build_pyramid(k[b]), K)[0][0]
+                    for b in range(B)])
+    dims = ops.make_dims(B, Hq, Hkv, K, "bf16")
+    out = torch.empty((B, Hq, 64), dtype=torch.float32, device="cuda")
+    print(f"decode attention batched B={B} t={t}", flush=True)
+    ops.decode_attention(to_device(q, "bf16"), None, to_device(k, "bf16"), to_device(v, "bf16"),
+                         torch.from_numpy(np.ascontiguousarray(idx)).cuda(), t, N, dims, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(B):
+        _check(got[b][None], oracle.attention(q[b][None], np.array([t]), k[b], v[b], idx[b][None]), v)
