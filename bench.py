@@ -565,6 +565,7 @@ def decode_bench(torch, ops, synth, dev, log):
     v_cache = dev_t(vals)
     vn = [v_cache[0, N0 + s].unsqueeze(0).contiguous() for s in range(steps)]
     att = torch.empty((1, wl.Hq, wl.d), dtype=torch.float32, device=dev)
+    wsd = ops.alloc_decode_attention_workspace(dims, device=dev)
     att_times = []
     for rep in range(2):
         ops.build_pyramid(k_cache, N0, cap, dims, pyr)
@@ -573,7 +574,7 @@ def decode_bench(torch, ops, synth, dev, log):
         ev[0].record(stream)
         for s in range(steps):
             ops.decode_update_select(qn[s], kn[s], k_cache, pyr, N0 + s, cap, dims, out, ws)
-            ops.decode_attention(qn[s], vn[s], k_cache, v_cache, out, N0 + s, cap, dims, att)
+            ops.decode_attention(qn[s], vn[s], k_cache, v_cache, out, N0 + s, cap, dims, att, wsd)
             ev[s + 1].record(stream)
         torch.cuda.synchronize()
         if rep:

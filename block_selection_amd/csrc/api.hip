@@ -48,7 +48,9 @@ __global__ void vt_tiles_kernel(const uint16_t*, Geom, Pack, int64_t, uint16_t*)
 __global__ void sparse_attention_kernel(const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*, Geom,
                                         Pack, int64_t, float*);
 __global__ void decode_attention_kernel(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, const int32_t*,
-                                        Geom, int64_t, float*);
+                                        Geom, int64_t, uint32_t*, float*, float*);
+constexpr int kDecAttnBlocksPerGroup = 4;                          // wavefronts (blocks) per workgroup
+constexpr int kDecAttnStateFloats = 2 * kMaxGroup + kMaxGroup * kD;  // one partial softmax state
 
 // The kernels that score candidates are built once per candidate score (pisa_score);
 // these pick the build for G.score.
@@ -742,9 +744,24 @@ int pisa_select_prefill_packed(const void* q, const void* k, const float* pyrami
                             (hipStream_t)stream, nullptr);
 }
 
+// Decoding-step attention workspace: one completion counter per (batch, KV head) (zero
+// before the first call, left zero by every call), then the partial states.
+static size_t decode_attention_ws(const pisa_dims* d, size_t* counters) {
+    const int64_t bh = (int64_t)d->B * d->Hkv;
+    const int64_t parts = (d->topk + kDecAttnBlocksPerGroup - 1) / kDecAttnBlocksPerGroup;
+    const size_t c = align_up((size_t)bh * sizeof(uint32_t));
+    if (counters) *counters = c;
+    return c + align_up((size_t)bh * parts * kDecAttnStateFloats * sizeof(float));
+}
+
+size_t pisa_decode_attention_workspace_bytes(const pisa_dims* dims) {
+    if (check_dims(dims) != PISA_OK) return 0;
+    return decode_attention_ws(dims, nullptr);
+}
+
 int pisa_decode_attention(const void* q_new, const void* v_new, const void* k_cache, void* v_cache,
                           const int32_t* idx, int64_t t, int64_t n_capacity, const pisa_dims* dims, float* out,
-                          void* stream) {
+                          void* workspace, size_t ws_bytes, void* stream) {
     int rc = check_dims(dims);
     if (rc != PISA_OK) return rc;
     if (!q_new || !k_cache || !v_cache || !idx || !out) return PISA_ERR_INVALID_ARG;
@@ -752,9 +769,16 @@ int pisa_decode_attention(const void* q_new, const void* v_new, const void* k_ca
     Geom G;
     if ((rc = make_geom(dims, t + 1, n_capacity, &G)) != PISA_OK) return rc;
     if (dims->dtype != PISA_DTYPE_BF16) return PISA_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(decode_attention_kernel, dim3((unsigned)(dims->B * dims->Hkv)), dim3(1024), 0, (hipStream_t)stream,
-                       (const uint16_t*)q_new, (const uint16_t*)v_new, (const uint16_t*)k_cache, (uint16_t*)v_cache,
-                       idx, G, t, out);
+    if ((int64_t)dims->B * dims->Hkv > 65535) return PISA_ERR_UNSUPPORTED;
+    size_t cbytes = 0;
+    if (!workspace || ws_bytes < decode_attention_ws(dims, &cbytes)) return PISA_ERR_WORKSPACE;
+    const unsigned parts = (unsigned)((dims->topk + kDecAttnBlocksPerGroup - 1) / kDecAttnBlocksPerGroup);
+    uint32_t* done = (uint32_t*)workspace;
+    float* states = (float*)((char*)workspace + cbytes);
+    hipLaunchKernelGGL(decode_attention_kernel, dim3(parts, (unsigned)(dims->B * dims->Hkv)),
+                       dim3(64 * kDecAttnBlocksPerGroup), 0, (hipStream_t)stream, (const uint16_t*)q_new,
+                       (const uint16_t*)v_new, (const uint16_t*)k_cache, (uint16_t*)v_cache, idx, G, t, done, states,
+                       out);
     return launch_status();
 }
 

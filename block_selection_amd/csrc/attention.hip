@@ -276,35 +276,58 @@ __global__ __launch_bounds__(kAttnThreads, 3) void sparse_attention_kernel(const
 namespace pisa {
 
 // ------------------------------------------------------------------ decoding step --
-// Attention of one decoding query per (batch, KV head) over its selected blocks: one
-// workgroup of kDecAttnWaves wavefronts; wavefront i takes selected blocks i, i + 16, ...
-// with the same tiles and online softmax as the prefill kernel, the value block staged
-// in its own LDS tile in the permuted [dim][key] order, and the sixteen partial results
-// (running maximum, exp sum, unnormalised output per head) are merged in LDS (the
-// output partials reuse the tile memory).
-constexpr int kDecAttnWaves = 16;
+// Attention of one decoding query per (batch, KV head) over its selected blocks. A single
+// CU gathering all of them is limited by its outstanding requests, so the blocks are spread
+// over ceil(K / 4) workgroups of four wavefronts, one block per wavefront: the same tiles
+// and online softmax as the prefill kernel, the value block staged in the wavefront's own
+// LDS tile in the permuted [dim][key] order. Each workgroup merges its four partial states
+// (running maximum, exp sum and unnormalised output per head) in LDS and stores one; the
+// last workgroup of a (batch, KV head) to finish (a completion counter it resets) merges
+// the stored ones into the output.
+constexpr int kDecAttnWaves = 4;
+constexpr int kDecPartFloats = 2 * kMaxGroup + kMaxGroup * kD;   // m, l, o of one partial state
 
-// v_new (may be null): the new token's value row per (batch, KV head), written to row t of v
-// before anything reads it.
+// Merge n partial states (m[h], l[h], o[h][64] at stride `stride` floats) for head h, dims
+// e, e+1: o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
+template <typename P>
+__device__ inline void merge_states(P part, int n, int h, int e, float& o0, float& o1) {
+    float M = -INFINITY;
+    for (int i = 0; i < n; ++i) M = fmaxf(M, part(i)[h]);
+    float den = 0.0f, n0 = 0.0f, n1 = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        const float mi = part(i)[h];
+        const float sc = (mi == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mi - M);
+        den += sc * part(i)[kMaxGroup + h];
+        n0 += sc * part(i)[2 * kMaxGroup + h * kD + e];
+        n1 += sc * part(i)[2 * kMaxGroup + h * kD + e + 1];
+    }
+    const float inv = (den > 0.0f) ? 1.0f / den : 0.0f;
+    o0 = n0 * inv;
+    o1 = n1 * inv;
+}
+
+// Grid: (ceil(K / 4), B * Hkv). v_new (may be null): the new token's value row per (batch,
+// KV head): key t's value is taken from it, and workgroup 0 writes it to row t of v.
+// done: one counter per (batch, KV head), zero before the call and left zero; parts:
+// [B * Hkv][gridDim.x][kDecPartFloats].
 __global__ __launch_bounds__(64 * kDecAttnWaves) void decode_attention_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ v_new, const uint16_t* __restrict__ k,
-    uint16_t* __restrict__ v, const int32_t* __restrict__ idx, Geom G, int64_t t, float* __restrict__ out) {
+    uint16_t* __restrict__ v, const int32_t* __restrict__ idx, Geom G, int64_t t, uint32_t* __restrict__ done,
+    float* __restrict__ parts, float* __restrict__ out) {
     __shared__ uint16_t s_vt[kDecAttnWaves][kD * kC];       // 8 KiB per wavefront
-    __shared__ float s_m[kDecAttnWaves][kMaxGroup], s_l[kDecAttnWaves][kMaxGroup];
-    static_assert(sizeof(float) * kDecAttnWaves * kMaxGroup * kD <= sizeof(uint16_t) * kDecAttnWaves * kD * kC,
-                  "the output partials fit the tile memory");
-    float (*s_o)[kMaxGroup][kD] = reinterpret_cast<float (*)[kMaxGroup][kD]>(&s_vt[0][0]);
+    __shared__ float s_part[kDecAttnWaves][kDecPartFloats];
+    __shared__ int s_last;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int gq = lane >> 4, n = lane & 15;
-    const int bh = blockIdx.x, b = bh / G.Hkv, kvh = bh % G.Hkv;
+    const int part = blockIdx.x, nparts = gridDim.x;
+    const int bh = blockIdx.y, b = bh / G.Hkv, kvh = bh % G.Hkv;
     const int K = G.topk;
     const int64_t row_stride = (int64_t)G.Hkv * kD;
     const uint16_t* kbase = k + ((int64_t)b * G.cap * G.Hkv + kvh) * kD;
     const uint16_t* vbase = v + ((int64_t)b * G.cap * G.Hkv + kvh) * kD;
-    if (v_new) {
-        if (threadIdx.x < kD) v[(((int64_t)b * G.cap + t) * G.Hkv + kvh) * kD + threadIdx.x] = v_new[(int64_t)bh * kD + threadIdx.x];
-        __syncthreads();   // the row is read below by this workgroup only
-    }
+    const uint16_t* vnew_row = v_new ? v_new + (int64_t)bh * kD : nullptr;
+    if (v_new && part == 0 && threadIdx.x < kD)
+        v[(((int64_t)b * G.cap + t) * G.Hkv + kvh) * kD + threadIdx.x] = vnew_row[threadIdx.x];
     u32x4 qa, qb;
     {
         const uint16_t* qrow = q + ((int64_t)b * G.Hq + (int64_t)kvh * G.GQ + (n < G.GQ ? n : 0)) * kD;
@@ -323,21 +346,26 @@ __global__ __launch_bounds__(64 * kDecAttnWaves) void decode_attention_kernel(
     f32x4 o[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint16_t* tile = s_vt[wave];
-    for (int s = wave; s < nsel; s += kDecAttnWaves) {
+    const int s = kDecAttnWaves * part + wave;                 // this wavefront's selected block
+    if (s < nsel) {
+        uint16_t* tile = s_vt[wave];
         const int blk = readlane_i(sel, s);
         const int64_t k0 = (int64_t)blk * kC;
         const int64_t nkeys = G.N - k0;
-        // value rows of the block -> this wavefront's LDS tile, [dim][slot of key]; all eight
-        // loads in flight together (rows past the keys read the last key and store zeros)
+        // value rows -> this wavefront's LDS tile, [dim][slot of key]; all eight loads in
+        // flight together (rows past the keys read the last key and store zeros; key t is
+        // read from v_new when given)
         u32x4 vx[8];
-        const int part = lane & 7;                                  // dims 8 part .. +7
+        const int dp = lane & 7;                                   // dims 8 dp .. +7
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int kk = 8 * i + (lane >> 3);
             const int64_t kr = (kk < nkeys) ? kk : nkeys - 1;
-            vx[i] = *reinterpret_cast<const u32x4*>(vbase + (k0 + kr) * row_stride + 8 * part);
+            const uint16_t* row = (vnew_row && k0 + kr == t) ? vnew_row : vbase + (k0 + kr) * row_stride;
+            vx[i] = *reinterpret_cast<const u32x4*>(row + 8 * dp);
         }
+        KFrag kf;
+        load_kfrag(kbase + k0 * row_stride, nkeys, row_stride, n, gq, kf);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int kk = 8 * i + (lane >> 3);
@@ -346,12 +374,10 @@ __global__ __launch_bounds__(64 * kDecAttnWaves) void decode_attention_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t x = in ? vx[i][e] : 0u;
-                tile[(8 * part + 2 * e) * kC + slot] = (uint16_t)(x & 0xffffu);
-                tile[(8 * part + 2 * e + 1) * kC + slot] = (uint16_t)(x >> 16);
+                tile[(8 * dp + 2 * e) * kC + slot] = (uint16_t)(x & 0xffffu);
+                tile[(8 * dp + 2 * e + 1) * kC + slot] = (uint16_t)(x >> 16);
             }
         }
-        KFrag kf;
-        load_kfrag(kbase + k0 * row_stride, nkeys, row_stride, n, gq, kf);
         f32x4 acc[4];
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
@@ -370,24 +396,15 @@ __global__ __launch_bounds__(64 * kDecAttnWaves) void decode_attention_kernel(
                 acc[tau][r] = (16 * tau + 4 * gq + r <= lim) ? x : -INFINITY;
                 mb = fmaxf(mb, acc[tau][r]);
             }
-        mb = cols4_max(mb);
-        const float mn = fmaxf(m, mb);
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);
-        m = mn;
-        float ps = 0.0f;
+        m = cols4_max(mb);
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float p = __builtin_amdgcn_exp2f(acc[tau][r] - mn);
+                const float p = __builtin_amdgcn_exp2f(acc[tau][r] - m);
                 acc[tau][r] = p;
-                ps += p;
+                lsum += p;
             }
-        lsum = lsum * alpha + ps;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[dt][r] *= alpha;
         // the tile writes above come from this wavefront only: order them before its reads
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -414,43 +431,61 @@ __global__ __launch_bounds__(64 * kDecAttnWaves) void decode_attention_kernel(
                 o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, blo, o[dt], 0, 0, 0);
             }
         }
-        // the next block's tile writes must not overtake these reads
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    // partials of this wavefront: column n = head n (the tiles are dead once every wavefront
-    // is past its last block)
+    // this wavefront's state (column n = head n), then the workgroup's merged state
     const float l = cols4_sum(lsum);
-    __syncthreads();
+    float* sp = s_part[wave];
     if (gq == 0) {
-        s_m[wave][n] = m;
-        s_l[wave][n] = l;
+        sp[n] = m;
+        sp[kMaxGroup + n] = l;
     }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s_o[wave][n][16 * dt + 4 * gq + r] = o[dt][r];
+        for (int r = 0; r < 4; ++r) sp[2 * kMaxGroup + n * kD + 16 * dt + 4 * gq + r] = o[dt][r];
     __syncthreads();
-    // merge: thread (head h, dims 2e, 2e+1)
+    float* gp = parts + ((int64_t)bh * nparts + part) * kDecPartFloats;
     for (int x = threadIdx.x; x < G.GQ * (kD / 2); x += 64 * kDecAttnWaves) {
-        const int h = x / (kD / 2), e = 2 * (x % (kD / 2));
-        float M = -INFINITY;
+        const int h = x >> 5, e = 2 * (x & 31);             // head h, dims e and e + 1
+        {
+            float M = -INFINITY, den = 0.0f, n0 = 0.0f, n1 = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kDecAttnWaves; ++w) M = fmaxf(M, s_m[w][h]);
-        float den = 0.0f, n0 = 0.0f, n1 = 0.0f;
+            for (int w = 0; w < kDecAttnWaves; ++w) M = fmaxf(M, s_part[w][h]);
 #pragma unroll
-        for (int w = 0; w < kDecAttnWaves; ++w) {
-            const float sc = (s_m[w][h] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(s_m[w][h] - M);
-            den += sc * s_l[w][h];
-            n0 += sc * s_o[w][h][e];
-            n1 += sc * s_o[w][h][e + 1];
+            for (int w = 0; w < kDecAttnWaves; ++w) {
+                const float mw = s_part[w][h];
+                const float sc = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+                den += sc * s_part[w][kMaxGroup + h];
+                n0 += sc * s_part[w][2 * kMaxGroup + h * kD + e];
+                n1 += sc * s_part[w][2 * kMaxGroup + h * kD + e + 1];
+            }
+            // stored unnormalised against the workgroup maximum M
+            if (e == 0) {
+                gp[h] = M;
+                gp[kMaxGroup + h] = den;
+            }
+            gp[2 * kMaxGroup + h * kD + e] = n0;
+            gp[2 * kMaxGroup + h * kD + e + 1] = n1;
         }
-        const float inv = (den > 0.0f) ? 1.0f / den : 0.0f;
-        float* orow = out + ((int64_t)b * G.Hq + (int64_t)kvh * G.GQ + h) * kD + e;
-        orow[0] = n0 * inv;
-        orow[1] = n1 * inv;
     }
+    __threadfence();   // the state visible device-wide before this workgroup counts itself done
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = (atomicAdd(&done[bh], 1u) == (uint32_t)(nparts - 1));
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();   // acquire: the other workgroups' states
+    for (int x = threadIdx.x; x < G.GQ * (kD / 2); x += 64 * kDecAttnWaves) {
+        const int h = x >> 5, e = 2 * (x & 31);
+        {
+            const float* base = parts + (int64_t)bh * nparts * kDecPartFloats;
+            float o0, o1;
+            merge_states([&](int i) { return base + (int64_t)i * kDecPartFloats; }, nparts, h, e, o0, o1);
+            float* orow = out + ((int64_t)b * G.Hq + (int64_t)kvh * G.GQ + h) * kD + e;
+            orow[0] = o0;
+            orow[1] = o1;
+        }
+    }
+    if (threadIdx.x == 0) done[bh] = 0u;   // ready for the next call
 }
 
 }  // namespace pisa

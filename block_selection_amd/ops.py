@@ -32,7 +32,7 @@ EXPORTED = ("pisa_pyramid_nodes", "pisa_level_offset", "pisa_pyramid_bytes", "pi
             "pisa_pack_level_offset", "pisa_pack_pyramid_bytes", "pisa_pack_workspace_bytes",
             "pisa_build_pyramid_packed", "pisa_select_prefill_packed", "pisa_attention_workspace_bytes",
             "pisa_sparse_attention", "pisa_pack_attention_workspace_bytes", "pisa_sparse_attention_packed",
-            "pisa_decode_attention")
+            "pisa_decode_attention", "pisa_decode_attention_workspace_bytes")
 
 
 class Dims(ctypes.Structure):
@@ -94,7 +94,9 @@ def _load() -> ctypes.CDLL:
     lib.pisa_pack_attention_workspace_bytes.restype = sz
     lib.pisa_sparse_attention_packed.argtypes = [P, P, P, P, P, i64, i64, D, P, P, sz, P]
     lib.pisa_sparse_attention_packed.restype = ctypes.c_int
-    lib.pisa_decode_attention.argtypes = [P, P, P, P, P, i64, i64, D, P, P]
+    lib.pisa_decode_attention_workspace_bytes.argtypes = [D]
+    lib.pisa_decode_attention_workspace_bytes.restype = sz
+    lib.pisa_decode_attention.argtypes = [P, P, P, P, P, i64, i64, D, P, P, sz, P]
     lib.pisa_decode_attention.restype = ctypes.c_int
     lib.pisa_status_string.argtypes = [ctypes.c_int]
     lib.pisa_status_string.restype = ctypes.c_char_p
@@ -333,11 +335,20 @@ def sparse_attention_packed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, i
         raise PisaError("pisa_sparse_attention_packed", rc)
 
 
+def decode_attention_workspace_bytes(dims: Dims) -> int:
+    return int(lib.pisa_decode_attention_workspace_bytes(ctypes.byref(dims)))
+
+
+def alloc_decode_attention_workspace(dims: Dims, device="cuda") -> torch.Tensor:
+    # zero-filled: it starts with completion counters that must be zero
+    return torch.zeros(decode_attention_workspace_bytes(dims), dtype=torch.uint8, device=device)
+
+
 def decode_attention(q_new: torch.Tensor, v_new: Optional[torch.Tensor], k_cache: torch.Tensor,
                      v_cache: torch.Tensor, idx: torch.Tensor, t: int, n_capacity: int, dims: Dims,
-                     out: torch.Tensor, stream=None) -> None:
+                     out: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
     """Attention of the decoding query at position t over its selected blocks (idx as
-    decode_update_select writes it); v_new, if given, is written to row t of v_cache first."""
+    decode_update_select writes it); v_new, if given, is written to row t of v_cache."""
     _check(q_new, "q_new", dims.torch_dtype, dims.B * dims.Hq * dims.d)
     if v_new is not None:
         _check(v_new, "v_new", dims.torch_dtype, dims.B * dims.Hkv * dims.d)
@@ -345,7 +356,8 @@ def decode_attention(q_new: torch.Tensor, v_new: Optional[torch.Tensor], k_cache
     _check(v_cache, "v_cache", dims.torch_dtype, dims.B * n_capacity * dims.Hkv * dims.d)
     _check(idx, "idx", torch.int32, dims.B * dims.Hkv * dims.topk)
     _check(out, "out", torch.float32, dims.B * dims.Hq * dims.d)
+    ws_n = workspace.numel() * workspace.element_size()
     rc = lib.pisa_decode_attention(_ptr(q_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(idx), t, n_capacity,
-                                   ctypes.byref(dims), _ptr(out), _stream(stream))
+                                   ctypes.byref(dims), _ptr(out), _ptr(workspace), ws_n, _stream(stream))
     if rc != PISA_OK:
         raise PisaError("pisa_decode_attention", rc)

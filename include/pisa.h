@@ -256,19 +256,27 @@ int pisa_select_prefill_packed(const void* q, const void* k, const float* pyrami
                                const pisa_dims* dims, int32_t* out_idx, void* workspace,
                                size_t ws_bytes, void* stream);
 
+/* Device workspace of pisa_decode_attention (0 on bad input): one completion counter per
+ * (batch, KV head), 4 * B * Hkv bytes at its start, that must be zero before the first call
+ * (e.g. allocate it zero-filled; every call leaves them zero again), then the partial
+ * softmax states of the call. Calls sharing one workspace must be enqueued in order. */
+size_t pisa_decode_attention_workspace_bytes(const pisa_dims* dims);
+
 /*
  * Attention of one decoding step (bf16 only), after pisa_decode_update_select has
  * selected the blocks for the query at position t = n_before:
  *   q_new   [B, Hq, d]; v_new [B, Hkv, d] or NULL: the new token's value row, written
- *           to row t of v_cache first (pisa_decode_update_select writes only the key);
- *   k_cache, v_cache [B, n_capacity, Hkv, d], rows 0..t valid;
+ *           to row t of v_cache (pisa_decode_update_select writes only the key);
+ *   k_cache, v_cache [B, n_capacity, Hkv, d], rows 0..t valid (row t of v_cache may be
+ *           stale when v_new is given);
  *   idx     int32 [B, Hkv, topk] as pisa_decode_update_select writes it;
  *   out     fp32 [B, Hq, d].
- * One workgroup per (batch, KV head); no workspace.
+ * The selected blocks are spread over ceil(topk / 4) workgroups per (batch, KV head),
+ * whose partial softmax states the last one to finish merges.
  */
 int pisa_decode_attention(const void* q_new, const void* v_new, const void* k_cache, void* v_cache,
                           const int32_t* idx, int64_t t, int64_t n_capacity, const pisa_dims* dims, float* out,
-                          void* stream);
+                          void* workspace, size_t ws_bytes, void* stream);
 
 /* Device workspace of pisa_sparse_attention_packed (0 on bad input): the value rows as
  * per-block tiles in packed slots, Hkv * ((T >> 6) + D + 1) * 64 * 64 bf16. */

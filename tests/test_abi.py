@@ -155,10 +155,13 @@ def test_decode_attention_argument_errors_return_before_launch():
     p = ctypes.c_void_p(8)
     good = ops.make_dims(1, 32, 2, 32)
 
-    def att(dims, t=100, cap=4096, ptr=p):
-        return ops.lib.pisa_decode_attention(ptr, None, p, p, p, t, cap, ctypes.byref(dims), p, None)
+    def att(dims, t=100, cap=4096, ptr=p, ws_bytes=1 << 20):
+        return ops.lib.pisa_decode_attention(ptr, None, p, p, p, t, cap, ctypes.byref(dims), p, p, ws_bytes, None)
 
+    # counters (256-byte aligned), then 8 partial states of (16 + 16 + 16 * 64) floats per KV head
+    assert ops.decode_attention_workspace_bytes(good) == 256 + (2 * 8 * (32 + 1024) * 4 + 255) // 256 * 256
     assert att(good, ptr=None) == ops.PISA_ERR_INVALID_ARG
     assert att(good, t=-1) == ops.PISA_ERR_INVALID_ARG
     assert att(good, t=4096) == ops.PISA_ERR_CAPACITY
     assert att(ops.make_dims(1, 32, 2, 32, dtype="f32")) == ops.PISA_ERR_UNSUPPORTED
+    assert att(good, ws_bytes=16) == ops.PISA_ERR_WORKSPACE

@@ -138,6 +138,7 @@ def test_decode_attention_on_the_oracle_selection():
     q, k, v = _inputs(N, Hq, Hkv, 21)
     cap = N + 64
     dims = ops.make_dims(1, Hq, Hkv, K, "bf16")
+    wsd = ops.alloc_decode_attention_workspace(dims)     # reused by every call (counters left zero)
     for t in (0, 63, 64, 2047, 4000, N - 1):
         pyr = oracle.build_pyramid(k[:t + 1])
         idx, _, _ = oracle.walk(q[t:t + 1], np.array([t]), k[:t + 1], pyr, K)
@@ -149,7 +150,7 @@ def test_decode_attention_on_the_oracle_selection():
         out = torch.full((1, Hq, 64), float("nan"), dtype=torch.float32, device="cuda")
         print(f"decode attention t={t}", flush=True)
         ops.decode_attention(to_device(q[t][None], "bf16"), to_device(v[t][None], "bf16"), kt, vt,
-                             torch.from_numpy(idx[0][None].copy()).cuda(), t, cap, dims, out)
+                             torch.from_numpy(idx[0][None].copy()).cuda(), t, cap, dims, out, wsd)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(vt.float().cpu().numpy()[0, t], v[t])   # the appended row
         ref = oracle.attention(q[t:t + 1], np.array([t]), k[:t + 1], v[:t + 1], idx)
@@ -173,12 +174,13 @@ def test_decode_steps_select_then_attend():
     ws = ops.alloc_workspace(dims, 1, cap, is_decode=True)
     sel = torch.empty((1, Hkv, K), dtype=torch.int32, device="cuda")
     out = torch.empty((1, Hq, 64), dtype=torch.float32, device="cuda")
+    wsd = ops.alloc_decode_attention_workspace(dims)
     compared = 0
     for s in range(steps):
         t = N0 + s
         qn, kn, vn = to_device(q[t][None], "bf16"), to_device(k[t][None], "bf16"), to_device(v[t][None], "bf16")
         ops.decode_update_select(qn, kn, kc, pyr, t, cap, dims, sel, ws)
-        ops.decode_attention(qn, vn, kc, vc, sel, t, cap, dims, out)
+        ops.decode_attention(qn, vn, kc, vc, sel, t, cap, dims, out, wsd)
         torch.cuda.synchronize()
         o_idx, _, _ = oracle.walk(q[t:t + 1], np.array([t]), k[:t + 1], oracle.build_pyramid(k[:t + 1]), K)
         if not np.array_equal(o_idx[0], sel.cpu().numpy()[0]):
@@ -225,7 +227,8 @@ def test_decode_attention_batched():
     out = torch.empty((B, Hq, 64), dtype=torch.float32, device="cuda")
     print(f"decode attention batched B={B} t={t}", flush=True)
     ops.decode_attention(to_device(q, "bf16"), None, to_device(k, "bf16"), to_device(v, "bf16"),
-                         torch.from_numpy(np.ascontiguousarray(idx)).cuda(), t, N, dims, out)
+                         torch.from_numpy(np.ascontiguousarray(idx)).cuda(), t, N, dims, out,
+                         ops.alloc_decode_attention_workspace(dims))
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     for b in range(B):
