@@ -224,6 +224,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device-to-device copy first (reference kernel for HBM counters)")
     ap.add_argument("--decode-only", action="store_true", help="time only the decode workload")
+    ap.add_argument("--packed-only", action="store_true", help="time only the packed-document workloads")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs into profiles/hbm_traffic.json (no GPU)")
     args = ap.parse_args()
@@ -320,6 +321,9 @@ def main():
 
     if args.decode_only:
         print(json.dumps({"decode": decode_bench(torch, ops, synth, dev, log)}), flush=True)
+        return
+    if args.packed_only:
+        print(json.dumps({"packed": packed_bench(torch, ops, synth, dev, log)}), flush=True)
         return
 
     if args.copy_calibration:
