@@ -456,12 +456,15 @@ def main():
     del q, k, pyr, out, ws
 
     if not args.no_extras:
+        # the headline shape at other lengths (the pages' benchmark spans short sequences, where
+        # selection is launch-bound, to 256K)
         sweep = {}
-        for name in ("long64k", "long128k"):
+        for name, n2 in (("N4096", 4096), ("N16384", 16384), ("N32768", 32768), ("long64k", None),
+                         ("long128k", None)):
             if name == args.workload:
                 continue
-            w2 = synth.WORKLOADS[name]
-            _, N2, d2, q2, k2, p2, o2, ws2 = setup(w2)
+            w2 = synth.WORKLOADS[name] if n2 is None else wl
+            _, N2, d2, q2, k2, p2, o2, ws2 = setup(w2, N=n2)
             tot2, b2, wk2, _, _ = time_steps(N2, d2, q2, k2, p2, o2, ws2, 10, 3)
             sweep[name] = {"N": N2, "ms": tot2 / 10, "queries_per_s": N2 / (tot2 / 10 / 1e3),
                            "build_ms": float(b2.mean()), "walk_ms": float(wk2.mean())}
