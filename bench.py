@@ -470,6 +470,7 @@ def main():
                            "build_ms": float(b2.mean()), "walk_ms": float(wk2.mean())}
             del q2, k2, p2, o2, ws2
         result["sweep"] = sweep
+        result["planted"] = planted_bench(torch, ops, synth, setup, time_steps, log)
         result["decode"] = decode_bench(torch, ops, synth, dev, log)
         result["packed"] = packed_bench(torch, ops, synth, dev, log)
 
@@ -477,6 +478,56 @@ def main():
         log("timing the CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(inp, wl.topk, args.cpu_positions)
     print(json.dumps(result), flush=True)
+
+
+def planted_bench(torch, ops, synth, setup, time_steps, log, n_flat: int = 96, seed: int = 5):
+    """The 32K workload with 64 planted leaf blocks: time, and recall of the planted blocks
+    (mean over walks at t >= K*C with an eligible planted block of |selected & planted| /
+    min(K, eligible planted)); beside it the chance level and, on a seeded sample of positions,
+    flat exact top-K by raw-key LogSumExp over all eligible leaves (numpy, fp64)."""
+    wl = synth.WORKLOADS["mid_planted"]
+    inp, N, dims, q, k, pyr, out, ws = setup(wl)
+    tot, b, wk, _, _ = time_steps(N, dims, q, k, pyr, out, ws, 10, 3)
+    idx = out.cpu().numpy()[0]
+    planted = np.sort(inp.planted)
+    K, C = wl.topk, wl.C
+    ts = np.arange(K * C, N)
+    n_elig = ts // C + 1
+    p_elig = np.searchsorted(planted, n_elig)           # planted blocks with index < n_elig
+    keep = p_elig > 0
+    ts, n_elig, p_elig = ts[keep], n_elig[keep], p_elig[keep]
+    hit = np.isin(idx[ts], planted).sum(axis=2)          # [positions, Hkv]
+    denom = np.minimum(K, p_elig)[:, None]
+    recall = float((hit / denom).mean())
+    chance = float((K * p_elig / n_elig / np.minimum(K, p_elig)).mean())
+    # flat exact top-K on a sample
+    rng = np.random.default_rng(seed)
+    sample = np.sort(rng.choice(ts, size=min(n_flat, len(ts)), replace=False))
+    GQ = wl.Hq // wl.Hkv
+    qf, kf = inp.q[0].astype(np.float64), inp.k[0].astype(np.float64)
+    flat, walk = [], []
+    for t in sample:
+        nl = t // C + 1
+        pe = planted[planted < nl]
+        for j in range(wl.Hkv):
+            z = qf[t, j * GQ:(j + 1) * GQ] @ kf[:t + 1, j].T / np.sqrt(wl.d)       # [GQ, t+1]
+            zp = np.full((GQ, nl * C), -np.inf)
+            zp[:, :t + 1] = z
+            zp = zp.reshape(GQ, nl, C)
+            m = zp.max(axis=2, keepdims=True)
+            lse = (np.log(np.exp(zp - m).sum(axis=2)) + m[:, :, 0]).sum(axis=0)  # [nl]
+            top = np.argsort(-lse, kind="stable")[:K]
+            d = min(K, len(pe))
+            flat.append(len(set(top.tolist()) & set(pe.tolist())) / d)
+            walk.append(len(set(idx[t, j].tolist()) & set(pe.tolist())) / d)
+    res = {"N": N, "ms": tot / 10, "queries_per_s": N / (tot / 10 / 1e3), "planted_recall": recall,
+           "chance_recall": chance, "flat_exact_recall_sample": float(np.mean(flat)),
+           "walk_recall_same_sample": float(np.mean(walk)), "sample_positions": int(len(sample))}
+    log(f"planted 32K: {res['ms']:.3f} ms, planted recall {recall:.3f} (chance {chance:.3f}; on "
+        f"{len(sample)} sampled positions flat exact top-K {res['flat_exact_recall_sample']:.3f}, the walk "
+        f"{res['walk_recall_same_sample']:.3f})")
+    del q, k, pyr, out, ws
+    return res
 
 
 def attention_bench(torch, ops, synth, wl, N, dims, q, k, idx, steps, warmup, select_ms, log):
