@@ -69,6 +69,13 @@ def test_prefill_long_sampled(name):
     _prefill_case(synth.WORKLOADS[name], n_sample=1200)
 
 
+def test_prefill_512k_sampled():
+    """A tree one level deeper than the headline (524288 positions, 14 levels; one KV head of 16
+    query heads): sampled positions against the oracle."""
+    wl = synth.Workload("long512k", N=524288, Hq=16, Hkv=1, topk=8, dtype="bf16", seed=17)
+    _prefill_case(wl, n_sample=400)
+
+
 @pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 1000, 4001])
 def test_prefill_ragged_lengths(N):
     wl = synth.Workload("ragged", N=N, Hq=32, Hkv=2, topk=8, dtype="bf16", seed=N)
