@@ -505,7 +505,7 @@ def planted_bench(torch, ops, synth, setup, time_steps, log, n_flat: int = 96, s
     sample = np.sort(rng.choice(ts, size=min(n_flat, len(ts)), replace=False))
     GQ = wl.Hq // wl.Hkv
     qf, kf = inp.q[0].astype(np.float64), inp.k[0].astype(np.float64)
-    flat, walk = [], []
+    flat, walk, overlap = [], [], []
     for t in sample:
         nl = t // C + 1
         pe = planted[planted < nl]
@@ -520,12 +520,16 @@ def planted_bench(torch, ops, synth, setup, time_steps, log, n_flat: int = 96, s
             d = min(K, len(pe))
             flat.append(len(set(top.tolist()) & set(pe.tolist())) / d)
             walk.append(len(set(idx[t, j].tolist()) & set(pe.tolist())) / d)
+            sel = set(x for x in idx[t, j].tolist() if x >= 0)
+            overlap.append(len(sel & set(top.tolist())) / min(K, nl))
     res = {"N": N, "ms": tot / 10, "queries_per_s": N / (tot / 10 / 1e3), "planted_recall": recall,
            "chance_recall": chance, "flat_exact_recall_sample": float(np.mean(flat)),
-           "walk_recall_same_sample": float(np.mean(walk)), "sample_positions": int(len(sample))}
+           "walk_recall_same_sample": float(np.mean(walk)), "sample_positions": int(len(sample)),
+           "overlap_recall_at_K_vs_flat_exact": float(np.mean(overlap))}
     log(f"planted 32K: {res['ms']:.3f} ms, planted recall {recall:.3f} (chance {chance:.3f}; on "
         f"{len(sample)} sampled positions flat exact top-K {res['flat_exact_recall_sample']:.3f}, the walk "
-        f"{res['walk_recall_same_sample']:.3f})")
+        f"{res['walk_recall_same_sample']:.3f}; overlap with flat exact top-K "
+        f"{res['overlap_recall_at_K_vs_flat_exact']:.3f})")
     del q, k, pyr, out, ws
     return res
 
