@@ -39,7 +39,7 @@ __global__ void bucket_pass_kernel(const int32_t*, const int32_t*, Geom, Cluster
                                    uint32_t*, const uint32_t*, const uint32_t*, uint2*, int);
 __global__ void pack_plan_kernel(Pack, int, int, int64_t*);
 __global__ void group_offsets_kernel(const uint32_t*, ClusterGeom, Pack, const int64_t*, uint32_t*, uint32_t*);
-__global__ void scan_groups_kernel(const uint32_t*, ClusterGeom, uint32_t*, int4*, uint32_t*);
+__global__ void scan_groups_kernel(const uint32_t*, ClusterGeom, uint32_t, uint32_t*, int4*, uint32_t*);
 template <int S>
 __global__ void leaf_cluster_kernel(const uint16_t*, const uint16_t*, Geom, ClusterGeom, Pack, int64_t,
                                     const int4*, const uint2*, uint32_t*, float*, float*);
@@ -112,7 +112,7 @@ struct Workspace {
     uint32_t* gtot;      // [ngroups] entries per group
     uint32_t* gbase;     // [ngroups] first entry of each group
     uint2* entries;      // [walks * 2K] incidences grouped by bucket
-    int4* items;         // [walks * 2K / kItemMax + ngroups]
+    int4* items;         // [walks * 2K / kItemMin + ngroups]
     uint32_t* meta;      // [0] items, [1] entries
     int64_t* cbase;      // [D + 1] first count of each document's block (packs only)
     // fused bf16 decoding step
@@ -164,7 +164,7 @@ static Workspace carve(const pisa_dims* d, int64_t N, int64_t P, bool decode, ch
         w.gtot = (uint32_t*)take((size_t)w.CG.ngroups * 4);
         w.gbase = (uint32_t*)take((size_t)w.CG.ngroups * 4);
         w.entries = (uint2*)take((size_t)walks * cs * sizeof(uint2));
-        w.items = (int4*)take(((size_t)walks * cs / kItemMax + w.CG.ngroups + 1) * sizeof(int4));
+        w.items = (int4*)take(((size_t)walks * cs / kItemMin + w.CG.ngroups + 1) * sizeof(int4));
         w.meta = (uint32_t*)take(16);
     }
     w.bytes = off;
@@ -210,7 +210,7 @@ static Workspace carve_pack(const pisa_dims* d, int64_t T, int64_t D, int64_t P,
     w.gtot = (uint32_t*)take((size_t)w.CG.ngroups * 4);
     w.gbase = (uint32_t*)take((size_t)w.CG.ngroups * 4);
     w.entries = (uint2*)take((size_t)walks * cs * sizeof(uint2));
-    w.items = (int4*)take(((size_t)walks * cs / kItemMax + w.CG.ngroups + 1) * sizeof(int4));
+    w.items = (int4*)take(((size_t)walks * cs / kItemMin + w.CG.ngroups + 1) * sizeof(int4));
     w.meta = (uint32_t*)take(16);
     w.cbase = (int64_t*)take((size_t)(D + 1) * sizeof(int64_t));
     w.bytes = off;
@@ -419,7 +419,8 @@ static int cluster_leaf_stage(const uint16_t* q, const uint16_t* k, const Geom& 
         if (fill) {
             hipLaunchKernelGGL(group_offsets_kernel, dim3((unsigned)((CG.ngroups + 3) / 4)), dim3(256), 0, s, W.counts,
                                CG, pk, cbase, W.offsets, W.gtot);
-            hipLaunchKernelGGL(scan_groups_kernel, dim3(1), dim3(1024), 0, s, W.gtot, CG, W.gbase, W.items, W.meta);
+            hipLaunchKernelGGL(scan_groups_kernel, dim3(1), dim3(1024), 0, s, W.gtot, CG, (uint32_t)((cus + 1) / 2),
+                               W.gbase, W.items, W.meta);
         }
         if (slots <= 16)
             hipLaunchKernelGGL(bucket_pass_kernel<16>, bgrid, dim3(1024), bins, s, W.cand, W.ncand, G, CG, pk, cbase,

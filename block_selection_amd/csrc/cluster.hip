@@ -14,7 +14,7 @@
 //   2. group_offsets: per (batch, KV head, superblock) group, one wavefront scans
 //      its ranges' counts (bucket offsets inside the group, group total);
 //      scan_groups: group offsets and work items of at most kItemMax entries of
-//      one group;
+//      one group (fewer for a short call);
 //   3. bucket_pass (fill): incidences written as entries at their offsets;
 //   4. leaf_cluster: persistent workgroups take items from a counter; a workgroup stages the
 //      superblock's keys in LDS once, then each wavefront takes entries (the
@@ -194,35 +194,48 @@ __global__ __launch_bounds__(256) void group_offsets_kernel(const uint32_t* __re
 }
 
 // One workgroup: the entry offset of every group (groups in order) and work items of at
-// most kItemMax entries of one group. Items holding kItemMax entries come first, the
+// most L entries of one group. L is kItemMax, halved (down to kItemMin) while the call's
+// entries would make fewer than min_items items of L: a short sequence then spreads its
+// scoring over more CUs, at the price of fewer entries per wavefront sharing a sibling
+// pair (the caller passes half the CU count: measured, items of kItemMax that leave some
+// CUs idle beat smaller ones in more rounds). Items holding L entries come first, the
 // smaller remainders after them, so that the workgroups taking items in order finish
 // together. meta[0] = number of items, meta[1] = number of entries, meta[2] = 0 (the
 // counter the scoring workgroups take items from).
 __global__ __launch_bounds__(1024) void scan_groups_kernel(const uint32_t* __restrict__ gtot, ClusterGeom CG,
-                                                           uint32_t* __restrict__ gbase,
+                                                           uint32_t min_items, uint32_t* __restrict__ gbase,
                                                            int4* __restrict__ items,
                                                            uint32_t* __restrict__ meta) {
     __shared__ uint32_t s_e[1024], s_f[1024], s_p[1024];
     const int tid = threadIdx.x;
     const int per = (CG.ngroups + 1023) / 1024;
     const int lo = tid * per, hi = min(CG.ngroups, lo + per);
-    uint32_t se = 0, sf = 0, sp = 0;
+    uint32_t se = 0;
+    for (int g = lo; g < hi; ++g) se += gtot[g];
+    s_e[tid] = se;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {       // inclusive Hillis-Steele scan of the entry counts
+        const uint32_t ae = (tid >= d) ? s_e[tid - d] : 0u;
+        __syncthreads();
+        s_e[tid] += ae;
+        __syncthreads();
+    }
+    const uint32_t total = s_e[1023];
+    uint32_t L = kItemMax;
+    while (L > (uint32_t)kItemMin && (uint64_t)total < (uint64_t)min_items * L) L >>= 1;
+    uint32_t sf = 0, sp = 0;
     for (int g = lo; g < hi; ++g) {
         const uint32_t tot = gtot[g];
-        se += tot;
-        sf += tot / kItemMax;              // full items
-        sp += (tot % kItemMax) ? 1u : 0u;  // remainder item
+        sf += tot / L;                  // full items
+        sp += (tot % L) ? 1u : 0u;      // remainder item
     }
-    s_e[tid] = se;
     s_f[tid] = sf;
     s_p[tid] = sp;
     __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {       // inclusive Hillis-Steele scans
-        const uint32_t ae = (tid >= d) ? s_e[tid - d] : 0u;
+    for (int d = 1; d < 1024; d <<= 1) {       // the same scan of the item counts
         const uint32_t af = (tid >= d) ? s_f[tid - d] : 0u;
         const uint32_t ap = (tid >= d) ? s_p[tid - d] : 0u;
         __syncthreads();
-        s_e[tid] += ae;
         s_f[tid] += af;
         s_p[tid] += ap;
         __syncthreads();
@@ -233,14 +246,14 @@ __global__ __launch_bounds__(1024) void scan_groups_kernel(const uint32_t* __res
         const uint32_t g0 = eoff, tot = gtot[g];
         gbase[g] = g0;
         eoff += tot;
-        for (uint32_t p = 0; p * kItemMax < tot; ++p) {
-            const uint32_t len = min((uint32_t)kItemMax, tot - p * kItemMax);
-            items[(len == kItemMax) ? foff++ : poff++] = make_int4(g, (int)(g0 + p * kItemMax), (int)len, 0);
+        for (uint32_t p = 0; p * L < tot; ++p) {
+            const uint32_t len = min(L, tot - p * L);
+            items[(len == L) ? foff++ : poff++] = make_int4(g, (int)(g0 + p * L), (int)len, 0);
         }
     }
     if (tid == 1023) {
         meta[0] = nfull + s_p[1023];
-        meta[1] = s_e[1023];
+        meta[1] = total;
         meta[2] = 0u;
     }
 }

@@ -192,12 +192,14 @@ __host__ __device__ inline void upper_cfg_for(const Seg& sg, int topk, UpperCfg&
 // bucketed by (batch, KV head, superblock, range of 2^RL query positions), so
 // that each bucket is counted and filled by one workgroup and the entries of one
 // (batch, KV head, superblock) group are contiguous; work items hold at most
-// kItemMax entries of one group. Ranges hold 512 positions, or fewer (down to 64)
-// when a call has too few ranges to give every CU a workgroup.
+// kItemMax entries of one group, or fewer (down to kItemMin) when a call has too few
+// entries to give every CU several items. Ranges hold 512 positions, or fewer (down
+// to 64) when a call has too few ranges to give every CU a workgroup.
 constexpr int kSbLeaves = 16;
 constexpr int kSbKeys = kSbLeaves * kC;           // 1024 keys
 constexpr int kLog2RangeMax = 9, kLog2RangeMin = 6;
 constexpr int kItemMax = 1024;                     // entries per work item
+constexpr int kItemMin = 256;                      // ... of a call with few entries
 constexpr int kClusterThreads = 1024;
 constexpr int kSbLdsBytes = kSbKeys * kD * 2;      // 128 KiB of bf16 keys
 struct ClusterGeom {
