@@ -107,18 +107,20 @@ def write_traffic(fetch_dir: str, write_dir: str, workload: str = "long256k") ->
         with open(path[0]) as f:
             for r in csv.DictReader(f):
                 if r["Counter_Name"] == counter:
-                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+                    vals.setdefault(r["Kernel_Name"], []).append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
         return vals
 
     fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
 
-    def find(tab, key):
+    def find(tab, key, first_only=False):
         hits = [v for k, v in tab.items() if key in k]
         if not hits:
             raise SystemExit(f"kernel {key} not in the counter runs")
-        return float(np.mean(hits[0]))
+        if first_only:   # the calibration copy is the program's first copy; later ones differ in size
+            return min(hits[0])[1]
+        return float(np.mean([x for _, x in hits[0]]))
 
-    copy_f, copy_w = find(fetch, "copyBuffer"), find(write, "copyBuffer")
+    copy_f, copy_w = find(fetch, "copyBuffer", True), find(write, "copyBuffer", True)
     fs, wsc = COPY_BYTES / (copy_f * 1024), COPY_BYTES / (copy_w * 1024)
     out = {"_calibration": {
         "copy_bytes_each_way": COPY_BYTES, "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
@@ -484,7 +486,10 @@ def planted_bench(torch, ops, synth, setup, time_steps, log, n_flat: int = 96, s
     """The 32K workload with 64 planted leaf blocks: time, and recall of the planted blocks
     (mean over walks at t >= K*C with an eligible planted block of |selected & planted| /
     min(K, eligible planted)); beside it the chance level and, on a seeded sample of positions,
-    flat exact top-K by raw-key LogSumExp over all eligible leaves (numpy, fp64)."""
+    flat exact top-K by raw-key LogSumExp over all eligible leaves (numpy, fp64): its planted
+    recall, its overlap with the walk's selection, and the block-selection diagnostic against the
+    K blocks of most attention mass (full softmax over keys <= t, mean over the group's heads):
+    Recall@K and the ratio of the selection's mass to theirs."""
     wl = synth.WORKLOADS["mid_planted"]
     inp, N, dims, q, k, pyr, out, ws = setup(wl)
     tot, b, wk, _, _ = time_steps(N, dims, q, k, pyr, out, ws, 10, 3)
@@ -505,7 +510,7 @@ def planted_bench(torch, ops, synth, setup, time_steps, log, n_flat: int = 96, s
     sample = np.sort(rng.choice(ts, size=min(n_flat, len(ts)), replace=False))
     GQ = wl.Hq // wl.Hkv
     qf, kf = inp.q[0].astype(np.float64), inp.k[0].astype(np.float64)
-    flat, walk, overlap = [], [], []
+    flat, walk, overlap, mref, mratio, mratio_flat, mratio_rand = [], [], [], [], [], [], []
     for t in sample:
         nl = t // C + 1
         pe = planted[planted < nl]
@@ -515,21 +520,38 @@ def planted_bench(torch, ops, synth, setup, time_steps, log, n_flat: int = 96, s
             zp[:, :t + 1] = z
             zp = zp.reshape(GQ, nl, C)
             m = zp.max(axis=2, keepdims=True)
-            lse = (np.log(np.exp(zp - m).sum(axis=2)) + m[:, :, 0]).sum(axis=0)  # [nl]
+            lse_h = np.log(np.exp(zp - m).sum(axis=2)) + m[:, :, 0]                 # [GQ, nl]
+            lse = lse_h.sum(axis=0)                                                   # [nl]
             top = np.argsort(-lse, kind="stable")[:K]
             d = min(K, len(pe))
             flat.append(len(set(top.tolist()) & set(pe.tolist())) / d)
             walk.append(len(set(idx[t, j].tolist()) & set(pe.tolist())) / d)
-            sel = set(x for x in idx[t, j].tolist() if x >= 0)
-            overlap.append(len(sel & set(top.tolist())) / min(K, nl))
+            sel = [x for x in idx[t, j].tolist() if x >= 0]
+            overlap.append(len(set(sel) & set(top.tolist())) / min(K, nl))
+            # attention mass of each block (full softmax over keys <= t, mean over the group's
+            # heads); the reference set is the K blocks of largest mass
+            top_h = lse_h.max(axis=1, keepdims=True)
+            mass = (np.exp(lse_h - top_h) / np.exp(lse_h - top_h).sum(axis=1, keepdims=True)).mean(axis=0)
+            ref = np.argsort(-mass, kind="stable")[:K]
+            mref.append(len(set(sel) & set(ref.tolist())) / min(K, nl))
+            mratio.append(float(mass[sel].sum() / mass[ref].sum()))
+            mratio_flat.append(float(mass[top].sum() / mass[ref].sum()))
+            mratio_rand.append(float(mass[rng.choice(nl, K, replace=False)].sum() / mass[ref].sum()))
     res = {"N": N, "ms": tot / 10, "queries_per_s": N / (tot / 10 / 1e3), "planted_recall": recall,
            "chance_recall": chance, "flat_exact_recall_sample": float(np.mean(flat)),
            "walk_recall_same_sample": float(np.mean(walk)), "sample_positions": int(len(sample)),
-           "overlap_recall_at_K_vs_flat_exact": float(np.mean(overlap))}
+           "overlap_recall_at_K_vs_flat_exact": float(np.mean(overlap)),
+           "recall_at_K_vs_attention_mass_top_K": float(np.mean(mref)),
+           "attention_mass_ratio": float(np.mean(mratio)),
+           "attention_mass_ratio_flat_exact": float(np.mean(mratio_flat)),
+           "attention_mass_ratio_random_K": float(np.mean(mratio_rand))}
     log(f"planted 32K: {res['ms']:.3f} ms, planted recall {recall:.3f} (chance {chance:.3f}; on "
         f"{len(sample)} sampled positions flat exact top-K {res['flat_exact_recall_sample']:.3f}, the walk "
         f"{res['walk_recall_same_sample']:.3f}; overlap with flat exact top-K "
-        f"{res['overlap_recall_at_K_vs_flat_exact']:.3f})")
+        f"{res['overlap_recall_at_K_vs_flat_exact']:.3f}; against the K blocks of most attention mass: "
+        f"recall {res['recall_at_K_vs_attention_mass_top_K']:.3f}, mass ratio {res['attention_mass_ratio']:.4f} "
+        f"(flat exact top-K {res['attention_mass_ratio_flat_exact']:.4f}, K random eligible blocks "
+        f"{res['attention_mass_ratio_random_K']:.4f}))")
     del q, k, pyr, out, ws
     return res
 
