@@ -33,7 +33,6 @@ template <typename KT>
 __global__ void leaf_walk_kernel(const KT*, const KT*, Geom, int64_t, int64_t, const int32_t*,
                                  const int32_t*, int32_t*);
 
-__global__ void fill_u32_kernel(uint32_t*, int64_t, uint32_t);
 template <int SL>
 __global__ void bucket_pass_kernel(const int32_t*, const int32_t*, Geom, ClusterGeom, Pack, const int64_t*, int64_t,
                                    uint32_t*, const uint32_t*, const uint32_t*, uint2*, int);

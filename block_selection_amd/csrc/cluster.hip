@@ -27,10 +27,6 @@
 
 namespace pisa {
 
-__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
-}
-
 // Counting (fill = 0) or placing (fill = 1) the incidences of one range of 2^RL
 // query positions of batch element blockIdx.y (range blockIdx.x). One incidence per
 // sibling pair of a walk's leaf candidates (the children of one level-2 survivor); a
