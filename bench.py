@@ -227,6 +227,7 @@ def main():
                     help="run one 256 MiB device-to-device copy first (reference kernel for HBM counters)")
     ap.add_argument("--decode-only", action="store_true", help="time only the decode workload")
     ap.add_argument("--packed-only", action="store_true", help="time only the packed-document workloads")
+    ap.add_argument("--batched-only", action="store_true", help="time only the batched (B > 1) workloads")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs into profiles/hbm_traffic.json (no GPU)")
     args = ap.parse_args()
@@ -326,6 +327,9 @@ def main():
         return
     if args.packed_only:
         print(json.dumps({"packed": packed_bench(torch, ops, synth, dev, log)}), flush=True)
+        return
+    if args.batched_only:
+        print(json.dumps({"batched": batched_bench(torch, ops, dev, log)}), flush=True)
         return
 
     if args.copy_calibration:
@@ -475,6 +479,7 @@ def main():
         result["planted"] = planted_bench(torch, ops, synth, setup, time_steps, log)
         result["decode"] = decode_bench(torch, ops, synth, dev, log)
         result["packed"] = packed_bench(torch, ops, synth, dev, log)
+        result["batched"] = batched_bench(torch, ops, dev, log)
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
@@ -671,6 +676,89 @@ def decode_bench(torch, ops, synth, dev, log):
            "steps_per_s": 1e6 / float(per.mean())}
     log(f"decode: {res['us_per_step_mean']:.1f} us/step, {res['us_per_step_with_attention']:.1f} us/step with "
         f"attention over the selected blocks")
+    return res
+
+
+def batched_bench(torch, ops, dev, log, seed: int = 11):
+    """Batches of independent sequences (B > 1): prefill of 4 x 65536 positions (the
+    headline's token count, K = 8) and decoding steps for 64 sequences of 32768 keys at
+    once (K = 32). Inputs: standard normal draws on the device from a seeded generator,
+    rounded to bf16 (timing only; batches are checked element by element against the
+    oracle by the tests)."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+
+    def randn(*shape):
+        return torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+    res = {}
+    B, N = 4, 65536
+    dims = ops.make_dims(B, 32, 2, 8, "bf16")
+    q, k = randn(B, N, 32, 64), randn(B, N, 2, 64)
+    pyr = ops.alloc_pyramid(dims, N, dev)
+    out = torch.empty((B, N, 2, 8), dtype=torch.int32, device=dev)
+    ws = ops.alloc_workspace(dims, N, N, device=dev)
+    for _ in range(3):
+        ops.build_pyramid(k, N, N, dims, pyr)
+        ops.select_prefill(q, k, pyr, N, N, dims, out, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        ops.build_pyramid(k, N, N, dims, pyr)
+        ops.select_prefill(q, k, pyr, N, N, dims, out, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    res["prefill_4x65536"] = {"B": B, "N": N, "K": 8, "ms_per_step": ms, "queries_per_s": B * N / (ms / 1e3)}
+    del q, k, pyr, out, ws
+
+    B, N0, steps, K = 64, 32768, 64, 32
+    cap = N0 + steps
+    dims = ops.make_dims(B, 32, 2, K, "bf16")
+    k_cache = torch.zeros((B, cap, 2, 64), dtype=torch.bfloat16, device=dev)
+    k_cache[:, :N0] = randn(B, N0, 2, 64)
+    k_new, q_new = randn(steps, B, 2, 64), randn(steps, B, 32, 64)
+    pyr = ops.alloc_pyramid(dims, cap, dev)
+    out = torch.empty((B, 2, K), dtype=torch.int32, device=dev)
+    ws = ops.alloc_workspace(dims, 1, cap, is_decode=True, device=dev)
+    per = []
+    for rep in range(3):   # first repetition is warm-up; each starts from the same prebuilt pyramid
+        ops.build_pyramid(k_cache, N0, cap, dims, pyr)
+        torch.cuda.synchronize()
+        e0.record()
+        for s_ in range(steps):
+            ops.decode_update_select(q_new[s_], k_new[s_], k_cache, pyr, N0 + s_, cap, dims, out, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        if rep:
+            per.append(e0.elapsed_time(e1) * 1e3 / steps)
+    us = float(np.mean(per))
+    # the same steps, each followed by attention over its selection (which appends the value row)
+    v_cache = torch.zeros_like(k_cache)
+    v_cache[:, :N0] = randn(B, N0, 2, 64)
+    v_new = randn(steps, B, 2, 64)
+    att = torch.empty((B, 32, 64), dtype=torch.float32, device=dev)
+    wsd = ops.alloc_decode_attention_workspace(dims, device=dev)
+    per_att = []
+    for rep in range(2):
+        ops.build_pyramid(k_cache, N0, cap, dims, pyr)
+        torch.cuda.synchronize()
+        e0.record()
+        for s_ in range(steps):
+            ops.decode_update_select(q_new[s_], k_new[s_], k_cache, pyr, N0 + s_, cap, dims, out, ws)
+            ops.decode_attention(q_new[s_], v_new[s_], k_cache, v_cache, out, N0 + s_, cap, dims, att, wsd)
+        e1.record()
+        torch.cuda.synchronize()
+        if rep:
+            per_att.append(e0.elapsed_time(e1) * 1e3 / steps)
+    us_att = float(np.mean(per_att))
+    res["decode_64x32768"] = {"B": B, "context": N0, "K": K, "steps": steps, "us_per_step": us,
+                              "sequence_steps_per_s": B / (us / 1e6), "us_per_step_with_attention": us_att,
+                              "sequence_steps_per_s_with_attention": B / (us_att / 1e6)}
+    del k_cache, v_cache, k_new, v_new, q_new, pyr, out, ws, att, wsd
+    log(f"batched: prefill 4 x 65536 {ms:.3f} ms ({res['prefill_4x65536']['queries_per_s'] / 1e6:.1f} M queries/s); "
+        f"decode 64 sequences x 32768 keys {us:.1f} us/step ({res['decode_64x32768']['sequence_steps_per_s'] / 1e6:.2f} M "
+        f"sequence-steps/s), {us_att:.1f} us/step with attention over the selected blocks")
     return res
 
 

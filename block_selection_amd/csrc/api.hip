@@ -620,8 +620,12 @@ int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cach
     const unsigned nbh = (unsigned)(dims->B * dims->Hkv);
     if (dims->dtype == PISA_DTYPE_BF16) {
         // append, refresh, walk and leaf top-K in one launch: ceil(2K/8) workgroups per
-        // (batch, KV head), the last one to finish writes the selection
-        const unsigned parts = (unsigned)((2 * dims->topk + 7) / 8);
+        // (batch, KV head), the last one to finish writes the selection; one per (batch,
+        // KV head) when that would exceed the CUs
+        int cus = 256;
+        if ((rc = device_cus(&cus)) != PISA_OK) return rc;
+        unsigned parts = (unsigned)((2 * dims->topk + 7) / 8);
+        if ((int64_t)parts * nbh > (int64_t)cus) parts = 1u;
         const uint16_t* qn = (const uint16_t*)q_new;
         const uint16_t* kn = (const uint16_t*)k_new;
         uint16_t* kc = (uint16_t*)k_cache;
@@ -772,7 +776,11 @@ int pisa_decode_attention(const void* q_new, const void* v_new, const void* k_ca
     if ((int64_t)dims->B * dims->Hkv > 65535) return PISA_ERR_UNSUPPORTED;
     size_t cbytes = 0;
     if (!workspace || ws_bytes < decode_attention_ws(dims, &cbytes)) return PISA_ERR_WORKSPACE;
-    const unsigned parts = (unsigned)((dims->topk + kDecAttnBlocksPerGroup - 1) / kDecAttnBlocksPerGroup);
+    // ceil(K/4) workgroups per (batch, KV head), or one when that would exceed the CUs
+    int cus = 256;
+    if ((rc = device_cus(&cus)) != PISA_OK) return rc;
+    unsigned parts = (unsigned)((dims->topk + kDecAttnBlocksPerGroup - 1) / kDecAttnBlocksPerGroup);
+    if ((int64_t)parts * dims->B * dims->Hkv > (int64_t)cus) parts = 1u;
     uint32_t* done = (uint32_t*)workspace;
     float* states = (float*)((char*)workspace + cbytes);
     hipLaunchKernelGGL(decode_attention_kernel, dim3(parts, (unsigned)(dims->B * dims->Hkv)),

@@ -277,13 +277,16 @@ namespace pisa {
 
 // ------------------------------------------------------------------ decoding step --
 // Attention of one decoding query per (batch, KV head) over its selected blocks. A single
-// CU gathering all of them is limited by its outstanding requests, so the blocks are spread
-// over ceil(K / 4) workgroups of four wavefronts, one block per wavefront: the same tiles
-// and online softmax as the prefill kernel, the value block staged in the wavefront's own
-// LDS tile in the permuted [dim][key] order. Each workgroup merges its four partial states
-// (running maximum, exp sum and unnormalised output per head) in LDS and stores one; the
-// last workgroup of a (batch, KV head) to finish (a completion counter it resets) merges
-// the stored ones into the output.
+// CU gathering all of them is limited by its outstanding requests, so for a few sequences
+// the blocks are spread over ceil(K / 4) workgroups of four wavefronts, one block per
+// wavefront: the same tiles and online softmax as the prefill kernel, the value block
+// staged in the wavefront's own LDS tile in the permuted [dim][key] order. Each workgroup
+// merges its four partial states (running maximum, exp sum and unnormalised output per
+// head) in LDS and stores one; the last workgroup of a (batch, KV head) to finish (a
+// completion counter it resets) merges the stored ones into the output. A batch that fills
+// the CUs by itself runs one workgroup per (batch, KV head), each wavefront taking every
+// fourth block, and writes the output from the LDS merge (the device-scope fences of the
+// hand-over cost more than the spread saves there).
 constexpr int kDecAttnWaves = 4;
 constexpr int kDecPartFloats = 2 * kMaxGroup + kMaxGroup * kD;   // m, l, o of one partial state
 
@@ -306,7 +309,7 @@ __device__ inline void merge_states(P part, int n, int h, int e, float& o0, floa
     o1 = n1 * inv;
 }
 
-// Grid: (ceil(K / 4), B * Hkv). v_new (may be null): the new token's value row per (batch,
+// Grid: (ceil(K / 4) or 1, B * Hkv). v_new (may be null): the new token's value row per (batch,
 // KV head): key t's value is taken from it, and workgroup 0 writes it to row t of v.
 // done: one counter per (batch, KV head), zero before the call and left zero; parts:
 // [B * Hkv][gridDim.x][kDecPartFloats].
@@ -346,9 +349,13 @@ __global__ __launch_bounds__(64 * kDecAttnWaves) void decode_attention_kernel(
     f32x4 o[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int s = kDecAttnWaves * part + wave;                 // this wavefront's selected block
-    if (s < nsel) {
+    // this wavefront's selected blocks: one when the blocks are spread over workgroups
+    for (int s = kDecAttnWaves * part + wave; s < nsel; s += kDecAttnWaves * nparts) {
         uint16_t* tile = s_vt[wave];
+        // the previous block's tile reads come before this block's tile writes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const int blk = readlane_i(sel, s);
         const int64_t k0 = (int64_t)blk * kC;
         const int64_t nkeys = G.N - k0;
@@ -396,15 +403,25 @@ __global__ __launch_bounds__(64 * kDecAttnWaves) void decode_attention_kernel(
                 acc[tau][r] = (16 * tau + 4 * gq + r <= lim) ? x : -INFINITY;
                 mb = fmaxf(mb, acc[tau][r]);
             }
-        m = cols4_max(mb);
+        // online softmax over the wavefront's blocks (the block holding t has a visible key,
+        // so the running maximum is finite after the first block)
+        const float mn = fmaxf(m, cols4_max(mb));
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);   // 0 on the first block (m = -inf)
+        m = mn;
+        float ps = 0.0f;
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float p = __builtin_amdgcn_exp2f(acc[tau][r] - m);
+                const float p = __builtin_amdgcn_exp2f(acc[tau][r] - mn);
                 acc[tau][r] = p;
-                lsum += p;
+                ps += p;
             }
+        lsum = lsum * alpha + ps;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[dt][r] *= alpha;
         // the tile writes above come from this wavefront only: order them before its reads
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -444,6 +461,18 @@ __global__ __launch_bounds__(64 * kDecAttnWaves) void decode_attention_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) sp[2 * kMaxGroup + n * kD + 16 * dt + 4 * gq + r] = o[dt][r];
     __syncthreads();
+    if (nparts == 1) {
+        // the workgroup's merged state is the answer: no hand-over between workgroups
+        for (int x = threadIdx.x; x < G.GQ * (kD / 2); x += 64 * kDecAttnWaves) {
+            const int h = x >> 5, e = 2 * (x & 31);
+            float o0, o1;
+            merge_states([&](int i) { return (const float*)s_part[i]; }, kDecAttnWaves, h, e, o0, o1);
+            float* orow = out + ((int64_t)b * G.Hq + (int64_t)kvh * G.GQ + h) * kD + e;
+            orow[0] = o0;
+            orow[1] = o1;
+        }
+        return;
+    }
     float* gp = parts + ((int64_t)bh * nparts + part) * kDecPartFloats;
     for (int x = threadIdx.x; x < G.GQ * (kD / 2); x += 64 * kDecAttnWaves) {
         const int h = x >> 5, e = 2 * (x & 31);             // head h, dims e and e + 1

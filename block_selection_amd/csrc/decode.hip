@@ -6,8 +6,9 @@
 // keeping all candidates of a level that has at most K of them), "Scoring:
 // LogSumExp" and section 4.1 (per-head LSE summed over the GQA group).
 //
-// ceil(2K / 8) workgroups of 8 wavefronts per (batch, KV head); the query position
-// is t = N - 1, the appended key. Every workgroup
+// P workgroups of 8 wavefronts per (batch, KV head), P = ceil(2K / 8) for a few
+// sequences and 1 for a batch that fills the CUs by itself; the query position is
+// t = N - 1, the appended key. Every workgroup
 //   1. appends the key and refreshes its leaf and ancestor path (wavefront 0; the
 //      copies in the other workgroups write identical bits);
 //   2. walks from the root down to level 2: the candidates of a level sit in the
@@ -16,12 +17,14 @@
 //      the fp32 pyramid and split into hi/lo bf16 planes in registers), the candidate
 //      scores go through LDS (double-buffered, so one barrier per level), and every
 //      wavefront sorts the 64 slots itself;
-//   3. scores the candidate leaves of its 8 slots, one per wavefront, from the raw keys
-//      in global memory, into a per-(batch, KV head) row of the workspace.
+//   3. scores the candidate leaves of its slots (8 * part + wavefront, every 8P-th slot
+//      after that) from the raw keys in global memory, into a per-(batch, KV head) row
+//      of the workspace.
 // The last workgroup to finish (a completion counter that it resets) takes the K best
 // leaves and writes them ascending, -1 padded. Spreading the leaf stage over several
-// CUs matters: its random 8 KiB key blocks are fetched far faster by several CUs than
-// one CU's outstanding-request capacity allows.
+// CUs matters for one sequence: its random 8 KiB key blocks are fetched far faster by
+// several CUs than one CU's outstanding-request capacity allows. For a batch the
+// device-scope fences of that hand-over cost more than they save, so P = 1 there.
 // The arithmetic is that of the prefill kernels (walk_math.h), so the step selects
 // exactly what prefill selects at the same query position.
 #include "pyramid_math.h"
@@ -231,22 +234,27 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
     }
     const bool scored = __popcll(ballot(leaf >= 0)) > K;
     if (scored) {
-        // this wavefront's leaf slot; the score goes to the per-(batch, KV head) row in
+        // this wavefront's leaf slots; each score goes to the per-(batch, KV head) row in
         // the workspace, and the last workgroup to finish reads the whole row
-        const int slot = 8 * part + wave;
-        const int f = readlane_i(leaf, slot);
-        if (f >= 0) {
-            const int fl[1] = {f};
-            float o[1];
-            score_leaves_global<1, S>(kbase, row_stride, fl, t, q0, q1, n, gq, G.GQ, o);
-            if (lane == 0) leaf_score[(int64_t)bh * 64 + slot] = o[0];
+        for (int slot = 8 * part + wave; slot < 2 * K; slot += 8 * nparts) {
+            const int f = readlane_i(leaf, slot);
+            if (f >= 0) {
+                const int fl[1] = {f};
+                float o[1];
+                score_leaves_global<1, S>(kbase, row_stride, fl, t, q0, q1, n, gq, G.GQ, o);
+                if (lane == 0) leaf_score[(int64_t)bh * 64 + slot] = o[0];
+            }
         }
-        __threadfence();   // scores visible device-wide before this workgroup counts itself done
-        __syncthreads();
-        if (threadIdx.x == 0) s_last = (atomicAdd(&done[bh], 1u) == (uint32_t)(nparts - 1));
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();   // acquire: the other workgroups' scores
+        if (nparts > 1) {
+            __threadfence();   // scores visible device-wide before this workgroup counts itself done
+            __syncthreads();
+            if (threadIdx.x == 0) s_last = (atomicAdd(&done[bh], 1u) == (uint32_t)(nparts - 1));
+            __syncthreads();
+            if (!s_last) return;
+            __threadfence();   // acquire: the other workgroups' scores
+        } else {
+            __syncthreads();   // one workgroup: its own wavefronts' scores
+        }
     } else if (part != 0) {
         return;            // at most K candidates: all kept, workgroup 0 writes them
     }

@@ -213,9 +213,11 @@ def test_attention_batched():
         _check(got[b], oracle.attention(q[b], np.arange(N), k[b], v[b], idx[b]), v)
 
 
-def test_decode_attention_batched():
+@pytest.mark.parametrize("B", [2, 20])
+def test_decode_attention_batched(B):
+    """B=20 (K=32, 2 KV heads) fills the CUs by itself: one workgroup per (batch, KV head)."""
     from block_selection_amd import ops
-    B, N, Hq, Hkv, K = 2, 3000, 32, 2, 32
+    N, Hq, Hkv, K = 3000, 32, 2, 32
     rng = np.random.default_rng(32)
     q = synth.bf16_round(rng.standard_normal((B, Hq, 64), dtype=np.float32))
     k = synth.bf16_round(rng.standard_normal((B, N, Hkv, 64), dtype=np.float32))

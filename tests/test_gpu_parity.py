@@ -309,12 +309,14 @@ def test_prefill_batched(B, dtype):
         assert rep.ok(), (b, str(rep))
 
 
-def test_decode_batched():
-    """Decode with B=2: per batch element, the refreshed pyramid equals a rebuild bitwise and
-    the selection matches the oracle (near-ties validated)."""
+@pytest.mark.parametrize("B,K,steps", [(2, 16, 12), (20, 32, 4)])
+def test_decode_batched(B, K, steps):
+    """Decode of a batch: per batch element, the refreshed pyramid equals a rebuild bitwise and
+    the selection matches the oracle (near-ties validated). B=20 with K=32 is a batch that
+    fills the CUs by itself (one workgroup per sequence and KV head instead of eight)."""
     from block_selection_amd import ops
-    B, N0, steps, K = 2, 2000, 12, 16
-    wl = synth.Workload("decode_b2", N=N0, Hq=16, Hkv=2, topk=K, dtype="bf16", B=B, decode_steps=steps, seed=5)
+    N0 = 2000
+    wl = synth.Workload(f"decode_b{B}", N=N0, Hq=16, Hkv=2, topk=K, dtype="bf16", B=B, decode_steps=steps, seed=5)
     inp = synth.make_decode(wl)
     cap = N0 + steps
     dims = ops.make_dims(B, 16, 2, K, "bf16")
@@ -331,7 +333,7 @@ def test_decode_batched():
     ref_k = to_device(k_all, "bf16")
     for s in range(steps):
         n = N0 + s
-        print(f"[case] decode B=2 step={s}", flush=True)
+        print(f"[case] decode B={B} K={K} step={s}", flush=True)
         ops.decode_update_select(q_new[s].contiguous(), k_new[s].contiguous(), k_cache, pyr, n, cap, dims, out, ws)
         torch.cuda.synchronize()
         ops.build_pyramid(ref_k, n + 1, cap, dims, pyr_rb)
