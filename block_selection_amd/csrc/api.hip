@@ -49,6 +49,11 @@ __global__ void sparse_attention_kernel(const uint16_t*, const uint16_t*, const 
 __global__ void decode_attention_kernel(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, const int32_t*,
                                         Geom, int64_t, uint32_t*, float*, float*);
 constexpr int kDecAttnBlocksPerGroup = 4;                          // wavefronts (blocks) per workgroup
+// A decoding step (selection or attention) spreads each sequence's leaf or block work over
+// several workgroups only while the whole grid stays within this many: past it the
+// device-scope fences of the hand-over cost more than the spread saves (measured on
+// MI355X, 32K keys, K = 32: the split wins up to 3-4 sequences x 2 KV heads).
+constexpr int64_t kDecodeSplitMaxWorkgroups = 64;
 constexpr int kDecAttnStateFloats = 2 * kMaxGroup + kMaxGroup * kD;  // one partial softmax state
 
 // The kernels that score candidates are built once per candidate score (pisa_score);
@@ -621,11 +626,9 @@ int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cach
     if (dims->dtype == PISA_DTYPE_BF16) {
         // append, refresh, walk and leaf top-K in one launch: ceil(2K/8) workgroups per
         // (batch, KV head), the last one to finish writes the selection; one per (batch,
-        // KV head) when that would exceed the CUs
-        int cus = 256;
-        if ((rc = device_cus(&cus)) != PISA_OK) return rc;
+        // KV head) when that would make more than kDecodeSplitMaxWorkgroups
         unsigned parts = (unsigned)((2 * dims->topk + 7) / 8);
-        if ((int64_t)parts * nbh > (int64_t)cus) parts = 1u;
+        if ((int64_t)parts * nbh > kDecodeSplitMaxWorkgroups) parts = 1u;
         const uint16_t* qn = (const uint16_t*)q_new;
         const uint16_t* kn = (const uint16_t*)k_new;
         uint16_t* kc = (uint16_t*)k_cache;
@@ -776,11 +779,10 @@ int pisa_decode_attention(const void* q_new, const void* v_new, const void* k_ca
     if ((int64_t)dims->B * dims->Hkv > 65535) return PISA_ERR_UNSUPPORTED;
     size_t cbytes = 0;
     if (!workspace || ws_bytes < decode_attention_ws(dims, &cbytes)) return PISA_ERR_WORKSPACE;
-    // ceil(K/4) workgroups per (batch, KV head), or one when that would exceed the CUs
-    int cus = 256;
-    if ((rc = device_cus(&cus)) != PISA_OK) return rc;
+    // ceil(K/4) workgroups per (batch, KV head), or one when that would make more than
+    // kDecodeSplitMaxWorkgroups
     unsigned parts = (unsigned)((dims->topk + kDecAttnBlocksPerGroup - 1) / kDecAttnBlocksPerGroup);
-    if ((int64_t)parts * dims->B * dims->Hkv > (int64_t)cus) parts = 1u;
+    if ((int64_t)parts * dims->B * dims->Hkv > kDecodeSplitMaxWorkgroups) parts = 1u;
     uint32_t* done = (uint32_t*)workspace;
     float* states = (float*)((char*)workspace + cbytes);
     hipLaunchKernelGGL(decode_attention_kernel, dim3(parts, (unsigned)(dims->B * dims->Hkv)),

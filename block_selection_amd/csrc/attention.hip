@@ -283,10 +283,10 @@ namespace pisa {
 // staged in the wavefront's own LDS tile in the permuted [dim][key] order. Each workgroup
 // merges its four partial states (running maximum, exp sum and unnormalised output per
 // head) in LDS and stores one; the last workgroup of a (batch, KV head) to finish (a
-// completion counter it resets) merges the stored ones into the output. A batch that fills
-// the CUs by itself runs one workgroup per (batch, KV head), each wavefront taking every
-// fourth block, and writes the output from the LDS merge (the device-scope fences of the
-// hand-over cost more than the spread saves there).
+// completion counter it resets) merges the stored ones into the output. A larger batch runs
+// one workgroup per (batch, KV head), each wavefront taking every fourth block, and writes
+// the output from the LDS merge (the device-scope fences of the hand-over cost more than
+// the spread saves there).
 constexpr int kDecAttnWaves = 4;
 constexpr int kDecPartFloats = 2 * kMaxGroup + kMaxGroup * kD;   // m, l, o of one partial state
 

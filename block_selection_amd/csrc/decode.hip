@@ -7,8 +7,8 @@
 // LogSumExp" and section 4.1 (per-head LSE summed over the GQA group).
 //
 // P workgroups of 8 wavefronts per (batch, KV head), P = ceil(2K / 8) for a few
-// sequences and 1 for a batch that fills the CUs by itself; the query position is
-// t = N - 1, the appended key. Every workgroup
+// sequences and 1 for a larger batch; the query position is t = N - 1, the appended
+// key. Every workgroup
 //   1. appends the key and refreshes its leaf and ancestor path (wavefront 0; the
 //      copies in the other workgroups write identical bits);
 //   2. walks from the root down to level 2: the candidates of a level sit in the

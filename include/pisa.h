@@ -271,8 +271,10 @@ size_t pisa_decode_attention_workspace_bytes(const pisa_dims* dims);
  *           stale when v_new is given);
  *   idx     int32 [B, Hkv, topk] as pisa_decode_update_select writes it;
  *   out     fp32 [B, Hq, d].
- * The selected blocks are spread over ceil(topk / 4) workgroups per (batch, KV head),
- * whose partial softmax states the last one to finish merges.
+ * For a few sequences the selected blocks are spread over ceil(topk / 4) workgroups per
+ * (batch, KV head), whose partial softmax states the last one to finish merges; a batch
+ * that would need more than 64 such workgroups runs one per (batch, KV head).
+ * Either way the result is the attention over the selection (rounding of the merge aside).
  */
 int pisa_decode_attention(const void* q_new, const void* v_new, const void* k_cache, void* v_cache,
                           const int32_t* idx, int64_t t, int64_t n_capacity, const pisa_dims* dims, float* out,
