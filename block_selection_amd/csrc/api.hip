@@ -242,6 +242,7 @@ static int check_dims(const pisa_dims* d) {
     if (d->score < PISA_SCORE_LSE || d->score > PISA_SCORE_MEAN_HALF_VAR) return PISA_ERR_INVALID_ARG;
     if (d->d != kD || d->C != kC || d->g != 2) return PISA_ERR_UNSUPPORTED;
     if (d->Hq / d->Hkv > kMaxGroup || d->topk > kMaxTopK) return PISA_ERR_UNSUPPORTED;
+    if ((int64_t)d->B * d->Hkv > 65535) return PISA_ERR_UNSUPPORTED;   // one grid row per (batch, KV head)
     return PISA_OK;
 }
 
@@ -684,7 +685,7 @@ int pisa_sparse_attention(const void* q, const void* k, const void* v, const int
     const int64_t nblk = (N + kC - 1) / kC;
     const int64_t walks = (int64_t)dims->B * N * dims->Hkv;
     const int64_t grid = (walks + 3) / 4;
-    if ((int64_t)dims->B * dims->Hkv > 65535 || grid > INT_MAX || nblk > INT_MAX) return PISA_ERR_UNSUPPORTED;
+    if (grid > INT_MAX || nblk > INT_MAX) return PISA_ERR_UNSUPPORTED;
     if (!workspace || ws_bytes < attention_ws(dims, N)) return PISA_ERR_WORKSPACE;
     return attention_impl((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, G, Pack{nullptr, 0, 0},
                           nblk, out, (uint16_t*)workspace, (hipStream_t)stream);
@@ -776,7 +777,6 @@ int pisa_decode_attention(const void* q_new, const void* v_new, const void* k_ca
     Geom G;
     if ((rc = make_geom(dims, t + 1, n_capacity, &G)) != PISA_OK) return rc;
     if (dims->dtype != PISA_DTYPE_BF16) return PISA_ERR_UNSUPPORTED;
-    if ((int64_t)dims->B * dims->Hkv > 65535) return PISA_ERR_UNSUPPORTED;
     size_t cbytes = 0;
     if (!workspace || ws_bytes < decode_attention_ws(dims, &cbytes)) return PISA_ERR_WORKSPACE;
     // ceil(K/4) workgroups per (batch, KV head), or one when that would make more than

@@ -77,7 +77,7 @@ typedef enum {
 
 /* Problem dimensions. dtype is the element type of q and k (both the same). */
 typedef struct {
-    int32_t B;      /* batch */
+    int32_t B;      /* batch; B * Hkv <= 65535, else PISA_ERR_UNSUPPORTED */
     int32_t Hq;     /* query heads */
     int32_t Hkv;    /* key heads; Hq % Hkv == 0, group size GQ = Hq / Hkv */
     int32_t d;      /* head dimension (64) */

@@ -52,6 +52,7 @@ def test_argument_errors_return_before_launch():
     assert _call_select(ops, ops.make_dims(1, 32, 2, 8, g=4)) == ops.PISA_ERR_UNSUPPORTED
     assert _call_select(ops, ops.make_dims(1, 34, 1, 8)) == ops.PISA_ERR_UNSUPPORTED   # group of 34
     assert _call_select(ops, ops.make_dims(1, 32, 2, 33)) == ops.PISA_ERR_UNSUPPORTED
+    assert _call_select(ops, ops.make_dims(32768, 32, 2, 8)) == ops.PISA_ERR_UNSUPPORTED   # B * Hkv > 65535
     assert _call_select(ops, ops.make_dims(1, 31, 2, 8)) == ops.PISA_ERR_INVALID_ARG
     assert _call_select(ops, ops.make_dims(1, 32, 2, 0)) == ops.PISA_ERR_INVALID_ARG
     assert _call_select(ops, ops.make_dims(0, 32, 2, 8)) == ops.PISA_ERR_INVALID_ARG
