@@ -213,11 +213,12 @@ def test_attention_batched():
         _check(got[b], oracle.attention(q[b], np.arange(N), k[b], v[b], idx[b]), v)
 
 
-@pytest.mark.parametrize("B", [2, 20])
-def test_decode_attention_batched(B):
-    """B=20 (K=32, 2 KV heads) fills the CUs by itself: one workgroup per (batch, KV head)."""
+@pytest.mark.parametrize("B,K", [(2, 32), (20, 32), (40, 8)])
+def test_decode_attention_batched(B, K):
+    """B=20 with K=32 and B=40 with K=8 (2 KV heads) run one workgroup per (batch, KV head),
+    each wavefront over several blocks; B=2 splits the blocks over workgroups."""
     from block_selection_amd import ops
-    N, Hq, Hkv, K = 3000, 32, 2, 32
+    N, Hq, Hkv = 3000, 32, 2
     rng = np.random.default_rng(32)
     q = synth.bf16_round(rng.standard_normal((B, Hq, 64), dtype=np.float32))
     k = synth.bf16_round(rng.standard_normal((B, N, Hkv, 64), dtype=np.float32))
@@ -227,7 +228,7 @@ def test_decode_attention_batched(B):
                     for b in range(B)])
     dims = ops.make_dims(B, Hq, Hkv, K, "bf16")
     out = torch.empty((B, Hq, 64), dtype=torch.float32, device="cuda")
-    print(f"decode attention batched B={B} t={t}", flush=True)
+    print(f"decode attention batched B={B} K={K} t={t}", flush=True)
     ops.decode_attention(to_device(q, "bf16"), None, to_device(k, "bf16"), to_device(v, "bf16"),
                          torch.from_numpy(np.ascontiguousarray(idx)).cuda(), t, N, dims, out,
                          ops.alloc_decode_attention_workspace(dims))

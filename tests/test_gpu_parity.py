@@ -309,11 +309,11 @@ def test_prefill_batched(B, dtype):
         assert rep.ok(), (b, str(rep))
 
 
-@pytest.mark.parametrize("B,K,steps", [(2, 16, 12), (20, 32, 4)])
+@pytest.mark.parametrize("B,K,steps", [(2, 16, 12), (20, 32, 4), (40, 8, 3)])
 def test_decode_batched(B, K, steps):
     """Decode of a batch: per batch element, the refreshed pyramid equals a rebuild bitwise and
-    the selection matches the oracle (near-ties validated). B=20 with K=32 is a batch that
-    fills the CUs by itself (one workgroup per sequence and KV head instead of eight)."""
+    the selection matches the oracle (near-ties validated). B=20 with K=32 and B=40 with K=8
+    run one workgroup per sequence and KV head instead of the split over several."""
     from block_selection_amd import ops
     N0 = 2000
     wl = synth.Workload(f"decode_b{B}", N=N0, Hq=16, Hkv=2, topk=K, dtype="bf16", B=B, decode_steps=steps, seed=5)
