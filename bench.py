@@ -82,6 +82,10 @@ def walk_counts(N: int, topk: int, GQ: int, Hkv: int, C: int = 64):
 # MI355X transcendental peak: 256 CUs x 32 lanes/clock (v_exp_f32 / v_log_f32 issue at half the
 # 64-lane VALU rate) x 2.4 GHz
 TRANSCENDENTAL_PEAK = 256 * 32 * 2.4e9
+# VALU issue slots: 256 CUs x 64 lanes/clock x 2.4 GHz. A leaf logit of the exact LSE needs at
+# least four: the base-2 scale, the exp (two slots at half rate) and its add into the sum.
+VALU_SLOT_PEAK = 256 * 64 * 2.4e9
+LEAF_SLOTS_PER_LOGIT = 4
 
 
 # sources of the two walk kernels (a traffic figure is only valid for the code it was taken on)
@@ -369,6 +373,9 @@ def main():
         "algorithmic_per_launch": transc,
         "leaf_pairs_per_launch": wc["leaf_pairs"],
         "launch_ms": leaf_ms,
+        # the same launch against its VALU issue-slot floor (scale + exp + add per logit)
+        "valu_slot_floor_ms": wc["leaf_logits"] * LEAF_SLOTS_PER_LOGIT / VALU_SLOT_PEAK * 1e3,
+        "valu_slot_frac": wc["leaf_logits"] * LEAF_SLOTS_PER_LOGIT / VALU_SLOT_PEAK / (leaf_ms / 1e3),
     }
     walk_s = walk_ms.mean() / 1e3
     upper_transc = wc["upper_logits"] + wc["upper_lse"]
