@@ -466,6 +466,18 @@ def main():
             log(f"score {sc}: {tot_s / 10:.3f} ms/step (upper walk {up_s.mean():.3f} ms, "
                 f"leaf scoring {lf_s.mean():.3f} ms)")
         result["score_variants"] = variants
+        # larger budgets on the same inputs (the pages' continued-pretraining setting uses K = 32)
+        ksweep = {}
+        for kk in (16, 32):
+            dims_k = ops.make_dims(wl.B, wl.Hq, wl.Hkv, kk, wl.dtype)
+            out_k = torch.empty((wl.B, N, wl.Hkv, kk), dtype=torch.int32, device=dev)
+            ws_k = ops.alloc_workspace(dims_k, N, N, device=dev)
+            tot_k, b_k, wk_k, up_k, lf_k = time_steps(N, dims_k, q, k, pyr, out_k, ws_k, 10, 3)
+            ksweep[f"K{kk}"] = {"ms_per_step": tot_k / 10, "queries_per_s": wl.B * N / (tot_k / 10 / 1e3),
+                                "upper_walk_ms": float(up_k.mean()), "leaf_scoring_ms": float(lf_k.mean())}
+            log(f"K={kk}: {tot_k / 10:.3f} ms/step (upper walk {up_k.mean():.3f} ms, leaf scoring {lf_k.mean():.3f} ms)")
+            del out_k, ws_k
+        result["topk_sweep"] = ksweep
     del q, k, pyr, out, ws
 
     if not args.no_extras:

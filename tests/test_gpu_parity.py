@@ -76,6 +76,14 @@ def test_prefill_512k_sampled():
     _prefill_case(wl, n_sample=400)
 
 
+@pytest.mark.parametrize("topk", [16, 32])
+def test_prefill_256k_larger_budgets(topk):
+    """The headline shape (262144 positions, Hq=32, Hkv=2) at K = 16 and 32 (the budgets
+    bench.py also times): sampled positions against the oracle."""
+    wl = synth.Workload(f"long256k_k{topk}", N=262144, Hq=32, Hkv=2, topk=topk, dtype="bf16", seed=3)
+    _prefill_case(wl, n_sample=300)
+
+
 @pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 1000, 4001])
 def test_prefill_ragged_lengths(N):
     wl = synth.Workload("ragged", N=N, Hq=32, Hkv=2, topk=8, dtype="bf16", seed=N)
