@@ -687,14 +687,31 @@ def decode_bench(torch, ops, synth, dev, log):
         torch.cuda.synchronize()
         if rep:
             att_times = [ev[s].elapsed_time(ev[s + 1]) * 1e3 for s in range(steps)]
+    # the same steps with K = 8 (the budget of the pages' selection-latency setting)
+    dims8 = ops.make_dims(1, wl.Hq, wl.Hkv, 8, "bf16")
+    out8 = torch.empty((1, wl.Hkv, 8), dtype=torch.int32, device=dev)
+    ws8 = ops.alloc_workspace(dims8, 1, cap, is_decode=True, device=dev)
+    k8_times = []
+    for rep in range(2):
+        ops.build_pyramid(k_cache, N0, cap, dims8, pyr)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for s in range(steps):
+            ops.decode_update_select(qn[s], kn[s], k_cache, pyr, N0 + s, cap, dims8, out8, ws8)
+            ev[s + 1].record(stream)
+        torch.cuda.synchronize()
+        if rep:
+            k8_times = [ev[s].elapsed_time(ev[s + 1]) * 1e3 for s in range(steps)]
     per = np.array(times)
     res = {"context": N0, "steps": steps, "K": wl.topk, "us_per_step_mean": float(per.mean()),
+           "us_per_step_K8": float(np.mean(k8_times)),
            "us_per_step_with_attention": float(np.mean(att_times)),
            "empty_kernel_launch_us": float(np.mean(fl)),
            "us_per_step_median": float(np.median(per)), "us_per_step_p90": float(np.percentile(per, 90)),
            "steps_per_s": 1e6 / float(per.mean())}
     log(f"decode: {res['us_per_step_mean']:.1f} us/step, {res['us_per_step_with_attention']:.1f} us/step with "
-        f"attention over the selected blocks")
+        f"attention over the selected blocks; K=8: {res['us_per_step_K8']:.1f} us/step")
     return res
 
 
