@@ -454,7 +454,9 @@ static int vwalk(vctx_t* V, int l, const int64_t* surv, int nsurv) {
     }
     qsort(sc, ncand, sizeof(scored_t), cmp_scored);
     const double sK = sc[K - 1].s;
-    int64_t* chosen = (int64_t*)malloc(sizeof(int64_t) * (K + 1));
+    /* surely kept (< K of them) plus band members forced by the target (up to K) can
+     * exceed K before the check below: room for every candidate */
+    int64_t* chosen = (int64_t*)malloc(sizeof(int64_t) * ncand);
     int64_t* band = (int64_t*)malloc(sizeof(int64_t) * ncand);
     int nch = 0, nband = 0, ok = 1;
     for (int c = 0; c < ncand; c++) {
