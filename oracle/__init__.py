@@ -196,15 +196,17 @@ def validate(q_row: np.ndarray, t: int, j: int, k: np.ndarray, pyr: np.ndarray, 
 
 
 def decode_step(k_all: np.ndarray, n: int, q_new: np.ndarray, topk: int, C: int = 64, g: int = 2,
-                nthreads: int = 0, score: str = "lse"):
+                nthreads: int = 0, score: str = "lse", with_level: bool = False):
     """Selection after appending key n: rebuild over keys 0..n and walk at t = n.
 
     k_all: float [>= n+1, Hkv, d]; q_new: float [Hq, d].
-    Returns (pyr, idx [Hkv, topk], min_gap [Hkv]).
+    Returns (pyr, idx [Hkv, topk], min_gap [Hkv]), plus gap_level [Hkv] if with_level.
     """
     k = _f32(k_all[: n + 1])
     pyr = build_pyramid(k, C, g, nthreads)
-    idx, gap, _ = walk(q_new[None], np.array([n]), k, pyr, topk, C, g, nthreads, score)
+    idx, gap, lvl = walk(q_new[None], np.array([n]), k, pyr, topk, C, g, nthreads, score)
+    if with_level:
+        return pyr, idx[0], gap[0], lvl[0]
     return pyr, idx[0], gap[0]
 
 
