@@ -90,6 +90,12 @@ template <int SLOTS>
 __global__ void final_topk_kernel(const int32_t*, const int32_t*, const float*, Geom, int64_t, int32_t*);
 
 constexpr size_t kAlign = 256;
+// The bucket pass counts one sequence's (KV head, superblock) groups in an LDS histogram of
+// this many bins (64 KiB): bf16 selection needs Hkv * ceil(N / 1024) <= kMaxClusterGroups.
+constexpr int64_t kMaxClusterGroups = 16384;
+static bool bf16_select_fits(const pisa_dims* d, int64_t N) {
+    return (int64_t)d->Hkv * ((N + kSbKeys - 1) / kSbKeys) <= kMaxClusterGroups;
+}
 
 static size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -153,8 +159,8 @@ static Workspace carve(const pisa_dims* d, int64_t N, int64_t P, bool decode, ch
     w.ncand = (int32_t*)take((size_t)walks * sizeof(int32_t));
     const int64_t m1 = (N + kC - 1) / kC;
     const int64_t nsb = (m1 + kSbLeaves - 1) / kSbLeaves;
-    // clustered leaf scoring for bf16 prefill while the per-range LDS histogram fits
-    w.clustered = !decode && d->dtype == PISA_DTYPE_BF16 && d->Hkv * nsb <= 16384;
+    // clustered leaf scoring for bf16 prefill (callers check kMaxClusterGroups first)
+    w.clustered = !decode && d->dtype == PISA_DTYPE_BF16 && d->Hkv * nsb <= kMaxClusterGroups;
     if (w.clustered) {
         w.CG.RL = range_log2((int64_t)d->B * N);
         w.CG.NR = (int32_t)((N + ((int64_t)1 << w.CG.RL) - 1) >> w.CG.RL);
@@ -509,7 +515,8 @@ static int select_impl(const KT* q, const KT* k, const float* pyr, const Geom& G
     if (rc != PISA_OK) return rc;
     mark(ev, 1, s);
     const int64_t walks = (int64_t)G.B * NT * G.Hkv;
-    if (!W.clustered) {
+    if constexpr (sizeof(KT) == 4) {
+        // fp32 inputs: one wavefront per walk scores its leaf candidates from the raw keys
         int64_t grid = (walks + 3) / 4;
         if (grid > (1 << 22)) grid = 1 << 22;
         mark(ev, 2, s);
@@ -517,8 +524,9 @@ static int select_impl(const KT* q, const KT* k, const float* pyr, const Geom& G
                            W.cand, W.ncand, out);
         mark(ev, 3, s);
         return launch_status();
+    } else {
+        return cluster_leaf_stage(q, k, G, Pack{nullptr, 0, 0}, NT, out, W, cus, s, ev);
     }
-    return cluster_leaf_stage((const uint16_t*)q, (const uint16_t*)k, G, Pack{nullptr, 0, 0}, NT, out, W, cus, s, ev);
 }
 
 // Packed documents, bf16: planes, the packed walk, clustered leaf scoring, final top-K.
@@ -570,6 +578,7 @@ size_t pisa_pyramid_bytes(const pisa_dims* dims, int64_t n_capacity) {
 
 size_t pisa_workspace_bytes(const pisa_dims* dims, int64_t N, int64_t n_capacity, int32_t is_decode) {
     if (check_dims(dims) != PISA_OK || n_capacity < 1 || (!is_decode && (N < 1 || N > n_capacity))) return 0;
+    if (!is_decode && dims->dtype == PISA_DTYPE_BF16 && !bf16_select_fits(dims, N)) return 0;
     const int64_t P = pisa_pyramid_nodes(dims, n_capacity);
     return carve(dims, is_decode ? 1 : N, P, is_decode != 0, nullptr).bytes;
 }
@@ -596,6 +605,7 @@ int pisa_select_prefill_profiled(const void* q, const void* k, const float* pyra
     if (!q || !k || !pyramid || !out_idx) return PISA_ERR_INVALID_ARG;
     Geom G;
     if ((rc = make_geom(dims, N, n_capacity, &G)) != PISA_OK) return rc;
+    if (dims->dtype == PISA_DTYPE_BF16 && !bf16_select_fits(dims, N)) return PISA_ERR_UNSUPPORTED;
     const Workspace W = carve(dims, N, G.P, false, (char*)workspace);
     if (!workspace || ws_bytes < W.bytes) return PISA_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
@@ -744,7 +754,7 @@ int pisa_select_prefill_packed(const void* q, const void* k, const float* pyrami
     if (!q || !k || !pyramid || !cu_seqlens || !out_idx) return PISA_ERR_INVALID_ARG;
     if (dims->dtype != PISA_DTYPE_BF16) return PISA_ERR_UNSUPPORTED;
     // the bucket pass holds one document's (KV head, superblock) bins in LDS
-    if ((int64_t)dims->Hkv * ((T + kSbKeys - 1) / kSbKeys) > 16384) return PISA_ERR_UNSUPPORTED;
+    if (!bf16_select_fits(dims, T)) return PISA_ERR_UNSUPPORTED;
     const Workspace W = carve_pack(dims, T, D, G.P, (char*)workspace);
     if (!workspace || ws_bytes < W.bytes) return PISA_ERR_WORKSPACE;
     const Pack pk{cu_seqlens, (int32_t)D, T};

@@ -1,9 +1,10 @@
 // attention.hip -- stage two: attention over the selected key blocks (gfx950).
 //
 // Reading note "Block Sparse Attention with Log-Linear Complexity", the two-stage
-// formulation it opens with: once stage one has selected K key blocks per query
-// (shared by the query heads of a GQA group, section 4.1), stage two attends over
-// the original keys and values inside those blocks. Per query head: softmax of
+// formulation it opens with: once stage one has picked K key blocks per query
+// (shared by the query heads of a GQA group, section 4.1), the second stage runs
+// ordinary attention restricted to the raw key/value rows of the picked blocks.
+// Per query head: softmax of
 // q.k/sqrt(d) over the keys <= t of the selected blocks, applied to their values.
 //
 // Layout and arithmetic:

@@ -238,8 +238,6 @@ __global__ __launch_bounds__(256) void leaf_walk_kernel(const KT* __restrict__ q
     }
 }
 
-template __global__ void leaf_walk_kernel<uint16_t>(const uint16_t*, const uint16_t*, Geom, int64_t, int64_t,
-                                                    const int32_t*, const int32_t*, int32_t*);
 template __global__ void leaf_walk_kernel<float>(const float*, const float*, Geom, int64_t, int64_t,
                                                  const int32_t*, const int32_t*, int32_t*);
 

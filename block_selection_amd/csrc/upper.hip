@@ -15,15 +15,23 @@
 //     so one bf16 MFMA chain v_mfma_f32_16x16x32_bf16 (hi and lo, two k-steps)
 //     yields base-2 logits directly. fp32 inputs use fp32 summaries on
 //     v_mfma_f32_16x16x4_f32 instead (exact products).
-//   * A wavefront walks 64/SLOTS queries at once, SLOTS = 16, 32 or 64 lanes
-//     per walk (2K <= SLOTS): lane i of a segment holds candidate slot i.
-//     Children rows of a walk fill 16-row MFMA tiles (rows = children, columns
-//     = the group's query heads); a lane holds both children of two
-//     candidates, so the pairwise LSE is in-lane and the group sum is four DPP
-//     adds across the 16 head columns.
-//   * The coarsest levels that can be read as children are staged in LDS
-//     once per workgroup; finer levels are gathered from global memory (L2).
-//   * Top-K: bitonic sort of each walk's slots on 64-bit (score, node) keys.
+//   * bf16 inputs (walk_upper_delta_kernel): a wavefront walks 64/SLOTS
+//     queries at once, SLOTS = 16, 32 or 64 lanes per walk (2K <= SLOTS), lane
+//     i of a segment holding candidate slot i. A candidate is scored from ONE
+//     row, delta(c) = s(2c) - s(c), and the head-summed logit P(c) of its own
+//     summary carried down the walk (the "delta form" in walk_math.h). Each
+//     16-column MFMA tile takes the group's query heads as its A operand and 16
+//     candidates' delta rows as its B operand, so a lane holds four heads of
+//     one candidate: the head sums are in-lane adds plus permlane16/32 swaps.
+//   * fp32 inputs (walk_upper_f32_kernel) score both children rows of each
+//     candidate on v_mfma_f32_16x16x4_f32 (exact products), children as tile
+//     rows and heads as columns.
+//   * The coarsest levels are staged in LDS once per workgroup (their delta
+//     rows, plus the summary rows of the level where most walks start
+//     scoring); finer levels are gathered from global memory (L2).
+//   * Top-K: bitonic network on each walk's slots over 64-bit (score, node)
+//     keys; when 2K equals the slot count, a partial network keeps the top
+//     half as a set.
 #include "walk_math.h"
 
 namespace pisa {

@@ -131,6 +131,10 @@ int pisa_build_pyramid(const void* k, int64_t N, int64_t n_capacity, const pisa_
  *   pyramid  as written by pisa_build_pyramid for the same N and n_capacity.
  *   out_idx  int32 [B, N, Hkv, topk]: ascending leaf indices, -1 padded.
  *   workspace at least pisa_workspace_bytes(dims, N, n_capacity, 0) bytes of device memory.
+ * bf16 inputs need Hkv * ceil(N / 1024) <= 16384 (the leaf stage counts its
+ * (KV head, 1024-key superblock) groups in one LDS histogram): N up to 8388608
+ * keys at Hkv = 2. Beyond that the call returns PISA_ERR_UNSUPPORTED and
+ * pisa_workspace_bytes returns 0.
  * Arithmetic: leaf scores use the exact bf16 (or fp32) q.k products accumulated
  * in fp32; upper-level scores multiply bf16 queries by the fp32 summaries held
  * as a hi + lo pair of bf16 values (relative error <= 2^-17 per element; fp32
@@ -176,8 +180,8 @@ int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cach
 /* ------------------------------------------------------- attention (stage two)
  *
  * Reading note "Block Sparse Attention with Log-Linear Complexity", the two-stage
- * formulation it opens with: stage two attends over the original keys and values
- * inside the blocks stage one selected. For query position t and query head h
+ * formulation it opens with: the second stage is attention limited to the raw
+ * key/value rows of the blocks stage one picked. For query position t and query head h
  * (KV head j = h / (Hq/Hkv)): softmax of q.k / sqrt(d) over the keys <= t of the
  * blocks idx[b][t][j][0..topk-1] (entries < 0 or after t's block are skipped;
  * each block is counted as often as it appears), applied to those keys' value

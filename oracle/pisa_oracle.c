@@ -25,9 +25,10 @@
  *     their mean and truncating it gives the two ablation scores, the mean
  *     of the logits (first order, "PISA-1") and the mean plus half their
  *     variance (second order, "PISA-2"). The walk takes any of the three.
- *   - same note, the two-stage formulation it opens with: stage two attends
- *     over the original keys and values inside the selected blocks; the
- *     attention function below is that softmax attention, causally masked.
+ *   - same note, the two-stage formulation it opens with: the second stage
+ *     computes attention only over the raw key and value rows that belong to
+ *     the picked blocks; the attention function below is that softmax
+ *     attention, causally masked.
  *
  * Readings taken where the pages are silent (each listed in the design notes):
  *   logit = q.k / sqrt(d); level sizes M_{l+1} = ceil(M_l / g) up to one node;
@@ -503,7 +504,7 @@ int pisa_oracle_validate(const float* q_row, int64_t t, int j, const float* k, c
 /*
  * Stage two: attention over the selected blocks ("Block Sparse Attention with
  * Log-Linear Complexity", the two-stage formulation at the top of the note:
- * stage two attends over the original keys and values inside the selected
+ * the second stage restricts attention to the raw key/value rows of the picked
  * blocks). For query row i at position t and query head h (KV head j = h / GQ),
  * the keys are those of the blocks idx[i][j][0..topk-1] (entries < 0 ignored;
  * block b holds keys b*C .. min((b+1)*C, N) - 1) that are <= t (causal); the

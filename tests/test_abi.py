@@ -75,6 +75,24 @@ def test_argument_errors_return_before_launch():
     assert ops.status_string(ops.PISA_ERR_WORKSPACE) == "workspace too small"
 
 
+def test_bf16_prefill_beyond_the_cluster_histogram_is_refused():
+    """bf16 selection needs Hkv * ceil(N / 1024) <= 16384 (one LDS histogram of the leaf
+    stage's groups); past it the call returns UNSUPPORTED before any launch and the
+    workspace query returns 0. fp32 selection has no such limit."""
+    from block_selection_amd import ops
+    big = 16384 * 1024 // 2                     # Hkv = 2: the largest N that fits
+    d = ops.make_dims(1, 32, 2, 8)
+    assert ops.workspace_bytes(d, big) > 0
+    assert ops.workspace_bytes(d, big + 1) == 0
+    assert _call_select(ops, d, N=big, cap=big, ws_bytes=16) == ops.PISA_ERR_WORKSPACE   # passes the limit
+    assert _call_select(ops, d, N=big + 1, cap=big + 1) == ops.PISA_ERR_UNSUPPORTED
+    d16 = ops.make_dims(1, 16, 16, 8)           # Hkv = 16: the limit falls at 1048576 keys
+    assert _call_select(ops, d16, N=1048577, cap=1048577) == ops.PISA_ERR_UNSUPPORTED
+    assert ops.workspace_bytes(d16, 1048576) > 0
+    f32 = ops.make_dims(1, 32, 2, 8, dtype="f32")
+    assert ops.workspace_bytes(f32, big + 1) > 0
+
+
 def test_pack_geometry_helpers():
     """Packed layout: level l has (T >> (5 + l)) + D + 1 rows per KV head, levels 1 .. L(T)."""
     from block_selection_amd import ops

@@ -1,8 +1,8 @@
 """Pins of the oracle's stage-two attention over the selected blocks.
 
 Stage two (reading note "Block Sparse Attention with Log-Linear Complexity", the
-two-stage formulation it opens with) attends over the original keys and values
-inside the selected blocks. The oracle's reading: per query head, softmax of
+two-stage formulation it opens with) is attention limited to the raw key/value rows
+of the blocks stage one picked. The oracle's reading: per query head, softmax of
 q.k/sqrt(d) over the keys <= t of the blocks its KV head selected, applied to their
 values. Pins:
   * every eligible block selected: dense causal attention (torch's
