@@ -332,7 +332,7 @@ def test_prefill_batched(B, dtype):
         check_pyramid(gpu.pyramid[b:b + 1], ref_pyr, N, gpu.cap)
         ts = sample_positions(N, 500, wl.topk)
         rep = compare_selection(gpu.idx[b, ts], ts, inp.q[b], inp.k[b], ref_pyr, wl.topk)
-        _log(f"prefill_batched_B{B}_{dtype}_b{b}", rep)
+        _log(f"prefill_batched_B{B}_{dtype}_b{b}", rep, {"positions": int(len(ts)), "all_positions": False})
         assert rep.ok(), (b, str(rep))
 
 
