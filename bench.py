@@ -79,13 +79,14 @@ def walk_counts(N: int, topk: int, GQ: int, Hkv: int, C: int = 64):
     return out
 
 
-# MI355X transcendental peak: 256 CUs x 32 lanes/clock (v_exp_f32 / v_log_f32 issue at half the
-# 64-lane VALU rate) x 2.4 GHz
+# MI355X transcendental peak: 256 CUs x 32 lanes/clock (v_exp_f32 / v_log_f32 issue at a quarter
+# of the 128 lanes/clock of fp32 FMA that the published 157.3 TFLOP/s fp32 vector peak implies)
+# x 2.4 GHz. device_ceilings() measures it (exp2 98% of this on an MI355X, profiles/).
 TRANSCENDENTAL_PEAK = 256 * 32 * 2.4e9
-# VALU issue slots: 256 CUs x 64 lanes/clock x 2.4 GHz. A leaf logit of the exact LSE needs at
-# least four: the base-2 scale, the exp (two slots at half rate) and its add into the sum.
-VALU_SLOT_PEAK = 256 * 64 * 2.4e9
-LEAF_SLOTS_PER_LOGIT = 4
+# fp32 FMA lane operations: 256 CUs x 128 lanes/clock x 2.4 GHz (157.3 TFLOP/s / 2)
+VALU_SLOT_PEAK = 256 * 128 * 2.4e9
+# dense bf16 MFMA peak of MI355X (published, no sparsity)
+MFMA_BF16_PEAK = 2.5e15
 
 
 # sources of the two walk kernels (a traffic figure is only valid for the code it was taken on)
@@ -182,6 +183,45 @@ def copy_bandwidth(torch, dev, nbytes: int = 1 << 30, reps: int = 10) -> float:
     return 2 * nbytes / (ms / 1e3) / 1e9
 
 
+def device_ceilings(torch, dev, log, iters: int = 512, grid: int = 2048, reps: int = 5) -> dict:
+    """Issue rates measured on this GPU by the probes of libpisa_ceilings.so: v_exp_f32 and
+    v_log_f32 (lane results/s), v_fma_f32 (lane ops/s) and v_mfma_f32_16x16x32_bf16 (flop/s).
+    Each probe runs 2048 workgroups of 256 threads issuing one instruction kind over
+    independent chains; the best of five launches, timed with events on the launch stream."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "block_selection_amd", "libpisa_ceilings.so"))
+    lib.pisa_ceiling_ops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.pisa_ceiling_ops.restype = ctypes.c_double
+    lib.pisa_ceiling_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.pisa_ceiling_launch.restype = ctypes.c_int
+    out = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    res = {"probe": f"{grid} workgroups x 256 threads, {iters} loop trips, best of {reps} launches"}
+    for kind, name in ((0, "exp2_per_s"), (1, "log2_per_s"), (2, "fma_lane_ops_per_s"), (3, "mfma_bf16_flop_per_s")):
+        if lib.pisa_ceiling_launch(kind, iters, grid, ctypes.c_void_p(out.data_ptr()),
+                                   ctypes.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("ceiling probe launch failed")
+        best = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            lib.pisa_ceiling_launch(kind, iters, grid, ctypes.c_void_p(out.data_ptr()),
+                                    ctypes.c_void_p(stream.cuda_stream))
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        res[name] = lib.pisa_ceiling_ops(kind, iters, grid) / (best / 1e3)
+    res["exp2_frac_of_derived_peak"] = res["exp2_per_s"] / TRANSCENDENTAL_PEAK
+    res["log2_frac_of_derived_peak"] = res["log2_per_s"] / TRANSCENDENTAL_PEAK
+    res["fma_frac_of_derived_peak"] = res["fma_lane_ops_per_s"] / VALU_SLOT_PEAK
+    res["mfma_bf16_frac_of_published_peak"] = res["mfma_bf16_flop_per_s"] / MFMA_BF16_PEAK
+    log(f"ceilings: exp2 {res['exp2_per_s'] / 1e12:.2f} T/s ({100 * res['exp2_frac_of_derived_peak']:.0f}% of "
+        f"{TRANSCENDENTAL_PEAK / 1e12:.2f}), log2 {res['log2_per_s'] / 1e12:.2f} T/s, fma "
+        f"{res['fma_lane_ops_per_s'] / 1e12:.1f} T lane-ops/s ({100 * res['fma_frac_of_derived_peak']:.0f}% of "
+        f"{VALU_SLOT_PEAK / 1e12:.1f}), bf16 MFMA {res['mfma_bf16_flop_per_s'] / 1e15:.2f} PFLOP/s")
+    del out
+    return res
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -193,29 +233,85 @@ def _cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(inp, topk: int, n_positions: int, seed: int = 1):
-    """The fp64 oracle on the host cores, on a seeded sample of query positions."""
+def cpu_baseline(inp, topk: int, n_positions: int, seed: int = 1, gpu_idx=None, gpu_pyr=None):
+    """The fp64 oracle on the host cores: the pyramid build over all N keys, then the walks of
+    every query position (n_positions <= 0) or of a seeded sample of them. When the GPU's
+    selection of the same inputs is given, every walked (position, KV head) is also compared
+    with the oracle's under the parity rule (bit-exact, or a near-tie whose mismatch
+    validates), and the result is returned as a second dict."""
     import oracle
     threads = len(os.sched_getaffinity(0))
     env_t = os.environ.get("OMP_NUM_THREADS")
     if env_t and env_t.isdigit():
         threads = min(threads, int(env_t))
     N = inp.q.shape[1]
-    rng = np.random.default_rng(seed)
-    ts = np.sort(rng.choice(N, size=min(n_positions, N), replace=False)).astype(np.int64)
     k0 = inp.k[0]
-    q_rows = np.ascontiguousarray(inp.q[0, ts])
+    if n_positions <= 0 or n_positions >= N:
+        ts = np.arange(N, dtype=np.int64)
+        q_rows = inp.q[0]
+        what = f"every one of the {N} query positions"
+    else:
+        rng = np.random.default_rng(seed)
+        ts = np.sort(rng.choice(N, size=n_positions, replace=False)).astype(np.int64)
+        q_rows = np.ascontiguousarray(inp.q[0, ts])
+        what = f"{len(ts)} seeded random query positions"
     t0 = time.perf_counter()
     pyr = oracle.build_pyramid(k0, nthreads=threads)
     t1 = time.perf_counter()
-    oracle.walk(q_rows, ts, k0, pyr, topk, nthreads=threads)
+    o_idx, o_gap, o_lvl = oracle.walk(q_rows, ts, k0, pyr, topk, nthreads=threads)
     t2 = time.perf_counter()
     build_s, walk_s = t1 - t0, t2 - t1
     per_query = walk_s / len(ts) + build_s / N
-    return {"value": 1.0 / per_query, "unit": "queries/s", "cores": threads, "kind": "oracle", "cpu": _cpu_model(),
-            "sample": (f"full fp64 pyramid build over N={N} keys ({build_s:.2f} s) plus walks for "
-                       f"{len(ts)} seeded random query positions x {inp.k.shape[2]} KV heads "
-                       f"({walk_s:.2f} s); queries/s = 1/(walk_s/positions + build_s/N)")}
+    base = {"value": 1.0 / per_query, "unit": "queries/s", "cores": threads, "kind": "oracle", "cpu": _cpu_model(),
+            "sample": (f"full fp64 pyramid build over N={N} keys ({build_s:.2f} s) plus walks for {what} x "
+                       f"{inp.k.shape[2]} KV heads ({walk_s:.2f} s); queries/s = 1/(walk_s/positions + build_s/N)")}
+    if gpu_idx is None:
+        return base, None
+    return base, parity_against_oracle(gpu_idx[0, ts], ts, inp.q[0], k0, pyr, topk, (o_idx, o_gap, o_lvl), gpu_pyr)
+
+
+NEAR_TIE = 1e-3
+
+
+def parity_against_oracle(gpu_idx, ts, q, k, pyr, topk, ora, gpu_pyr=None) -> dict:
+    """The parity rule on the benchmark's own output: per (position, KV head) the GPU's index
+    set equals the oracle's, or the oracle's walk had a near-tie (K-th and (K+1)-th scores
+    closer than 1e-3 at some scored level) and the GPU's set is reachable by resolving those
+    ties (oracle.validate; an undecided search counts against parity)."""
+    import oracle
+    o_idx, o_gap, o_lvl = ora
+    eq = np.all(gpu_idx == o_idx, axis=-1)
+    near = o_gap < NEAR_TIE
+    rec = {"walks": int(eq.size), "all_positions": bool(len(ts) == q.shape[0]), "exact": int(eq.sum()),
+           "near_tie_walks": int(near.sum()), "near_tie_rule": "gap < 1e-3 at any scored level",
+           "mismatch_valid": 0, "mismatch_invalid": 0, "mismatch_undecided": 0, "mismatch_outside_near_tie": 0}
+    lv, cnt = np.unique(o_lvl[near], return_counts=True)
+    rec["near_tie_by_level"] = {str(int(a)): int(b) for a, b in zip(lv, cnt)}
+    fin = np.isfinite(o_gap)
+    rec["min_gap"] = float(o_gap[fin].min()) if fin.any() else None
+    for i, j in zip(*np.nonzero(~eq)):
+        t = int(ts[i])
+        if not near[i, j]:
+            rec["mismatch_outside_near_tie"] += 1
+            continue
+        v = oracle.validate(q[t], t, int(j), k, pyr, topk, gpu_idx[i, j], NEAR_TIE, 200000)
+        if v < 0:
+            v = oracle.validate(q[t], t, int(j), k, pyr, topk, gpu_idx[i, j], NEAR_TIE, 5000000)
+        rec["mismatch_valid" if v == 1 else "mismatch_invalid" if v == 0 else "mismatch_undecided"] += 1
+    rec["green"] = (rec["mismatch_invalid"] + rec["mismatch_undecided"] + rec["mismatch_outside_near_tie"]) == 0
+    if gpu_pyr is not None:
+        # pyramid: per node ||gpu - ref||_2 <= 1e-5 ||ref||_2 and max|gpu - ref| <= 1e-5 max|ref|
+        worst = 0.0
+        for j in range(pyr.shape[0]):
+            ref = pyr[j]
+            got = gpu_pyr[0, j, :ref.shape[0]].astype(np.float64)
+            diff = got - ref
+            n2 = np.linalg.norm(diff, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+            ninf = np.abs(diff).max(axis=1) / np.maximum(np.abs(ref).max(axis=1), 1e-30)
+            worst = max(worst, float(n2.max()), float(ninf.max()))
+        rec["pyramid_worst_rel"] = worst
+        rec["green"] = rec["green"] and worst <= 1e-5
+    return rec
 
 
 def main():
@@ -226,7 +322,9 @@ def main():
     ap.add_argument("--workload", default="long256k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--cpu-positions", type=int, default=65536)
+    ap.add_argument("--cpu-positions", type=int, default=0,
+                    help="query positions the CPU oracle walks (0: all of them)")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the device-ceiling probes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device-to-device copy first (reference kernel for HBM counters)")
     ap.add_argument("--decode-only", action="store_true", help="time only the decode workload")
@@ -348,6 +446,9 @@ def main():
                                                                       args.warmup)
     ms_per_step = total_ms / args.steps
     value = wl.B * N / (ms_per_step / 1e3)
+    # the last timed step's output, for the parity check beside the CPU baseline
+    idx_host = out.cpu().numpy()
+    pyr_host = pyr.cpu().numpy()
     log(f"N={N}: {ms_per_step:.3f} ms/step (build {build_ms.mean():.3f} ms, select {walk_ms.mean():.3f} ms: "
         f"upper walk {np.mean(upper_ms):.3f} ms, leaf scoring {np.mean(leaf_ms_steps):.3f} ms)")
 
@@ -373,9 +474,8 @@ def main():
         "algorithmic_per_launch": transc,
         "leaf_pairs_per_launch": wc["leaf_pairs"],
         "launch_ms": leaf_ms,
-        # the same launch against its VALU issue-slot floor (scale + exp + add per logit)
-        "valu_slot_floor_ms": wc["leaf_logits"] * LEAF_SLOTS_PER_LOGIT / VALU_SLOT_PEAK * 1e3,
-        "valu_slot_frac": wc["leaf_logits"] * LEAF_SLOTS_PER_LOGIT / VALU_SLOT_PEAK / (leaf_ms / 1e3),
+        # the launch's floor at the transcendental peak (every other instruction overlapped)
+        "transcendental_floor_ms": transc / TRANSCENDENTAL_PEAK * 1e3,
     }
     walk_s = walk_ms.mean() / 1e3
     upper_transc = wc["upper_logits"] + wc["upper_lse"]
@@ -393,6 +493,13 @@ def main():
         "algorithmic_per_launch": upper_transc,
         "launch_ms": upper_ms,
     }
+    # the peaks above are derived from unit counts and clock; the probes measure what this
+    # GPU issues (v_exp_f32 at half the VALU rate, the bf16 MFMA) for the same comparison
+    ceil = None if args.no_ceilings else device_ceilings(torch, dev, log)
+    if ceil:
+        for rf in (roofline, roofline_upper):
+            rf["measured_exp2_peak"] = ceil["exp2_per_s"] / 1e9
+            rf["frac_of_measured_exp2_peak"] = rf["achieved"] * 1e9 / ceil["exp2_per_s"]
     elt = 2 if wl.dtype == "bf16" else 4
     # the pyramid build is HBM-bound: compulsory bytes = keys read once + every node written once
     build_bytes = wl.B * N * wl.Hkv * wl.d * elt + wl.B * wl.Hkv * ops.pyramid_nodes(dims, N) * wl.d * 4
@@ -408,18 +515,19 @@ def main():
     # the pages' IO ledger (reading note section 5.1: per walk, gK candidate blocks whose queries
     # (GQ heads) and keys (C rows, shared by a tile of Qtile = 4 queries) cross HBM, 2-byte elements)
     ledger = wl.B * N * wl.Hkv * wl.g * wl.topk * wl.d * (GQ + wl.C / 4) * 2
-    hbm["ledger_bytes"] = ledger
-    hbm["ledger_GBs"] = ledger / (ms_per_step / 1e3) / 1e9
-    hbm["ledger_frac_of_8TBs"] = hbm["ledger_GBs"] / HBM_PEAK_GBS
+    # the pages' modelled bytes, not bytes that cross HBM: a rate, never a fraction of HBM peak
+    hbm["ledger_model_bytes"] = ledger
+    hbm["ledger_model_GBs"] = ledger / (ms_per_step / 1e3) / 1e9
     copy_gbs = copy_bandwidth(torch, q.device)
     hbm["device_copy_GBs"] = copy_gbs
+    # rocprofv3 FETCH_SIZE / WRITE_SIZE (calibrated) count bytes that miss L2; the Infinity
+    # Cache may serve part of them, so they bound the HBM bytes from above
     if traffic:
-        hbm["leaf_kernel_measured_GBs"] = traffic / (leaf_ms / 1e3) / 1e9
-        hbm["leaf_kernel_measured_frac_of_8TBs"] = traffic / (leaf_ms / 1e3) / 1e9 / HBM_PEAK_GBS
-        hbm["leaf_kernel_measured_frac_of_copy"] = traffic / (leaf_ms / 1e3) / 1e9 / copy_gbs
+        hbm["leaf_kernel_l2_miss_GBs_upper_bound"] = traffic / (leaf_ms / 1e3) / 1e9
+        hbm["leaf_kernel_l2_miss_frac_of_copy"] = traffic / (leaf_ms / 1e3) / 1e9 / copy_gbs
     if upper_traffic:
-        hbm["upper_kernel_measured_GBs"] = upper_traffic / (upper_ms / 1e3) / 1e9
-        hbm["upper_kernel_measured_frac_of_copy"] = upper_traffic / (upper_ms / 1e3) / 1e9 / copy_gbs
+        hbm["upper_kernel_l2_miss_GBs_upper_bound"] = upper_traffic / (upper_ms / 1e3) / 1e9
+        hbm["upper_kernel_l2_miss_frac_of_copy"] = upper_traffic / (upper_ms / 1e3) / 1e9 / copy_gbs
     work = {
         "select_ms": walk_ms.mean(),
         "upper_walk_ms": upper_ms,
@@ -450,6 +558,7 @@ def main():
                        "min_build_plus_walk": float(np.min(build_ms + walk_ms))},
         "roofline": roofline,
         "roofline_upper": roofline_upper,
+        "ceilings": ceil,
         "hbm": hbm,
         "work": work,
     }
@@ -501,8 +610,15 @@ def main():
         result["batched"] = batched_bench(torch, ops, dev, log)
 
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle baseline")
-        result["cpu_baseline"] = cpu_baseline(inp, wl.topk, args.cpu_positions)
+        log("timing the CPU oracle baseline, then comparing the timed steps' selection with it")
+        result["cpu_baseline"], par = cpu_baseline(inp, wl.topk, args.cpu_positions, gpu_idx=idx_host,
+                                                   gpu_pyr=pyr_host)
+        if par is not None:
+            result["parity"] = par
+            log(f"parity: {par['walks']} walks, {par['exact']} bit-exact, {par['near_tie_walks']} near-tie, "
+                f"mismatches valid {par['mismatch_valid']} / invalid {par['mismatch_invalid']} / undecided "
+                f"{par['mismatch_undecided']} / outside a near-tie {par['mismatch_outside_near_tie']}; "
+                f"pyramid worst {par.get('pyramid_worst_rel', float('nan')):.2e}")
     print(json.dumps(result), flush=True)
 
 
@@ -608,17 +724,28 @@ def attention_bench(torch, ops, synth, wl, N, dims, q, k, idx, steps, warmup, se
     alg = nsel * blk_bytes + walks * GQ * wl.d * (2 + 4)
     traffic = measured_traffic(f"sparse_attention_kernel:{wl.name}", _hash_sources(ATTN_SOURCES))
     flops = nsel * GQ * wl.C * wl.d * 2 * 2
+    # compulsory bytes of the call: Q, K and V once, the indices once, the fp32 output once
+    compulsory = walks * GQ * wl.d * 2 + 2 * walks * wl.d * 2 + walks * wl.topk * 4 + walks * GQ * wl.d * 4
     res = {"ms": ms, "queries_per_s": wl.B * N / (ms / 1e3),
            "step_plus_attention_ms": select_ms + ms, "selection_share": select_ms / (select_ms + ms),
            "roofline": {"kernel": "sparse_attention_kernel (+ vt_tiles_kernel, the per-call V re-layout)",
-                        "bound": "hbm", "achieved": alg / (ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": alg / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
-                        "algorithmic_per_launch": alg,
-                        "algorithmic_model": "per walk: K and V of each selected block (64 x 64 x 2 B each) + "
-                                             "its group's queries (bf16) and outputs (fp32)"},
-           "mfma_tflops": flops / (ms / 1e3) / 1e12}
-    log(f"attention over the selected blocks: {ms:.3f} ms ({res['roofline']['achieved']:.0f} GB/s of the "
-        f"per-query block reads); selection is {100 * res['selection_share']:.0f}% of selection + attention")
+                        "bound": "hbm", "achieved": compulsory / (ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": compulsory / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                        "traffic": None,
+                        "algorithmic_per_launch": compulsory,
+                        "algorithmic_model": "compulsory bytes: Q (bf16), K and V (bf16) and the indices read "
+                                             "once, the fp32 output written once",
+                        "mfma_tflops": flops / (ms / 1e3) / 1e12,
+                        "mfma_frac_of_bf16_peak": flops / (ms / 1e3) / MFMA_BF16_PEAK,
+                        # what the kernel actually moves: every query gathers its K blocks' keys and
+                        # values; L2 and the Infinity Cache serve part of it, so neither figure is HBM
+                        "per_query_block_reads_per_launch": alg,
+                        "per_query_block_reads_GBs": alg / (ms / 1e3) / 1e9,
+                        "l2_miss_bytes_per_launch": traffic,
+                        "l2_miss_GBs": None if not traffic else traffic / (ms / 1e3) / 1e9}}
+    log(f"attention over the selected blocks: {ms:.3f} ms ({res['roofline']['per_query_block_reads_GBs']:.0f} GB/s "
+        f"of per-query block reads, {res['roofline']['mfma_tflops']:.0f} TFLOP/s on the MFMA); selection is "
+        f"{100 * res['selection_share']:.0f}% of selection + attention")
     del v, out, ws
     return res
 

@@ -1,7 +1,8 @@
-"""Builds libpisa.so (HIP, gfx950) in-tree with hipcc.
+"""Builds libpisa.so (HIP, gfx950) in-tree with hipcc, and libpisa_ceilings.so
+(the benchmark's probes of the device ceilings).
 
-Usage: ``python -m block_selection_amd.build``. The library lands next to
-this file, where ``block_selection_amd.ops`` loads it from.
+Usage: ``python -m block_selection_amd.build``. The libraries land next to
+this file, where ``block_selection_amd.ops`` and bench.py load them from.
 """
 from __future__ import annotations
 
@@ -34,15 +35,26 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+# measurement probes of the device ceilings (not part of the selection), a library of their own
+CEILINGS_SOURCES = ["ceilings.hip"]
+CEILINGS_LIB = os.path.join(PKG, "libpisa_ceilings.so")
+
+
+def _compile(sources, out: str, verbose: bool) -> str:
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = out + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Builds libpisa.so and the ceilings probe library; returns the path of libpisa.so."""
+    _compile(CEILINGS_SOURCES, CEILINGS_LIB, verbose)
+    return _compile(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":
