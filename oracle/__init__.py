@@ -62,6 +62,10 @@ def _load():
     lib.pisa_oracle_validate.restype = i32
     lib.pisa_oracle_attention.argtypes = [P, P, i64, P, P, P, i64, i32, i32, i32, i32, i32, P, i32]
     lib.pisa_oracle_attention.restype = i32
+    lib.pisa_oracle_flat_select.argtypes = [P, P, i64, P, i64, i32, i32, i32, i32, i32, P, P, i32]
+    lib.pisa_oracle_flat_select.restype = i32
+    lib.pisa_oracle_flat_validate.argtypes = [P, i64, i32, P, i64, i32, i32, i32, i32, i32, P, dbl]
+    lib.pisa_oracle_flat_validate.restype = i32
     _lib = lib
     return lib
 
@@ -227,6 +231,43 @@ def attention(q_rows: np.ndarray, t_rows, k: np.ndarray, v: np.ndarray, idx: np.
     if rc != 0:
         raise RuntimeError(f"oracle attention failed ({rc})")
     return out
+
+
+def flat_select(q_rows: np.ndarray, t_rows, pyr: np.ndarray, N: int, topk: int, C: int = 64,
+                nthreads: int = 0):
+    """Flat stage-one selection: each query scores every eligible leaf summary (the sum over
+    its group's heads of q.kbar/sqrt(d)) and keeps the K best.
+
+    q_rows: float [n, Hq, d]; pyr from build_pyramid over N keys ([Hkv, rows, d]).
+    Returns (idx int32 [n, Hkv, topk] ascending, -1 padded; min_gap double [n, Hkv]).
+    """
+    q_rows = _f32(q_rows)
+    t_rows = np.ascontiguousarray(t_rows, dtype=np.int64)
+    n, Hq, d = q_rows.shape
+    Hkv = pyr.shape[0]
+    assert t_rows.shape == (n,)
+    pyr = np.ascontiguousarray(pyr, dtype=np.float64)
+    idx = np.zeros((n, Hkv, topk), np.int32)
+    gap = np.zeros((n, Hkv), np.float64)
+    rc = _load().pisa_oracle_flat_select(_p(q_rows), _p(t_rows), n, _p(pyr), N, Hq, Hkv, d, C, topk, _p(idx),
+                                         _p(gap), nthreads)
+    if rc != 0:
+        raise RuntimeError(f"oracle flat_select failed ({rc})")
+    return idx, gap
+
+
+def flat_validate(q_row: np.ndarray, t: int, j: int, pyr: np.ndarray, N: int, topk: int, target, eps: float,
+                  C: int = 64) -> int:
+    """1 if target is the flat selection under some resolution of the near-ties within eps, else 0."""
+    q_row = _f32(q_row)
+    Hq, d = q_row.shape
+    tg = np.ascontiguousarray(target, dtype=np.int32)
+    assert tg.shape == (topk,)
+    pyr = np.ascontiguousarray(pyr, dtype=np.float64)
+    r = _load().pisa_oracle_flat_validate(_p(q_row), t, j, _p(pyr), N, Hq, pyr.shape[0], d, C, topk, _p(tg), eps)
+    if r == -2:
+        raise RuntimeError("oracle flat_validate: bad arguments")
+    return int(r)
 
 
 # ------------------------------------------------------------------ packed documents --

@@ -29,6 +29,11 @@
  *     computes attention only over the raw key and value rows that belong to
  *     the picked blocks; the attention function below is that softmax
  *     attention, causally masked.
+ *   - same note, "Background: two stages, and the bottleneck in the first"
+ *     (and the ai4snews summary's first paragraph): the conventional stage one
+ *     the pyramid replaces scores every block summary against the query and
+ *     keeps the best K -- the flat selection below, with the leaf means as the
+ *     summaries.
  *
  * Readings taken where the pages are silent (each listed in the design notes):
  *   logit = q.k / sqrt(d); level sizes M_{l+1} = ceil(M_l / g) up to one node;
@@ -565,4 +570,116 @@ int pisa_oracle_attention(const float* q_rows, const int64_t* t_rows, int64_t n_
         free(key);
     }
     return bad ? -1 : 0;
+}
+
+
+/*
+ * Flat stage-one selection ("Block Sparse Attention with Log-Linear Complexity",
+ * "Background: two stages, and the bottleneck in the first"; ai4snews summary, first
+ * paragraph): every leaf block has a mean-pooled summary (level 1 of the pyramid), and
+ * each query scores ALL of them and keeps the K best -- no hierarchy. Readings (the score
+ * formula is stripped on the pages): the score of block b for query position t and KV
+ * head j is the sum over the group's query heads of q_{t,h} . kbar_b / sqrt(d), the
+ * group aggregation the note's section 4.1 gives for the pyramid's scores; block b is
+ * eligible iff its first key b*C <= t (its summary covers all its keys, as at the upper
+ * levels of the walk); equal scores rank the lower index first; the output is the
+ * selected set in ascending order, -1 padded (all eligible blocks when at most K are).
+ */
+static double flat_score(const geom_t* G, const float* q, const double* pyr, int j, int64_t b) {
+    const int GQ = G->Hq / G->Hkv, d = G->d;
+    const double* kb = pyr + ((int64_t)j * G->total + G->off[1] + b) * d;
+    double S = 0.0;
+    for (int hh = 0; hh < GQ; hh++) {
+        const float* qh = q + (int64_t)(j * GQ + hh) * d;
+        double dot = 0.0;
+        for (int e = 0; e < d; e++) dot += (double)qh[e] * kb[e];
+        S += dot / sqrt((double)d);
+    }
+    return S;
+}
+
+/* Scores of the eligible blocks of position t, sorted in selection order; returns their count. */
+static int64_t flat_sorted(const geom_t* G, const float* q, const double* pyr, int64_t t, int j, scored_t* sc) {
+    int64_t n = t / G->C + 1;
+    if (n > G->M[1]) n = G->M[1];
+    for (int64_t b = 0; b < n; b++) {
+        sc[b].node = b;
+        sc[b].s = flat_score(G, q, pyr, j, b);
+    }
+    qsort(sc, (size_t)n, sizeof(scored_t), cmp_scored);
+    return n;
+}
+
+/*
+ * Flat selection for the query rows of positions t_rows (one batch element).
+ * q_rows: float [n_rows, Hq, d]; pyr from pisa_oracle_build_pyramid over N keys.
+ * Outputs: out_idx int32 [n_rows, Hkv, topk] (ascending, -1 padded), min_gap double
+ * [n_rows, Hkv] = S_(K) - S_(K+1) (INFINITY when at most K blocks are eligible).
+ */
+int pisa_oracle_flat_select(const float* q_rows, const int64_t* t_rows, int64_t n_rows, const double* pyr,
+                            int64_t N, int Hq, int Hkv, int d, int C, int topk, int32_t* out_idx,
+                            double* min_gap, int nthreads) {
+    geom_t G;
+    if (topk < 1 || topk > ORACLE_MAX_TOPK) return -1;
+    if (make_geom(&G, N, Hq, Hkv, d, C, 2, topk) != 0) return -1;
+    for (int64_t i = 0; i < n_rows; i++) if (t_rows[i] < 0 || t_rows[i] >= N) return -2;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    const int64_t total = n_rows * Hkv;
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t w = 0; w < total; w++) {
+        const int64_t i = w / Hkv;
+        const int j = (int)(w % Hkv);
+        scored_t* sc = (scored_t*)malloc(sizeof(scored_t) * (size_t)G.M[1]);
+        int64_t* keep = (int64_t*)malloc(sizeof(int64_t) * (size_t)topk);
+        const int64_t n = flat_sorted(&G, q_rows + i * (int64_t)Hq * d, pyr, t_rows[i], j, sc);
+        const int nk = (n < topk) ? (int)n : topk;
+        for (int c = 0; c < nk; c++) keep[c] = sc[c].node;
+        qsort(keep, (size_t)nk, sizeof(int64_t), cmp_i64);
+        for (int c = 0; c < topk; c++) out_idx[w * topk + c] = (c < nk) ? (int32_t)keep[c] : -1;
+        if (min_gap) min_gap[w] = (n > topk) ? sc[topk - 1].s - sc[topk].s : INFINITY;
+        free(sc);
+        free(keep);
+    }
+    return 0;
+}
+
+/*
+ * Near-tie check of a flat selection: 1 if `target` (topk entries, -1 padded, any order)
+ * is the K best eligible blocks under some resolution of the scores within eps of the
+ * K-th score (it holds min(K, eligible) distinct eligible blocks, every block scoring more
+ * than eps above the K-th, and none scoring more than eps below it), else 0.
+ */
+int pisa_oracle_flat_validate(const float* q_row, int64_t t, int j, const double* pyr, int64_t N, int Hq,
+                              int Hkv, int d, int C, int topk, const int32_t* target, double eps) {
+    geom_t G;
+    if (topk < 1 || topk > ORACLE_MAX_TOPK) return -2;
+    if (make_geom(&G, N, Hq, Hkv, d, C, 2, topk) != 0) return -2;
+    if (t < 0 || t >= N || j < 0 || j >= Hkv) return -2;
+    scored_t* sc = (scored_t*)malloc(sizeof(scored_t) * (size_t)G.M[1]);
+    const int64_t n = flat_sorted(&G, q_row, pyr, t, j, sc);
+    const int want = (n < topk) ? (int)n : topk;
+    int ok = 1, cnt = 0;
+    for (int c = 0; c < topk && ok; c++) {
+        const int32_t b = target[c];
+        if (b < 0) continue;
+        if (b >= n) { ok = 0; break; }                       /* not eligible */
+        for (int e = 0; e < c; e++) if (target[e] == b) ok = 0;   /* duplicate */
+        cnt++;
+    }
+    if (ok && cnt != want) ok = 0;
+    if (ok && n > topk) {
+        const double sK = sc[topk - 1].s;
+        for (int64_t r = 0; r < n && ok; r++) {
+            int in = 0;
+            for (int c = 0; c < topk; c++) if (target[c] == sc[r].node) in = 1;
+            if (sc[r].s > sK + eps && !in) ok = 0;           /* surely kept, missing */
+            if (sc[r].s < sK - eps && in) ok = 0;            /* surely dropped, present */
+        }
+    }
+    free(sc);
+    return ok;
 }
