@@ -424,6 +424,29 @@ def main():
                 hip.hipEventDestroy(ctypes.c_void_p(e))
         return total_ms, build, walk, upper, leaf
 
+    def time_flat(N, dims, q, k, pyr, steps, warmup):
+        """K steps of the flat stage-one selection (pyramid build, whose leaf means it scores, then
+        pisa_select_flat), timed like time_steps; returns (ms per step, selection ms per step, out)."""
+        stream = torch.cuda.current_stream()
+        out_f = torch.empty((dims.B, N, dims.Hkv, dims.topk), dtype=torch.int32, device=dev)
+        ws_f = ops.alloc_flat_workspace(dims, N, device=dev)
+        for _ in range(warmup):
+            ops.build_pyramid(k, N, N, dims, pyr)
+            ops.select_flat(q, pyr, N, N, dims, out_f, ws_f)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record(stream)
+            ops.build_pyramid(k, N, N, dims, pyr)
+            ev[i][1].record(stream)
+            ops.select_flat(q, pyr, N, N, dims, out_f, ws_f)
+            ev[i][2].record(stream)
+        torch.cuda.synchronize()
+        tot = float(np.mean([e[0].elapsed_time(e[2]) for e in ev]))
+        sel = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+        del ws_f
+        return tot, sel, out_f
+
     if args.decode_only:
         print(json.dumps({"decode": decode_bench(torch, ops, synth, dev, log)}), flush=True)
         return
@@ -587,11 +610,16 @@ def main():
             log(f"K={kk}: {tot_k / 10:.3f} ms/step (upper walk {up_k.mean():.3f} ms, leaf scoring {lf_k.mean():.3f} ms)")
             del out_k, ws_k
         result["topk_sweep"] = ksweep
+        # the flat stage-one selection at the headline length, beside the pyramid walk
+        ftot, fsel, out_flat = time_flat(N, dims, q, k, pyr, 10, 3)
+        flat = {args.workload: {"N": N, "pyramid_step_ms": ms_per_step, "flat_step_ms": ftot,
+                                "flat_select_ms": fsel, "pyramid_over_flat": ms_per_step / ftot}}
+        del out_flat
     del q, k, pyr, out, ws
 
     if not args.no_extras:
         # the headline shape at other lengths (the pages' benchmark spans short sequences, where
-        # selection is launch-bound, to 256K)
+        # selection is launch-bound, to 256K), the flat selection beside it
         sweep = {}
         for name, n2 in (("N4096", 4096), ("N16384", 16384), ("N32768", 32768), ("long64k", None),
                          ("long128k", None)):
@@ -602,8 +630,14 @@ def main():
             tot2, b2, wk2, _, _ = time_steps(N2, d2, q2, k2, p2, o2, ws2, 10, 3)
             sweep[name] = {"N": N2, "ms": tot2 / 10, "queries_per_s": N2 / (tot2 / 10 / 1e3),
                            "build_ms": float(b2.mean()), "walk_ms": float(wk2.mean())}
+            ftot, fsel, _ = time_flat(N2, d2, q2, k2, p2, 10, 3)
+            flat[name] = {"N": N2, "pyramid_step_ms": tot2 / 10, "flat_step_ms": ftot,
+                          "flat_select_ms": fsel, "pyramid_over_flat": (tot2 / 10) / ftot}
             del q2, k2, p2, o2, ws2
         result["sweep"] = sweep
+        result["flat"] = flat
+        log("flat stage-one selection beside the pyramid walk (ms per step, build included): " +
+            ", ".join(f"N={v['N']}: {v['flat_step_ms']:.3f} vs {v['pyramid_step_ms']:.3f}" for v in flat.values()))
         result["planted"] = planted_bench(torch, ops, synth, setup, time_steps, log)
         result["decode"] = decode_bench(torch, ops, synth, dev, log)
         result["packed"] = packed_bench(torch, ops, synth, dev, log)
@@ -645,12 +679,19 @@ def planted_bench(torch, ops, synth, setup, time_steps, log, n_flat: int = 96, s
     denom = np.minimum(K, p_elig)[:, None]
     recall = float((hit / denom).mean())
     chance = float((K * p_elig / n_elig / np.minimum(K, p_elig)).mean())
+    # the flat stage-one selection (pisa_select_flat: every leaf mean scored) on the same inputs
+    out_f = torch.empty_like(out)
+    ops.build_pyramid(k, N, N, dims, pyr)
+    ops.select_flat(q, pyr, N, N, dims, out_f, ops.alloc_flat_workspace(dims, N, device=q.device))
+    fidx = out_f.cpu().numpy()[0]
+    recall_flat_mean = float((np.isin(fidx[ts], planted).sum(axis=2) / denom).mean())
     # flat exact top-K on a sample
     rng = np.random.default_rng(seed)
     sample = np.sort(rng.choice(ts, size=min(n_flat, len(ts)), replace=False))
     GQ = wl.Hq // wl.Hkv
     qf, kf = inp.q[0].astype(np.float64), inp.k[0].astype(np.float64)
     flat, walk, overlap, mref, mratio, mratio_flat, mratio_rand = [], [], [], [], [], [], []
+    mratio_fm, overlap_fm = [], []
     for t in sample:
         nl = t // C + 1
         pe = planted[planted < nl]
@@ -677,6 +718,9 @@ def planted_bench(torch, ops, synth, setup, time_steps, log, n_flat: int = 96, s
             mratio.append(float(mass[sel].sum() / mass[ref].sum()))
             mratio_flat.append(float(mass[top].sum() / mass[ref].sum()))
             mratio_rand.append(float(mass[rng.choice(nl, K, replace=False)].sum() / mass[ref].sum()))
+            fsel = [x for x in fidx[t, j].tolist() if x >= 0]
+            mratio_fm.append(float(mass[fsel].sum() / mass[ref].sum()))
+            overlap_fm.append(len(set(fsel) & set(top.tolist())) / min(K, nl))
     res = {"N": N, "ms": tot / 10, "queries_per_s": N / (tot / 10 / 1e3), "planted_recall": recall,
            "chance_recall": chance, "flat_exact_recall_sample": float(np.mean(flat)),
            "walk_recall_same_sample": float(np.mean(walk)), "sample_positions": int(len(sample)),
@@ -684,15 +728,19 @@ def planted_bench(torch, ops, synth, setup, time_steps, log, n_flat: int = 96, s
            "recall_at_K_vs_attention_mass_top_K": float(np.mean(mref)),
            "attention_mass_ratio": float(np.mean(mratio)),
            "attention_mass_ratio_flat_exact": float(np.mean(mratio_flat)),
-           "attention_mass_ratio_random_K": float(np.mean(mratio_rand))}
+           "attention_mass_ratio_random_K": float(np.mean(mratio_rand)),
+           "flat_mean_summary_planted_recall": recall_flat_mean,
+           "flat_mean_summary_attention_mass_ratio": float(np.mean(mratio_fm)),
+           "flat_mean_summary_overlap_vs_flat_exact": float(np.mean(overlap_fm))}
     log(f"planted 32K: {res['ms']:.3f} ms, planted recall {recall:.3f} (chance {chance:.3f}; on "
         f"{len(sample)} sampled positions flat exact top-K {res['flat_exact_recall_sample']:.3f}, the walk "
         f"{res['walk_recall_same_sample']:.3f}; overlap with flat exact top-K "
         f"{res['overlap_recall_at_K_vs_flat_exact']:.3f}; against the K blocks of most attention mass: "
         f"recall {res['recall_at_K_vs_attention_mass_top_K']:.3f}, mass ratio {res['attention_mass_ratio']:.4f} "
         f"(flat exact top-K {res['attention_mass_ratio_flat_exact']:.4f}, K random eligible blocks "
-        f"{res['attention_mass_ratio_random_K']:.4f}))")
-    del q, k, pyr, out, ws
+        f"{res['attention_mass_ratio_random_K']:.4f})); flat stage-one selection by leaf means: planted recall "
+        f"{recall_flat_mean:.3f}, mass ratio {res['flat_mean_summary_attention_mass_ratio']:.4f}")
+    del q, k, pyr, out, ws, out_f
     return res
 
 

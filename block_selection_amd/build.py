@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpisa.so")
-SOURCES = ["pyramid.hip", "upper.hip", "leaf.hip", "cluster.hip", "decode.hip", "attention.hip", "api.hip"]
+SOURCES = ["pyramid.hip", "upper.hip", "leaf.hip", "cluster.hip", "decode.hip", "attention.hip", "flat.hip",
+           "api.hip"]
 ARCH = os.environ.get("PISA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -48,6 +48,9 @@ __global__ void sparse_attention_kernel(const uint16_t*, const uint16_t*, const 
                                         Pack, int64_t, float*);
 __global__ void decode_attention_kernel(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, const int32_t*,
                                         Geom, int64_t, uint32_t*, float*, float*);
+__global__ void flat_planes_kernel(const float*, Geom, uint16_t*);
+template <typename KT, int CAP>
+__global__ void flat_select_kernel(const KT*, const uint16_t*, Geom, int32_t*);
 constexpr int kDecAttnBlocksPerGroup = 4;                          // wavefronts (blocks) per workgroup
 // A decoding step (selection or attention) spreads each sequence's leaf or block work over
 // several workgroups only while the whole grid stays within this many: past it the
@@ -825,6 +828,48 @@ int pisa_sparse_attention_packed(const void* q, const void* k, const void* v, co
     const Pack pk{cu_seqlens, (int32_t)D, T};
     return attention_impl((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, G, pk, nslots, out,
                           (uint16_t*)workspace, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------- flat stage-one selection --
+
+// hi/lo bf16 planes of the leaf means: 2 * B * Hkv * ceil(N / 64) rows of 64 elements.
+static size_t flat_ws(const pisa_dims* d, int64_t N) {
+    const int64_t m1 = (N + kC - 1) / kC;
+    return align_up((size_t)2 * d->B * d->Hkv * m1 * kD * sizeof(uint16_t));
+}
+
+size_t pisa_flat_workspace_bytes(const pisa_dims* dims, int64_t N, int64_t n_capacity) {
+    Geom G;
+    if (check_dims(dims) != PISA_OK || make_geom(dims, N, n_capacity, &G) != PISA_OK) return 0;
+    return flat_ws(dims, N);
+}
+
+int pisa_select_flat(const void* q, const float* pyramid, int64_t N, int64_t n_capacity, const pisa_dims* dims,
+                     int32_t* out_idx, void* workspace, size_t ws_bytes, void* stream) {
+    int rc = check_dims(dims);
+    if (rc != PISA_OK) return rc;
+    if (!q || !pyramid || !out_idx) return PISA_ERR_INVALID_ARG;
+    Geom G;
+    if ((rc = make_geom(dims, N, n_capacity, &G)) != PISA_OK) return rc;
+    const int64_t waves = (int64_t)dims->B * dims->Hkv * G.M[1];   // one per 64 positions
+    if (waves > INT_MAX) return PISA_ERR_UNSUPPORTED;
+    if (!workspace || ws_bytes < flat_ws(dims, N)) return PISA_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    uint16_t* planes = (uint16_t*)workspace;
+    int64_t pgrid = ((int64_t)dims->B * dims->Hkv * G.M[1] * kD + 255) / 256;
+    if (pgrid > 8192) pgrid = 8192;
+    hipLaunchKernelGGL(flat_planes_kernel, dim3((unsigned)pgrid), dim3(256), 0, s, pyramid, G, planes);
+    // a list holds the K best plus one tile (16) of new candidates
+    const bool small = dims->topk <= 16;
+    const dim3 grid((unsigned)waves), block(64);
+    if (dims->dtype == PISA_DTYPE_BF16) {
+        if (small) hipLaunchKernelGGL((flat_select_kernel<uint16_t, 32>), grid, block, 0, s, (const uint16_t*)q, planes, G, out_idx);
+        else hipLaunchKernelGGL((flat_select_kernel<uint16_t, 64>), grid, block, 0, s, (const uint16_t*)q, planes, G, out_idx);
+    } else {
+        if (small) hipLaunchKernelGGL((flat_select_kernel<float, 32>), grid, block, 0, s, (const float*)q, planes, G, out_idx);
+        else hipLaunchKernelGGL((flat_select_kernel<float, 64>), grid, block, 0, s, (const float*)q, planes, G, out_idx);
+    }
+    return launch_status();
 }
 
 const char* pisa_status_string(int status) {

@@ -32,7 +32,8 @@ EXPORTED = ("pisa_pyramid_nodes", "pisa_level_offset", "pisa_pyramid_bytes", "pi
             "pisa_pack_level_offset", "pisa_pack_pyramid_bytes", "pisa_pack_workspace_bytes",
             "pisa_build_pyramid_packed", "pisa_select_prefill_packed", "pisa_attention_workspace_bytes",
             "pisa_sparse_attention", "pisa_pack_attention_workspace_bytes", "pisa_sparse_attention_packed",
-            "pisa_decode_attention", "pisa_decode_attention_workspace_bytes")
+            "pisa_decode_attention", "pisa_decode_attention_workspace_bytes", "pisa_flat_workspace_bytes",
+            "pisa_select_flat")
 
 
 class Dims(ctypes.Structure):
@@ -98,6 +99,10 @@ def _load() -> ctypes.CDLL:
     lib.pisa_decode_attention_workspace_bytes.restype = sz
     lib.pisa_decode_attention.argtypes = [P, P, P, P, P, i64, i64, D, P, P, sz, P]
     lib.pisa_decode_attention.restype = ctypes.c_int
+    lib.pisa_flat_workspace_bytes.argtypes = [D, i64, i64]
+    lib.pisa_flat_workspace_bytes.restype = sz
+    lib.pisa_select_flat.argtypes = [P, P, i64, i64, D, P, P, sz, P]
+    lib.pisa_select_flat.restype = ctypes.c_int
     lib.pisa_status_string.argtypes = [ctypes.c_int]
     lib.pisa_status_string.restype = ctypes.c_char_p
     return lib
@@ -361,3 +366,31 @@ def decode_attention(q_new: torch.Tensor, v_new: Optional[torch.Tensor], k_cache
                                    ctypes.byref(dims), _ptr(out), _ptr(workspace), ws_n, _stream(stream))
     if rc != PISA_OK:
         raise PisaError("pisa_decode_attention", rc)
+
+
+# ------------------------------------------------------- flat stage-one selection --
+# The selection the pyramid replaces: every query scores every eligible leaf summary (the
+# sum over its group's heads of q.kbar/sqrt(d)) and keeps the K best. Reads level 1 of a
+# pyramid written by build_pyramid; out_idx [B, N, Hkv, K] as select_prefill writes it.
+
+def flat_workspace_bytes(dims: Dims, N: int, n_capacity: Optional[int] = None) -> int:
+    cap = N if n_capacity is None else n_capacity
+    return int(lib.pisa_flat_workspace_bytes(ctypes.byref(dims), N, cap))
+
+
+def alloc_flat_workspace(dims: Dims, N: int, n_capacity: Optional[int] = None,
+                         device="cuda") -> Optional[torch.Tensor]:
+    n = flat_workspace_bytes(dims, N, n_capacity)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def select_flat(q: torch.Tensor, pyramid: torch.Tensor, N: int, n_capacity: int, dims: Dims,
+                out_idx: torch.Tensor, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    _check(q, "q", dims.torch_dtype, dims.B * N * dims.Hq * dims.d)
+    _check(pyramid, "pyramid", torch.float32, dims.B * dims.Hkv * pyramid_nodes(dims, n_capacity) * dims.d)
+    _check(out_idx, "out_idx", torch.int32, dims.B * N * dims.Hkv * dims.topk)
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.pisa_select_flat(_ptr(q), _ptr(pyramid), N, n_capacity, ctypes.byref(dims), _ptr(out_idx),
+                              _ptr(workspace), ws_n, _stream(stream))
+    if rc != PISA_OK:
+        raise PisaError("pisa_select_flat", rc)

@@ -299,6 +299,39 @@ int pisa_sparse_attention_packed(const void* q, const void* k, const void* v, co
                                  const int32_t* cu_seqlens, int64_t D, int64_t T, const pisa_dims* dims,
                                  float* out, void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------- flat stage-one selection
+ *
+ * The selection the pyramid replaces (reading note "Block Sparse Attention with
+ * Log-Linear Complexity", "Background: two stages, and the bottleneck in the first";
+ * ai4snews summary, first paragraph): every query scores every eligible leaf block's
+ * mean-pooled summary and keeps the K best, with no hierarchy. Score of block b for
+ * query position t and KV head j: the sum over the group's query heads h of
+ * q_{t,h} . kbar_b / sqrt(d), kbar_b the mean of all the block's keys (level 1 of the
+ * pyramid); block b is eligible iff b * C <= t; equal scores rank the lower block first.
+ */
+
+/* Device workspace of pisa_select_flat (0 on bad input): the leaf summaries as bf16
+ * hi/lo planes, 2 * B * Hkv * ceil(N / 64) * 64 * 2 bytes. Contents need not be
+ * initialised and are meaningless after the call. */
+size_t pisa_flat_workspace_bytes(const pisa_dims* dims, int64_t N, int64_t n_capacity);
+
+/*
+ * Flat selection for every query position t in 0..N-1.
+ *   q        [B, N, Hq, d] of dims->dtype (bf16 or fp32).
+ *   pyramid  as written by pisa_build_pyramid for the same N and n_capacity (only level 1,
+ *            the leaf means, is read).
+ *   out_idx  int32 [B, N, Hkv, topk]: the K best eligible blocks in ascending order, -1
+ *            padded (every eligible block when at most K are).
+ *   workspace at least pisa_flat_workspace_bytes(dims, N, n_capacity) bytes.
+ * dims->score is not used (this selector has the one score above).
+ * Arithmetic: the group's query rows are summed in fp32; that sum and the leaf means are
+ * each held as a hi + lo pair of bf16 values, whose three leading cross products are
+ * accumulated in fp32 on the MFMA (scores within about 2^-16 relative of the exact dot
+ * product). Errors: as pisa_select_prefill.
+ */
+int pisa_select_flat(const void* q, const float* pyramid, int64_t N, int64_t n_capacity, const pisa_dims* dims,
+                     int32_t* out_idx, void* workspace, size_t ws_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* pisa_status_string(int status);
 
