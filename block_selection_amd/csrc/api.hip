@@ -6,6 +6,8 @@
 #include <limits.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "pisa.h"
 #include "pisa_device.h"
 
@@ -624,6 +626,25 @@ int pisa_select_prefill(const void* q, const void* k, const float* pyramid, int6
                                         stream, nullptr);
 }
 
+// The bf16 decoding step: append, refresh, walk and leaf top-K in one launch, ceil(2K/8)
+// workgroups per (batch, KV head) -- the last one to finish writes the selection -- or one
+// per (batch, KV head) when that would make more than kDecodeSplitMaxWorkgroups. W holds the
+// completion counters (zero before the step, left zero) and the leaf-score rows.
+static int launch_decode_bf16(const void* q_new, const void* k_new, void* k_cache, float* pyramid, const Geom& G,
+                              const pisa_dims* dims, int32_t* out_idx, const Workspace& W, hipStream_t s) {
+    const unsigned nbh = (unsigned)(dims->B * dims->Hkv);
+    unsigned parts = (unsigned)((2 * dims->topk + 7) / 8);
+    if ((int64_t)parts * nbh > kDecodeSplitMaxWorkgroups) parts = 1u;
+    const uint16_t* qn = (const uint16_t*)q_new;
+    const uint16_t* kn = (const uint16_t*)k_new;
+    uint16_t* kc = (uint16_t*)k_cache;
+    void* args[] = {(void*)&qn, (void*)&kn, (void*)&kc, (void*)&pyramid, (void*)&G, (void*)&W.done,
+                    (void*)&W.leaf_score, (void*)&out_idx};
+    if (hipLaunchKernel(decode_step_fn(G.score), dim3(parts, nbh), dim3(kDecodeThreads), args, 0, s) != hipSuccess)
+        return PISA_ERR_HIP;
+    return launch_status();
+}
+
 int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cache, float* pyramid,
                               int64_t n_before, int64_t n_capacity, const pisa_dims* dims,
                               int32_t* out_idx, void* workspace, size_t ws_bytes, void* stream) {
@@ -637,27 +658,70 @@ int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cach
     if (!workspace || ws_bytes < W.bytes) return PISA_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     const unsigned nbh = (unsigned)(dims->B * dims->Hkv);
-    if (dims->dtype == PISA_DTYPE_BF16) {
-        // append, refresh, walk and leaf top-K in one launch: ceil(2K/8) workgroups per
-        // (batch, KV head), the last one to finish writes the selection; one per (batch,
-        // KV head) when that would make more than kDecodeSplitMaxWorkgroups
-        unsigned parts = (unsigned)((2 * dims->topk + 7) / 8);
-        if ((int64_t)parts * nbh > kDecodeSplitMaxWorkgroups) parts = 1u;
-        const uint16_t* qn = (const uint16_t*)q_new;
-        const uint16_t* kn = (const uint16_t*)k_new;
-        uint16_t* kc = (uint16_t*)k_cache;
-        void* args[] = {(void*)&qn, (void*)&kn, (void*)&kc, (void*)&pyramid, (void*)&G, (void*)&W.done,
-                        (void*)&W.leaf_score, (void*)&out_idx};
-        if (hipLaunchKernel(decode_step_fn(G.score), dim3(parts, nbh), dim3(kDecodeThreads), args, 0, s) !=
-            hipSuccess)
-            return PISA_ERR_HIP;
-        return launch_status();
-    }
+    if (dims->dtype == PISA_DTYPE_BF16)
+        return launch_decode_bf16(q_new, k_new, k_cache, pyramid, G, dims, out_idx, W, s);
     hipLaunchKernelGGL(decode_refresh_kernel<float>, dim3(nbh), dim3(64), 0, s,
                        (const float*)k_new, (float*)k_cache, G, pyramid);
     if ((rc = launch_status()) != PISA_OK) return rc;
     return select_impl((const float*)q_new, (const float*)k_cache, pyramid, G, n_before, 1, out_idx, W, s,
                        nullptr);
+}
+
+// ------------------------------------------------- decoding step without allocation --
+// For callers that cannot allocate (graph capture, tight serving loops): the step's
+// counters and leaf-score rows live in this file-scope device array, one copy per GPU,
+// held until the process ends. Host code never passes `scratch` itself (its host-side
+// name is not a device address): the first call on a device takes the array's address
+// there with hipGetSymbolAddress and keeps it per device.
+constexpr int64_t kNoAllocMaxBH = 4096;                                  // batch x KV heads
+constexpr size_t kNoAllocCounterBytes = (size_t)kNoAllocMaxBH * sizeof(uint32_t);
+constexpr size_t kNoAllocBytes = kNoAllocCounterBytes + (size_t)kNoAllocMaxBH * 64 * sizeof(float);
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+constexpr int kNoAllocMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kNoAllocMaxDevices];
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
+// Device address of this device's scratch; at the first call on a device the completion
+// counters are zeroed (a fill kernel on `s`, ordered before the caller's step).
+static int noalloc_scratch(hipStream_t s, char** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PISA_ERR_HIP;
+    if (dev < 0 || dev >= kNoAllocMaxDevices) return PISA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PISA_ERR_HIP;
+        hipLaunchKernelGGL(zero_words_kernel, dim3(16), dim3(256), 0, s, (uint32_t*)ptr,
+                           (int64_t)(kNoAllocCounterBytes / sizeof(uint32_t)));
+        if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = (char*)g_scratch_ptr[dev];
+    return PISA_OK;
+}
+
+int pisa_decode_update_select_noalloc(const void* q_new, const void* k_new, void* k_cache, float* pyramid,
+                                      int64_t n_before, int64_t n_capacity, const pisa_dims* dims,
+                                      int32_t* out_idx, void* stream) {
+    int rc = check_dims(dims);
+    if (rc != PISA_OK) return rc;
+    if (!q_new || !k_new || !k_cache || !pyramid || !out_idx) return PISA_ERR_INVALID_ARG;
+    if (n_before < 1) return PISA_ERR_INVALID_ARG;
+    if (dims->dtype != PISA_DTYPE_BF16) return PISA_ERR_UNSUPPORTED;
+    if ((int64_t)dims->B * dims->Hkv > kNoAllocMaxBH) return PISA_ERR_WORKSPACE;   // beyond the static scratch
+    Geom G;
+    if ((rc = make_geom(dims, n_before + 1, n_capacity, &G)) != PISA_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    char* base = nullptr;
+    if ((rc = noalloc_scratch(s, &base)) != PISA_OK) return rc;
+    const Workspace W = carve(dims, 1, G.P, true, base);
+    if (W.bytes > kNoAllocBytes) return PISA_ERR_WORKSPACE;
+    return launch_decode_bf16(q_new, k_new, k_cache, pyramid, G, dims, out_idx, W, s);
 }
 
 // ------------------------------------------------------------- attention (stage two) --

@@ -33,7 +33,7 @@ EXPORTED = ("pisa_pyramid_nodes", "pisa_level_offset", "pisa_pyramid_bytes", "pi
             "pisa_build_pyramid_packed", "pisa_select_prefill_packed", "pisa_attention_workspace_bytes",
             "pisa_sparse_attention", "pisa_pack_attention_workspace_bytes", "pisa_sparse_attention_packed",
             "pisa_decode_attention", "pisa_decode_attention_workspace_bytes", "pisa_flat_workspace_bytes",
-            "pisa_select_flat")
+            "pisa_select_flat", "pisa_decode_update_select_noalloc")
 
 
 class Dims(ctypes.Structure):
@@ -103,6 +103,8 @@ def _load() -> ctypes.CDLL:
     lib.pisa_flat_workspace_bytes.restype = sz
     lib.pisa_select_flat.argtypes = [P, P, i64, i64, D, P, P, sz, P]
     lib.pisa_select_flat.restype = ctypes.c_int
+    lib.pisa_decode_update_select_noalloc.argtypes = [P, P, P, P, i64, i64, D, P, P]
+    lib.pisa_decode_update_select_noalloc.restype = ctypes.c_int
     lib.pisa_status_string.argtypes = [ctypes.c_int]
     lib.pisa_status_string.restype = ctypes.c_char_p
     return lib
@@ -224,6 +226,22 @@ def decode_update_select(q_new: torch.Tensor, k_new: torch.Tensor, k_cache: torc
                                        ws_n, _stream(stream))
     if rc != PISA_OK:
         raise PisaError("pisa_decode_update_select", rc)
+
+
+def decode_update_select_noalloc(q_new: torch.Tensor, k_new: torch.Tensor, k_cache: torch.Tensor,
+                                 pyramid: torch.Tensor, n_before: int, n_capacity: int, dims: Dims,
+                                 out_idx: torch.Tensor, stream=None) -> None:
+    """decode_update_select (bf16) without a workspace: the library's static per-GPU scratch
+    serves instead (B * Hkv <= 4096; calls overlapping on one GPU race)."""
+    _check(q_new, "q_new", dims.torch_dtype, dims.B * dims.Hq * dims.d)
+    _check(k_new, "k_new", dims.torch_dtype, dims.B * dims.Hkv * dims.d)
+    _check(k_cache, "k_cache", dims.torch_dtype, dims.B * n_capacity * dims.Hkv * dims.d)
+    _check(pyramid, "pyramid", torch.float32, dims.B * dims.Hkv * pyramid_nodes(dims, n_capacity) * dims.d)
+    _check(out_idx, "out_idx", torch.int32, dims.B * dims.Hkv * dims.topk)
+    rc = lib.pisa_decode_update_select_noalloc(_ptr(q_new), _ptr(k_new), _ptr(k_cache), _ptr(pyramid), n_before,
+                                               n_capacity, ctypes.byref(dims), _ptr(out_idx), _stream(stream))
+    if rc != PISA_OK:
+        raise PisaError("pisa_decode_update_select_noalloc", rc)
 
 
 # ------------------------------------------------------------------ packed documents --

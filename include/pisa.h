@@ -177,6 +177,25 @@ int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cach
                               const pisa_dims* dims, int32_t* out_idx, void* workspace,
                               size_t ws_bytes, void* stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): pisa_decode_update_select for bf16
+ * inputs without a workspace argument. Its completion counters and leaf-score rows live in
+ * a static device array of the library (1,064,960 bytes per GPU, held until the process
+ * ends), whose address is taken once per device at the first call there (that call also
+ * enqueues one small kernel on `stream` that zeroes the counters; every step leaves them
+ * zero again). It allocates nothing and calls no allocating routine.
+ * Limits and errors: B * Hkv <= 4096 (else PISA_ERR_WORKSPACE); fp32 inputs return
+ * PISA_ERR_UNSUPPORTED; otherwise as pisa_decode_update_select, whose selection and
+ * refreshed pyramid it reproduces bit for bit.
+ * Every call on one GPU shares that array: calls that overlap on one GPU (two streams or
+ * host threads with steps in flight at the same time) race and give undefined results;
+ * enqueue them on one stream, or order them.
+ */
+int pisa_decode_update_select_noalloc(const void* q_new, const void* k_new, void* k_cache, float* pyramid,
+                                      int64_t n_before, int64_t n_capacity, const pisa_dims* dims,
+                                      int32_t* out_idx, void* stream);
+
 /* ------------------------------------------------------- attention (stage two)
  *
  * Reading note "Block Sparse Attention with Log-Linear Complexity", the two-stage

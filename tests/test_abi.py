@@ -75,6 +75,22 @@ def test_argument_errors_return_before_launch():
     assert ops.status_string(ops.PISA_ERR_WORKSPACE) == "workspace too small"
 
 
+def test_noalloc_decode_argument_errors_return_before_launch():
+    """The decoding step without allocation rejects, before touching the GPU, batches beyond
+    its static scratch (B * Hkv > 4096), fp32 inputs, bad pointers and bad lengths."""
+    from block_selection_amd import ops
+    p = ctypes.c_void_p(8)
+
+    def step(dims, n_before=64, cap=128, ptr=p):
+        return ops.lib.pisa_decode_update_select_noalloc(ptr, p, p, p, n_before, cap, ctypes.byref(dims), p, None)
+    assert step(ops.make_dims(2049, 32, 2, 8)) == ops.PISA_ERR_WORKSPACE       # 4098 pairs
+    assert step(ops.make_dims(1, 32, 2, 8, dtype="f32")) == ops.PISA_ERR_UNSUPPORTED
+    assert step(ops.make_dims(1, 32, 2, 8), ptr=None) == ops.PISA_ERR_INVALID_ARG
+    assert step(ops.make_dims(1, 32, 2, 8), n_before=0) == ops.PISA_ERR_INVALID_ARG
+    assert step(ops.make_dims(1, 32, 2, 8), n_before=128) == ops.PISA_ERR_CAPACITY
+    assert step(ops.make_dims(1, 32, 2, 33)) == ops.PISA_ERR_UNSUPPORTED
+
+
 def test_bf16_prefill_beyond_the_cluster_histogram_is_refused():
     """bf16 selection needs Hkv * ceil(N / 1024) <= 16384 (one LDS histogram of the leaf
     stage's groups); past it the call returns UNSUPPORTED before any launch and the
