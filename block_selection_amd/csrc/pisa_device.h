@@ -221,6 +221,17 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 
 __device__ inline float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
+// Raw buffer reads (gfx9 buffer resource, word 3 = 0x00020000): a wave-uniform base and
+// range in scalar registers, a 32-bit per-lane byte offset, constant offsets folded into
+// the instruction; reads at or past `bytes` return zero.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc_t;
+__device__ inline buf_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ inline u32x4 load_b128(buf_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
 // Eight consecutive elements of a row as floats (bf16 or fp32 storage).
 __device__ inline void load8_f32(const uint16_t* p, float v[8]) {
     const u32x4 w = *reinterpret_cast<const u32x4*>(p);

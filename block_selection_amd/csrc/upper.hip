@@ -123,6 +123,18 @@ __device__ inline TileRows rows_lds(const lds_char_t* lds, int lds_node, int gq)
     return r;
 }
 
+// Row `row` of a level's hi and lo planes through buffer resources based at the level's
+// first row (64 bf16 = 128 bytes per row): one 32-bit offset per lane.
+__device__ inline TileRows rows_buffer(buf_rsrc_t hi, buf_rsrc_t lo, int row, int gq) {
+    const uint32_t off = ((uint32_t)row << 7) + ((uint32_t)gq << 4);
+    TileRows r;
+    r.h0 = load_b128(hi, off);
+    r.h1 = load_b128(hi, off + 64);
+    r.l0 = load_b128(lo, off);
+    r.l1 = load_b128(lo, off + 64);
+    return r;
+}
+
 __device__ inline TileRows rows_global(const uint16_t* __restrict__ plane, int64_t plane_stride, int gq) {
     TileRows r;
     r.h0 = *reinterpret_cast<const u32x4*>(plane + 8 * gq);
@@ -391,17 +403,17 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
     }
 
     UpperQ<uint16_t> qf[WPW];
-    int64_t tw[WPW];
+    int tw[WPW];   // positions of the wavefront's walks (wave-uniform; positions fit 31 bits)
 #pragma unroll
     for (int w = 0; w < WPW; ++w) {
         const int64_t ti = grp * WPW + w;
-        tw[w] = t0 + ti;
+        tw[w] = __builtin_amdgcn_readfirstlane((int)(t0 + ti));
         const bool ok = ti < NT && n < G.GQ;
         const uint16_t* qrow = q + ((qrow0 + (ti < NT ? ti : 0)) * G.Hq + (int64_t)kvh * G.GQ + n) * kD;
         qf[w].load(qrow, ok, gq);
     }
     const int64_t my_ti = grp * WPW + wl;
-    const int64_t my_t = t0 + my_ti;
+    const int my_t = (int)(t0 + my_ti);
     const bool my_ok = my_ti < NT;
 
     uint32_t surv_low = 0;     // sorted key low word in slots < K: the survivors
@@ -416,8 +428,7 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
             const uint32_t lowk = (uint32_t)shfl_i((int)surv_low, dslot_lane<SLOTS>(wl, ml >> 1));
             const int pnode = key_node(lowk);
             const int child = 2 * pnode + (ml & 1);
-            const bool ok = ml < 2 * K && pnode >= 0 && child < sg.M(l) &&
-                            child <= (int)(my_t >> (kLog2C + l - 1));
+            const bool ok = (ml < 2 * K) & (pnode >= 0) & (child < sg.M(l)) & (child <= (my_t >> (kLog2C + l - 1)));
             cand = ok ? child : -1;
             const int src = dslot_lane<SLOTS>(wl, key_slot(lowk));
             const float pa = shfl_f(Pa, src), pb = shfl_f(Pb, src);
@@ -436,6 +447,11 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
             const int Mc = sg.M(lc);
             const int64_t row_l = bh_row0 + G.off[l] + sg.shift(l);
             const int64_t row_lc = bh_row0 + G.off[lc] + sg.shift(lc);
+            const uint32_t lvl_bytes = (uint32_t)sg.M(l) * (kD * 2);
+            // children <= tl[w] are eligible for walk w
+            int tl[WPW];
+#pragma unroll
+            for (int w = 0; w < WPW; ++w) tl[w] = tw[w] >> shc;
             // candidate of MFMA column n of tile i (lane 16i + n)
             auto row_cand = [&](int i) -> int { return shfl_i(cand, 16 * i + n); };
             // (1) P of the candidates of walks that were not scored at the level above:
@@ -443,12 +459,13 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
             const uint32_t need_p = scored & ~pk;
             if (need_p) {
                 const bool s_lds = l == U.s_level;
+                const buf_rsrc_t shi = make_rsrc(splanes + row_l * kD, lvl_bytes);
+                const buf_rsrc_t slo = make_rsrc(splanes + plane_stride + row_l * kD, lvl_bytes);
 #pragma unroll
                 for (int i = 0; i < NTILE; ++i) {
                     const int c = row_cand(i);
                     const int cc = (c >= 0) ? c : 0;
-                    const TileRows r = s_lds ? rows_lds(lds, U.s_first + cc, gq)
-                                             : rows_global(splanes + (row_l + cc) * kD, plane_stride, gq);
+                    const TileRows r = s_lds ? rows_lds(lds, U.s_first + cc, gq) : rows_buffer(shi, slo, cc, gq);
                     const f32x4 acc = summary_tile_mfma(qf[i / TPW].k0, qf[i / TPW].k1, r.h0, r.h1, r.l0, r.l1);
                     const float ps = tile_head_sums(acc, gq, G.GQ);
                     if (u == i && ((need_p >> wl) & 1)) P = ps;
@@ -457,17 +474,18 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
             // (2) the delta tiles, the next tile's row in flight
             const bool in_lds = l >= U.j_lo && l <= U.j_hi;
             const int lds_lvl = in_lds ? U.lds_first[l] : 0;
-            const uint16_t* dplane_lvl = dplanes + row_l * kD;
+            const buf_rsrc_t dhi = make_rsrc(dplanes + row_l * kD, lvl_bytes);
+            const buf_rsrc_t dlo = make_rsrc(dplanes + plane_stride + row_l * kD, lvl_bytes);
             auto pick = [&](int i, int& row) -> uint32_t {
                 const int c = row_cand(i);
                 const int rc = 2 * c + 1;                 // right child
-                const bool rv = c >= 0 && rc < Mc && rc <= (int)(tw[i / TPW] >> shc);
+                const bool rv = (c >= 0) & (rc < Mc) & (rc <= tl[i / TPW]);
                 row = (c >= 0) ? c : 0;
                 return (uint32_t)ballot(rv);              // bit n: column n has an eligible right child
             };
             auto fetch = [&](int row) -> TileRows {
                 if (in_lds) return rows_lds(lds, lds_lvl + row, gq);
-                return rows_global(dplane_lvl + (int64_t)row * kD, plane_stride, gq);
+                return rows_buffer(dhi, dlo, row, gq);
             };
             float F = 0.0f, D = 0.0f;
             int row0;
@@ -499,7 +517,7 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
             // read directly when a walk has it as a candidate with an eligible right child
             const int crag = sg.M(l) - 1, brag = 2 * crag + 1;
             if (brag < Mc && covered(lc, brag, sg.N) < span_of(lc)) {
-                const bool is_rag = cand == crag && brag <= (int)(my_t >> shc);
+                const bool is_rag = cand == crag && brag <= (my_t >> shc);
                 const uint64_t rm = ballot(is_rag);
 #pragma unroll
                 for (int w = 0; w < WPW; ++w) {
@@ -520,12 +538,24 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
             }
         }
         pk = scored;
-        // walks with at most K candidates keep them all whatever their scores
-        const uint64_t key = slot_key((cand >= 0) ? score : -INFINITY, cand, ml);
-        // the survivors are the K best as a set; with 2K = SLOTS a partial network finds them
-        const uint64_t sorted = (2 * K == SLOTS) ? bitonic_top_half<SLOTS, SegmentLanes>(key, ml)
-                                                 : bitonic_desc<SLOTS, SegmentLanes>(key, ml);
-        surv_low = (ml < K) ? (uint32_t)sorted : 0u;
+        if (scored) {
+            // walks with at most K candidates keep them all whatever their scores
+            const uint64_t key = slot_key((cand >= 0) ? score : -INFINITY, cand, ml);
+            // the survivors are the K best as a set; with 2K = SLOTS a partial network finds them
+            const uint64_t sorted = (2 * K == SLOTS) ? bitonic_top_half<SLOTS, SegmentLanes>(key, ml)
+                                                     : bitonic_desc<SLOTS, SegmentLanes>(key, ml);
+            surv_low = (ml < K) ? (uint32_t)sorted : 0u;
+        } else {
+            // no walk of the wavefront has more than K candidates here: all survive. Each walk's
+            // candidates move to its first slots (the survivors are a set: order is free), the
+            // empty slots after them, by one lane permutation instead of the sorting network.
+            const int base = wl * SLOTS;
+            const uint64_t seg = (SLOTS == 64) ? ~0ull : (((1ull << SLOTS) - 1ull) << base);
+            const int below_c = lanes_below(vm & seg), below_e = lanes_below(~vm & seg);
+            const int dst = base + ((cand >= 0) ? below_c : __popcll(vm & seg) + below_e);
+            const uint32_t moved = (uint32_t)push_to_lane(dst, (int)(uint32_t)slot_key(0.0f, cand, ml));
+            surv_low = (ml < K) ? moved : 0u;
+        }
     }
     // leaf candidates: children of the level-2 survivors (or the root if it is a leaf)
     int leaf;
@@ -535,7 +565,7 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
         const uint32_t lowk = (uint32_t)shfl_i((int)surv_low, dslot_lane<SLOTS>(wl, ml >> 1));
         const int pnode = key_node(lowk);
         const int child = 2 * pnode + (ml & 1);
-        const bool ok = ml < 2 * K && pnode >= 0 && child < sg.M(1) && child <= (int)(my_t >> kLog2C);
+        const bool ok = (ml < 2 * K) & (pnode >= 0) & (child < sg.M(1)) & (child <= (my_t >> kLog2C));
         leaf = ok ? child : -1;
     }
     // ascending order, -1 last
