@@ -93,6 +93,7 @@ MFMA_BF16_PEAK = 2.5e15
 LEAF_SOURCES = ["cluster.hip", "walk_math.h", "lanes.h", "pisa_device.h"]
 UPPER_SOURCES = ["upper.hip", "walk_math.h", "lanes.h", "pisa_device.h"]
 ATTN_SOURCES = ["attention.hip", "walk_math.h", "lanes.h", "pisa_device.h"]
+FLAT_SOURCES = ["flat.hip", "walk_math.h", "lanes.h", "pisa_device.h"]
 COPY_BYTES = 256 << 20          # the calibration copy: 256 MiB read + 256 MiB written
 
 
@@ -140,6 +141,12 @@ def write_traffic(fetch_dir: str, write_dir: str, workload: str = "long256k") ->
             "fetch_kib": f_kib, "write_kib": w_kib,
             "bytes_per_launch": f_kib * 1024 * fs + w_kib * 1024 * wsc,
             "source_hash": _hash_sources(srcs)}
+    if any("flat_select_kernel" in k for k in fetch):
+        f_kib, w_kib = find(fetch, "flat_select_kernel"), find(write, "flat_select_kernel")
+        out[f"flat_select_kernel:{workload}"] = {
+            "fetch_kib": f_kib, "write_kib": w_kib,
+            "bytes_per_launch": f_kib * 1024 * fs + w_kib * 1024 * wsc,
+            "source_hash": _hash_sources(FLAT_SOURCES)}
     if any("sparse_attention_kernel" in k for k in fetch):
         f_kib, w_kib = find(fetch, "sparse_attention_kernel"), find(write, "sparse_attention_kernel")
         out[f"sparse_attention_kernel:{workload}"] = {
@@ -610,11 +617,27 @@ def main():
             log(f"K={kk}: {tot_k / 10:.3f} ms/step (upper walk {up_k.mean():.3f} ms, leaf scoring {lf_k.mean():.3f} ms)")
             del out_k, ws_k
         result["topk_sweep"] = ksweep
-        # the flat stage-one selection at the headline length, beside the pyramid walk
-        ftot, fsel, out_flat = time_flat(N, dims, q, k, pyr, 10, 3)
-        flat = {args.workload: {"N": N, "pyramid_step_ms": ms_per_step, "flat_step_ms": ftot,
-                                "flat_select_ms": fsel, "pyramid_over_flat": ms_per_step / ftot}}
-        del out_flat
+    # the flat stage-one selection (every leaf summary scored) at the headline length, beside
+    # the pyramid walk: a dense contraction (one dot product of the group-summed query with each
+    # eligible leaf mean) feeding a streaming top K
+    ftot, fsel, out_flat = time_flat(N, dims, q, k, pyr, 10, 3)
+    del out_flat
+    n_scores = float(np.minimum(np.arange(N) // wl.C + 1, -(-N // wl.C)).sum()) * wl.B * wl.Hkv
+    flat_flops = n_scores * wl.d * 2
+    traffic_flat = measured_traffic(f"flat_select_kernel:{wl.name}", _hash_sources(FLAT_SOURCES))
+    flat = {args.workload: {"N": N, "pyramid_step_ms": ms_per_step, "flat_step_ms": ftot,
+                            "flat_select_ms": fsel, "pyramid_over_flat": ms_per_step / ftot,
+                            "roofline": {"kernel": "flat_select_kernel (+ flat_planes_kernel)", "bound": "mfma",
+                                         "achieved": flat_flops / (fsel / 1e3) / 1e12, "peak": MFMA_BF16_PEAK / 1e12,
+                                         "unit": "TFLOP/s", "frac": flat_flops / (fsel / 1e3) / MFMA_BF16_PEAK,
+                                         "traffic": traffic_flat, "algorithmic_per_launch": flat_flops,
+                                         "scores_per_launch": n_scores,
+                                         "algorithmic_model": "one 64-dim dot product per (position, KV head, "
+                                                              "eligible leaf); the kernel issues three bf16 products "
+                                                              "per dot product (hi/lo split)"}}}
+    log(f"flat stage-one selection at N={N}: {ftot:.3f} ms per step ({fsel:.3f} ms selection), pyramid walk "
+        f"{ms_per_step:.3f} ms")
+    result["flat"] = flat
     del q, k, pyr, out, ws
 
     if not args.no_extras:
@@ -635,7 +658,6 @@ def main():
                           "flat_select_ms": fsel, "pyramid_over_flat": (tot2 / 10) / ftot}
             del q2, k2, p2, o2, ws2
         result["sweep"] = sweep
-        result["flat"] = flat
         log("flat stage-one selection beside the pyramid walk (ms per step, build included): " +
             ", ".join(f"N={v['N']}: {v['flat_step_ms']:.3f} vs {v['pyramid_step_ms']:.3f}" for v in flat.values()))
         result["planted"] = planted_bench(torch, ops, synth, setup, time_steps, log)

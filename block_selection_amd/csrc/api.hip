@@ -915,7 +915,7 @@ int pisa_select_flat(const void* q, const float* pyramid, int64_t N, int64_t n_c
     if (!q || !pyramid || !out_idx) return PISA_ERR_INVALID_ARG;
     Geom G;
     if ((rc = make_geom(dims, N, n_capacity, &G)) != PISA_OK) return rc;
-    const int64_t waves = (int64_t)dims->B * dims->Hkv * G.M[1];   // one per 64 positions
+    const int64_t waves = (int64_t)dims->B * dims->Hkv * ((N + 31) / 32);   // one per 32 positions
     if (waves > INT_MAX) return PISA_ERR_UNSUPPORTED;
     if (!workspace || ws_bytes < flat_ws(dims, N)) return PISA_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;

@@ -14,10 +14,10 @@
 // Layout and arithmetic:
 //   * flat_planes_kernel: the fp32 leaf means (pyramid level 1) as two bf16 planes,
 //     hi = rne(x) and lo = rne(x - hi) (a 17-bit mantissa).
-//   * flat_select_kernel: one wavefront per 64 consecutive positions of one (batch, KV
+//   * flat_select_kernel: one wavefront per 32 consecutive positions of one (batch, KV
 //     head); they share one causal bound (blocks 0 .. T0/64). The summed query rows (fp32
 //     sums of the group's heads, split into hi and lo the same way) are the B operand of
-//     v_mfma_f32_16x16x32_bf16 (4 column tiles of 16 positions), 16 blocks' summary planes
+//     v_mfma_f32_16x16x32_bf16 (2 column tiles of 16 positions), 16 blocks' summary planes
 //     the A operand; hi*hi + hi*lo + lo*hi over two k-steps give fp32 scores within about
 //     2^-16 of the exact product. Lane (gq, n) of column tile c receives blocks
 //     16 bt + 4 gq + r (r < 4) of position T0 + 16 c + n.
@@ -80,7 +80,9 @@ __device__ inline void split_hi_lo8(const float s[8], bf16x8& hi, bf16x8& lo) {
     lo = __builtin_bit_cast(bf16x8, l);
 }
 
-constexpr int kFlatCols = 4;                 // column tiles of 16 positions per wavefront
+// Column tiles of 16 positions per wavefront: 2 (32 positions) measured fastest at 256K keys
+// on an MI355X (64 positions: fewer waves fit a CU; 16: each summary tile serves too few).
+constexpr int kFlatCols = 2;
 constexpr int kFlatPositions = 16 * kFlatCols;
 
 // Cut the lists of the positions in `mask` (bit p: position p of the wavefront) back to their
@@ -106,8 +108,8 @@ __device__ inline void flat_compact(uint64_t mask, uint64_t* s_buf, uint32_t* s_
     }
 }
 
-// One wavefront per workgroup: positions T0 .. T0 + 63 of (batch, KV head) bh, where the
-// workgroups of the longest causal spans run first.
+// One wavefront per workgroup: positions T0 .. T0 + kFlatPositions - 1 of (batch, KV head) bh,
+// where the workgroups of the longest causal spans run first.
 template <typename KT, int CAP>
 __global__ __launch_bounds__(64) void flat_select_kernel(const KT* __restrict__ q,
                                                          const uint16_t* __restrict__ planes, Geom G,
@@ -120,15 +122,16 @@ __global__ __launch_bounds__(64) void flat_select_kernel(const KT* __restrict__ 
     const int BH = G.B * G.Hkv;
     const int64_t M1 = G.M[1];
     const int bh = (int)(blockIdx.x % BH);
-    const int64_t grp = M1 - 1 - (int64_t)(blockIdx.x / BH);
+    const int64_t ngrp = (G.N + kFlatPositions - 1) / kFlatPositions;
+    const int64_t grp = ngrp - 1 - (int64_t)(blockIdx.x / BH);
     const int b = bh / G.Hkv, kvh = bh % G.Hkv;
     const int K = G.topk;
     const int64_t T0 = grp * kFlatPositions;
-    const int64_t n_elig = grp + 1;          // blocks 0 .. T0/64, the same for all 64 positions
+    const int64_t n_elig = (T0 >> 6) + 1;    // blocks 0 .. T0/64, the same for all the wavefront's positions
     const int64_t plane_stride = (int64_t)BH * M1 * kD;
     const uint16_t* pl = planes + (int64_t)bh * M1 * kD;
 
-    // B operand: the group-summed query rows of the wavefront's 64 positions, hi and lo
+    // B operand: the group-summed query rows of the wavefront's positions, hi and lo
     bf16x8 qh[kFlatCols][2], ql[kFlatCols][2];
 #pragma unroll
     for (int c = 0; c < kFlatCols; ++c) {
@@ -145,22 +148,27 @@ __global__ __launch_bounds__(64) void flat_select_kernel(const KT* __restrict__ 
         split_hi_lo8(s0, qh[c][0], ql[c][0]);
         split_hi_lo8(s1, qh[c][1], ql[c][1]);
     }
-    s_cnt[lane] = 0u;
-    s_thr[lane] = -INFINITY;
+    if (lane < kFlatPositions) {
+        s_cnt[lane] = 0u;
+        s_thr[lane] = -INFINITY;
+    }
+    // each position's threshold in units of the raw product (8 x the score; the 1/8 scale is
+    // exact, so comparing products is comparing scores)
     float thr[kFlatCols];
 #pragma unroll
     for (int c = 0; c < kFlatCols; ++c) thr[c] = -INFINITY;
     __syncthreads();
 
-    // A operand of block tile bt: row 16 bt + n (clamped to a valid row past the bound)
+    // A operand of block tile bt: row 16 bt + n; rows past the causal bound lie outside the
+    // buffer range (read as zero) and are masked in the last tile
+    const uint32_t range = (uint32_t)(n_elig * kD * 2);
+    const buf_rsrc_t ahi = make_rsrc(pl, range), alo = make_rsrc(pl + plane_stride, range);
     auto load_a = [&](int64_t bt, u32x4 (&a)[4]) {
-        int64_t r = bt * 16 + n;
-        r = (r < n_elig) ? r : 0;
-        const uint16_t* src = pl + r * kD;
-        a[0] = *reinterpret_cast<const u32x4*>(src + 8 * gq);
-        a[1] = *reinterpret_cast<const u32x4*>(src + 32 + 8 * gq);
-        a[2] = *reinterpret_cast<const u32x4*>(src + plane_stride + 8 * gq);
-        a[3] = *reinterpret_cast<const u32x4*>(src + plane_stride + 32 + 8 * gq);
+        const uint32_t off = ((uint32_t)(bt * 16 + n) << 7) + ((uint32_t)gq << 4);
+        a[0] = load_b128(ahi, off);
+        a[1] = load_b128(ahi, off + 64);
+        a[2] = load_b128(alo, off);
+        a[3] = load_b128(alo, off + 64);
     };
     const int64_t nbt = (n_elig + 15) / 16;
     u32x4 a_cur[4], a_nxt[4];
@@ -169,34 +177,36 @@ __global__ __launch_bounds__(64) void flat_select_kernel(const KT* __restrict__ 
         if (bt + 1 < nbt) load_a(bt + 1, a_nxt);
         const bf16x8 ah0 = __builtin_bit_cast(bf16x8, a_cur[0]), ah1 = __builtin_bit_cast(bf16x8, a_cur[1]);
         const bf16x8 al0 = __builtin_bit_cast(bf16x8, a_cur[2]), al1 = __builtin_bit_cast(bf16x8, a_cur[3]);
-        float sc[kFlatCols][4];
-        bool any = false;
         const int64_t blk0 = bt * 16 + 4 * gq;
+        const bool last = bt + 1 == nbt;     // wave-uniform: the only tile that can hold blocks past the bound
+        f32x4 acc[kFlatCols];
+        bool any = false;
 #pragma unroll
         for (int c = 0; c < kFlatCols; ++c) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah0, qh[c][0], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah1, qh[c][1], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah0, ql[c][0], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah1, ql[c][1], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al0, qh[c][0], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al1, qh[c][1], acc, 0, 0, 0);
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
+            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah0, qh[c][0], a, 0, 0, 0);
+            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah1, qh[c][1], a, 0, 0, 0);
+            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah0, ql[c][0], a, 0, 0, 0);
+            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah1, ql[c][1], a, 0, 0, 0);
+            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al0, qh[c][0], a, 0, 0, 0);
+            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al1, qh[c][1], a, 0, 0, 0);
+            if (last) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                sc[c][r] = (blk0 + r < n_elig) ? acc[r] * 0.125f : -INFINITY;
-                any = any || (blk0 + r < n_elig && sc[c][r] >= thr[c]);
+                for (int r = 0; r < 4; ++r) a[r] = (blk0 + r < n_elig) ? a[r] : -INFINITY;
             }
+            acc[c] = a;
+            any = any || fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])) >= thr[c];
         }
         if (ballot(any)) {
-            // append every score at or above its position's threshold
+            // append every eligible score at or above its position's threshold
 #pragma unroll
             for (int c = 0; c < kFlatCols; ++c) {
                 const int p = 16 * c + n;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    if (blk0 + r < n_elig && sc[c][r] >= thr[c]) {
+                    if (acc[c][r] >= thr[c] && acc[c][r] > -INFINITY) {
                         const uint32_t i = atomicAdd(&s_cnt[p], 1u);
-                        s_buf[p * CAP + i] = select_key(sc[c][r], (int)(blk0 + r));
+                        s_buf[p * CAP + i] = select_key(acc[c][r] * 0.125f, (int)(blk0 + r));
                     }
                 }
             }
@@ -212,7 +222,7 @@ __global__ __launch_bounds__(64) void flat_select_kernel(const KT* __restrict__ 
                 flat_compact<CAP>(mask, s_buf, s_cnt, s_thr, K);
                 __syncthreads();
 #pragma unroll
-                for (int c = 0; c < kFlatCols; ++c) thr[c] = s_thr[16 * c + n];
+                for (int c = 0; c < kFlatCols; ++c) thr[c] = 8.0f * s_thr[16 * c + n];
             }
         }
 #pragma unroll
