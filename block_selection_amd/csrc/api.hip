@@ -6,6 +6,7 @@
 #include <limits.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "pisa.h"
@@ -19,7 +20,8 @@ __global__ void build_upper_kernel(Geom, Pack, float*);
 template <typename KT>
 __global__ void decode_refresh_kernel(const KT*, KT*, Geom, float*);
 template <int S>
-__global__ void decode_step_kernel(const uint16_t*, const uint16_t*, uint16_t*, float*, Geom, uint32_t*, float*,
+__global__ void decode_step_kernel(const uint16_t*, const uint16_t*, uint16_t*, float*, Geom, unsigned long long*,
+                                   uint32_t, float*,
                                    int32_t*);
 __global__ void split_planes_kernel(const float*, uint16_t*, int64_t);
 template <int SLOTS, int S>
@@ -49,7 +51,7 @@ __global__ void vt_tiles_kernel(const uint16_t*, Geom, Pack, int64_t, uint16_t*)
 __global__ void sparse_attention_kernel(const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*, Geom,
                                         Pack, int64_t, float*);
 __global__ void decode_attention_kernel(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, const int32_t*,
-                                        Geom, int64_t, uint32_t*, float*, float*);
+                                        Geom, int64_t, unsigned long long*, uint32_t, float*, float*);
 __global__ void flat_planes_kernel(const float*, Geom, uint16_t*);
 template <typename KT, int CAP>
 __global__ void flat_select_kernel(const KT*, const uint16_t*, Geom, int32_t*);
@@ -95,6 +97,15 @@ template <int SLOTS>
 __global__ void final_topk_kernel(const int32_t*, const int32_t*, const float*, Geom, int64_t, int32_t*);
 
 constexpr size_t kAlign = 256;
+
+// Tags of the split launches' completion counters: process-wide, distinct for every call
+// (until 2^32 - 1 calls have been made), never 0.
+static std::atomic<uint32_t> g_call_tag{0};
+static uint32_t next_call_tag() {
+    uint32_t t = g_call_tag.fetch_add(1u, std::memory_order_relaxed) + 1u;
+    while (t == 0u) t = g_call_tag.fetch_add(1u, std::memory_order_relaxed) + 1u;
+    return t;
+}
 // The bucket pass counts one sequence's (KV head, superblock) groups in an LDS histogram of
 // this many bins (64 KiB): bf16 selection needs Hkv * ceil(N / 1024) <= kMaxClusterGroups.
 constexpr int64_t kMaxClusterGroups = 16384;
@@ -131,7 +142,7 @@ struct Workspace {
     uint32_t* meta;      // [0] items, [1] entries
     int64_t* cbase;      // [D + 1] first count of each document's block (packs only)
     // fused bf16 decoding step
-    uint32_t* done;      // [B*Hkv] completion counters (zero between steps)
+    unsigned long long* done;   // [B*Hkv] tagged completion counters (any contents)
     float* leaf_score;   // [B*Hkv][64] leaf scores of one step
     ClusterGeom CG;
     bool clustered;
@@ -151,8 +162,7 @@ static Workspace carve(const pisa_dims* d, int64_t N, int64_t P, bool decode, ch
         return p;
     };
     if (decode && d->dtype == PISA_DTYPE_BF16) {
-        // the counters come first so that the zero-once contract covers a fixed prefix
-        w.done = (uint32_t*)take((size_t)d->B * d->Hkv * sizeof(uint32_t));
+        w.done = (unsigned long long*)take((size_t)d->B * d->Hkv * sizeof(unsigned long long));
         w.leaf_score = (float*)take((size_t)d->B * d->Hkv * 64 * sizeof(float));
         w.bytes = off;
         return w;
@@ -629,7 +639,7 @@ int pisa_select_prefill(const void* q, const void* k, const float* pyramid, int6
 // The bf16 decoding step: append, refresh, walk and leaf top-K in one launch, ceil(2K/8)
 // workgroups per (batch, KV head) -- the last one to finish writes the selection -- or one
 // per (batch, KV head) when that would make more than kDecodeSplitMaxWorkgroups. W holds the
-// completion counters (zero before the step, left zero) and the leaf-score rows.
+// tagged completion counters (any contents) and the leaf-score rows.
 static int launch_decode_bf16(const void* q_new, const void* k_new, void* k_cache, float* pyramid, const Geom& G,
                               const pisa_dims* dims, int32_t* out_idx, const Workspace& W, hipStream_t s) {
     const unsigned nbh = (unsigned)(dims->B * dims->Hkv);
@@ -638,8 +648,9 @@ static int launch_decode_bf16(const void* q_new, const void* k_new, void* k_cach
     const uint16_t* qn = (const uint16_t*)q_new;
     const uint16_t* kn = (const uint16_t*)k_new;
     uint16_t* kc = (uint16_t*)k_cache;
+    const uint32_t tag = next_call_tag();
     void* args[] = {(void*)&qn, (void*)&kn, (void*)&kc, (void*)&pyramid, (void*)&G, (void*)&W.done,
-                    (void*)&W.leaf_score, (void*)&out_idx};
+                    (void*)&tag, (void*)&W.leaf_score, (void*)&out_idx};
     if (hipLaunchKernel(decode_step_fn(G.score), dim3(parts, nbh), dim3(kDecodeThreads), args, 0, s) != hipSuccess)
         return PISA_ERR_HIP;
     return launch_status();
@@ -674,7 +685,7 @@ int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cach
 // name is not a device address): the first call on a device takes the array's address
 // there with hipGetSymbolAddress and keeps it per device.
 constexpr int64_t kNoAllocMaxBH = 4096;                                  // batch x KV heads
-constexpr size_t kNoAllocCounterBytes = (size_t)kNoAllocMaxBH * sizeof(uint32_t);
+constexpr size_t kNoAllocCounterBytes = (size_t)kNoAllocMaxBH * sizeof(unsigned long long);
 constexpr size_t kNoAllocBytes = kNoAllocCounterBytes + (size_t)kNoAllocMaxBH * 64 * sizeof(float);
 static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
 
@@ -682,13 +693,10 @@ constexpr int kNoAllocMaxDevices = 64;
 static std::mutex g_scratch_mu;
 static void* g_scratch_ptr[kNoAllocMaxDevices];
 
-__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
-}
-
-// Device address of this device's scratch; at the first call on a device the completion
-// counters are zeroed (a fill kernel on `s`, ordered before the caller's step).
-static int noalloc_scratch(hipStream_t s, char** out) {
+// Device address of this device's scratch, taken at the first call on the device. Nothing
+// in it needs clearing: the completion counters are tagged per call (arrive_last), and the
+// leaf-score rows are written before they are read within a step.
+static int noalloc_scratch(char** out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return PISA_ERR_HIP;
     if (dev < 0 || dev >= kNoAllocMaxDevices) return PISA_ERR_UNSUPPORTED;
@@ -696,9 +704,6 @@ static int noalloc_scratch(hipStream_t s, char** out) {
     if (!g_scratch_ptr[dev]) {
         void* ptr = nullptr;
         if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PISA_ERR_HIP;
-        hipLaunchKernelGGL(zero_words_kernel, dim3(16), dim3(256), 0, s, (uint32_t*)ptr,
-                           (int64_t)(kNoAllocCounterBytes / sizeof(uint32_t)));
-        if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
         g_scratch_ptr[dev] = ptr;
     }
     *out = (char*)g_scratch_ptr[dev];
@@ -718,7 +723,7 @@ int pisa_decode_update_select_noalloc(const void* q_new, const void* k_new, void
     if ((rc = make_geom(dims, n_before + 1, n_capacity, &G)) != PISA_OK) return rc;
     hipStream_t s = (hipStream_t)stream;
     char* base = nullptr;
-    if ((rc = noalloc_scratch(s, &base)) != PISA_OK) return rc;
+    if ((rc = noalloc_scratch(&base)) != PISA_OK) return rc;
     const Workspace W = carve(dims, 1, G.P, true, base);
     if (W.bytes > kNoAllocBytes) return PISA_ERR_WORKSPACE;
     return launch_decode_bf16(q_new, k_new, k_cache, pyramid, G, dims, out_idx, W, s);
@@ -829,12 +834,12 @@ int pisa_select_prefill_packed(const void* q, const void* k, const float* pyrami
                             (hipStream_t)stream, nullptr);
 }
 
-// Decoding-step attention workspace: one completion counter per (batch, KV head) (zero
-// before the first call, left zero by every call), then the partial states.
+// Decoding-step attention workspace: one tagged completion counter per (batch, KV head)
+// (any contents), then the partial states.
 static size_t decode_attention_ws(const pisa_dims* d, size_t* counters) {
     const int64_t bh = (int64_t)d->B * d->Hkv;
     const int64_t parts = (d->topk + kDecAttnBlocksPerGroup - 1) / kDecAttnBlocksPerGroup;
-    const size_t c = align_up((size_t)bh * sizeof(uint32_t));
+    const size_t c = align_up((size_t)bh * sizeof(unsigned long long));
     if (counters) *counters = c;
     return c + align_up((size_t)bh * parts * kDecAttnStateFloats * sizeof(float));
 }
@@ -860,11 +865,11 @@ int pisa_decode_attention(const void* q_new, const void* v_new, const void* k_ca
     // kDecodeSplitMaxWorkgroups
     unsigned parts = (unsigned)((dims->topk + kDecAttnBlocksPerGroup - 1) / kDecAttnBlocksPerGroup);
     if ((int64_t)parts * dims->B * dims->Hkv > kDecodeSplitMaxWorkgroups) parts = 1u;
-    uint32_t* done = (uint32_t*)workspace;
+    unsigned long long* done = (unsigned long long*)workspace;
     float* states = (float*)((char*)workspace + cbytes);
     hipLaunchKernelGGL(decode_attention_kernel, dim3(parts, (unsigned)(dims->B * dims->Hkv)),
                        dim3(64 * kDecAttnBlocksPerGroup), 0, (hipStream_t)stream, (const uint16_t*)q_new,
-                       (const uint16_t*)v_new, (const uint16_t*)k_cache, (uint16_t*)v_cache, idx, G, t, done, states,
+                       (const uint16_t*)v_new, (const uint16_t*)k_cache, (uint16_t*)v_cache, idx, G, t, done, next_call_tag(), states,
                        out);
     return launch_status();
 }

@@ -312,12 +312,12 @@ __device__ inline void merge_states(P part, int n, int h, int e, float& o0, floa
 
 // Grid: (ceil(K / 4) or 1, B * Hkv). v_new (may be null): the new token's value row per (batch,
 // KV head): key t's value is taken from it, and workgroup 0 writes it to row t of v.
-// done: one counter per (batch, KV head), zero before the call and left zero; parts:
+// done: one tagged completion counter per (batch, KV head), any contents (arrive_last); parts:
 // [B * Hkv][gridDim.x][kDecPartFloats].
 __global__ __launch_bounds__(64 * kDecAttnWaves) void decode_attention_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ v_new, const uint16_t* __restrict__ k,
-    uint16_t* __restrict__ v, const int32_t* __restrict__ idx, Geom G, int64_t t, uint32_t* __restrict__ done,
-    float* __restrict__ parts, float* __restrict__ out) {
+    uint16_t* __restrict__ v, const int32_t* __restrict__ idx, Geom G, int64_t t, unsigned long long* __restrict__ done,
+    uint32_t tag, float* __restrict__ parts, float* __restrict__ out) {
     __shared__ uint16_t s_vt[kDecAttnWaves][kD * kC];       // 8 KiB per wavefront
     __shared__ float s_part[kDecAttnWaves][kDecPartFloats];
     __shared__ int s_last;
@@ -500,7 +500,7 @@ __global__ __launch_bounds__(64 * kDecAttnWaves) void decode_attention_kernel(
     }
     __threadfence();   // the state visible device-wide before this workgroup counts itself done
     __syncthreads();
-    if (threadIdx.x == 0) s_last = (atomicAdd(&done[bh], 1u) == (uint32_t)(nparts - 1));
+    if (threadIdx.x == 0) s_last = arrive_last(&done[bh], tag, (uint32_t)nparts);
     __syncthreads();
     if (!s_last) return;
     __threadfence();   // acquire: the other workgroups' states
@@ -515,7 +515,7 @@ __global__ __launch_bounds__(64 * kDecAttnWaves) void decode_attention_kernel(
             orow[1] = o1;
         }
     }
-    if (threadIdx.x == 0) done[bh] = 0u;   // ready for the next call
+    if (threadIdx.x == 0) done[bh] = 0ull;   // no tag: a replay of this launch starts afresh
 }
 
 }  // namespace pisa

@@ -67,7 +67,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
                                                                      const uint16_t* __restrict__ k_new,
                                                                      uint16_t* __restrict__ k_cache,
                                                                      float* __restrict__ pyr, Geom G,
-                                                                     uint32_t* __restrict__ done,
+                                                                     unsigned long long* __restrict__ done,
+                                                                     uint32_t tag,
                                                                      float* __restrict__ leaf_score,
                                                                      int32_t* __restrict__ out) {
     __shared__ float s_F[2][64], s_D[2][64], s_P[2][64], s_fix[2][4];
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
         if (nparts > 1) {
             __threadfence();   // scores visible device-wide before this workgroup counts itself done
             __syncthreads();
-            if (threadIdx.x == 0) s_last = (atomicAdd(&done[bh], 1u) == (uint32_t)(nparts - 1));
+            if (threadIdx.x == 0) s_last = arrive_last(&done[bh], tag, (uint32_t)nparts);
             __syncthreads();
             if (!s_last) return;
             __threadfence();   // acquire: the other workgroups' scores
@@ -264,13 +265,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
         const int nd = (2 * K == 64) ? select_top_half<64>(my, lidx, lane) : select_sort<64>(my, lidx, lane);
         const int keep = index_sort<64>((lane < K) ? nd : INT_MAX, lane);   // ascending, INT_MAX last
         if (lane < K) out[(int64_t)bh * K + lane] = (keep != INT_MAX) ? keep : -1;
-        if (scored && lane == 0) done[bh] = 0u;   // ready for the next step
+        if (scored && lane == 0) done[bh] = 0ull;   // no tag: a replay of this launch starts afresh
     }
 }
 
 #define PISA_DECODE_INST(S)                                                                              \
     template __global__ void decode_step_kernel<S>(const uint16_t*, const uint16_t*, uint16_t*, float*, Geom, \
-                                                   uint32_t*, float*, int32_t*);
+                                                   unsigned long long*, uint32_t, float*, int32_t*);
 PISA_DECODE_INST(kScoreLse)
 PISA_DECODE_INST(kScoreMean)
 PISA_DECODE_INST(kScoreMeanHalfVar)

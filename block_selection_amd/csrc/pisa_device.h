@@ -259,6 +259,23 @@ __device__ inline int readlane_i(int v, int lane) { return __builtin_amdgcn_read
 
 __device__ inline uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
+// Completion counter of a split launch: one 64-bit word per (batch, KV head), the call's tag
+// (never 0, unique per call) in the high half and the number of its workgroups that have
+// finished in the low half. A workgroup arriving at a word whose tag is another call's
+// discards the count it finds (stale, from another call, or stray data) and starts from
+// zero, so the workgroup that sees `nparts` arrivals is this call's last whatever the word
+// held before. One thread per workgroup calls this, after a device-scope fence.
+__device__ inline bool arrive_last(unsigned long long* word, uint32_t tag, uint32_t nparts) {
+    unsigned long long old = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+        const uint32_t cnt = ((uint32_t)(old >> 32) == tag) ? (uint32_t)old : 0u;
+        const unsigned long long nv = ((unsigned long long)tag << 32) | (unsigned long long)(cnt + 1u);
+        const unsigned long long seen = atomicCAS(word, old, nv);
+        if (seen == old) return cnt + 1u == nparts;
+        old = seen;   // another workgroup arrived first: retry against what it wrote
+    }
+}
+
 // Number of set bits of m below this lane.
 __device__ inline int lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));

@@ -167,7 +167,7 @@ def alloc_pyramid(dims: Dims, n_capacity: int, device="cuda") -> torch.Tensor:
 def alloc_workspace(dims: Dims, N: int, n_capacity: Optional[int] = None, is_decode: bool = False,
                     device="cuda") -> Optional[torch.Tensor]:
     n = workspace_bytes(dims, N, n_capacity, is_decode)
-    # zero-filled: a decode workspace starts with completion counters that must be zero
+    # zero-filled, though nothing requires it: a decode workspace's completion counters are tagged per call
     return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
 
 
@@ -363,7 +363,7 @@ def decode_attention_workspace_bytes(dims: Dims) -> int:
 
 
 def alloc_decode_attention_workspace(dims: Dims, device="cuda") -> torch.Tensor:
-    # zero-filled: it starts with completion counters that must be zero
+    # zero-filled, though nothing requires it: its completion counters are tagged per call
     return torch.zeros(decode_attention_workspace_bytes(dims), dtype=torch.uint8, device=device)
 
 

@@ -105,10 +105,13 @@ size_t pisa_pyramid_bytes(const pisa_dims* dims, int64_t n_capacity);
  * Prefill: scratch between the kernels of one call; its contents need not be
  * initialised and are meaningless after the call.
  * Decode with bf16 inputs: the workspace starts with one completion counter
- * per (batch, KV head) (4 * B * Hkv bytes) that must be zero before the first
- * step (e.g. allocate it zero-filled); every step leaves the counters at zero
- * again. Do not share a decode workspace with prefill calls, or zero it again
- * before the next step. */
+ * per (batch, KV head) (8 * B * Hkv bytes), then one row of leaf scores per
+ * (batch, KV head). Its contents need no initialisation: each counter carries
+ * a tag that is distinct for every call (the library hands them out), and a
+ * count left by another call, by a prefill call sharing the buffer or by stray
+ * data is discarded. (Stray data equal to the call's own tag in the high half
+ * of a counter, a 1-in-2^32 coincidence, is the only exception; zero-filled
+ * memory never matches.) Steps sharing one workspace must be enqueued in order. */
 size_t pisa_workspace_bytes(const pisa_dims* dims, int64_t N, int64_t n_capacity, int32_t is_decode);
 
 /*
@@ -181,10 +184,10 @@ int pisa_decode_update_select(const void* q_new, const void* k_new, void* k_cach
  * For callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation): pisa_decode_update_select for bf16
  * inputs without a workspace argument. Its completion counters and leaf-score rows live in
- * a static device array of the library (1,064,960 bytes per GPU, held until the process
- * ends), whose address is taken once per device at the first call there (that call also
- * enqueues one small kernel on `stream` that zeroes the counters; every step leaves them
- * zero again). It allocates nothing and calls no allocating routine.
+ * a static device array of the library (1,081,344 bytes per GPU, held until the process
+ * ends), whose address is taken once per device at the first call there; nothing in it
+ * needs clearing (the counters are tagged per call, as in pisa_workspace_bytes). It
+ * allocates nothing, launches nothing but the step, and calls no allocating routine.
  * Limits and errors: B * Hkv <= 4096 (else PISA_ERR_WORKSPACE); fp32 inputs return
  * PISA_ERR_UNSUPPORTED; otherwise as pisa_decode_update_select, whose selection and
  * refreshed pyramid it reproduces bit for bit.
@@ -280,9 +283,9 @@ int pisa_select_prefill_packed(const void* q, const void* k, const float* pyrami
                                size_t ws_bytes, void* stream);
 
 /* Device workspace of pisa_decode_attention (0 on bad input): one completion counter per
- * (batch, KV head), 4 * B * Hkv bytes at its start, that must be zero before the first call
- * (e.g. allocate it zero-filled; every call leaves them zero again), then the partial
- * softmax states of the call. Calls sharing one workspace must be enqueued in order. */
+ * (batch, KV head), 8 * B * Hkv bytes at its start, then the partial softmax states of the
+ * call. Its contents need no initialisation (tagged counters, as in pisa_workspace_bytes).
+ * Calls sharing one workspace must be enqueued in order. */
 size_t pisa_decode_attention_workspace_bytes(const pisa_dims* dims);
 
 /*

@@ -34,7 +34,9 @@ def test_geometry_helpers():
     assert ops.pyramid_bytes(d, 262144) == 2 * 8191 * 64 * 4
     assert ops.pyramid_nodes(d, 1) == 1
     assert ops.workspace_bytes(d, 4096) > 0
-    assert ops.workspace_bytes(d, 1, 131328, is_decode=True) > 0
+    # bf16 decode: 8-byte tagged counters per (batch, KV head), 256-byte aligned, then 64 leaf scores each
+    assert ops.workspace_bytes(d, 1, 131328, is_decode=True) == 256 + 2 * 64 * 4
+    assert ops.workspace_bytes(ops.make_dims(40, 32, 2, 8), 1, 4096, is_decode=True) == 768 + 80 * 64 * 4
     assert ops.workspace_bytes(d, 5000, 4000) == 0
 
 

@@ -236,3 +236,40 @@ def test_decode_attention_batched(B, K):
     got = out.cpu().numpy()
     for b in range(B):
         _check(got[b][None], oracle.attention(q[b][None], np.array([t]), k[b], v[b], idx[b][None]), v)
+
+
+def test_decode_attention_workspace_needs_no_zeroing():
+    """Tagged completion counters: a decode-attention workspace full of stray bytes, or whose
+    counters hold a foreign tag one arrival short of the last, gives bit for bit the output of
+    a zero-filled one (K = 32: eight workgroups per (batch, KV head) meet at each counter)."""
+    from block_selection_amd import ops
+    B, N, Hq, Hkv, K = 2, 3000, 32, 2, 32
+    rng = np.random.default_rng(33)
+    q = synth.bf16_round(rng.standard_normal((B, Hq, 64), dtype=np.float32))
+    k = synth.bf16_round(rng.standard_normal((B, N, Hkv, 64), dtype=np.float32))
+    v = synth.make_values(B, N, Hkv, seed=33)
+    t = N - 1
+    idx = np.stack([oracle.walk(q[b][None], np.array([t]), k[b], oracle.build_pyramid(k[b]), K)[0][0]
+                    for b in range(B)])
+    dims = ops.make_dims(B, Hq, Hkv, K, "bf16")
+    qd, kd, vd = to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16")
+    idxd = torch.from_numpy(np.ascontiguousarray(idx)).cuda()
+    ws = ops.alloc_decode_attention_workspace(dims)
+    gen = torch.Generator(device="cpu").manual_seed(4)
+    outs = []
+    for poison in (None, "bytes", "one_short", None):
+        if poison == "bytes":
+            ws.copy_(torch.randint(0, 256, (ws.numel(),), dtype=torch.uint8, generator=gen).cuda())
+        elif poison == "one_short":
+            words = torch.randint(1, 1 << 31, (B * Hkv,), dtype=torch.int64, generator=gen)
+            ws[: 8 * B * Hkv].copy_(((words << 32) | 7).view(torch.uint8).cuda())
+        out = torch.empty((B, Hq, 64), dtype=torch.float32, device="cuda")
+        print(f"decode attention workspace poison={poison}", flush=True)
+        ops.decode_attention(qd, None, kd, vd, idxd, t, N, dims, out, ws)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+    got = outs[0]
+    for b in range(B):
+        _check(got[b][None], oracle.attention(q[b][None], np.array([t]), k[b], v[b], idx[b][None]), v)

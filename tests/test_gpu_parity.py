@@ -318,6 +318,51 @@ def test_decode_equals_prefill_at_same_position(topk, score):
     assert checked == 5
 
 
+def test_decode_workspace_needs_no_zeroing():
+    """The decoding step's completion counters are tagged per call, so a workspace holding
+    stray bytes, or counters one arrival short of "last" under a foreign tag, gives bit for bit
+    the selection and pyramid of a zero-filled one (B = 2, K = 16: four workgroups per
+    (batch, KV head) meet at each counter)."""
+    from block_selection_amd import ops
+    B, K, N0, steps = 2, 16, 3000, 6
+    wl = synth.Workload("decode_ws", N=N0, Hq=16, Hkv=2, topk=K, dtype="bf16", B=B, decode_steps=steps, seed=9)
+    inp = synth.make_decode(wl)
+    cap = N0 + steps
+    dims = ops.make_dims(B, 16, 2, K, "bf16")
+    kc_host = np.zeros((B, cap, 2, 64), np.float32)
+    kc_host[:, :N0] = inp.k_ctx
+    k_new, q_new = to_device(inp.k_new, "bf16"), to_device(inp.q_new, "bf16")
+    nbytes = ops.workspace_bytes(dims, 1, cap, True)
+    gen = torch.Generator(device="cpu").manual_seed(3)
+
+    def run(poison):
+        k_cache = to_device(kc_host, "bf16")
+        pyr = ops.alloc_pyramid(dims, cap)
+        ops.build_pyramid(k_cache, N0, cap, dims, pyr)
+        ws = ops.alloc_workspace(dims, 1, cap, is_decode=True)
+        out = torch.full((B, 2, K), -7, dtype=torch.int32, device="cuda")
+        sel = []
+        for s in range(steps):
+            if poison == "bytes":
+                ws.copy_(torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=gen).cuda())
+            elif poison == "one_short":
+                words = torch.randint(1, 1 << 31, (B * 2,), dtype=torch.int64, generator=gen)
+                ws[: 8 * B * 2].copy_(((words << 32) | 3).view(torch.uint8).cuda())
+            print(f"[case] decode workspace poison={poison} step={s}", flush=True)
+            ops.decode_update_select(q_new[s].contiguous(), k_new[s].contiguous(), k_cache, pyr, N0 + s, cap,
+                                     dims, out, ws)
+            torch.cuda.synchronize()
+            sel.append(out.cpu().numpy().copy())
+        return np.stack(sel), pyr.cpu().numpy()
+
+    ref_sel, ref_pyr = run(None)
+    assert (ref_sel >= 0).all()
+    for poison in ("bytes", "one_short"):
+        sel, pyr = run(poison)
+        assert np.array_equal(sel, ref_sel), poison
+        assert np.array_equal(pyr.view(np.uint32), ref_pyr.view(np.uint32)), poison
+
+
 @pytest.mark.parametrize("B,dtype", [(3, "bf16"), (4, "bf16"), (3, "f32")])
 def test_prefill_batched(B, dtype):
     """Several batch elements with their own keys and queries (B*Hkv = 6 or 8 walks per
