@@ -25,6 +25,9 @@ HIPCC_FLAGS = [
     # inputs are finite by contract (NaN inputs give unspecified indices); lets max/min
     # skip operand canonicalisation. Infinities stay honoured (-inf is a sentinel).
     "-fno-honor-nans",
+    # MFMA results in ordinary VGPRs (no accumulation-register copies): fewer registers and
+    # VALU moves in the leaf, attention and flat kernels
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -43,7 +43,7 @@ __global__ void bucket_pass_kernel(const int32_t*, const int32_t*, Geom, Cluster
 __global__ void pack_plan_kernel(Pack, int, int, int64_t*);
 __global__ void group_offsets_kernel(const uint32_t*, ClusterGeom, Pack, const int64_t*, uint32_t*, uint32_t*);
 __global__ void scan_groups_kernel(const uint32_t*, ClusterGeom, uint32_t, uint32_t*, int4*, uint32_t*);
-template <int S>
+template <int S, bool kOneEach>
 __global__ void leaf_cluster_kernel(const uint16_t*, const uint16_t*, Geom, ClusterGeom, Pack, int64_t,
                                     const int4*, const uint2*, uint32_t*, float*, float*);
 
@@ -83,10 +83,15 @@ static const void* upper_f32_fn(int score) {
     if (score == kScoreMeanHalfVar) return (const void*)walk_upper_f32_kernel<SLOTS, kScoreMeanHalfVar>;
     return (const void*)walk_upper_f32_kernel<SLOTS, kScoreLse>;
 }
-static const void* leaf_cluster_fn(int score) {
-    if (score == kScoreMean) return (const void*)leaf_cluster_kernel<kScoreMean>;
-    if (score == kScoreMeanHalfVar) return (const void*)leaf_cluster_kernel<kScoreMeanHalfVar>;
-    return (const void*)leaf_cluster_kernel<kScoreLse>;
+static const void* leaf_cluster_fn(int score, bool one_each) {
+    if (one_each) {
+        if (score == kScoreMean) return (const void*)leaf_cluster_kernel<kScoreMean, true>;
+        if (score == kScoreMeanHalfVar) return (const void*)leaf_cluster_kernel<kScoreMeanHalfVar, true>;
+        return (const void*)leaf_cluster_kernel<kScoreLse, true>;
+    }
+    if (score == kScoreMean) return (const void*)leaf_cluster_kernel<kScoreMean, false>;
+    if (score == kScoreMeanHalfVar) return (const void*)leaf_cluster_kernel<kScoreMeanHalfVar, false>;
+    return (const void*)leaf_cluster_kernel<kScoreLse, false>;
 }
 static const void* decode_step_fn(int score) {
     if (score == kScoreMean) return (const void*)decode_step_kernel<kScoreMean>;
@@ -106,21 +111,25 @@ static uint32_t next_call_tag() {
     while (t == 0u) t = g_call_tag.fetch_add(1u, std::memory_order_relaxed) + 1u;
     return t;
 }
-// The bucket pass counts one sequence's (KV head, superblock) groups in an LDS histogram of
-// this many bins (64 KiB): bf16 selection needs Hkv * ceil(N / 1024) <= kMaxClusterGroups.
-constexpr int64_t kMaxClusterGroups = 16384;
-static bool bf16_select_fits(const pisa_dims* d, int64_t N) {
-    return (int64_t)d->Hkv * ((N + kSbKeys - 1) / kSbKeys) <= kMaxClusterGroups;
+// The leaf stage numbers its entries (one per walk and sibling pair of candidates, at most
+// 2K per walk) and its (KV head, pair) groups in 32 bits: bf16 selection needs
+// walks * 2K < 2^32 and Hkv * ceil(N / 128) < 2^31 (N positions per sequence).
+static bool bf16_select_fits(const pisa_dims* d, int64_t walks, int64_t N) {
+    return walks * 2 * d->topk < ((int64_t)1 << 32) &&
+           (int64_t)d->Hkv * ((N + kGrpKeys - 1) / kGrpKeys) < ((int64_t)1 << 31);
 }
 
 static size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Positions per bucket range (log2): 512, halved down to 64 while the call has fewer ranges
-// than kRangeWorkgroups (one bucket-pass workgroup per CU of an MI355X).
+// Positions per bucket range (log2): 1024, halved down to 64 while the call has fewer ranges
+// than kRangeWorkgroups (one bucket-pass workgroup per CU of an MI355X), and doubled while
+// the buckets (groups x ranges) would number more than kMaxBuckets (a very long call).
 constexpr int64_t kRangeWorkgroups = 256;
-static int range_log2(int64_t positions) {
+constexpr int64_t kMaxBuckets = (int64_t)1 << 26;
+static int range_log2(int64_t positions, int64_t groups) {
     int rl = kLog2RangeMax;
     while (rl > kLog2RangeMin && ((positions + ((int64_t)1 << rl) - 1) >> rl) < kRangeWorkgroups) --rl;
+    while (groups * ((positions + ((int64_t)1 << rl) - 1) >> rl) > kMaxBuckets) ++rl;
     return rl;
 }
 
@@ -132,14 +141,14 @@ struct Workspace {
     int32_t* ncand;      // [walks]
     // clustered leaf scoring (prefill, bf16 inputs)
     float* score;        // [walks][2K]
-    float* sink;         // [kClusterThreads] stores of lanes without a score
+    float* sink;         // [kLeafThreads] stores of lanes without a score
     uint32_t* counts;    // [nb] group-major: bucket (range r, group g) at g * NR + r
     uint32_t* offsets;   // [nb] offset of each bucket inside its group
     uint32_t* gtot;      // [ngroups] entries per group
     uint32_t* gbase;     // [ngroups] first entry of each group
     uint2* entries;      // [walks * 2K] incidences grouped by bucket
     int4* items;         // [walks * 2K / kItemMin + ngroups]
-    uint32_t* meta;      // [0] items, [1] entries
+    uint32_t* meta;      // [0] items, [1] entries, item-stream counters (kMetaWords)
     int64_t* cbase;      // [D + 1] first count of each document's block (packs only)
     // fused bf16 decoding step
     unsigned long long* done;   // [B*Hkv] tagged completion counters (any contents)
@@ -173,24 +182,24 @@ static Workspace carve(const pisa_dims* d, int64_t N, int64_t P, bool decode, ch
     w.cand = (int32_t*)take((size_t)walks * cs * sizeof(int32_t));
     w.ncand = (int32_t*)take((size_t)walks * sizeof(int32_t));
     const int64_t m1 = (N + kC - 1) / kC;
-    const int64_t nsb = (m1 + kSbLeaves - 1) / kSbLeaves;
-    // clustered leaf scoring for bf16 prefill (callers check kMaxClusterGroups first)
-    w.clustered = !decode && d->dtype == PISA_DTYPE_BF16 && d->Hkv * nsb <= kMaxClusterGroups;
+    const int64_t ngp = (m1 + kGrpLeaves - 1) / kGrpLeaves;
+    // clustered leaf scoring for bf16 prefill (callers check bf16_select_fits first)
+    w.clustered = !decode && d->dtype == PISA_DTYPE_BF16 && bf16_select_fits(d, walks, N);
     if (w.clustered) {
-        w.CG.RL = range_log2((int64_t)d->B * N);
+        w.CG.RL = range_log2((int64_t)d->B * N, (int64_t)d->B * d->Hkv * ngp);
         w.CG.NR = (int32_t)((N + ((int64_t)1 << w.CG.RL) - 1) >> w.CG.RL);
-        w.CG.NSB = (int32_t)nsb;
-        w.CG.ngroups = (int32_t)(d->B * d->Hkv * nsb);
+        w.CG.NGP = (int32_t)ngp;
+        w.CG.ngroups = (int32_t)(d->B * d->Hkv * ngp);
         w.CG.nb = w.CG.ngroups * w.CG.NR;
         w.score = (float*)take((size_t)walks * cs * sizeof(float));
-        w.sink = (float*)take((size_t)kClusterThreads * sizeof(float));
+        w.sink = (float*)take((size_t)kLeafThreads * sizeof(float));
         w.counts = (uint32_t*)take((size_t)w.CG.nb * 4);
         w.offsets = (uint32_t*)take((size_t)w.CG.nb * 4);
         w.gtot = (uint32_t*)take((size_t)w.CG.ngroups * 4);
         w.gbase = (uint32_t*)take((size_t)w.CG.ngroups * 4);
         w.entries = (uint2*)take((size_t)walks * cs * sizeof(uint2));
         w.items = (int4*)take(((size_t)walks * cs / kItemMin + w.CG.ngroups + 1) * sizeof(int4));
-        w.meta = (uint32_t*)take(16);
+        w.meta = (uint32_t*)take(kMetaWords * sizeof(uint32_t));
     }
     w.bytes = off;
     return w;
@@ -199,10 +208,10 @@ static Workspace carve(const pisa_dims* d, int64_t N, int64_t P, bool decode, ch
 // Packs of D documents over T tokens (bf16, clustered leaf scoring) on the packed layout
 // of P rows per KV head.
 static int64_t pack_count_bound(int Hkv, int64_t T, int64_t D, int rl) {
-    // sum over documents of ceil(n/1024) * ceil(n/R) <= sum (n/1024 + 1)(n/R + 1)
-    // <= T^2 / (1024 R) + T/1024 + T/R + D
+    // sum over documents of ceil(n/128) * ceil(n/R) <= sum (n/128 + 1)(n/R + 1)
+    // <= T^2 / (128 R) + T/128 + T/R + D
     const int64_t R = (int64_t)1 << rl;
-    return (int64_t)Hkv * (((T + 1023) / 1024) * ((T + R - 1) / R) + T / 1024 + T / R + D + 4);
+    return (int64_t)Hkv * (((T + kGrpKeys - 1) / kGrpKeys) * ((T + R - 1) / R) + T / kGrpKeys + T / R + D + 4);
 }
 
 static Workspace carve_pack(const pisa_dims* d, int64_t T, int64_t D, int64_t P, char* base) {
@@ -222,21 +231,21 @@ static Workspace carve_pack(const pisa_dims* d, int64_t T, int64_t D, int64_t P,
     w.cand = (int32_t*)take((size_t)walks * cs * sizeof(int32_t));
     w.ncand = (int32_t*)take((size_t)walks * sizeof(int32_t));
     w.clustered = true;
-    w.CG.NSB = (int32_t)((T >> (kLog2C + 4)) + D + 1);   // superblock slots per KV head
-    w.CG.RL = range_log2(T);
+    w.CG.NGP = (int32_t)((T >> (kLog2GrpKeys)) + D + 1);   // pair slots per KV head
+    w.CG.RL = range_log2(T, (int64_t)d->Hkv * ((T + kGrpKeys - 1) / kGrpKeys) + D);
     w.CG.NR = (int32_t)((T >> w.CG.RL) + D + 1);        // range slots
-    w.CG.ngroups = (int32_t)(d->Hkv * (int64_t)w.CG.NSB);
+    w.CG.ngroups = (int32_t)(d->Hkv * (int64_t)w.CG.NGP);
     const int64_t ncount = pack_count_bound(d->Hkv, T, D, w.CG.RL);
     w.CG.nb = 0;
     w.score = (float*)take((size_t)walks * cs * sizeof(float));
-    w.sink = (float*)take((size_t)kClusterThreads * sizeof(float));
+    w.sink = (float*)take((size_t)kLeafThreads * sizeof(float));
     w.counts = (uint32_t*)take((size_t)ncount * 4);
     w.offsets = (uint32_t*)take((size_t)ncount * 4);
     w.gtot = (uint32_t*)take((size_t)w.CG.ngroups * 4);
     w.gbase = (uint32_t*)take((size_t)w.CG.ngroups * 4);
     w.entries = (uint2*)take((size_t)walks * cs * sizeof(uint2));
     w.items = (int4*)take(((size_t)walks * cs / kItemMin + w.CG.ngroups + 1) * sizeof(int4));
-    w.meta = (uint32_t*)take(16);
+    w.meta = (uint32_t*)take(kMetaWords * sizeof(uint32_t));
     w.cbase = (int64_t*)take((size_t)(D + 1) * sizeof(int64_t));
     w.bytes = off;
     return w;
@@ -294,7 +303,7 @@ static int make_pack_geom(const pisa_dims* d, int64_t T, int64_t D, Geom* G) {
     if (T < 1 || D < 1) return PISA_ERR_INVALID_ARG;
     if (d->B != 1) return PISA_ERR_INVALID_ARG;
     if (T > (int64_t)INT_MAX / 2 || D > (int64_t)INT_MAX / 4) return PISA_ERR_UNSUPPORTED;
-    if ((int64_t)d->Hkv * ((T >> (kLog2C + 4)) + D + 1) > (int64_t)INT_MAX) return PISA_ERR_UNSUPPORTED;
+    if ((int64_t)d->Hkv * ((T >> (kLog2GrpKeys)) + D + 1) > (int64_t)INT_MAX) return PISA_ERR_UNSUPPORTED;
     memset(G, 0, sizeof(*G));
     const int L = root_level(T);
     int64_t off = 0;
@@ -425,6 +434,21 @@ static void mark(void* const* ev, int i, hipStream_t s) {
     if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], s);
 }
 
+// Resident workgroups per CU of each leaf-scoring kernel (a property of the code object,
+// queried once per variant; 0 if the query fails).
+static int leaf_blocks_per_cu(int score, bool one_each) {
+    static std::atomic<int> cache[6] = {{-1}, {-1}, {-1}, {-1}, {-1}, {-1}};
+    const int i = ((score == kScoreMean) ? 1 : (score == kScoreMeanHalfVar) ? 2 : 0) + (one_each ? 3 : 0);
+    int v = cache[i].load(std::memory_order_relaxed);
+    if (v < 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, leaf_cluster_fn(score, one_each), kLeafThreads, 0) !=
+            hipSuccess)
+            return 0;
+        cache[i].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
 static int cluster_leaf_stage(const uint16_t* q, const uint16_t* k, const Geom& G, const Pack& pk, int64_t NT,
                               int32_t* out, const Workspace& W, int cus, hipStream_t s, void* const* ev) {
     const int64_t walks = (int64_t)G.B * NT * G.Hkv;
@@ -435,17 +459,19 @@ static int cluster_leaf_stage(const uint16_t* q, const uint16_t* k, const Geom& 
     if (pk.cu) {
         hipLaunchKernelGGL(pack_plan_kernel, dim3(1), dim3(1024), 0, s, pk, G.Hkv, (int)CG.RL, W.cbase);
         bgrid = dim3((unsigned)CG.NR, 1u);
-        bins = (size_t)G.Hkv * ((pk.T + kSbKeys - 1) / kSbKeys) * 4;   // the longest document's groups
+        bins = (size_t)G.Hkv * ((pk.T + kGrpKeys - 1) / kGrpKeys);   // the longest document's groups
     } else {
         bgrid = dim3((unsigned)CG.NR, (unsigned)G.B);
-        bins = (size_t)G.Hkv * CG.NSB * 4;
+        bins = (size_t)G.Hkv * CG.NGP;
     }
+    bins = (bins < (size_t)kBinSlice ? bins : (size_t)kBinSlice) * sizeof(uint32_t);   // LDS bytes
     const int64_t* cbase = W.cbase;
     for (int fill = 0; fill < 2; ++fill) {
         if (fill) {
             hipLaunchKernelGGL(group_offsets_kernel, dim3((unsigned)((CG.ngroups + 3) / 4)), dim3(256), 0, s, W.counts,
                                CG, pk, cbase, W.offsets, W.gtot);
-            hipLaunchKernelGGL(scan_groups_kernel, dim3(1), dim3(1024), 0, s, W.gtot, CG, (uint32_t)((cus + 1) / 2),
+            // about two items per wavefront the leaf stage keeps resident (3 per SIMD)
+            hipLaunchKernelGGL(scan_groups_kernel, dim3(1), dim3(1024), 0, s, W.gtot, CG, (uint32_t)(cus * 24),
                                W.gbase, W.items, W.meta);
         }
         if (slots <= 16)
@@ -458,16 +484,20 @@ static int cluster_leaf_stage(const uint16_t* q, const uint16_t* k, const Geom& 
             hipLaunchKernelGGL(bucket_pass_kernel<64>, bgrid, dim3(1024), bins, s, W.cand, W.ncand, G, CG, pk, cbase,
                                NT, W.counts, W.offsets, W.gbase, W.entries, fill);
     }
-    const void* leaf_fn = leaf_cluster_fn(G.score);
-    if (hipFuncSetAttribute(leaf_fn, hipFuncAttributeMaxDynamicSharedMemorySize, kSbLdsBytes) != hipSuccess)
-        return PISA_ERR_HIP;
+    // persistent wavefronts: as many workgroups as fit the CUs at once. A short call (at most
+    // about two items of kItemMin entries per wavefront, counting K entries per walk) gives
+    // each wavefront its first item without an atomic.
+    const bool one_each = (int64_t)walks * G.topk <= (int64_t)cus * 12 * 2 * kItemMin;
+    const void* leaf_fn = leaf_cluster_fn(G.score, one_each);
+    const int per_cu = leaf_blocks_per_cu(G.score, one_each);
+    if (per_cu < 1) return PISA_ERR_HIP;
     mark(ev, 2, s);
     {
         const int4* items = W.items;
         const uint2* entries = W.entries;
         void* args[] = {(void*)&q, (void*)&k, (void*)&G, (void*)&CG, (void*)&pk, (void*)&NT, (void*)&items,
                         (void*)&entries, (void*)&W.meta, (void*)&W.score, (void*)&W.sink};
-        if (hipLaunchKernel(leaf_fn, dim3((unsigned)cus), dim3(kClusterThreads), args, kSbLdsBytes, s) != hipSuccess)
+        if (hipLaunchKernel(leaf_fn, dim3((unsigned)(cus * per_cu)), dim3(kLeafThreads), args, 0, s) != hipSuccess)
             return PISA_ERR_HIP;
     }
     mark(ev, 3, s);
@@ -593,7 +623,8 @@ size_t pisa_pyramid_bytes(const pisa_dims* dims, int64_t n_capacity) {
 
 size_t pisa_workspace_bytes(const pisa_dims* dims, int64_t N, int64_t n_capacity, int32_t is_decode) {
     if (check_dims(dims) != PISA_OK || n_capacity < 1 || (!is_decode && (N < 1 || N > n_capacity))) return 0;
-    if (!is_decode && dims->dtype == PISA_DTYPE_BF16 && !bf16_select_fits(dims, N)) return 0;
+    if (!is_decode && dims->dtype == PISA_DTYPE_BF16 && !bf16_select_fits(dims, (int64_t)dims->B * N * dims->Hkv, N))
+        return 0;
     const int64_t P = pisa_pyramid_nodes(dims, n_capacity);
     return carve(dims, is_decode ? 1 : N, P, is_decode != 0, nullptr).bytes;
 }
@@ -620,7 +651,8 @@ int pisa_select_prefill_profiled(const void* q, const void* k, const float* pyra
     if (!q || !k || !pyramid || !out_idx) return PISA_ERR_INVALID_ARG;
     Geom G;
     if ((rc = make_geom(dims, N, n_capacity, &G)) != PISA_OK) return rc;
-    if (dims->dtype == PISA_DTYPE_BF16 && !bf16_select_fits(dims, N)) return PISA_ERR_UNSUPPORTED;
+    if (dims->dtype == PISA_DTYPE_BF16 && !bf16_select_fits(dims, (int64_t)dims->B * N * dims->Hkv, N))
+        return PISA_ERR_UNSUPPORTED;
     const Workspace W = carve(dims, N, G.P, false, (char*)workspace);
     if (!workspace || ws_bytes < W.bytes) return PISA_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
@@ -825,8 +857,7 @@ int pisa_select_prefill_packed(const void* q, const void* k, const float* pyrami
     if (rc != PISA_OK) return rc;
     if (!q || !k || !pyramid || !cu_seqlens || !out_idx) return PISA_ERR_INVALID_ARG;
     if (dims->dtype != PISA_DTYPE_BF16) return PISA_ERR_UNSUPPORTED;
-    // the bucket pass holds one document's (KV head, superblock) bins in LDS
-    if (!bf16_select_fits(dims, T)) return PISA_ERR_UNSUPPORTED;
+    if (!bf16_select_fits(dims, T * dims->Hkv, T)) return PISA_ERR_UNSUPPORTED;
     const Workspace W = carve_pack(dims, T, D, G.P, (char*)workspace);
     if (!workspace || ws_bytes < W.bytes) return PISA_ERR_WORKSPACE;
     const Pack pk{cu_seqlens, (int32_t)D, T};

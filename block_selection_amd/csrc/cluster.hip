@@ -23,6 +23,8 @@
 //   5. final_topk: per walk, the K best leaf candidates in ascending order.
 // Per incidence the walk's queries (2 KiB) are read once; the keys of a
 // superblock are read from memory once per work item.
+#include <type_traits>
+
 #include "walk_math.h"
 
 namespace pisa {
@@ -36,12 +38,13 @@ namespace pisa {
 // Entry = {query position t, leaf mask | first slot << 16}: the mask holds the superblock
 // offsets of one leaf or of a sibling pair (batch element and KV head are the bucket's).
 // Counts and offsets are group-major: bucket (range r, group g) at g * NR + r; the fill
-// pass starts bucket (r, g) at gbase[g] + offsets[g * NR + r].
+// pass starts bucket (r, g) at gbase[g] + offsets[g * NR + r]. The bins live in LDS
+// kBinSlice at a time (a sequence with more groups is counted slice by slice).
 // With a pack (pk.cu non-null) blockIdx.x is a range slot of the packed layout: range j of
 // one document d (or nothing), positions t count from the document's start, and the
-// workgroup's bins are the document's own groups, x = kvh * nsb_d + s (superblock s of the
-// document is superblock slot (cu[d] >> 10) + d + s, group kvh * CG.NSB + that slot). Its
-// counts sit in the document's block at cbase[d] + x * nr_d + j (nr_d ranges).
+// workgroup's bins are the document's own groups, x = kvh * nsb_d + s (pair s of the
+// document is pair slot (cu[d] >> 7) + d + s, group kvh * CG.NGP + that slot). Its counts
+// sit in the document's block at cbase[d] + x * nr_d + j (nr_d ranges).
 template <int SL>
 __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __restrict__ cand,
                                                           const int32_t* __restrict__ ncand, Geom G,
@@ -57,8 +60,8 @@ __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __rest
     const int K = G.topk, CS = 2 * G.topk;
     const int nthr = blockDim.x, nw = nthr >> 6;
     int64_t bt0, t_lo, t_hi;   // first query row of the sequence, positions [t_lo, t_hi)
-    int nsb;                   // superblocks per KV head in the bins: x = kvh * nsb + s
-    int64_t g_sb0, c0, c_str;  // bin x -> group (x / nsb) * CG.NSB + g_sb0 + x % nsb; count c0 + x * c_str
+    int nsb;                   // pair groups per KV head in the bins: x = kvh * nsb + s
+    int64_t g_sb0, c0, c_str;  // bin x -> group (x / nsb) * CG.NGP + g_sb0 + x % nsb; count c0 + x * c_str
     if (pk.cu) {
         const int d = pack_find_slot(pk, CG.RL, r);
         const Seg sg = pack_seg(pk, d);
@@ -68,8 +71,8 @@ __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __rest
         bt0 = sg.lsh;
         t_lo = j << CG.RL;
         t_hi = (t_lo + (1 << CG.RL) < sg.N) ? t_lo + (1 << CG.RL) : sg.N;
-        nsb = (int)((sg.N + kSbKeys - 1) / kSbKeys);
-        g_sb0 = (sg.lsh >> (kLog2C + 4)) + d;
+        nsb = (int)((sg.N + kGrpKeys - 1) / kGrpKeys);
+        g_sb0 = (sg.lsh >> (kLog2GrpKeys)) + d;
         c0 = cbase[d] + j;
         c_str = nr;
     } else {
@@ -77,15 +80,19 @@ __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __rest
         bt0 = (int64_t)b * NT;
         t_lo = (int64_t)r << CG.RL;
         t_hi = (t_lo + (1 << CG.RL) < NT) ? t_lo + (1 << CG.RL) : NT;
-        nsb = CG.NSB;
-        g_sb0 = (int64_t)b * G.Hkv * CG.NSB;
+        nsb = CG.NGP;
+        g_sb0 = (int64_t)b * G.Hkv * CG.NGP;
         c0 = g_sb0 * CG.NR + r;
         c_str = CG.NR;
     }
+    // the bins are held in LDS kBinSlice at a time; a longer sequence's range is read once per slice
     const int nbins = G.Hkv * nsb;
-    for (int x = tid; x < nbins; x += nthr) {
-        const int64_t g = (int64_t)(x / nsb) * CG.NSB + g_sb0 + x % nsb;
-        bins[x] = fill ? gbase[g] + offsets[c0 + x * c_str] : 0u;
+    for (int x0 = 0; x0 < nbins; x0 += kBinSlice) {
+    const int nx = min(kBinSlice, nbins - x0);
+    if (x0) __syncthreads();   // the previous slice's counts are written out
+    for (int x = tid; x < nx; x += nthr) {
+        const int64_t g = (int64_t)((x0 + x) / nsb) * CG.NGP + g_sb0 + (x0 + x) % nsb;
+        bins[x] = fill ? gbase[g] + offsets[c0 + (int64_t)(x0 + x) * c_str] : 0u;
     }
     __syncthreads();
     const int64_t w_lo = (bt0 + t_lo) * G.Hkv, w_hi = (bt0 + t_hi) * G.Hkv;
@@ -95,7 +102,7 @@ __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __rest
         const int nc = ok ? ncand[w] : 0;
         const int leaf = (ok && i < CS && i < nc) ? cand[w * CS + i] : -1;
         const int kvh = (int)(w % G.Hkv);
-        const int sbv = (leaf >= 0) ? leaf / kSbLeaves : -1;
+        const int sbv = (leaf >= 0) ? leaf / kGrpLeaves : -1;
         // candidates ascend and come as sibling pairs (2c, then 2c+1 if eligible): an entry
         // starts at an even leaf, or at an odd one whose sibling is not a candidate
         const int prv = shfl_i(leaf, lane > 0 ? lane - 1 : 0);
@@ -103,15 +110,17 @@ __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __rest
         const bool even = (leaf & 1) == 0;
         const bool start = nc > K && leaf >= 0 && (even || i == 0 || prv != leaf - 1);
         const bool pair = even && i + 1 < SL && nxt == leaf + 1;
-        const uint32_t m = (leaf >= 0) ? ((pair ? 3u : 1u) << (leaf % kSbLeaves)) : 0u;
-        if (start) {
-            const uint32_t pos = atomicAdd(&bins[kvh * nsb + sbv], 1u);
+        const uint32_t m = (leaf >= 0) ? ((pair ? 3u : 1u) << (leaf % kGrpLeaves)) : 0u;
+        const int bx = kvh * nsb + sbv - x0;
+        if (start && bx >= 0 && bx < nx) {
+            const uint32_t pos = atomicAdd(&bins[bx], 1u);
             if (fill) entries[pos] = make_uint2((uint32_t)(w / G.Hkv - bt0), m | ((uint32_t)i << 16));
         }
     }
     __syncthreads();
     if (!fill) {
-        for (int x = tid; x < nbins; x += nthr) counts[c0 + x * c_str] = bins[x];
+        for (int x = tid; x < nx; x += nthr) counts[c0 + (int64_t)(x0 + x) * c_str] = bins[x];
+    }
     }
 }
 
@@ -124,7 +133,7 @@ __global__ __launch_bounds__(1024) void pack_plan_kernel(Pack pk, int Hkv, int R
     const int lo = tid * per, hi = min(pk.D, lo + per);
     auto size_of = [&](int d) -> int64_t {
         const Seg sg = pack_seg(pk, d);
-        return sg.N ? (int64_t)Hkv * ((sg.N + kSbKeys - 1) / kSbKeys) * (((sg.N - 1) >> RL) + 1) : 0;
+        return sg.N ? (int64_t)Hkv * ((sg.N + kGrpKeys - 1) / kGrpKeys) * (((sg.N - 1) >> RL) + 1) : 0;
     };
     int64_t acc = 0;
     for (int d = lo; d < hi; ++d) acc += size_of(d);
@@ -146,7 +155,7 @@ __global__ __launch_bounds__(1024) void pack_plan_kernel(Pack pk, int Hkv, int R
 
 // One wavefront per group g: the exclusive scan of its ranges' counts (the offset of
 // each bucket inside the group) and the group's total. Grid: ceil(ngroups / 4)
-// workgroups of 4 wavefronts. With a pack, group g = kvh * CG.NSB + superblock slot; a
+// workgroups of 4 wavefronts. With a pack, group g = kvh * CG.NGP + superblock slot; a
 // slot that names no superblock of a document has total 0.
 __global__ __launch_bounds__(256) void group_offsets_kernel(const uint32_t* __restrict__ counts, ClusterGeom CG,
                                                             Pack pk, const int64_t* __restrict__ cbase,
@@ -158,12 +167,12 @@ __global__ __launch_bounds__(256) void group_offsets_kernel(const uint32_t* __re
     int64_t c0 = g * CG.NR;
     int nr = CG.NR;
     if (pk.cu) {
-        const int kvh = (int)(g / CG.NSB);
-        const int64_t slot = g % CG.NSB;
-        const int d = pack_find_slot(pk, kLog2C + 4, slot);
+        const int kvh = (int)(g / CG.NGP);
+        const int64_t slot = g % CG.NGP;
+        const int d = pack_find_slot(pk, kLog2GrpKeys, slot);
         const Seg sg = pack_seg(pk, d);
-        const int64_t s = slot - ((sg.lsh >> (kLog2C + 4)) + d);
-        const int64_t nsb = (sg.N + kSbKeys - 1) / kSbKeys;
+        const int64_t s = slot - ((sg.lsh >> (kLog2GrpKeys)) + d);
+        const int64_t nsb = (sg.N + kGrpKeys - 1) / kGrpKeys;
         if (sg.N == 0 || s < 0 || s >= nsb) {
             if (lane == 0) gtot[g] = 0u;
             return;
@@ -192,12 +201,11 @@ __global__ __launch_bounds__(256) void group_offsets_kernel(const uint32_t* __re
 // One workgroup: the entry offset of every group (groups in order) and work items of at
 // most L entries of one group. L is kItemMax, halved (down to kItemMin) while the call's
 // entries would make fewer than min_items items of L: a short sequence then spreads its
-// scoring over more CUs, at the price of fewer entries per wavefront sharing a sibling
-// pair (the caller passes half the CU count: measured, items of kItemMax that leave some
-// CUs idle beat smaller ones in more rounds). Items holding L entries come first, the
-// smaller remainders after them, so that the workgroups taking items in order finish
-// together. meta[0] = number of items, meta[1] = number of entries, meta[2] = 0 (the
-// counter the scoring workgroups take items from).
+// scoring over more wavefronts, at the price of loading a pair's keys for fewer entries.
+// Items holding L entries come first, the smaller remainders after them, so that the
+// wavefronts taking items in order finish together. meta[0] = number of items, meta[1] =
+// number of entries, and the kItemStreams counters the scoring wavefronts take items from
+// are set to 0.
 __global__ __launch_bounds__(1024) void scan_groups_kernel(const uint32_t* __restrict__ gtot, ClusterGeom CG,
                                                            uint32_t min_items, uint32_t* __restrict__ gbase,
                                                            int4* __restrict__ items,
@@ -250,8 +258,8 @@ __global__ __launch_bounds__(1024) void scan_groups_kernel(const uint32_t* __res
     if (tid == 1023) {
         meta[0] = nfull + s_p[1023];
         meta[1] = total;
-        meta[2] = 0u;
     }
+    if (tid < kItemStreams) meta[kItemCounter0 + kItemCounterStride * tid] = 0u;
 }
 
 template __global__ void bucket_pass_kernel<16>(const int32_t*, const int32_t*, Geom, ClusterGeom, Pack, const int64_t*, int64_t,
@@ -261,45 +269,54 @@ template __global__ void bucket_pass_kernel<32>(const int32_t*, const int32_t*, 
 template __global__ void bucket_pass_kernel<64>(const int32_t*, const int32_t*, Geom, ClusterGeom, Pack, const int64_t*, int64_t,
                                                 uint32_t*, const uint32_t*, const uint32_t*, uint2*, int);
 
-// LDS image of a superblock: key row r (0..1023) at r*128 bytes, its 16-byte chunk c
-// stored at chunk position c ^ (r & 7) so that the MFMA A-fragment reads of 8
-// consecutive rows hit distinct banks.
-__device__ inline int sb_lds_offset(int r, int chunk) { return r * 128 + ((chunk ^ (r & 7)) << 4); }
+// Key fragments of one sibling pair, held in registers for a whole work item: f[j][tau][h]
+// is the MFMA A operand of leaf j's 16-key tile tau in lane (gq, n): key 16 tau + n of the
+// leaf, dims 8 gq .. 8 gq + 7 (h = 0) or 32 + 8 gq .. 32 + 8 gq + 7 (h = 1). Keys at or
+// past the sequence's end are zero.
+struct PairKeys {
+    u32x4 f[2][4][2];
+};
 
-// MFMA logits of one leaf (superblock offset `bit`) for one walk's query fragments:
-// acc[tau] in lane (gq, n) holds keys 16 tau + 4 gq + r of head n.
-__device__ inline void leaf_logits(const lds_char_t* lds, int bit, const bf16x8 q0, const bf16x8 q1, int n, int gq,
-                                   f32x4 acc[4]) {
+__device__ inline void load_pair_keys(const uint16_t* __restrict__ kb, int64_t row_stride, int64_t key0,
+                                      int64_t nkeys, int n, int gq, PairKeys& K) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau) {
+            const int64_t key = key0 + j * kC + 16 * tau + n;
+            u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+            if (key < nkeys) {
+                const uint16_t* row = kb + key * row_stride;
+                a = *reinterpret_cast<const u32x4*>(row + 8 * gq);
+                b = *reinterpret_cast<const u32x4*>(row + 32 + 8 * gq);
+            }
+            K.f[j][tau][0] = a;
+            K.f[j][tau][1] = b;
+        }
+    }
+}
+
+// MFMA logits of leaf J of the pair for one walk's query fragments: acc[tau] in lane
+// (gq, n) holds keys 16 tau + 4 gq + r of head n.
+template <int J>
+__device__ inline void leaf_logits(const PairKeys& K, const bf16x8 q0, const bf16x8 q1, f32x4 acc[4]) {
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) {
-        const int r = bit * kC + 16 * tau + n;
-        const u32x4 a0 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, gq));
-        const u32x4 a1 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, 4 + gq));
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), q0, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), q1, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, K.f[J][tau][0]), q0, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, K.f[J][tau][1]), q1, c, 0, 0, 0);
         acc[tau] = c;
     }
 }
 
 // This lane's exp sums of the four (walk, leaf) combinations of a unit (see score_unit),
-// in row order r = (walk r >> 1, leaf r & 1). The eight 16-key tiles (leaf j, tile tau)
-// run as a pipeline: the key fragments of the next tile are read from LDS while the
-// current one is multiplied and exponentiated (two fragment buffers, half the registers
-// of reading a whole leaf ahead). Per tile each walk's four terms are added as
-// (e0 + e1) + (e2 + e3), and the four tiles of a leaf as (t0 + t1) + (t2 + t3): the
-// balanced-tree order of leaf_exp_sum. Without a second walk (kTwo false) walk b's rows
-// repeat walk a's sums.
+// in row order r = (walk r >> 1, leaf r & 1), over the pair's eight 16-key tiles (leaf j,
+// tile tau). Per tile each walk's four terms are added as (e0 + e1) + (e2 + e3), and the
+// four tiles of a leaf as (t0 + t1) + (t2 + t3): the balanced-tree order of leaf_exp_sum.
+// Without a second walk (kTwo false) walk b's rows repeat walk a's sums.
 template <bool kFull, bool kTwo>
-__device__ inline void unit_exp_sums(const lds_char_t* lds, const int (&bits)[2], const int (&lim)[4],
-                                     const bf16x8 qa0, const bf16x8 qa1, const bf16x8 qb0, const bf16x8 qb1,
-                                     int n, int gq, float (&sum)[4]) {
-    u32x4 fa[2], fb[2];
-    auto read = [&](int st) {
-        const int r = bits[st >> 2] * kC + 16 * (st & 3) + n;
-        fa[st & 1] = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, gq));
-        fb[st & 1] = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, 4 + gq));
-    };
+__device__ inline void unit_exp_sums(const PairKeys& K, const int (&lim)[4], const bf16x8 qa0, const bf16x8 qa1,
+                                     const bf16x8 qb0, const bf16x8 qb1, int gq, float (&sum)[4]) {
     auto tile_sum = [&](const f32x4& c, int tau, int lm) -> float {
         float e[4];
 #pragma unroll
@@ -310,19 +327,19 @@ __device__ inline void unit_exp_sums(const lds_char_t* lds, const int (&bits)[2]
         return (e[0] + e[1]) + (e[2] + e[3]);
     };
     float ta[4], tb[4];
-    read(0);
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
-        const int j = st >> 2, tau = st & 3, b = st & 1;
-        if (st + 1 < 8) read(st + 1);
+        const int j = st >> 2, tau = st & 3;
+        const bf16x8 f0 = __builtin_bit_cast(bf16x8, K.f[j][tau][0]);
+        const bf16x8 f1 = __builtin_bit_cast(bf16x8, K.f[j][tau][1]);
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[b]), qa0, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[b]), qa1, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f0, qa0, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f1, qa1, c, 0, 0, 0);
         ta[tau] = tile_sum(c, tau, lim[j]);
         if (kTwo) {
             f32x4 d = {0.f, 0.f, 0.f, 0.f};
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[b]), qb0, d, 0, 0, 0);
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[b]), qb1, d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f0, qb0, d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f1, qb1, d, 0, 0, 0);
             tb[tau] = tile_sum(d, tau, lim[2 + j]);
         }
         if (tau == 3) {
@@ -332,17 +349,15 @@ __device__ inline void unit_exp_sums(const lds_char_t* lds, const int (&bits)[2]
     }
 }
 
-// Scores of a unit: two walks a and b (b may repeat a) against the two leaves of one
-// sibling pair (superblock offsets bits[0], bits[1]; the second may repeat the first).
-// Each key fragment is read from LDS once and used for both walks. The four
-// (walk, leaf) sums are reduced in one vector; returns, in lanes of row group r,
-// the score of (walk r >> 1, leaf r & 1), bitwise what leaf_lse_from_acc gives for the
-// leaf alone. lim[] are per (walk, leaf) in that row order; an ineligible leaf (lim < 0)
-// is computed with one key and its score discarded by the caller. two = false: the unit has
-// walk a only (b repeats a), whose second copy is not computed.
-__device__ inline float score_unit(const lds_char_t* lds, const int (&bits)[2], const int (&lim_in)[4],
-                                   const bf16x8 qa0, const bf16x8 qa1, const bf16x8 qb0, const bf16x8 qb1, int n,
-                                   int gq, int GQ, bool two) {
+// Scores of a unit: two walks a and b (b may repeat a) against both leaves of the pair.
+// Each key fragment is used for both walks. The four (walk, leaf) sums are reduced in one
+// vector; returns, in lanes of row group r, the score of (walk r >> 1, leaf r & 1),
+// bitwise what leaf_lse_from_acc gives for the leaf alone. lim[] are per (walk, leaf) in
+// that row order; an ineligible leaf (lim < 0) is computed with one key and its score
+// discarded by the caller. two = false: the unit has walk a only (b repeats a), whose
+// second copy is not computed.
+__device__ inline float score_unit(const PairKeys& K, const int (&lim_in)[4], const bf16x8 qa0, const bf16x8 qa1,
+                                   const bf16x8 qb0, const bf16x8 qb1, int n, int gq, int GQ, bool two) {
     int lim[4];
     bool full = true;
 #pragma unroll
@@ -353,13 +368,13 @@ __device__ inline float score_unit(const lds_char_t* lds, const int (&bits)[2], 
     // one branch per unit: a unit with no masked key (the common case) runs straight-line code
     float sum[4];
     if (full && two)
-        unit_exp_sums<true, true>(lds, bits, lim, qa0, qa1, qb0, qb1, n, gq, sum);
+        unit_exp_sums<true, true>(K, lim, qa0, qa1, qb0, qb1, gq, sum);
     else if (full)
-        unit_exp_sums<true, false>(lds, bits, lim, qa0, qa1, qb0, qb1, n, gq, sum);
+        unit_exp_sums<true, false>(K, lim, qa0, qa1, qb0, qb1, gq, sum);
     else if (two)
-        unit_exp_sums<false, true>(lds, bits, lim, qa0, qa1, qb0, qb1, n, gq, sum);
+        unit_exp_sums<false, true>(K, lim, qa0, qa1, qb0, qb1, gq, sum);
     else
-        unit_exp_sums<false, false>(lds, bits, lim, qa0, qa1, qb0, qb1, n, gq, sum);
+        unit_exp_sums<false, false>(K, lim, qa0, qa1, qb0, qb1, gq, sum);
     // column totals of the four sums in one vector: row r = (walk r >> 1, leaf r & 1)
     const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(sum[0]), __float_as_uint(sum[1]), false, false);
     const float Sa = __uint_as_float(x[0]) + __uint_as_float(x[1]);
@@ -370,12 +385,12 @@ __device__ inline float score_unit(const lds_char_t* lds, const int (&bits)[2], 
     float shift = 0.0f;
     const uint64_t bad = ballot(!(T < INFINITY && T > 0x1p-100f));
     if (bad) {
-#pragma unroll 1
-        for (int r = 0; r < 4; ++r) {
+        // rare: the (walk, leaf) of a bad row group again, shifted by each column's maximum logit
+        auto redo = [&](auto r_const, const bf16x8 q0, const bf16x8 q1) {
+            constexpr int r = decltype(r_const)::value;
             if (bad & (0xffffull << (16 * r))) {
-                // rare: this (walk, leaf) again, shifted by each column's maximum logit
                 f32x4 acc[4];
-                leaf_logits(lds, bits[r & 1], (r >> 1) ? qb0 : qa0, (r >> 1) ? qb1 : qa1, n, gq, acc);
+                leaf_logits<r & 1>(K, q0, q1, acc);
                 const float moff = cols4_max(leaf_lane_max(acc, lim[r], gq)) * kScale2;
                 const float v = leaf_exp_sum<false>(acc, lim[r], gq, moff);
                 const float sr = cols4_sum(v);
@@ -384,44 +399,34 @@ __device__ inline float score_unit(const lds_char_t* lds, const int (&bits)[2], 
                     shift = moff;
                 }
             }
-        }
+        };
+        redo(std::integral_constant<int, 0>{}, qa0, qa1);
+        redo(std::integral_constant<int, 1>{}, qa0, qa1);
+        redo(std::integral_constant<int, 2>{}, qb0, qb1);
+        redo(std::integral_constant<int, 3>{}, qb0, qb1);
     }
     const float lse2 = shift + __builtin_amdgcn_logf(T);
     return row16_sum((n < GQ) ? lse2 : 0.0f);
 }
 
 // Truncated scores of a unit (the layout and result convention of score_unit): the
-// moments of the four (walk, leaf) combinations, each key fragment read once for both
-// walks (walk b skipped when two is false), reduced over the row groups in one packed
-// exchange per moment (the order of cols4_sum), then mean (+ var/2) per head and the
-// group sum: the bits leaf_trunc_from_acc gives for each leaf alone.
+// moments of the four (walk, leaf) combinations, each key fragment used for both walks
+// (walk b skipped when two is false), reduced over the row groups in one packed exchange
+// per moment (the order of cols4_sum), then mean (+ var/2) per head and the group sum: the
+// bits leaf_trunc_from_acc gives for each leaf alone.
 template <int S>
-__device__ inline float score_unit_trunc(const lds_char_t* lds, const int (&bits)[2], const int (&lim_in)[4],
-                                         const bf16x8 qa0, const bf16x8 qa1, const bf16x8 qb0, const bf16x8 qb1,
-                                         int n, int gq, int GQ, bool two) {
+__device__ inline float score_unit_trunc(const PairKeys& K, const int (&lim_in)[4], const bf16x8 qa0,
+                                         const bf16x8 qa1, const bf16x8 qb0, const bf16x8 qb1, int n, int gq, int GQ,
+                                         bool two) {
     int lim[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) lim[r] = max(lim_in[r], 0);
     float s1[4], s2[4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    auto leaf = [&](auto j_const) {
+        constexpr int j = decltype(j_const)::value;
         f32x4 acca[4], accb[4];
-#pragma unroll
-        for (int tau = 0; tau < 4; ++tau) {
-            const int r = bits[j] * kC + 16 * tau + n;
-            const u32x4 a0 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, gq));
-            const u32x4 a1 = *reinterpret_cast<const lds_u32x4_t*>(lds + sb_lds_offset(r, 4 + gq));
-            f32x4 c = {0.f, 0.f, 0.f, 0.f};
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), qa0, c, 0, 0, 0);
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), qa1, c, 0, 0, 0);
-            acca[tau] = c;
-            if (two) {
-                f32x4 d = {0.f, 0.f, 0.f, 0.f};
-                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), qb0, d, 0, 0, 0);
-                d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), qb1, d, 0, 0, 0);
-                accb[tau] = d;
-            }
-        }
+        leaf_logits<j>(K, qa0, qa1, acca);
+        if (two) leaf_logits<j>(K, qb0, qb1, accb);
         if (lim[j] == kC - 1) leaf_moments<true>(acca, lim[j], gq, s1[j], s2[j]);
         else leaf_moments<false>(acca, lim[j], gq, s1[j], s2[j]);
         if (two) {
@@ -431,7 +436,9 @@ __device__ inline float score_unit_trunc(const lds_char_t* lds, const int (&bits
             s1[2 + j] = s1[j];
             s2[2 + j] = s2[j];
         }
-    }
+    };
+    leaf(std::integral_constant<int, 0>{});
+    leaf(std::integral_constant<int, 1>{});
     // column totals of the four combinations: row group r = (walk r >> 1, leaf r & 1)
     auto pack = [](const float (&v)[4]) -> float {
         const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[0]), __float_as_uint(v[1]), false, false);
@@ -449,7 +456,7 @@ __device__ inline float score_unit_trunc(const lds_char_t* lds, const int (&bits
 
 // B fragments of one walk's queries: head n of the group, dims {8gq..8gq+7} and
 // {32+8gq..32+8gq+7}. Always loads (columns n >= GQ read head 0; their results are
-// excluded from the group sum), so the number of loads per entry is fixed.
+// excluded from the group sum), so the number of loads per unit is fixed.
 __device__ inline void load_q(const uint16_t* __restrict__ q, int64_t bt, int Hq, int kvh, int GQ, int n,
                               int gq, u32x4& qa, u32x4& qb) {
     const uint16_t* qrow = q + (bt * Hq + (int64_t)kvh * GQ + (n < GQ ? n : 0)) * kD;
@@ -457,156 +464,143 @@ __device__ inline void load_q(const uint16_t* __restrict__ q, int64_t bt, int Hq
     qb = *reinterpret_cast<const u32x4*>(qrow + 32 + 8 * gq);
 }
 
-template <int S>
-__global__ __launch_bounds__(kClusterThreads) void leaf_cluster_kernel(
+// Persistent wavefronts, each on its own: a wavefront takes a work item from the counter,
+// loads the item's sibling pair of leaves (128 keys) into registers as MFMA A fragments,
+// and scores the item's entries two at a time (a unit: two walks, both leaves), the next
+// unit's queries in flight while the current one is scored. No LDS and no barrier.
+template <int S, bool kOneEach>
+__global__ __launch_bounds__(kLeafThreads) void leaf_cluster_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, Geom G, ClusterGeom CG, Pack pk, int64_t NT,
     const int4* __restrict__ items, const uint2* __restrict__ entries, uint32_t* __restrict__ meta,
     float* __restrict__ score, float* __restrict__ sink) {
-    static_assert(kItemMax <= 64 * (kClusterThreads / 64), "a wavefront holds its entries in one VGPR pair");
-    extern __shared__ u32x4 lds_u4[];
-    lds_char_t* lds = (lds_char_t*)lds_u4;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = kClusterThreads / 64;
+    static_assert(kItemMax % 64 == 0, "an item is scored in whole batches of 64 entries");
+    constexpr int kW = 2;   // walks per unit (one walk per unit at four wavefronts per SIMD measured slower)
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, gq = lane >> 4;
     const int CS = 2 * G.topk;
-    __shared__ uint32_t s_item;
     const uint32_t n_items = meta[0];
     const int64_t row_stride = (int64_t)G.Hkv * kD;
+    float* const wsink = sink + wave * 64 + lane;
 
-    // items are taken from a counter, so a workgroup that finishes early takes the next one
+    // Items come in kItemStreams interleaved streams (stream s: items s, s + S, s + 2S, ...),
+    // each with its own counter on its own 256-byte line, so that the atomics spread over S
+    // addresses; a wavefront starts on its workgroup's stream and moves to the next one when
+    // that is exhausted. kOneEach (chosen for short calls, which have about as many items as
+    // wavefronts): wavefront w first takes item w without an atomic, and the streams then
+    // hand out the items past the wavefront count.
+    const int s0 = (int)(blockIdx.x % kItemStreams);
+    const uint32_t skip = kOneEach ? gridDim.x * (kLeafThreads / 64) : 0u;
+    int si = kOneEach ? -1 : 0;
     for (;;) {
-        __syncthreads();   // the previous item's readers are done with LDS and s_item
-        if (threadIdx.x == 0) s_item = atomicAdd(&meta[2], 1u);
-        __syncthreads();
-        const uint32_t it = s_item;
-        if (it >= n_items) break;
+        uint32_t it;
+        if (kOneEach && si < 0) {
+            it = blockIdx.x * (kLeafThreads / 64) + wave;
+            si = 0;
+            if (it >= n_items) break;
+        } else {
+            const int sidx = (s0 + si) % kItemStreams;
+            uint32_t got = 0u;
+            if (lane == 0) got = atomicAdd(meta + kItemCounter0 + kItemCounterStride * sidx, 1u);
+            it = skip + (uint32_t)__builtin_amdgcn_readlane((int)got, 0) * kItemStreams + sidx;
+            if (it >= n_items) {
+                if (++si == kItemStreams) break;
+                continue;
+            }
+        }
         const int4 item = items[it];
         const int grp = item.x;
-        const int sbs = grp % CG.NSB;
-        const int kvh = (grp / CG.NSB) % G.Hkv;
+        const int gs = grp % CG.NGP;
+        const int kvh = (grp / CG.NGP) % G.Hkv;
         // the group's sequence: its first query row, first key row and key count
         int64_t bt0, tk0, nkeys;
-        int sb;
+        int pg;
         if (pk.cu) {
-            const int d = pack_find_slot(pk, kLog2C + 4, sbs);
+            const int d = pack_find_slot(pk, kLog2GrpKeys, gs);
             const Seg sg = pack_seg(pk, d);
-            sb = sbs - (int)((sg.lsh >> (kLog2C + 4)) + d);
+            pg = gs - (int)((sg.lsh >> kLog2GrpKeys) + d);
             bt0 = sg.lsh;
             tk0 = sg.tk0;
             nkeys = sg.N;
         } else {
-            const int b = grp / (CG.NSB * G.Hkv);
-            sb = sbs;
+            const int b = grp / (CG.NGP * G.Hkv);
+            pg = gs;
             bt0 = (int64_t)b * NT;
             tk0 = (int64_t)b * G.cap;
             nkeys = G.N;
         }
-        const int key_base = sb * kSbKeys;
-        const uint16_t* kb = k + (tk0 * G.Hkv + kvh) * kD;
-        // this wavefront's entries item.y + wave + j*nwaves, j < cnt: lane j holds entry j
-        const int first = item.y + wave;
-        const int cnt = (item.z > wave) ? (item.z - wave + nwaves - 1) / nwaves : 0;
-        const uint2 ev0 = (lane < cnt) ? entries[first + lane * nwaves] : make_uint2(0u, 0u);
-        // Units: the wavefront's entries are ordered by sibling pair (a 64-lane sort), and
-        // two entries of the same pair form a unit whose key fragments are read once.
-        // Lane u < nunits ends up holding unit u: entries (ua, ub); ub.y = 0 if alone.
-        const uint32_t m0 = ev0.y & 0xffffu;
-        const int pr0 = (lane < cnt && m0) ? (__builtin_ctz(m0) >> 1) : 15;
-        const uint32_t skey = index_sort<64>(((uint32_t)pr0 << 6) | (uint32_t)lane, lane);   // ascending
-        const int pj = (int)(skey >> 6), sl = (int)(skey & 63u);
-        const uint2 ev = make_uint2((uint32_t)shfl_i((int)ev0.x, sl), (uint32_t)shfl_i((int)ev0.y, sl));
-        int rk = 0;
-#pragma unroll
-        for (int v = 0; v < kSbLeaves / 2; ++v) {
-            const uint64_t mv = ballot(pj == v);
-            if (pj == v) rk = lanes_below(mv);
-        }
-        const int pj_next = shfl_i(pj, lane < 63 ? lane + 1 : lane);
-        const bool leader = pj < kSbLeaves / 2 && (rk & 1) == 0;
-        const bool has_b = leader && lane < 63 && pj_next == pj;
-        const uint64_t lm = ballot(leader);
-        const int nunits = __popcll(lm);
-        const int lead = push_to_lane(leader ? lanes_below(lm) : nunits + lanes_below(~lm), lane);
-        const int hb = push_to_lane(leader ? lanes_below(lm) : nunits + lanes_below(~lm), has_b ? 1 : 0);
-        // (cross-lane reads with every lane active: a lane outside a branch supplies nothing)
-        const bool uok = lane < nunits;
-        const uint32_t sax = (uint32_t)shfl_i((int)ev.x, lead), say = (uint32_t)shfl_i((int)ev.y, lead);
-        const uint32_t sbx = (uint32_t)shfl_i((int)ev.x, min(lead + 1, 63));
-        const uint32_t sby = (uint32_t)shfl_i((int)ev.y, min(lead + 1, 63));
-        const uint32_t uax = uok ? sax : 0u, uay = uok ? say : 0u;
-        const uint32_t ubx = uok ? sbx : 0u, uby = (uok && hb) ? sby : 0u;
-        // queries of the first two units, in flight during the key staging; units past
-        // nunits read walk 0 (a valid row) and score nothing
-        u32x4 qa0, qa1, qb0, qb1, ra0, ra1, rb0, rb1;
-        auto qload = [&](int u, u32x4& a0, u32x4& a1, u32x4& b0, u32x4& b1) {
-            const uint32_t ta = (uint32_t)__builtin_amdgcn_readlane((int)uax, u);
-            const uint32_t tb = (uint32_t)__builtin_amdgcn_readlane((int)(uby ? ubx : uax), u);
-            load_q(q, bt0 + ta, G.Hq, kvh, G.GQ, n, gq, a0, a1);
-            load_q(q, bt0 + tb, G.Hq, kvh, G.GQ, n, gq, b0, b1);
-        };
-        qload(0, qa0, qa1, qb0, qb1);
-        qload(1, ra0, ra1, rb0, rb1);
-        for (int idx = tid; idx < kSbKeys * 8; idx += kClusterThreads) {
-            const int r = idx >> 3, ch = idx & 7;
-            const int key = key_base + r;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (key < nkeys) v = *reinterpret_cast<const u32x4*>(kb + (int64_t)key * row_stride + ch * 8);
-            *reinterpret_cast<lds_u32x4_t*>(lds + sb_lds_offset(r, ch)) = v;
-        }
-        __syncthreads();
-        // one store instruction per unit: lanes 0 / 16 write walk a's two leaves, lanes 32 / 48
-        // walk b's, every other lane (and every lane of an empty unit) writes the sink
-        auto process = [&](int u, const u32x4& a0, const u32x4& a1, const u32x4& b0, const u32x4& b1) {
-            const int ul = min(u, 63);
-            const uint32_t tua = (uint32_t)__builtin_amdgcn_readlane((int)uax, ul);
-            const uint32_t ya = (u < nunits) ? (uint32_t)__builtin_amdgcn_readlane((int)uay, ul) : 0u;
-            const uint32_t tbr = (uint32_t)__builtin_amdgcn_readlane((int)ubx, ul);
-            const uint32_t yb = (u < nunits) ? (uint32_t)__builtin_amdgcn_readlane((int)uby, ul) : 0u;
-            const uint32_t ma = ya & 0xffffu, mb = yb & 0xffffu;
-            const uint32_t tub = mb ? tbr : tua;
-            // walk index (b, t, kvh)
-            const int64_t wa = (bt0 + tua) * G.Hkv + kvh, wb = (bt0 + tub) * G.Hkv + kvh;
-            float v = 0.0f;
-            bool two_a = false, two_b = false;
-            if (ma) {
-                const int b0i = __builtin_ctz(ma);
-                two_a = (ma >> (b0i + 1)) & 1u;
-                two_b = (mb >> (b0i + 1)) & 1u;
-                const int bits[2] = {b0i, b0i + 1 < kSbLeaves ? b0i + 1 : b0i};
-                const int ta = (int)tua, tb = (int)tub;
-                const int k0 = key_base + b0i * kC;
-                const int lim[4] = {min(ta - k0, kC - 1), min(ta - k0 - kC, kC - 1), min(tb - k0, kC - 1),
-                                    min(tb - k0 - kC, kC - 1)};
-                const bf16x8 fa0 = __builtin_bit_cast(bf16x8, a0), fa1 = __builtin_bit_cast(bf16x8, a1);
-                const bf16x8 fb0 = __builtin_bit_cast(bf16x8, b0), fb1 = __builtin_bit_cast(bf16x8, b1);
-                if constexpr (S == kScoreLse)
-                    v = score_unit(lds, bits, lim, fa0, fa1, fb0, fb1, n, gq, G.GQ, mb != 0u);
-                else
-                    v = score_unit_trunc<S>(lds, bits, lim, fa0, fa1, fb0, fb1, n, gq, G.GQ, mb != 0u);
+        const int key0 = pg * kGrpKeys;
+        PairKeys K;
+        load_pair_keys(k + (tk0 * G.Hkv + kvh) * kD, row_stride, key0, nkeys, n, gq, K);
+        for (int base = 0; base < item.z; base += 64) {
+            // lane i holds entry base + i of the item; unit u is entries W*u .. W*u + W - 1
+            const int m = min(64, item.z - base);
+            const uint2 ev = (lane < m) ? entries[item.y + base + lane] : make_uint2(0u, 0u);
+            const int nunits = (m + kW - 1) / kW;
+            // queries of unit u (units past the batch read position 0, a valid row, and score nothing)
+            auto qload = [&](int u, u32x4& a0, u32x4& a1, u32x4& b0, u32x4& b1) {
+                const int la = min(kW * u, 63), lb = (kW == 2 && 2 * u + 1 < m) ? 2 * u + 1 : la;
+                const uint32_t ta = (uint32_t)__builtin_amdgcn_readlane((int)ev.x, la);
+                load_q(q, bt0 + ta, G.Hq, kvh, G.GQ, n, gq, a0, a1);
+                if (kW == 2) {
+                    const uint32_t tb = (uint32_t)__builtin_amdgcn_readlane((int)ev.x, lb);
+                    load_q(q, bt0 + tb, G.Hq, kvh, G.GQ, n, gq, b0, b1);
+                }
+            };
+            // one store instruction per unit: lanes 0 / 16 write walk a's two leaves, lanes 32 / 48
+            // walk b's, every other lane (and every lane of an empty unit) writes the sink
+            auto process = [&](int u, const u32x4& a0, const u32x4& a1, const u32x4& b0, const u32x4& b1) {
+                const int la = min(kW * u, 63), lb = min(kW * u + 1, 63);
+                const uint32_t tua = (uint32_t)__builtin_amdgcn_readlane((int)ev.x, la);
+                const uint32_t ya = (kW * u < m) ? (uint32_t)__builtin_amdgcn_readlane((int)ev.y, la) : 0u;
+                const uint32_t tbr = (kW == 2) ? (uint32_t)__builtin_amdgcn_readlane((int)ev.x, lb) : tua;
+                const uint32_t yb = (kW == 2 && 2 * u + 1 < m) ? (uint32_t)__builtin_amdgcn_readlane((int)ev.y, lb) : 0u;
+                const uint32_t ma = ya & 3u, mb = yb & 3u;
+                const uint32_t tub = mb ? tbr : tua;
+                const int64_t wa = (bt0 + tua) * G.Hkv + kvh, wb = (bt0 + tub) * G.Hkv + kvh;
+                float v = 0.0f;
+                if (ma) {
+                    const int ta = (int)tua, tb = (int)tub;
+                    const int lim[4] = {min(ta - key0, kC - 1), min(ta - key0 - kC, kC - 1), min(tb - key0, kC - 1),
+                                        min(tb - key0 - kC, kC - 1)};
+                    const bf16x8 fa0 = __builtin_bit_cast(bf16x8, a0), fa1 = __builtin_bit_cast(bf16x8, a1);
+                    const bf16x8 fb0 = __builtin_bit_cast(bf16x8, kW == 2 ? b0 : a0);
+                    const bf16x8 fb1 = __builtin_bit_cast(bf16x8, kW == 2 ? b1 : a1);
+                    if constexpr (S == kScoreLse)
+                        v = score_unit(K, lim, fa0, fa1, fb0, fb1, n, gq, G.GQ, mb != 0u);
+                    else
+                        v = score_unit_trunc<S>(K, lim, fa0, fa1, fb0, fb1, n, gq, G.GQ, mb != 0u);
+                }
+                float* dst = wsink;
+                if (lane == 0 && (ma & 1u)) dst = score + wa * CS + (ya >> 16);
+                if (lane == 16 && (ma & 2u)) dst = score + wa * CS + (ya >> 16) + (ma & 1u);
+                if (lane == 32 && (mb & 1u)) dst = score + wb * CS + (yb >> 16);
+                if (lane == 48 && (mb & 2u)) dst = score + wb * CS + (yb >> 16) + (mb & 1u);
+                *dst = v;
+            };
+            u32x4 qa0, qa1, qb0 = {0u, 0u, 0u, 0u}, qb1 = qb0, ra0, ra1, rb0 = qb0, rb1 = qb0;
+            qload(0, qa0, qa1, qb0, qb1);
+            qload(1, ra0, ra1, rb0, rb1);
+            // steady state: a fixed sequence of memory operations per iteration (one store per
+            // unit, four loads per prefetch), so wait counts stay exact across iterations
+            for (int u = 0; u < nunits; u += 2) {
+                process(u, qa0, qa1, qb0, qb1);
+                qload(min(u + 2, 64 / kW), qa0, qa1, qb0, qb1);
+                process(u + 1, ra0, ra1, rb0, rb1);
+                qload(min(u + 3, 64 / kW), ra0, ra1, rb0, rb1);
             }
-            float* dst = sink + wave * 64 + lane;
-            if (lane == 0 && ma) dst = score + wa * CS + (ya >> 16);
-            if (lane == 16 && two_a) dst = score + wa * CS + (ya >> 16) + 1;
-            if (lane == 32 && mb) dst = score + wb * CS + (yb >> 16);
-            if (lane == 48 && two_b) dst = score + wb * CS + (yb >> 16) + 1;
-            *dst = v;
-        };
-        // steady state: a fixed sequence of memory operations per iteration (one store per
-        // unit, four loads per prefetch), so wait counts stay exact across iterations
-        for (int u = 0; u < nunits; u += 2) {
-            process(u, qa0, qa1, qb0, qb1);
-            qload(min(u + 2, 63), qa0, qa1, qb0, qb1);
-            process(u + 1, ra0, ra1, rb0, rb1);
-            qload(min(u + 3, 63), ra0, ra1, rb0, rb1);
         }
     }
 }
 
-#define PISA_LEAF_CLUSTER_INST(S)                                                                         \
-    template __global__ void leaf_cluster_kernel<S>(const uint16_t*, const uint16_t*, Geom, ClusterGeom, Pack, int64_t, \
-                                                    const int4*, const uint2*, uint32_t*, float*, float*);
-PISA_LEAF_CLUSTER_INST(kScoreLse)
-PISA_LEAF_CLUSTER_INST(kScoreMean)
-PISA_LEAF_CLUSTER_INST(kScoreMeanHalfVar)
+#define PISA_LEAF_CLUSTER_INST(S, O)                                                                      \
+    template __global__ void leaf_cluster_kernel<S, O>(const uint16_t*, const uint16_t*, Geom, ClusterGeom, Pack, \
+                                                       int64_t, const int4*, const uint2*, uint32_t*, float*, float*);
+PISA_LEAF_CLUSTER_INST(kScoreLse, false)
+PISA_LEAF_CLUSTER_INST(kScoreMean, false)
+PISA_LEAF_CLUSTER_INST(kScoreMeanHalfVar, false)
+PISA_LEAF_CLUSTER_INST(kScoreLse, true)
+PISA_LEAF_CLUSTER_INST(kScoreMean, true)
+PISA_LEAF_CLUSTER_INST(kScoreMeanHalfVar, true)
 #undef PISA_LEAF_CLUSTER_INST
 
 // Per walk (SLOTS lanes each): at most K candidates are all kept; otherwise the K best

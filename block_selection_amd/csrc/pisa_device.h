@@ -188,24 +188,29 @@ __host__ __device__ inline void upper_cfg_for(const Seg& sg, int topk, UpperCfg&
     U.lds_nodes = slot;
 }
 
-// Clustered leaf scoring (prefill): superblocks of 16 leaves; incidences are
-// bucketed by (batch, KV head, superblock, range of 2^RL query positions), so
-// that each bucket is counted and filled by one workgroup and the entries of one
-// (batch, KV head, superblock) group are contiguous; work items hold at most
-// kItemMax entries of one group, or fewer (down to kItemMin) when a call has too few
-// entries to give every CU several items. Ranges hold 512 positions, or fewer (down
-// to 64) when a call has too few ranges to give every CU a workgroup.
-constexpr int kSbLeaves = 16;
-constexpr int kSbKeys = kSbLeaves * kC;           // 1024 keys
-constexpr int kLog2RangeMax = 9, kLog2RangeMin = 6;
-constexpr int kItemMax = 1024;                     // entries per work item
-constexpr int kItemMin = 256;                      // ... of a call with few entries
-constexpr int kClusterThreads = 1024;
-constexpr int kSbLdsBytes = kSbKeys * kD * 2;      // 128 KiB of bf16 keys
+// Clustered leaf scoring (prefill): incidences are bucketed by (batch, KV head, sibling
+// pair of leaves, range of 2^RL query positions), so that each bucket is counted and
+// filled by one workgroup and the entries of one (batch, KV head, pair) group are
+// contiguous; work items hold at most kItemMax entries of one group, or fewer (down to
+// kItemMin) when a call has too few entries to give every wavefront several items. Ranges
+// hold 1024 positions, or fewer (down to 64) when a call has too few ranges to give every
+// CU a workgroup.
+constexpr int kGrpLeaves = 2;                      // one sibling pair of leaves per group
+constexpr int kGrpKeys = kGrpLeaves * kC;          // 128 keys
+constexpr int kLog2GrpKeys = kLog2C + 1;
+constexpr int kLog2RangeMax = 10, kLog2RangeMin = 6;
+constexpr int kItemMax = 128;                      // entries per work item
+constexpr int kItemMin = 32;                       // ... of a call with few entries
+constexpr int kLeafThreads = 256;                  // independent wavefronts, one work item each
+constexpr int kBinSlice = 16384;                   // bucket-pass bins held in LDS at once (64 KiB)
+constexpr int kItemStreams = 8;                    // item counters of the leaf stage ...
+constexpr int kItemCounter0 = 64;                  // ... at meta[64 + 64 s], 256 bytes apart
+constexpr int kItemCounterStride = 64;
+constexpr int kMetaWords = kItemCounter0 + kItemCounterStride * kItemStreams;
 struct ClusterGeom {
     int32_t NR;      // position ranges per batch element (range slots of a pack)
-    int32_t NSB;     // superblocks per KV head (superblock slots of a pack)
-    int32_t ngroups; // B * Hkv * NSB
+    int32_t NGP;     // pair groups per KV head (pair slots of a pack)
+    int32_t ngroups; // B * Hkv * NGP
     int32_t nb;      // buckets = ngroups * NR
     int32_t RL;      // log2 of the positions per range
 };

@@ -134,10 +134,10 @@ int pisa_build_pyramid(const void* k, int64_t N, int64_t n_capacity, const pisa_
  *   pyramid  as written by pisa_build_pyramid for the same N and n_capacity.
  *   out_idx  int32 [B, N, Hkv, topk]: ascending leaf indices, -1 padded.
  *   workspace at least pisa_workspace_bytes(dims, N, n_capacity, 0) bytes of device memory.
- * bf16 inputs need Hkv * ceil(N / 1024) <= 16384 (the leaf stage counts its
- * (KV head, 1024-key superblock) groups in one LDS histogram): N up to 8388608
- * keys at Hkv = 2. Beyond that the call returns PISA_ERR_UNSUPPORTED and
- * pisa_workspace_bytes returns 0.
+ * bf16 inputs need B * N * Hkv * 2 * topk < 2^32 (the leaf stage numbers its
+ * entries, one per walk and sibling pair of candidate leaves, in 32 bits): N up
+ * to 8388607 keys at Hkv = 8, topk = 32. Beyond that the call returns
+ * PISA_ERR_UNSUPPORTED and pisa_workspace_bytes returns 0.
  * Arithmetic: leaf scores use the exact bf16 (or fp32) q.k products accumulated
  * in fp32; upper-level scores multiply bf16 queries by the fp32 summaries held
  * as a hi + lo pair of bf16 values (relative error <= 2^-17 per element; fp32
@@ -269,7 +269,7 @@ int pisa_build_pyramid_packed(const void* k, const int32_t* cu_seqlens, int64_t 
 
 /*
  * Prefill selection for every row of a pack (bf16 only; fp32 returns
- * PISA_ERR_UNSUPPORTED, as does T with Hkv * ceil(T / 1024) > 16384).
+ * PISA_ERR_UNSUPPORTED, as does T with T * Hkv * 2 * topk >= 2^32).
  *   q        [T, Hq, d] bf16; k [T, Hkv, d] bf16, the keys the pyramid was built from.
  *   pyramid  as written by pisa_build_pyramid_packed for the same cu_seqlens.
  *   out_idx  int32 [T, Hkv, topk]: per row, its document's leaf indices,

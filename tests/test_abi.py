@@ -93,22 +93,23 @@ def test_noalloc_decode_argument_errors_return_before_launch():
     assert step(ops.make_dims(1, 32, 2, 33)) == ops.PISA_ERR_UNSUPPORTED
 
 
-def test_bf16_prefill_beyond_the_cluster_histogram_is_refused():
-    """bf16 selection needs Hkv * ceil(N / 1024) <= 16384 (one LDS histogram of the leaf
-    stage's groups); past it the call returns UNSUPPORTED before any launch and the
-    workspace query returns 0. fp32 selection has no such limit."""
+def test_bf16_prefill_limits_are_the_32_bit_entry_numbering():
+    """bf16 selection numbers the leaf stage's entries in 32 bits: it needs walks * 2K < 2^32
+    (B * N * Hkv walks); past it the call returns UNSUPPORTED before any launch and the
+    workspace query returns 0. The bucket pass's LDS histogram sets no limit of its own
+    (more groups are counted slice by slice), and fp32 selection has no such limit."""
     from block_selection_amd import ops
-    big = 16384 * 1024 // 2                     # Hkv = 2: the largest N that fits
     d = ops.make_dims(1, 32, 2, 8)
-    assert ops.workspace_bytes(d, big) > 0
-    assert ops.workspace_bytes(d, big + 1) == 0
-    assert _call_select(ops, d, N=big, cap=big, ws_bytes=16) == ops.PISA_ERR_WORKSPACE   # passes the limit
-    assert _call_select(ops, d, N=big + 1, cap=big + 1) == ops.PISA_ERR_UNSUPPORTED
-    d16 = ops.make_dims(1, 16, 16, 8)           # Hkv = 16: the limit falls at 1048576 keys
-    assert _call_select(ops, d16, N=1048577, cap=1048577) == ops.PISA_ERR_UNSUPPORTED
-    assert ops.workspace_bytes(d16, 1048576) > 0
-    f32 = ops.make_dims(1, 32, 2, 8, dtype="f32")
-    assert ops.workspace_bytes(f32, big + 1) > 0
+    old_limit = 16384 * 1024 // 2 + 1             # past the 16384-bin histogram of a single pass
+    assert ops.workspace_bytes(d, old_limit) > 0
+    assert _call_select(ops, d, N=old_limit, cap=old_limit, ws_bytes=16) == ops.PISA_ERR_WORKSPACE
+    d8 = ops.make_dims(1, 32, 8, 32)              # Hkv = 8, K = 32: N * 8 * 64 reaches 2^32 at 2^23
+    assert ops.workspace_bytes(d8, (1 << 23) - 1) > 0
+    assert ops.workspace_bytes(d8, 1 << 23) == 0
+    assert _call_select(ops, d8, N=(1 << 23) - 1, cap=(1 << 23) - 1, ws_bytes=16) == ops.PISA_ERR_WORKSPACE
+    assert _call_select(ops, d8, N=1 << 23, cap=1 << 23) == ops.PISA_ERR_UNSUPPORTED
+    f32 = ops.make_dims(1, 32, 8, 32, dtype="f32")
+    assert ops.workspace_bytes(f32, 1 << 23) > 0
 
 
 def test_pack_geometry_helpers():
@@ -147,7 +148,8 @@ def test_pack_argument_errors_return_before_launch():
     assert sel(ops.make_dims(2, 32, 2, 8)) == ops.PISA_ERR_INVALID_ARG
     assert sel(ops.make_dims(1, 32, 2, 8, dtype="f32")) == ops.PISA_ERR_UNSUPPORTED
     assert sel(ops.make_dims(1, 32, 2, 8, d=32)) == ops.PISA_ERR_UNSUPPORTED
-    assert sel(good, T=1 << 24) == ops.PISA_ERR_UNSUPPORTED   # one document's bins exceed LDS
+    assert sel(good, T=1 << 24, ws_bytes=16) == ops.PISA_ERR_WORKSPACE   # within the limits
+    assert sel(good, T=1 << 27) == ops.PISA_ERR_UNSUPPORTED   # T * Hkv * 2K entries reach 2^32
     assert sel(good, ws_bytes=16) == ops.PISA_ERR_WORKSPACE
     assert ops.lib.pisa_build_pyramid_packed(p, None, 3, 4096, ctypes.byref(good), p, None) == ops.PISA_ERR_INVALID_ARG
     assert ops.lib.pisa_build_pyramid_packed(None, p, 3, 4096, ctypes.byref(good), p, None) == ops.PISA_ERR_INVALID_ARG

@@ -75,6 +75,14 @@ def test_prefill_512k_sampled():
     _prefill_case(wl, n_sample=400)
 
 
+def test_prefill_1m_sliced_buckets_sampled():
+    """1048640 positions at Hkv = 2: 16386 (KV head, sibling pair) groups, more than the
+    16384 bins one pass of the leaf stage's bucket histogram holds, so each range is counted
+    and filled in two slices; sampled positions (edges included) against the oracle."""
+    wl = synth.Workload("long1m", N=1048640, Hq=32, Hkv=2, topk=8, dtype="bf16", seed=19)
+    _prefill_case(wl, n_sample=300)
+
+
 @pytest.mark.parametrize("topk", [16, 32])
 def test_prefill_256k_larger_budgets(topk):
     """The headline shape (262144 positions, Hq=32, Hkv=2) at K = 16 and 32 (the budgets
