@@ -39,13 +39,13 @@ __global__ void leaf_walk_kernel(const KT*, const KT*, Geom, int64_t, int64_t, c
 
 template <int SL>
 __global__ void bucket_pass_kernel(const int32_t*, const int32_t*, Geom, ClusterGeom, Pack, const int64_t*, int64_t,
-                                   uint32_t*, const uint32_t*, const uint32_t*, uint2*, int);
+                                   uint32_t*, const uint32_t*, const uint32_t*, uint2*, uint32_t*, int);
 __global__ void pack_plan_kernel(Pack, int, int, int64_t*);
-__global__ void group_offsets_kernel(const uint32_t*, ClusterGeom, Pack, const int64_t*, uint32_t*, uint32_t*);
-__global__ void scan_groups_kernel(const uint32_t*, ClusterGeom, uint32_t, uint32_t*, int4*, uint32_t*);
+__global__ void plan_groups_kernel(const uint32_t*, Geom, ClusterGeom, Pack, const int64_t*, uint32_t, uint32_t,
+                                   uint32_t*, uint32_t*, int4*, uint32_t*);
 template <int S, bool kOneEach>
 __global__ void leaf_cluster_kernel(const uint16_t*, const uint16_t*, Geom, ClusterGeom, Pack, int64_t,
-                                    const int4*, const uint2*, uint32_t*, float*, float*);
+                                    const int4*, uint32_t, const uint2*, uint32_t*, float*, float*);
 
 __global__ void vt_tiles_kernel(const uint16_t*, Geom, Pack, int64_t, uint16_t*);
 __global__ void sparse_attention_kernel(const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*, Geom,
@@ -144,12 +144,12 @@ struct Workspace {
     float* sink;         // [kLeafThreads] stores of lanes without a score
     uint32_t* counts;    // [nb] group-major: bucket (range r, group g) at g * NR + r
     uint32_t* offsets;   // [nb] offset of each bucket inside its group
-    uint32_t* gtot;      // [ngroups] entries per group
     uint32_t* gbase;     // [ngroups] first entry of each group
     uint2* entries;      // [walks * 2K] incidences grouped by bucket
-    int4* items;         // [walks * 2K / kItemMin + ngroups]
+    int4* items;         // [item_cap] full items from the front, remainders from the back
+    uint32_t item_cap;
     uint32_t* meta;      // [0] items, [1] entries, item-stream counters (kMetaWords)
-    int64_t* cbase;      // [D + 1] first count of each document's block (packs only)
+    int64_t* cbase;      // [2D + 2] first count and first plan chunk of each document (packs only)
     // fused bf16 decoding step
     unsigned long long* done;   // [B*Hkv] tagged completion counters (any contents)
     float* leaf_score;   // [B*Hkv][64] leaf scores of one step
@@ -195,10 +195,10 @@ static Workspace carve(const pisa_dims* d, int64_t N, int64_t P, bool decode, ch
         w.sink = (float*)take((size_t)kLeafThreads * sizeof(float));
         w.counts = (uint32_t*)take((size_t)w.CG.nb * 4);
         w.offsets = (uint32_t*)take((size_t)w.CG.nb * 4);
-        w.gtot = (uint32_t*)take((size_t)w.CG.ngroups * 4);
         w.gbase = (uint32_t*)take((size_t)w.CG.ngroups * 4);
         w.entries = (uint2*)take((size_t)walks * cs * sizeof(uint2));
-        w.items = (int4*)take(((size_t)walks * cs / kItemMin + w.CG.ngroups + 1) * sizeof(int4));
+        w.item_cap = (uint32_t)(walks * cs / kItemMin + w.CG.ngroups + 1);
+        w.items = (int4*)take((size_t)w.item_cap * sizeof(int4));
         w.meta = (uint32_t*)take(kMetaWords * sizeof(uint32_t));
     }
     w.bytes = off;
@@ -241,12 +241,12 @@ static Workspace carve_pack(const pisa_dims* d, int64_t T, int64_t D, int64_t P,
     w.sink = (float*)take((size_t)kLeafThreads * sizeof(float));
     w.counts = (uint32_t*)take((size_t)ncount * 4);
     w.offsets = (uint32_t*)take((size_t)ncount * 4);
-    w.gtot = (uint32_t*)take((size_t)w.CG.ngroups * 4);
     w.gbase = (uint32_t*)take((size_t)w.CG.ngroups * 4);
     w.entries = (uint2*)take((size_t)walks * cs * sizeof(uint2));
-    w.items = (int4*)take(((size_t)walks * cs / kItemMin + w.CG.ngroups + 1) * sizeof(int4));
+    w.item_cap = (uint32_t)(walks * cs / kItemMin + w.CG.ngroups + 1);
+    w.items = (int4*)take((size_t)w.item_cap * sizeof(int4));
     w.meta = (uint32_t*)take(kMetaWords * sizeof(uint32_t));
-    w.cbase = (int64_t*)take((size_t)(D + 1) * sizeof(int64_t));
+    w.cbase = (int64_t*)take((size_t)(2 * D + 2) * sizeof(int64_t));
     w.bytes = off;
     return w;
 }
@@ -466,23 +466,30 @@ static int cluster_leaf_stage(const uint16_t* q, const uint16_t* k, const Geom& 
     }
     bins = (bins < (size_t)kBinSlice ? bins : (size_t)kBinSlice) * sizeof(uint32_t);   // LDS bytes
     const int64_t* cbase = W.cbase;
+    // items of L entries: kItemMax, halved (down to kItemMin) while the call's entries, about
+    // K per walk, would make fewer than two items per wavefront the leaf stage keeps resident
+    // (three per SIMD): a short call spreads its scoring over more wavefronts, at the price
+    // of loading a pair's keys for fewer entries
+    uint32_t L = kItemMax;
+    while (L > (uint32_t)kItemMin && (int64_t)walks * G.topk < (int64_t)cus * 24 * L) L >>= 1;
+    // plan workgroups: one per unit of 64 bins (a pack's units, at most Hkv (T / 128 + D) / 64
+    // + D, are counted by its plan), the grid striding past 65536
+    int64_t units = pk.cu ? (int64_t)G.Hkv * (pk.T / kGrpKeys + pk.D) / 64 + pk.D
+                          : (int64_t)G.B * ((G.Hkv * (int64_t)CG.NGP + 63) / 64);
+    const dim3 pgrid((unsigned)(units < 65536 ? units : 65536));
     for (int fill = 0; fill < 2; ++fill) {
-        if (fill) {
-            hipLaunchKernelGGL(group_offsets_kernel, dim3((unsigned)((CG.ngroups + 3) / 4)), dim3(256), 0, s, W.counts,
-                               CG, pk, cbase, W.offsets, W.gtot);
-            // about two items per wavefront the leaf stage keeps resident (3 per SIMD)
-            hipLaunchKernelGGL(scan_groups_kernel, dim3(1), dim3(1024), 0, s, W.gtot, CG, (uint32_t)(cus * 24),
-                               W.gbase, W.items, W.meta);
-        }
+        if (fill)
+            hipLaunchKernelGGL(plan_groups_kernel, pgrid, dim3(64 * kPlanWaves), 0, s, W.counts, G, CG, pk, cbase, L, W.item_cap,
+                               W.offsets, W.gbase, W.items, W.meta);
         if (slots <= 16)
             hipLaunchKernelGGL(bucket_pass_kernel<16>, bgrid, dim3(1024), bins, s, W.cand, W.ncand, G, CG, pk, cbase,
-                               NT, W.counts, W.offsets, W.gbase, W.entries, fill);
+                               NT, W.counts, W.offsets, W.gbase, W.entries, W.meta, fill);
         else if (slots <= 32)
             hipLaunchKernelGGL(bucket_pass_kernel<32>, bgrid, dim3(1024), bins, s, W.cand, W.ncand, G, CG, pk, cbase,
-                               NT, W.counts, W.offsets, W.gbase, W.entries, fill);
+                               NT, W.counts, W.offsets, W.gbase, W.entries, W.meta, fill);
         else
             hipLaunchKernelGGL(bucket_pass_kernel<64>, bgrid, dim3(1024), bins, s, W.cand, W.ncand, G, CG, pk, cbase,
-                               NT, W.counts, W.offsets, W.gbase, W.entries, fill);
+                               NT, W.counts, W.offsets, W.gbase, W.entries, W.meta, fill);
     }
     // persistent wavefronts: as many workgroups as fit the CUs at once. A short call (at most
     // about two items of kItemMin entries per wavefront, counting K entries per walk) gives
@@ -496,7 +503,7 @@ static int cluster_leaf_stage(const uint16_t* q, const uint16_t* k, const Geom& 
         const int4* items = W.items;
         const uint2* entries = W.entries;
         void* args[] = {(void*)&q, (void*)&k, (void*)&G, (void*)&CG, (void*)&pk, (void*)&NT, (void*)&items,
-                        (void*)&entries, (void*)&W.meta, (void*)&W.score, (void*)&W.sink};
+                        (void*)&W.item_cap, (void*)&entries, (void*)&W.meta, (void*)&W.score, (void*)&W.sink};
         if (hipLaunchKernel(leaf_fn, dim3((unsigned)(cus * per_cu)), dim3(kLeafThreads), args, 0, s) != hipSuccess)
             return PISA_ERR_HIP;
     }

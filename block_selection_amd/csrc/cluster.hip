@@ -6,23 +6,23 @@
 // LogSumExp" and section 4.1). The pages' prefill kernel clusters queries that
 // need the same candidate key block so each loaded block is reused (ai4snews
 // summary, second paragraph; reading note section 5.1). Here the cluster is a
-// 16-leaf superblock (1024 keys, 128 KiB of bf16 per KV head, held in LDS) and
-// its group of walks:
+// sibling pair of leaves (128 keys, 16 KiB of bf16 per KV head, held in one
+// wavefront's registers) and the walks that score it:
 //   1. bucket_pass (count): one incidence per sibling pair of a walk's leaf
-//      candidates inside a superblock, counted per bucket (batch, KV head,
-//      superblock, range of query positions) in an LDS histogram;
-//   2. group_offsets: per (batch, KV head, superblock) group, one wavefront scans
-//      its ranges' counts (bucket offsets inside the group, group total);
-//      scan_groups: group offsets and work items of at most kItemMax entries of
-//      one group (fewer for a short call);
+//      candidates, counted per bucket (batch, KV head, pair, range of query
+//      positions) in an LDS histogram;
+//   2. plan_groups: per (batch, KV head, pair) group, the scan of its ranges'
+//      counts (bucket offsets inside the group, group total), its place in the
+//      entry array and its work items of at most L entries;
 //   3. bucket_pass (fill): incidences written as entries at their offsets;
-//   4. leaf_cluster: persistent workgroups take items from a counter; a workgroup stages the
-//      superblock's keys in LDS once, then each wavefront takes entries (the
-//      next entry's queries are prefetched while the current one is scored)
-//      and scores every leaf of the entry's mask from LDS;
+//   4. leaf_cluster: persistent wavefronts, each on its own, take items from
+//      counters; a wavefront loads the item's pair of leaves into registers as
+//      MFMA A fragments once, then scores the item's entries two walks at a time
+//      (the next two walks' queries are prefetched while the current ones are
+//      scored);
 //   5. final_topk: per walk, the K best leaf candidates in ascending order.
-// Per incidence the walk's queries (2 KiB) are read once; the keys of a
-// superblock are read from memory once per work item.
+// Per incidence the walk's queries (2 KiB) are read once; the keys of a pair are
+// read from memory once per work item.
 #include <type_traits>
 
 #include "walk_math.h"
@@ -33,18 +33,20 @@ namespace pisa {
 // query positions of batch element blockIdx.y (range blockIdx.x). One incidence per
 // sibling pair of a walk's leaf candidates (the children of one level-2 survivor); a
 // walk with at most K candidates has none (its candidates are all kept). The workgroup owns the
-// buckets (b, kvh, sb, r) of its range: an LDS histogram counts them, and in the fill
+// buckets (b, kvh, pair, r) of its range: an LDS histogram counts them, and in the fill
 // pass the same bins, seeded with the bucket offsets, hand out entry positions.
-// Entry = {query position t, leaf mask | first slot << 16}: the mask holds the superblock
+// Entry = {query position t, leaf mask | first slot << 16}: the mask holds the pair
 // offsets of one leaf or of a sibling pair (batch element and KV head are the bucket's).
-// Counts and offsets are group-major: bucket (range r, group g) at g * NR + r; the fill
-// pass starts bucket (r, g) at gbase[g] + offsets[g * NR + r]. The bins live in LDS
-// kBinSlice at a time (a sequence with more groups is counted slice by slice).
+// Counts and offsets are range-major per sequence: bucket (range r, bin x) of batch element
+// b at (b * NR + r) * nbins + x, so that a workgroup reads and writes one contiguous row;
+// the fill pass starts bucket (r, x) at gbase[g] + offsets[...] (g: the bin's group). The
+// bins live in LDS kBinSlice at a time (a sequence with more groups is counted slice by
+// slice). The count pass also clears the counters in meta that the later kernels use.
 // With a pack (pk.cu non-null) blockIdx.x is a range slot of the packed layout: range j of
 // one document d (or nothing), positions t count from the document's start, and the
 // workgroup's bins are the document's own groups, x = kvh * nsb_d + s (pair s of the
 // document is pair slot (cu[d] >> 7) + d + s, group kvh * CG.NGP + that slot). Its counts
-// sit in the document's block at cbase[d] + x * nr_d + j (nr_d ranges).
+// sit in the document's block at cbase[d] + j * nbins_d + x.
 template <int SL>
 __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __restrict__ cand,
                                                           const int32_t* __restrict__ ncand, Geom G,
@@ -52,8 +54,13 @@ __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __rest
                                                           int64_t NT, uint32_t* __restrict__ counts,
                                                           const uint32_t* __restrict__ offsets,
                                                           const uint32_t* __restrict__ gbase,
-                                                          uint2* __restrict__ entries, int fill) {
+                                                          uint2* __restrict__ entries, uint32_t* __restrict__ meta,
+                                                          int fill) {
     extern __shared__ uint32_t bins[];
+    // the count pass clears the counters of the plan and of the leaf stage (before any exit)
+    if (!fill && blockIdx.x == 0 && blockIdx.y == 0) {
+        for (int i = threadIdx.x; i < kMetaWords; i += blockDim.x) meta[i] = 0u;
+    }
     constexpr int WPW = 64 / SL;
     const int r = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, seg = lane / SL, i = lane % SL;
@@ -61,7 +68,7 @@ __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __rest
     const int nthr = blockDim.x, nw = nthr >> 6;
     int64_t bt0, t_lo, t_hi;   // first query row of the sequence, positions [t_lo, t_hi)
     int nsb;                   // pair groups per KV head in the bins: x = kvh * nsb + s
-    int64_t g_sb0, c0, c_str;  // bin x -> group (x / nsb) * CG.NGP + g_sb0 + x % nsb; count c0 + x * c_str
+    int64_t g_sb0, c0;         // bin x -> group (x / nsb) * CG.NGP + g_sb0 + x % nsb; count c0 + x
     if (pk.cu) {
         const int d = pack_find_slot(pk, CG.RL, r);
         const Seg sg = pack_seg(pk, d);
@@ -73,8 +80,7 @@ __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __rest
         t_hi = (t_lo + (1 << CG.RL) < sg.N) ? t_lo + (1 << CG.RL) : sg.N;
         nsb = (int)((sg.N + kGrpKeys - 1) / kGrpKeys);
         g_sb0 = (sg.lsh >> (kLog2GrpKeys)) + d;
-        c0 = cbase[d] + j;
-        c_str = nr;
+        c0 = cbase[d] + j * (int64_t)(G.Hkv * nsb);
     } else {
         const int b = blockIdx.y;
         bt0 = (int64_t)b * NT;
@@ -82,8 +88,7 @@ __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __rest
         t_hi = (t_lo + (1 << CG.RL) < NT) ? t_lo + (1 << CG.RL) : NT;
         nsb = CG.NGP;
         g_sb0 = (int64_t)b * G.Hkv * CG.NGP;
-        c0 = g_sb0 * CG.NR + r;
-        c_str = CG.NR;
+        c0 = ((int64_t)b * CG.NR + r) * (G.Hkv * CG.NGP);
     }
     // the bins are held in LDS kBinSlice at a time; a longer sequence's range is read once per slice
     const int nbins = G.Hkv * nsb;
@@ -92,42 +97,55 @@ __global__ __launch_bounds__(1024) void bucket_pass_kernel(const int32_t* __rest
     if (x0) __syncthreads();   // the previous slice's counts are written out
     for (int x = tid; x < nx; x += nthr) {
         const int64_t g = (int64_t)((x0 + x) / nsb) * CG.NGP + g_sb0 + (x0 + x) % nsb;
-        bins[x] = fill ? gbase[g] + offsets[c0 + (int64_t)(x0 + x) * c_str] : 0u;
+        bins[x] = fill ? gbase[g] + offsets[c0 + x0 + x] : 0u;
     }
     __syncthreads();
     const int64_t w_lo = (bt0 + t_lo) * G.Hkv, w_hi = (bt0 + t_hi) * G.Hkv;
-    for (int64_t w0 = w_lo + (int64_t)(tid >> 6) * WPW; w0 < w_hi; w0 += (int64_t)nw * WPW) {
-        const int64_t w = w0 + seg;
-        const bool ok = w < w_hi;
-        const int nc = ok ? ncand[w] : 0;
-        const int leaf = (ok && i < CS && i < nc) ? cand[w * CS + i] : -1;
-        const int kvh = (int)(w % G.Hkv);
-        const int sbv = (leaf >= 0) ? leaf / kGrpLeaves : -1;
-        // candidates ascend and come as sibling pairs (2c, then 2c+1 if eligible): an entry
-        // starts at an even leaf, or at an odd one whose sibling is not a candidate
-        const int prv = shfl_i(leaf, lane > 0 ? lane - 1 : 0);
-        const int nxt = shfl_i(leaf, lane < 63 ? lane + 1 : lane);
-        const bool even = (leaf & 1) == 0;
-        const bool start = nc > K && leaf >= 0 && (even || i == 0 || prv != leaf - 1);
-        const bool pair = even && i + 1 < SL && nxt == leaf + 1;
-        const uint32_t m = (leaf >= 0) ? ((pair ? 3u : 1u) << (leaf % kGrpLeaves)) : 0u;
-        const int bx = kvh * nsb + sbv - x0;
-        if (start && bx >= 0 && bx < nx) {
-            const uint32_t pos = atomicAdd(&bins[bx], 1u);
-            if (fill) entries[pos] = make_uint2((uint32_t)(w / G.Hkv - bt0), m | ((uint32_t)i << 16));
+    // kBucketUnroll rounds of walks per loop trip, their loads issued together
+    const int64_t step = (int64_t)nw * WPW;
+    for (int64_t w0 = w_lo + (int64_t)(tid >> 6) * WPW; w0 < w_hi; w0 += kBucketUnroll * step) {
+        int nc[kBucketUnroll], leafv[kBucketUnroll];
+#pragma unroll
+        for (int u = 0; u < kBucketUnroll; ++u) {
+            const int64_t w = w0 + u * step + seg;
+            const bool ok = w < w_hi;
+            nc[u] = ok ? ncand[w] : 0;
+            leafv[u] = (ok && i < CS) ? cand[w * CS + i] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kBucketUnroll; ++u) {
+            const int64_t w = w0 + u * step + seg;
+            const int leaf = (i < nc[u]) ? leafv[u] : -1;
+            const int kvh = (int)(w % G.Hkv);
+            const int sbv = (leaf >= 0) ? leaf / kGrpLeaves : -1;
+            // candidates ascend and come as sibling pairs (2c, then 2c+1 if eligible): an entry
+            // starts at an even leaf, or at an odd one whose sibling is not a candidate
+            const int prv = shfl_i(leaf, lane > 0 ? lane - 1 : 0);
+            const int nxt = shfl_i(leaf, lane < 63 ? lane + 1 : lane);
+            const bool even = (leaf & 1) == 0;
+            const bool start = nc[u] > K && leaf >= 0 && (even || i == 0 || prv != leaf - 1);
+            const bool pair = even && i + 1 < SL && nxt == leaf + 1;
+            const uint32_t m = (leaf >= 0) ? ((pair ? 3u : 1u) << (leaf % kGrpLeaves)) : 0u;
+            const int bx = kvh * nsb + sbv - x0;
+            if (start && bx >= 0 && bx < nx) {
+                const uint32_t pos = atomicAdd(&bins[bx], 1u);
+                if (fill) entries[pos] = make_uint2((uint32_t)(w / G.Hkv - bt0), m | ((uint32_t)i << 16));
+            }
         }
     }
     __syncthreads();
     if (!fill) {
-        for (int x = tid; x < nx; x += nthr) counts[c0 + (int64_t)(x0 + x) * c_str] = bins[x];
+        for (int x = tid; x < nx; x += nthr) counts[c0 + x0 + x] = bins[x];
     }
     }
 }
 
 // Pack plan (one workgroup): cbase[d] = first count of document d's block (KV heads x its
-// superblocks x its ranges), an exclusive scan over the documents; cbase[D] = the total.
+// pairs x its ranges), an exclusive scan over the documents, cbase[D] = the total; and
+// cbase[D + 1 + d] = the first 64-bin chunk of document d in the flat chunk space of the
+// plan, cbase[2D + 1] = the number of chunks.
 __global__ __launch_bounds__(1024) void pack_plan_kernel(Pack pk, int Hkv, int RL, int64_t* __restrict__ cbase) {
-    __shared__ int64_t s_sum[1024];
+    __shared__ int64_t s_sum[1024], s_chk[1024];
     const int tid = threadIdx.x;
     const int per = (pk.D + 1023) / 1024;
     const int lo = tid * per, hi = min(pk.D, lo + per);
@@ -135,139 +153,158 @@ __global__ __launch_bounds__(1024) void pack_plan_kernel(Pack pk, int Hkv, int R
         const Seg sg = pack_seg(pk, d);
         return sg.N ? (int64_t)Hkv * ((sg.N + kGrpKeys - 1) / kGrpKeys) * (((sg.N - 1) >> RL) + 1) : 0;
     };
-    int64_t acc = 0;
-    for (int d = lo; d < hi; ++d) acc += size_of(d);
+    auto chunks_of = [&](int d) -> int64_t {
+        const Seg sg = pack_seg(pk, d);
+        return sg.N ? ((int64_t)Hkv * ((sg.N + kGrpKeys - 1) / kGrpKeys) + 63) / 64 : 0;
+    };
+    int64_t acc = 0, acc_c = 0;
+    for (int d = lo; d < hi; ++d) {
+        acc += size_of(d);
+        acc_c += chunks_of(d);
+    }
     s_sum[tid] = acc;
+    s_chk[tid] = acc_c;
     __syncthreads();
-    for (int st = 1; st < 1024; st <<= 1) {   // inclusive Hillis-Steele scan
+    for (int st = 1; st < 1024; st <<= 1) {   // inclusive Hillis-Steele scans
         const int64_t add = (tid >= st) ? s_sum[tid - st] : 0;
+        const int64_t add_c = (tid >= st) ? s_chk[tid - st] : 0;
         __syncthreads();
         s_sum[tid] += add;
+        s_chk[tid] += add_c;
         __syncthreads();
     }
-    int64_t run = s_sum[tid] - acc;
+    int64_t run = s_sum[tid] - acc, run_c = s_chk[tid] - acc_c;
     for (int d = lo; d < hi; ++d) {
         cbase[d] = run;
         run += size_of(d);
-    }
-    if (tid == 1023) cbase[pk.D] = s_sum[1023];
-}
-
-// One wavefront per group g: the exclusive scan of its ranges' counts (the offset of
-// each bucket inside the group) and the group's total. Grid: ceil(ngroups / 4)
-// workgroups of 4 wavefronts. With a pack, group g = kvh * CG.NGP + superblock slot; a
-// slot that names no superblock of a document has total 0.
-__global__ __launch_bounds__(256) void group_offsets_kernel(const uint32_t* __restrict__ counts, ClusterGeom CG,
-                                                            Pack pk, const int64_t* __restrict__ cbase,
-                                                            uint32_t* __restrict__ offsets,
-                                                            uint32_t* __restrict__ gtot) {
-    const int lane = threadIdx.x & 63;
-    const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (g >= CG.ngroups) return;   // whole wavefronts leave together
-    int64_t c0 = g * CG.NR;
-    int nr = CG.NR;
-    if (pk.cu) {
-        const int kvh = (int)(g / CG.NGP);
-        const int64_t slot = g % CG.NGP;
-        const int d = pack_find_slot(pk, kLog2GrpKeys, slot);
-        const Seg sg = pack_seg(pk, d);
-        const int64_t s = slot - ((sg.lsh >> (kLog2GrpKeys)) + d);
-        const int64_t nsb = (sg.N + kGrpKeys - 1) / kGrpKeys;
-        if (sg.N == 0 || s < 0 || s >= nsb) {
-            if (lane == 0) gtot[g] = 0u;
-            return;
-        }
-        nr = (int)(((sg.N - 1) >> CG.RL) + 1);
-        c0 = cbase[d] + (kvh * nsb + s) * nr;
-    }
-    const uint32_t* c = counts + c0;
-    uint32_t* o = offsets + c0;
-    uint32_t run = 0;
-    for (int r0 = 0; r0 < nr; r0 += 64) {
-        const int r = r0 + lane;
-        const uint32_t v = (r < nr) ? c[r] : 0u;
-        uint32_t x = v;   // inclusive scan over the wavefront
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t y = (uint32_t)shfl_i((int)x, lane >= d ? lane - d : lane);
-            x += (lane >= d) ? y : 0u;
-        }
-        if (r < nr) o[r] = run + x - v;
-        run += (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
-    }
-    if (lane == 0) gtot[g] = run;
-}
-
-// One workgroup: the entry offset of every group (groups in order) and work items of at
-// most L entries of one group. L is kItemMax, halved (down to kItemMin) while the call's
-// entries would make fewer than min_items items of L: a short sequence then spreads its
-// scoring over more wavefronts, at the price of loading a pair's keys for fewer entries.
-// Items holding L entries come first, the smaller remainders after them, so that the
-// wavefronts taking items in order finish together. meta[0] = number of items, meta[1] =
-// number of entries, and the kItemStreams counters the scoring wavefronts take items from
-// are set to 0.
-__global__ __launch_bounds__(1024) void scan_groups_kernel(const uint32_t* __restrict__ gtot, ClusterGeom CG,
-                                                           uint32_t min_items, uint32_t* __restrict__ gbase,
-                                                           int4* __restrict__ items,
-                                                           uint32_t* __restrict__ meta) {
-    __shared__ uint32_t s_e[1024], s_f[1024], s_p[1024];
-    const int tid = threadIdx.x;
-    const int per = (CG.ngroups + 1023) / 1024;
-    const int lo = tid * per, hi = min(CG.ngroups, lo + per);
-    uint32_t se = 0;
-    for (int g = lo; g < hi; ++g) se += gtot[g];
-    s_e[tid] = se;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {       // inclusive Hillis-Steele scan of the entry counts
-        const uint32_t ae = (tid >= d) ? s_e[tid - d] : 0u;
-        __syncthreads();
-        s_e[tid] += ae;
-        __syncthreads();
-    }
-    const uint32_t total = s_e[1023];
-    uint32_t L = kItemMax;
-    while (L > (uint32_t)kItemMin && (uint64_t)total < (uint64_t)min_items * L) L >>= 1;
-    uint32_t sf = 0, sp = 0;
-    for (int g = lo; g < hi; ++g) {
-        const uint32_t tot = gtot[g];
-        sf += tot / L;                  // full items
-        sp += (tot % L) ? 1u : 0u;      // remainder item
-    }
-    s_f[tid] = sf;
-    s_p[tid] = sp;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {       // the same scan of the item counts
-        const uint32_t af = (tid >= d) ? s_f[tid - d] : 0u;
-        const uint32_t ap = (tid >= d) ? s_p[tid - d] : 0u;
-        __syncthreads();
-        s_f[tid] += af;
-        s_p[tid] += ap;
-        __syncthreads();
-    }
-    const uint32_t nfull = s_f[1023];
-    uint32_t eoff = s_e[tid] - se, foff = s_f[tid] - sf, poff = nfull + s_p[tid] - sp;
-    for (int g = lo; g < hi; ++g) {
-        const uint32_t g0 = eoff, tot = gtot[g];
-        gbase[g] = g0;
-        eoff += tot;
-        for (uint32_t p = 0; p * L < tot; ++p) {
-            const uint32_t len = min(L, tot - p * L);
-            items[(len == L) ? foff++ : poff++] = make_int4(g, (int)(g0 + p * L), (int)len, 0);
-        }
+        cbase[pk.D + 1 + d] = run_c;
+        run_c += chunks_of(d);
     }
     if (tid == 1023) {
-        meta[0] = nfull + s_p[1023];
-        meta[1] = total;
+        cbase[pk.D] = s_sum[1023];
+        cbase[2 * pk.D + 1] = s_chk[1023];
     }
-    if (tid < kItemStreams) meta[kItemCounter0 + kItemCounterStride * tid] = 0u;
+}
+
+// Plan of the leaf stage: a work unit is 64 consecutive bins x (groups) of one sequence (a
+// batch element, or a document of a pack), one workgroup (4 wavefronts) per unit, the grid
+// striding over the units. For each group: the exclusive scan
+// of its ranges' counts (the offset of each bucket inside the group; wavefront w scans a
+// quarter of the ranges), its total, its first entry gbase (wavefront 0 places its 64
+// groups with one atomic on the entry counter), and its work items of at most L entries:
+// the full ones at the front of the item array (from position meta[kMetaFront]), the
+// remainder at the back (position item_cap - 1 - k, k from meta[kMetaBack]), so that the
+// wavefronts taking items in order score the small remainders last.
+__global__ __launch_bounds__(64 * kPlanWaves) void plan_groups_kernel(const uint32_t* __restrict__ counts, Geom G, ClusterGeom CG,
+                                                          Pack pk, const int64_t* __restrict__ cbase, uint32_t L,
+                                                          uint32_t item_cap, uint32_t* __restrict__ offsets,
+                                                          uint32_t* __restrict__ gbase, int4* __restrict__ items,
+                                                          uint32_t* __restrict__ meta) {
+    __shared__ uint32_t s_part[kPlanWaves][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // work units: (sequence, chunk of 64 bins); a batch element has nchunks of them, a
+    // document of a pack its own number (the flat chunk space of the pack plan)
+    const int nchunks = (int)((G.Hkv * (int64_t)CG.NGP + 63) / 64);
+    const int64_t nunits = pk.cu ? cbase[2 * pk.D + 1] : (int64_t)G.B * nchunks;
+    for (int64_t unit = blockIdx.x; unit < nunits; unit += gridDim.x) {   // workgroup-uniform
+        int nsb, nr, chunk;
+        int64_t cb, g_sb0;   // the sequence's first count; bin x -> group (x / nsb) * CG.NGP + g_sb0 + x % nsb
+        if (pk.cu) {
+            const int64_t* cpre = cbase + pk.D + 1;
+            int lo = 0, hi = pk.D - 1;   // the last document whose first chunk is <= unit
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (cpre[mid] <= unit) lo = mid;
+                else hi = mid - 1;
+            }
+            const int q = lo;
+            const Seg sg = pack_seg(pk, q);
+            chunk = (int)(unit - cpre[q]);
+            nsb = (int)((sg.N + kGrpKeys - 1) / kGrpKeys);
+            nr = (int)(((sg.N - 1) >> CG.RL) + 1);
+            cb = cbase[q];
+            g_sb0 = (sg.lsh >> kLog2GrpKeys) + q;
+        } else {
+            const int q = (int)(unit / nchunks);
+            chunk = (int)(unit % nchunks);
+            nsb = CG.NGP;
+            nr = CG.NR;
+            cb = (int64_t)q * CG.NR * (G.Hkv * CG.NGP);
+            g_sb0 = (int64_t)q * G.Hkv * CG.NGP;
+        }
+        const int nbins = G.Hkv * nsb;
+        const int x = chunk * 64 + lane;
+        const bool ok = x < nbins;
+        const int r0 = (int)((int64_t)nr * wave / kPlanWaves), r1 = (int)((int64_t)nr * (wave + 1) / kPlanWaves);
+        uint32_t part = 0;
+        if (ok) {
+            for (int r = r0; r < r1; ++r) part += counts[cb + (int64_t)r * nbins + x];
+        }
+        s_part[wave][lane] = part;
+        __syncthreads();
+        uint32_t run = 0, tot = 0;
+#pragma unroll
+        for (int w = 0; w < kPlanWaves; ++w) {
+            const uint32_t pw = s_part[w][lane];
+            run += (w < wave) ? pw : 0u;
+            tot += pw;
+        }
+        __syncthreads();   // s_part is read by every wavefront before the next sequence writes it
+        if (ok) {
+            for (int r = r0; r < r1; ++r) {
+                const int64_t c = cb + (int64_t)r * nbins + x;
+                const uint32_t v = counts[c];
+                offsets[c] = run;
+                run += v;
+            }
+        }
+        if (wave == 0) {
+            // place the 64 groups' entries and items
+            const uint32_t te = ok ? tot : 0u;
+            const uint32_t nf = te / L, np = (te % L) ? 1u : 0u;
+            uint32_t ie = te, i_f = nf, ip = np;   // inclusive scans over the wavefront
+#pragma unroll
+            for (int dd = 1; dd < 64; dd <<= 1) {
+                const int src = lane >= dd ? lane - dd : lane;
+                const uint32_t ye = (uint32_t)shfl_i((int)ie, src), yf = (uint32_t)shfl_i((int)i_f, src);
+                const uint32_t yp = (uint32_t)shfl_i((int)ip, src);
+                ie += (lane >= dd) ? ye : 0u;
+                i_f += (lane >= dd) ? yf : 0u;
+                ip += (lane >= dd) ? yp : 0u;
+            }
+            // the wavefront totals are read with every lane active (a cross-lane read inside the
+            // lane-0 branch below would see lane 63 as it was before the branch)
+            const uint32_t te_w = (uint32_t)__builtin_amdgcn_readlane((int)ie, 63);
+            const uint32_t nf_w = (uint32_t)__builtin_amdgcn_readlane((int)i_f, 63);
+            const uint32_t np_w = (uint32_t)__builtin_amdgcn_readlane((int)ip, 63);
+            uint32_t eb = 0u, fb = 0u, pb = 0u;
+            if (lane == 0) {
+                eb = atomicAdd(&meta[kMetaEntries], te_w);
+                fb = atomicAdd(&meta[kMetaFront], nf_w);
+                pb = atomicAdd(&meta[kMetaBack], np_w);
+            }
+            eb = (uint32_t)__builtin_amdgcn_readlane((int)eb, 0);
+            fb = (uint32_t)__builtin_amdgcn_readlane((int)fb, 0);
+            pb = (uint32_t)__builtin_amdgcn_readlane((int)pb, 0);
+            if (ok) {
+                const int64_t g = (int64_t)(x / nsb) * CG.NGP + g_sb0 + x % nsb;
+                const uint32_t g0 = eb + ie - te;
+                gbase[g] = g0;
+                const uint32_t f0 = fb + i_f - nf;
+                for (uint32_t k = 0; k < nf; ++k) items[f0 + k] = make_int4((int)g, (int)(g0 + k * L), (int)L, 0);
+                if (np)
+                    items[item_cap - 1u - (pb + ip - np)] = make_int4((int)g, (int)(g0 + nf * L), (int)(te - nf * L), 0);
+            }
+        }
+    }
 }
 
 template __global__ void bucket_pass_kernel<16>(const int32_t*, const int32_t*, Geom, ClusterGeom, Pack, const int64_t*, int64_t,
-                                                uint32_t*, const uint32_t*, const uint32_t*, uint2*, int);
+                                                uint32_t*, const uint32_t*, const uint32_t*, uint2*, uint32_t*, int);
 template __global__ void bucket_pass_kernel<32>(const int32_t*, const int32_t*, Geom, ClusterGeom, Pack, const int64_t*, int64_t,
-                                                uint32_t*, const uint32_t*, const uint32_t*, uint2*, int);
+                                                uint32_t*, const uint32_t*, const uint32_t*, uint2*, uint32_t*, int);
 template __global__ void bucket_pass_kernel<64>(const int32_t*, const int32_t*, Geom, ClusterGeom, Pack, const int64_t*, int64_t,
-                                                uint32_t*, const uint32_t*, const uint32_t*, uint2*, int);
+                                                uint32_t*, const uint32_t*, const uint32_t*, uint2*, uint32_t*, int);
 
 // Key fragments of one sibling pair, held in registers for a whole work item: f[j][tau][h]
 // is the MFMA A operand of leaf j's 16-key tile tau in lane (gq, n): key 16 tau + n of the
@@ -471,14 +508,16 @@ __device__ inline void load_q(const uint16_t* __restrict__ q, int64_t bt, int Hq
 template <int S, bool kOneEach>
 __global__ __launch_bounds__(kLeafThreads) void leaf_cluster_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, Geom G, ClusterGeom CG, Pack pk, int64_t NT,
-    const int4* __restrict__ items, const uint2* __restrict__ entries, uint32_t* __restrict__ meta,
-    float* __restrict__ score, float* __restrict__ sink) {
+    const int4* __restrict__ items, uint32_t item_cap, const uint2* __restrict__ entries,
+    uint32_t* __restrict__ meta, float* __restrict__ score, float* __restrict__ sink) {
     static_assert(kItemMax % 64 == 0, "an item is scored in whole batches of 64 entries");
     constexpr int kW = 2;   // walks per unit (one walk per unit at four wavefronts per SIMD measured slower)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, gq = lane >> 4;
     const int CS = 2 * G.topk;
-    const uint32_t n_items = meta[0];
+    // items 0 .. n_front - 1 at the front of the array, then the remainders from its back
+    const uint32_t n_front = meta[kMetaFront];
+    const uint32_t n_items = n_front + meta[kMetaBack];
     const int64_t row_stride = (int64_t)G.Hkv * kD;
     float* const wsink = sink + wave * 64 + lane;
 
@@ -507,7 +546,7 @@ __global__ __launch_bounds__(kLeafThreads) void leaf_cluster_kernel(
                 continue;
             }
         }
-        const int4 item = items[it];
+        const int4 item = items[it < n_front ? it : item_cap - 1u - (it - n_front)];
         const int grp = item.x;
         const int gs = grp % CG.NGP;
         const int kvh = (grp / CG.NGP) % G.Hkv;
@@ -594,7 +633,8 @@ __global__ __launch_bounds__(kLeafThreads) void leaf_cluster_kernel(
 
 #define PISA_LEAF_CLUSTER_INST(S, O)                                                                      \
     template __global__ void leaf_cluster_kernel<S, O>(const uint16_t*, const uint16_t*, Geom, ClusterGeom, Pack, \
-                                                       int64_t, const int4*, const uint2*, uint32_t*, float*, float*);
+                                                       int64_t, const int4*, uint32_t, const uint2*, uint32_t*, float*, \
+                                                       float*);
 PISA_LEAF_CLUSTER_INST(kScoreLse, false)
 PISA_LEAF_CLUSTER_INST(kScoreMean, false)
 PISA_LEAF_CLUSTER_INST(kScoreMeanHalfVar, false)

@@ -90,7 +90,7 @@ __host__ __device__ inline Seg batch_seg(int64_t N, int64_t tk0) {
 // (cu[d] >> (5 + l)) + d. These starts increase with d by at least the node count, so the
 // documents never overlap, and they are found from cu alone. The same "slot" rule at other
 // granularities (2^s tokens: slot of (d, j) = (cu[d] >> s) + d + j) numbers per-document
-// work units (16-leaf subtrees, superblocks, position ranges) in one flat space.
+// work units (16-leaf subtrees, sibling pairs of leaves, position ranges) in one flat space.
 struct Pack {
     const int32_t* cu;
     int32_t D;
@@ -203,8 +203,13 @@ constexpr int kItemMax = 128;                      // entries per work item
 constexpr int kItemMin = 32;                       // ... of a call with few entries
 constexpr int kLeafThreads = 256;                  // independent wavefronts, one work item each
 constexpr int kBinSlice = 16384;                   // bucket-pass bins held in LDS at once (64 KiB)
-constexpr int kItemStreams = 8;                    // item counters of the leaf stage ...
-constexpr int kItemCounter0 = 64;                  // ... at meta[64 + 64 s], 256 bytes apart
+constexpr int kBucketUnroll = 4;                   // rounds of walks per bucket-pass loop trip
+constexpr int kPlanWaves = 16;                     // wavefronts of a plan workgroup
+// meta words of the leaf stage: items at the front / back of the item array, entries
+// placed, then kItemStreams item counters at meta[64 + 64 s], 256 bytes apart
+constexpr int kMetaFront = 0, kMetaEntries = 1, kMetaBack = 2;
+constexpr int kItemStreams = 8;
+constexpr int kItemCounter0 = 64;
 constexpr int kItemCounterStride = 64;
 constexpr int kMetaWords = kItemCounter0 + kItemCounterStride * kItemStreams;
 struct ClusterGeom {

@@ -487,7 +487,9 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
                 if (in_lds) return rows_lds(lds, lds_lvl + row, gq);
                 return rows_buffer(dhi, dlo, row, gq);
             };
-            float F = 0.0f, D = 0.0f;
+            // each tile's in-lane head parts, then one exchange pattern leaves lane (gq, n)
+            // with the sums of tile gq, column n
+            float fp[NTILE], xp[NTILE];
             int row0;
             uint32_t rvm = pick(0, row0);
             TileRows cur = fetch(row0);
@@ -501,15 +503,12 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
                     nxt = fetch(rown);
                 }
                 const f32x4 acc = summary_tile_mfma(qf[i / TPW].k0, qf[i / TPW].k1, cur.h0, cur.h1, cur.l0, cur.l1);
-                float Ft, Dt;
-                delta_tile_sums<S>(acc, rvm, n, gq, G.GQ, Ft, Dt);
-                if (u == i) {
-                    F = Ft;
-                    D = Dt;
-                }
+                delta_tile_parts<S>(acc, rvm, n, gq, G.GQ, fp[i], xp[i]);
                 cur = nxt;
                 rvm = rvm_next;
             }
+            float F, D;
+            delta_sums4(fp, xp, F, D);
             score = P + F;
             Pa = P + D;
             Pb = P - D;

@@ -161,14 +161,14 @@ __device__ inline float pair_term2(float x) {
     return (x * x) * (0.25f * kHalfVar2);
 }
 
-// Pair sums of a delta tile (column n = candidate n, its doubled delta row: acc = 2d):
-// F = sum over the group's heads of the pair term (g(d) for the LSE), or of d alone when
-// the candidate has no eligible right child (bit n of rvm clear: one child, whose logit
-// is p + d for every score), and D = sum of d. Every lane of column n receives both.
-// Halving is exact, so D = (sum of 2d) / 2 has the bits of the sum of d.
+// Per-element pair terms of a delta tile (column n = candidate n, its doubled delta row:
+// acc = 2d; lane (gq, n) holds heads 4gq .. 4gq+3): tv = the pair term of each head of the
+// group (g(d) for the LSE), or d alone when the candidate has no eligible right child (bit n
+// of rvm clear: one child, whose logit is p + d for every score), dv = 2d; heads past the
+// group are 0. The masked form computes every term and selects (no branch per element).
 template <int S>
-__device__ inline void delta_tile_sums(const f32x4& acc, uint32_t rvm, int n, int gq, int GQ, float& F, float& D) {
-    float tv[4], dv[4];
+__device__ inline void delta_tile_terms(const f32x4& acc, uint32_t rvm, int n, int gq, int GQ, float (&tv)[4],
+                                        float (&dv)[4]) {
     if ((rvm & 0xffffu) == 0xffffu && GQ == kMaxGroup) {
         // every right child eligible and every row a head of the group (same result)
 #pragma unroll
@@ -181,13 +181,53 @@ __device__ inline void delta_tile_sums(const f32x4& acc, uint32_t rvm, int n, in
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const bool h = 4 * gq + k < GQ;
+            const float t = pair_term2<S>(acc[k]);
             dv[k] = h ? acc[k] : 0.0f;
-            tv[k] = h ? (rv ? pair_term2<S>(acc[k]) : 0.5f * acc[k]) : 0.0f;
+            tv[k] = h ? (rv ? t : 0.5f * acc[k]) : 0.0f;
         }
     }
+}
+
+// Pair sums of one delta tile: F = sum over the group's heads of the pair terms, D = sum of
+// d (halving is exact, so D = (sum of 2d) / 2 has the bits of the sum of d). Every lane of
+// column n receives both.
+template <int S>
+__device__ inline void delta_tile_sums(const f32x4& acc, uint32_t rvm, int n, int gq, int GQ, float& F, float& D) {
+    float tv[4], dv[4];
+    delta_tile_terms<S>(acc, rvm, n, gq, GQ, tv, dv);
     float D2;
     heads_total2(tv, dv, F, D2);
     D = 0.5f * D2;
+}
+
+// In-lane parts of delta_tile_sums: the terms added as (t0 + t1) + (t2 + t3).
+template <int S>
+__device__ inline void delta_tile_parts(const f32x4& acc, uint32_t rvm, int n, int gq, int GQ, float& f, float& x2) {
+    float tv[4], dv[4];
+    delta_tile_terms<S>(acc, rvm, n, gq, GQ, tv, dv);
+    f = (tv[0] + tv[1]) + (tv[2] + tv[3]);
+    x2 = (dv[0] + dv[1]) + (dv[2] + dv[3]);
+}
+
+// The pair sums of four delta tiles at once, scattered: lane (gq, n) receives F and D of
+// tile gq, column n. f[i], x2[i] are tile i's in-lane parts (delta_tile_parts). The row
+// groups are added as (r0 + r1) + (r2 + r3), the order of heads_total2, so every total has
+// the bits the tile would get alone: four permlane16 exchanges add row pairs (0, 1) and
+// (2, 3) while halving the values each lane holds, two permlane32 exchanges add the pairs.
+__device__ inline void delta_sums4(const float (&f)[4], const float (&x2)[4], float& F, float& D) {
+    auto pair16 = [](float a, float b) -> float {   // rows 0, 2: a of rows 0+1 / 2+3; rows 1, 3: b
+        const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        return __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    };
+    auto pair32 = [](float a, float b) -> float {   // rows 0, 1: a of (rows 0/1) + (rows 2/3); rows 2, 3: b
+        const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+        return __uint_as_float(y[0]) + __uint_as_float(y[1]);
+    };
+    // rows 0/2 hold tile 0 (resp. 2), rows 1/3 tile 1 (resp. 3), each summed over a row pair
+    const float f01 = pair16(f[0], f[1]), f23 = pair16(f[2], f[3]);
+    const float d01 = pair16(x2[0], x2[1]), d23 = pair16(x2[2], x2[3]);
+    F = pair32(f01, f23);
+    D = 0.5f * pair32(d01, d23);
 }
 
 // The ragged node's children read directly: column 0 of the tile holds the left child's
