@@ -501,15 +501,16 @@ __device__ inline void load_q(const uint16_t* __restrict__ q, int64_t bt, int Hq
     qb = *reinterpret_cast<const u32x4*>(qrow + 32 + 8 * gq);
 }
 
-// Persistent wavefronts, each on its own: a wavefront takes a work item from the counter,
+// Persistent wavefronts, each on its own: a wavefront takes a work item from the counters,
 // loads the item's sibling pair of leaves (128 keys) into registers as MFMA A fragments,
 // and scores the item's entries two at a time (a unit: two walks, both leaves), the next
-// unit's queries in flight while the current one is scored. No LDS and no barrier.
+// two units' queries in flight while one is scored. No LDS and no barrier.
 template <int S, bool kOneEach>
-__global__ __launch_bounds__(kLeafThreads) void leaf_cluster_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, Geom G, ClusterGeom CG, Pack pk, int64_t NT,
-    const int4* __restrict__ items, uint32_t item_cap, const uint2* __restrict__ entries,
-    uint32_t* __restrict__ meta, float* __restrict__ score, float* __restrict__ sink) {
+__device__ inline void leaf_cluster_body(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const Geom& G,
+                                         const ClusterGeom& CG, const Pack& pk, int64_t NT,
+                                         const int4* __restrict__ items, uint32_t item_cap,
+                                         const uint2* __restrict__ entries, uint32_t* __restrict__ meta,
+                                         float* __restrict__ score, float* __restrict__ sink) {
     static_assert(kItemMax % 64 == 0, "an item is scored in whole batches of 64 entries");
     constexpr int kW = 2;   // walks per unit (one walk per unit at four wavefronts per SIMD measured slower)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -616,26 +617,49 @@ __global__ __launch_bounds__(kLeafThreads) void leaf_cluster_kernel(
                 if (lane == 48 && (mb & 2u)) dst = score + wb * CS + (yb >> 16) + (mb & 1u);
                 *dst = v;
             };
+            // the queries of the next two units are in flight while a unit is scored; the
+            // steady state is a fixed sequence of memory operations per iteration (one store per
+            // unit, four loads per prefetch), so wait counts stay exact across iterations
             u32x4 qa0, qa1, qb0 = {0u, 0u, 0u, 0u}, qb1 = qb0, ra0, ra1, rb0 = qb0, rb1 = qb0;
+            u32x4 sa0, sa1, sb0 = qb0, sb1 = qb0;
             qload(0, qa0, qa1, qb0, qb1);
             qload(1, ra0, ra1, rb0, rb1);
-            // steady state: a fixed sequence of memory operations per iteration (one store per
-            // unit, four loads per prefetch), so wait counts stay exact across iterations
-            for (int u = 0; u < nunits; u += 2) {
+            qload(2, sa0, sa1, sb0, sb1);
+            for (int u = 0; u < nunits; u += 3) {
                 process(u, qa0, qa1, qb0, qb1);
-                qload(min(u + 2, 64 / kW), qa0, qa1, qb0, qb1);
+                qload(min(u + 3, 64 / kW), qa0, qa1, qb0, qb1);
                 process(u + 1, ra0, ra1, rb0, rb1);
-                qload(min(u + 3, 64 / kW), ra0, ra1, rb0, rb1);
+                qload(min(u + 4, 64 / kW), ra0, ra1, rb0, rb1);
+                process(u + 2, sa0, sa1, sb0, sb1);
+                qload(min(u + 5, 64 / kW), sa0, sa1, sb0, sb1);
             }
         }
     }
+}
+
+template <int S, bool kOneEach>
+__global__ __launch_bounds__(kLeafThreads) void leaf_cluster_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, Geom G, ClusterGeom CG, Pack pk, int64_t NT,
+    const int4* __restrict__ items, uint32_t item_cap, const uint2* __restrict__ entries,
+    uint32_t* __restrict__ meta, float* __restrict__ score, float* __restrict__ sink) {
+    leaf_cluster_body<S, kOneEach>(q, k, G, CG, pk, NT, items, item_cap, entries, meta, score, sink);
+}
+// The LSE kernel of long calls: held to three wavefronts per SIMD (166 VGPRs, no spill);
+// the others take the occupancy their registers give.
+template <>
+__global__ __launch_bounds__(kLeafThreads) __attribute__((amdgpu_waves_per_eu(3))) void
+leaf_cluster_kernel<kScoreLse, false>(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, Geom G,
+                                      ClusterGeom CG, Pack pk, int64_t NT, const int4* __restrict__ items,
+                                      uint32_t item_cap, const uint2* __restrict__ entries,
+                                      uint32_t* __restrict__ meta, float* __restrict__ score,
+                                      float* __restrict__ sink) {
+    leaf_cluster_body<kScoreLse, false>(q, k, G, CG, pk, NT, items, item_cap, entries, meta, score, sink);
 }
 
 #define PISA_LEAF_CLUSTER_INST(S, O)                                                                      \
     template __global__ void leaf_cluster_kernel<S, O>(const uint16_t*, const uint16_t*, Geom, ClusterGeom, Pack, \
                                                        int64_t, const int4*, uint32_t, const uint2*, uint32_t*, float*, \
                                                        float*);
-PISA_LEAF_CLUSTER_INST(kScoreLse, false)
 PISA_LEAF_CLUSTER_INST(kScoreMean, false)
 PISA_LEAF_CLUSTER_INST(kScoreMeanHalfVar, false)
 PISA_LEAF_CLUSTER_INST(kScoreLse, true)
