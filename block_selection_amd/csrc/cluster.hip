@@ -512,7 +512,7 @@ __device__ inline void leaf_cluster_body(const uint16_t* __restrict__ q, const u
                                          const uint2* __restrict__ entries, uint32_t* __restrict__ meta,
                                          float* __restrict__ score, float* __restrict__ sink) {
     static_assert(kItemMax % 64 == 0, "an item is scored in whole batches of 64 entries");
-    constexpr int kW = 2;   // walks per unit (one walk per unit at four wavefronts per SIMD measured slower)
+    // a unit is two walks (one walk per unit at four wavefronts per SIMD measured slower)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, gq = lane >> 4;
     const int CS = 2 * G.topk;
@@ -527,26 +527,34 @@ __device__ inline void leaf_cluster_body(const uint16_t* __restrict__ q, const u
     // addresses; a wavefront starts on its workgroup's stream and moves to the next one when
     // that is exhausted. kOneEach (chosen for short calls, which have about as many items as
     // wavefronts): wavefront w first takes item w without an atomic, and the streams then
-    // hand out the items past the wavefront count.
+    // hand out the items past the wavefront count. The ticket for a wavefront's next item is
+    // taken when an item starts and read when it ends, so its round trip overlaps the scoring.
     const int s0 = (int)(blockIdx.x % kItemStreams);
     const uint32_t skip = kOneEach ? gridDim.x * (kLeafThreads / 64) : 0u;
-    int si = kOneEach ? -1 : 0;
-    for (;;) {
-        uint32_t it;
-        if (kOneEach && si < 0) {
-            it = blockIdx.x * (kLeafThreads / 64) + wave;
-            si = 0;
-            if (it >= n_items) break;
-        } else {
-            const int sidx = (s0 + si) % kItemStreams;
-            uint32_t got = 0u;
-            if (lane == 0) got = atomicAdd(meta + kItemCounter0 + kItemCounterStride * sidx, 1u);
-            it = skip + (uint32_t)__builtin_amdgcn_readlane((int)got, 0) * kItemStreams + sidx;
-            if (it >= n_items) {
-                if (++si == kItemStreams) break;
-                continue;
-            }
+    constexpr uint32_t kNone = 0xffffffffu;
+    int si = 0;
+    auto ticket = [&]() -> uint32_t {   // lane 0: a ticket of the current stream
+        uint32_t got = 0u;
+        if (lane == 0) got = atomicAdd(meta + kItemCounter0 + kItemCounterStride * ((s0 + si) % kItemStreams), 1u);
+        return got;
+    };
+    auto resolve = [&](uint32_t got) -> uint32_t {   // the item of a ticket, else the next stream's
+        for (;;) {
+            const uint32_t it = skip + (uint32_t)__builtin_amdgcn_readlane((int)got, 0) * kItemStreams +
+                                (uint32_t)((s0 + si) % kItemStreams);
+            if (it < n_items) return it;
+            if (++si == kItemStreams) return kNone;
+            got = ticket();
         }
+    };
+    uint32_t it;
+    if (kOneEach) {
+        it = blockIdx.x * (kLeafThreads / 64) + wave;
+        if (it >= n_items) return;
+    } else {
+        it = resolve(ticket());
+    }
+    while (it != kNone) {
         const int4 item = items[it < n_front ? it : item_cap - 1u - (it - n_front)];
         const int grp = item.x;
         const int gs = grp % CG.NGP;
@@ -571,69 +579,75 @@ __device__ inline void leaf_cluster_body(const uint16_t* __restrict__ q, const u
         const int key0 = pg * kGrpKeys;
         PairKeys K;
         load_pair_keys(k + (tk0 * G.Hkv + kvh) * kD, row_stride, key0, nkeys, n, gq, K);
-        for (int base = 0; base < item.z; base += 64) {
-            // lane i holds entry base + i of the item; unit u is entries W*u .. W*u + W - 1
-            const int m = min(64, item.z - base);
-            const uint2 ev = (lane < m) ? entries[item.y + base + lane] : make_uint2(0u, 0u);
-            const int nunits = (m + kW - 1) / kW;
-            // queries of unit u (units past the batch read position 0, a valid row, and score nothing)
-            auto qload = [&](int u, u32x4& a0, u32x4& a1, u32x4& b0, u32x4& b1) {
-                const int la = min(kW * u, 63), lb = (kW == 2 && 2 * u + 1 < m) ? 2 * u + 1 : la;
-                const uint32_t ta = (uint32_t)__builtin_amdgcn_readlane((int)ev.x, la);
-                load_q(q, bt0 + ta, G.Hq, kvh, G.GQ, n, gq, a0, a1);
-                if (kW == 2) {
-                    const uint32_t tb = (uint32_t)__builtin_amdgcn_readlane((int)ev.x, lb);
-                    load_q(q, bt0 + tb, G.Hq, kvh, G.GQ, n, gq, b0, b1);
-                }
-            };
-            // one store instruction per unit: lanes 0 / 16 write walk a's two leaves, lanes 32 / 48
-            // walk b's, every other lane (and every lane of an empty unit) writes the sink
-            auto process = [&](int u, const u32x4& a0, const u32x4& a1, const u32x4& b0, const u32x4& b1) {
-                const int la = min(kW * u, 63), lb = min(kW * u + 1, 63);
-                const uint32_t tua = (uint32_t)__builtin_amdgcn_readlane((int)ev.x, la);
-                const uint32_t ya = (kW * u < m) ? (uint32_t)__builtin_amdgcn_readlane((int)ev.y, la) : 0u;
-                const uint32_t tbr = (kW == 2) ? (uint32_t)__builtin_amdgcn_readlane((int)ev.x, lb) : tua;
-                const uint32_t yb = (kW == 2 && 2 * u + 1 < m) ? (uint32_t)__builtin_amdgcn_readlane((int)ev.y, lb) : 0u;
-                const uint32_t ma = ya & 3u, mb = yb & 3u;
-                const uint32_t tub = mb ? tbr : tua;
-                const int64_t wa = (bt0 + tua) * G.Hkv + kvh, wb = (bt0 + tub) * G.Hkv + kvh;
-                float v = 0.0f;
-                if (ma) {
-                    const int ta = (int)tua, tb = (int)tub;
-                    const int lim[4] = {min(ta - key0, kC - 1), min(ta - key0 - kC, kC - 1), min(tb - key0, kC - 1),
-                                        min(tb - key0 - kC, kC - 1)};
-                    const bf16x8 fa0 = __builtin_bit_cast(bf16x8, a0), fa1 = __builtin_bit_cast(bf16x8, a1);
-                    const bf16x8 fb0 = __builtin_bit_cast(bf16x8, kW == 2 ? b0 : a0);
-                    const bf16x8 fb1 = __builtin_bit_cast(bf16x8, kW == 2 ? b1 : a1);
-                    if constexpr (S == kScoreLse)
-                        v = score_unit(K, lim, fa0, fa1, fb0, fb1, n, gq, G.GQ, mb != 0u);
-                    else
-                        v = score_unit_trunc<S>(K, lim, fa0, fa1, fb0, fb1, n, gq, G.GQ, mb != 0u);
-                }
-                float* dst = wsink;
-                if (lane == 0 && (ma & 1u)) dst = score + wa * CS + (ya >> 16);
-                if (lane == 16 && (ma & 2u)) dst = score + wa * CS + (ya >> 16) + (ma & 1u);
-                if (lane == 32 && (mb & 1u)) dst = score + wb * CS + (yb >> 16);
-                if (lane == 48 && (mb & 2u)) dst = score + wb * CS + (yb >> 16) + (mb & 1u);
-                *dst = v;
-            };
-            // the queries of the next two units are in flight while a unit is scored; the
-            // steady state is a fixed sequence of memory operations per iteration (one store per
-            // unit, four loads per prefetch), so wait counts stay exact across iterations
-            u32x4 qa0, qa1, qb0 = {0u, 0u, 0u, 0u}, qb1 = qb0, ra0, ra1, rb0 = qb0, rb1 = qb0;
-            u32x4 sa0, sa1, sb0 = qb0, sb1 = qb0;
-            qload(0, qa0, qa1, qb0, qb1);
-            qload(1, ra0, ra1, rb0, rb1);
-            qload(2, sa0, sa1, sb0, sb1);
-            for (int u = 0; u < nunits; u += 3) {
-                process(u, qa0, qa1, qb0, qb1);
-                qload(min(u + 3, 64 / kW), qa0, qa1, qb0, qb1);
-                process(u + 1, ra0, ra1, rb0, rb1);
-                qload(min(u + 4, 64 / kW), ra0, ra1, rb0, rb1);
-                process(u + 2, sa0, sa1, sb0, sb1);
-                qload(min(u + 5, 64 / kW), sa0, sa1, sb0, sb1);
-            }
+        // lane u holds unit u of the item (its entries 2u and 2u + 1; an item of kItemMax = 128
+        // entries is 64 units): walk a's (position, slot word) in x, y and walk b's in z, w. A
+        // unit without a second entry repeats walk a's position with a zero slot word; lanes past
+        // the item hold zeros (position 0, a valid row, and no slot).
+        static_assert(kItemMax == 2 * 64, "one unit per lane");
+        const int m = item.z;
+        const int nunits = (m + 1) >> 1;
+        uint4 ev = make_uint4(0u, 0u, 0u, 0u);
+        if (2 * lane < m) {
+            const uint2 ea = entries[item.y + 2 * lane];
+            const uint2 eb = (2 * lane + 1 < m) ? entries[item.y + 2 * lane + 1] : make_uint2(ea.x, 0u);
+            ev = make_uint4(ea.x, ea.y, eb.x, eb.y);
         }
+        const uint32_t next = ticket();
+        // queries of unit u (u <= 63)
+        auto qload = [&](int u, u32x4& a0, u32x4& a1, u32x4& b0, u32x4& b1) {
+            const uint32_t ta = (uint32_t)__builtin_amdgcn_readlane((int)ev.x, u);
+            const uint32_t tb = (uint32_t)__builtin_amdgcn_readlane((int)ev.z, u);
+            load_q(q, bt0 + ta, G.Hq, kvh, G.GQ, n, gq, a0, a1);
+            load_q(q, bt0 + tb, G.Hq, kvh, G.GQ, n, gq, b0, b1);
+        };
+        // one store instruction per unit: lanes 0 / 16 write walk a's two leaves, lanes 32 / 48
+        // walk b's, every other lane (and every lane of a unit past the item) writes the sink
+        auto process = [&](int u, const u32x4& a0, const u32x4& a1, const u32x4& b0, const u32x4& b1) {
+            const bool real = u < nunits;
+            const int lu = min(u, 63);
+            const uint32_t tua = (uint32_t)__builtin_amdgcn_readlane((int)ev.x, lu);
+            const uint32_t ya = real ? (uint32_t)__builtin_amdgcn_readlane((int)ev.y, lu) : 0u;
+            const uint32_t tbr = (uint32_t)__builtin_amdgcn_readlane((int)ev.z, lu);
+            const uint32_t yb = real ? (uint32_t)__builtin_amdgcn_readlane((int)ev.w, lu) : 0u;
+            const uint32_t ma = ya & 3u, mb = yb & 3u;
+            const uint32_t tub = mb ? tbr : tua;
+            const int64_t wa = (bt0 + tua) * G.Hkv + kvh, wb = (bt0 + tub) * G.Hkv + kvh;
+            float v = 0.0f;
+            if (ma) {
+                const int ta = (int)tua, tb = (int)tub;
+                const int lim[4] = {min(ta - key0, kC - 1), min(ta - key0 - kC, kC - 1), min(tb - key0, kC - 1),
+                                    min(tb - key0 - kC, kC - 1)};
+                const bf16x8 fa0 = __builtin_bit_cast(bf16x8, a0), fa1 = __builtin_bit_cast(bf16x8, a1);
+                const bf16x8 fb0 = __builtin_bit_cast(bf16x8, b0), fb1 = __builtin_bit_cast(bf16x8, b1);
+                if constexpr (S == kScoreLse)
+                    v = score_unit(K, lim, fa0, fa1, fb0, fb1, n, gq, G.GQ, mb != 0u);
+                else
+                    v = score_unit_trunc<S>(K, lim, fa0, fa1, fb0, fb1, n, gq, G.GQ, mb != 0u);
+            }
+            float* dst = wsink;
+            if (lane == 0 && (ma & 1u)) dst = score + wa * CS + (ya >> 16);
+            if (lane == 16 && (ma & 2u)) dst = score + wa * CS + (ya >> 16) + (ma & 1u);
+            if (lane == 32 && (mb & 1u)) dst = score + wb * CS + (yb >> 16);
+            if (lane == 48 && (mb & 2u)) dst = score + wb * CS + (yb >> 16) + (mb & 1u);
+            *dst = v;
+        };
+        // the queries of the next two units are in flight while a unit is scored, over the
+        // whole item; the steady state is a fixed sequence of memory operations per iteration
+        // (one store per unit, four loads per prefetch), so wait counts stay exact across
+        // iterations
+        u32x4 qa0, qa1, qb0, qb1, ra0, ra1, rb0, rb1, sa0, sa1, sb0, sb1;
+        qload(0, qa0, qa1, qb0, qb1);
+        qload(1, ra0, ra1, rb0, rb1);
+        qload(2, sa0, sa1, sb0, sb1);
+        for (int u = 0; u < nunits; u += 3) {
+            process(u, qa0, qa1, qb0, qb1);
+            qload(min(u + 3, 63), qa0, qa1, qb0, qb1);
+            process(u + 1, ra0, ra1, rb0, rb1);
+            qload(min(u + 4, 63), ra0, ra1, rb0, rb1);
+            process(u + 2, sa0, sa1, sb0, sb1);
+            qload(min(u + 5, 63), sa0, sa1, sb0, sb1);
+        }
+        it = resolve(next);
     }
 }
 
