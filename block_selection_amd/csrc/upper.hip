@@ -135,6 +135,18 @@ __device__ inline TileRows rows_buffer(buf_rsrc_t hi, buf_rsrc_t lo, int row, in
     return r;
 }
 
+// Node `row` of a level of M nodes stored chunk-major (chunk g at byte (g * M + row) * 16
+// of each plane's level region), through buffer resources based at the level's region.
+__device__ inline TileRows rows_chunk_major(buf_rsrc_t hi, buf_rsrc_t lo, int row, uint32_t M, int gq) {
+    const uint32_t o0 = ((uint32_t)gq * M + (uint32_t)row) << 4, o1 = o0 + (M << 6);   // chunks gq, 4 + gq
+    TileRows r;
+    r.h0 = load_b128(hi, o0);
+    r.h1 = load_b128(hi, o1);
+    r.l0 = load_b128(lo, o0);
+    r.l1 = load_b128(lo, o1);
+    return r;
+}
+
 __device__ inline TileRows rows_global(const uint16_t* __restrict__ plane, int64_t plane_stride, int gq) {
     TileRows r;
     r.h0 = *reinterpret_cast<const u32x4*>(plane + 8 * gq);
@@ -287,10 +299,16 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_f32_kernel(const flo
 // only at the first scored level of a walk (to start P), and the children of the one
 // ragged node of a level (a partial right child) are read directly.
 
-// delta planes: row c of level l >= 2 holds hi/lo bf16 planes of
+// delta planes: node c of level l >= 2 holds hi/lo bf16 planes of
 // 2 (s_{l-1}(2c) - s_l(c)) * log2(e)/8 (the doubled delta), rounded like the summary
-// planes. Grid: (chunks, B * Hkv); with a pack (pk.cu non-null), (D * Hkv, chunks), one
-// row of workgroups per (document, KV head).
+// planes. Chunk-major inside each level of a sequence: the level's M rows keep their
+// place in the plane (M * 128 bytes from its first row), and chunk g (dims 8g .. 8g+7,
+// 16 bytes) of node c sits at byte (g * M + c) * 16 of it. The walk gathers one chunk of
+// 16 candidates per quarter-wavefront and instruction; candidates come as sibling pairs,
+// which this layout puts side by side, so a quarter-wavefront touches at most 8 cache
+// lines per load instead of 16 (the tag lookups, not the bytes, bound those gathers).
+// Grid: (chunks, B * Hkv); with a pack (pk.cu non-null), (D * Hkv, chunks), one row of
+// workgroups per (document, KV head).
 __global__ __launch_bounds__(256) void delta_planes_kernel(const float* __restrict__ pyr,
                                                            uint16_t* __restrict__ dplanes, Geom G, Pack pk) {
     int64_t row0;
@@ -318,10 +336,10 @@ __global__ __launch_bounds__(256) void delta_planes_kernel(const float* __restri
         int64_t r = i >> 6;
         int l = 2;
         while (r >= sg.M(l)) { r -= sg.M(l); ++l; }
-        const int64_t prow = G.off[l] + sg.shift(l) + r, crow = G.off[l - 1] + sg.shift(l - 1) + 2 * r;
+        const int64_t lrow = G.off[l] + sg.shift(l), prow = lrow + r, crow = G.off[l - 1] + sg.shift(l - 1) + 2 * r;
         uint32_t hi, lo;
         split_scaled(2.0f * (base[crow * kD + e] - base[prow * kD + e]), hi, lo);
-        const int64_t o = (row0 + prow) * kD + e;
+        const int64_t o = (row0 + lrow) * kD + ((int64_t)(e >> 3) * sg.M(l) + r) * 8 + (e & 7);
         dplanes[o] = (uint16_t)hi;
         dplanes[plane_stride + o] = (uint16_t)lo;
     }
@@ -359,8 +377,8 @@ __device__ inline void stage_upper_lds(lds_char_t* lds, const uint16_t* __restri
         const int mj = sg.M(j);
         const int64_t r0 = bh_row0 + G.off[j] + sg.shift(j);
         for (int c = threadIdx.x; c < mj * 16; c += blockDim.x) {
-            const int node = c >> 4, part = c & 15;
-            const uint16_t* src = dplanes + (part >> 3) * plane_stride + (r0 + node) * kD + (part & 7) * 8;
+            const int part = c / mj, node = c - part * mj;   // chunk part & 7 of plane part >> 3
+            const uint16_t* src = dplanes + (part >> 3) * plane_stride + r0 * kD + ((part & 7) * mj + node) * 8;
             *reinterpret_cast<lds_u32x4_t*>(lds + (U.lds_first[j] + node) * kLdsNodeBytes + (part >> 3) * 128 +
                                             (part & 7) * 16) = *reinterpret_cast<const u32x4*>(src);
         }
@@ -483,9 +501,10 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
                 row = (c >= 0) ? c : 0;
                 return (uint32_t)ballot(rv);              // bit n: column n has an eligible right child
             };
+            const uint32_t Ml = (uint32_t)sg.M(l);
             auto fetch = [&](int row) -> TileRows {
                 if (in_lds) return rows_lds(lds, lds_lvl + row, gq);
-                return rows_buffer(dhi, dlo, row, gq);
+                return rows_chunk_major(dhi, dlo, row, Ml, gq);
             };
             // each tile's in-lane head parts, then one exchange pattern leaves lane (gq, n)
             // with the sums of tile gq, column n
