@@ -437,7 +437,9 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
     uint32_t surv_low = 0;     // sorted key low word in slots < K: the survivors
     float Pa = 0.0f, Pb = 0.0f;  // head-summed logits of this slot's candidate's children
     uint32_t pk = 0;           // walks whose candidates' P is known (scored at the level above)
-    for (int l = sg.L; l >= 2; --l) {
+    // one level of the walk; kInLds: the level's delta rows are staged in LDS (else gathered)
+    auto level = [&](int l, auto in_lds_const) {
+        constexpr bool in_lds = decltype(in_lds_const)::value;
         int cand;
         float P = 0.0f;
         if (l == sg.L) {
@@ -490,7 +492,6 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
                 }
             }
             // (2) the delta tiles, the next tile's row in flight
-            const bool in_lds = l >= U.j_lo && l <= U.j_hi;
             const int lds_lvl = in_lds ? U.lds_first[l] : 0;
             const buf_rsrc_t dhi = make_rsrc(dplanes + row_l * kD, lvl_bytes);
             const buf_rsrc_t dlo = make_rsrc(dplanes + plane_stride + row_l * kD, lvl_bytes);
@@ -503,8 +504,8 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
             };
             const uint32_t Ml = (uint32_t)sg.M(l);
             auto fetch = [&](int row) -> TileRows {
-                if (in_lds) return rows_lds(lds, lds_lvl + row, gq);
-                return rows_chunk_major(dhi, dlo, row, Ml, gq);
+                if constexpr (in_lds) return rows_lds(lds, lds_lvl + row, gq);
+                else return rows_chunk_major(dhi, dlo, row, Ml, gq);
             };
             // each tile's in-lane head parts, then one exchange pattern leaves lane (gq, n)
             // with the sums of tile gq, column n
@@ -574,7 +575,13 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
             const uint32_t moved = (uint32_t)push_to_lane(dst, (int)(uint32_t)slot_key(0.0f, cand, ml));
             surv_low = (ml < K) ? moved : 0u;
         }
-    }
+    };
+    // the levels down to the last one staged in LDS (the levels above it are not scored), then
+    // the gathered ones: each phase without a per-tile choice of source
+    int l = sg.L;
+    if (U.j_lo <= U.j_hi)
+        for (; l >= 2 && l >= U.j_lo; --l) level(l, std::true_type{});
+    for (; l >= 2; --l) level(l, std::false_type{});
     // leaf candidates: children of the level-2 survivors (or the root if it is a leaf)
     int leaf;
     if (sg.L == 1) {

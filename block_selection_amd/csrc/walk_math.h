@@ -89,9 +89,11 @@ __device__ inline void heads_total2(const float f[4], const float d[4], float& F
 
 // Head sum of the logits of each column of a summary tile (heads past the group masked).
 __device__ inline float tile_head_sums(const f32x4& acc, int gq, int GQ) {
-    float v[4];
+    float v[4] = {acc[0], acc[1], acc[2], acc[3]};
+    if (GQ != kMaxGroup) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = (4 * gq + k < GQ) ? acc[k] : 0.0f;
+        for (int k = 0; k < 4; ++k) v[k] = (4 * gq + k < GQ) ? v[k] : 0.0f;
+    }
     return heads_total(v);
 }
 
@@ -165,25 +167,28 @@ __device__ inline float pair_term2(float x) {
 // acc = 2d; lane (gq, n) holds heads 4gq .. 4gq+3): tv = the pair term of each head of the
 // group (g(d) for the LSE), or d alone when the candidate has no eligible right child (bit n
 // of rvm clear: one child, whose logit is p + d for every score), dv = 2d; heads past the
-// group are 0. The masked form computes every term and selects (no branch per element).
+// group are 0. The terms are computed for every element and then corrected in place by
+// selects (a tile with an ineligible right child, a group of fewer than 16 heads), so the
+// common tile carries no copy of its logits.
 template <int S>
 __device__ inline void delta_tile_terms(const f32x4& acc, uint32_t rvm, int n, int gq, int GQ, float (&tv)[4],
                                         float (&dv)[4]) {
-    if ((rvm & 0xffffu) == 0xffffu && GQ == kMaxGroup) {
-        // every right child eligible and every row a head of the group (same result)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            dv[k] = acc[k];
-            tv[k] = pair_term2<S>(acc[k]);
-        }
-    } else {
+    for (int k = 0; k < 4; ++k) {
+        dv[k] = acc[k];
+        tv[k] = pair_term2<S>(acc[k]);
+    }
+    if ((rvm & 0xffffu) != 0xffffu) {
         const bool rv = (rvm >> n) & 1u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) tv[k] = rv ? tv[k] : 0.5f * dv[k];
+    }
+    if (GQ != kMaxGroup) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const bool h = 4 * gq + k < GQ;
-            const float t = pair_term2<S>(acc[k]);
-            dv[k] = h ? acc[k] : 0.0f;
-            tv[k] = h ? (rv ? t : 0.5f * acc[k]) : 0.0f;
+            tv[k] = h ? tv[k] : 0.0f;
+            dv[k] = h ? dv[k] : 0.0f;
         }
     }
 }
