@@ -509,8 +509,14 @@ static int cluster_leaf_stage(const uint16_t* q, const uint16_t* k, const Geom& 
     }
     mark(ev, 3, s);
     const int wpw = slots <= 16 ? 4 : (slots <= 32 ? 2 : 1);
-    int64_t fgrid = ((walks + wpw - 1) / wpw + 3) / 4;
-    if (fgrid > 65536) fgrid = 65536;
+    // workgroups of 4 wavefronts: one group of walks per wavefront while every wavefront can be
+    // resident at once, else about kTopkBatch groups per wavefront trip
+    const int64_t fgroups = (walks + wpw - 1) / wpw;
+    int64_t fgrid = (fgroups + 3) / 4;
+    if (fgroups > (int64_t)cus * 32) {
+        fgrid = (fgroups + 4 * kTopkBatch - 1) / (4 * kTopkBatch);
+        if (fgrid > (int64_t)cus * 16) fgrid = (int64_t)cus * 16;
+    }
     if (slots <= 16)
         hipLaunchKernelGGL(final_topk_kernel<16>, dim3((unsigned)fgrid), dim3(256), 0, s, W.cand, W.ncand, W.score, G, NT, out);
     else if (slots <= 32)

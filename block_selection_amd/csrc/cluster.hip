@@ -682,7 +682,9 @@ PISA_LEAF_CLUSTER_INST(kScoreMeanHalfVar, true)
 #undef PISA_LEAF_CLUSTER_INST
 
 // Per walk (SLOTS lanes each): at most K candidates are all kept; otherwise the K best
-// by (score desc, index asc). Written in ascending leaf order, -1 padded.
+// by (score desc, index asc). Written in ascending leaf order, -1 padded. A wavefront
+// takes kTopkBatch groups of walks per trip (grid stride) and issues all their loads
+// before it selects, so one memory round trip serves several groups.
 template <int SLOTS>
 __global__ __launch_bounds__(256) void final_topk_kernel(const int32_t* __restrict__ cand,
                                                          const int32_t* __restrict__ ncand,
@@ -693,17 +695,29 @@ __global__ __launch_bounds__(256) void final_topk_kernel(const int32_t* __restri
     const int lane = threadIdx.x & 63, seg = lane / SLOTS, i = lane % SLOTS;
     const int64_t walks = (int64_t)G.B * NT * G.Hkv;
     const int64_t groups = (walks + WPW - 1) / WPW;
-    for (int64_t grp = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); grp < groups; grp += (int64_t)gridDim.x * 4) {
-        const int64_t w = grp * WPW + seg;
-        const bool ok = w < walks;
-        const int nc = ok ? ncand[w] : 0;
-        const int c = (ok && i < CS) ? cand[w * CS + i] : -1;
-        float s = -INFINITY;
-        if (c >= 0) s = (nc > K) ? score[w * CS + i] : 0.0f;
-        const int cidx = (c >= 0) ? c : INT_MAX;
-        const int nd = (2 * K == SLOTS) ? select_top_half<SLOTS>(s, cidx, i) : select_sort<SLOTS>(s, cidx, i);
-        const int nd2 = index_sort<SLOTS>((i < K) ? nd : INT_MAX, i);
-        if (ok && i < K) out[w * K + i] = (nd2 != INT_MAX) ? nd2 : -1;
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    for (int64_t g0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); g0 < groups; g0 += stride * kTopkBatch) {
+        int nc[kTopkBatch], c[kTopkBatch];
+        float sv[kTopkBatch];
+#pragma unroll
+        for (int j = 0; j < kTopkBatch; ++j) {
+            const int64_t w = (g0 + j * stride) * WPW + seg;
+            const bool ok = g0 + j * stride < groups && w < walks;
+            nc[j] = ok ? ncand[w] : 0;
+            c[j] = (ok && i < CS) ? cand[w * CS + i] : -1;
+            sv[j] = (ok && i < CS) ? score[w * CS + i] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < kTopkBatch; ++j) {
+            if (g0 + j * stride >= groups) break;   // wavefront-uniform
+            const int64_t w = (g0 + j * stride) * WPW + seg;
+            float s = -INFINITY;
+            if (c[j] >= 0) s = (nc[j] > K) ? sv[j] : 0.0f;
+            const int cidx = (c[j] >= 0) ? c[j] : INT_MAX;
+            const int nd = (2 * K == SLOTS) ? select_top_half<SLOTS>(s, cidx, i) : select_sort<SLOTS>(s, cidx, i);
+            const int nd2 = index_sort<SLOTS>((i < K) ? nd : INT_MAX, i);
+            if (w < walks && i < K) out[w * K + i] = (nd2 != INT_MAX) ? nd2 : -1;
+        }
     }
 }
 

@@ -205,6 +205,7 @@ constexpr int kLeafThreads = 256;                  // independent wavefronts, on
 constexpr int kBinSlice = 16384;                   // bucket-pass bins held in LDS at once (64 KiB)
 constexpr int kBucketUnroll = 4;                   // rounds of walks per bucket-pass loop trip
 constexpr int kPlanWaves = 16;                     // wavefronts of a plan workgroup
+constexpr int kTopkBatch = 4;                      // groups of walks per final top-K wavefront trip
 // meta words of the leaf stage: items at the front / back of the item array, entries
 // placed, then kItemStreams item counters at meta[64 + 64 s], 256 bytes apart
 constexpr int kMetaFront = 0, kMetaEntries = 1, kMetaBack = 2;
