@@ -47,7 +47,9 @@ def walk_counts(N: int, topk: int, GQ: int, Hkv: int, C: int = 64):
     leaf its eligible raw keys per head; every scored candidate costs one LSE
     (one log) per head. The count assumes the causal frontier node survives
     (exact for full-depth walks). Returns a dict of totals over all walks:
-    leaf_logits, leaf_lse, upper_logits, upper_lse, leaf_pairs.
+    leaf_logits, leaf_lse, upper_logits, upper_lse, leaf_pairs, and leaf_entries (the
+    leaf stage's incidences: one per scored walk and level-2 survivor, whose children form
+    one sibling pair).
     """
     t = np.arange(N, dtype=np.int64)
     sizes, span = [], C
@@ -58,7 +60,7 @@ def walk_counts(N: int, topk: int, GQ: int, Hkv: int, C: int = 64):
             break
         m, span = -(-m // 2), span * 2
     L = len(sizes)
-    out = dict(leaf_logits=0.0, leaf_lse=0.0, upper_logits=0.0, upper_lse=0.0, leaf_pairs=0.0)
+    out = dict(leaf_logits=0.0, leaf_lse=0.0, upper_logits=0.0, upper_lse=0.0, leaf_pairs=0.0, leaf_entries=0.0)
     surv = np.ones(N, np.int64)
     for l in range(L, 0, -1):
         M, sp = sizes[l - 1]
@@ -75,6 +77,7 @@ def walk_counts(N: int, topk: int, GQ: int, Hkv: int, C: int = 64):
             out["leaf_logits"] += float(np.where(scored, keys, 0).sum()) * GQ * Hkv
             out["leaf_lse"] += float(np.where(scored, cand, 0).sum()) * GQ * Hkv
             out["leaf_pairs"] += float(np.where(scored, cand, 0).sum()) * Hkv
+            out["leaf_entries"] += float(np.where(scored, surv, 0).sum()) * Hkv
         surv = np.where(scored, topk, cand)
     return out
 
@@ -135,7 +138,7 @@ def write_traffic(fetch_dir: str, write_dir: str, workload: str = "long256k") ->
                     "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-extras --copy-calibration; "
                     "python3 bench.py --write-traffic <fetch dir> <write dir>")}}
     # the LSE builds (score template argument 0) that the headline step runs
-    for key, srcs in (("leaf_cluster_kernel<0>", LEAF_SOURCES), ("walk_upper_delta_kernel<16, 0>", UPPER_SOURCES)):
+    for key, srcs in (("leaf_cluster_kernel<0, false>", LEAF_SOURCES), ("walk_upper_delta_kernel<16, 0>", UPPER_SOURCES)):
         f_kib, w_kib = find(fetch, key), find(write, key)
         out[f"{key.split('<')[0]}:{workload}"] = {
             "fetch_kib": f_kib, "write_kib": w_kib,
@@ -507,6 +510,12 @@ def main():
         # the launch's floor at the transcendental peak (every other instruction overlapped)
         "transcendental_floor_ms": transc / TRANSCENDENTAL_PEAK * 1e3,
     }
+    if clustered:
+        # the design's query stream: each entry (a walk and one sibling pair of leaves) reads the
+        # walk's GQ query rows once; the pair's keys stay in registers for a whole work item
+        qbytes = wc["leaf_entries"] * GQ * wl.d * 2
+        roofline["query_stream_bytes_per_launch"] = qbytes
+        roofline["query_stream_GBs"] = qbytes / (leaf_ms / 1e3) / 1e9
     walk_s = walk_ms.mean() / 1e3
     upper_transc = wc["upper_logits"] + wc["upper_lse"]
     upper_ms = float(np.mean(upper_ms))
@@ -550,6 +559,8 @@ def main():
     hbm["ledger_model_GBs"] = ledger / (ms_per_step / 1e3) / 1e9
     copy_gbs = copy_bandwidth(torch, q.device)
     hbm["device_copy_GBs"] = copy_gbs
+    if "query_stream_GBs" in roofline:
+        roofline["query_stream_frac_of_copy"] = roofline["query_stream_GBs"] / copy_gbs
     # rocprofv3 FETCH_SIZE / WRITE_SIZE (calibrated) count bytes that miss L2; the Infinity
     # Cache may serve part of them, so they bound the HBM bytes from above
     if traffic:
