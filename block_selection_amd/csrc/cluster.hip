@@ -18,8 +18,8 @@
 //   4. leaf_cluster: persistent wavefronts, each on its own, take items from
 //      counters; a wavefront loads the item's pair of leaves into registers as
 //      MFMA A fragments once, then scores the item's entries two walks at a time
-//      (the next two walks' queries are prefetched while the current ones are
-//      scored);
+//      (the queries of the next two such units are in flight while one is
+//      scored, across the whole item);
 //   5. final_topk: per walk, the K best leaf candidates in ascending order.
 // Per incidence the walk's queries (2 KiB) are read once; the keys of a pair are
 // read from memory once per work item.
@@ -511,7 +511,6 @@ __device__ inline void leaf_cluster_body(const uint16_t* __restrict__ q, const u
                                          const int4* __restrict__ items, uint32_t item_cap,
                                          const uint2* __restrict__ entries, uint32_t* __restrict__ meta,
                                          float* __restrict__ score, float* __restrict__ sink) {
-    static_assert(kItemMax % 64 == 0, "an item is scored in whole batches of 64 entries");
     // a unit is two walks (one walk per unit at four wavefronts per SIMD measured slower)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, gq = lane >> 4;
