@@ -136,7 +136,8 @@ static int range_log2(int64_t positions, int64_t groups) {
 // Workspace carve-up for `walks` walks over a pyramid of P rows per (batch, head).
 struct Workspace {
     uint16_t* planes;    // [2][B*Hkv*P*64] bf16 hi/lo planes of the summaries (bf16 inputs only)
-    uint16_t* dplanes;   // [2][B*Hkv*P*64] bf16 hi/lo planes of delta(c) = s(2c) - s(c), levels >= 2
+    uint16_t* dplanes;   // [B*Hkv*P*128] bf16: delta(c) = s(2c) - s(c) of levels >= 2, hi and lo split,
+                         // 256 bytes per node, quarter-major inside each level (delta_planes_kernel)
     int32_t* cand;       // [walks][2K] leaf candidates
     int32_t* ncand;      // [walks]
     // clustered leaf scoring (prefill, bf16 inputs)

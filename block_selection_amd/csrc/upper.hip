@@ -135,15 +135,16 @@ __device__ inline TileRows rows_buffer(buf_rsrc_t hi, buf_rsrc_t lo, int row, in
     return r;
 }
 
-// Node `row` of a level of M nodes stored chunk-major (chunk g at byte (g * M + row) * 16
-// of each plane's level region), through buffer resources based at the level's region.
-__device__ inline TileRows rows_chunk_major(buf_rsrc_t hi, buf_rsrc_t lo, int row, uint32_t M, int gq) {
-    const uint32_t o0 = ((uint32_t)gq * M + (uint32_t)row) << 4, o1 = o0 + (M << 6);   // chunks gq, 4 + gq
+// The delta row of node `row` of a level of M nodes in the quarter-major layout of the delta
+// planes (see delta_planes_kernel): lane quarter gq reads the 64 bytes of (gq, row), hi chunks
+// gq and 4 + gq then lo chunks gq and 4 + gq, through a buffer resource based at the level.
+__device__ inline TileRows rows_quarter_major(buf_rsrc_t lvl, int row, uint32_t M, int gq) {
+    const uint32_t o = ((uint32_t)gq * M + (uint32_t)row) << 6;
     TileRows r;
-    r.h0 = load_b128(hi, o0);
-    r.h1 = load_b128(hi, o1);
-    r.l0 = load_b128(lo, o0);
-    r.l1 = load_b128(lo, o1);
+    r.h0 = load_b128(lvl, o);
+    r.h1 = load_b128(lvl, o + 16);
+    r.l0 = load_b128(lvl, o + 32);
+    r.l1 = load_b128(lvl, o + 48);
     return r;
 }
 
@@ -299,14 +300,15 @@ __global__ __launch_bounds__(kUpperThreads) void walk_upper_f32_kernel(const flo
 // only at the first scored level of a walk (to start P), and the children of the one
 // ragged node of a level (a partial right child) are read directly.
 
-// delta planes: node c of level l >= 2 holds hi/lo bf16 planes of
+// delta planes: node c of level l >= 2 holds the hi/lo bf16 split of
 // 2 (s_{l-1}(2c) - s_l(c)) * log2(e)/8 (the doubled delta), rounded like the summary
-// planes. Chunk-major inside each level of a sequence: the level's M rows keep their
-// place in the plane (M * 128 bytes from its first row), and chunk g (dims 8g .. 8g+7,
-// 16 bytes) of node c sits at byte (g * M + c) * 16 of it. The walk gathers one chunk of
-// 16 candidates per quarter-wavefront and instruction; candidates come as sibling pairs,
-// which this layout puts side by side, so a quarter-wavefront touches at most 8 cache
-// lines per load instead of 16 (the tag lookups, not the bytes, bound those gathers).
+// planes, 256 bytes per node (both planes). Quarter-major inside each level of a sequence:
+// the level's M nodes take M * 256 bytes from twice its first row's summary offset, and
+// the 64 bytes that MFMA lane quarter q needs of node c (hi chunks q and 4 + q, lo chunks q
+// and 4 + q; chunk g = dims 8g .. 8g+7, 16 bytes) sit together at byte (q * M + c) * 64. A
+// walk's 16 candidates come as sibling pairs, which this puts in one 128-byte line, so a
+// quarter-wavefront's four loads of a tile touch at most 8 cache lines (the row-major
+// planes took 32: the lookups, not the bytes, bound those gathers).
 // Grid: (chunks, B * Hkv); with a pack (pk.cu non-null), (D * Hkv, chunks), one row of
 // workgroups per (document, KV head).
 __global__ __launch_bounds__(256) void delta_planes_kernel(const float* __restrict__ pyr,
@@ -329,7 +331,6 @@ __global__ __launch_bounds__(256) void delta_planes_kernel(const float* __restri
     }
     int64_t total = 0;
     for (int l = 2; l <= sg.L; ++l) total += (int64_t)sg.M(l) * kD;
-    const int64_t plane_stride = (int64_t)G.B * G.Hkv * G.P * kD;
     const float* base = pyr + row0 * kD;
     for (int64_t i = (int64_t)chunk * 256 + threadIdx.x; i < total; i += (int64_t)nchunks * 256) {
         const int e = (int)(i & (kD - 1));
@@ -339,9 +340,10 @@ __global__ __launch_bounds__(256) void delta_planes_kernel(const float* __restri
         const int64_t lrow = G.off[l] + sg.shift(l), prow = lrow + r, crow = G.off[l - 1] + sg.shift(l - 1) + 2 * r;
         uint32_t hi, lo;
         split_scaled(2.0f * (base[crow * kD + e] - base[prow * kD + e]), hi, lo);
-        const int64_t o = (row0 + lrow) * kD + ((int64_t)(e >> 3) * sg.M(l) + r) * 8 + (e & 7);
+        const int g = e >> 3;
+        const int64_t o = (row0 + lrow) * (2 * kD) + (((int64_t)(g & 3) * sg.M(l) + r) * 4 + (g >> 2)) * 8 + (e & 7);
         dplanes[o] = (uint16_t)hi;
-        dplanes[plane_stride + o] = (uint16_t)lo;
+        dplanes[o + 16] = (uint16_t)lo;   // the lo chunk two 16-byte pieces on
     }
 }
 
@@ -377,10 +379,11 @@ __device__ inline void stage_upper_lds(lds_char_t* lds, const uint16_t* __restri
         const int mj = sg.M(j);
         const int64_t r0 = bh_row0 + G.off[j] + sg.shift(j);
         for (int c = threadIdx.x; c < mj * 16; c += blockDim.x) {
-            const int part = c / mj, node = c - part * mj;   // chunk part & 7 of plane part >> 3
-            const uint16_t* src = dplanes + (part >> 3) * plane_stride + r0 * kD + ((part & 7) * mj + node) * 8;
-            *reinterpret_cast<lds_u32x4_t*>(lds + (U.lds_first[j] + node) * kLdsNodeBytes + (part >> 3) * 128 +
-                                            (part & 7) * 16) = *reinterpret_cast<const u32x4*>(src);
+            // 16-byte pieces in memory order: quarter q, node, piece p (hi q, hi 4 + q, lo q, lo 4 + q)
+            const int qq = c / (4 * mj), r2 = c - qq * 4 * mj, node = r2 >> 2, pp = r2 & 3;
+            const uint16_t* src = dplanes + r0 * (2 * kD) + (int64_t)c * 8;
+            *reinterpret_cast<lds_u32x4_t*>(lds + (U.lds_first[j] + node) * kLdsNodeBytes + (pp >> 1) * 128 +
+                                            (qq + 4 * (pp & 1)) * 16) = *reinterpret_cast<const u32x4*>(src);
         }
     }
     if (U.s_level >= 2) {
@@ -493,8 +496,7 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
             }
             // (2) the delta tiles, the next tile's row in flight
             const int lds_lvl = in_lds ? U.lds_first[l] : 0;
-            const buf_rsrc_t dhi = make_rsrc(dplanes + row_l * kD, lvl_bytes);
-            const buf_rsrc_t dlo = make_rsrc(dplanes + plane_stride + row_l * kD, lvl_bytes);
+            const buf_rsrc_t dlvl = make_rsrc(dplanes + row_l * (2 * kD), 2 * lvl_bytes);
             auto pick = [&](int i, int& row) -> uint32_t {
                 const int c = row_cand(i);
                 const int rc = 2 * c + 1;                 // right child
@@ -505,7 +507,7 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
             const uint32_t Ml = (uint32_t)sg.M(l);
             auto fetch = [&](int row) -> TileRows {
                 if constexpr (in_lds) return rows_lds(lds, lds_lvl + row, gq);
-                else return rows_chunk_major(dhi, dlo, row, Ml, gq);
+                else return rows_quarter_major(dlvl, row, Ml, gq);
             };
             // each tile's in-lane head parts, then one exchange pattern leaves lane (gq, n)
             // with the sums of tile gq, column n
