@@ -714,7 +714,8 @@ __global__ __launch_bounds__(256) void final_topk_kernel(const int32_t* __restri
             if (c[j] >= 0) s = (nc[j] > K) ? sv[j] : 0.0f;
             const int cidx = (c[j] >= 0) ? c[j] : INT_MAX;
             const int nd = (2 * K == SLOTS) ? select_top_half<SLOTS>(s, cidx, i) : select_sort<SLOTS>(s, cidx, i);
-            const int nd2 = index_sort<SLOTS>((i < K) ? nd : INT_MAX, i);
+            // the K kept indices sit in slots below K <= SLOTS / 2: sort the first half of the slots
+            const int nd2 = index_sort<SLOTS / 2>((i < K) ? nd : INT_MAX, i % (SLOTS / 2));
             if (w < walks && i < K) out[w * K + i] = (nd2 != INT_MAX) ? nd2 : -1;
         }
     }

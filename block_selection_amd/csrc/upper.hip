@@ -28,7 +28,10 @@
 //     rows and heads as columns.
 //   * The coarsest levels are staged in LDS once per workgroup (their delta
 //     rows, plus the summary rows of the level where most walks start
-//     scoring); finer levels are gathered from global memory (L2).
+//     scoring); finer levels are gathered from global memory (L2), their delta
+//     rows stored quarter-major (the 64 bytes one MFMA lane quarter reads of a
+//     node together, see delta_planes_kernel). The two kinds of level run in
+//     separate loops.
 //   * Top-K: bitonic network on each walk's slots over 64-bit (score, node)
 //     keys; when 2K equals the slot count, a partial network keeps the top
 //     half as a set.
