@@ -140,7 +140,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
             const int c = shfl_i(cand, 16 * wave + n);
             const int rc = 2 * c + 1;
             const bool rv = c >= 0 && rc < Mc && rc <= (int)(t >> shc);
-            const uint32_t rvm = (uint32_t)ballot(rv);
             const int cc = (c >= 0) ? c : 0;
             const float* prow = pyr_bh + (G.off[l] + cc) * kD;
             const float* crow = pyr_bh + (G.off[lc] + 2 * cc) * kD;
@@ -161,7 +160,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
                 split8(d1, h1, l1);
                 const f32x4 acc = summary_tile_mfma(q0, q1, h0, h1, l0, l1);
                 float F, D;
-                delta_tile_sums<S>(acc, rvm, n, gq, G.GQ, F, D);
+                delta_tile_sums<S>(acc, rv, gq, G.GQ, F, D);
                 if (gq == 0) {
                     s_F[buf][16 * wave + n] = F;
                     s_D[buf][16 * wave + n] = D;
@@ -173,7 +172,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
                 split8(vp0, h0, l0);
                 split8(vp1, h1, l1);
                 const f32x4 acc = summary_tile_mfma(q0, q1, h0, h1, l0, l1);
-                const float ps = tile_head_sums(acc, gq, G.GQ);
+                const float ps = tile_head_sums(acc);
                 if (gq == 0) s_P[buf][16 * wave + n] = ps;
             }
         } else if (wave == 4) {

@@ -133,6 +133,56 @@ __device__ inline T bitonic_top_half(T key, int m) {
     return key;
 }
 
+// Value of lane l ^ (B - 1) within blocks of B lanes (the mirror image inside the block), one
+// DPP move for B <= 16.
+template <int B>
+__device__ inline uint32_t lane_mirror_u32(uint32_t v) {
+    if constexpr (B == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);    // quad_perm 1,0,3,2
+    else if constexpr (B == 4) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x1B, 0xF, 0xF, true);  // quad_perm 3,2,1,0
+    else if constexpr (B == 8) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true); // row_half_mirror
+    else {
+        static_assert(B == 16, "lane_mirror: B must be 2, 4, 8 or 16");
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true);                       // row_mirror
+    }
+}
+
+// Compare-exchange of slot m with slot m ^ (B - 1) (mirror, MIRROR) or m ^ B (xor) on plain
+// lanes: the slot whose bit H = B / 2 (mirror) or B (xor) is clear keeps the larger key.
+template <int B, bool MIRROR>
+__device__ inline void key_step_fixed(uint64_t& key, int m) {
+    uint64_t o;
+    if constexpr (MIRROR) {
+        o = ((uint64_t)lane_mirror_u32<B>((uint32_t)(key >> 32)) << 32) | lane_mirror_u32<B>((uint32_t)key);
+    } else {
+        o = lane_xor_u64<B>(key);
+    }
+    const bool low = (m & (MIRROR ? B / 2 : B)) == 0;
+    key = ((key > o) == low) ? key : o;
+}
+
+// bitonic_top_half for segments of at most 16 plain lanes, in the form whose comparators all
+// point one way: each merge of blocks of size k starts with a mirror step (slot m against m ^ (k
+// - 1)) followed by xor steps at k/4 .. 1, so every block ends sorted descending; the final
+// mirror step over the whole segment keeps max(A[i], B[SLOTS/2 - 1 - i]) of the two sorted
+// halves A, B: the larger half as a set. Every move is one DPP instruction per 32-bit word
+// (the xor network needs two for distance 4).
+template <int SLOTS>
+__device__ inline uint64_t top_half_mirror(uint64_t key, int m) {
+    static_assert(SLOTS >= 2 && SLOTS <= 16, "segments of 2 .. 16 lanes");
+    if constexpr (SLOTS >= 4) key_step_fixed<2, true>(key, m);
+    if constexpr (SLOTS >= 8) {
+        key_step_fixed<4, true>(key, m);
+        key_step_fixed<1, false>(key, m);
+    }
+    if constexpr (SLOTS >= 16) {
+        key_step_fixed<8, true>(key, m);
+        key_step_fixed<2, false>(key, m);
+        key_step_fixed<1, false>(key, m);
+    }
+    key_step_fixed<SLOTS, true>(key, m);
+    return key;
+}
+
 // The index at slot m after ordering each segment's (score, index) pairs by selection
 // order (slot 0 = the pair that precedes all others).
 template <int SLOTS, typename Lanes = SegmentLanes>

@@ -117,7 +117,8 @@ struct TileRows {
 };
 
 __device__ inline TileRows rows_lds(const lds_char_t* lds, int lds_node, int gq) {
-    const lds_char_t* p = lds + lds_node * kLdsNodeBytes;
+    // 24-bit multiply (a full-rate VALU op): LDS slots number fewer than 2^24
+    const lds_char_t* p = lds + __umul24((uint32_t)lds_node, (uint32_t)kLdsNodeBytes);
     TileRows r;
     r.h0 = *reinterpret_cast<const lds_u32x4_t*>(p + 16 * gq);
     r.h1 = *reinterpret_cast<const lds_u32x4_t*>(p + 64 + 16 * gq);
@@ -142,7 +143,7 @@ __device__ inline TileRows rows_buffer(buf_rsrc_t hi, buf_rsrc_t lo, int row, in
 // planes (see delta_planes_kernel): lane quarter gq reads the 64 bytes of (gq, row), hi chunks
 // gq and 4 + gq then lo chunks gq and 4 + gq, through a buffer resource based at the level.
 __device__ inline TileRows rows_quarter_major(buf_rsrc_t lvl, int row, uint32_t M, int gq) {
-    const uint32_t o = ((uint32_t)gq * M + (uint32_t)row) << 6;
+    const uint32_t o = (__umul24((uint32_t)gq, M) + (uint32_t)row) << 6;   // M < 2^24
     TileRows r;
     r.h0 = load_b128(lvl, o);
     r.h1 = load_b128(lvl, o + 16);
@@ -428,13 +429,14 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
 
     UpperQ<uint16_t> qf[WPW];
     int tw[WPW];   // positions of the wavefront's walks (wave-uniform; positions fit 31 bits)
+    // query rows of consecutive walks are Hq * 64 elements apart; rows past NT are not read
+    const uint16_t* qrow0p = q + ((qrow0 + grp * WPW) * G.Hq + (int64_t)kvh * G.GQ + n) * kD;
 #pragma unroll
     for (int w = 0; w < WPW; ++w) {
         const int64_t ti = grp * WPW + w;
         tw[w] = __builtin_amdgcn_readfirstlane((int)(t0 + ti));
         const bool ok = ti < NT && n < G.GQ;
-        const uint16_t* qrow = q + ((qrow0 + (ti < NT ? ti : 0)) * G.Hq + (int64_t)kvh * G.GQ + n) * kD;
-        qf[w].load(qrow, ok, gq);
+        qf[w].load(qrow0p + (int64_t)w * G.Hq * kD, ok, gq);
     }
     const int64_t my_ti = grp * WPW + wl;
     const int my_t = (int)(t0 + my_ti);
@@ -474,10 +476,15 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
             const int64_t row_l = bh_row0 + G.off[l] + sg.shift(l);
             const int64_t row_lc = bh_row0 + G.off[lc] + sg.shift(lc);
             const uint32_t lvl_bytes = (uint32_t)sg.M(l) * (kD * 2);
-            // children <= tl[w] are eligible for walk w
-            int tl[WPW];
+            // level-lc nodes up to tw[w] >> shc are eligible for walk w, so a right child 2c + 1
+            // is eligible when it is at most rlim[w] = min(Mc - 1, tw[w] >> shc): one unsigned
+            // compare, which c = -1 (2c + 1 = 0xffffffff) fails
+            uint32_t rlim[WPW];
 #pragma unroll
-            for (int w = 0; w < WPW; ++w) tl[w] = tw[w] >> shc;
+            for (int w = 0; w < WPW; ++w) {
+                const int tl = tw[w] >> shc;
+                rlim[w] = (uint32_t)(Mc - 1 < tl ? Mc - 1 : tl);
+            }
             // candidate of MFMA column n of tile i (lane 16i + n)
             auto row_cand = [&](int i) -> int { return shfl_i(cand, 16 * i + n); };
             // (1) P of the candidates of walks that were not scored at the level above:
@@ -493,19 +500,17 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
                     const int cc = (c >= 0) ? c : 0;
                     const TileRows r = s_lds ? rows_lds(lds, U.s_first + cc, gq) : rows_buffer(shi, slo, cc, gq);
                     const f32x4 acc = summary_tile_mfma(qf[i / TPW].k0, qf[i / TPW].k1, r.h0, r.h1, r.l0, r.l1);
-                    const float ps = tile_head_sums(acc, gq, G.GQ);
+                    const float ps = tile_head_sums(acc);
                     if (u == i && ((need_p >> wl) & 1)) P = ps;
                 }
             }
             // (2) the delta tiles, the next tile's row in flight
             const int lds_lvl = in_lds ? U.lds_first[l] : 0;
             const buf_rsrc_t dlvl = make_rsrc(dplanes + row_l * (2 * kD), 2 * lvl_bytes);
-            auto pick = [&](int i, int& row) -> uint32_t {
+            auto pick = [&](int i, int& row) -> bool {   // column n's candidate has an eligible right child
                 const int c = row_cand(i);
-                const int rc = 2 * c + 1;                 // right child
-                const bool rv = (c >= 0) & (rc < Mc) & (rc <= tl[i / TPW]);
-                row = (c >= 0) ? c : 0;
-                return (uint32_t)ballot(rv);              // bit n: column n has an eligible right child
+                row = c > 0 ? c : 0;
+                return (uint32_t)(2 * c + 1) <= rlim[i / TPW];
             };
             const uint32_t Ml = (uint32_t)sg.M(l);
             auto fetch = [&](int row) -> TileRows {
@@ -516,21 +521,21 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
             // with the sums of tile gq, column n
             float fp[NTILE], xp[NTILE];
             int row0;
-            uint32_t rvm = pick(0, row0);
+            bool rv = pick(0, row0);
             TileRows cur = fetch(row0);
 #pragma unroll
             for (int i = 0; i < NTILE; ++i) {
                 TileRows nxt = cur;
-                uint32_t rvm_next = 0;
+                bool rv_next = false;
                 if (i + 1 < NTILE) {
                     int rown;
-                    rvm_next = pick(i + 1, rown);
+                    rv_next = pick(i + 1, rown);
                     nxt = fetch(rown);
                 }
                 const f32x4 acc = summary_tile_mfma(qf[i / TPW].k0, qf[i / TPW].k1, cur.h0, cur.h1, cur.l0, cur.l1);
-                delta_tile_parts<S>(acc, rvm, n, gq, G.GQ, fp[i], xp[i]);
+                delta_tile_parts<S>(acc, rv, gq, G.GQ, fp[i], xp[i]);
                 cur = nxt;
-                rvm = rvm_next;
+                rv = rv_next;
             }
             float F, D;
             delta_sums4(fp, xp, F, D);
@@ -566,8 +571,12 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
             // walks with at most K candidates keep them all whatever their scores
             const uint64_t key = slot_key((cand >= 0) ? score : -INFINITY, cand, ml);
             // the survivors are the K best as a set; with 2K = SLOTS a partial network finds them
-            const uint64_t sorted = (2 * K == SLOTS) ? bitonic_top_half<SLOTS, SegmentLanes>(key, ml)
-                                                     : bitonic_desc<SLOTS, SegmentLanes>(key, ml);
+            uint64_t sorted;
+            if constexpr (SLOTS <= 16)
+                sorted = (2 * K == SLOTS) ? top_half_mirror<SLOTS>(key, ml) : bitonic_desc<SLOTS, SegmentLanes>(key, ml);
+            else
+                sorted = (2 * K == SLOTS) ? bitonic_top_half<SLOTS, SegmentLanes>(key, ml)
+                                          : bitonic_desc<SLOTS, SegmentLanes>(key, ml);
             surv_low = (ml < K) ? (uint32_t)sorted : 0u;
         } else {
             // no walk of the wavefront has more than K candidates here: all survive. Each walk's

@@ -71,11 +71,11 @@ __device__ inline f32x4 summary_tile_mfma(const bf16x8 q0, const bf16x8 q1, u32x
 // lane ^ 32). Every lane of column n receives the same bits.
 __device__ inline float heads_total(const float v[4]) { return cols4_sum((v[0] + v[1]) + (v[2] + v[3])); }
 
-// Two head sums at once, in the order of heads_total: one permlane16 exchange packs the
-// two quantities into alternate row groups, one permlane32 exchange completes both, and a
-// last permlane16 exchange hands each lane both totals of its column.
-__device__ inline void heads_total2(const float f[4], const float d[4], float& F, float& D) {
-    const float sf = (f[0] + f[1]) + (f[2] + f[3]), sd = (d[0] + d[1]) + (d[2] + d[3]);
+// Two column totals at once: sf and sd are a lane's in-lane parts of two quantities; one
+// permlane16 exchange packs them into alternate row groups, one permlane32 exchange
+// completes both as (r0 + r1) + (r2 + r3), and a last permlane16 exchange hands each lane
+// both totals of its column.
+__device__ inline void cols4_sum2(float sf, float sd, float& F, float& D) {
     // row groups 0..3 of the sum: f 0+1, d 0+1, f 2+3, d 2+3
     const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(sf), __float_as_uint(sd), false, false);
     const float S = __uint_as_float(x[0]) + __uint_as_float(x[1]);
@@ -87,13 +87,15 @@ __device__ inline void heads_total2(const float f[4], const float d[4], float& F
     D = __uint_as_float(z[1]);
 }
 
-// Head sum of the logits of each column of a summary tile (heads past the group masked).
-__device__ inline float tile_head_sums(const f32x4& acc, int gq, int GQ) {
-    float v[4] = {acc[0], acc[1], acc[2], acc[3]};
-    if (GQ != kMaxGroup) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = (4 * gq + k < GQ) ? v[k] : 0.0f;
-    }
+// Two head sums at once, in the order of heads_total.
+__device__ inline void heads_total2(const float f[4], const float d[4], float& F, float& D) {
+    cols4_sum2((f[0] + f[1]) + (f[2] + f[3]), (d[0] + d[1]) + (d[2] + d[3]), F, D);
+}
+
+// Head sum of the logits of each column of a summary tile. Heads past the group have zero
+// query rows, so their logits are exactly 0 and add nothing.
+__device__ inline float tile_head_sums(const f32x4& acc) {
+    const float v[4] = {acc[0], acc[1], acc[2], acc[3]};
     return heads_total(v);
 }
 
@@ -149,76 +151,66 @@ __device__ inline void pair_scores(const f32x4& acc, uint32_t rows_ok, int gq, i
 // One summary row (delta) per candidate replaces the two children rows. The delta rows
 // are stored doubled (2 delta: exact, as is every step below), so a tile yields x = 2d.
 
-// g(d) = log2(2^d + 2^-d) = |d| + log2(1 + 2^(-2|d|)), from x = 2d: the exponent -|x|
-// needs no multiply, and |d| = |x| / 2 folds into one fma.
-__device__ inline float pair_lse_term2(float x) {
-    return __builtin_fmaf(fabsf(x), 0.5f, __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(-fabsf(x))));
-}
-// The same pair term for each score, from x = 2d: the children's logits p +- d have mean
-// p (the term is 0: the score is the carried P) and variance d^2 = x^2 / 4.
-template <int S>
-__device__ inline float pair_term2(float x) {
-    if constexpr (S == kScoreLse) return pair_lse_term2(x);
-    if constexpr (S == kScoreMean) return 0.0f;
-    return (x * x) * (0.25f * kHalfVar2);
+// 2^-m, m = the number of heads of lane quarter gq (heads 4gq .. 4gq+3) past a group of GQ.
+__device__ inline float past_group_scale(int gq, int GQ) {
+    int m = 4 * gq + 4 - GQ;
+    m = m < 0 ? 0 : (m > 4 ? 4 : m);
+    return __uint_as_float((uint32_t)(127 - m) << 23);
 }
 
-// Per-element pair terms of a delta tile (column n = candidate n, its doubled delta row:
-// acc = 2d; lane (gq, n) holds heads 4gq .. 4gq+3): tv = the pair term of each head of the
-// group (g(d) for the LSE), or d alone when the candidate has no eligible right child (bit n
-// of rvm clear: one child, whose logit is p + d for every score), dv = 2d; heads past the
-// group are 0. The terms are computed for every element and then corrected in place by
-// selects (a tile with an ineligible right child, a group of fewer than 16 heads), so the
-// common tile carries no copy of its logits.
+// g(d) = log2(2^d + 2^-d) = |d| + log2(1 + 2^(-2|d|)); from x = 2d the exponent is -|x| (no
+// multiply) and |d| = |x| / 2. Over the four heads a lane holds, the sum of the g is taken as
+// (|x_1| + .. + |x_4|) / 2 + log2 of the product of the four factors 1 + 2^-|x_k|, each in
+// (1, 2]: one logarithm per lane and tile rather than one per head.
+//
+// In-lane parts of one delta tile (column n = candidate n, its doubled delta row: acc = 2d;
+// lane (gq, n) holds heads 4gq .. 4gq+3): x2 = the sum of the four 2d, as (x1 + x2) + (x3 +
+// x4); f = the sum of the four pair terms: the above for the LSE, 0 for the mean (the
+// children's logits p +- d have mean p: the score is the carried P), and for mean + var/2 the
+// variance terms d^2 ln2/2 = x^2 ln2/8. A candidate without an eligible right child (rv
+// false) has one child, whose logit is p + d for every score: f = x2 / 2 (halving is exact,
+// so these are the bits of the sum of the d).
+// Heads past the group have zero query rows, so their x are exactly 0: they add nothing to
+// x2, the absolute sum or the variance terms, and a factor of exactly 2 each to the product,
+// which scaling the last factor by 2^-m (past_group_scale) removes exactly (power-of-two
+// scalings round exactly). For a full group the scale is 1 and the fma is the plain add.
 template <int S>
-__device__ inline void delta_tile_terms(const f32x4& acc, uint32_t rvm, int n, int gq, int GQ, float (&tv)[4],
-                                        float (&dv)[4]) {
+__device__ inline void delta_tile_parts(const f32x4& acc, bool rv, int gq, int GQ, float& f, float& x2) {
+    x2 = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    if constexpr (S == kScoreLse) {
+        const float sc = past_group_scale(gq, GQ);
+        const float e0 = 1.0f + __builtin_amdgcn_exp2f(-fabsf(acc[0]));
+        const float e1 = 1.0f + __builtin_amdgcn_exp2f(-fabsf(acc[1]));
+        const float e2 = 1.0f + __builtin_amdgcn_exp2f(-fabsf(acc[2]));
+        const float e3 = __builtin_fmaf(sc, __builtin_amdgcn_exp2f(-fabsf(acc[3])), sc);
+        const float a = (fabsf(acc[0]) + fabsf(acc[1])) + (fabsf(acc[2]) + fabsf(acc[3]));
+        f = __builtin_fmaf(a, 0.5f, __builtin_amdgcn_logf((e0 * e1) * (e2 * e3)));
+    } else if constexpr (S == kScoreMean) {
+        f = 0.0f;
+    } else {
+        float v[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        dv[k] = acc[k];
-        tv[k] = pair_term2<S>(acc[k]);
+        for (int k = 0; k < 4; ++k) v[k] = (acc[k] * acc[k]) * (0.25f * kHalfVar2);
+        f = (v[0] + v[1]) + (v[2] + v[3]);
     }
-    if ((rvm & 0xffffu) != 0xffffu) {
-        const bool rv = (rvm >> n) & 1u;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) tv[k] = rv ? tv[k] : 0.5f * dv[k];
-    }
-    if (GQ != kMaxGroup) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const bool h = 4 * gq + k < GQ;
-            tv[k] = h ? tv[k] : 0.0f;
-            dv[k] = h ? dv[k] : 0.0f;
-        }
-    }
+    f = rv ? f : 0.5f * x2;
 }
 
 // Pair sums of one delta tile: F = sum over the group's heads of the pair terms, D = sum of
-// d (halving is exact, so D = (sum of 2d) / 2 has the bits of the sum of d). Every lane of
-// column n receives both.
+// d (D = (sum of 2d) / 2 exactly). Every lane of column n receives both.
 template <int S>
-__device__ inline void delta_tile_sums(const f32x4& acc, uint32_t rvm, int n, int gq, int GQ, float& F, float& D) {
-    float tv[4], dv[4];
-    delta_tile_terms<S>(acc, rvm, n, gq, GQ, tv, dv);
-    float D2;
-    heads_total2(tv, dv, F, D2);
+__device__ inline void delta_tile_sums(const f32x4& acc, bool rv, int gq, int GQ, float& F, float& D) {
+    float f, x2, D2;
+    delta_tile_parts<S>(acc, rv, gq, GQ, f, x2);
+    cols4_sum2(f, x2, F, D2);
     D = 0.5f * D2;
-}
-
-// In-lane parts of delta_tile_sums: the terms added as (t0 + t1) + (t2 + t3).
-template <int S>
-__device__ inline void delta_tile_parts(const f32x4& acc, uint32_t rvm, int n, int gq, int GQ, float& f, float& x2) {
-    float tv[4], dv[4];
-    delta_tile_terms<S>(acc, rvm, n, gq, GQ, tv, dv);
-    f = (tv[0] + tv[1]) + (tv[2] + tv[3]);
-    x2 = (dv[0] + dv[1]) + (dv[2] + dv[3]);
 }
 
 // The pair sums of four delta tiles at once, scattered: lane (gq, n) receives F and D of
 // tile gq, column n. f[i], x2[i] are tile i's in-lane parts (delta_tile_parts). The row
-// groups are added as (r0 + r1) + (r2 + r3), the order of heads_total2, so every total has
-// the bits the tile would get alone: four permlane16 exchanges add row pairs (0, 1) and
-// (2, 3) while halving the values each lane holds, two permlane32 exchanges add the pairs.
+// groups are added as (r0 + r1) + (r2 + r3), the order of cols4_sum2, so every total has the
+// bits delta_tile_sums gives the tile alone: four permlane16 exchanges add row pairs (0, 1)
+// and (2, 3) while halving the values each lane holds, two permlane32 exchanges add the pairs.
 __device__ inline void delta_sums4(const float (&f)[4], const float (&x2)[4], float& F, float& D) {
     auto pair16 = [](float a, float b) -> float {   // rows 0, 2: a of rows 0+1 / 2+3; rows 1, 3: b
         const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
@@ -253,12 +245,13 @@ __device__ inline void ragged_sums(const f32x4& acc, int gq, int GQ, float& F, f
 }
 
 // Selection key that also records the slot a candidate came from: selection order
-// (score desc, node asc); low word (2^26 - 1 - node) << 6 | slot, 0 for an empty slot.
-// Nodes of levels >= 2 are below 2^24.
+// (score desc, node asc); low word (2^26 - 1 - node) << 6 | slot, and for an empty slot
+// (node -1) the slot alone: low >> 6 = 0 marks it. Nodes of levels >= 2 are below 2^24.
 __device__ inline uint64_t slot_key(float s, int node, int slot) {
     const uint32_t u = __float_as_uint(s + 0.0f);
-    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    const uint32_t low = (node >= 0) ? (((uint32_t)((1 << 26) - 1 - node) << 6) | (uint32_t)slot) : 0u;
+    const uint32_t o = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+    // (~node) << 6 is (2^26 - 1 - node) << 6 for 0 <= node < 2^26, and 0 for node = -1
+    const uint32_t low = ((uint32_t)~node << 6) | (uint32_t)slot;
     return ((uint64_t)o << 32) | low;
 }
 __device__ inline int key_node(uint32_t low) { return (low >> 6) ? (1 << 26) - 1 - (int)(low >> 6) : -1; }
