@@ -101,15 +101,24 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(const uint1
     // candidate slot = lane; slot 2i + c holds child c of survivor i. A survivor is kept as
     // the low word of its selection key (node and the slot it came from); Pa / Pb hold, in
     // the slot a candidate was scored in, the head-summed logits of its two children.
+    // Levels of at most K nodes keep every eligible node unscored: the walk starts at the
+    // highest level with more than K nodes (at most 2K), node m in slot m, else at the root.
+    int ls = G.L;
+    for (int j = G.L; j >= 2; --j) {
+        if (G.M[j] > K) {
+            ls = j;
+            break;
+        }
+    }
     uint32_t surv_low = 0;
     float Pa = 0.0f, Pb = 0.0f;
     bool pk = false;                 // P of this level's candidates known (scored level above)
     int buf = 0;
-    for (int l = G.L; l >= 2; --l) {
+    for (int l = ls; l >= 2; --l) {
         int cand;
         float P = 0.0f;
-        if (l == G.L) {
-            cand = (lane == 0) ? 0 : -1;
+        if (l == ls) {
+            cand = (lane < G.M[l] && lane <= (int)(t >> (kLog2C + l - 1))) ? lane : -1;
         } else {
             const uint32_t lowk = (uint32_t)shfl_i((int)surv_low, lane >> 1);
             const int pnode = key_node(lowk);

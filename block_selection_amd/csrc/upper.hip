@@ -442,6 +442,17 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
     const int my_t = (int)(t0 + my_ti);
     const bool my_ok = my_ti < NT;
 
+    // Levels of at most K nodes keep every eligible node unscored, so the walk starts at the
+    // highest level with more than K nodes (at most 2K, since the level above has at most K):
+    // its candidates are its eligible nodes, node m in slot m. Without such a level it starts at
+    // the root.
+    int ls = sg.L;
+    for (int j = sg.L; j >= 2; --j) {
+        if (sg.M(j) > K) {
+            ls = j;
+            break;
+        }
+    }
     uint32_t surv_low = 0;     // sorted key low word in slots < K: the survivors
     float Pa = 0.0f, Pb = 0.0f;  // head-summed logits of this slot's candidate's children
     uint32_t pk = 0;           // walks whose candidates' P is known (scored at the level above)
@@ -450,8 +461,8 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
         constexpr bool in_lds = decltype(in_lds_const)::value;
         int cand;
         float P = 0.0f;
-        if (l == sg.L) {
-            cand = (ml == 0 && my_ok) ? 0 : -1;
+        if (l == ls) {
+            cand = (my_ok && ml < sg.M(l) && ml <= (my_t >> (kLog2C + l - 1))) ? ml : -1;
         } else {
             const uint32_t lowk = (uint32_t)shfl_i((int)surv_low, dslot_lane<SLOTS>(wl, ml >> 1));
             const int pnode = key_node(lowk);
@@ -592,7 +603,7 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
     };
     // the levels down to the last one staged in LDS (the levels above it are not scored), then
     // the gathered ones: each phase without a per-tile choice of source
-    int l = sg.L;
+    int l = ls;
     if (U.j_lo <= U.j_hi)
         for (; l >= 2 && l >= U.j_lo; --l) level(l, std::true_type{});
     for (; l >= 2; --l) level(l, std::false_type{});
