@@ -66,6 +66,10 @@ def _load():
     lib.pisa_oracle_flat_select.restype = i32
     lib.pisa_oracle_flat_validate.argtypes = [P, i64, i32, P, i64, i32, i32, i32, i32, i32, P, dbl]
     lib.pisa_oracle_flat_validate.restype = i32
+    lib.pisa_oracle_flat_exact_select.argtypes = [P, P, i64, P, i64, i32, i32, i32, i32, i32, P, P, i32]
+    lib.pisa_oracle_flat_exact_select.restype = i32
+    lib.pisa_oracle_flat_exact_validate.argtypes = [P, i64, i32, P, i64, i32, i32, i32, i32, i32, P, dbl]
+    lib.pisa_oracle_flat_exact_validate.restype = i32
     _lib = lib
     return lib
 
@@ -318,3 +322,42 @@ def varlen_walk(q: np.ndarray, k: np.ndarray, cu: np.ndarray, topk: int, rows=No
         i_, g_, l_ = walk(q[rows[sel]], rows[sel] - lo, k[lo:hi], pyrs[dd], topk, C, g, nthreads, score)
         idx[sel], gap[sel], lvl[sel] = i_, g_, l_
     return idx, gap, lvl
+
+
+def flat_exact_select(q_rows: np.ndarray, t_rows, k: np.ndarray, topk: int, C: int = 64, nthreads: int = 0):
+    """Exact flat selection: each query scores every eligible leaf block as the walk scores a
+    leaf candidate (the sum over its group's heads of the LSE of q.k/sqrt(d) over the block's
+    raw keys up to t) and keeps the K best.
+
+    q_rows: float [n, Hq, d]; k: float [N, Hkv, d] raw keys.
+    Returns (idx int32 [n, Hkv, topk] ascending, -1 padded; min_gap double [n, Hkv]).
+    """
+    q_rows = _f32(q_rows)
+    k = _f32(k)
+    t_rows = np.ascontiguousarray(t_rows, dtype=np.int64)
+    n, Hq, d = q_rows.shape
+    N, Hkv, _ = k.shape
+    assert t_rows.shape == (n,)
+    idx = np.zeros((n, Hkv, topk), np.int32)
+    gap = np.zeros((n, Hkv), np.float64)
+    rc = _load().pisa_oracle_flat_exact_select(_p(q_rows), _p(t_rows), n, _p(k), N, Hq, Hkv, d, C, topk, _p(idx),
+                                               _p(gap), nthreads)
+    if rc != 0:
+        raise RuntimeError(f"oracle flat_exact_select failed ({rc})")
+    return idx, gap
+
+
+def flat_exact_validate(q_row: np.ndarray, t: int, j: int, k: np.ndarray, topk: int, target, eps: float,
+                        C: int = 64) -> int:
+    """1 if target is the exact flat selection under some resolution of the near-ties within
+    eps, else 0."""
+    q_row = _f32(q_row)
+    k = _f32(k)
+    Hq, d = q_row.shape
+    N, Hkv, _ = k.shape
+    tg = np.ascontiguousarray(target, dtype=np.int32)
+    assert tg.shape == (topk,)
+    r = _load().pisa_oracle_flat_exact_validate(_p(q_row), t, j, _p(k), N, Hq, Hkv, d, C, topk, _p(tg), eps)
+    if r == -2:
+        raise RuntimeError("oracle flat_exact_validate: bad arguments")
+    return int(r)

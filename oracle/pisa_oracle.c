@@ -33,7 +33,8 @@
  *     (and the ai4snews summary's first paragraph): the conventional stage one
  *     the pyramid replaces scores every block summary against the query and
  *     keeps the best K -- the flat selection below, with the leaf means as the
- *     summaries.
+ *     summaries; its exact counterpart scores every eligible leaf as the walk
+ *     scores a leaf candidate (the LSE over its raw keys).
  *
  * Readings taken where the pages are silent (each listed in the design notes):
  *   logit = q.k / sqrt(d); level sizes M_{l+1} = ceil(M_l / g) up to one node;
@@ -610,6 +611,44 @@ static int64_t flat_sorted(const geom_t* G, const float* q, const double* pyr, i
     return n;
 }
 
+/* The K best of a sorted candidate list, ascending, -1 padded; the gap S_(K) - S_(K+1)
+ * (INFINITY when at most K candidates are eligible). */
+static void flat_keep(const scored_t* sc, int64_t n, int topk, int32_t* out, double* gap) {
+    int64_t keep[ORACLE_MAX_TOPK];
+    const int nk = (n < topk) ? (int)n : topk;
+    for (int c = 0; c < nk; c++) keep[c] = sc[c].node;
+    qsort(keep, (size_t)nk, sizeof(int64_t), cmp_i64);
+    for (int c = 0; c < topk; c++) out[c] = (c < nk) ? (int32_t)keep[c] : -1;
+    if (gap) *gap = (n > topk) ? sc[topk - 1].s - sc[topk].s : INFINITY;
+}
+
+/* 1 if `target` (topk entries, -1 padded, any order) is the K best of the sorted list sc[0..n)
+ * under some resolution of the scores within eps of the K-th score: it holds min(K, n)
+ * distinct eligible candidates, every one scoring more than eps above the K-th, and none
+ * scoring more than eps below it. */
+static int flat_check(const scored_t* sc, int64_t n, int topk, const int32_t* target, double eps) {
+    const int want = (n < topk) ? (int)n : topk;
+    int ok = 1, cnt = 0;
+    for (int c = 0; c < topk && ok; c++) {
+        const int32_t b = target[c];
+        if (b < 0) continue;
+        if (b >= n) { ok = 0; break; }                       /* not eligible */
+        for (int e = 0; e < c; e++) if (target[e] == b) ok = 0;   /* duplicate */
+        cnt++;
+    }
+    if (ok && cnt != want) ok = 0;
+    if (ok && n > topk) {
+        const double sK = sc[topk - 1].s;
+        for (int64_t r = 0; r < n && ok; r++) {
+            int in = 0;
+            for (int c = 0; c < topk; c++) if (target[c] == sc[r].node) in = 1;
+            if (sc[r].s > sK + eps && !in) ok = 0;           /* surely kept, missing */
+            if (sc[r].s < sK - eps && in) ok = 0;            /* surely dropped, present */
+        }
+    }
+    return ok;
+}
+
 /*
  * Flat selection for the query rows of positions t_rows (one batch element).
  * q_rows: float [n_rows, Hq, d]; pyr from pisa_oracle_build_pyramid over N keys.
@@ -634,25 +673,14 @@ int pisa_oracle_flat_select(const float* q_rows, const int64_t* t_rows, int64_t 
         const int64_t i = w / Hkv;
         const int j = (int)(w % Hkv);
         scored_t* sc = (scored_t*)malloc(sizeof(scored_t) * (size_t)G.M[1]);
-        int64_t* keep = (int64_t*)malloc(sizeof(int64_t) * (size_t)topk);
         const int64_t n = flat_sorted(&G, q_rows + i * (int64_t)Hq * d, pyr, t_rows[i], j, sc);
-        const int nk = (n < topk) ? (int)n : topk;
-        for (int c = 0; c < nk; c++) keep[c] = sc[c].node;
-        qsort(keep, (size_t)nk, sizeof(int64_t), cmp_i64);
-        for (int c = 0; c < topk; c++) out_idx[w * topk + c] = (c < nk) ? (int32_t)keep[c] : -1;
-        if (min_gap) min_gap[w] = (n > topk) ? sc[topk - 1].s - sc[topk].s : INFINITY;
+        flat_keep(sc, n, topk, out_idx + w * topk, min_gap ? min_gap + w : NULL);
         free(sc);
-        free(keep);
     }
     return 0;
 }
 
-/*
- * Near-tie check of a flat selection: 1 if `target` (topk entries, -1 padded, any order)
- * is the K best eligible blocks under some resolution of the scores within eps of the
- * K-th score (it holds min(K, eligible) distinct eligible blocks, every block scoring more
- * than eps above the K-th, and none scoring more than eps below it), else 0.
- */
+/* Near-tie check of a flat selection (flat_check) for position t, KV head j. */
 int pisa_oracle_flat_validate(const float* q_row, int64_t t, int j, const double* pyr, int64_t N, int Hq,
                               int Hkv, int d, int C, int topk, const int32_t* target, double eps) {
     geom_t G;
@@ -661,25 +689,77 @@ int pisa_oracle_flat_validate(const float* q_row, int64_t t, int j, const double
     if (t < 0 || t >= N || j < 0 || j >= Hkv) return -2;
     scored_t* sc = (scored_t*)malloc(sizeof(scored_t) * (size_t)G.M[1]);
     const int64_t n = flat_sorted(&G, q_row, pyr, t, j, sc);
-    const int want = (n < topk) ? (int)n : topk;
-    int ok = 1, cnt = 0;
-    for (int c = 0; c < topk && ok; c++) {
-        const int32_t b = target[c];
-        if (b < 0) continue;
-        if (b >= n) { ok = 0; break; }                       /* not eligible */
-        for (int e = 0; e < c; e++) if (target[e] == b) ok = 0;   /* duplicate */
-        cnt++;
+    const int ok = flat_check(sc, n, topk, target, eps);
+    free(sc);
+    return ok;
+}
+
+/*
+ * Flat selection by the exact leaf score (the exhaustive selection by the walk's own leaf
+ * score, against which the walk's choice of blocks is measured): every eligible leaf block b
+ * (b*C <= t) is scored the way the walk scores a candidate at the leaf level -- the sum over
+ * the group's heads of the LogSumExp of the scaled dot products with the block's raw keys up
+ * to t (node_score at level 1; reading note, "Scoring: LogSumExp" and section 4.1) -- and the
+ * K best are kept, with no hierarchy. Equal scores rank the lower block first.
+ */
+static int64_t flat_exact_sorted(const geom_t* G, const float* q, const float* k, int64_t t, int j,
+                                 scored_t* sc, double* scratch) {
+    int64_t n = t / G->C + 1;
+    if (n > G->M[1]) n = G->M[1];
+    for (int64_t b = 0; b < n; b++) {
+        sc[b].node = b;
+        sc[b].s = node_score(G, q, k, NULL, t, j, 1, b, scratch);
     }
-    if (ok && cnt != want) ok = 0;
-    if (ok && n > topk) {
-        const double sK = sc[topk - 1].s;
-        for (int64_t r = 0; r < n && ok; r++) {
-            int in = 0;
-            for (int c = 0; c < topk; c++) if (target[c] == sc[r].node) in = 1;
-            if (sc[r].s > sK + eps && !in) ok = 0;           /* surely kept, missing */
-            if (sc[r].s < sK - eps && in) ok = 0;            /* surely dropped, present */
-        }
+    qsort(sc, (size_t)n, sizeof(scored_t), cmp_scored);
+    return n;
+}
+
+/*
+ * Exact flat selection for the query rows of positions t_rows (one batch element).
+ * q_rows: float [n_rows, Hq, d]; k: float [N, Hkv, d] raw keys. Outputs as
+ * pisa_oracle_flat_select.
+ */
+int pisa_oracle_flat_exact_select(const float* q_rows, const int64_t* t_rows, int64_t n_rows, const float* k,
+                                  int64_t N, int Hq, int Hkv, int d, int C, int topk, int32_t* out_idx,
+                                  double* min_gap, int nthreads) {
+    geom_t G;
+    if (topk < 1 || topk > ORACLE_MAX_TOPK) return -1;
+    if (make_geom(&G, N, Hq, Hkv, d, C, 2, topk) != 0) return -1;
+    G.score = SCORE_LSE;
+    for (int64_t i = 0; i < n_rows; i++) if (t_rows[i] < 0 || t_rows[i] >= N) return -2;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    const int64_t total = n_rows * Hkv;
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t w = 0; w < total; w++) {
+        const int64_t i = w / Hkv;
+        const int j = (int)(w % Hkv);
+        scored_t* sc = (scored_t*)malloc(sizeof(scored_t) * (size_t)G.M[1]);
+        double* scratch = (double*)malloc(sizeof(double) * (size_t)(C + d));
+        const int64_t n = flat_exact_sorted(&G, q_rows + i * (int64_t)Hq * d, k, t_rows[i], j, sc, scratch);
+        flat_keep(sc, n, topk, out_idx + w * topk, min_gap ? min_gap + w : NULL);
+        free(scratch);
+        free(sc);
     }
+    return 0;
+}
+
+/* Near-tie check of an exact flat selection (flat_check) for position t, KV head j. */
+int pisa_oracle_flat_exact_validate(const float* q_row, int64_t t, int j, const float* k, int64_t N, int Hq,
+                                    int Hkv, int d, int C, int topk, const int32_t* target, double eps) {
+    geom_t G;
+    if (topk < 1 || topk > ORACLE_MAX_TOPK) return -2;
+    if (make_geom(&G, N, Hq, Hkv, d, C, 2, topk) != 0) return -2;
+    G.score = SCORE_LSE;
+    if (t < 0 || t >= N || j < 0 || j >= Hkv) return -2;
+    scored_t* sc = (scored_t*)malloc(sizeof(scored_t) * (size_t)G.M[1]);
+    double* scratch = (double*)malloc(sizeof(double) * (size_t)(C + d));
+    const int64_t n = flat_exact_sorted(&G, q_row, k, t, j, sc, scratch);
+    const int ok = flat_check(sc, n, topk, target, eps);
+    free(scratch);
     free(sc);
     return ok;
 }

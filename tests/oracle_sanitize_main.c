@@ -32,6 +32,16 @@ int pisa_oracle_validate(const float* q_row, int64_t t, int j, const float* k, c
 int pisa_oracle_attention(const float* q_rows, const int64_t* t_rows, int64_t n_rows, const float* k, const float* v,
                           const int32_t* idx, int64_t N, int Hq, int Hkv, int d, int C, int topk, double* out,
                           int nthreads);
+int pisa_oracle_flat_select(const float* q_rows, const int64_t* t_rows, int64_t n_rows, const double* pyr,
+                            int64_t N, int Hq, int Hkv, int d, int C, int topk, int32_t* out_idx,
+                            double* min_gap, int nthreads);
+int pisa_oracle_flat_validate(const float* q_row, int64_t t, int j, const double* pyr, int64_t N, int Hq,
+                              int Hkv, int d, int C, int topk, const int32_t* target, double eps);
+int pisa_oracle_flat_exact_select(const float* q_rows, const int64_t* t_rows, int64_t n_rows, const float* k,
+                                  int64_t N, int Hq, int Hkv, int d, int C, int topk, int32_t* out_idx,
+                                  double* min_gap, int nthreads);
+int pisa_oracle_flat_exact_validate(const float* q_row, int64_t t, int j, const float* k, int64_t N, int Hq,
+                                    int Hkv, int d, int C, int topk, const int32_t* target, double eps);
 
 static int failures = 0;
 #define CHECK(cond, ...)                                   \
@@ -110,6 +120,16 @@ static void random_case(int64_t N, int Hq, int Hkv, int K, int score) {
     double* att = (double*)malloc(sizeof(double) * (size_t)nt * Hq * d);
     CHECK(pisa_oracle_attention(qr, ts, nt, k, v, idx, N, Hq, Hkv, d, C, K, att, 2) == 0, "attention");
     free(att);
+    /* both flat selections, each validating its own result */
+    int32_t* fidx = (int32_t*)malloc(sizeof(int32_t) * (size_t)nt * Hkv * K);
+    double* fgap = (double*)malloc(sizeof(double) * (size_t)nt * Hkv);
+    CHECK(pisa_oracle_flat_select(qr, ts, nt, pyr, N, Hq, Hkv, d, C, K, fidx, fgap, 2) == 0, "flat");
+    CHECK(pisa_oracle_flat_validate(qr, ts[0], 0, pyr, N, Hq, Hkv, d, C, K, fidx, 1e-3) == 1, "flat validate");
+    CHECK(pisa_oracle_flat_exact_select(qr, ts, nt, k, N, Hq, Hkv, d, C, K, fidx, fgap, 2) == 0, "flat exact");
+    CHECK(pisa_oracle_flat_exact_validate(qr, ts[0], 0, k, N, Hq, Hkv, d, C, K, fidx, 1e-3) == 1,
+          "flat exact validate");
+    free(fidx);
+    free(fgap);
     free(q); free(qr); free(k); free(v); free(pyr); free(ts); free(idx); free(gap); free(lvl);
 }
 
