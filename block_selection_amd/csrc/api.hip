@@ -55,6 +55,8 @@ __global__ void decode_attention_kernel(const uint16_t*, const uint16_t*, const 
 __global__ void flat_planes_kernel(const float*, Geom, uint16_t*);
 template <typename KT, int CAP>
 __global__ void flat_select_kernel(const KT*, const uint16_t*, Geom, int32_t*);
+__global__ void flat_exact_scores_kernel(const uint16_t*, const uint16_t*, Geom, float*);
+__global__ void flat_exact_topk_kernel(const float*, Geom, int32_t*);
 constexpr int kDecAttnBlocksPerGroup = 4;                          // wavefronts (blocks) per workgroup
 // A decoding step (selection or attention) spreads each sequence's leaf or block work over
 // several workgroups only while the whole grid stays within this many: past it the
@@ -983,6 +985,39 @@ int pisa_select_flat(const void* q, const float* pyramid, int64_t N, int64_t n_c
         if (small) hipLaunchKernelGGL((flat_select_kernel<float, 32>), grid, block, 0, s, (const float*)q, planes, G, out_idx);
         else hipLaunchKernelGGL((flat_select_kernel<float, 64>), grid, block, 0, s, (const float*)q, planes, G, out_idx);
     }
+    return launch_status();
+}
+
+// Exact flat selection: the score of every (position, eligible leaf), fp32, B * Hkv * N * M1.
+static size_t flat_exact_ws(const pisa_dims* d, int64_t N) {
+    const int64_t m1 = (N + kC - 1) / kC;
+    return align_up((size_t)d->B * d->Hkv * N * m1 * sizeof(float));
+}
+
+size_t pisa_flat_exact_workspace_bytes(const pisa_dims* dims, int64_t N, int64_t n_capacity) {
+    Geom G;
+    if (check_dims(dims) != PISA_OK || make_geom(dims, N, n_capacity, &G) != PISA_OK) return 0;
+    return flat_exact_ws(dims, N);
+}
+
+int pisa_select_flat_exact(const void* q, const void* k, int64_t N, int64_t n_capacity, const pisa_dims* dims,
+                           int32_t* out_idx, void* workspace, size_t ws_bytes, void* stream) {
+    int rc = check_dims(dims);
+    if (rc != PISA_OK) return rc;
+    if (!q || !k || !out_idx) return PISA_ERR_INVALID_ARG;
+    if (dims->dtype != PISA_DTYPE_BF16 || dims->score != PISA_SCORE_LSE) return PISA_ERR_UNSUPPORTED;
+    Geom G;
+    if ((rc = make_geom(dims, N, n_capacity, &G)) != PISA_OK) return rc;
+    const int64_t chunks = (N + kGrpKeys - 1) / kGrpKeys;             // 128 positions per workgroup
+    const int64_t walks = (int64_t)dims->B * N * dims->Hkv;
+    if (chunks > INT_MAX || (walks + 3) / 4 > INT_MAX || (int64_t)dims->B * dims->Hkv > 65535)
+        return PISA_ERR_UNSUPPORTED;
+    if (!workspace || ws_bytes < flat_exact_ws(dims, N)) return PISA_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    float* S = (float*)workspace;
+    hipLaunchKernelGGL(flat_exact_scores_kernel, dim3((unsigned)chunks, (unsigned)(dims->B * dims->Hkv)), dim3(256),
+                       0, s, (const uint16_t*)q, (const uint16_t*)k, G, S);
+    hipLaunchKernelGGL(flat_exact_topk_kernel, dim3((unsigned)((walks + 3) / 4)), dim3(256), 0, s, S, G, out_idx);
     return launch_status();
 }
 

@@ -251,4 +251,40 @@ template __global__ void flat_select_kernel<uint16_t, 64>(const uint16_t*, const
 template __global__ void flat_select_kernel<float, 32>(const float*, const uint16_t*, Geom, int32_t*);
 template __global__ void flat_select_kernel<float, 64>(const float*, const uint16_t*, Geom, int32_t*);
 
+// Top K per (position, KV head) of the exact flat scores S (flat_exact_scores_kernel in
+// cluster.hip): one wavefront per walk w = (b * N + t) * Hkv + kvh (the output's order), four
+// per workgroup. The wavefront keeps the 64 best selection keys (score, then the lower block)
+// sorted in descending order over its lanes; the keys of each next 64 eligible blocks are sorted
+// ascending and merged in: slot i keeps the larger of kept key i and new key i, which leaves the
+// 64 best as a bitonic sequence, and the descending merge (the last stage of a 64-slot sort)
+// orders it again. The K best are then listed by block index, -1 padded.
+__global__ __launch_bounds__(256) void flat_exact_topk_kernel(const float* __restrict__ S, Geom G,
+                                                              int32_t* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (w >= (int64_t)G.B * G.N * G.Hkv) return;   // wavefront-uniform
+    const int kvh = (int)(w % G.Hkv);
+    const int64_t bt = w / G.Hkv, b = bt / G.N, t = bt % G.N;
+    const int64_t M1 = G.M[1];
+    const int64_t n_el = (t / kC + 1 < M1) ? t / kC + 1 : M1;   // blocks 0 .. n_el - 1 are eligible
+    const float* row = S + ((b * G.Hkv + kvh) * G.N + t) * M1;
+    uint64_t best = 0ull;   // 0: an empty slot, below every key
+    for (int64_t L0 = 0; L0 < n_el; L0 += 64) {
+        const int64_t L = L0 + lane;
+        uint64_t key = (L < n_el) ? select_key(row[L], (int)L) : 0ull;
+        key = ~bitonic_desc<64, SegmentLanes>(~key, lane);   // ascending
+        best = (best > key) ? best : key;
+        key_step<32, 32>(best, lane, 64);
+        key_step<16, 16>(best, lane, 64);
+        key_step<8, 8>(best, lane, 64);
+        key_step<4, 4>(best, lane, 64);
+        key_step<2, 2>(best, lane, 64);
+        key_step<1, 1>(best, lane, 64);
+    }
+    const int K = G.topk;
+    const int nd = (lane < K && best != 0ull) ? key_index(best) : INT_MAX;
+    const int srt = index_sort<64>(nd, lane);
+    if (lane < K) out[w * K + lane] = (srt != INT_MAX) ? srt : -1;
+}
+
 }  // namespace pisa

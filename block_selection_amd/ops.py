@@ -33,7 +33,8 @@ EXPORTED = ("pisa_pyramid_nodes", "pisa_level_offset", "pisa_pyramid_bytes", "pi
             "pisa_build_pyramid_packed", "pisa_select_prefill_packed", "pisa_attention_workspace_bytes",
             "pisa_sparse_attention", "pisa_pack_attention_workspace_bytes", "pisa_sparse_attention_packed",
             "pisa_decode_attention", "pisa_decode_attention_workspace_bytes", "pisa_flat_workspace_bytes",
-            "pisa_select_flat", "pisa_decode_update_select_noalloc")
+            "pisa_select_flat", "pisa_decode_update_select_noalloc", "pisa_flat_exact_workspace_bytes",
+            "pisa_select_flat_exact")
 
 
 class Dims(ctypes.Structure):
@@ -103,6 +104,10 @@ def _load() -> ctypes.CDLL:
     lib.pisa_flat_workspace_bytes.restype = sz
     lib.pisa_select_flat.argtypes = [P, P, i64, i64, D, P, P, sz, P]
     lib.pisa_select_flat.restype = ctypes.c_int
+    lib.pisa_flat_exact_workspace_bytes.argtypes = [D, i64, i64]
+    lib.pisa_flat_exact_workspace_bytes.restype = sz
+    lib.pisa_select_flat_exact.argtypes = [P, P, i64, i64, D, P, P, sz, P]
+    lib.pisa_select_flat_exact.restype = ctypes.c_int
     lib.pisa_decode_update_select_noalloc.argtypes = [P, P, P, P, i64, i64, D, P, P]
     lib.pisa_decode_update_select_noalloc.restype = ctypes.c_int
     lib.pisa_status_string.argtypes = [ctypes.c_int]
@@ -412,3 +417,31 @@ def select_flat(q: torch.Tensor, pyramid: torch.Tensor, N: int, n_capacity: int,
                               _ptr(workspace), ws_n, _stream(stream))
     if rc != PISA_OK:
         raise PisaError("pisa_select_flat", rc)
+
+
+# ------------------------------------------------------------ exact flat selection --
+# Every eligible leaf block scored by the exact LSE over its raw keys up to t (summed over the
+# group's heads), the K best kept: the ground truth the walk's recall is measured against.
+# bf16 and the LSE score only; out_idx [B, N, Hkv, K] as select_prefill writes it.
+
+def flat_exact_workspace_bytes(dims: Dims, N: int, n_capacity: Optional[int] = None) -> int:
+    cap = N if n_capacity is None else n_capacity
+    return int(lib.pisa_flat_exact_workspace_bytes(ctypes.byref(dims), N, cap))
+
+
+def alloc_flat_exact_workspace(dims: Dims, N: int, n_capacity: Optional[int] = None,
+                               device="cuda") -> Optional[torch.Tensor]:
+    n = flat_exact_workspace_bytes(dims, N, n_capacity)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def select_flat_exact(q: torch.Tensor, k: torch.Tensor, N: int, n_capacity: int, dims: Dims,
+                      out_idx: torch.Tensor, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    _check(q, "q", dims.torch_dtype, dims.B * N * dims.Hq * dims.d)
+    _check(k, "k", dims.torch_dtype, dims.B * n_capacity * dims.Hkv * dims.d)
+    _check(out_idx, "out_idx", torch.int32, dims.B * N * dims.Hkv * dims.topk)
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.pisa_select_flat_exact(_ptr(q), _ptr(k), N, n_capacity, ctypes.byref(dims), _ptr(out_idx),
+                                    _ptr(workspace), ws_n, _stream(stream))
+    if rc != PISA_OK:
+        raise PisaError("pisa_select_flat_exact", rc)

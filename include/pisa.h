@@ -354,6 +354,37 @@ size_t pisa_flat_workspace_bytes(const pisa_dims* dims, int64_t N, int64_t n_cap
 int pisa_select_flat(const void* q, const float* pyramid, int64_t N, int64_t n_capacity, const pisa_dims* dims,
                      int32_t* out_idx, void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------- exact flat selection
+ *
+ * The selection the pyramid approximates, taken exactly (reading note "Block Sparse
+ * Attention with Log-Linear Complexity", "Scoring: LogSumExp" and the accuracy comparison
+ * of section 4.1): every eligible leaf block is scored as the walk scores a leaf candidate --
+ * the sum over the group's query heads h of log sum_{s in block b, s <= t} exp(q_{t,h} . k_s
+ * / sqrt(d)) over the block's raw keys -- and the K best are kept, with no hierarchy. Block b
+ * is eligible iff b * C <= t; equal scores rank the lower block first. It is the ground truth
+ * the pyramid walk's recall is measured against, at O(N^2) work.
+ */
+
+/* Device workspace of pisa_select_flat_exact (0 on bad input): every (position, eligible
+ * leaf) score, fp32, B * Hkv * N * ceil(N / 64) * 4 bytes. Contents need not be initialised
+ * and are meaningless after the call. */
+size_t pisa_flat_exact_workspace_bytes(const pisa_dims* dims, int64_t N, int64_t n_capacity);
+
+/*
+ * Exact flat selection for every query position t in 0..N-1.
+ *   q        [B, N, Hq, d] bf16.
+ *   k        [B, n_capacity, Hkv, d] bf16 (the first N rows are read).
+ *   out_idx  int32 [B, N, Hkv, topk]: the K best eligible blocks in ascending order, -1
+ *            padded (every eligible block when at most K are).
+ *   workspace at least pisa_flat_exact_workspace_bytes(dims, N, n_capacity) bytes.
+ * dims->dtype must be PISA_DTYPE_BF16 and dims->score PISA_SCORE_LSE (else
+ * PISA_ERR_UNSUPPORTED). Arithmetic: q.k on the MFMA in fp32 from the bf16 inputs, the
+ * log-sum-exp in fp32 with base-2 exponentials, as the walk's leaf stage. Errors: as
+ * pisa_select_prefill; also PISA_ERR_UNSUPPORTED when B * Hkv > 65535.
+ */
+int pisa_select_flat_exact(const void* q, const void* k, int64_t N, int64_t n_capacity, const pisa_dims* dims,
+                           int32_t* out_idx, void* workspace, size_t ws_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* pisa_status_string(int status);
 
