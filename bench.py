@@ -722,6 +722,34 @@ def planted_bench(torch, ops, synth, setup, time_steps, log, n_flat: int = 96, s
     ops.select_flat(q, pyr, N, N, dims, out_f, ops.alloc_flat_workspace(dims, N, device=q.device))
     fidx = out_f.cpu().numpy()[0]
     recall_flat_mean = float((np.isin(fidx[ts], planted).sum(axis=2) / denom).mean())
+    # flat exact top-K at every position on the GPU (pisa_select_flat_exact: every eligible leaf
+    # scored by its raw-key LogSumExp, the walk's leaf arithmetic), timed on the library's stream
+    stream = torch.cuda.current_stream()
+    out_x = torch.empty_like(out)
+    ws_x = ops.alloc_flat_exact_workspace(dims, N, device=q.device)
+    ops.select_flat_exact(q, k, N, N, dims, out_x, ws_x)
+    torch.cuda.synchronize()
+    ex0, ex1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ex0.record(stream)
+    for _ in range(3):
+        ops.select_flat_exact(q, k, N, N, dims, out_x, ws_x)
+    ex1.record(stream)
+    torch.cuda.synchronize()
+    exact_ms = ex0.elapsed_time(ex1) / 3
+    # its algorithmic exponentials: one per (query head, key <= t) at every position
+    exact_exps = float(N) * (N + 1) / 2 * wl.Hq * wl.B
+    xidx = out_x.cpu().numpy()[0]
+    recall_exact = float((np.isin(xidx[ts], planted).sum(axis=2) / denom).mean())
+    # overlap Recall@K against flat exact top-K at every position with more than K eligible leaves
+    # (both sets then hold K blocks)
+    tk = np.arange(K * C, N)
+
+    def overlap_all(sel):
+        a, b = sel[tk], xidx[tk]
+        return float(((a[..., :, None] == b[..., None, :]).any(axis=-1).sum(axis=-1) / K).mean())
+
+    overlap_walk_all, overlap_flat_mean_all = overlap_all(idx), overlap_all(fidx)
+    del out_x, ws_x
     # flat exact top-K on a sample
     rng = np.random.default_rng(seed)
     sample = np.sort(rng.choice(ts, size=min(n_flat, len(ts)), replace=False))
@@ -768,7 +796,13 @@ def planted_bench(torch, ops, synth, setup, time_steps, log, n_flat: int = 96, s
            "attention_mass_ratio_random_K": float(np.mean(mratio_rand)),
            "flat_mean_summary_planted_recall": recall_flat_mean,
            "flat_mean_summary_attention_mass_ratio": float(np.mean(mratio_fm)),
-           "flat_mean_summary_overlap_vs_flat_exact": float(np.mean(overlap_fm))}
+           "flat_mean_summary_overlap_vs_flat_exact": float(np.mean(overlap_fm)),
+           "flat_exact_gpu": {"ms": exact_ms, "planted_recall": recall_exact,
+                              "exp_per_s": exact_exps / (exact_ms / 1e3),
+                              "transcendental_frac": exact_exps / (exact_ms / 1e3) / TRANSCENDENTAL_PEAK,
+                              "walk_overlap_recall_at_K": overlap_walk_all,
+                              "flat_mean_summary_overlap_recall_at_K": overlap_flat_mean_all,
+                              "positions": int(len(tk))}}
     log(f"planted 32K: {res['ms']:.3f} ms, planted recall {recall:.3f} (chance {chance:.3f}; on "
         f"{len(sample)} sampled positions flat exact top-K {res['flat_exact_recall_sample']:.3f}, the walk "
         f"{res['walk_recall_same_sample']:.3f}; overlap with flat exact top-K "
@@ -777,6 +811,9 @@ def planted_bench(torch, ops, synth, setup, time_steps, log, n_flat: int = 96, s
         f"(flat exact top-K {res['attention_mass_ratio_flat_exact']:.4f}, K random eligible blocks "
         f"{res['attention_mass_ratio_random_K']:.4f})); flat stage-one selection by leaf means: planted recall "
         f"{recall_flat_mean:.3f}, mass ratio {res['flat_mean_summary_attention_mass_ratio']:.4f}")
+    log(f"flat exact top-K on the GPU at all {len(tk)} positions with more than K eligible blocks: "
+        f"{exact_ms:.3f} ms, planted recall {recall_exact:.3f}; overlap Recall@K against it: the walk "
+        f"{overlap_walk_all:.4f}, the flat leaf-mean selection {overlap_flat_mean_all:.4f}")
     del q, k, pyr, out, ws, out_f
     return res
 
