@@ -340,6 +340,8 @@ def main():
     ap.add_argument("--decode-only", action="store_true", help="time only the decode workload")
     ap.add_argument("--packed-only", action="store_true", help="time only the packed-document workloads")
     ap.add_argument("--batched-only", action="store_true", help="time only the batched (B > 1) workloads")
+    ap.add_argument("--flat-exact-only", action="store_true",
+                    help="time only the exact flat selection (pisa_select_flat_exact) on the planted 32K workload")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs into profiles/hbm_traffic.json (no GPU)")
     args = ap.parse_args()
@@ -469,6 +471,27 @@ def main():
         return
     if args.batched_only:
         print(json.dumps({"batched": batched_bench(torch, ops, dev, log)}), flush=True)
+        return
+    if args.flat_exact_only:
+        wl = synth.WORKLOADS["mid_planted"]
+        inp, N, dims, q, k, pyr, out, ws = setup(wl)
+        ws_x = ops.alloc_flat_exact_workspace(dims, N, device=dev)
+        for _ in range(2):
+            ops.select_flat_exact(q, k, N, N, dims, out, ws_x)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            ops.select_flat_exact(q, k, N, N, dims, out, ws_x)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        exps = float(N) * (N + 1) / 2 * wl.Hq * wl.B
+        res = {"N": N, "ms": ms, "exp_per_s": exps / (ms / 1e3),
+               "transcendental_frac": exps / (ms / 1e3) / TRANSCENDENTAL_PEAK}
+        log(f"exact flat selection N={N}: {ms:.3f} ms ({res['transcendental_frac']:.3f} of the exp peak)")
+        print(json.dumps({"flat_exact": res}), flush=True)
         return
 
     if args.copy_calibration:

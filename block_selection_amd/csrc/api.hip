@@ -1008,14 +1008,15 @@ int pisa_select_flat_exact(const void* q, const void* k, int64_t N, int64_t n_ca
     if (dims->dtype != PISA_DTYPE_BF16 || dims->score != PISA_SCORE_LSE) return PISA_ERR_UNSUPPORTED;
     Geom G;
     if ((rc = make_geom(dims, N, n_capacity, &G)) != PISA_OK) return rc;
-    const int64_t chunks = (N + kGrpKeys - 1) / kGrpKeys;             // 128 positions per workgroup
+    const int64_t chunks = (N + kGrpKeys - 1) / kGrpKeys;             // 128 positions per chunk
+    const int64_t tiles = chunks * (chunks + 1) / 2;                   // (chunk, sibling pair <= chunk)
     const int64_t walks = (int64_t)dims->B * N * dims->Hkv;
-    if (chunks > INT_MAX || (walks + 3) / 4 > INT_MAX || (int64_t)dims->B * dims->Hkv > 65535)
+    if ((tiles + 3) / 4 > INT_MAX || (walks + 3) / 4 > INT_MAX || (int64_t)dims->B * dims->Hkv > 65535)
         return PISA_ERR_UNSUPPORTED;
     if (!workspace || ws_bytes < flat_exact_ws(dims, N)) return PISA_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     float* S = (float*)workspace;
-    hipLaunchKernelGGL(flat_exact_scores_kernel, dim3((unsigned)chunks, (unsigned)(dims->B * dims->Hkv)), dim3(256),
+    hipLaunchKernelGGL(flat_exact_scores_kernel, dim3((unsigned)((tiles + 3) / 4), (unsigned)(dims->B * dims->Hkv)), dim3(256),
                        0, s, (const uint16_t*)q, (const uint16_t*)k, G, S);
     hipLaunchKernelGGL(flat_exact_topk_kernel, dim3((unsigned)((walks + 3) / 4)), dim3(256), 0, s, S, G, out_idx);
     return launch_status();

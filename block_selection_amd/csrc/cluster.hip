@@ -728,54 +728,73 @@ template __global__ void final_topk_kernel<64>(const int32_t*, const int32_t*, c
 // Exact flat scores (pisa_select_flat_exact): S[(bh * N + t) * M1 + L] = the score the walk
 // gives leaf L as a candidate of position t (score_unit: the group sum of the base-2 LSE over
 // the leaf's raw keys up to t) for every eligible (t, L), i.e. L * 64 <= t; other entries are
-// not written. Grid (ceil(N / 128), B * Hkv), four wavefronts: workgroup c covers positions
-// 128c .. 128c + 127, and its wavefronts take in turn the sibling pairs p <= c (the pairs with
-// a leaf eligible for some position of the range), holding the pair's keys in registers and
-// scoring the range's positions two at a time.
+// not written. The work is the lower triangle of (128-position chunk c, sibling pair p <= c)
+// tiles, the pairs with a leaf eligible for some position of the chunk: tile c (c + 1) / 2 + p.
+// One wavefront per tile, four per workgroup, grid (ceil(tiles / 4), B * Hkv): the wavefront
+// holds the pair's keys in registers and scores the chunk's positions two at a time (a unit),
+// the next unit's queries in flight while one is scored.
 __global__ __launch_bounds__(256) void flat_exact_scores_kernel(const uint16_t* __restrict__ q,
                                                                 const uint16_t* __restrict__ k, Geom G,
                                                                 float* __restrict__ S) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int n = lane & 15, gq = lane >> 4;
-    const int bh = blockIdx.y, b = bh / G.Hkv, kvh = bh % G.Hkv;
     const int64_t N = G.N, M1 = G.M[1];
-    const int64_t t0 = (int64_t)blockIdx.x * kGrpKeys;
-    const int64_t npairs = (M1 + 1) / 2;
-    const int64_t pmax = ((int64_t)blockIdx.x < npairs - 1) ? (int64_t)blockIdx.x : npairs - 1;
+    const int64_t chunks = (N + kGrpKeys - 1) / kGrpKeys;
+    const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (tile >= chunks * (chunks + 1) / 2) return;   // wavefront-uniform
+    int64_t c = (int64_t)((sqrt(8.0 * (double)tile + 1.0) - 1.0) * 0.5);
+    while (c > 0 && c * (c + 1) / 2 > tile) --c;
+    while ((c + 1) * (c + 2) / 2 <= tile) ++c;
+    const int64_t p = tile - c * (c + 1) / 2;
+    const int bh = blockIdx.y, b = bh / G.Hkv, kvh = bh % G.Hkv;
     const int64_t row_stride = (int64_t)G.Hkv * kD;
     const uint16_t* kb = k + ((int64_t)b * G.cap * G.Hkv + kvh) * kD;
     const int64_t qrow0 = (int64_t)b * N;   // query row of position 0 of batch element b
     float* Sb = S + (int64_t)bh * N * M1;
     // this lane's row group gq reports (position gq >> 1 of the unit, leaf gq & 1 of the pair)
     const int my_walk = gq >> 1, my_leaf = gq & 1;
-    for (int64_t p = wave; p <= pmax; p += 4) {
-        PairKeys K;
-        load_pair_keys(kb, row_stride, p * kGrpKeys, N, n, gq, K);
-        for (int u = 0; u < kGrpKeys / 2; ++u) {
-            const int64_t ta = t0 + 2 * u;
-            if (ta >= N) break;
-            const bool two = ta + 1 < N;
-            const int64_t tb = two ? ta + 1 : ta;   // a unit of one position repeats it
-            int lim[4];   // per (walk r >> 1, leaf r & 1): the leaf's keys up to t are 0 .. lim
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t rel = ((r >> 1) ? tb : ta) - (2 * p + (r & 1)) * kC;
-                lim[r] = rel < 0 ? -1 : (rel > kC - 1 ? kC - 1 : (int)rel);
-            }
-            u32x4 a0, a1, b0, b1;
-            load_q(q, qrow0 + ta, G.Hq, kvh, G.GQ, n, gq, a0, a1);
-            if (two) {
-                load_q(q, qrow0 + tb, G.Hq, kvh, G.GQ, n, gq, b0, b1);
-            } else {
-                b0 = a0;
-                b1 = a1;
-            }
-            const float sc = score_unit(K, lim, __builtin_bit_cast(bf16x8, a0), __builtin_bit_cast(bf16x8, a1),
-                                        __builtin_bit_cast(bf16x8, b0), __builtin_bit_cast(bf16x8, b1), n, gq,
-                                        G.GQ, two);
-            const int64_t t = my_walk ? tb : ta, L = 2 * p + my_leaf;
-            if (n == 0 && (two || my_walk == 0) && L < M1 && L * kC <= t) Sb[t * M1 + L] = sc;
+    PairKeys K;
+    load_pair_keys(kb, row_stride, p * kGrpKeys, N, n, gq, K);
+    const int64_t t0 = c * kGrpKeys;
+    const int64_t rest = N - t0;
+    const int nu = (int)(rest >= kGrpKeys ? kGrpKeys / 2 : (rest + 1) / 2);
+    auto unit_pos = [&](int u, int64_t& ta, int64_t& tb) {
+        ta = t0 + 2 * u;
+        tb = (ta + 1 < N) ? ta + 1 : ta;   // a unit of one position repeats it
+    };
+    u32x4 a0, a1, b0, b1;
+    {
+        int64_t ta, tb;
+        unit_pos(0, ta, tb);
+        load_q(q, qrow0 + ta, G.Hq, kvh, G.GQ, n, gq, a0, a1);
+        load_q(q, qrow0 + tb, G.Hq, kvh, G.GQ, n, gq, b0, b1);
+    }
+    for (int u = 0; u < nu; ++u) {
+        int64_t ta, tb;
+        unit_pos(u, ta, tb);
+        const bool two = tb != ta;
+        u32x4 na0 = a0, na1 = a1, nb0 = b0, nb1 = b1;
+        if (u + 1 < nu) {
+            int64_t tan, tbn;
+            unit_pos(u + 1, tan, tbn);
+            load_q(q, qrow0 + tan, G.Hq, kvh, G.GQ, n, gq, na0, na1);
+            load_q(q, qrow0 + tbn, G.Hq, kvh, G.GQ, n, gq, nb0, nb1);
         }
+        int lim[4];   // per (walk r >> 1, leaf r & 1): the leaf's keys up to t are 0 .. lim
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t rel = ((r >> 1) ? tb : ta) - (2 * p + (r & 1)) * kC;
+            lim[r] = rel < 0 ? -1 : (rel > kC - 1 ? kC - 1 : (int)rel);
+        }
+        const float sc = score_unit(K, lim, __builtin_bit_cast(bf16x8, a0), __builtin_bit_cast(bf16x8, a1),
+                                    __builtin_bit_cast(bf16x8, b0), __builtin_bit_cast(bf16x8, b1), n, gq, G.GQ,
+                                    two);
+        const int64_t t = my_walk ? tb : ta, L = 2 * p + my_leaf;
+        if (n == 0 && (two || my_walk == 0) && L < M1 && L * kC <= t) Sb[t * M1 + L] = sc;
+        a0 = na0;
+        a1 = na1;
+        b0 = nb0;
+        b1 = nb1;
     }
 }
 
