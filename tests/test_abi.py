@@ -204,3 +204,30 @@ def test_decode_attention_argument_errors_return_before_launch():
     assert att(good, t=4096) == ops.PISA_ERR_CAPACITY
     assert att(ops.make_dims(1, 32, 2, 32, dtype="f32")) == ops.PISA_ERR_UNSUPPORTED
     assert att(good, ws_bytes=16) == ops.PISA_ERR_WORKSPACE
+
+
+def test_flat_exact_argument_errors_return_before_launch():
+    from block_selection_amd import ops
+    p = ctypes.c_void_p(8)
+    good = ops.make_dims(1, 32, 2, 8)
+
+    def sel(dims, N=4096, cap=4096, ptr=p, ws_bytes=None):
+        if ws_bytes is None:
+            ws_bytes = ops.flat_exact_workspace_bytes(dims, N, cap)
+        return ops.lib.pisa_select_flat_exact(ptr, p, N, cap, ctypes.byref(dims), p, p, ws_bytes, None)
+
+    # one fp32 score per (batch, KV head, position, leaf), rounded up to 256 bytes
+    assert ops.flat_exact_workspace_bytes(good, 4096) == 2 * 4096 * 64 * 4
+    assert ops.flat_exact_workspace_bytes(ops.make_dims(3, 8, 1, 4), 1000, 2000) == \
+        (3 * 1000 * 16 * 4 + 255) // 256 * 256
+    assert ops.flat_exact_workspace_bytes(good, 0) == 0
+    assert ops.flat_exact_workspace_bytes(good, 10, 5) == 0
+    assert sel(good, ptr=None, ws_bytes=1 << 30) == ops.PISA_ERR_INVALID_ARG
+    assert sel(good, N=0, ws_bytes=1 << 30) == ops.PISA_ERR_INVALID_ARG
+    assert sel(good, N=5000, cap=4096, ws_bytes=1 << 30) == ops.PISA_ERR_CAPACITY
+    assert sel(ops.make_dims(1, 32, 2, 8, dtype="f32"), ws_bytes=1 << 30) == ops.PISA_ERR_UNSUPPORTED
+    assert sel(ops.make_dims(1, 32, 2, 8, score="mean"), ws_bytes=1 << 30) == ops.PISA_ERR_UNSUPPORTED
+    assert sel(ops.make_dims(1, 32, 2, 40), ws_bytes=1 << 30) == ops.PISA_ERR_UNSUPPORTED   # K > 32
+    assert sel(good, ws_bytes=ops.flat_exact_workspace_bytes(good, 4096) - 4) == ops.PISA_ERR_WORKSPACE
+    assert ops.lib.pisa_select_flat_exact(p, p, 4096, 4096, ctypes.byref(good), p, None, 1 << 30,
+                                          None) == ops.PISA_ERR_WORKSPACE

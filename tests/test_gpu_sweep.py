@@ -126,3 +126,24 @@ def test_decode_random_shapes_equal_prefill(c, N0, Hq, Hkv, K):
             q[0, n] = inp.q_new[s, 0]
             ref = run_prefill(q, k_all[None, : n + 1], K, "bf16")
             assert np.array_equal(dec, ref.idx[0, n]), (s, dec, ref.idx[0, n])
+
+
+def _flat_exact_configs(seed: int, n: int):
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        Hq, Hkv = SHAPES[rng.integers(len(SHAPES))]
+        K = int(TOPK[rng.integers(len(TOPK))])
+        N = int(rng.integers(1, 6001))
+        out.append((c, N, Hq, Hkv, K))
+    return out
+
+
+@pytest.mark.parametrize("c,N,Hq,Hkv,K", _flat_exact_configs(313, 12))
+def test_flat_exact_random_shape(c, N, Hq, Hkv, K):
+    """The exact flat selection at every position of seeded random lengths, group sizes and
+    budgets, under the same rule (oracle.flat_exact_select / flat_exact_validate)."""
+    from test_gpu_flat_exact import _case
+    inp = synth.make_prefill(synth.Workload("sweep_flat_exact", N=N, Hq=Hq, Hkv=Hkv, topk=K, dtype="bf16",
+                                            seed=9000 + c))
+    _case(f"sweep{c}", inp.q, inp.k, K)
