@@ -459,6 +459,10 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
     // one level of the walk; kInLds: the level's delta rows are staged in LDS (else gathered)
     auto level = [&](int l, auto in_lds_const) {
         constexpr bool in_lds = decltype(in_lds_const)::value;
+        // the serial chain from the survivors to the level's row loads runs at a raised wave
+        // priority, so that a wavefront's next loads issue ahead of the other wavefronts'
+        // scoring arithmetic; the scoring and the sort run at the normal priority
+        __builtin_amdgcn_s_setprio(2);
         int cand;
         float P = 0.0f;
         if (l == ls) {
@@ -543,6 +547,7 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
                     rv_next = pick(i + 1, rown);
                     nxt = fetch(rown);
                 }
+                if (i == 0) __builtin_amdgcn_s_setprio(0);
                 const f32x4 acc = summary_tile_mfma(qf[i / TPW].k0, qf[i / TPW].k1, cur.h0, cur.h1, cur.l0, cur.l1);
                 delta_tile_parts<S>(acc, rv, gq, G.GQ, fp[i], xp[i]);
                 cur = nxt;
@@ -600,6 +605,7 @@ __device__ inline void upper_delta_group(const uint16_t* __restrict__ q, const u
             const uint32_t moved = (uint32_t)push_to_lane(dst, (int)(uint32_t)slot_key(0.0f, cand, ml));
             surv_low = (ml < K) ? moved : 0u;
         }
+        __builtin_amdgcn_s_setprio(0);
     };
     // the levels down to the last one staged in LDS (the levels above it are not scored), then
     // the gathered ones: each phase without a per-tile choice of source
